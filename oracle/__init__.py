@@ -1,0 +1,169 @@
+"""CPU oracle for MoE expert-parallel dispatch and combine.
+
+TEST INFRASTRUCTURE ONLY. A plain, slow, single-threaded C definition of what
+dispatch and combine compute (``ep_oracle.c``), bound here with ctypes over
+numpy arrays. Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline
+leg of ``bench.py`` may import it; the GPU library never does, and the two
+share no code. Passages followed and readings taken are listed in
+``ep_oracle.h``.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+BF16 = 0
+FP16 = 1
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    lib = ctypes.CDLL(_build.LIB)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    Z = ctypes.c_size_t
+    lib.oracle_dispatch.argtypes = [I, I, I, I, Z, Z, P, P, P, P, P, P, P, P, P, P, P, P]
+    lib.oracle_dispatch.restype = I
+    lib.oracle_layout_by_sort.argtypes = [I, I, I, I, P, P, P, P]
+    lib.oracle_layout_by_sort.restype = I
+    lib.oracle_combine.argtypes = [I, I, I, I, I, P, P, P, P, P, P]
+    lib.oracle_combine.restype = I
+    lib.oracle_combine_push.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P]
+    lib.oracle_combine_push.restype = I
+    for name in ("oracle_f32_to_bf16_n", "oracle_f32_to_f16_n",
+                 "oracle_bf16_to_f32_n", "oracle_f16_to_f32_n"):
+        getattr(lib, name).argtypes = [P, P, Z]
+        getattr(lib, name).restype = None
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _c(a, dtype=None):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if dtype is not None:
+        assert a.dtype == dtype, (a.dtype, dtype)
+    return a
+
+
+def dispatch(W, M, k, Er, ntok, x, idx, w=None, scales=None):
+    """Dispatch by definition. ``x`` is any contiguous array shaped [W, M, ...]
+    whose trailing bytes form one payload row; ``scales`` likewise (or None).
+    Returns a dict of out_x (uint8 [W, W*M, row_bytes]), out_idx, out_w,
+    out_scales (uint8 rows), recv [W], src_pos [W, W*M], fwd [W, M, min(W,k)].
+    Rows that receive nothing stay zero."""
+    lib = _load()
+    ntok = _c(np.asarray(ntok, dtype=np.int32))
+    x = _c(x)
+    idx = _c(idx, np.int32)
+    w = _c(w, np.float32)
+    scales = _c(scales)
+    WM = W * M
+    P = min(W, k)
+    row_bytes = x.nbytes // (W * M)
+    scale_bytes = 0 if scales is None else scales.nbytes // (W * M)
+    out = dict(
+        out_x=np.zeros((W, WM, row_bytes), np.uint8),
+        out_idx=np.zeros((W, WM, k), np.int32),
+        out_w=None if w is None else np.zeros((W, WM, k), np.float32),
+        out_scales=None if scales is None else np.zeros((W, WM, scale_bytes), np.uint8),
+        recv=np.zeros(W, np.int32),
+        src_pos=np.full((W, WM), -1, np.int32),
+        fwd=np.full((W, M, P), -1, np.int32),
+    )
+    rc = lib.oracle_dispatch(W, M, k, Er, row_bytes, scale_bytes, _ptr(ntok), _ptr(x), _ptr(idx),
+                             _ptr(w), _ptr(scales), _ptr(out["out_x"]), _ptr(out["out_idx"]),
+                             _ptr(out["out_w"]), _ptr(out["out_scales"]), _ptr(out["recv"]),
+                             _ptr(out["src_pos"]), _ptr(out["fwd"]))
+    if rc != 0:
+        raise RuntimeError(f"oracle_dispatch failed ({rc})")
+    return out
+
+
+def layout_by_sort(W, M, k, Er, ntok, idx):
+    """Second formulation of the receive layout (sort of (d, r, t) triples).
+    Returns (recv [W], src_pos [W, W*M])."""
+    lib = _load()
+    ntok = _c(np.asarray(ntok, dtype=np.int32))
+    idx = _c(idx, np.int32)
+    recv = np.zeros(W, np.int32)
+    src_pos = np.full((W, W * M), -1, np.int32)
+    rc = lib.oracle_layout_by_sort(W, M, k, Er, _ptr(ntok), _ptr(idx), _ptr(recv), _ptr(src_pos))
+    if rc != 0:
+        raise RuntimeError(f"oracle_layout_by_sort failed ({rc})")
+    return recv, src_pos
+
+
+def combine(W, M, k, H, dtype, ntok, fwd, y, y_w=None):
+    """Combine by definition (gather form). ``y`` holds 16-bit words
+    [W, W*M, H] (bf16 when dtype == BF16, fp16 when FP16). Returns
+    (out uint16 [W, M, H], out_w float32 [W, M, k] or None); rows of absent
+    tokens stay zero."""
+    lib = _load()
+    ntok = _c(np.asarray(ntok, dtype=np.int32))
+    fwd = _c(fwd, np.int32)
+    y = _c(y).view(np.uint16)
+    y_w = _c(y_w, np.float32)
+    out = np.zeros((W, M, H), np.uint16)
+    out_w = None if y_w is None else np.zeros((W, M, k), np.float32)
+    rc = lib.oracle_combine(W, M, k, H, dtype, _ptr(ntok), _ptr(fwd), _ptr(y), _ptr(y_w),
+                            _ptr(out), _ptr(out_w))
+    if rc != 0:
+        raise RuntimeError(f"oracle_combine failed ({rc})")
+    return out, out_w
+
+
+def combine_push(W, M, k, Er, H, dtype, ntok, idx, recv, src_pos, y, y_w=None):
+    """Combine, second formulation (push form through src_pos)."""
+    lib = _load()
+    ntok = _c(np.asarray(ntok, dtype=np.int32))
+    idx = _c(idx, np.int32)
+    recv = _c(recv, np.int32)
+    src_pos = _c(src_pos, np.int32)
+    y = _c(y).view(np.uint16)
+    y_w = _c(y_w, np.float32)
+    out = np.zeros((W, M, H), np.uint16)
+    out_w = None if y_w is None else np.zeros((W, M, k), np.float32)
+    rc = lib.oracle_combine_push(W, M, k, Er, H, dtype, _ptr(ntok), _ptr(idx), _ptr(recv),
+                                 _ptr(src_pos), _ptr(y), _ptr(y_w), _ptr(out), _ptr(out_w))
+    if rc != 0:
+        raise RuntimeError(f"oracle_combine_push failed ({rc})")
+    return out, out_w
+
+
+def _conv(name, a, in_dtype, out_dtype):
+    lib = _load()
+    a = np.ascontiguousarray(a, dtype=in_dtype)
+    out = np.empty(a.shape, out_dtype)
+    getattr(lib, name)(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def f32_to_bf16(a):
+    return _conv("oracle_f32_to_bf16_n", a, np.float32, np.uint16)
+
+
+def f32_to_f16(a):
+    return _conv("oracle_f32_to_f16_n", a, np.float32, np.uint16)
+
+
+def bf16_to_f32(a):
+    return _conv("oracle_bf16_to_f32_n", a, np.uint16, np.float32)
+
+
+def f16_to_f32(a):
+    return _conv("oracle_f16_to_f32_n", a, np.uint16, np.float32)

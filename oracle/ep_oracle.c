@@ -1,0 +1,368 @@
+/*
+ * CPU oracle for MoE expert-parallel dispatch and combine.
+ *
+ * TEST INFRASTRUCTURE ONLY: a plain, slow, obviously correct definition that
+ * the GPU library is checked against. Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load it. It shares no code with the GPU
+ * library. Page citations and the readings taken are listed in ep_oracle.h.
+ *
+ * Built with a host C compiler in ISO C11 mode: binary32 arithmetic in SSE
+ * registers, round-to-nearest-even, no contraction, no reassociation.
+ */
+#include "ep_oracle.h"
+
+#include <stdlib.h>
+#include <string.h>
+#include <math.h>
+
+/* ------------------------------------------------------------------------ */
+/* IEEE 754 conversions, from the formats' definitions.                      */
+/* ------------------------------------------------------------------------ */
+
+static uint32_t f32_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+static float bits_f32(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+/* bfloat16 keeps binary32's sign and 8-bit exponent and the top 7 fraction
+ * bits. Binary32 encodings of one sign are ordered like their magnitudes, so
+ * rounding to nearest on the encoding is rounding to nearest on the value: drop
+ * the low 16 bits, round up when they exceed half, or equal half and the kept
+ * part is odd. A carry out of the fraction moves to the next binade, and out of
+ * the largest finite value to infinity, as the format requires. */
+uint16_t oracle_f32_to_bf16(float f)
+{
+    uint32_t u = f32_bits(f);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0)
+        return 0x7FC0; /* NaN -> quiet NaN */
+    uint32_t kept = u >> 16;
+    uint32_t dropped = u & 0xFFFFu;
+    if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u)))
+        kept += 1;
+    return (uint16_t)kept;
+}
+
+float oracle_bf16_to_f32(uint16_t h) { return bits_f32((uint32_t)h << 16); }
+
+/* binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits; normal values
+ * (1 + f/1024) * 2^(e-15) for e in 1..30; subnormals f * 2^-24; e = 31 is
+ * infinity / NaN. The largest finite value is 65504; the rounding boundary to
+ * infinity is 65520 (a tie that rounds to the even neighbour, which is 2^16,
+ * i.e. infinity). */
+uint16_t oracle_f32_to_f16(float f)
+{
+    uint32_t u = f32_bits(f);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    uint32_t e32 = (u >> 23) & 0xFFu;
+    uint32_t frac = u & 0x007FFFFFu;
+    if (e32 == 0xFFu)
+        return frac ? (uint16_t)0x7E00 : (uint16_t)(sign | 0x7C00u);
+    if (fabsf(f) >= 65520.0f)
+        return (uint16_t)(sign | 0x7C00u);
+    if (e32 == 0)           /* binary32 zero or subnormal: |f| < 2^-126, far */
+        return sign;        /* below half of the smallest binary16 subnormal  */
+    /* |f| = sig * 2^(e - 23), sig in [2^23, 2^24), e = unbiased exponent. */
+    int e = (int)e32 - 127;
+    uint64_t sig = (uint64_t)(frac | 0x00800000u);
+    /* binary16 quantum at this magnitude: 2^(max(e, -14) - 10). */
+    int qe = (e < -14 ? -14 : e) - 10;
+    int shift = qe - (e - 23); /* low bits of sig below the quantum (>= 13) */
+    uint64_t n;
+    if (shift >= 40) {
+        n = 0;              /* far below half a quantum */
+    } else {
+        n = sig >> shift;
+        uint64_t rem = sig & ((1ull << shift) - 1);
+        uint64_t half = 1ull << (shift - 1);
+        if (rem > half || (rem == half && (n & 1u)))
+            n += 1;
+    }
+    /* magnitude = n * 2^qe. Normal range (e >= -14): n in [1024, 2048],
+     * exponent field e + 15 and fraction n - 1024, where n = 2048 carries into
+     * the exponent. Subnormal range: the encoding is n itself, and n = 1024
+     * is exactly the smallest normal's encoding. Both are one formula. */
+    int ebase = (e < -14 ? -14 : e) + 14;
+    uint32_t mag = ((uint32_t)ebase << 10) + (uint32_t)n;
+    return (uint16_t)(sign | mag);
+}
+
+float oracle_f16_to_f32(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1F;
+    int f = h & 0x3FF;
+    float v;
+    if (e == 0)
+        v = ldexpf((float)f, -24);
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexpf((float)(1024 + f), e - 25);
+    return sign ? -v : v;
+}
+
+void oracle_f32_to_bf16_n(const float *in, uint16_t *out, size_t n)
+{ for (size_t i = 0; i < n; ++i) out[i] = oracle_f32_to_bf16(in[i]); }
+void oracle_f32_to_f16_n(const float *in, uint16_t *out, size_t n)
+{ for (size_t i = 0; i < n; ++i) out[i] = oracle_f32_to_f16(in[i]); }
+void oracle_bf16_to_f32_n(const uint16_t *in, float *out, size_t n)
+{ for (size_t i = 0; i < n; ++i) out[i] = oracle_bf16_to_f32(in[i]); }
+void oracle_f16_to_f32_n(const uint16_t *in, float *out, size_t n)
+{ for (size_t i = 0; i < n; ++i) out[i] = oracle_f16_to_f32(in[i]); }
+
+/* ------------------------------------------------------------------------ */
+/* Routing: the ordered distinct destination ranks of one token.             */
+/* ------------------------------------------------------------------------ */
+
+/* [PR712] "How the gfx1201 kernels work", Dispatch: a token's selected
+ * experts map to destination ranks, and experts on the same rank share one
+ * payload. Expert e lives on rank e / Er (ranks hold contiguous blocks of
+ * experts_per_rank experts; [GUIDE] section 2 shows 256 experts over 8 ranks
+ * as 32 a rank). Ranks are listed in the order their first expert appears in
+ * the top-k row. An id outside [0, W*Er) selects no rank. */
+static int token_ranks(const int32_t *idx_row, int k, int Er, int W, int32_t *ranks)
+{
+    int n = 0;
+    for (int j = 0; j < k; ++j) {
+        int32_t e = idx_row[j];
+        if (e < 0 || e >= W * Er)
+            continue;
+        int32_t d = e / Er;
+        int seen = 0;
+        for (int q = 0; q < n; ++q)
+            if (ranks[q] == d)
+                seen = 1;
+        if (!seen)
+            ranks[n++] = d;
+    }
+    return n;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dispatch.                                                                 */
+/* ------------------------------------------------------------------------ */
+
+int oracle_dispatch(int W, int M, int k, int Er, size_t row_bytes, size_t scale_bytes,
+                    const int32_t *ntok, const uint8_t *x, const int32_t *idx,
+                    const float *w, const uint8_t *sc,
+                    uint8_t *out_x, int32_t *out_idx, float *out_w, uint8_t *out_sc,
+                    int32_t *recv, int32_t *src_pos, int32_t *fwd)
+{
+    const int64_t WM = (int64_t)W * M;
+    if (WM * W > 2147483647LL)
+        return -1;
+    const int P = W < k ? W : k;
+
+    /* Step 1: each token's ordered distinct ranks. */
+    int32_t *ranks = malloc(sizeof(int32_t) * (size_t)WM * (size_t)P);
+    int32_t *nr = malloc(sizeof(int32_t) * (size_t)WM);
+    int64_t *cnt = calloc((size_t)W * W, sizeof(int64_t));
+    int64_t *base = calloc((size_t)W * W, sizeof(int64_t));
+    int64_t *run = calloc((size_t)W * W, sizeof(int64_t));
+    if (!ranks || !nr || !cnt || !base || !run) {
+        free(ranks); free(nr); free(cnt); free(base); free(run);
+        return -1;
+    }
+    for (int r = 0; r < W; ++r)
+        for (int t = 0; t < ntok[r]; ++t) {
+            int64_t tok = (int64_t)r * M + t;
+            nr[tok] = token_ranks(idx + tok * k, k, Er, W, ranks + tok * P);
+        }
+
+    /* Step 2: cnt[r][d] tokens of rank r that go to d; the rows rank d
+     * receives are grouped by source rank in ascending order, so source r's
+     * group on d starts at the sum of the groups of ranks r' < r. */
+    for (int r = 0; r < W; ++r)
+        for (int t = 0; t < ntok[r]; ++t) {
+            int64_t tok = (int64_t)r * M + t;
+            for (int i = 0; i < nr[tok]; ++i)
+                cnt[(int64_t)r * W + ranks[tok * P + i]] += 1;
+        }
+    for (int d = 0; d < W; ++d) {
+        int64_t acc = 0;
+        for (int r = 0; r < W; ++r) {
+            base[(int64_t)r * W + d] = acc;
+            acc += cnt[(int64_t)r * W + d];
+        }
+        recv[d] = (int32_t)acc;
+    }
+
+    /* Step 3: walk tokens in (rank, token) order; each (token, rank) pair
+     * takes the next row of its group. [PR712] Dispatch: one receive row per
+     * token per destination rank, the payload and routing metadata copied to
+     * it, and the way back to the source recorded. [GUIDE] dispatch() returns
+     * the received tokens with their weights, scales and expert indices;
+     * get_dispatch_src_token_pos() encodes a row's source as
+     * src_rank * (world_size * max_num_inp_token_per_rank) + src_token_id. */
+    for (int r = 0; r < W; ++r)
+        for (int t = 0; t < ntok[r]; ++t) {
+            int64_t tok = (int64_t)r * M + t;
+            for (int i = 0; i < P; ++i)
+                fwd[tok * P + i] = -1;
+            for (int i = 0; i < nr[tok]; ++i) {
+                int d = ranks[tok * P + i];
+                int64_t s = base[(int64_t)r * W + d] + run[(int64_t)r * W + d];
+                run[(int64_t)r * W + d] += 1;
+                int64_t row = (int64_t)d * WM + s;
+                memcpy(out_x + (size_t)row * row_bytes, x + (size_t)tok * row_bytes, row_bytes);
+                memcpy(out_idx + (size_t)row * k, idx + (size_t)tok * k, sizeof(int32_t) * (size_t)k);
+                if (w)
+                    memcpy(out_w + (size_t)row * k, w + (size_t)tok * k, sizeof(float) * (size_t)k);
+                if (scale_bytes)
+                    memcpy(out_sc + (size_t)row * scale_bytes, sc + (size_t)tok * scale_bytes, scale_bytes);
+                src_pos[row] = (int32_t)((int64_t)r * WM + t);
+                fwd[tok * P + i] = (int32_t)row;
+            }
+        }
+
+    free(ranks); free(nr); free(cnt); free(base); free(run);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Layout, second formulation: sort the (d, r, t) triples.                   */
+/* ------------------------------------------------------------------------ */
+
+typedef struct { int32_t d, r, t; } triple_t;
+
+static int triple_cmp(const void *a, const void *b)
+{
+    const triple_t *x = a, *y = b;
+    if (x->d != y->d) return x->d < y->d ? -1 : 1;
+    if (x->r != y->r) return x->r < y->r ? -1 : 1;
+    if (x->t != y->t) return x->t < y->t ? -1 : 1;
+    return 0;
+}
+
+int oracle_layout_by_sort(int W, int M, int k, int Er, const int32_t *ntok,
+                          const int32_t *idx, int32_t *recv, int32_t *src_pos)
+{
+    const int64_t WM = (int64_t)W * M;
+    const int P = W < k ? W : k;
+    triple_t *tri = malloc(sizeof(triple_t) * (size_t)(WM * P + 1));
+    int32_t *ranks = malloc(sizeof(int32_t) * (size_t)P);
+    if (!tri || !ranks) { free(tri); free(ranks); return -1; }
+    int64_t n = 0;
+    for (int r = 0; r < W; ++r)
+        for (int t = 0; t < ntok[r]; ++t) {
+            int nd = token_ranks(idx + ((int64_t)r * M + t) * k, k, Er, W, ranks);
+            for (int i = 0; i < nd; ++i) {
+                tri[n].d = ranks[i]; tri[n].r = r; tri[n].t = t;
+                ++n;
+            }
+        }
+    qsort(tri, (size_t)n, sizeof(triple_t), triple_cmp);
+    for (int d = 0; d < W; ++d)
+        recv[d] = 0;
+    for (int64_t q = 0; q < n; ++q) {
+        int d = tri[q].d;
+        int64_t s = recv[d]++;
+        src_pos[(int64_t)d * WM + s] = (int32_t)((int64_t)tri[q].r * WM + tri[q].t);
+    }
+    free(tri); free(ranks);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Combine.                                                                  */
+/* ------------------------------------------------------------------------ */
+
+static float widen(uint16_t v, int dtype)
+{ return dtype == 0 ? oracle_bf16_to_f32(v) : oracle_f16_to_f32(v); }
+static uint16_t narrow(float v, int dtype)
+{ return dtype == 0 ? oracle_f32_to_bf16(v) : oracle_f32_to_f16(v); }
+
+/* Fold one token's n contribution rows (flat row numbers rows[0..n)) in the
+ * given order. [PR712] "How the gfx1201 kernels work", Combine: the source
+ * sums its contributions in FP32, then converts the output to BF16/FP16;
+ * optional FP32 weights are summed separately and no routing weight is
+ * applied. The sum starts from the first contribution and adds the rest one
+ * at a time in the token's distinct-rank order; an empty sum is +0. */
+static void fold_token(int n, const int64_t *rows, int H, int k, int dtype,
+                       const uint16_t *y, const float *y_w, uint16_t *out_row, float *out_w_row)
+{
+    for (int h = 0; h < H; ++h) {
+        if (n == 0) {
+            out_row[h] = 0;
+            continue;
+        }
+        float acc = widen(y[(size_t)rows[0] * H + h], dtype);
+        for (int i = 1; i < n; ++i)
+            acc = acc + widen(y[(size_t)rows[i] * H + h], dtype);
+        out_row[h] = narrow(acc, dtype);
+    }
+    if (y_w && out_w_row) {
+        for (int j = 0; j < k; ++j) {
+            if (n == 0) {
+                out_w_row[j] = 0.0f;
+                continue;
+            }
+            float acc = y_w[(size_t)rows[0] * k + j];
+            for (int i = 1; i < n; ++i)
+                acc = acc + y_w[(size_t)rows[i] * k + j];
+            out_w_row[j] = acc;
+        }
+    }
+}
+
+int oracle_combine(int W, int M, int k, int H, int dtype, const int32_t *ntok,
+                   const int32_t *fwd, const uint16_t *y, const float *y_w,
+                   uint16_t *out, float *out_w)
+{
+    const int P = W < k ? W : k;
+    int64_t rows[64];
+    for (int r = 0; r < W; ++r)
+        for (int t = 0; t < ntok[r]; ++t) {
+            int64_t tok = (int64_t)r * M + t;
+            int n = 0;
+            for (int i = 0; i < P; ++i)
+                if (fwd[tok * P + i] >= 0)
+                    rows[n++] = fwd[tok * P + i];
+            fold_token(n, rows, H, k, dtype, y, y_w, out + (size_t)tok * H,
+                       out_w ? out_w + (size_t)tok * k : NULL);
+        }
+    return 0;
+}
+
+int oracle_combine_push(int W, int M, int k, int Er, int H, int dtype,
+                        const int32_t *ntok, const int32_t *idx,
+                        const int32_t *recv, const int32_t *src_pos,
+                        const uint16_t *y, const float *y_w,
+                        uint16_t *out, float *out_w)
+{
+    const int64_t WM = (int64_t)W * M;
+    const int P = W < k ? W : k;
+    int64_t *slots = malloc(sizeof(int64_t) * (size_t)(WM * P));
+    int32_t ranks[64];
+    if (!slots)
+        return -1;
+    for (int64_t q = 0; q < WM * P; ++q)
+        slots[q] = -1;
+    /* Every received row goes back to its source token, at the place its
+     * rank holds in that token's distinct-rank order. */
+    for (int d = 0; d < W; ++d)
+        for (int32_t s = 0; s < recv[d]; ++s) {
+            int64_t row = (int64_t)d * WM + s;
+            int32_t p = src_pos[row];
+            int r = (int)(p / WM), t = (int)(p % WM);
+            int nd = token_ranks(idx + ((int64_t)r * M + t) * k, k, Er, W, ranks);
+            for (int i = 0; i < nd; ++i)
+                if (ranks[i] == d)
+                    slots[((int64_t)r * M + t) * P + i] = row;
+        }
+    int64_t rows[64];
+    for (int r = 0; r < W; ++r)
+        for (int t = 0; t < ntok[r]; ++t) {
+            int64_t tok = (int64_t)r * M + t;
+            int nd = token_ranks(idx + tok * k, k, Er, W, ranks);
+            for (int i = 0; i < nd; ++i) {
+                rows[i] = slots[tok * P + i];
+                if (rows[i] < 0) {      /* a (token, rank) pair never received */
+                    free(slots);
+                    return -2;
+                }
+            }
+            fold_token(nd, rows, H, k, dtype, y, y_w, out + (size_t)tok * H,
+                       out_w ? out_w + (size_t)tok * k : NULL);
+        }
+    free(slots);
+    return 0;
+}

@@ -1,0 +1,112 @@
+/*
+ * CPU oracle for MoE expert-parallel dispatch and combine.
+ *
+ * TEST INFRASTRUCTURE ONLY. This is a plain, slow, single-threaded definition
+ * of what dispatch and combine compute. It exists to check the GPU library
+ * against; nothing on the product path may include, link or call it. It
+ * shares no code, header, table or helper with the GPU library.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [PR712]  "feat(ep): add opt-in gfx1201 EP2/EP4 support" (ROCm/mori PR 712),
+ *           section "How the gfx1201 kernels work": the Dispatch and Combine
+ *           bullets define the method.
+ *  [GUIDE]  "MORI-EP User Guide", section 3 "Operator API": dispatch() and
+ *           combine() outputs and shapes; get_dispatch_src_token_pos() gives
+ *           the reverse-map encoding.
+ *  [PR726]  "gfx1250 EPv2: EP4 topk-9 geometry; selfFirst follows
+ *           MORI_EP_TOKOFF_EXT" (ROCm/mori PR 726): a token's combine rows
+ *           come from at most min(world size, top-k) distinct ranks.
+ *  [PR703]  "refactor(EPv2): replace per-module __device__ staging with shared
+ *           buffer" (ROCm/mori PR 703), section "Motivation": the receive
+ *           capacity of a rank is world size x max tokens per rank.
+ *
+ * Readings taken where the pages are silent (each also listed in the design
+ * notes): expert e lives on rank e / experts_per_rank; received rows on a
+ * rank are ordered by (source rank, source token); the combine sum runs in
+ * first-occurrence top-k order of the token's distinct ranks, seeded with the
+ * first contribution; the FP32 result is rounded to nearest even; an expert
+ * id outside [0, E) selects no rank; a token with no rank combines to +0.
+ *
+ * Parity status: every function here is pinned by tests that do not call it
+ * through itself (brute force, a second formulation, closed forms, library
+ * conversions); none is "parity unpinned".
+ */
+#ifndef EP_ORACLE_H
+#define EP_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Dispatch, by definition.
+ *   W ranks, M = max tokens per rank, k = top-k, Er = experts per rank.
+ *   row_bytes   = bytes of one payload row (hidden x element size).
+ *   scale_bytes = bytes of one scale row (0: no scales, sc/out_sc unused).
+ *   ntok[W]                 tokens present on each rank (<= M).
+ *   x[W][M][row_bytes]      payload rows (only t < ntok[r] are read).
+ *   idx[W][M][k]            expert ids.
+ *   w[W][M][k]              routing weights (may be NULL: out_w unused).
+ *   sc[W][M][scale_bytes]   scale rows.
+ * Outputs, with WM = W * M:
+ *   out_x[W][WM][row_bytes], out_idx[W][WM][k], out_w[W][WM][k],
+ *   out_sc[W][WM][scale_bytes]: rows s < recv[d] are written, others untouched.
+ *   recv[W]                 rows received by each rank.
+ *   src_pos[W][WM]          src_rank * WM + src_token for each received row.
+ *   fwd[W][M][P], P = min(W, k): for token (r,t), entry i is d * WM + s for
+ *                           the i-th distinct rank d of the token, -1 after.
+ * Returns 0, or -1 on a size overflow. */
+int oracle_dispatch(int W, int M, int k, int Er, size_t row_bytes, size_t scale_bytes,
+                    const int32_t *ntok, const uint8_t *x, const int32_t *idx,
+                    const float *w, const uint8_t *sc,
+                    uint8_t *out_x, int32_t *out_idx, float *out_w, uint8_t *out_sc,
+                    int32_t *recv, int32_t *src_pos, int32_t *fwd);
+
+/* Second formulation of the receive layout: every (d, r, t) triple with d a
+ * rank of token (r,t) is sorted by the C library's qsort on (d, r, t), and a
+ * row's slot is its position among the triples of its d. Writes recv[W] and
+ * src_pos[W][WM]. Returns 0, or -1 if memory runs out. */
+int oracle_layout_by_sort(int W, int M, int k, int Er, const int32_t *ntok,
+                          const int32_t *idx, int32_t *recv, int32_t *src_pos);
+
+/* Combine, by definition (gather form).
+ *   H = hidden size, dtype 0 = bf16, 1 = fp16 for y and out.
+ *   fwd[W][M][P] as written by oracle_dispatch.
+ *   y[W][WM][H]   expert outputs, one per received row.
+ *   y_w[W][WM][k] optional FP32 weights to sum (NULL: out_w unused).
+ * out[W][M][H] and out_w[W][M][k]: rows t < ntok[r] are written. */
+int oracle_combine(int W, int M, int k, int H, int dtype, const int32_t *ntok,
+                   const int32_t *fwd, const uint16_t *y, const float *y_w,
+                   uint16_t *out, float *out_w);
+
+/* Combine, second formulation (push form): walk the received rows, route each
+ * back to its source through src_pos, place it at the position its rank takes
+ * in the token's distinct-rank order, then fold every token in that order.
+ * Needs idx to know each token's rank order. Same outputs as oracle_combine. */
+int oracle_combine_push(int W, int M, int k, int Er, int H, int dtype,
+                        const int32_t *ntok, const int32_t *idx,
+                        const int32_t *recv, const int32_t *src_pos,
+                        const uint16_t *y, const float *y_w,
+                        uint16_t *out, float *out_w);
+
+/* IEEE 754 conversions used by the combine cast, written from the formats'
+ * definitions: binary32 -> bfloat16 / binary16 with round-to-nearest-even,
+ * overflow to infinity, NaN to a quiet NaN; and the exact widenings back. */
+uint16_t oracle_f32_to_bf16(float f);
+uint16_t oracle_f32_to_f16(float f);
+float oracle_bf16_to_f32(uint16_t h);
+float oracle_f16_to_f32(uint16_t h);
+
+/* Bulk forms of the four conversions, for tests. */
+void oracle_f32_to_bf16_n(const float *in, uint16_t *out, size_t n);
+void oracle_f32_to_f16_n(const float *in, uint16_t *out, size_t n);
+void oracle_bf16_to_f32_n(const uint16_t *in, float *out, size_t n);
+void oracle_f16_to_f32_n(const uint16_t *in, float *out, size_t n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_ORACLE_H */
