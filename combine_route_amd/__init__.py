@@ -1,0 +1,296 @@
+"""Python binding of the combine_route_amd C ABI (include/ep.h).
+
+MoE expert-parallel dispatch and combine for W virtual ranks held in one
+MI355X's HBM, computed by the gfx950 kernels of libcombine_route_amd.so. This
+module only marshals arguments: the functions below carry the C names and
+pass tensor addresses through; torch provides device memory and streams.
+Before a pointer reaches the library, each tensor is checked to be a
+contiguous device tensor at least as large as the call will touch, so a
+wrong-sized buffer raises here instead of faulting the GPU.
+
+There is no CPU fallback: if the library is not built, importing succeeds but
+the first call raises.
+"""
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcombine_route_amd.so")
+
+EP_BF16, EP_FP16, EP_FP8_E4M3 = 0, 1, 2
+EP_OK, EP_ERR_NULL, EP_ERR_ARG, EP_ERR_ALIGN, EP_ERR_SIZE, EP_ERR_STATE, EP_ERR_HIP = (
+    0, -1, -2, -3, -4, -5, -6)
+EP_KERNEL_ROUTE, EP_KERNEL_SCAN, EP_KERNEL_COPY, EP_KERNEL_COMBINE = 0, 1, 2, 3
+
+DTYPES = {"bf16": EP_BF16, "fp16": EP_FP16, "fp8": EP_FP8_E4M3}
+ELEM_BYTES = {EP_BF16: 2, EP_FP16: 2, EP_FP8_E4M3: 1}
+
+EXPORTED = ("ep_workspace_bytes", "ep_plan_create", "ep_plan_destroy", "ep_dispatch",
+            "ep_combine", "ep_get_src_token_pos", "ep_last_error", "ep_plan_set_launch",
+            "ep_plan_get_launch", "ep_plan_set_timing", "ep_plan_kernel_time")
+
+
+class EpConfig(ctypes.Structure):
+    """ep_config_t: after the pages' EpDispatchCombineConfig."""
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "world_size", "hidden_dim", "scale_dim", "scale_type_size", "max_num_inp_token_per_rank",
+        "num_experts_per_rank", "num_experts_per_token", "dispatch_dtype", "combine_dtype")]
+
+
+class EpDispatchArgs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "num_tokens", "x", "indices", "weights", "scales", "out_x", "out_indices",
+        "out_weights", "out_scales", "recv_num_token")]
+
+
+class EpCombineArgs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("y", "y_weights", "out", "out_weights")]
+
+
+class EpLaunch(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "tile_tokens", "dispatch_waves", "dispatch_row_split", "combine_waves",
+        "combine_row_split")]
+
+
+class EpError(RuntimeError):
+    def __init__(self, fn, code, msg):
+        super().__init__(f"{fn} failed ({code}): {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load():
+    """The loaded library. Raises if it was not built (no fallback exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run `python -m combine_route_amd.build` "
+                           "(or __graft_entry__.build()) first; there is no CPU fallback")
+    lib = ctypes.CDLL(LIB_PATH)
+    V, I, Z, P = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.POINTER
+    lib.ep_workspace_bytes.argtypes = [P(EpConfig)]
+    lib.ep_workspace_bytes.restype = Z
+    lib.ep_plan_create.argtypes = [P(EpConfig), V, Z, P(V)]
+    lib.ep_plan_destroy.argtypes = [V]
+    lib.ep_dispatch.argtypes = [V, P(EpDispatchArgs), V]
+    lib.ep_combine.argtypes = [V, P(EpCombineArgs), V]
+    lib.ep_get_src_token_pos.argtypes = [V, ctypes.c_int32, P(V)]
+    lib.ep_last_error.argtypes = []
+    lib.ep_last_error.restype = ctypes.c_char_p
+    lib.ep_plan_set_launch.argtypes = [V, P(EpLaunch)]
+    lib.ep_plan_get_launch.argtypes = [V, V, P(EpLaunch)]
+    lib.ep_plan_set_timing.argtypes = [V, I]
+    lib.ep_plan_kernel_time.argtypes = [V, I, P(ctypes.c_int32), P(ctypes.c_double)]
+    for name in EXPORTED:
+        if name not in ("ep_workspace_bytes", "ep_last_error"):
+            getattr(lib, name).restype = I
+    _lib = lib
+    return lib
+
+
+def ep_last_error() -> str:
+    return load().ep_last_error().decode()
+
+
+def _check(fn, rc):
+    if rc != EP_OK:
+        raise EpError(fn, rc, ep_last_error())
+
+
+def make_config(world_size, hidden_dim, max_num_inp_token_per_rank, num_experts_per_rank,
+                num_experts_per_token, dispatch_dtype="bf16", combine_dtype=None,
+                scale_dim=0, scale_type_size=4) -> EpConfig:
+    dd = DTYPES[dispatch_dtype] if isinstance(dispatch_dtype, str) else dispatch_dtype
+    if combine_dtype is None:
+        combine_dtype = EP_FP16 if dd == EP_FP16 else EP_BF16
+    cd = DTYPES[combine_dtype] if isinstance(combine_dtype, str) else combine_dtype
+    return EpConfig(world_size, hidden_dim, scale_dim, scale_type_size if scale_dim else 0,
+                    max_num_inp_token_per_rank, num_experts_per_rank, num_experts_per_token,
+                    dd, cd)
+
+
+def ep_workspace_bytes(cfg: EpConfig) -> int:
+    n = load().ep_workspace_bytes(ctypes.byref(cfg))
+    if n == 0:
+        raise EpError("ep_workspace_bytes", EP_ERR_ARG, ep_last_error())
+    return n
+
+
+def _dev(t: Optional[torch.Tensor], name: str, nbytes: int):
+    """Address of a contiguous device tensor of at least nbytes, or None."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU, not {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name} holds {have} bytes; this call needs {nbytes}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def ep_plan_create(cfg: EpConfig, workspace: torch.Tensor) -> int:
+    """Create a plan over a caller-owned workspace tensor (keep it alive)."""
+    need = ep_workspace_bytes(cfg)
+    ws = _dev(workspace, "workspace", need)
+    out = ctypes.c_void_p()
+    _check("ep_plan_create", load().ep_plan_create(
+        ctypes.byref(cfg), ws, workspace.numel() * workspace.element_size(), ctypes.byref(out)))
+    return out.value
+
+
+def ep_plan_destroy(plan: int) -> None:
+    _check("ep_plan_destroy", load().ep_plan_destroy(plan))
+
+
+def _sizes(cfg: EpConfig):
+    W, M, k = cfg.world_size, cfg.max_num_inp_token_per_rank, cfg.num_experts_per_token
+    row = cfg.hidden_dim * ELEM_BYTES[cfg.dispatch_dtype]
+    crow = cfg.hidden_dim * 2
+    srow = cfg.scale_dim * cfg.scale_type_size
+    return W, M, k, row, crow, srow
+
+
+def ep_dispatch(plan: int, cfg: EpConfig, num_tokens: Sequence[int], x, indices, weights,
+                scales, out_x, out_indices, out_weights, out_scales, recv_num_token,
+                stream=None) -> None:
+    """ep_dispatch(); tensors as in include/ep.h, sizes checked against cfg."""
+    W, M, k, row, _, srow = _sizes(cfg)
+    WM = W * M
+    nt = (ctypes.c_int32 * W)(*[int(v) for v in num_tokens])
+    if len(num_tokens) != W:
+        raise ValueError(f"num_tokens has {len(num_tokens)} entries; world_size is {W}")
+    a = EpDispatchArgs(
+        ctypes.cast(nt, ctypes.c_void_p),
+        _dev(x, "x", W * M * row), _dev(indices, "indices", W * M * k * 4),
+        _dev(weights, "weights", W * M * k * 4), _dev(scales, "scales", W * M * srow),
+        _dev(out_x, "out_x", W * WM * row), _dev(out_indices, "out_indices", W * WM * k * 4),
+        _dev(out_weights, "out_weights", W * WM * k * 4),
+        _dev(out_scales, "out_scales", W * WM * srow),
+        _dev(recv_num_token, "recv_num_token", W * 4))
+    _check("ep_dispatch", load().ep_dispatch(plan, ctypes.byref(a), _stream(stream)))
+
+
+def ep_combine(plan: int, cfg: EpConfig, y, y_weights, out, out_weights, stream=None) -> None:
+    """ep_combine(); tensors as in include/ep.h, sizes checked against cfg."""
+    W, M, k, _, crow, _ = _sizes(cfg)
+    WM = W * M
+    a = EpCombineArgs(_dev(y, "y", W * WM * crow), _dev(y_weights, "y_weights", W * WM * k * 4),
+                      _dev(out, "out", W * M * crow), _dev(out_weights, "out_weights", W * M * k * 4))
+    _check("ep_combine", load().ep_combine(plan, ctypes.byref(a), _stream(stream)))
+
+
+def ep_get_src_token_pos(plan: int, rank: int) -> int:
+    """Device address of rank `rank`'s src_token_pos array (int32 [W*M])."""
+    p = ctypes.c_void_p()
+    _check("ep_get_src_token_pos", load().ep_get_src_token_pos(plan, rank, ctypes.byref(p)))
+    return p.value
+
+
+def ep_plan_set_launch(plan: int, launch: Optional[dict] = None) -> None:
+    l = None if launch is None else ctypes.byref(EpLaunch(**{
+        f: int(launch.get(f, 0)) for f, _ in EpLaunch._fields_}))
+    _check("ep_plan_set_launch", load().ep_plan_set_launch(plan, l))
+
+
+def ep_plan_get_launch(plan: int, num_tokens: Sequence[int]) -> dict:
+    nt = (ctypes.c_int32 * len(num_tokens))(*[int(v) for v in num_tokens])
+    out = EpLaunch()
+    _check("ep_plan_get_launch", load().ep_plan_get_launch(
+        plan, ctypes.cast(nt, ctypes.c_void_p), ctypes.byref(out)))
+    return {f: getattr(out, f) for f, _ in EpLaunch._fields_}
+
+
+def ep_plan_set_timing(plan: int, enable: bool) -> None:
+    _check("ep_plan_set_timing", load().ep_plan_set_timing(plan, 1 if enable else 0))
+
+
+def ep_plan_kernel_time(plan: int, kernel: int):
+    """(launches timed, total milliseconds) of one EP_KERNEL_* kernel."""
+    c = ctypes.c_int32()
+    ms = ctypes.c_double()
+    _check("ep_plan_kernel_time", load().ep_plan_kernel_time(
+        plan, kernel, ctypes.byref(c), ctypes.byref(ms)))
+    return c.value, ms.value
+
+
+_TORCH = {EP_BF16: torch.bfloat16, EP_FP16: torch.float16, EP_FP8_E4M3: torch.float8_e4m3fn}
+
+
+class EpDispatchCombineOp:
+    """One plan with its workspace and output buffers, allocated once with
+    torch on the current device and reused by every call, in the manner of the
+    pages' EpDispatchCombineOp ("MORI-EP User Guide", section 3). dispatch()
+    and combine() return views of those buffers, valid until the next
+    dispatch ("MORI (ROCm/mori) — L2 Distillation", section 9)."""
+
+    def __init__(self, cfg: EpConfig, device=None, with_weights=True):
+        self.cfg = cfg
+        dev = torch.device("cuda") if device is None else torch.device(device)
+        W, M, k, _, _, srow = _sizes(cfg)
+        WM = W * M
+        H = cfg.hidden_dim
+        self.workspace = torch.empty(ep_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+        self.out_x = torch.empty((W, WM, H), dtype=_TORCH[cfg.dispatch_dtype], device=dev)
+        self.out_indices = torch.empty((W, WM, k), dtype=torch.int32, device=dev)
+        self.out_weights = (torch.empty((W, WM, k), dtype=torch.float32, device=dev)
+                            if with_weights else None)
+        self.out_scales = (torch.empty((W, WM, srow), dtype=torch.uint8, device=dev)
+                           if cfg.scale_dim else None)
+        self.recv_num_token = torch.empty((W,), dtype=torch.int32, device=dev)
+        self.combine_out = torch.empty((W, M, H), dtype=_TORCH[cfg.combine_dtype], device=dev)
+        self.combine_weights = (torch.empty((W, M, k), dtype=torch.float32, device=dev)
+                                if with_weights else None)
+        self.plan = ep_plan_create(cfg, self.workspace)
+        self._src_pos_off = [ep_get_src_token_pos(self.plan, r) - self.workspace.data_ptr()
+                             for r in range(W)]
+
+    def dispatch(self, num_tokens, x, indices, weights=None, scales=None, stream=None):
+        ep_dispatch(self.plan, self.cfg, num_tokens, x, indices, weights, scales, self.out_x,
+                    self.out_indices, self.out_weights if weights is not None else None,
+                    self.out_scales if scales is not None else None, self.recv_num_token, stream)
+        return (self.out_x, self.out_weights, self.out_scales, self.out_indices,
+                self.recv_num_token)
+
+    def combine(self, y, y_weights=None, stream=None):
+        ep_combine(self.plan, self.cfg, y, y_weights, self.combine_out,
+                   self.combine_weights if y_weights is not None else None, stream)
+        return self.combine_out, (self.combine_weights if y_weights is not None else None)
+
+    def src_token_pos(self, rank: int) -> torch.Tensor:
+        """int32 [W*M] view of rank's reverse map inside the workspace."""
+        WM = self.cfg.world_size * self.cfg.max_num_inp_token_per_rank
+        off = self._src_pos_off[rank]
+        return self.workspace[off: off + 4 * WM].view(torch.int32)
+
+    def set_launch(self, launch: Optional[dict] = None):
+        ep_plan_set_launch(self.plan, launch)
+
+    def close(self):
+        if self.plan:
+            ep_plan_destroy(self.plan)
+            self.plan = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

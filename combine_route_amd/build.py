@@ -1,0 +1,46 @@
+"""Build the gfx950 library libcombine_route_amd.so in-tree with hipcc.
+
+Run as ``python -m combine_route_amd.build`` (or through
+``__graft_entry__.build()``); it always recompiles.
+"""
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+LIB = os.path.join(PKG, "libcombine_route_amd.so")
+SOURCES = [os.path.join(PKG, "csrc", "ep_plan.cpp"), os.path.join(PKG, "csrc", "ep_kernels.hip")]
+ARCH = "gfx950"
+
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    # packed FP32 instructions stay off: the compiler would otherwise pair
+    # the combine's FP32 adds into v_pk_add_f32
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fno-fast-math", "-ffp-contract=off",
+    "-Wall", "-Wno-unused-command-line-argument",
+    "-I", os.path.join(ROOT, "include"),
+    "-I", os.path.join(PKG, "csrc"),
+]
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc"):
+        if c and os.path.exists(c):
+            return c
+    return "hipcc"
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *FLAGS, *extra, "-o", tmp, *SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

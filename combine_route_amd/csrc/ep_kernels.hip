@@ -1,0 +1,523 @@
+// gfx950 (MI355X, CDNA4) kernels of MoE expert-parallel dispatch and combine.
+//
+// The method ("feat(ep): add opt-in gfx1201 EP2/EP4 support", How the gfx1201
+// kernels work): dispatch maps each token's top-k experts to destination
+// ranks, keeps one row per (token, distinct rank), copies the payload and the
+// routing metadata to it and records the way back; combine gathers each
+// token's rows back, sums them in FP32 and casts to BF16/FP16.
+//
+// Four kernels, all enqueued on the caller's stream, none waiting on another
+// block or on a flag:
+//   route    one wave per routing tile (16..64 tokens of one rank, one token a
+//            lane): each token's destination mask, then one 64-lane ballot per
+//            destination rank gives the tile's per-rank row counts.
+//   scan     one block per destination rank: exclusive prefix sum of the
+//            tile counts in (source rank, tile) order -> first receive slot of
+//            every tile on every rank, and the rank's received-row count.
+//            Together with the in-tile ballot prefix this is a counting sort:
+//            rows on a rank are ordered by (source rank, source token), with
+//            no atomic deciding any position.
+//   copy     one block per (tile, row piece): wave 0 routes the tile again
+//            (masks, ordered rank lists, ballot prefixes into LDS); then every
+//            wave takes tokens, loads its piece of the payload row into
+//            registers once (16 B a lane) and stores it to each destination
+//            row; blocks of piece 0 also write the id, weight and scale rows,
+//            src_pos and the forward map.
+//   combine  one wave per (token, row piece): the token's forward-map entries
+//            (at most min(W, k), one a lane) become scalar row numbers; for
+//            each 16-byte column every contribution row is loaded before any
+//            is added, then folded in the token's rank order in FP32, rounded
+//            to nearest even by the hardware conversion, and stored.
+//
+// Pure data movement: no MFMA. Work is spread over source tokens (and row
+// pieces for small calls), never over destinations, so routing skew does
+// not serialise any block.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ep_kernels.h"
+
+namespace ep {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxTile = 64;
+
+// Number of lanes below this one whose bit is set in b.
+__device__ __forceinline__ int lanes_below(uint64_t b)
+{
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+}
+
+// A value every lane of the wave holds identically, moved to a scalar register.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+template <bool kNT>
+__device__ __forceinline__ void store16(u32x4* p, u32x4 v)
+{
+    if constexpr (kNT)
+        __builtin_nontemporal_store(v, p);
+    else
+        *p = v;
+}
+
+// Rank r owning tile g: the largest r with tile_start[r] <= g (ranks without
+// tiles share their start with the next rank and are skipped).
+__device__ __forceinline__ int rank_of_tile(const TileMap& tm, int g)
+{
+    int lo = 0, hi = tm.W - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tm.tile_start[mid] <= g)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ int rank_of_token(const TokenMap& tk, int flat)
+{
+    int lo = 0, hi = tk.W - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tk.tok_start[mid] <= flat)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// Destination ranks of one token (one lane). Expert e is on rank e / Er; an id
+// outside [0, E) selects none. With kList, the distinct ranks are written to
+// list[] in the order their first expert appears in the top-k row.
+template <bool kList>
+__device__ __forceinline__ uint64_t route_token(const int32_t* row, bool valid, int k, int Er,
+                                                int E, uint8_t* list, int& n)
+{
+    uint64_t m = 0;
+    n = 0;
+    if (!valid)
+        return 0;
+    auto take = [&](int32_t e) {
+        if ((uint32_t)e < (uint32_t)E) {
+            const uint32_t d = (uint32_t)e / (uint32_t)Er;
+            const uint64_t bit = 1ull << d;
+            if (!(m & bit)) {
+                m |= bit;
+                if constexpr (kList)
+                    list[n] = (uint8_t)d;
+                ++n;
+            }
+        }
+    };
+    if ((k & 3) == 0) {
+        for (int j = 0; j < k; j += 4) {
+            const int4 v = *reinterpret_cast<const int4*>(row + j);
+            take(v.x);
+            take(v.y);
+            take(v.z);
+            take(v.w);
+        }
+    } else {
+        for (int j = 0; j < k; ++j)
+            take(row[j]);
+    }
+    return m;
+}
+
+// ---------------------------------------------------------------------------
+// route: per-tile row counts for every destination rank.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void ep_route_kernel(RouteArgs a, TileMap tm)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int g = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (g >= tm.total_tiles)
+        return;  // whole waves only
+    const int r = rank_of_tile(tm, g);
+    const int t0 = (g - tm.tile_start[r]) * tm.tile_tokens;
+    const int cnt = min(tm.tile_tokens, tm.ntok[r] - t0);
+    int n;
+    const uint64_t m = route_token<false>(a.idx + ((int64_t)r * a.M + t0 + lane) * a.k,
+                                          lane < cnt, a.k, a.Er, a.E, nullptr, n);
+    int mine = 0;
+    for (int d = 0; d < tm.W; ++d) {
+        const uint64_t b = __ballot((m >> d) & 1);
+        if (lane == d)
+            mine = __popcll(b);
+    }
+    if (lane < tm.W)
+        a.tile_counts[(int64_t)lane * a.tile_stride + g] = mine;
+}
+
+// ---------------------------------------------------------------------------
+// scan: exclusive prefix of one destination rank's tile counts.
+// ---------------------------------------------------------------------------
+constexpr int kScanThreads = 256;
+constexpr int kScanPerThread = 4;
+
+__global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(ScanArgs a)
+{
+    __shared__ int32_t s_wave[kScanThreads / kWave];
+    const int d = blockIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int32_t* col = a.tile_counts + (int64_t)d * a.tile_stride;
+    int32_t* out = a.tile_base + (int64_t)d * a.tile_stride;
+    const int n = a.total_tiles;
+    int32_t carry = 0;
+    for (int base = 0; base < n; base += kScanThreads * kScanPerThread) {
+        const int i0 = base + threadIdx.x * kScanPerThread;
+        int32_t v[kScanPerThread];
+        int32_t sum = 0;
+#pragma unroll
+        for (int q = 0; q < kScanPerThread; ++q) {
+            v[q] = (i0 + q < n) ? col[i0 + q] : 0;
+            sum += v[q];
+        }
+        // inclusive scan of the per-thread sums across the wave
+        int32_t x = sum;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int32_t y = __shfl_up(x, off);
+            if (lane >= off)
+                x += y;
+        }
+        if (lane == kWave - 1)
+            s_wave[wave] = x;
+        __syncthreads();
+        int32_t before = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < kScanThreads / kWave; ++w) {
+            before += (w < wave) ? s_wave[w] : 0;
+            total += s_wave[w];
+        }
+        int32_t run = carry + before + x - sum;
+#pragma unroll
+        for (int q = 0; q < kScanPerThread; ++q) {
+            if (i0 + q < n)
+                out[i0 + q] = run;
+            run += v[q];
+        }
+        carry += total;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0)
+        a.recv[d] = carry;
+}
+
+// ---------------------------------------------------------------------------
+// copy: payload rows, metadata rows, src_pos and the forward map.
+// ---------------------------------------------------------------------------
+template <int VPL, bool kNT>
+__global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
+{
+    __shared__ uint8_t s_list[kMaxTile][kMaxRanks];  // [token][i]: i-th distinct rank
+    __shared__ uint8_t s_loc[kMaxTile][kMaxRanks];   // [token][d]: rows to d before it in the tile
+    __shared__ int32_t s_n[kMaxTile];                // distinct ranks of the token
+    __shared__ int32_t s_base[kMaxRanks];            // first slot of this tile on rank d
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nwaves = blockDim.x / kWave;
+    const int g = blockIdx.x;
+    const int piece = blockIdx.y;
+    const int r = rank_of_tile(tm, g);
+    const int t0 = (g - tm.tile_start[r]) * tm.tile_tokens;
+    const int cnt = min(tm.tile_tokens, tm.ntok[r] - t0);
+
+    if (wave == 0) {
+        int n;
+        const uint64_t m = route_token<true>(a.idx + ((int64_t)r * a.M + t0 + lane) * a.k,
+                                             lane < cnt, a.k, a.Er, a.E, s_list[lane], n);
+        s_n[lane] = n;
+        for (int d = 0; d < tm.W; ++d) {
+            const bool has = (m >> d) & 1;
+            const uint64_t b = __ballot(has);
+            if (has)
+                s_loc[lane][d] = (uint8_t)lanes_below(b);
+        }
+        if (lane < tm.W)
+            s_base[lane] = a.tile_base[(int64_t)lane * a.tile_stride + g];
+    }
+    __syncthreads();
+
+    if (piece == 0) {
+        const int k = a.k;
+        const int per = kWave / k;  // destination rows per store instruction
+        const int j = lane % k;
+        const int sub = lane / k;
+        for (int tok = wave; tok < cnt; tok += nwaves) {
+            const int t = t0 + tok;
+            const int64_t src = (int64_t)r * a.M + t;
+            const int n = uniform(s_n[tok]);
+            if (lane < a.P) {
+                int32_t v = -1;
+                if (lane < n) {
+                    const int d = s_list[tok][lane];
+                    v = d * a.WM + s_base[d] + s_loc[tok][d];
+                    a.src_pos[v] = r * a.WM + t;
+                }
+                a.fwd[src * a.P + lane] = v;
+            }
+            int32_t e = 0;
+            float wv = 0.f;
+            if (sub < per) {
+                e = a.idx[src * k + j];
+                if (a.w)
+                    wv = a.w[src * k + j];
+            }
+            for (int i0 = 0; i0 < n; i0 += per) {
+                const int i = i0 + sub;
+                if (sub < per && i < n) {
+                    const int d = s_list[tok][i];
+                    const int64_t row = (int64_t)d * a.WM + s_base[d] + s_loc[tok][d];
+                    a.out_idx[row * k + j] = e;
+                    if (a.w)
+                        a.out_w[row * k + j] = wv;
+                }
+            }
+            for (int q0 = 0; q0 < a.scale_dwords; q0 += kWave) {
+                const int q = q0 + lane;
+                const bool in = q < a.scale_dwords;
+                const uint32_t v = in ? a.sc[src * a.scale_dwords + q] : 0u;
+                for (int i = 0; i < n; ++i) {
+                    const int d = uniform(s_list[tok][i]);
+                    const int64_t row = (int64_t)d * a.WM + uniform(s_base[d] + s_loc[tok][d]);
+                    if (in)
+                        a.out_sc[row * a.scale_dwords + q] = v;
+                }
+            }
+        }
+    }
+
+    const int64_t vbeg = (int64_t)piece * a.piece_vecs;
+    const int64_t vend = min(a.row_vecs, vbeg + (int64_t)a.piece_vecs);
+    const u32x4* __restrict__ xs = reinterpret_cast<const u32x4*>(a.x);
+    u32x4* __restrict__ xd = reinterpret_cast<u32x4*>(a.out_x);
+    for (int tok = wave; tok < cnt; tok += nwaves) {
+        const int64_t src = (int64_t)r * a.M + t0 + tok;
+        const int n = uniform(s_n[tok]);
+        const u32x4* sp = xs + src * a.row_vecs;
+        for (int64_t v0 = vbeg; v0 < vend; v0 += (int64_t)kWave * VPL) {
+            u32x4 buf[VPL];
+#pragma unroll
+            for (int u = 0; u < VPL; ++u) {
+                const int64_t v = v0 + u * kWave + lane;
+                if (v < vend)
+                    buf[u] = sp[v];
+            }
+            for (int i = 0; i < n; ++i) {
+                const int d = uniform(s_list[tok][i]);
+                const int s = uniform(s_base[d] + s_loc[tok][d]);
+                u32x4* dp = xd + ((int64_t)d * a.WM + s) * a.row_vecs;
+#pragma unroll
+                for (int u = 0; u < VPL; ++u) {
+                    const int64_t v = v0 + u * kWave + lane;
+                    if (v < vend)
+                        store16<kNT>(dp + v, buf[u]);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// combine: ordered FP32 gather-sum and RNE cast.
+// ---------------------------------------------------------------------------
+template <int DT>
+__device__ __forceinline__ void widen(const u32x4& w, float (&f)[8])
+{
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if constexpr (DT == 0) {  // bf16: the upper half of a binary32
+            f[2 * q] = __builtin_bit_cast(float, w[q] << 16);
+            f[2 * q + 1] = __builtin_bit_cast(float, w[q] & 0xFFFF0000u);
+        } else {                  // fp16: exact hardware widening
+            f[2 * q] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[q] & 0xFFFFu));
+            f[2 * q + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[q] >> 16));
+        }
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ u32x4 narrow(const float (&f)[8])
+{
+    u32x4 w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if constexpr (DT == 0) {  // v_cvt_pk_bf16_f32: round to nearest even
+            const f32x2 p = {f[2 * q], f[2 * q + 1]};
+            w[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
+        } else {                  // v_cvt_f16_f32: round to nearest even
+            const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)f[2 * q]);
+            const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)f[2 * q + 1]);
+            w[q] = lo | (hi << 16);
+        }
+    }
+    return w;
+}
+
+// G: contribution rows loaded before folding; U: 16-byte columns per lane in
+// flight.
+template <int G, int U, int DT>
+__global__ __launch_bounds__(1024) void ep_combine_kernel(CombineArgs a, TokenMap tk)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int flat = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (flat >= tk.total)
+        return;  // whole waves only
+    const int piece = blockIdx.y;
+    const int r = rank_of_token(tk, flat);
+    const int64_t tok = (int64_t)r * a.M + (flat - tk.tok_start[r]);
+    const int32_t gl = lane < a.P ? a.fwd[tok * a.P + lane] : -1;
+    const int n = __popcll(__ballot(gl >= 0));  // entries >= 0 form a prefix
+
+    const u32x4* __restrict__ ys = reinterpret_cast<const u32x4*>(a.y);
+    u32x4* __restrict__ dst = reinterpret_cast<u32x4*>(a.out) + tok * a.row_vecs;
+    const int vbeg = piece * a.piece_vecs;
+    const int vend = min(a.row_vecs, vbeg + a.piece_vecs);
+    for (int v0 = vbeg; v0 < vend; v0 += kWave * U) {
+        float acc[U][8];
+        for (int i0 = 0; i0 < n; i0 += G) {
+            u32x4 rows[U][G];
+#pragma unroll
+            for (int q = 0; q < G; ++q) {
+                if (i0 + q < n) {
+                    const int64_t gq = __builtin_amdgcn_readlane(gl, i0 + q);
+                    const u32x4* yp = ys + gq * a.row_vecs;
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int v = v0 + u * kWave + lane;
+                        if (v < vend)
+                            rows[u][q] = yp[v];
+                    }
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < G; ++q) {
+                if (i0 + q < n) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        float f[8];
+                        widen<DT>(rows[u][q], f);
+                        if (i0 + q == 0) {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                acc[u][e] = f[e];
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                acc[u][e] = acc[u][e] + f[e];
+                        }
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = v0 + u * kWave + lane;
+            if (v < vend) {
+                if (n == 0) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        acc[u][e] = 0.0f;
+                }
+                dst[v] = narrow<DT>(acc[u]);
+            }
+        }
+    }
+
+    if (piece == 0 && a.yw != nullptr && lane < a.k) {
+        float acc = 0.0f;
+        for (int i = 0; i < n; ++i) {
+            const int64_t gi = __builtin_amdgcn_readlane(gl, i);
+            const float v = a.yw[gi * a.k + lane];
+            acc = (i == 0) ? v : acc + v;
+        }
+        a.out_w[tok * a.k + lane] = acc;
+    }
+}
+
+template <int VPL>
+hipError_t copy_with_vpl(const CopyArgs& a, const TileMap& tm, dim3 grid, dim3 block, bool nt,
+                         hipStream_t s)
+{
+    if (nt)
+        hipLaunchKernelGGL((ep_copy_kernel<VPL, true>), grid, block, 0, s, a, tm);
+    else
+        hipLaunchKernelGGL((ep_copy_kernel<VPL, false>), grid, block, 0, s, a, tm);
+    return hipGetLastError();
+}
+
+template <int G, int U>
+hipError_t combine_with(const CombineArgs& a, const TokenMap& tk, int dtype, dim3 grid,
+                        dim3 block, hipStream_t s)
+{
+    if (dtype == 0)
+        hipLaunchKernelGGL((ep_combine_kernel<G, U, 0>), grid, block, 0, s, a, tk);
+    else
+        hipLaunchKernelGGL((ep_combine_kernel<G, U, 1>), grid, block, 0, s, a, tk);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_route(const RouteArgs& a, const TileMap& tm, hipStream_t s)
+{
+    if (tm.total_tiles == 0)
+        return hipSuccess;
+    constexpr int kWaves = 4;
+    const dim3 grid((tm.total_tiles + kWaves - 1) / kWaves);
+    hipLaunchKernelGGL(ep_route_kernel, grid, dim3(kWaves * kWave), 0, s, a, tm);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan(const ScanArgs& a, int W, hipStream_t s)
+{
+    hipLaunchKernelGGL(ep_scan_kernel, dim3(W), dim3(kScanThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy(const CopyArgs& a, const TileMap& tm, int waves, int row_split,
+                       bool nontemporal, hipStream_t s)
+{
+    if (tm.total_tiles == 0)
+        return hipSuccess;
+    const dim3 grid(tm.total_tiles, row_split);
+    const dim3 block(waves * kWave);
+    const int per_lane = (a.piece_vecs + kWave - 1) / kWave;
+    if (per_lane <= 1)
+        return copy_with_vpl<1>(a, tm, grid, block, nontemporal, s);
+    if (per_lane <= 2)
+        return copy_with_vpl<2>(a, tm, grid, block, nontemporal, s);
+    if (per_lane <= 4)
+        return copy_with_vpl<4>(a, tm, grid, block, nontemporal, s);
+    if (per_lane <= 8)
+        return copy_with_vpl<8>(a, tm, grid, block, nontemporal, s);
+    return copy_with_vpl<16>(a, tm, grid, block, nontemporal, s);
+}
+
+hipError_t launch_combine(const CombineArgs& a, const TokenMap& tk, int dtype, int waves,
+                          int row_split, hipStream_t s)
+{
+    if (tk.total == 0)
+        return hipSuccess;
+    const dim3 grid((tk.total + waves - 1) / waves, row_split);
+    const dim3 block(waves * kWave);
+    if (a.P <= 1)
+        return combine_with<1, 4>(a, tk, dtype, grid, block, s);
+    if (a.P <= 2)
+        return combine_with<2, 4>(a, tk, dtype, grid, block, s);
+    if (a.P <= 4)
+        return combine_with<4, 2>(a, tk, dtype, grid, block, s);
+    return combine_with<8, 2>(a, tk, dtype, grid, block, s);
+}
+
+}  // namespace ep

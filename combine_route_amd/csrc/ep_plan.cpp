@@ -1,0 +1,614 @@
+// Host side of the C ABI in include/ep.h: configuration checks, workspace
+// layout, launch geometry, argument checks and kernel launches.
+//
+// Every precondition is checked before anything is enqueued, and a failed
+// check names the argument, as the gfx125x staging refactor does for an
+// unbound or misaligned buffer ("refactor(EPv2): replace per-module __device__
+// staging with shared buffer", Caller contract). Plans never allocate device
+// memory: the caller's workspace holds all device state.
+#include "ep.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "ep_kernels.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return code;
+}
+
+int ok()
+{
+    g_error.clear();
+    return EP_OK;
+}
+
+constexpr size_t kWorkspaceAlign = 256;
+constexpr size_t kPtrAlign = 16;
+constexpr int kTimerPool = 1024;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int elem_bytes(int dtype) { return dtype == EP_FP8_E4M3 ? 1 : 2; }
+
+// Derived sizes of a configuration; valid only if check_config() passed.
+struct Shape {
+    int W, M, k, Er, P, H;
+    int64_t E, WM;
+    int64_t row_bytes;    // dispatch payload row
+    int64_t crow_bytes;   // combine row
+    int64_t scale_bytes;  // scale row
+    int tile_stride;      // tiles a rank-major tile array can need (tile 16)
+    // workspace offsets
+    size_t off_counts, off_base, off_src_pos, off_fwd, total;
+};
+
+int check_config(const ep_config_t* c, Shape* s)
+{
+    if (!c)
+        return fail(EP_ERR_NULL, "cfg is NULL");
+    if (c->world_size < 1 || c->world_size > ep::kMaxRanks)
+        return fail(EP_ERR_ARG, "cfg.world_size = %d: must be in [1, %d]", c->world_size,
+                    ep::kMaxRanks);
+    if (c->max_num_inp_token_per_rank < 1)
+        return fail(EP_ERR_ARG, "cfg.max_num_inp_token_per_rank = %d: must be >= 1",
+                    c->max_num_inp_token_per_rank);
+    if (c->num_experts_per_token < 1 || c->num_experts_per_token > ep::kMaxTopk)
+        return fail(EP_ERR_ARG, "cfg.num_experts_per_token = %d: must be in [1, %d]",
+                    c->num_experts_per_token, ep::kMaxTopk);
+    if (c->num_experts_per_rank < 1)
+        return fail(EP_ERR_ARG, "cfg.num_experts_per_rank = %d: must be >= 1",
+                    c->num_experts_per_rank);
+    if (c->dispatch_dtype != EP_BF16 && c->dispatch_dtype != EP_FP16 &&
+        c->dispatch_dtype != EP_FP8_E4M3)
+        return fail(EP_ERR_ARG, "cfg.dispatch_dtype = %d: must be EP_BF16, EP_FP16 or EP_FP8_E4M3",
+                    c->dispatch_dtype);
+    if (c->combine_dtype != EP_BF16 && c->combine_dtype != EP_FP16)
+        return fail(EP_ERR_ARG, "cfg.combine_dtype = %d: must be EP_BF16 or EP_FP16",
+                    c->combine_dtype);
+    if (c->hidden_dim < 1)
+        return fail(EP_ERR_ARG, "cfg.hidden_dim = %d: must be >= 1", c->hidden_dim);
+    const int64_t W = c->world_size, M = c->max_num_inp_token_per_rank;
+    const int64_t row = (int64_t)c->hidden_dim * elem_bytes(c->dispatch_dtype);
+    const int64_t crow = (int64_t)c->hidden_dim * 2;
+    if (row % 16 != 0 || crow % 16 != 0)
+        return fail(EP_ERR_ARG,
+                    "cfg.hidden_dim = %d: payload (%lld B) and combine (%lld B) rows must be "
+                    "multiples of 16 bytes",
+                    c->hidden_dim, (long long)row, (long long)crow);
+    if (c->scale_dim < 0)
+        return fail(EP_ERR_ARG, "cfg.scale_dim = %d: must be >= 0", c->scale_dim);
+    int64_t sbytes = 0;
+    if (c->scale_dim > 0) {
+        const int sts = c->scale_type_size;
+        if (sts != 1 && sts != 2 && sts != 4 && sts != 8)
+            return fail(EP_ERR_ARG, "cfg.scale_type_size = %d: must be 1, 2, 4 or 8", sts);
+        sbytes = (int64_t)c->scale_dim * sts;
+        if (sbytes % 4 != 0)
+            return fail(EP_ERR_ARG,
+                        "cfg.scale_dim * cfg.scale_type_size = %lld: must be a multiple of 4",
+                        (long long)sbytes);
+    }
+    if (W * W * M > INT32_MAX)
+        return fail(EP_ERR_SIZE,
+                    "world_size^2 * max_num_inp_token_per_rank = %lld exceeds 2^31 - 1 "
+                    "(int32 row numbers)",
+                    (long long)(W * W * M));
+    if (W * (int64_t)c->num_experts_per_rank > INT32_MAX)
+        return fail(EP_ERR_SIZE, "world_size * num_experts_per_rank exceeds 2^31 - 1");
+
+    s->W = (int)W;
+    s->M = (int)M;
+    s->k = c->num_experts_per_token;
+    s->Er = c->num_experts_per_rank;
+    s->P = std::min(s->W, s->k);
+    s->H = c->hidden_dim;
+    s->E = W * c->num_experts_per_rank;
+    s->WM = W * M;
+    s->row_bytes = row;
+    s->crow_bytes = crow;
+    s->scale_bytes = sbytes;
+    const int64_t tiles_per_rank = (M + ep::kMinTile - 1) / ep::kMinTile;
+    s->tile_stride = (int)(W * tiles_per_rank);
+    size_t off = 0;
+    s->off_counts = off;
+    off = align_up(off + sizeof(int32_t) * (size_t)W * s->tile_stride, kWorkspaceAlign);
+    s->off_base = off;
+    off = align_up(off + sizeof(int32_t) * (size_t)W * s->tile_stride, kWorkspaceAlign);
+    s->off_src_pos = off;
+    off = align_up(off + sizeof(int32_t) * (size_t)W * s->WM, kWorkspaceAlign);
+    s->off_fwd = off;
+    off = align_up(off + sizeof(int32_t) * (size_t)W * M * s->P, kWorkspaceAlign);
+    s->total = off;
+    return EP_OK;
+}
+
+struct Timer {
+    std::vector<hipEvent_t> start, stop;
+    int next = 0;
+    int32_t count = 0;
+    double total_ms = 0.0;
+};
+
+}  // namespace
+
+struct ep_plan {
+    ep_config_t cfg;
+    Shape s;
+    uint8_t* ws;
+    bool dispatched = false;
+    int32_t last_ntok[ep::kMaxRanks] = {};
+    hipStream_t last_stream = nullptr;
+    bool launched = false;
+    ep_launch_t launch = {};
+    bool timing = false;
+    Timer timers[4];
+};
+
+namespace {
+
+int32_t* ws_counts(ep_plan* p) { return reinterpret_cast<int32_t*>(p->ws + p->s.off_counts); }
+int32_t* ws_base(ep_plan* p) { return reinterpret_cast<int32_t*>(p->ws + p->s.off_base); }
+int32_t* ws_src_pos(const ep_plan* p)
+{
+    return reinterpret_cast<int32_t*>(p->ws + p->s.off_src_pos);
+}
+int32_t* ws_fwd(ep_plan* p) { return reinterpret_cast<int32_t*>(p->ws + p->s.off_fwd); }
+
+int tiles_for(const int32_t* ntok, int W, int tt)
+{
+    int n = 0;
+    for (int r = 0; r < W; ++r)
+        n += (ntok[r] + tt - 1) / tt;
+    return n;
+}
+
+// Automatic geometry. Small calls get smaller routing tiles and rows split
+// into pieces so that the grid still covers the 256 compute units several
+// times over, as the gfx1201 kernels do below 256 tokens ("feat(ep): add
+// opt-in gfx1201 EP2/EP4 support", How the gfx1201 kernels work: hidden tiles
+// of 512 or 1024 elements).
+ep_launch_t auto_launch(const ep_plan* p, const int32_t* ntok)
+{
+    const Shape& s = p->s;
+    int64_t N = 0;
+    for (int r = 0; r < s.W; ++r)
+        N += ntok[r];
+    ep_launch_t l;
+    constexpr int kTargetBlocks = 1024;
+    l.tile_tokens = 16;
+    for (int tt : {64, 32}) {
+        if (tiles_for(ntok, s.W, tt) >= 512) {
+            l.tile_tokens = tt;
+            break;
+        }
+    }
+    const int tiles = std::max(1, tiles_for(ntok, s.W, l.tile_tokens));
+    const int64_t row_vecs = s.row_bytes / 16;
+    const int64_t max_split = std::max<int64_t>(1, row_vecs / ep::kWave);
+    l.dispatch_row_split = (int)std::min<int64_t>(
+        std::min<int64_t>(max_split, 65535), std::max(1, (kTargetBlocks + tiles - 1) / tiles));
+    l.dispatch_waves = l.tile_tokens >= 32 ? 8 : 4;
+    l.combine_waves = 4;
+    const int64_t cblocks = std::max<int64_t>(1, (N + l.combine_waves - 1) / l.combine_waves);
+    const int64_t crow_vecs = s.crow_bytes / 16;
+    const int64_t cmax_split = std::max<int64_t>(1, crow_vecs / ep::kWave);
+    l.combine_row_split = (int)std::min<int64_t>(
+        std::min<int64_t>(cmax_split, 65535),
+        std::max<int64_t>(1, (kTargetBlocks + cblocks - 1) / cblocks));
+    return l;
+}
+
+ep_launch_t effective_launch(const ep_plan* p, const int32_t* ntok)
+{
+    ep_launch_t l = auto_launch(p, ntok);
+    if (p->launch.tile_tokens > 0)
+        l.tile_tokens = p->launch.tile_tokens;
+    if (p->launch.dispatch_waves > 0)
+        l.dispatch_waves = p->launch.dispatch_waves;
+    if (p->launch.dispatch_row_split > 0)
+        l.dispatch_row_split = p->launch.dispatch_row_split;
+    if (p->launch.combine_waves > 0)
+        l.combine_waves = p->launch.combine_waves;
+    if (p->launch.combine_row_split > 0)
+        l.combine_row_split = p->launch.combine_row_split;
+    return l;
+}
+
+void timer_drain(Timer& t)
+{
+    for (int i = 0; i < t.next; ++i) {
+        float ms = 0.f;
+        if (hipEventSynchronize(t.stop[i]) == hipSuccess &&
+            hipEventElapsedTime(&ms, t.start[i], t.stop[i]) == hipSuccess) {
+            t.total_ms += ms;
+            t.count += 1;
+        }
+    }
+    t.next = 0;
+}
+
+void timers_destroy(ep_plan* p)
+{
+    for (Timer& t : p->timers) {
+        for (hipEvent_t e : t.start)
+            (void)hipEventDestroy(e);
+        for (hipEvent_t e : t.stop)
+            (void)hipEventDestroy(e);
+        t = Timer();
+    }
+}
+
+// Launch one kernel, bracketed by timing events when enabled.
+template <typename F>
+hipError_t timed(ep_plan* p, int kernel, hipStream_t stream, F&& launch)
+{
+    if (!p->timing)
+        return launch();
+    Timer& t = p->timers[kernel];
+    if (t.next == (int)t.start.size())
+        timer_drain(t);
+    hipError_t e = hipEventRecord(t.start[t.next], stream);
+    if (e != hipSuccess)
+        return e;
+    e = launch();
+    if (e != hipSuccess)
+        return e;
+    e = hipEventRecord(t.stop[t.next], stream);
+    if (e == hipSuccess)
+        t.next += 1;
+    return e;
+}
+
+int check_launch(const ep_plan* p, const ep_launch_t* l)
+{
+    const Shape& s = p->s;
+    if (l->tile_tokens > 0 && l->tile_tokens != 16 && l->tile_tokens != 32 && l->tile_tokens != 64)
+        return fail(EP_ERR_ARG, "launch.tile_tokens = %d: must be 16, 32 or 64", l->tile_tokens);
+    if (l->dispatch_waves > 16)
+        return fail(EP_ERR_ARG, "launch.dispatch_waves = %d: must be <= 16", l->dispatch_waves);
+    if (l->combine_waves > 16)
+        return fail(EP_ERR_ARG, "launch.combine_waves = %d: must be <= 16", l->combine_waves);
+    if (l->dispatch_row_split > 65535 || l->combine_row_split > 65535)
+        return fail(EP_ERR_ARG, "launch row splits must be <= 65535 (grid y limit)");
+    if (l->dispatch_row_split > s.row_bytes / 16)
+        return fail(EP_ERR_ARG, "launch.dispatch_row_split = %d: must be <= %lld",
+                    l->dispatch_row_split, (long long)(s.row_bytes / 16));
+    if (l->combine_row_split > s.crow_bytes / 16)
+        return fail(EP_ERR_ARG, "launch.combine_row_split = %d: must be <= %lld",
+                    l->combine_row_split, (long long)(s.crow_bytes / 16));
+    return EP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ep_workspace_bytes(const ep_config_t* cfg)
+{
+    Shape s;
+    if (check_config(cfg, &s) != EP_OK)
+        return 0;
+    ok();
+    return s.total;
+}
+
+int ep_plan_create(const ep_config_t* cfg, void* workspace, size_t workspace_bytes,
+                   ep_plan_t** out)
+{
+    Shape s;
+    int rc = check_config(cfg, &s);
+    if (rc != EP_OK)
+        return rc;
+    if (!workspace)
+        return fail(EP_ERR_NULL, "workspace is NULL");
+    if (!out)
+        return fail(EP_ERR_NULL, "out is NULL");
+    if (!aligned(workspace, kWorkspaceAlign))
+        return fail(EP_ERR_ALIGN, "workspace %p is not %zu-byte aligned", workspace,
+                    kWorkspaceAlign);
+    if (workspace_bytes < s.total)
+        return fail(EP_ERR_SIZE, "workspace_bytes = %zu: ep_workspace_bytes() requires %zu",
+                    workspace_bytes, s.total);
+    ep_plan* p = new (std::nothrow) ep_plan();
+    if (!p)
+        return fail(EP_ERR_SIZE, "out of host memory for the plan");
+    p->cfg = *cfg;
+    p->s = s;
+    p->ws = static_cast<uint8_t*>(workspace);
+    *out = p;
+    return ok();
+}
+
+int ep_plan_destroy(ep_plan_t* p)
+{
+    if (!p)
+        return ok();
+    int rc = EP_OK;
+    if (p->launched) {
+        const hipError_t e = hipStreamSynchronize(p->last_stream);
+        if (e != hipSuccess)
+            rc = fail(EP_ERR_HIP, "hipStreamSynchronize before destroy: %s", hipGetErrorString(e));
+    }
+    timers_destroy(p);
+    delete p;
+    return rc == EP_OK ? ok() : rc;
+}
+
+int ep_dispatch(ep_plan_t* p, const ep_dispatch_args_t* a, void* stream_ptr)
+{
+    if (!p)
+        return fail(EP_ERR_NULL, "plan is NULL");
+    if (!a)
+        return fail(EP_ERR_NULL, "args is NULL");
+    const Shape& s = p->s;
+    if (!a->num_tokens)
+        return fail(EP_ERR_NULL, "args.num_tokens is NULL");
+    for (int r = 0; r < s.W; ++r)
+        if (a->num_tokens[r] < 0 || a->num_tokens[r] > s.M)
+            return fail(EP_ERR_ARG, "args.num_tokens[%d] = %d: must be in [0, %d]", r,
+                        a->num_tokens[r], s.M);
+    struct {
+        const void* ptr;
+        const char* name;
+    } req[] = {{a->x, "args.x"},
+               {a->indices, "args.indices"},
+               {a->out_x, "args.out_x"},
+               {a->out_indices, "args.out_indices"},
+               {a->recv_num_token, "args.recv_num_token"}};
+    for (auto& q : req) {
+        if (!q.ptr)
+            return fail(EP_ERR_NULL, "%s is NULL", q.name);
+        if (!aligned(q.ptr, kPtrAlign))
+            return fail(EP_ERR_ALIGN, "%s = %p is not 16-byte aligned", q.name, q.ptr);
+    }
+    if ((a->weights == nullptr) != (a->out_weights == nullptr))
+        return fail(EP_ERR_ARG, "args.weights and args.out_weights must both be set or both NULL");
+    if (a->weights && (!aligned(a->weights, kPtrAlign) || !aligned(a->out_weights, kPtrAlign)))
+        return fail(EP_ERR_ALIGN, "args.weights / args.out_weights are not 16-byte aligned");
+    if (s.scale_bytes > 0) {
+        if (!a->scales || !a->out_scales)
+            return fail(EP_ERR_NULL, "args.scales and args.out_scales are required (scale_dim = %d)",
+                        p->cfg.scale_dim);
+        if (!aligned(a->scales, kPtrAlign) || !aligned(a->out_scales, kPtrAlign))
+            return fail(EP_ERR_ALIGN, "args.scales / args.out_scales are not 16-byte aligned");
+    } else if (a->scales || a->out_scales) {
+        return fail(EP_ERR_ARG, "args.scales and args.out_scales must be NULL when scale_dim = 0");
+    }
+    const ep_launch_t l = effective_launch(p, a->num_tokens);
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+
+    ep::TileMap tm = {};
+    tm.W = s.W;
+    tm.tile_tokens = l.tile_tokens;
+    int tiles = 0;
+    for (int r = 0; r < s.W; ++r) {
+        tm.tile_start[r] = tiles;
+        tm.ntok[r] = a->num_tokens[r];
+        tiles += (a->num_tokens[r] + l.tile_tokens - 1) / l.tile_tokens;
+    }
+    tm.tile_start[s.W] = tiles;
+    tm.total_tiles = tiles;
+
+    ep::RouteArgs ra;
+    ra.idx = a->indices;
+    ra.tile_counts = ws_counts(p);
+    ra.M = s.M;
+    ra.k = s.k;
+    ra.Er = s.Er;
+    ra.E = (int32_t)s.E;
+    ra.tile_stride = s.tile_stride;
+
+    ep::ScanArgs sa;
+    sa.tile_counts = ws_counts(p);
+    sa.tile_base = ws_base(p);
+    sa.recv = a->recv_num_token;
+    sa.total_tiles = tiles;
+    sa.tile_stride = s.tile_stride;
+
+    ep::CopyArgs ca;
+    ca.x = static_cast<const uint8_t*>(a->x);
+    ca.idx = a->indices;
+    ca.w = a->weights;
+    ca.sc = static_cast<const uint32_t*>(a->scales);
+    ca.out_x = static_cast<uint8_t*>(a->out_x);
+    ca.out_idx = a->out_indices;
+    ca.out_w = a->out_weights;
+    ca.out_sc = static_cast<uint32_t*>(a->out_scales);
+    ca.tile_base = ws_base(p);
+    ca.src_pos = ws_src_pos(p);
+    ca.fwd = ws_fwd(p);
+    ca.row_vecs = s.row_bytes / 16;
+    ca.piece_vecs = (int32_t)((ca.row_vecs + l.dispatch_row_split - 1) / l.dispatch_row_split);
+    ca.scale_dwords = (int32_t)(s.scale_bytes / 4);
+    ca.M = s.M;
+    ca.k = s.k;
+    ca.Er = s.Er;
+    ca.E = (int32_t)s.E;
+    ca.P = s.P;
+    ca.WM = (int32_t)s.WM;
+    ca.tile_stride = s.tile_stride;
+    const int row_split = (int)((ca.row_vecs + ca.piece_vecs - 1) / ca.piece_vecs);
+
+    hipError_t e = timed(p, EP_KERNEL_ROUTE, stream, [&] { return ep::launch_route(ra, tm, stream); });
+    if (e == hipSuccess)
+        e = timed(p, EP_KERNEL_SCAN, stream, [&] { return ep::launch_scan(sa, s.W, stream); });
+    if (e == hipSuccess)
+        e = timed(p, EP_KERNEL_COPY, stream, [&] {
+            return ep::launch_copy(ca, tm, l.dispatch_waves, row_split, false, stream);
+        });
+    p->launched = true;
+    p->last_stream = stream;
+    if (e != hipSuccess) {
+        p->dispatched = false;
+        return fail(EP_ERR_HIP, "dispatch launch failed: %s", hipGetErrorString(e));
+    }
+    p->dispatched = true;
+    std::memcpy(p->last_ntok, a->num_tokens, sizeof(int32_t) * s.W);
+    return ok();
+}
+
+int ep_combine(ep_plan_t* p, const ep_combine_args_t* a, void* stream_ptr)
+{
+    if (!p)
+        return fail(EP_ERR_NULL, "plan is NULL");
+    if (!a)
+        return fail(EP_ERR_NULL, "args is NULL");
+    if (!a->y)
+        return fail(EP_ERR_NULL, "args.y is NULL");
+    if (!a->out)
+        return fail(EP_ERR_NULL, "args.out is NULL");
+    if (!aligned(a->y, kPtrAlign) || !aligned(a->out, kPtrAlign))
+        return fail(EP_ERR_ALIGN, "args.y / args.out are not 16-byte aligned");
+    if ((a->y_weights == nullptr) != (a->out_weights == nullptr))
+        return fail(EP_ERR_ARG, "args.y_weights and args.out_weights must both be set or both NULL");
+    if (a->y_weights && (!aligned(a->y_weights, 4) || !aligned(a->out_weights, 4)))
+        return fail(EP_ERR_ALIGN, "args.y_weights / args.out_weights are not 4-byte aligned");
+    if (!p->dispatched)
+        return fail(EP_ERR_STATE, "combine before any dispatch on this plan");
+    const Shape& s = p->s;
+    const ep_launch_t l = effective_launch(p, p->last_ntok);
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+
+    ep::TokenMap tk = {};
+    tk.W = s.W;
+    int total = 0;
+    for (int r = 0; r < s.W; ++r) {
+        tk.tok_start[r] = total;
+        total += p->last_ntok[r];
+    }
+    tk.tok_start[s.W] = total;
+    tk.total = total;
+
+    ep::CombineArgs ca;
+    ca.y = static_cast<const uint8_t*>(a->y);
+    ca.yw = a->y_weights;
+    ca.out = static_cast<uint8_t*>(a->out);
+    ca.out_w = a->out_weights;
+    ca.fwd = ws_fwd(p);
+    ca.row_vecs = (int32_t)(s.crow_bytes / 16);
+    ca.piece_vecs = (ca.row_vecs + l.combine_row_split - 1) / l.combine_row_split;
+    ca.M = s.M;
+    ca.k = s.k;
+    ca.P = s.P;
+    const int row_split = (ca.row_vecs + ca.piece_vecs - 1) / ca.piece_vecs;
+    const int dtype = p->cfg.combine_dtype == EP_BF16 ? 0 : 1;
+
+    const hipError_t e = timed(p, EP_KERNEL_COMBINE, stream, [&] {
+        return ep::launch_combine(ca, tk, dtype, l.combine_waves, row_split, stream);
+    });
+    p->launched = true;
+    p->last_stream = stream;
+    if (e != hipSuccess)
+        return fail(EP_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int ep_get_src_token_pos(const ep_plan_t* p, int32_t rank, const int32_t** dev_ptr)
+{
+    if (!p)
+        return fail(EP_ERR_NULL, "plan is NULL");
+    if (!dev_ptr)
+        return fail(EP_ERR_NULL, "dev_ptr is NULL");
+    if (rank < 0 || rank >= p->s.W)
+        return fail(EP_ERR_ARG, "rank = %d: must be in [0, %d)", rank, p->s.W);
+    *dev_ptr = ws_src_pos(p) + (int64_t)rank * p->s.WM;
+    return ok();
+}
+
+const char* ep_last_error(void) { return g_error.c_str(); }
+
+int ep_plan_set_launch(ep_plan_t* p, const ep_launch_t* l)
+{
+    if (!p)
+        return fail(EP_ERR_NULL, "plan is NULL");
+    if (!l) {
+        p->launch = ep_launch_t{};
+        return ok();
+    }
+    const int rc = check_launch(p, l);
+    if (rc != EP_OK)
+        return rc;
+    p->launch = *l;
+    return ok();
+}
+
+int ep_plan_get_launch(const ep_plan_t* p, const int32_t* num_tokens, ep_launch_t* out)
+{
+    if (!p)
+        return fail(EP_ERR_NULL, "plan is NULL");
+    if (!num_tokens)
+        return fail(EP_ERR_NULL, "num_tokens is NULL");
+    if (!out)
+        return fail(EP_ERR_NULL, "out is NULL");
+    for (int r = 0; r < p->s.W; ++r)
+        if (num_tokens[r] < 0 || num_tokens[r] > p->s.M)
+            return fail(EP_ERR_ARG, "num_tokens[%d] = %d: must be in [0, %d]", r, num_tokens[r],
+                        p->s.M);
+    *out = effective_launch(p, num_tokens);
+    return ok();
+}
+
+int ep_plan_set_timing(ep_plan_t* p, int enable)
+{
+    if (!p)
+        return fail(EP_ERR_NULL, "plan is NULL");
+    if (!enable) {
+        timers_destroy(p);
+        p->timing = false;
+        return ok();
+    }
+    timers_destroy(p);
+    for (Timer& t : p->timers) {
+        for (int i = 0; i < kTimerPool; ++i) {
+            hipEvent_t e0 = nullptr, e1 = nullptr;
+            if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+                if (e0)
+                    (void)hipEventDestroy(e0);
+                timers_destroy(p);
+                return fail(EP_ERR_HIP, "hipEventCreate failed");
+            }
+            t.start.push_back(e0);
+            t.stop.push_back(e1);
+        }
+    }
+    p->timing = true;
+    return ok();
+}
+
+int ep_plan_kernel_time(ep_plan_t* p, int kernel, int32_t* count, double* total_ms)
+{
+    if (!p)
+        return fail(EP_ERR_NULL, "plan is NULL");
+    if (kernel < 0 || kernel > 3)
+        return fail(EP_ERR_ARG, "kernel = %d: must be an EP_KERNEL_* value", kernel);
+    if (!count || !total_ms)
+        return fail(EP_ERR_NULL, "count / total_ms is NULL");
+    Timer& t = p->timers[kernel];
+    timer_drain(t);
+    *count = t.count;
+    *total_ms = t.total_ms;
+    return ok();
+}
+
+}  // extern "C"

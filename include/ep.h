@@ -1,0 +1,245 @@
+/*
+ * combine_route_amd: MoE expert-parallel dispatch and combine on one MI355X.
+ *
+ * C ABI of the GPU library (libcombine_route_amd.so). All W expert-parallel
+ * ranks are "virtual": their send and receive buffers live in the one GPU's
+ * HBM, side by side, and one call processes every rank at once.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [PR712]  "feat(ep): add opt-in gfx1201 EP2/EP4 support" (ROCm/mori PR 712),
+ *           "How the gfx1201 kernels work": the Dispatch and Combine bullets
+ *           define the two operations.
+ *  [GUIDE]  "MORI-EP User Guide": section 2 (EpDispatchCombineConfig fields),
+ *           section 3 (dispatch(), combine(), get_dispatch_src_token_pos()).
+ *  [L2]     "MORI (ROCm/mori) — L2 Distillation", section 9: results are views
+ *           of preallocated buffers that the next dispatch overwrites.
+ *  [PR703]  "refactor(EPv2): replace per-module __device__ staging with shared
+ *           buffer" (ROCm/mori PR 703): a caller-allocated buffer sized by one
+ *           exported function, and a host-side error naming the argument for a
+ *           missing or misaligned buffer (sections "Motivation", "Caller
+ *           contract"); receive capacity W * M rows per rank.
+ *  [PR726]  "gfx1250 EPv2: EP4 topk-9 geometry; selfFirst follows
+ *           MORI_EP_TOKOFF_EXT" (ROCm/mori PR 726): a token has at most
+ *           min(W, k) destination rows.
+ *
+ * Notation: W = world_size, M = max_num_inp_token_per_rank, k =
+ * num_experts_per_token, Er = num_experts_per_rank, E = W * Er, H =
+ * hidden_dim, S = scale_dim, WM = W * M, P = min(W, k). T_r = tokens present
+ * on rank r (num_tokens[r] <= M).
+ *
+ * Semantics (readings of the pages where they are silent are marked R):
+ *  - Expert e lives on rank e / Er (R: contiguous blocks, [GUIDE] section 2's
+ *    "256 experts / 8 GPUs"). An id outside [0, E) selects no rank (R).
+ *  - A token's destination ranks D are its experts' ranks without repeats, in
+ *    the order each first appears in its top-k row ([PR712] Dispatch).
+ *  - Rank d receives one row per (token, d in D). Its rows are ordered by
+ *    (source rank, source token) (R: a deterministic counting-sort layout
+ *    replaces the pages' atomic slot reservation). At most WM rows ([PR703]).
+ *  - Each received row carries the token's payload row, its whole top-k id
+ *    and weight rows verbatim, its scale row, and its source
+ *    src_rank * WM + src_token ([GUIDE] get_dispatch_src_token_pos()).
+ *  - Combine returns token (r,t) as the FP32 sum of its rows' expert outputs,
+ *    in D order, starting from the first, rounded to nearest even into
+ *    bf16/fp16 ([PR712] Combine). No routing weight is applied; optional
+ *    FP32 weights are summed the same way without a cast. A token with no
+ *    rank combines to +0 (R).
+ *  All outputs are bit-for-bit deterministic: no atomic operation decides a
+ *  position or an order.
+ *
+ * Errors: every call returns EP_OK (0) or a negative EP_ERR_* code, and
+ * ep_last_error() then names the argument at fault. Every precondition is
+ * checked on the host before anything is enqueued: on error nothing is
+ * enqueued and no output is touched.
+ */
+#ifndef COMBINE_ROUTE_AMD_EP_H
+#define COMBINE_ROUTE_AMD_EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. Dispatch payload: any of the three (the library copies
+ * bytes; EP_FP8_E4M3 is one byte an element). Combine: EP_BF16 or EP_FP16. */
+enum { EP_BF16 = 0, EP_FP16 = 1, EP_FP8_E4M3 = 2 };
+
+enum {
+    EP_OK = 0,
+    EP_ERR_NULL = -1,  /* a required pointer is NULL                          */
+    EP_ERR_ARG = -2,   /* a value out of range or inconsistent                */
+    EP_ERR_ALIGN = -3, /* a pointer is not aligned as required                */
+    EP_ERR_SIZE = -4,  /* a buffer is too small, or a size overflows          */
+    EP_ERR_STATE = -5, /* call order: combine before any dispatch on the plan */
+    EP_ERR_HIP = -6    /* the HIP runtime reported an error for a launch      */
+};
+
+/* Static configuration, after [GUIDE] section 2's EpDispatchCombineConfig
+ * (rank, launch, kernel-type and RDMA fields dropped: one call covers all
+ * ranks of one GPU). Valid when:
+ *   1 <= world_size <= 64; 1 <= max_num_inp_token_per_rank;
+ *   W * W * M <= 2^31 - 1 (src_pos and forward-map entries are int32);
+ *   1 <= num_experts_per_token <= 64; 1 <= num_experts_per_rank and
+ *   W * num_experts_per_rank <= 2^31 - 1;
+ *   hidden_dim >= 1, hidden_dim * elem(dispatch_dtype) % 16 == 0 and
+ *   hidden_dim * 2 % 16 == 0 (rows move in 16-byte pieces);
+ *   scale_dim >= 0; if scale_dim > 0: scale_type_size in {1, 2, 4, 8} and
+ *   scale_dim * scale_type_size % 4 == 0;
+ *   dispatch_dtype in {EP_BF16, EP_FP16, EP_FP8_E4M3};
+ *   combine_dtype in {EP_BF16, EP_FP16}. */
+typedef struct ep_config {
+    int32_t world_size;
+    int32_t hidden_dim;
+    int32_t scale_dim;
+    int32_t scale_type_size;
+    int32_t max_num_inp_token_per_rank;
+    int32_t num_experts_per_rank;
+    int32_t num_experts_per_token;
+    int32_t dispatch_dtype;
+    int32_t combine_dtype;
+} ep_config_t;
+
+typedef struct ep_plan ep_plan_t;
+
+/* Bytes of device workspace a plan needs for cfg: routing counts and bases,
+ * src_pos [W][WM] int32, the forward map [W][M][P] int32 (the routing handle
+ * combine replays). Returns 0 if cfg is NULL or invalid (ep_last_error() says
+ * why). [PR703]: one exported function sizes the caller's buffer. */
+size_t ep_workspace_bytes(const ep_config_t *cfg);
+
+/* Create a plan. Host-only: validates, records pointers, launches nothing and
+ * makes no HIP call. workspace: caller-owned device memory of at least
+ * ep_workspace_bytes(cfg) bytes, 256-byte aligned; the plan borrows it and
+ * the caller keeps it alive and unused by others until ep_plan_destroy. Its
+ * contents need no initialisation.
+ * Errors: EP_ERR_NULL (cfg, workspace or out is NULL), EP_ERR_ARG (cfg
+ * invalid), EP_ERR_ALIGN (workspace not 256-byte aligned), EP_ERR_SIZE
+ * (workspace_bytes too small). On error *out is left unchanged. */
+int ep_plan_create(const ep_config_t *cfg, void *workspace, size_t workspace_bytes,
+                   ep_plan_t **out);
+
+/* Destroy a plan: waits for the last stream the plan launched on, then frees
+ * the plan's host state. The caller frees the workspace afterwards. NULL is a
+ * no-op returning EP_OK. EP_ERR_HIP if that wait fails (the plan is freed
+ * anyway). */
+int ep_plan_destroy(ep_plan_t *plan);
+
+/* Dispatch arguments. Device pointers are caller-owned, 16-byte aligned, and
+ * laid out rank-major with the rank stride fixed by M (not by T_r):
+ *   num_tokens     HOST int32 [W]: T_r, 0 <= T_r <= M.
+ *   x              [W][M][H] dispatch_dtype: rows t < T_r are read.
+ *   indices        [W][M][k] int32 expert ids.
+ *   weights        [W][M][k] float, or NULL (then out_weights must be NULL).
+ *   scales         [W][M][S] elements of scale_type_size bytes; NULL iff S == 0.
+ *   out_x          [W][WM][H] dispatch_dtype.
+ *   out_indices    [W][WM][k] int32.
+ *   out_weights    [W][WM][k] float, NULL iff weights is NULL.
+ *   out_scales     [W][WM][S], NULL iff S == 0.
+ *   recv_num_token DEVICE int32 [W]: rows each rank received.
+ * Rows s >= recv_num_token[d] of the outputs, and input rows t >= T_r, are
+ * neither written nor read. ([GUIDE] section 3, dispatch(): the five outputs
+ * and their shapes.) */
+typedef struct ep_dispatch_args {
+    const int32_t *num_tokens;
+    const void *x;
+    const int32_t *indices;
+    const float *weights;
+    const void *scales;
+    void *out_x;
+    int32_t *out_indices;
+    float *out_weights;
+    void *out_scales;
+    int32_t *recv_num_token;
+} ep_dispatch_args_t;
+
+/* Dispatch every rank's tokens ([PR712] Dispatch). Asynchronous on stream (a
+ * hipStream_t; NULL = the default stream); no host synchronisation; no
+ * allocation; capturable in a HIP graph. Overwrites the plan's routing handle
+ * (src_pos and forward map in the workspace): the results of the previous
+ * dispatch on this plan are invalid once this call is enqueued ([L2] section
+ * 9). The outputs must not overlap the inputs or the workspace.
+ * Errors: EP_ERR_NULL, EP_ERR_ARG (T_r out of range, NULL/non-NULL pairing),
+ * EP_ERR_ALIGN, EP_ERR_HIP (a launch failed; outputs undefined). */
+int ep_dispatch(ep_plan_t *plan, const ep_dispatch_args_t *args, void *stream);
+
+/* Combine arguments (device pointers, 16-byte aligned):
+ *   y            [W][WM][H] combine_dtype: expert output for each received
+ *                row (rows s < recv_num_token[d] are read). May be the
+ *                dispatch's out_x when the types match.
+ *   y_weights    [W][WM][k] float, or NULL (then out_weights must be NULL).
+ *   out          [W][M][H] combine_dtype: rows t < T_r of the last dispatch
+ *                are written, others untouched. Must not overlap y.
+ *   out_weights  [W][M][k] float, NULL iff y_weights is NULL.
+ * ([GUIDE] section 3, combine(): combine_output and combine_weights.) */
+typedef struct ep_combine_args {
+    const void *y;
+    const float *y_weights;
+    void *out;
+    float *out_weights;
+} ep_combine_args_t;
+
+/* Combine ([PR712] Combine) using the routing handle of the last ep_dispatch
+ * enqueued on this plan. Asynchronous on stream; no allocation; capturable.
+ * May be called any number of times per dispatch (each call recomputes the
+ * same sums); no reset between iterations is needed. Two routings in flight
+ * need two plans.
+ * Errors: EP_ERR_NULL, EP_ERR_ARG (NULL/non-NULL pairing), EP_ERR_ALIGN,
+ * EP_ERR_STATE (no dispatch yet on this plan), EP_ERR_HIP. */
+int ep_combine(ep_plan_t *plan, const ep_combine_args_t *args, void *stream);
+
+/* Reverse map of rank `rank` ([GUIDE] section 3, get_dispatch_src_token_pos():
+ * src_rank * (world_size * max_num_inp_token_per_rank) + src_token_id).
+ * Sets *dev_ptr to a device pointer into the workspace, int32 [WM], of which
+ * [0, recv_num_token[rank]) are valid once the last dispatch has completed on
+ * its stream; valid until the next ep_dispatch on the plan is enqueued.
+ * Makes no HIP call. Errors: EP_ERR_NULL, EP_ERR_ARG (rank not in [0, W)). */
+int ep_get_src_token_pos(const ep_plan_t *plan, int32_t rank, const int32_t **dev_ptr);
+
+/* Message for the last error on the calling thread ("" if none). The string
+ * stays valid until the next library call on this thread. */
+const char *ep_last_error(void);
+
+/* Launch geometry, after the block_num / warp_per_block overrides of
+ * [GUIDE] section 3's dispatch() and combine(). A field <= 0 means "choose
+ * automatically" (the default). Limits:
+ *   tile_tokens          tokens per routing tile: 16, 32 or 64.
+ *   dispatch_waves       wavefronts per dispatch-copy block: 1..16.
+ *   dispatch_row_split   blocks sharing one tile's rows, each a contiguous
+ *                        piece of the row: 1..row_bytes/16.
+ *   combine_waves        wavefronts per combine block (a token each): 1..16.
+ *   combine_row_split    pieces a combined row is split into: 1..H/8.
+ * Geometry never changes results. */
+typedef struct ep_launch {
+    int32_t tile_tokens;
+    int32_t dispatch_waves;
+    int32_t dispatch_row_split;
+    int32_t combine_waves;
+    int32_t combine_row_split;
+} ep_launch_t;
+
+/* Override (launch != NULL) or reset to automatic (launch == NULL) the plan's
+ * geometry. Host-only. EP_ERR_ARG if a field is out of its limits. */
+int ep_plan_set_launch(ep_plan_t *plan, const ep_launch_t *launch);
+
+/* The geometry a call with these token counts would use (host [W] int32).
+ * Host-only. */
+int ep_plan_get_launch(const ep_plan_t *plan, const int32_t *num_tokens, ep_launch_t *out);
+
+/* Per-kernel timing with HIP events, for measurement. While enabled, every
+ * kernel the plan launches is bracketed by two events recorded on its
+ * stream; ep_plan_kernel_time waits for the recorded events and returns, for
+ * one kernel, how many launches were timed and their total milliseconds since
+ * enabling. Kernels: EP_KERNEL_ROUTE (per-tile rank counts), EP_KERNEL_SCAN
+ * (receive layout), EP_KERNEL_COPY (dispatch row and metadata copy),
+ * EP_KERNEL_COMBINE (gather-reduce). Enabling creates the events (no device
+ * memory); disabling destroys them. Not for use under graph capture. */
+enum { EP_KERNEL_ROUTE = 0, EP_KERNEL_SCAN = 1, EP_KERNEL_COPY = 2, EP_KERNEL_COMBINE = 3 };
+int ep_plan_set_timing(ep_plan_t *plan, int enable);
+int ep_plan_kernel_time(ep_plan_t *plan, int kernel, int32_t *count, double *total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COMBINE_ROUTE_AMD_EP_H */

@@ -1,0 +1,251 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is ever launched).
+
+The library must load, export every function include/ep.h declares, size the
+workspace from one function, and reject every bad argument on the host with
+a message naming it before anything is enqueued (the staging refactor's
+caller contract: "refactor(EPv2): replace per-module __device__ staging with
+shared buffer", Caller contract). Every call below fails validation before a
+launch, so these tests are safe on a machine with a GPU too; pointers are
+fake addresses that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import combine_route_amd as cra
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE_WS = 0x7F0000000000          # 256-byte aligned, never dereferenced
+FAKE = 0x7F1000000000             # 16-byte aligned device-looking address
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(cra.LIB_PATH):
+        import combine_route_amd.build as b
+        b.build()
+    return cra.load()
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "ep.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ep_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    assert len(names) == 11
+    assert sorted(cra.EXPORTED) == names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def wl_config(wl):
+    return cra.make_config(wl.world_size, wl.hidden, wl.max_tokens, wl.experts_per_rank,
+                           wl.topk, wl.dispatch_dtype, wl.combine_dtype,
+                           scale_dim=wl.scale_dim, scale_type_size=4)
+
+
+def expected_workspace(W, M, k):
+    """Layout: tile counts and tile bases (W x W*ceil(M/16) int32 each),
+    src_pos (W x W*M int32), forward map (W x M x min(W,k) int32), each
+    rounded up to 256 bytes."""
+    up = lambda v: (v + 255) // 256 * 256
+    tiles = W * ((M + 15) // 16)
+    return 2 * up(4 * W * tiles) + up(4 * W * W * M) + up(4 * W * M * min(W, k))
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_workspace_bytes_golden(lib, name):
+    wl = workloads.WORKLOADS[name]
+    cfg = wl_config(wl)
+    assert cra.ep_workspace_bytes(cfg) == expected_workspace(wl.world_size, wl.max_tokens, wl.topk)
+
+
+def test_workspace_bytes_headline_value(lib):
+    # 8 ranks x 4096 tokens, top-8: 2 x 32 KiB tiles + 1 MiB src_pos + 1 MiB fwd
+    cfg = wl_config(workloads.WORKLOADS[workloads.HEADLINE])
+    assert cra.ep_workspace_bytes(cfg) == 2 * 8 * 8 * 256 * 4 + 8 * 8 * 4096 * 4 + 8 * 4096 * 8 * 4
+
+
+BAD_CONFIGS = [
+    (dict(world_size=0), "world_size"), (dict(world_size=65), "world_size"),
+    (dict(max_num_inp_token_per_rank=0), "max_num_inp_token_per_rank"),
+    (dict(num_experts_per_token=0), "num_experts_per_token"),
+    (dict(num_experts_per_token=65), "num_experts_per_token"),
+    (dict(num_experts_per_rank=0), "num_experts_per_rank"),
+    (dict(hidden_dim=0), "hidden_dim"), (dict(hidden_dim=260), "hidden_dim"),
+    (dict(dispatch_dtype=7), "dispatch_dtype"), (dict(combine_dtype=2), "combine_dtype"),
+    (dict(scale_dim=-1), "scale_dim"), (dict(scale_dim=3, scale_type_size=3), "scale_type_size"),
+    (dict(scale_dim=3, scale_type_size=2), "scale_dim * cfg.scale_type_size"),
+    (dict(world_size=64, max_num_inp_token_per_rank=600000), "2^31"),
+]
+
+
+@pytest.mark.parametrize("change,word", BAD_CONFIGS)
+def test_bad_config_rejected(lib, change, word):
+    base = dict(world_size=8, hidden_dim=7168, scale_dim=0, scale_type_size=0,
+                max_num_inp_token_per_rank=4096, num_experts_per_rank=32,
+                num_experts_per_token=8, dispatch_dtype=0, combine_dtype=0)
+    base.update(change)
+    cfg = cra.EpConfig(**base)
+    assert lib.ep_workspace_bytes(ctypes.byref(cfg)) == 0
+    assert word in cra.ep_last_error()
+    out = ctypes.c_void_p(0)
+    rc = lib.ep_plan_create(ctypes.byref(cfg), FAKE_WS, 1 << 40, ctypes.byref(out))
+    assert rc in (cra.EP_ERR_ARG, cra.EP_ERR_SIZE) and out.value is None
+
+
+def test_fp8_hidden_must_fill_16_bytes(lib):
+    cfg = cra.make_config(8, 7160, 128, 32, 8, "fp8", "bf16", scale_dim=56)
+    assert lib.ep_workspace_bytes(ctypes.byref(cfg)) == 0
+
+
+def make_plan(lib, cfg, ws=FAKE_WS, nbytes=None):
+    out = ctypes.c_void_p(0)
+    n = cra.ep_workspace_bytes(cfg) if nbytes is None else nbytes
+    rc = lib.ep_plan_create(ctypes.byref(cfg), ws, n, ctypes.byref(out))
+    return rc, out.value
+
+
+def test_plan_create_errors(lib):
+    cfg = cra.make_config(4, 4096, 256, 64, 8)
+    need = cra.ep_workspace_bytes(cfg)
+    out = ctypes.c_void_p(0)
+    assert lib.ep_plan_create(None, FAKE_WS, need, ctypes.byref(out)) == cra.EP_ERR_NULL
+    assert lib.ep_plan_create(ctypes.byref(cfg), None, need, ctypes.byref(out)) == cra.EP_ERR_NULL
+    assert "workspace" in cra.ep_last_error()
+    assert lib.ep_plan_create(ctypes.byref(cfg), FAKE_WS, need, None) == cra.EP_ERR_NULL
+    assert make_plan(lib, cfg, ws=FAKE_WS + 16)[0] == cra.EP_ERR_ALIGN
+    assert "256" in cra.ep_last_error()
+    assert make_plan(lib, cfg, nbytes=need - 1)[0] == cra.EP_ERR_SIZE
+    assert str(need) in cra.ep_last_error()
+    rc, plan = make_plan(lib, cfg)
+    assert rc == cra.EP_OK and plan
+    assert lib.ep_plan_destroy(plan) == cra.EP_OK
+    assert lib.ep_plan_destroy(None) == cra.EP_OK
+
+
+def test_src_token_pos_pointer_and_rank_check(lib):
+    W, M, k = 4, 256, 8
+    cfg = cra.make_config(W, 4096, M, 64, k)
+    rc, plan = make_plan(lib, cfg)
+    assert rc == 0
+    p = ctypes.c_void_p()
+    up = lambda v: (v + 255) // 256 * 256
+    off = 2 * up(4 * W * W * ((M + 15) // 16))
+    for r in range(W):
+        assert lib.ep_get_src_token_pos(plan, r, ctypes.byref(p)) == 0
+        assert p.value == FAKE_WS + off + r * W * M * 4
+    assert lib.ep_get_src_token_pos(plan, W, ctypes.byref(p)) == cra.EP_ERR_ARG
+    assert lib.ep_get_src_token_pos(plan, -1, ctypes.byref(p)) == cra.EP_ERR_ARG
+    assert lib.ep_get_src_token_pos(plan, 0, None) == cra.EP_ERR_NULL
+    lib.ep_plan_destroy(plan)
+
+
+def dispatch_args(W, **over):
+    nt = (ctypes.c_int32 * W)(*([4] * W))
+    a = dict(num_tokens=ctypes.cast(nt, ctypes.c_void_p).value, x=FAKE, indices=FAKE + 0x1000,
+             weights=None, scales=None, out_x=FAKE + 0x2000, out_indices=FAKE + 0x3000,
+             out_weights=None, out_scales=None, recv_num_token=FAKE + 0x4000)
+    a.update(over)
+    return cra.EpDispatchArgs(**a), nt
+
+
+@pytest.mark.parametrize("over,code,word", [
+    (dict(num_tokens=None), cra.EP_ERR_NULL, "num_tokens"),
+    (dict(x=None), cra.EP_ERR_NULL, "args.x"),
+    (dict(indices=None), cra.EP_ERR_NULL, "args.indices"),
+    (dict(out_x=None), cra.EP_ERR_NULL, "args.out_x"),
+    (dict(out_indices=None), cra.EP_ERR_NULL, "args.out_indices"),
+    (dict(recv_num_token=None), cra.EP_ERR_NULL, "recv_num_token"),
+    (dict(x=FAKE + 8), cra.EP_ERR_ALIGN, "args.x"),
+    (dict(out_x=FAKE + 4), cra.EP_ERR_ALIGN, "args.out_x"),
+    (dict(weights=FAKE + 0x5000), cra.EP_ERR_ARG, "weights"),
+    (dict(out_weights=FAKE + 0x5000), cra.EP_ERR_ARG, "weights"),
+    (dict(scales=FAKE + 0x6000, out_scales=FAKE + 0x7000), cra.EP_ERR_ARG, "scale_dim = 0"),
+])
+def test_dispatch_rejects_before_launch(lib, over, code, word):
+    cfg = cra.make_config(2, 256, 16, 4, 2)
+    rc, plan = make_plan(lib, cfg)
+    a, keep = dispatch_args(2, **over)
+    assert lib.ep_dispatch(plan, ctypes.byref(a), None) == code
+    assert word in cra.ep_last_error()
+    lib.ep_plan_destroy(plan)
+
+
+def test_dispatch_rejects_token_counts(lib):
+    cfg = cra.make_config(2, 256, 16, 4, 2)
+    rc, plan = make_plan(lib, cfg)
+    for bad in ([17, 0], [0, -1]):
+        nt = (ctypes.c_int32 * 2)(*bad)
+        a, _ = dispatch_args(2, num_tokens=ctypes.cast(nt, ctypes.c_void_p).value, x=None)
+        # T_r is checked before any pointer
+        assert lib.ep_dispatch(plan, ctypes.byref(a), None) == cra.EP_ERR_ARG
+        assert "num_tokens" in cra.ep_last_error()
+    lib.ep_plan_destroy(plan)
+
+
+def test_dispatch_requires_scales_when_configured(lib):
+    cfg = cra.make_config(8, 7168, 128, 32, 8, "fp8", "bf16", scale_dim=56)
+    rc, plan = make_plan(lib, cfg)
+    a, _ = dispatch_args(8, scales=FAKE + 0x6000)
+    assert lib.ep_dispatch(plan, ctypes.byref(a), None) == cra.EP_ERR_NULL
+    assert "scales" in cra.ep_last_error()
+    a, _ = dispatch_args(8, scales=FAKE + 0x6004, out_scales=FAKE + 0x7000)
+    assert lib.ep_dispatch(plan, ctypes.byref(a), None) == cra.EP_ERR_ALIGN
+    lib.ep_plan_destroy(plan)
+
+
+def test_combine_errors_and_state(lib):
+    cfg = cra.make_config(2, 256, 16, 4, 2)
+    rc, plan = make_plan(lib, cfg)
+    ok = dict(y=FAKE, y_weights=None, out=FAKE + 0x1000, out_weights=None)
+    cases = [(dict(y=None), cra.EP_ERR_NULL, "args.y"), (dict(out=None), cra.EP_ERR_NULL, "args.out"),
+             (dict(y=FAKE + 2), cra.EP_ERR_ALIGN, "aligned"),
+             (dict(y_weights=FAKE + 0x2000), cra.EP_ERR_ARG, "weights"),
+             ({}, cra.EP_ERR_STATE, "before any dispatch")]
+    for over, code, word in cases:
+        a = cra.EpCombineArgs(**{**ok, **over})
+        assert lib.ep_combine(plan, ctypes.byref(a), None) == code
+        assert word in cra.ep_last_error()
+    assert lib.ep_combine(None, ctypes.byref(cra.EpCombineArgs(**ok)), None) == cra.EP_ERR_NULL
+    lib.ep_plan_destroy(plan)
+
+
+def test_launch_override_limits_and_auto_geometry(lib):
+    wl = workloads.WORKLOADS[workloads.HEADLINE]
+    cfg = wl_config(wl)
+    rc, plan = make_plan(lib, cfg)
+    auto = cra.ep_plan_get_launch(plan, [4096] * 8)
+    assert auto["tile_tokens"] in (16, 32, 64)
+    assert 1 <= auto["dispatch_row_split"] <= 7168 * 2 // 16
+    for bad in (dict(tile_tokens=8), dict(dispatch_waves=17), dict(combine_waves=17),
+                dict(dispatch_row_split=7168 * 2 // 16 + 1), dict(combine_row_split=897)):
+        with pytest.raises(cra.EpError):
+            cra.ep_plan_set_launch(plan, bad)
+    cra.ep_plan_set_launch(plan, dict(tile_tokens=32, dispatch_waves=2))
+    got = cra.ep_plan_get_launch(plan, [4096] * 8)
+    assert got["tile_tokens"] == 32 and got["dispatch_waves"] == 2
+    cra.ep_plan_set_launch(plan, None)
+    assert cra.ep_plan_get_launch(plan, [4096] * 8) == auto
+    small = cra.ep_plan_get_launch(plan, [1] + [0] * 7)
+    assert small["tile_tokens"] == 16
+    with pytest.raises(cra.EpError):
+        cra.ep_plan_get_launch(plan, [4097] + [0] * 7)
+    lib.ep_plan_destroy(plan)
+
+
+def test_kernel_time_argument_checks(lib):
+    cfg = cra.make_config(2, 256, 16, 4, 2)
+    rc, plan = make_plan(lib, cfg)
+    c, ms = ctypes.c_int32(), ctypes.c_double()
+    assert lib.ep_plan_kernel_time(plan, 4, ctypes.byref(c), ctypes.byref(ms)) == cra.EP_ERR_ARG
+    assert lib.ep_plan_kernel_time(plan, 0, ctypes.byref(c), ctypes.byref(ms)) == 0
+    assert c.value == 0 and ms.value == 0.0
+    lib.ep_plan_destroy(plan)
