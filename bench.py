@@ -2,17 +2,26 @@
 
 One step = one ep_dispatch + one ep_combine over all W virtual ranks of the
 workload (default: 8 ranks x 4096 tokens, hidden 7168 bf16, 256 experts,
-top-8, FP32 routing weights dispatched and summed back; identity experts, so
-the combine reads the dispatch's output rows in place). Inputs are generated
-on the host from the seeded workload and are resident in HBM before the
-timed region. Before timing, one call is checked bit for bit against the CPU
-oracle, which is also timed on the host as the CPU baseline.
+top-8, FP32 routing weights dispatched and summed back). With identity
+experts the combine reads the dispatch's output rows in place; otherwise
+the expert output is a seeded random bf16/fp16 buffer, written before the
+timed region. Inputs are resident in HBM before the timed region. Before
+timing, one call is checked bit for bit against the CPU oracle, which is
+also timed on the host as the CPU baseline.
 
-Prints one JSON line. `value` is payload HBM throughput (GB/s): algorithmic
-payload bytes of one call (dispatch reads N rows and writes R rows, combine
-reads R rows and writes N rows) over the time of one call.
+Prints one JSON line. `value` is payload HBM throughput in GB/s: the
+algorithmic payload bytes of one call (dispatch reads N rows and writes R
+rows, combine reads R rows and writes N rows; R = rows received) over the
+time of one call.
+
+Other modes (measurement tooling, no JSON line of the workload):
+  --copy-calibration MIB   time a plain device-to-device copy of MIB MiB
+  --summarize-stats CSV OUT.md CMD...          rocprofv3 --stats table
+  --summarize-counters FETCH WRITE CAL_FETCH CAL_WRITE CAL_MIB WORKLOAD
+                           per-launch HBM bytes of the two large kernels
 """
 import argparse
+import csv
 import hashlib
 import json
 import os
@@ -26,6 +35,7 @@ PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
 METRIC = "dispatch+combine µs/call and payload HBM GB/s (% of peak), EP8 H=7168 k=8"
 KERNEL_SOURCES = [os.path.join(ROOT, "combine_route_amd", "csrc", f)
                   for f in ("ep_kernels.hip", "ep_kernels.h", "ep_plan.cpp")]
+KERNELS = {"copy": "ep_copy_kernel", "combine": "ep_combine_kernel"}
 
 
 def kernel_source_hash() -> str:
@@ -36,10 +46,14 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def counters_path(kernel: str, workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.txt")
+
+
 def read_traffic(workload: str, kernel: str):
     """Per-launch HBM bytes measured by rocprofv3 counters, from the summary
     under profiles/, if it was taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.txt")
+    path = counters_path(kernel, workload)
     if not os.path.exists(path):
         return None
     vals = {}
@@ -54,6 +68,23 @@ def read_traffic(workload: str, kernel: str):
         return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def algorithmic_bytes(wl, ntok, recv_total):
+    """Bytes one call must move (each byte read or written once)."""
+    N, R = int(sum(ntok)), int(recv_total)
+    k, P = wl.topk, min(wl.world_size, wl.topk)
+    row = wl.hidden * (1 if wl.dispatch_dtype == "fp8" else 2)
+    crow = wl.hidden * 2
+    sb = wl.scale_dim * 4
+    payload = N * (row + sb) + R * (row + sb) + R * crow + N * crow
+    # dispatch copy: payload, scale, id and weight rows of N tokens read; of R
+    # rows written, plus src_pos per row and the forward map per token
+    copy = N * (row + sb + 8 * k) + R * (row + sb + 8 * k + 4) + N * P * 4
+    # combine: R expert-output rows and their weights read, N rows and weight
+    # rows written, forward map read
+    combine = R * (crow + 4 * k) + N * (crow + 4 * k) + N * P * 4
+    return payload, {"copy": copy, "combine": combine}
 
 
 def copy_ceiling(torch, mib, steps, warmup):
@@ -77,41 +108,86 @@ def copy_ceiling(torch, mib, steps, warmup):
                       "GB/s": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
-    ap.add_argument("--no-cpu-baseline", action="store_true",
-                    help="skip the oracle (CPU baseline and the bit-exact check)")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="instead of the workload, time a plain device-to-device copy of MIB "
-                         "MiB (the box's copy ceiling, and the known-size kernel that scales "
-                         "rocprofv3's byte counters)")
-    args = ap.parse_args()
+def summarize_stats(csv_path, out_md, command):
+    rows = list(csv.DictReader(open(csv_path)))
+    out = ["# rocprofv3 kernel statistics", "",
+           f"Kernel sources sha256[:16]: {kernel_source_hash()}", "",
+           "Command (from the repository root):", "", "    " + command, "",
+           "| kernel | calls | average us | min us | max us | share |",
+           "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].replace("(anonymous namespace)::", "")
+        out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                   f"{float(r['Percentage']):.2f}% |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
 
-    if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs all virtual "
-              "expert-parallel ranks on one GPU; only --gpus 1 is measured.", file=sys.stderr)
-        sys.exit(2)
 
+def _counter_means(path):
+    sums, counts = {}, {}
+    for r in csv.DictReader(open(path)):
+        key = (r["Kernel_Name"], r["Counter_Name"])
+        sums[key] = sums.get(key, 0.0) + float(r["Counter_Value"])
+        counts[key] = counts.get(key, 0) + 1
+    return {k: sums[k] / counts[k] for k in sums}
+
+
+def summarize_counters(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, cal_mib, workload):
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the two large kernels,
+    each scaled by what the same counter reads for the calibration copy
+    (cal_mib MiB read and cal_mib MiB written per launch)."""
+    import workloads
+
+    fetch, write = _counter_means(fetch_csv), _counter_means(write_csv)
+    cal_f, cal_w = _counter_means(cal_fetch_csv), _counter_means(cal_write_csv)
+    cal_bytes = cal_mib << 20
+    # the calibration copy is the kernel that moved the most bytes in its run
+    f_cal = max(v for (k, c), v in cal_f.items() if c == "FETCH_SIZE") * 1024
+    w_cal = max(v for (k, c), v in cal_w.items() if c == "WRITE_SIZE") * 1024
+    f_scale, w_scale = cal_bytes / f_cal, cal_bytes / w_cal
+    wl = workloads.WORKLOADS[workload]
+    for short, kname in KERNELS.items():
+        fk = [v for (k, c), v in fetch.items() if kname in k]
+        wk = [v for (k, c), v in write.items() if kname in k]
+        if not fk or not wk:
+            continue
+        rd = fk[0] * 1024 * f_scale
+        wr = wk[0] * 1024 * w_scale
+        lines = [f"# HBM traffic per launch of {kname}, workload {workload}",
+                 "# rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE, one run each;",
+                 f"# each scaled by the same counter on a plain {cal_mib} MiB device copy",
+                 "# Commands (from the repository root):",
+                 "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- "
+                 "python -u bench.py --no-cpu-baseline --steps 5 --warmup 2",
+                 "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- "
+                 "python -u bench.py --no-cpu-baseline --steps 5 --warmup 2",
+                 f"#   rocprofv3 --pmc FETCH_SIZE ... -- python -u bench.py --copy-calibration {cal_mib} --steps 3 --warmup 1",
+                 f"#   rocprofv3 --pmc WRITE_SIZE ... -- python -u bench.py --copy-calibration {cal_mib} --steps 3 --warmup 1",
+                 f"#   python bench.py --summarize-counters <the four counter_collection.csv> {cal_mib} {workload}",
+                 f"kernel_source_sha256_16: {kernel_source_hash()}",
+                 f"fetch_size_kib_raw: {fk[0]:.1f}",
+                 f"write_size_kib_raw: {wk[0]:.1f}",
+                 f"fetch_scale: {f_scale:.4f}",
+                 f"write_scale: {w_scale:.4f}",
+                 f"hbm_read_bytes_per_launch: {rd:.0f}",
+                 f"hbm_write_bytes_per_launch: {wr:.0f}",
+                 f"hbm_bytes_per_launch: {rd + wr:.0f}"]
+        with open(counters_path(kname, workload), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+
+
+def run(args):
     import numpy as np
     import torch
-
-    if args.copy_calibration:
-        copy_ceiling(torch, args.copy_calibration, args.steps, args.warmup)
-        return
 
     import combine_route_amd as cra
     import workloads
 
     wl = workloads.WORKLOADS[args.workload or workloads.HEADLINE]
     W, M, k, H = wl.world_size, wl.max_tokens, wl.topk, wl.hidden
-    if wl.expert != "identity" or wl.dispatch_dtype != wl.combine_dtype:
-        print("bench.py times identity experts (combine reads the dispatched rows); "
-              f"{wl.name} needs a different expert", file=sys.stderr)
-        sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -127,25 +203,28 @@ def main():
     w = inp["w"].to(dev)
     sc = None if inp["scales"] is None else inp["scales"].to(dev)
     ntok = inp["ntok"]
+    cdt = workloads.TORCH_DTYPE[wl.combine_dtype]
+    in_place = wl.expert == "identity" and wl.dispatch_dtype == wl.combine_dtype
+    if in_place:
+        y_host = None
+        y = op.out_x
+    else:
+        g = torch.Generator().manual_seed(workloads.BASE_SEED + 77)
+        y_host = torch.randn((W, W * M, H), generator=g).to(cdt)
+        y = y_host.to(dev)
     stream = torch.cuda.current_stream()
 
     def step():
         op.dispatch(ntok, x, idx, w, sc, stream=stream)
-        op.combine(op.out_x, op.out_weights, stream=stream)
+        op.combine(y, op.out_weights, stream=stream)
 
     # -- correctness first, and the CPU baseline -----------------------------
     step()
     torch.cuda.synchronize()
     recv = op.recv_num_token.cpu().numpy()
-    R = int(recv.sum())
-    N = int(sum(ntok))
+    payload_bytes, kernel_bytes = algorithmic_bytes(wl, ntok, recv.sum())
     check = "skipped"
     cpu_baseline = None
-    row = H * (1 if wl.dispatch_dtype == "fp8" else 2)
-    crow = H * 2
-    sb = wl.scale_dim * 4
-    P = min(W, k)
-    payload_bytes = N * (row + sb) + R * (row + sb) + R * crow + N * crow
     if not args.no_cpu_baseline:
         import oracle
 
@@ -154,14 +233,15 @@ def main():
         t = time.perf_counter()
         ref = oracle.dispatch(W, M, k, wl.experts_per_rank, ntok, xb, inp["idx"].numpy(),
                               inp["w"].numpy(), scn)
-        y = ref["out_x"].view(np.uint16).reshape(W, W * M, H)
+        y16 = (ref["out_x"].view(np.uint16).reshape(W, W * M, H) if in_place
+               else y_host.view(torch.int16).numpy().view(np.uint16))
         ro, rw = oracle.combine(W, M, k, H, oracle.BF16 if wl.combine_dtype == "bf16"
-                                else oracle.FP16, ntok, ref["fwd"], y, ref["out_w"])
+                                else oracle.FP16, ntok, ref["fwd"], y16, ref["out_w"])
         cpu_s = time.perf_counter() - t
         cpu_baseline = {"value": round(payload_bytes / cpu_s / 1e9, 3), "unit": "GB/s",
                         "cores": 1, "kind": "oracle",
-                        "sample": f"the whole {wl.name} workload, one dispatch+combine call, "
-                                  f"single-threaded C oracle, {cpu_s:.2f} s"}
+                        "sample": f"the whole {wl.name} workload: one dispatch+combine call of "
+                                  f"the single-threaded C oracle, {cpu_s:.2f} s"}
         print(f"[bench] oracle call took {cpu_s:.2f}s", file=sys.stderr, flush=True)
         ok = np.array_equal(recv, ref["recv"])
         for d in range(W):
@@ -173,23 +253,24 @@ def main():
             ok = ok and np.array_equal(op.out_indices[d, :Rd].cpu().numpy(), ref["out_idx"][d, :Rd])
             ok = ok and np.array_equal(op.out_weights[d, :Rd].cpu().numpy().view(np.uint32),
                                        ref["out_w"][d, :Rd].view(np.uint32))
-        g = op.combine_out.view(torch.int16).cpu().numpy().view(np.uint16)
+            if ref["out_scales"] is not None:
+                ok = ok and np.array_equal(op.out_scales[d, :Rd].cpu().numpy(),
+                                           ref["out_scales"][d, :Rd])
+        gout = op.combine_out.view(torch.int16).cpu().numpy().view(np.uint16)
         gw = op.combine_weights.cpu().numpy().view(np.uint32)
         for r in range(W):
             T = ntok[r]
-            ok = ok and np.array_equal(g[r, :T], ro[r, :T])
+            ok = ok and np.array_equal(gout[r, :T], ro[r, :T])
             ok = ok and np.array_equal(gw[r, :T], rw[r, :T].view(np.uint32))
-        del ref, y, ro, rw
+        del ref, y16, ro, rw
         if not ok:
             print("bench.py: GPU results differ from the oracle; not timing", file=sys.stderr)
             sys.exit(1)
         check = "bit-exact vs oracle"
 
-    # -- timed region ---------------------------------------------------------
+    # -- timed region: K steps between two HIP events on the launch stream ---
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    cra.ep_plan_set_timing(op.plan, True)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -199,6 +280,14 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
+    # -- the same K steps again with every kernel bracketed by HIP events on
+    # its stream (the library records them), for per-kernel durations; the
+    # records add small gaps between kernels, so this pass is not the value
+    cra.ep_plan_set_timing(op.plan, True)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
     kern = {}
     for name, kid in (("route", cra.EP_KERNEL_ROUTE), ("scan", cra.EP_KERNEL_SCAN),
                       ("copy", cra.EP_KERNEL_COPY), ("combine", cra.EP_KERNEL_COMBINE)):
@@ -206,17 +295,9 @@ def main():
         kern[name] = ms / max(c, 1)
     cra.ep_plan_set_timing(op.plan, False)
 
-    # algorithmic bytes per launch of the two large kernels
-    has_w = 1
-    copy_bytes = (N * (row + sb + 4 * k * (1 + has_w)) + R * (row + sb + 4 * k * (1 + has_w) + 4)
-                  + N * P * 4)
-    combine_bytes = R * crow + N * crow + N * P * 4 + has_w * (R * 4 * k + N * 4 * k)
     dom = "copy" if kern["copy"] >= kern["combine"] else "combine"
-    dom_bytes = copy_bytes if dom == "copy" else combine_bytes
-    achieved = dom_bytes / (kern[dom] * 1e-3) / 1e9
-    kernel_name = {"copy": "ep_copy_kernel", "combine": "ep_combine_kernel"}[dom]
-    traffic = read_traffic(wl.name, kernel_name)
-
+    achieved = kernel_bytes[dom] / (kern[dom] * 1e-3) / 1e9
+    traffic = read_traffic(wl.name, KERNELS[dom])
     value = payload_bytes / (ms_per_step * 1e-3) / 1e9
     line = {
         "metric": METRIC,
@@ -231,24 +312,60 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dispatch_dtype,
         "data": "synthetic",
-        "config": {"workload": wl.name, "world_size": W, "tokens_per_rank": ntok[0] if
-                   len(set(ntok)) == 1 else ntok, "hidden": H, "topk": k,
-                   "experts": wl.num_experts, "dispatch_dtype": wl.dispatch_dtype,
-                   "combine_dtype": wl.combine_dtype, "weights": True,
+        "config": {"workload": wl.name, "world_size": W,
+                   "tokens_per_rank": ntok[0] if len(set(ntok)) == 1 else ntok,
+                   "hidden": H, "topk": k, "experts": wl.num_experts,
+                   "dispatch_dtype": wl.dispatch_dtype, "combine_dtype": wl.combine_dtype,
+                   "scale_dim": wl.scale_dim, "weights": True,
+                   "expert": "identity, in place" if in_place else "seeded random output",
                    "launch": cra.ep_plan_get_launch(op.plan, ntok)},
         "us_per_call": round(ms_per_step * 1e3, 2),
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "payload_bytes_per_call": payload_bytes,
-        "received_rows": R,
+        "received_rows": int(recv.sum()),
         "kernel_us": {k_: round(v * 1e3, 2) for k_, v in kern.items()},
         "check": check,
-        "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": round(achieved, 2),
-                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": dom_bytes},
+        "roofline": {"bound": "hbm", "kernel": KERNELS[dom], "achieved": round(achieved, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": kernel_bytes[dom]},
         "cpu_baseline": cpu_baseline,
     }
     op.close()
     print(json.dumps(line), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle (CPU baseline and the bit-exact check); for profiling")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
+    ap.add_argument("--summarize-stats", nargs="+", metavar="ARG")
+    ap.add_argument("--summarize-counters", nargs=6, metavar="ARG")
+    args = ap.parse_args()
+
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats[0], args.summarize_stats[1],
+                        " ".join(args.summarize_stats[2:]))
+        return
+    if args.summarize_counters:
+        a = args.summarize_counters
+        summarize_counters(a[0], a[1], a[2], a[3], int(a[4]), a[5])
+        return
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs all virtual "
+              "expert-parallel ranks on one GPU; only --gpus 1 is measured.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        import torch
+
+        copy_ceiling(torch, args.copy_calibration, args.steps, args.warmup)
+        return
+    run(args)
 
 
 if __name__ == "__main__":

@@ -57,7 +57,7 @@ struct CopyArgs {
     const int32_t* tile_base;    // [W][tile_stride]
     int32_t* src_pos;            // [W][WM]
     int32_t* fwd;                // [W][M][P]
-    int64_t row_vecs;            // 16-byte vectors per payload row
+    int32_t row_vecs;            // 16-byte vectors per payload row
     int32_t piece_vecs;          // 16-byte vectors per row piece (one block)
     int32_t scale_dwords;        // 4-byte words per scale row (0: none)
     int32_t M, k, Er, E, P, WM;
@@ -78,7 +78,7 @@ struct CombineArgs {
 hipError_t launch_route(const RouteArgs& a, const TileMap& tm, hipStream_t s);
 hipError_t launch_scan(const ScanArgs& a, int W, hipStream_t s);
 hipError_t launch_copy(const CopyArgs& a, const TileMap& tm, int waves, int row_split,
-                       bool nontemporal, hipStream_t s);
+                       hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, const TokenMap& tk, int dtype, int waves,
                           int row_split, hipStream_t s);
 

@@ -29,6 +29,10 @@
 //            is added, then folded in the token's rank order in FP32, rounded
 //            to nearest even by the hardware conversion, and stored.
 //
+// Rows move through per-row buffer resources (raw buffer loads and stores,
+// 16 bytes a lane, 1 KiB a wave instruction): the cache policy is explicit,
+// and the hardware range-checks each access against its own row.
+//
 // Pure data movement: no MFMA. Work is spread over source tokens (and row
 // pieces for small calls), never over destinations, so routing skew does
 // not serialise any block.
@@ -36,6 +40,23 @@
 #include <stdint.h>
 
 #include "ep_kernels.h"
+
+// Cache policy of the row moves, as gfx950 buffer-instruction bits (1 = sc0,
+// 2 = nt, 16 = sc1). Every payload row is touched once per call, so loads
+// stream past the caches (nt). The combine's stores stream too; the dispatch's
+// stores do not: measured on MI355X at 8 ranks x 4096 tokens x 7168 bf16, nt
+// stores in the dispatch copy cost it ~40 us a call, and plain stores in the
+// combine leave dirty lines that the next dispatch pays ~40 us to write back.
+constexpr int kCopyLoadPolicy = 2;
+constexpr int kCopyStorePolicy = 0;
+constexpr int kCombineLoadPolicy = 2;
+constexpr int kCombineStorePolicy = 2;
+// The combine loads up to kCombineGroup contribution rows, kCombineColumns
+// 16-byte columns each, before folding (8 x 2 measured best: smaller groups
+// split a top-8 token's rows into two dependent rounds, larger column counts
+// cost occupancy).
+constexpr int kCombineGroup = 8;
+constexpr int kCombineColumns = 2;
 
 namespace ep {
 namespace {
@@ -56,13 +77,27 @@ __device__ __forceinline__ int lanes_below(uint64_t b)
 // A value every lane of the wave holds identically, moved to a scalar register.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-template <bool kNT>
-__device__ __forceinline__ void store16(u32x4* p, u32x4 v)
+// A buffer resource covering one row: every access through it is range-checked
+// by the hardware against the row's bytes (an out-of-range load reads zero, an
+// out-of-range store is dropped), so a row move cannot spill into its
+// neighbour. Word 3 is the raw (untyped) buffer format.
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uint32_t bytes)
 {
-    if constexpr (kNT)
-        __builtin_nontemporal_store(v, p);
-    else
-        *p = v;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
+}
+
+template <int AUX>
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX);
+}
+
+template <int AUX>
+__device__ __forceinline__ void bstore16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, AUX);
 }
 
 // Rank r owning tile g: the largest r with tile_start[r] <= g (ranks without
@@ -215,7 +250,7 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(ScanArgs a)
 // ---------------------------------------------------------------------------
 // copy: payload rows, metadata rows, src_pos and the forward map.
 // ---------------------------------------------------------------------------
-template <int VPL, bool kNT>
+template <int VPL>
 __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
 {
     __shared__ uint8_t s_list[kMaxTile][kMaxRanks];  // [token][i]: i-th distinct rank
@@ -297,31 +332,31 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
         }
     }
 
-    const int64_t vbeg = (int64_t)piece * a.piece_vecs;
-    const int64_t vend = min(a.row_vecs, vbeg + (int64_t)a.piece_vecs);
-    const u32x4* __restrict__ xs = reinterpret_cast<const u32x4*>(a.x);
-    u32x4* __restrict__ xd = reinterpret_cast<u32x4*>(a.out_x);
+    const int vbeg = piece * a.piece_vecs;
+    const int vend = min(a.row_vecs, vbeg + a.piece_vecs);
+    const uint32_t row_bytes = (uint32_t)a.row_vecs * 16u;
     for (int tok = wave; tok < cnt; tok += nwaves) {
         const int64_t src = (int64_t)r * a.M + t0 + tok;
         const int n = uniform(s_n[tok]);
-        const u32x4* sp = xs + src * a.row_vecs;
-        for (int64_t v0 = vbeg; v0 < vend; v0 += (int64_t)kWave * VPL) {
+        const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.x + src * row_bytes, row_bytes);
+        for (int v0 = vbeg; v0 < vend; v0 += kWave * VPL) {
             u32x4 buf[VPL];
 #pragma unroll
             for (int u = 0; u < VPL; ++u) {
-                const int64_t v = v0 + u * kWave + lane;
+                const int v = v0 + u * kWave + lane;
                 if (v < vend)
-                    buf[u] = sp[v];
+                    buf[u] = bload16<kCopyLoadPolicy>(rs, (uint32_t)v * 16u);
             }
             for (int i = 0; i < n; ++i) {
                 const int d = uniform(s_list[tok][i]);
                 const int s = uniform(s_base[d] + s_loc[tok][d]);
-                u32x4* dp = xd + ((int64_t)d * a.WM + s) * a.row_vecs;
+                const __amdgpu_buffer_rsrc_t rd =
+                    row_rsrc(a.out_x + ((int64_t)d * a.WM + s) * row_bytes, row_bytes);
 #pragma unroll
                 for (int u = 0; u < VPL; ++u) {
-                    const int64_t v = v0 + u * kWave + lane;
+                    const int v = v0 + u * kWave + lane;
                     if (v < vend)
-                        store16<kNT>(dp + v, buf[u]);
+                        bstore16<kCopyStorePolicy>(buf[u], rd, (uint32_t)v * 16u);
                 }
             }
         }
@@ -379,8 +414,8 @@ __global__ __launch_bounds__(1024) void ep_combine_kernel(CombineArgs a, TokenMa
     const int32_t gl = lane < a.P ? a.fwd[tok * a.P + lane] : -1;
     const int n = __popcll(__ballot(gl >= 0));  // entries >= 0 form a prefix
 
-    const u32x4* __restrict__ ys = reinterpret_cast<const u32x4*>(a.y);
-    u32x4* __restrict__ dst = reinterpret_cast<u32x4*>(a.out) + tok * a.row_vecs;
+    const uint32_t row_bytes = (uint32_t)a.row_vecs * 16u;
+    const __amdgpu_buffer_rsrc_t rdst = row_rsrc(a.out + tok * row_bytes, row_bytes);
     const int vbeg = piece * a.piece_vecs;
     const int vend = min(a.row_vecs, vbeg + a.piece_vecs);
     for (int v0 = vbeg; v0 < vend; v0 += kWave * U) {
@@ -391,12 +426,12 @@ __global__ __launch_bounds__(1024) void ep_combine_kernel(CombineArgs a, TokenMa
             for (int q = 0; q < G; ++q) {
                 if (i0 + q < n) {
                     const int64_t gq = __builtin_amdgcn_readlane(gl, i0 + q);
-                    const u32x4* yp = ys + gq * a.row_vecs;
+                    const __amdgpu_buffer_rsrc_t ry = row_rsrc(a.y + gq * row_bytes, row_bytes);
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         const int v = v0 + u * kWave + lane;
                         if (v < vend)
-                            rows[u][q] = yp[v];
+                            rows[u][q] = bload16<kCombineLoadPolicy>(ry, (uint32_t)v * 16u);
                     }
                 }
             }
@@ -429,7 +464,7 @@ __global__ __launch_bounds__(1024) void ep_combine_kernel(CombineArgs a, TokenMa
                     for (int e = 0; e < 8; ++e)
                         acc[u][e] = 0.0f;
                 }
-                dst[v] = narrow<DT>(acc[u]);
+                bstore16<kCombineStorePolicy>(narrow<DT>(acc[u]), rdst, (uint32_t)v * 16u);
             }
         }
     }
@@ -446,13 +481,10 @@ __global__ __launch_bounds__(1024) void ep_combine_kernel(CombineArgs a, TokenMa
 }
 
 template <int VPL>
-hipError_t copy_with_vpl(const CopyArgs& a, const TileMap& tm, dim3 grid, dim3 block, bool nt,
+hipError_t copy_with_vpl(const CopyArgs& a, const TileMap& tm, dim3 grid, dim3 block,
                          hipStream_t s)
 {
-    if (nt)
-        hipLaunchKernelGGL((ep_copy_kernel<VPL, true>), grid, block, 0, s, a, tm);
-    else
-        hipLaunchKernelGGL((ep_copy_kernel<VPL, false>), grid, block, 0, s, a, tm);
+    hipLaunchKernelGGL((ep_copy_kernel<VPL>), grid, block, 0, s, a, tm);
     return hipGetLastError();
 }
 
@@ -486,7 +518,7 @@ hipError_t launch_scan(const ScanArgs& a, int W, hipStream_t s)
 }
 
 hipError_t launch_copy(const CopyArgs& a, const TileMap& tm, int waves, int row_split,
-                       bool nontemporal, hipStream_t s)
+                       hipStream_t s)
 {
     if (tm.total_tiles == 0)
         return hipSuccess;
@@ -494,14 +526,14 @@ hipError_t launch_copy(const CopyArgs& a, const TileMap& tm, int waves, int row_
     const dim3 block(waves * kWave);
     const int per_lane = (a.piece_vecs + kWave - 1) / kWave;
     if (per_lane <= 1)
-        return copy_with_vpl<1>(a, tm, grid, block, nontemporal, s);
+        return copy_with_vpl<1>(a, tm, grid, block, s);
     if (per_lane <= 2)
-        return copy_with_vpl<2>(a, tm, grid, block, nontemporal, s);
+        return copy_with_vpl<2>(a, tm, grid, block, s);
     if (per_lane <= 4)
-        return copy_with_vpl<4>(a, tm, grid, block, nontemporal, s);
+        return copy_with_vpl<4>(a, tm, grid, block, s);
     if (per_lane <= 8)
-        return copy_with_vpl<8>(a, tm, grid, block, nontemporal, s);
-    return copy_with_vpl<16>(a, tm, grid, block, nontemporal, s);
+        return copy_with_vpl<8>(a, tm, grid, block, s);
+    return copy_with_vpl<16>(a, tm, grid, block, s);
 }
 
 hipError_t launch_combine(const CombineArgs& a, const TokenMap& tk, int dtype, int waves,
@@ -516,8 +548,8 @@ hipError_t launch_combine(const CombineArgs& a, const TokenMap& tk, int dtype, i
     if (a.P <= 2)
         return combine_with<2, 4>(a, tk, dtype, grid, block, s);
     if (a.P <= 4)
-        return combine_with<4, 2>(a, tk, dtype, grid, block, s);
-    return combine_with<8, 2>(a, tk, dtype, grid, block, s);
+        return combine_with<4, kCombineColumns>(a, tk, dtype, grid, block, s);
+    return combine_with<kCombineGroup, kCombineColumns>(a, tk, dtype, grid, block, s);
 }
 
 }  // namespace ep

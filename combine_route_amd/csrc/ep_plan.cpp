@@ -96,6 +96,9 @@ int check_config(const ep_config_t* c, Shape* s)
                     "cfg.hidden_dim = %d: payload (%lld B) and combine (%lld B) rows must be "
                     "multiples of 16 bytes",
                     c->hidden_dim, (long long)row, (long long)crow);
+    if (row >= (int64_t)1 << 31 || crow >= (int64_t)1 << 31)
+        return fail(EP_ERR_SIZE, "cfg.hidden_dim = %d: a row must stay below 2^31 bytes",
+                    c->hidden_dim);
     if (c->scale_dim < 0)
         return fail(EP_ERR_ARG, "cfg.scale_dim = %d: must be >= 0", c->scale_dim);
     int64_t sbytes = 0;
@@ -438,8 +441,8 @@ int ep_dispatch(ep_plan_t* p, const ep_dispatch_args_t* a, void* stream_ptr)
     ca.tile_base = ws_base(p);
     ca.src_pos = ws_src_pos(p);
     ca.fwd = ws_fwd(p);
-    ca.row_vecs = s.row_bytes / 16;
-    ca.piece_vecs = (int32_t)((ca.row_vecs + l.dispatch_row_split - 1) / l.dispatch_row_split);
+    ca.row_vecs = (int32_t)(s.row_bytes / 16);
+    ca.piece_vecs = (ca.row_vecs + l.dispatch_row_split - 1) / l.dispatch_row_split;
     ca.scale_dwords = (int32_t)(s.scale_bytes / 4);
     ca.M = s.M;
     ca.k = s.k;
@@ -455,7 +458,7 @@ int ep_dispatch(ep_plan_t* p, const ep_dispatch_args_t* a, void* stream_ptr)
         e = timed(p, EP_KERNEL_SCAN, stream, [&] { return ep::launch_scan(sa, s.W, stream); });
     if (e == hipSuccess)
         e = timed(p, EP_KERNEL_COPY, stream, [&] {
-            return ep::launch_copy(ca, tm, l.dispatch_waves, row_split, false, stream);
+            return ep::launch_copy(ca, tm, l.dispatch_waves, row_split, stream);
         });
     p->launched = true;
     p->last_stream = stream;
