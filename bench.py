@@ -274,10 +274,29 @@ def run(args):
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
+    if args.graph:
+        # one step captured in a HIP graph, replayed K times (no host launch
+        # cost between kernels; the pages time their pairs this way)
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                op.dispatch(ntok, x, idx, w, sc, stream=side)
+                op.combine(y, op.out_weights, stream=side)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        end.record(stream)
+    else:
+        start.record(stream)
+        for _ in range(args.steps):
+            step()
+        end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
     # -- the same K steps again with every kernel bracketed by HIP events on
@@ -318,6 +337,7 @@ def run(args):
                    "dispatch_dtype": wl.dispatch_dtype, "combine_dtype": wl.combine_dtype,
                    "scale_dim": wl.scale_dim, "weights": True,
                    "expert": "identity, in place" if in_place else "seeded random output",
+                   "launches": "graph replay" if args.graph else "eager",
                    "launch": cra.ep_plan_get_launch(op.plan, ntok)},
         "us_per_call": round(ms_per_step * 1e3, 2),
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
@@ -343,6 +363,8 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle (CPU baseline and the bit-exact check); for profiling")
+    ap.add_argument("--graph", action="store_true",
+                    help="time K replays of one step captured in a HIP graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--summarize-stats", nargs="+", metavar="ARG")
     ap.add_argument("--summarize-counters", nargs=6, metavar="ARG")

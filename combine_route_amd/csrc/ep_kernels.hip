@@ -130,8 +130,11 @@ __device__ __forceinline__ int rank_of_token(const TokenMap& tk, int flat)
 
 // Destination ranks of one token (one lane). Expert e is on rank e / Er; an id
 // outside [0, E) selects none. With kList, the distinct ranks are written to
-// list[] in the order their first expert appears in the top-k row.
-template <bool kList>
+// list[] in the order their first expert appears in the top-k row. KB >= k is
+// the top-k bucket: all KB ids are loaded at once, at addresses clamped into
+// the row, so every load issues before any is waited on; ids past k are
+// loaded but ignored.
+template <bool kList, int KB>
 __device__ __forceinline__ uint64_t route_token(const int32_t* row, bool valid, int k, int Er,
                                                 int E, uint8_t* list, int& n)
 {
@@ -152,23 +155,92 @@ __device__ __forceinline__ uint64_t route_token(const int32_t* row, bool valid, 
         }
     };
     if ((k & 3) == 0) {
-        for (int j = 0; j < k; j += 4) {
-            const int4 v = *reinterpret_cast<const int4*>(row + j);
-            take(v.x);
-            take(v.y);
-            take(v.z);
-            take(v.w);
+        constexpr int NV = KB / 4;
+        int4 v[NV];
+#pragma unroll
+        for (int q = 0; q < NV; ++q)
+            v[q] = *reinterpret_cast<const int4*>(row + min(4 * q, k - 4));
+#pragma unroll
+        for (int q = 0; q < NV; ++q) {
+            if (4 * q < k) {
+                take(v[q].x);
+                take(v[q].y);
+                take(v[q].z);
+                take(v[q].w);
+            }
         }
     } else {
-        for (int j = 0; j < k; ++j)
-            take(row[j]);
+        int32_t v[KB];
+#pragma unroll
+        for (int q = 0; q < KB; ++q)
+            v[q] = row[min(q, k - 1)];
+#pragma unroll
+        for (int q = 0; q < KB; ++q)
+            if (q < k)
+                take(v[q]);
     }
     return m;
+}
+
+// Routing of a whole tile by one wave, for k > 16. Tokens are taken one at a
+// time with one lane per top-k slot: lane j holds id j, every id of a batch
+// of 16 tokens loaded at once (addresses clamped into the tile, so all loads
+// issue unconditionally). A token's distinct ranks come from a leader loop:
+// the lowest lane not yet covered names the next rank, one ballot marks every
+// slot on that rank; each iteration finds one rank, in the order of first
+// appearance. Returns, in lane tt, the destination mask and rank count of the
+// tile's token tt; with kList the ordered ranks go to list[tt][*].
+template <bool kList>
+__device__ __forceinline__ uint64_t route_tile_by_slot(const int32_t* rows, int cnt, int k,
+                                                       int Er, int E, uint8_t (*list)[kMaxRanks],
+                                                       int& n_out)
+{
+    constexpr int kBatch = 16;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int j = min(lane, k - 1);
+    uint64_t my_mask = 0;
+    int my_n = 0;
+    for (int b0 = 0; b0 < cnt; b0 += kBatch) {
+        int32_t ids[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q)
+            ids[q] = rows[(int64_t)min(b0 + q, cnt - 1) * k + j];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            const int tt = b0 + q;
+            if (tt >= cnt)
+                break;
+            const int32_t e = ids[q];
+            const bool valid = lane < k && (uint32_t)e < (uint32_t)E;
+            const int d = valid ? (int)((uint32_t)e / (uint32_t)Er) : -1;
+            uint64_t rem = __ballot(valid);
+            uint64_t mask = 0;
+            int n = 0;
+            while (rem) {
+                const int leader = __builtin_ctzll(rem);
+                const int dl = __builtin_amdgcn_readlane(d, leader);
+                rem &= ~__ballot(d == dl);
+                if constexpr (kList) {
+                    if (lane == 0)
+                        list[tt][n] = (uint8_t)dl;
+                }
+                mask |= 1ull << dl;
+                ++n;
+            }
+            if (lane == tt) {
+                my_mask = mask;
+                my_n = n;
+            }
+        }
+    }
+    n_out = my_n;
+    return my_mask;
 }
 
 // ---------------------------------------------------------------------------
 // route: per-tile row counts for every destination rank.
 // ---------------------------------------------------------------------------
+template <int KB>
 __global__ __launch_bounds__(256) void ep_route_kernel(RouteArgs a, TileMap tm)
 {
     const int lane = threadIdx.x & (kWave - 1);
@@ -179,8 +251,13 @@ __global__ __launch_bounds__(256) void ep_route_kernel(RouteArgs a, TileMap tm)
     const int t0 = (g - tm.tile_start[r]) * tm.tile_tokens;
     const int cnt = min(tm.tile_tokens, tm.ntok[r] - t0);
     int n;
-    const uint64_t m = route_token<false>(a.idx + ((int64_t)r * a.M + t0 + lane) * a.k,
-                                          lane < cnt, a.k, a.Er, a.E, nullptr, n);
+    uint64_t m;
+    if constexpr (KB >= 32)
+        m = route_tile_by_slot<false>(a.idx + ((int64_t)r * a.M + t0) * a.k, cnt, a.k, a.Er,
+                                      a.E, nullptr, n);
+    else
+        m = route_token<false, KB>(a.idx + ((int64_t)r * a.M + t0 + lane) * a.k, lane < cnt,
+                                   a.k, a.Er, a.E, nullptr, n);
     int mine = 0;
     for (int d = 0; d < tm.W; ++d) {
         const uint64_t b = __ballot((m >> d) & 1);
@@ -250,7 +327,18 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(ScanArgs a)
 // ---------------------------------------------------------------------------
 // copy: payload rows, metadata rows, src_pos and the forward map.
 // ---------------------------------------------------------------------------
+// One work item of a wave: one chunk (up to 64 x VPL 16-byte vectors) of one
+// token's row piece, and, for the first chunk of a piece-0 block, the lane's
+// share of the token's id, weight and scale rows.
 template <int VPL>
+struct CopyItem {
+    u32x4 v[VPL];
+    int32_t e;
+    float wv;
+    uint32_t sc;
+};
+
+template <int VPL, int KB>
 __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
 {
     __shared__ uint8_t s_list[kMaxTile][kMaxRanks];  // [token][i]: i-th distinct rank
@@ -267,10 +355,116 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
     const int t0 = (g - tm.tile_start[r]) * tm.tile_tokens;
     const int cnt = min(tm.tile_tokens, tm.ntok[r] - t0);
 
-    if (wave == 0) {
+    // This wave's items: tokens wave, wave + nwaves, ... of the tile, each cut
+    // into nch chunks of its row piece [vbeg, vend).
+    const int vbeg = piece * a.piece_vecs;
+    const int vend = min(a.row_vecs, vbeg + a.piece_vecs);
+    const int nch = (vend - vbeg + kWave * VPL - 1) / (kWave * VPL);
+    const int ntw = wave < cnt ? (cnt - wave + nwaves - 1) / nwaves : 0;
+    const int items = ntw * nch;
+    const bool meta = piece == 0;
+    const uint32_t row_bytes = (uint32_t)a.row_vecs * 16u;
+    const int k = a.k;
+    const int per = kWave / k;  // destination id/weight rows per store instruction
+    const int j = lane % k;
+    const int sub = lane / k;
+    const int sd = a.scale_dwords;
+
+    // id, weight and scale rows, src_pos and forward map of one token, from
+    // the lane's share (e, wv, sc) of its source rows
+    auto store_meta = [&](int tok, int32_t e, float wv, uint32_t sc) {
+        const int t = t0 + tok;
+        const int64_t src = (int64_t)r * a.M + t;
+        const int n = uniform(s_n[tok]);
+        if (lane < a.P) {
+            int32_t f = -1;
+            if (lane < n) {
+                const int d = s_list[tok][lane];
+                f = d * a.WM + s_base[d] + s_loc[tok][d];
+                a.src_pos[f] = r * a.WM + t;
+            }
+            a.fwd[src * a.P + lane] = f;
+        }
+        for (int i0 = 0; i0 < n; i0 += per) {
+            const int i = i0 + sub;
+            if (sub < per && i < n) {
+                const int d = s_list[tok][i];
+                const int64_t row = (int64_t)d * a.WM + s_base[d] + s_loc[tok][d];
+                a.out_idx[row * k + j] = e;
+                if (a.w)
+                    a.out_w[row * k + j] = wv;
+            }
+        }
+        for (int i = 0; i < n && sd > 0; ++i) {
+            const int d = uniform(s_list[tok][i]);
+            const int64_t row = (int64_t)d * a.WM + uniform(s_base[d] + s_loc[tok][d]);
+            if (lane < sd)
+                a.out_sc[row * sd + lane] = sc;
+            for (int qd = kWave + lane; qd < sd; qd += kWave)  // scale rows past 64 words
+                a.out_sc[row * sd + qd] = a.sc[src * sd + qd];
+        }
+    };
+    auto load_meta = [&](int64_t src, int32_t& e, float& wv, uint32_t& sc) {
+        if (sub < per) {
+            e = a.idx[src * k + j];
+            wv = a.w ? a.w[src * k + j] : 0.0f;
+        }
+        if (lane < sd)
+            sc = a.sc[src * sd + lane];
+    };
+    // one chunk of a token's row piece to every destination row of the token
+    auto store_payload = [&](int tok, int v0, const u32x4 (&v)[VPL]) {
+        const int n = uniform(s_n[tok]);
+        for (int i = 0; i < n; ++i) {
+            const int d = uniform(s_list[tok][i]);
+            const int s = uniform(s_base[d] + s_loc[tok][d]);
+            const __amdgpu_buffer_rsrc_t rd =
+                row_rsrc(a.out_x + ((int64_t)d * a.WM + s) * row_bytes, row_bytes);
+#pragma unroll
+            for (int u = 0; u < VPL; ++u) {
+                const int vv = v0 + u * kWave + lane;
+                if (vv < vend)
+                    bstore16<kCopyStorePolicy>(v[u], rd, (uint32_t)vv * 16u);
+            }
+        }
+    };
+    auto load_payload = [&](int64_t src, int v0, u32x4 (&v)[VPL]) {
+        const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.x + src * row_bytes, row_bytes);
+#pragma unroll
+        for (int u = 0; u < VPL; ++u) {
+            const int vv = v0 + u * kWave + lane;
+            if (vv < vend)
+                v[u] = bload16<kCopyLoadPolicy>(rs, (uint32_t)vv * 16u);
+        }
+    };
+    auto load_item = [&](int it, CopyItem<VPL>& I) {
+        const int q = it / nch;
+        const int c = it - q * nch;
+        const int64_t src = (int64_t)r * a.M + t0 + wave + q * nwaves;
+        load_payload(src, vbeg + c * kWave * VPL, I.v);
+        if (meta && c == 0)
+            load_meta(src, I.e, I.wv, I.sc);
+    };
+    auto store_item = [&](int it, const CopyItem<VPL>& I) {
+        const int q = it / nch;
+        const int c = it - q * nch;
+        const int tok = wave + q * nwaves;
+        store_payload(tok, vbeg + c * kWave * VPL, I.v);
+        if (meta && c == 0)
+            store_meta(tok, I.e, I.wv, I.sc);
+    };
+    auto route_tile = [&]() {
+        if (wave != 0)
+            return;
+        const int32_t base = lane < tm.W ? a.tile_base[(int64_t)lane * a.tile_stride + g] : 0;
         int n;
-        const uint64_t m = route_token<true>(a.idx + ((int64_t)r * a.M + t0 + lane) * a.k,
-                                             lane < cnt, a.k, a.Er, a.E, s_list[lane], n);
+        uint64_t m;
+        if constexpr (KB >= 32)
+            m = route_tile_by_slot<true>(a.idx + ((int64_t)r * a.M + t0) * a.k, cnt, a.k, a.Er,
+                                         a.E, s_list, n);
+        else
+            m = route_token<true, KB>(a.idx + ((int64_t)r * a.M + t0 + lane) * a.k, lane < cnt,
+                                      a.k, a.Er, a.E, s_list[lane], n);
         s_n[lane] = n;
         for (int d = 0; d < tm.W; ++d) {
             const bool has = (m >> d) & 1;
@@ -279,85 +473,49 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
                 s_loc[lane][d] = (uint8_t)lanes_below(b);
         }
         if (lane < tm.W)
-            s_base[lane] = a.tile_base[(int64_t)lane * a.tile_stride + g];
-    }
-    __syncthreads();
+            s_base[lane] = base;
+    };
 
-    if (piece == 0) {
-        const int k = a.k;
-        const int per = kWave / k;  // destination rows per store instruction
-        const int j = lane % k;
-        const int sub = lane / k;
-        for (int tok = wave; tok < cnt; tok += nwaves) {
-            const int t = t0 + tok;
-            const int64_t src = (int64_t)r * a.M + t;
-            const int n = uniform(s_n[tok]);
-            if (lane < a.P) {
-                int32_t v = -1;
-                if (lane < n) {
-                    const int d = s_list[tok][lane];
-                    v = d * a.WM + s_base[d] + s_loc[tok][d];
-                    a.src_pos[v] = r * a.WM + t;
-                }
-                a.fwd[src * a.P + lane] = v;
-            }
-            int32_t e = 0;
-            float wv = 0.f;
-            if (sub < per) {
-                e = a.idx[src * k + j];
-                if (a.w)
-                    wv = a.w[src * k + j];
-            }
-            for (int i0 = 0; i0 < n; i0 += per) {
-                const int i = i0 + sub;
-                if (sub < per && i < n) {
-                    const int d = s_list[tok][i];
-                    const int64_t row = (int64_t)d * a.WM + s_base[d] + s_loc[tok][d];
-                    a.out_idx[row * k + j] = e;
-                    if (a.w)
-                        a.out_w[row * k + j] = wv;
-                }
-            }
-            for (int q0 = 0; q0 < a.scale_dwords; q0 += kWave) {
-                const int q = q0 + lane;
-                const bool in = q < a.scale_dwords;
-                const uint32_t v = in ? a.sc[src * a.scale_dwords + q] : 0u;
-                for (int i = 0; i < n; ++i) {
-                    const int d = uniform(s_list[tok][i]);
-                    const int64_t row = (int64_t)d * a.WM + uniform(s_base[d] + s_loc[tok][d]);
-                    if (in)
-                        a.out_sc[row * a.scale_dwords + q] = v;
-                }
+    if constexpr (VPL < 8) {
+        // Small pieces (small calls, where time is latency): each wave's first
+        // item loads while wave 0 routes the tile, then two items in flight,
+        // item i+1 loading while item i stores.
+        CopyItem<VPL> A, B;
+        if (items > 0)
+            load_item(0, A);
+        route_tile();
+        __syncthreads();
+        for (int it = 0; it < items; it += 2) {
+            if (it + 1 < items)
+                load_item(it + 1, B);
+            store_item(it, A);
+            if (it + 1 < items) {
+                if (it + 2 < items)
+                    load_item(it + 2, A);
+                store_item(it + 1, B);
             }
         }
-    }
-
-    const int vbeg = piece * a.piece_vecs;
-    const int vend = min(a.row_vecs, vbeg + a.piece_vecs);
-    const uint32_t row_bytes = (uint32_t)a.row_vecs * 16u;
-    for (int tok = wave; tok < cnt; tok += nwaves) {
-        const int64_t src = (int64_t)r * a.M + t0 + tok;
-        const int n = uniform(s_n[tok]);
-        const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.x + src * row_bytes, row_bytes);
-        for (int v0 = vbeg; v0 < vend; v0 += kWave * VPL) {
-            u32x4 buf[VPL];
-#pragma unroll
-            for (int u = 0; u < VPL; ++u) {
-                const int v = v0 + u * kWave + lane;
-                if (v < vend)
-                    buf[u] = bload16<kCopyLoadPolicy>(rs, (uint32_t)v * 16u);
+    } else {
+        // Large pieces (throughput): metadata first, then one chunk a wave in
+        // flight, which keeps the register count, and so the waves resident
+        // per SIMD, at its lowest.
+        route_tile();
+        __syncthreads();
+        if (meta) {
+            for (int tok = wave; tok < cnt; tok += nwaves) {
+                int32_t e = 0;
+                float wv = 0.0f;
+                uint32_t sc = 0;
+                load_meta((int64_t)r * a.M + t0 + tok, e, wv, sc);
+                store_meta(tok, e, wv, sc);
             }
-            for (int i = 0; i < n; ++i) {
-                const int d = uniform(s_list[tok][i]);
-                const int s = uniform(s_base[d] + s_loc[tok][d]);
-                const __amdgpu_buffer_rsrc_t rd =
-                    row_rsrc(a.out_x + ((int64_t)d * a.WM + s) * row_bytes, row_bytes);
-#pragma unroll
-                for (int u = 0; u < VPL; ++u) {
-                    const int v = v0 + u * kWave + lane;
-                    if (v < vend)
-                        bstore16<kCopyStorePolicy>(buf[u], rd, (uint32_t)v * 16u);
-                }
+        }
+        for (int tok = wave; tok < cnt; tok += nwaves) {
+            const int64_t src = (int64_t)r * a.M + t0 + tok;
+            for (int v0 = vbeg; v0 < vend; v0 += kWave * VPL) {
+                u32x4 v[VPL];
+                load_payload(src, v0, v);
+                store_payload(tok, v0, v);
             }
         }
     }
@@ -480,12 +638,27 @@ __global__ __launch_bounds__(1024) void ep_combine_kernel(CombineArgs a, TokenMa
     }
 }
 
+// Top-k bucket of k: the smallest of 4, 8, 16, 32, 64 that holds it.
+int topk_bucket(int k) { return k <= 4 ? 4 : k <= 8 ? 8 : k <= 16 ? 16 : k <= 32 ? 32 : 64; }
+
+template <int VPL, int KB>
+hipError_t copy_with(const CopyArgs& a, const TileMap& tm, dim3 grid, dim3 block, hipStream_t s)
+{
+    hipLaunchKernelGGL((ep_copy_kernel<VPL, KB>), grid, block, 0, s, a, tm);
+    return hipGetLastError();
+}
+
 template <int VPL>
 hipError_t copy_with_vpl(const CopyArgs& a, const TileMap& tm, dim3 grid, dim3 block,
                          hipStream_t s)
 {
-    hipLaunchKernelGGL((ep_copy_kernel<VPL>), grid, block, 0, s, a, tm);
-    return hipGetLastError();
+    switch (topk_bucket(a.k)) {
+    case 4: return copy_with<VPL, 4>(a, tm, grid, block, s);
+    case 8: return copy_with<VPL, 8>(a, tm, grid, block, s);
+    case 16: return copy_with<VPL, 16>(a, tm, grid, block, s);
+    case 32: return copy_with<VPL, 32>(a, tm, grid, block, s);
+    default: return copy_with<VPL, 64>(a, tm, grid, block, s);
+    }
 }
 
 template <int G, int U>
@@ -507,7 +680,14 @@ hipError_t launch_route(const RouteArgs& a, const TileMap& tm, hipStream_t s)
         return hipSuccess;
     constexpr int kWaves = 4;
     const dim3 grid((tm.total_tiles + kWaves - 1) / kWaves);
-    hipLaunchKernelGGL(ep_route_kernel, grid, dim3(kWaves * kWave), 0, s, a, tm);
+    const dim3 block(kWaves * kWave);
+    switch (topk_bucket(a.k)) {
+    case 4: hipLaunchKernelGGL((ep_route_kernel<4>), grid, block, 0, s, a, tm); break;
+    case 8: hipLaunchKernelGGL((ep_route_kernel<8>), grid, block, 0, s, a, tm); break;
+    case 16: hipLaunchKernelGGL((ep_route_kernel<16>), grid, block, 0, s, a, tm); break;
+    case 32: hipLaunchKernelGGL((ep_route_kernel<32>), grid, block, 0, s, a, tm); break;
+    default: hipLaunchKernelGGL((ep_route_kernel<64>), grid, block, 0, s, a, tm); break;
+    }
     return hipGetLastError();
 }
 
@@ -531,9 +711,7 @@ hipError_t launch_copy(const CopyArgs& a, const TileMap& tm, int waves, int row_
         return copy_with_vpl<2>(a, tm, grid, block, s);
     if (per_lane <= 4)
         return copy_with_vpl<4>(a, tm, grid, block, s);
-    if (per_lane <= 8)
-        return copy_with_vpl<8>(a, tm, grid, block, s);
-    return copy_with_vpl<16>(a, tm, grid, block, s);
+    return copy_with_vpl<8>(a, tm, grid, block, s);
 }
 
 hipError_t launch_combine(const CombineArgs& a, const TokenMap& tk, int dtype, int waves,

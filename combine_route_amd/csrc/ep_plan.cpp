@@ -211,7 +211,9 @@ ep_launch_t auto_launch(const ep_plan* p, const int32_t* ntok)
     const int64_t max_split = std::max<int64_t>(1, row_vecs / ep::kWave);
     l.dispatch_row_split = (int)std::min<int64_t>(
         std::min<int64_t>(max_split, 65535), std::max(1, (kTargetBlocks + tiles - 1) / tiles));
-    l.dispatch_waves = l.tile_tokens >= 32 ? 8 : 4;
+    // one token a wave below 64-token tiles: a small call's time is load
+    // latency, and a wave per token keeps every token's loads in flight at once
+    l.dispatch_waves = l.tile_tokens >= 64 ? 8 : 16;
     l.combine_waves = 4;
     const int64_t cblocks = std::max<int64_t>(1, (N + l.combine_waves - 1) / l.combine_waves);
     const int64_t crow_vecs = s.crow_bytes / 16;
