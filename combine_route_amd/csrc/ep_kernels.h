@@ -77,9 +77,11 @@ struct CombineArgs {
 
 hipError_t launch_route(const RouteArgs& a, const TileMap& tm, hipStream_t s);
 hipError_t launch_scan(const ScanArgs& a, int W, hipStream_t s);
+// stream: true = streaming cache policy (rows bypass the caches), false =
+// cache-allocating moves.
 hipError_t launch_copy(const CopyArgs& a, const TileMap& tm, int waves, int row_split,
-                       hipStream_t s);
+                       bool stream, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, const TokenMap& tk, int dtype, int waves,
-                          int row_split, hipStream_t s);
+                          int row_split, bool stream, hipStream_t s);
 
 }  // namespace ep

@@ -42,15 +42,21 @@
 #include "ep_kernels.h"
 
 // Cache policy of the row moves, as gfx950 buffer-instruction bits (1 = sc0,
-// 2 = nt, 16 = sc1). Every payload row is touched once per call, so loads
-// stream past the caches (nt). The combine's stores stream too; the dispatch's
-// stores do not: measured on MI355X at 8 ranks x 4096 tokens x 7168 bf16, nt
-// stores in the dispatch copy cost it ~40 us a call, and plain stores in the
-// combine leave dirty lines that the next dispatch pays ~40 us to write back.
-constexpr int kCopyLoadPolicy = 2;
-constexpr int kCopyStorePolicy = 0;
-constexpr int kCombineLoadPolicy = 2;
-constexpr int kCombineStorePolicy = 2;
+// 2 = nt, 16 = sc1). Streaming calls (footprint well past the 256 MB MALL)
+// touch every payload row once, so loads stream past the caches (nt); the
+// combine's stores stream too; the dispatch's stores do not. Measured on
+// MI355X at 8 ranks x 4096 tokens x 7168 bf16: nt stores in the dispatch copy
+// cost it ~40 us a call, plain stores in the combine leave dirty lines that the
+// next dispatch pays ~40 us to write back, and cached combine loads cost ~70
+// us. Calls that fit in the MALL use plain (cache-allocating) moves: rows an
+// expert has just written are still there, and 8 ranks x 128 fp8 tokens runs
+// ~10% faster that way.
+template <bool kStream> struct Policy {
+    static constexpr int copy_load = kStream ? 2 : 0;
+    static constexpr int copy_store = 0;
+    static constexpr int combine_load = kStream ? 2 : 0;
+    static constexpr int combine_store = kStream ? 2 : 0;
+};
 // The combine loads up to kCombineGroup contribution rows, kCombineColumns
 // 16-byte columns each, before folding (8 x 2 measured best: smaller groups
 // split a top-8 token's rows into two dependent rounds, larger column counts
@@ -182,82 +188,77 @@ __device__ __forceinline__ uint64_t route_token(const int32_t* row, bool valid, 
     return m;
 }
 
-// Routing of a whole tile by one wave, for k > 16. Tokens are taken one at a
-// time with one lane per top-k slot: lane j holds id j, every id of a batch
-// of 16 tokens loaded at once (addresses clamped into the tile, so all loads
-// issue unconditionally). A token's distinct ranks come from a leader loop:
-// the lowest lane not yet covered names the next rank, one ballot marks every
-// slot on that rank; each iteration finds one rank, in the order of first
-// appearance. Returns, in lane tt, the destination mask and rank count of the
-// tile's token tt; with kList the ordered ranks go to list[tt][*].
+// Routing of a tile's tokens for k > 16, spread over the waves of a block:
+// wave w takes tokens w, w + nwaves, ... one at a time, with one lane per
+// top-k slot (lane j holds id j). A token's distinct ranks come from a leader
+// loop: the lowest lane not yet covered names the next rank, one ballot marks
+// every slot on that rank, so each iteration finds one rank, in the order of
+// first appearance. Writes the token's destination mask, rank count and (with
+// kList) ordered ranks to LDS.
 template <bool kList>
-__device__ __forceinline__ uint64_t route_tile_by_slot(const int32_t* rows, int cnt, int k,
-                                                       int Er, int E, uint8_t (*list)[kMaxRanks],
-                                                       int& n_out)
+__device__ __forceinline__ void route_tile_by_slot(const int32_t* rows, int cnt, int k, int Er,
+                                                   int E, uint8_t (*list)[kMaxRanks],
+                                                   uint64_t* s_mask, int32_t* s_n)
 {
-    constexpr int kBatch = 16;
     const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nwaves = blockDim.x / kWave;
     const int j = min(lane, k - 1);
-    uint64_t my_mask = 0;
-    int my_n = 0;
-    for (int b0 = 0; b0 < cnt; b0 += kBatch) {
-        int32_t ids[kBatch];
-#pragma unroll
-        for (int q = 0; q < kBatch; ++q)
-            ids[q] = rows[(int64_t)min(b0 + q, cnt - 1) * k + j];
-#pragma unroll
-        for (int q = 0; q < kBatch; ++q) {
-            const int tt = b0 + q;
-            if (tt >= cnt)
-                break;
-            const int32_t e = ids[q];
-            const bool valid = lane < k && (uint32_t)e < (uint32_t)E;
-            const int d = valid ? (int)((uint32_t)e / (uint32_t)Er) : -1;
-            uint64_t rem = __ballot(valid);
-            uint64_t mask = 0;
-            int n = 0;
-            while (rem) {
-                const int leader = __builtin_ctzll(rem);
-                const int dl = __builtin_amdgcn_readlane(d, leader);
-                rem &= ~__ballot(d == dl);
-                if constexpr (kList) {
-                    if (lane == 0)
-                        list[tt][n] = (uint8_t)dl;
-                }
-                mask |= 1ull << dl;
-                ++n;
+    for (int tt = wave; tt < cnt; tt += nwaves) {
+        const int32_t e = rows[(int64_t)tt * k + j];
+        const bool valid = lane < k && (uint32_t)e < (uint32_t)E;
+        const int d = valid ? (int)((uint32_t)e / (uint32_t)Er) : -1;
+        uint64_t rem = __ballot(valid);
+        uint64_t mask = 0;
+        int n = 0;
+        while (rem) {
+            const int leader = __builtin_ctzll(rem);
+            const int dl = __builtin_amdgcn_readlane(d, leader);
+            rem &= ~__ballot(d == dl);
+            if constexpr (kList) {
+                if (lane == 0)
+                    list[tt][n] = (uint8_t)dl;
             }
-            if (lane == tt) {
-                my_mask = mask;
-                my_n = n;
-            }
+            mask |= 1ull << dl;
+            ++n;
+        }
+        if (lane == 0) {
+            s_mask[tt] = mask;
+            s_n[tt] = n;
         }
     }
-    n_out = my_n;
-    return my_mask;
 }
 
 // ---------------------------------------------------------------------------
 // route: per-tile row counts for every destination rank.
 // ---------------------------------------------------------------------------
+// k <= 16: one wave per tile, one lane per token. k > 16: one block per tile,
+// its waves routing the tile's tokens one lane per top-k slot.
 template <int KB>
-__global__ __launch_bounds__(256) void ep_route_kernel(RouteArgs a, TileMap tm)
+__global__ __launch_bounds__(1024) void ep_route_kernel(RouteArgs a, TileMap tm)
 {
+    __shared__ uint64_t s_mask[kMaxTile];
+    __shared__ int32_t s_n[kMaxTile];
     const int lane = threadIdx.x & (kWave - 1);
-    const int g = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const int g = KB >= 32 ? (int)blockIdx.x : (int)(blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave);
     if (g >= tm.total_tiles)
-        return;  // whole waves only
+        return;  // whole waves only (one tile a block when k > 16)
     const int r = rank_of_tile(tm, g);
     const int t0 = (g - tm.tile_start[r]) * tm.tile_tokens;
     const int cnt = min(tm.tile_tokens, tm.ntok[r] - t0);
-    int n;
     uint64_t m;
-    if constexpr (KB >= 32)
-        m = route_tile_by_slot<false>(a.idx + ((int64_t)r * a.M + t0) * a.k, cnt, a.k, a.Er,
-                                      a.E, nullptr, n);
-    else
+    if constexpr (KB >= 32) {
+        route_tile_by_slot<false>(a.idx + ((int64_t)r * a.M + t0) * a.k, cnt, a.k, a.Er, a.E,
+                                  nullptr, s_mask, s_n);
+        __syncthreads();
+        if (threadIdx.x >= kWave)
+            return;
+        m = lane < cnt ? s_mask[lane] : 0;
+    } else {
+        int n;
         m = route_token<false, KB>(a.idx + ((int64_t)r * a.M + t0 + lane) * a.k, lane < cnt,
                                    a.k, a.Er, a.E, nullptr, n);
+    }
     int mine = 0;
     for (int d = 0; d < tm.W; ++d) {
         const uint64_t b = __ballot((m >> d) & 1);
@@ -338,13 +339,14 @@ struct CopyItem {
     uint32_t sc;
 };
 
-template <int VPL, int KB>
+template <int VPL, int KB, bool kStream>
 __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
 {
     __shared__ uint8_t s_list[kMaxTile][kMaxRanks];  // [token][i]: i-th distinct rank
     __shared__ uint8_t s_loc[kMaxTile][kMaxRanks];   // [token][d]: rows to d before it in the tile
     __shared__ int32_t s_n[kMaxTile];                // distinct ranks of the token
     __shared__ int32_t s_base[kMaxRanks];            // first slot of this tile on rank d
+    __shared__ uint64_t s_mask[KB >= 32 ? kMaxTile : 1];  // destination masks (k > 16)
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -424,7 +426,7 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
             for (int u = 0; u < VPL; ++u) {
                 const int vv = v0 + u * kWave + lane;
                 if (vv < vend)
-                    bstore16<kCopyStorePolicy>(v[u], rd, (uint32_t)vv * 16u);
+                    bstore16<Policy<kStream>::copy_store>(v[u], rd, (uint32_t)vv * 16u);
             }
         }
     };
@@ -434,7 +436,7 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
         for (int u = 0; u < VPL; ++u) {
             const int vv = v0 + u * kWave + lane;
             if (vv < vend)
-                v[u] = bload16<kCopyLoadPolicy>(rs, (uint32_t)vv * 16u);
+                v[u] = bload16<Policy<kStream>::copy_load>(rs, (uint32_t)vv * 16u);
         }
     };
     auto load_item = [&](int it, CopyItem<VPL>& I) {
@@ -454,18 +456,24 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
             store_meta(tok, I.e, I.wv, I.sc);
     };
     auto route_tile = [&]() {
-        if (wave != 0)
-            return;
-        const int32_t base = lane < tm.W ? a.tile_base[(int64_t)lane * a.tile_stride + g] : 0;
-        int n;
         uint64_t m;
-        if constexpr (KB >= 32)
-            m = route_tile_by_slot<true>(a.idx + ((int64_t)r * a.M + t0) * a.k, cnt, a.k, a.Er,
-                                         a.E, s_list, n);
-        else
+        if constexpr (KB >= 32) {
+            // every wave routes some of the tile's tokens, then wave 0 ranks them
+            route_tile_by_slot<true>(a.idx + ((int64_t)r * a.M + t0) * a.k, cnt, a.k, a.Er, a.E,
+                                     s_list, s_mask, s_n);
+            __syncthreads();
+            if (wave != 0)
+                return;
+            m = lane < cnt ? s_mask[lane] : 0;
+        } else {
+            if (wave != 0)
+                return;
+            int n;
             m = route_token<true, KB>(a.idx + ((int64_t)r * a.M + t0 + lane) * a.k, lane < cnt,
                                       a.k, a.Er, a.E, s_list[lane], n);
-        s_n[lane] = n;
+            s_n[lane] = n;
+        }
+        const int32_t base = lane < tm.W ? a.tile_base[(int64_t)lane * a.tile_stride + g] : 0;
         for (int d = 0; d < tm.W; ++d) {
             const bool has = (m >> d) & 1;
             const uint64_t b = __ballot(has);
@@ -559,7 +567,7 @@ __device__ __forceinline__ u32x4 narrow(const float (&f)[8])
 
 // G: contribution rows loaded before folding; U: 16-byte columns per lane in
 // flight.
-template <int G, int U, int DT>
+template <int G, int U, int DT, bool kStream>
 __global__ __launch_bounds__(1024) void ep_combine_kernel(CombineArgs a, TokenMap tk)
 {
     const int lane = threadIdx.x & (kWave - 1);
@@ -589,7 +597,7 @@ __global__ __launch_bounds__(1024) void ep_combine_kernel(CombineArgs a, TokenMa
                     for (int u = 0; u < U; ++u) {
                         const int v = v0 + u * kWave + lane;
                         if (v < vend)
-                            rows[u][q] = bload16<kCombineLoadPolicy>(ry, (uint32_t)v * 16u);
+                            rows[u][q] = bload16<Policy<kStream>::combine_load>(ry, (uint32_t)v * 16u);
                     }
                 }
             }
@@ -622,7 +630,7 @@ __global__ __launch_bounds__(1024) void ep_combine_kernel(CombineArgs a, TokenMa
                     for (int e = 0; e < 8; ++e)
                         acc[u][e] = 0.0f;
                 }
-                bstore16<kCombineStorePolicy>(narrow<DT>(acc[u]), rdst, (uint32_t)v * 16u);
+                bstore16<Policy<kStream>::combine_store>(narrow<DT>(acc[u]), rdst, (uint32_t)v * 16u);
             }
         }
     }
@@ -642,33 +650,44 @@ __global__ __launch_bounds__(1024) void ep_combine_kernel(CombineArgs a, TokenMa
 int topk_bucket(int k) { return k <= 4 ? 4 : k <= 8 ? 8 : k <= 16 ? 16 : k <= 32 ? 32 : 64; }
 
 template <int VPL, int KB>
-hipError_t copy_with(const CopyArgs& a, const TileMap& tm, dim3 grid, dim3 block, hipStream_t s)
+hipError_t copy_with(const CopyArgs& a, const TileMap& tm, dim3 grid, dim3 block, bool stream,
+                     hipStream_t s)
 {
-    hipLaunchKernelGGL((ep_copy_kernel<VPL, KB>), grid, block, 0, s, a, tm);
+    if (stream)
+        hipLaunchKernelGGL((ep_copy_kernel<VPL, KB, true>), grid, block, 0, s, a, tm);
+    else
+        hipLaunchKernelGGL((ep_copy_kernel<VPL, KB, false>), grid, block, 0, s, a, tm);
     return hipGetLastError();
 }
 
 template <int VPL>
 hipError_t copy_with_vpl(const CopyArgs& a, const TileMap& tm, dim3 grid, dim3 block,
-                         hipStream_t s)
+                         bool stream, hipStream_t s)
 {
     switch (topk_bucket(a.k)) {
-    case 4: return copy_with<VPL, 4>(a, tm, grid, block, s);
-    case 8: return copy_with<VPL, 8>(a, tm, grid, block, s);
-    case 16: return copy_with<VPL, 16>(a, tm, grid, block, s);
-    case 32: return copy_with<VPL, 32>(a, tm, grid, block, s);
-    default: return copy_with<VPL, 64>(a, tm, grid, block, s);
+    case 4: return copy_with<VPL, 4>(a, tm, grid, block, stream, s);
+    case 8: return copy_with<VPL, 8>(a, tm, grid, block, stream, s);
+    case 16: return copy_with<VPL, 16>(a, tm, grid, block, stream, s);
+    case 32: return copy_with<VPL, 32>(a, tm, grid, block, stream, s);
+    default: return copy_with<VPL, 64>(a, tm, grid, block, stream, s);
     }
 }
 
 template <int G, int U>
 hipError_t combine_with(const CombineArgs& a, const TokenMap& tk, int dtype, dim3 grid,
-                        dim3 block, hipStream_t s)
+                        dim3 block, bool stream, hipStream_t s)
 {
-    if (dtype == 0)
-        hipLaunchKernelGGL((ep_combine_kernel<G, U, 0>), grid, block, 0, s, a, tk);
-    else
-        hipLaunchKernelGGL((ep_combine_kernel<G, U, 1>), grid, block, 0, s, a, tk);
+    if (dtype == 0) {
+        if (stream)
+            hipLaunchKernelGGL((ep_combine_kernel<G, U, 0, true>), grid, block, 0, s, a, tk);
+        else
+            hipLaunchKernelGGL((ep_combine_kernel<G, U, 0, false>), grid, block, 0, s, a, tk);
+    } else {
+        if (stream)
+            hipLaunchKernelGGL((ep_combine_kernel<G, U, 1, true>), grid, block, 0, s, a, tk);
+        else
+            hipLaunchKernelGGL((ep_combine_kernel<G, U, 1, false>), grid, block, 0, s, a, tk);
+    }
     return hipGetLastError();
 }
 
@@ -678,15 +697,18 @@ hipError_t launch_route(const RouteArgs& a, const TileMap& tm, hipStream_t s)
 {
     if (tm.total_tiles == 0)
         return hipSuccess;
-    constexpr int kWaves = 4;
+    constexpr int kWaves = 4;  // k <= 16: tiles a block, one a wave
     const dim3 grid((tm.total_tiles + kWaves - 1) / kWaves);
     const dim3 block(kWaves * kWave);
+    // k > 16: one tile a block, one wave per token of the tile (up to 16)
+    const dim3 grid_tile(tm.total_tiles);
+    const dim3 block_tile(min(tm.tile_tokens, 16) * kWave);
     switch (topk_bucket(a.k)) {
     case 4: hipLaunchKernelGGL((ep_route_kernel<4>), grid, block, 0, s, a, tm); break;
     case 8: hipLaunchKernelGGL((ep_route_kernel<8>), grid, block, 0, s, a, tm); break;
     case 16: hipLaunchKernelGGL((ep_route_kernel<16>), grid, block, 0, s, a, tm); break;
-    case 32: hipLaunchKernelGGL((ep_route_kernel<32>), grid, block, 0, s, a, tm); break;
-    default: hipLaunchKernelGGL((ep_route_kernel<64>), grid, block, 0, s, a, tm); break;
+    case 32: hipLaunchKernelGGL((ep_route_kernel<32>), grid_tile, block_tile, 0, s, a, tm); break;
+    default: hipLaunchKernelGGL((ep_route_kernel<64>), grid_tile, block_tile, 0, s, a, tm); break;
     }
     return hipGetLastError();
 }
@@ -698,7 +720,7 @@ hipError_t launch_scan(const ScanArgs& a, int W, hipStream_t s)
 }
 
 hipError_t launch_copy(const CopyArgs& a, const TileMap& tm, int waves, int row_split,
-                       hipStream_t s)
+                       bool stream, hipStream_t s)
 {
     if (tm.total_tiles == 0)
         return hipSuccess;
@@ -706,28 +728,28 @@ hipError_t launch_copy(const CopyArgs& a, const TileMap& tm, int waves, int row_
     const dim3 block(waves * kWave);
     const int per_lane = (a.piece_vecs + kWave - 1) / kWave;
     if (per_lane <= 1)
-        return copy_with_vpl<1>(a, tm, grid, block, s);
+        return copy_with_vpl<1>(a, tm, grid, block, stream, s);
     if (per_lane <= 2)
-        return copy_with_vpl<2>(a, tm, grid, block, s);
+        return copy_with_vpl<2>(a, tm, grid, block, stream, s);
     if (per_lane <= 4)
-        return copy_with_vpl<4>(a, tm, grid, block, s);
-    return copy_with_vpl<8>(a, tm, grid, block, s);
+        return copy_with_vpl<4>(a, tm, grid, block, stream, s);
+    return copy_with_vpl<8>(a, tm, grid, block, stream, s);
 }
 
 hipError_t launch_combine(const CombineArgs& a, const TokenMap& tk, int dtype, int waves,
-                          int row_split, hipStream_t s)
+                          int row_split, bool stream, hipStream_t s)
 {
     if (tk.total == 0)
         return hipSuccess;
     const dim3 grid((tk.total + waves - 1) / waves, row_split);
     const dim3 block(waves * kWave);
     if (a.P <= 1)
-        return combine_with<1, 4>(a, tk, dtype, grid, block, s);
+        return combine_with<1, 4>(a, tk, dtype, grid, block, stream, s);
     if (a.P <= 2)
-        return combine_with<2, 4>(a, tk, dtype, grid, block, s);
+        return combine_with<2, 4>(a, tk, dtype, grid, block, stream, s);
     if (a.P <= 4)
-        return combine_with<4, kCombineColumns>(a, tk, dtype, grid, block, s);
-    return combine_with<kCombineGroup, kCombineColumns>(a, tk, dtype, grid, block, s);
+        return combine_with<4, kCombineColumns>(a, tk, dtype, grid, block, stream, s);
+    return combine_with<kCombineGroup, kCombineColumns>(a, tk, dtype, grid, block, stream, s);
 }
 
 }  // namespace ep

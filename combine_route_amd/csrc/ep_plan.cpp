@@ -42,6 +42,9 @@ int ok()
 }
 
 constexpr size_t kWorkspaceAlign = 256;
+// Upper bound of a call's payload rows (every token sent to min(W, k) ranks)
+// at which its moves still use the caches: the 256 MB MALL of an MI355X.
+constexpr int64_t kKeepBytes = 256ll << 20;
 constexpr size_t kPtrAlign = 16;
 constexpr int kTimerPool = 1024;
 
@@ -221,6 +224,9 @@ ep_launch_t auto_launch(const ep_plan* p, const int32_t* ntok)
     l.combine_row_split = (int)std::min<int64_t>(
         std::min<int64_t>(cmax_split, 65535),
         std::max<int64_t>(1, (kTargetBlocks + cblocks - 1) / cblocks));
+    // rows one call moves at most (every token sent to min(W, k) ranks)
+    const int64_t rows_bytes = N * (s.row_bytes + s.crow_bytes) * (1 + s.P);
+    l.cache_policy = rows_bytes <= kKeepBytes ? EP_CACHE_KEEP : EP_CACHE_STREAM;
     return l;
 }
 
@@ -237,6 +243,8 @@ ep_launch_t effective_launch(const ep_plan* p, const int32_t* ntok)
         l.combine_waves = p->launch.combine_waves;
     if (p->launch.combine_row_split > 0)
         l.combine_row_split = p->launch.combine_row_split;
+    if (p->launch.cache_policy > 0)
+        l.cache_policy = p->launch.cache_policy;
     return l;
 }
 
@@ -294,6 +302,9 @@ int check_launch(const ep_plan* p, const ep_launch_t* l)
         return fail(EP_ERR_ARG, "launch.dispatch_waves = %d: must be <= 16", l->dispatch_waves);
     if (l->combine_waves > 16)
         return fail(EP_ERR_ARG, "launch.combine_waves = %d: must be <= 16", l->combine_waves);
+    if (l->cache_policy < 0 || l->cache_policy > EP_CACHE_KEEP)
+        return fail(EP_ERR_ARG, "launch.cache_policy = %d: must be EP_CACHE_AUTO, "
+                    "EP_CACHE_STREAM or EP_CACHE_KEEP", l->cache_policy);
     if (l->dispatch_row_split > 65535 || l->combine_row_split > 65535)
         return fail(EP_ERR_ARG, "launch row splits must be <= 65535 (grid y limit)");
     if (l->dispatch_row_split > s.row_bytes / 16)
@@ -460,7 +471,8 @@ int ep_dispatch(ep_plan_t* p, const ep_dispatch_args_t* a, void* stream_ptr)
         e = timed(p, EP_KERNEL_SCAN, stream, [&] { return ep::launch_scan(sa, s.W, stream); });
     if (e == hipSuccess)
         e = timed(p, EP_KERNEL_COPY, stream, [&] {
-            return ep::launch_copy(ca, tm, l.dispatch_waves, row_split, stream);
+            return ep::launch_copy(ca, tm, l.dispatch_waves, row_split,
+                                   l.cache_policy == EP_CACHE_STREAM, stream);
         });
     p->launched = true;
     p->last_stream = stream;
@@ -520,7 +532,8 @@ int ep_combine(ep_plan_t* p, const ep_combine_args_t* a, void* stream_ptr)
     const int dtype = p->cfg.combine_dtype == EP_BF16 ? 0 : 1;
 
     const hipError_t e = timed(p, EP_KERNEL_COMBINE, stream, [&] {
-        return ep::launch_combine(ca, tk, dtype, l.combine_waves, row_split, stream);
+        return ep::launch_combine(ca, tk, dtype, l.combine_waves, row_split,
+                                  l.cache_policy == EP_CACHE_STREAM, stream);
     });
     p->launched = true;
     p->last_stream = stream;

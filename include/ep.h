@@ -209,13 +209,21 @@ const char *ep_last_error(void);
  *                        piece of the row: 1..row_bytes/16.
  *   combine_waves        wavefronts per combine block (a token each): 1..16.
  *   combine_row_split    pieces a combined row is split into: 1..H/8.
- * Geometry never changes results. */
+ *   cache_policy         EP_CACHE_STREAM: payload rows bypass the caches;
+ *                        EP_CACHE_KEEP: rows are cached (best when the call's
+ *                        rows fit in the 256 MB last-level cache, e.g. expert
+ *                        outputs just written). Automatic: keep when the
+ *                        call's rows (every token sent to min(W, k) ranks)
+ *                        fit in 256 MB, stream above.
+ * Geometry and cache policy never change results. */
+enum { EP_CACHE_AUTO = 0, EP_CACHE_STREAM = 1, EP_CACHE_KEEP = 2 };
 typedef struct ep_launch {
     int32_t tile_tokens;
     int32_t dispatch_waves;
     int32_t dispatch_row_split;
     int32_t combine_waves;
     int32_t combine_row_split;
+    int32_t cache_policy;
 } ep_launch_t;
 
 /* Override (launch != NULL) or reset to automatic (launch == NULL) the plan's

@@ -226,7 +226,8 @@ def test_launch_override_limits_and_auto_geometry(lib):
     assert auto["tile_tokens"] in (16, 32, 64)
     assert 1 <= auto["dispatch_row_split"] <= 7168 * 2 // 16
     for bad in (dict(tile_tokens=8), dict(dispatch_waves=17), dict(combine_waves=17),
-                dict(dispatch_row_split=7168 * 2 // 16 + 1), dict(combine_row_split=897)):
+                dict(dispatch_row_split=7168 * 2 // 16 + 1), dict(combine_row_split=897),
+                dict(cache_policy=3), dict(cache_policy=-1)):
         with pytest.raises(cra.EpError):
             cra.ep_plan_set_launch(plan, bad)
     cra.ep_plan_set_launch(plan, dict(tile_tokens=32, dispatch_waves=2))
@@ -236,6 +237,10 @@ def test_launch_override_limits_and_auto_geometry(lib):
     assert cra.ep_plan_get_launch(plan, [4096] * 8) == auto
     small = cra.ep_plan_get_launch(plan, [1] + [0] * 7)
     assert small["tile_tokens"] == 16
+    # rows of the full call far exceed the last-level cache: streaming moves;
+    # one token's rows fit: cached moves
+    assert auto["cache_policy"] == cra.EP_CACHE_STREAM
+    assert small["cache_policy"] == cra.EP_CACHE_KEEP
     with pytest.raises(cra.EpError):
         cra.ep_plan_get_launch(plan, [4097] + [0] * 7)
     lib.ep_plan_destroy(plan)

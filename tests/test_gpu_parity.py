@@ -173,6 +173,8 @@ def test_topk_and_world_sweep(W, k):
     dict(tile_tokens=16, dispatch_waves=16, combine_waves=16),
     dict(dispatch_row_split=3, combine_row_split=5),
     dict(dispatch_row_split=64, combine_row_split=64, dispatch_waves=2),
+    dict(cache_policy=cra.EP_CACHE_STREAM), dict(cache_policy=cra.EP_CACHE_KEEP),
+    dict(tile_tokens=64, dispatch_row_split=1, cache_policy=cra.EP_CACHE_STREAM),
 ], ids=str)
 def test_geometry_does_not_change_results(launch):
     wl = workloads.custom("geom_ep4_t300_h4096", 4, 300, 4096, 8, 256, "bf16", ragged=True,
