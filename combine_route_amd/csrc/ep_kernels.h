@@ -54,7 +54,10 @@ struct CopyArgs {
     int32_t* out_idx;            // [W][WM][k]
     float* out_w;                // [W][WM][k] or null
     uint32_t* out_sc;            // [W][WM][scale_dwords] or null
-    const int32_t* tile_base;    // [W][tile_stride]
+    const int32_t* tile_base;    // [W][tile_stride] (separate scan)
+    const int32_t* tile_counts;  // [W][tile_stride] (scan in the copy kernel)
+    int32_t* recv;               // [W] (scan in the copy kernel)
+    int32_t scan_in_copy;        // 1: each block sums the counts of the tiles before it
     int32_t* src_pos;            // [W][WM]
     int32_t* fwd;                // [W][M][P]
     int32_t row_vecs;            // 16-byte vectors per payload row

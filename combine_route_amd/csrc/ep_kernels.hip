@@ -455,6 +455,37 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
         if (meta && c == 0)
             store_meta(tok, I.e, I.wv, I.sc);
     };
+    // First slot of this tile on every destination: read from the scan, or,
+    // for calls of few tiles, summed here over the tiles before this one (an
+    // exact integer sum, the same in every block); block (0, 0) also writes
+    // the received-row counts. Spread over the waves, one destination each.
+    auto tile_bases = [&]() {
+        if (!a.scan_in_copy) {
+            if (wave == 0 && lane < tm.W)
+                s_base[lane] = a.tile_base[(int64_t)lane * a.tile_stride + g];
+            return;
+        }
+        const bool first = g == 0 && piece == 0;
+        for (int d = wave; d < tm.W; d += nwaves) {
+            const int32_t* col = a.tile_counts + (int64_t)d * a.tile_stride;
+            int32_t before = 0, all = 0;
+            for (int gg = lane; gg < (first ? tm.total_tiles : g); gg += kWave) {
+                const int32_t c = col[gg];
+                before += gg < g ? c : 0;
+                all += c;
+            }
+#pragma unroll
+            for (int off = kWave / 2; off > 0; off >>= 1) {
+                before += __shfl_xor(before, off);
+                all += __shfl_xor(all, off);
+            }
+            if (lane == 0) {
+                s_base[d] = before;
+                if (first)
+                    a.recv[d] = all;
+            }
+        }
+    };
     auto route_tile = [&]() {
         uint64_t m;
         if constexpr (KB >= 32) {
@@ -473,15 +504,12 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
                                       a.k, a.Er, a.E, s_list[lane], n);
             s_n[lane] = n;
         }
-        const int32_t base = lane < tm.W ? a.tile_base[(int64_t)lane * a.tile_stride + g] : 0;
         for (int d = 0; d < tm.W; ++d) {
             const bool has = (m >> d) & 1;
             const uint64_t b = __ballot(has);
             if (has)
                 s_loc[lane][d] = (uint8_t)lanes_below(b);
         }
-        if (lane < tm.W)
-            s_base[lane] = base;
     };
 
     if constexpr (VPL < 8) {
@@ -491,6 +519,7 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
         CopyItem<VPL> A, B;
         if (items > 0)
             load_item(0, A);
+        tile_bases();
         route_tile();
         __syncthreads();
         for (int it = 0; it < items; it += 2) {
@@ -507,6 +536,7 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
         // Large pieces (throughput): metadata first, then one chunk a wave in
         // flight, which keeps the register count, and so the waves resident
         // per SIMD, at its lowest.
+        tile_bases();
         route_tile();
         __syncthreads();
         if (meta) {

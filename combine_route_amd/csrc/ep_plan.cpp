@@ -45,6 +45,9 @@ constexpr size_t kWorkspaceAlign = 256;
 // Upper bound of a call's payload rows (every token sent to min(W, k) ranks)
 // at which its moves still use the caches: the 256 MB MALL of an MI355X.
 constexpr int64_t kKeepBytes = 256ll << 20;
+// Most routing tiles a call may have for the copy blocks to sum the tile
+// counts themselves instead of a separate scan launch.
+constexpr int kScanInCopyTiles = 256;
 constexpr size_t kPtrAlign = 16;
 constexpr int kTimerPool = 1024;
 
@@ -227,6 +230,9 @@ ep_launch_t auto_launch(const ep_plan* p, const int32_t* ntok)
     // rows one call moves at most (every token sent to min(W, k) ranks)
     const int64_t rows_bytes = N * (s.row_bytes + s.crow_bytes) * (1 + s.P);
     l.cache_policy = rows_bytes <= kKeepBytes ? EP_CACHE_KEEP : EP_CACHE_STREAM;
+    // few tiles: every copy block sums the counts before its tile itself
+    const int ntiles = tiles_for(ntok, s.W, l.tile_tokens);
+    l.scan = ntiles >= 1 && ntiles <= kScanInCopyTiles ? EP_SCAN_IN_COPY : EP_SCAN_KERNEL;
     return l;
 }
 
@@ -245,6 +251,8 @@ ep_launch_t effective_launch(const ep_plan* p, const int32_t* ntok)
         l.combine_row_split = p->launch.combine_row_split;
     if (p->launch.cache_policy > 0)
         l.cache_policy = p->launch.cache_policy;
+    if (p->launch.scan > 0)
+        l.scan = p->launch.scan;
     return l;
 }
 
@@ -302,6 +310,9 @@ int check_launch(const ep_plan* p, const ep_launch_t* l)
         return fail(EP_ERR_ARG, "launch.dispatch_waves = %d: must be <= 16", l->dispatch_waves);
     if (l->combine_waves > 16)
         return fail(EP_ERR_ARG, "launch.combine_waves = %d: must be <= 16", l->combine_waves);
+    if (l->scan < 0 || l->scan > EP_SCAN_IN_COPY)
+        return fail(EP_ERR_ARG, "launch.scan = %d: must be EP_SCAN_AUTO, EP_SCAN_KERNEL or "
+                    "EP_SCAN_IN_COPY", l->scan);
     if (l->cache_policy < 0 || l->cache_policy > EP_CACHE_KEEP)
         return fail(EP_ERR_ARG, "launch.cache_policy = %d: must be EP_CACHE_AUTO, "
                     "EP_CACHE_STREAM or EP_CACHE_KEEP", l->cache_policy);
@@ -452,6 +463,11 @@ int ep_dispatch(ep_plan_t* p, const ep_dispatch_args_t* a, void* stream_ptr)
     ca.out_w = a->out_weights;
     ca.out_sc = static_cast<uint32_t*>(a->out_scales);
     ca.tile_base = ws_base(p);
+    ca.tile_counts = ws_counts(p);
+    ca.recv = a->recv_num_token;
+    // a call without tiles launches no copy block: the scan kernel writes the
+    // (zero) receive counts then
+    ca.scan_in_copy = (l.scan == EP_SCAN_IN_COPY && tiles > 0) ? 1 : 0;
     ca.src_pos = ws_src_pos(p);
     ca.fwd = ws_fwd(p);
     ca.row_vecs = (int32_t)(s.row_bytes / 16);
@@ -467,7 +483,7 @@ int ep_dispatch(ep_plan_t* p, const ep_dispatch_args_t* a, void* stream_ptr)
     const int row_split = (int)((ca.row_vecs + ca.piece_vecs - 1) / ca.piece_vecs);
 
     hipError_t e = timed(p, EP_KERNEL_ROUTE, stream, [&] { return ep::launch_route(ra, tm, stream); });
-    if (e == hipSuccess)
+    if (e == hipSuccess && !ca.scan_in_copy)
         e = timed(p, EP_KERNEL_SCAN, stream, [&] { return ep::launch_scan(sa, s.W, stream); });
     if (e == hipSuccess)
         e = timed(p, EP_KERNEL_COPY, stream, [&] {

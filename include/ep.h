@@ -215,7 +215,13 @@ const char *ep_last_error(void);
  *                        outputs just written). Automatic: keep when the
  *                        call's rows (every token sent to min(W, k) ranks)
  *                        fit in 256 MB, stream above.
- * Geometry and cache policy never change results. */
+ *   scan                 EP_SCAN_KERNEL: a separate kernel turns the routing
+ *                        counts into receive slots; EP_SCAN_IN_COPY: each
+ *                        dispatch-copy block sums the counts before its tile
+ *                        (one launch fewer; automatic for calls of at most
+ *                        256 routing tiles).
+ * Geometry, cache policy and scan placement never change results. */
+enum { EP_SCAN_AUTO = 0, EP_SCAN_KERNEL = 1, EP_SCAN_IN_COPY = 2 };
 enum { EP_CACHE_AUTO = 0, EP_CACHE_STREAM = 1, EP_CACHE_KEEP = 2 };
 typedef struct ep_launch {
     int32_t tile_tokens;
@@ -224,6 +230,7 @@ typedef struct ep_launch {
     int32_t combine_waves;
     int32_t combine_row_split;
     int32_t cache_policy;
+    int32_t scan;
 } ep_launch_t;
 
 /* Override (launch != NULL) or reset to automatic (launch == NULL) the plan's

@@ -227,7 +227,7 @@ def test_launch_override_limits_and_auto_geometry(lib):
     assert 1 <= auto["dispatch_row_split"] <= 7168 * 2 // 16
     for bad in (dict(tile_tokens=8), dict(dispatch_waves=17), dict(combine_waves=17),
                 dict(dispatch_row_split=7168 * 2 // 16 + 1), dict(combine_row_split=897),
-                dict(cache_policy=3), dict(cache_policy=-1)):
+                dict(cache_policy=3), dict(cache_policy=-1), dict(scan=3), dict(scan=-2)):
         with pytest.raises(cra.EpError):
             cra.ep_plan_set_launch(plan, bad)
     cra.ep_plan_set_launch(plan, dict(tile_tokens=32, dispatch_waves=2))
@@ -241,6 +241,9 @@ def test_launch_override_limits_and_auto_geometry(lib):
     # one token's rows fit: cached moves
     assert auto["cache_policy"] == cra.EP_CACHE_STREAM
     assert small["cache_policy"] == cra.EP_CACHE_KEEP
+    # 512 routing tiles: a separate scan; one tile: the copy blocks scan
+    assert auto["scan"] == cra.EP_SCAN_KERNEL
+    assert small["scan"] == cra.EP_SCAN_IN_COPY
     with pytest.raises(cra.EpError):
         cra.ep_plan_get_launch(plan, [4097] + [0] * 7)
     lib.ep_plan_destroy(plan)
