@@ -25,7 +25,7 @@ EP_OK, EP_ERR_NULL, EP_ERR_ARG, EP_ERR_ALIGN, EP_ERR_SIZE, EP_ERR_STATE, EP_ERR_
     0, -1, -2, -3, -4, -5, -6)
 EP_KERNEL_ROUTE, EP_KERNEL_SCAN, EP_KERNEL_COPY, EP_KERNEL_COMBINE = 0, 1, 2, 3
 EP_CACHE_AUTO, EP_CACHE_STREAM, EP_CACHE_KEEP = 0, 1, 2
-EP_SCAN_AUTO, EP_SCAN_KERNEL, EP_SCAN_IN_COPY = 0, 1, 2
+EP_LAYOUT_AUTO, EP_LAYOUT_KERNELS, EP_LAYOUT_SCAN_IN_COPY, EP_LAYOUT_IN_COPY = 0, 1, 2, 3
 
 DTYPES = {"bf16": EP_BF16, "fp16": EP_FP16, "fp8": EP_FP8_E4M3}
 ELEM_BYTES = {EP_BF16: 2, EP_FP16: 2, EP_FP8_E4M3: 1}
@@ -55,7 +55,7 @@ class EpCombineArgs(ctypes.Structure):
 class EpLaunch(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "tile_tokens", "dispatch_waves", "dispatch_row_split", "combine_waves",
-        "combine_row_split", "cache_policy", "scan")]
+        "combine_row_split", "cache_policy", "layout")]
 
 
 class EpError(RuntimeError):

@@ -23,6 +23,16 @@ struct TileMap {
     int32_t ntok[kMaxRanks];             // T_r
 };
 
+// Where the dispatch copy gets each tile's first receive slot on every rank.
+enum LayoutMode : int32_t {
+    kLayoutFromScan = 0,   // tile_base, written by the scan kernel
+    kLayoutScanInCopy = 1, // summed by the copy block from tile_counts
+    kLayoutInCopy = 2,     // counted by the copy block from the ids of the whole call
+};
+
+// Most (tiles x ranks) counters the copy kernel keeps in LDS in kLayoutInCopy.
+constexpr int kLayoutInCopyCells = 4096;
+
 // Token counts as a prefix, for the combine's flat token index.
 struct TokenMap {
     int32_t W;
@@ -54,10 +64,10 @@ struct CopyArgs {
     int32_t* out_idx;            // [W][WM][k]
     float* out_w;                // [W][WM][k] or null
     uint32_t* out_sc;            // [W][WM][scale_dwords] or null
-    const int32_t* tile_base;    // [W][tile_stride] (separate scan)
-    const int32_t* tile_counts;  // [W][tile_stride] (scan in the copy kernel)
-    int32_t* recv;               // [W] (scan in the copy kernel)
-    int32_t scan_in_copy;        // 1: each block sums the counts of the tiles before it
+    const int32_t* tile_base;    // [W][tile_stride] (kLayoutFromScan)
+    const int32_t* tile_counts;  // [W][tile_stride] (kLayoutScanInCopy)
+    int32_t* recv;               // [W] (written here unless kLayoutFromScan)
+    int32_t layout;              // LayoutMode
     int32_t* src_pos;            // [W][WM]
     int32_t* fwd;                // [W][M][P]
     int32_t row_vecs;            // 16-byte vectors per payload row

@@ -339,7 +339,10 @@ struct CopyItem {
     uint32_t sc;
 };
 
-template <int VPL, int KB, bool kStream>
+// kInCopy: the block counts every tile of the call itself (kLayoutInCopy, k <=
+// 16 only); a separate instantiation, so the other calls do not carry its
+// registers.
+template <int VPL, int KB, bool kStream, bool kInCopy>
 __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
 {
     __shared__ uint8_t s_list[kMaxTile][kMaxRanks];  // [token][i]: i-th distinct rank
@@ -455,22 +458,54 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
         if (meta && c == 0)
             store_meta(tok, I.e, I.wv, I.sc);
     };
-    // First slot of this tile on every destination: read from the scan, or,
-    // for calls of few tiles, summed here over the tiles before this one (an
-    // exact integer sum, the same in every block); block (0, 0) also writes
-    // the received-row counts. Spread over the waves, one destination each.
+    // First slot of this tile on every destination. Large calls read it from
+    // the scan kernel. Calls of few tiles sum the per-tile counts before this
+    // tile here; calls of few tokens (k <= 16) first count every tile of the
+    // call here too, from the ids, into LDS (integer adds: the counts do not
+    // depend on the order they arrive in). These sums are the same in every
+    // block; block (0, 0) also writes the received-row counts. The sums are
+    // spread over the waves, one destination each.
     auto tile_bases = [&]() {
-        if (!a.scan_in_copy) {
+        if (a.layout == kLayoutFromScan) {
             if (wave == 0 && lane < tm.W)
                 s_base[lane] = a.tile_base[(int64_t)lane * a.tile_stride + g];
             return;
+        }
+        extern __shared__ int32_t s_cnt[];  // [total_tiles][W], kLayoutInCopy only
+        constexpr bool in_copy = kInCopy;
+        if constexpr (kInCopy) {
+            {
+                // a wave takes 64 / TT whole tiles a pass, a lane per token;
+                // a tile's count on d is the popcount of its lanes' ballot bits
+                const int TT = tm.tile_tokens;
+                const int per_wave = kWave / TT;
+                const int seg = lane / TT;
+                const uint64_t seg_bits = TT == 64 ? ~0ull : ((1ull << TT) - 1);
+                for (int g0 = wave * per_wave; g0 < tm.total_tiles; g0 += nwaves * per_wave) {
+                    const int tile = g0 + seg;
+                    int n;
+                    uint64_t m = 0;
+                    if (tile < tm.total_tiles) {
+                        const int rr = rank_of_tile(tm, tile);
+                        const int t = (tile - tm.tile_start[rr]) * TT + lane % TT;
+                        m = route_token<false, KB>(a.idx + ((int64_t)rr * a.M + t) * k,
+                                                   t < tm.ntok[rr], k, a.Er, a.E, nullptr, n);
+                    }
+                    for (int d = 0; d < tm.W; ++d) {
+                        const uint64_t b = __ballot((m >> d) & 1);
+                        if (lane % TT == 0 && tile < tm.total_tiles)
+                            s_cnt[tile * tm.W + d] = __popcll((b >> (seg * TT)) & seg_bits);
+                    }
+                }
+                __syncthreads();
+            }
         }
         const bool first = g == 0 && piece == 0;
         for (int d = wave; d < tm.W; d += nwaves) {
             const int32_t* col = a.tile_counts + (int64_t)d * a.tile_stride;
             int32_t before = 0, all = 0;
             for (int gg = lane; gg < (first ? tm.total_tiles : g); gg += kWave) {
-                const int32_t c = col[gg];
+                const int32_t c = in_copy ? s_cnt[gg * tm.W + d] : col[gg];
                 before += gg < g ? c : 0;
                 all += c;
             }
@@ -683,10 +718,24 @@ template <int VPL, int KB>
 hipError_t copy_with(const CopyArgs& a, const TileMap& tm, dim3 grid, dim3 block, bool stream,
                      hipStream_t s)
 {
+    if constexpr (KB <= 16) {
+        if (a.layout == kLayoutInCopy) {
+            const size_t lds = sizeof(int32_t) * tm.total_tiles * tm.W;
+            if (stream)
+                hipLaunchKernelGGL((ep_copy_kernel<VPL, KB, true, true>), grid, block, lds, s, a,
+                                   tm);
+            else
+                hipLaunchKernelGGL((ep_copy_kernel<VPL, KB, false, true>), grid, block, lds, s,
+                                   a, tm);
+            return hipGetLastError();
+        }
+    }
+    if (a.layout == kLayoutInCopy)
+        return hipErrorInvalidValue;  // k > 16: the host never selects it
     if (stream)
-        hipLaunchKernelGGL((ep_copy_kernel<VPL, KB, true>), grid, block, 0, s, a, tm);
+        hipLaunchKernelGGL((ep_copy_kernel<VPL, KB, true, false>), grid, block, 0, s, a, tm);
     else
-        hipLaunchKernelGGL((ep_copy_kernel<VPL, KB, false>), grid, block, 0, s, a, tm);
+        hipLaunchKernelGGL((ep_copy_kernel<VPL, KB, false, false>), grid, block, 0, s, a, tm);
     return hipGetLastError();
 }
 

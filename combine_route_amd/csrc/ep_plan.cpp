@@ -48,6 +48,11 @@ constexpr int64_t kKeepBytes = 256ll << 20;
 // Most routing tiles a call may have for the copy blocks to sum the tile
 // counts themselves instead of a separate scan launch.
 constexpr int kScanInCopyTiles = 256;
+// Most tokens a call may have for every copy block to count all its tiles
+// itself: each block reads every id of the call, which beats a routing
+// launch only for tiny calls (measured on MI355X: 2 x 16 tokens 17.5 -> 15.3
+// us a call; 8 x 128 tokens 33.9 -> 38.0 us).
+constexpr int64_t kLayoutInCopyTokens = 256;
 constexpr size_t kPtrAlign = 16;
 constexpr int kTimerPool = 1024;
 
@@ -184,6 +189,13 @@ int32_t* ws_src_pos(const ep_plan* p)
 }
 int32_t* ws_fwd(ep_plan* p) { return reinterpret_cast<int32_t*>(p->ws + p->s.off_fwd); }
 
+// Whether the copy blocks can count every tile of a call themselves: a lane
+// per token reads whole id rows (k <= 16), and the counters fit in LDS.
+bool layout_in_copy_fits(const Shape& s, int ntiles)
+{
+    return s.k <= 16 && (int64_t)ntiles * s.W <= ep::kLayoutInCopyCells;
+}
+
 int tiles_for(const int32_t* ntok, int W, int tt)
 {
     int n = 0;
@@ -230,9 +242,14 @@ ep_launch_t auto_launch(const ep_plan* p, const int32_t* ntok)
     // rows one call moves at most (every token sent to min(W, k) ranks)
     const int64_t rows_bytes = N * (s.row_bytes + s.crow_bytes) * (1 + s.P);
     l.cache_policy = rows_bytes <= kKeepBytes ? EP_CACHE_KEEP : EP_CACHE_STREAM;
-    // few tiles: every copy block sums the counts before its tile itself
+    // few tiles: the copy blocks work out the receive slots themselves
     const int ntiles = tiles_for(ntok, s.W, l.tile_tokens);
-    l.scan = ntiles >= 1 && ntiles <= kScanInCopyTiles ? EP_SCAN_IN_COPY : EP_SCAN_KERNEL;
+    if (ntiles >= 1 && N <= kLayoutInCopyTokens && layout_in_copy_fits(s, ntiles))
+        l.layout = EP_LAYOUT_IN_COPY;
+    else if (ntiles >= 1 && ntiles <= kScanInCopyTiles)
+        l.layout = EP_LAYOUT_SCAN_IN_COPY;
+    else
+        l.layout = EP_LAYOUT_KERNELS;
     return l;
 }
 
@@ -251,8 +268,8 @@ ep_launch_t effective_launch(const ep_plan* p, const int32_t* ntok)
         l.combine_row_split = p->launch.combine_row_split;
     if (p->launch.cache_policy > 0)
         l.cache_policy = p->launch.cache_policy;
-    if (p->launch.scan > 0)
-        l.scan = p->launch.scan;
+    if (p->launch.layout > 0)
+        l.layout = p->launch.layout;
     return l;
 }
 
@@ -310,9 +327,11 @@ int check_launch(const ep_plan* p, const ep_launch_t* l)
         return fail(EP_ERR_ARG, "launch.dispatch_waves = %d: must be <= 16", l->dispatch_waves);
     if (l->combine_waves > 16)
         return fail(EP_ERR_ARG, "launch.combine_waves = %d: must be <= 16", l->combine_waves);
-    if (l->scan < 0 || l->scan > EP_SCAN_IN_COPY)
-        return fail(EP_ERR_ARG, "launch.scan = %d: must be EP_SCAN_AUTO, EP_SCAN_KERNEL or "
-                    "EP_SCAN_IN_COPY", l->scan);
+    if (l->layout < 0 || l->layout > EP_LAYOUT_IN_COPY)
+        return fail(EP_ERR_ARG, "launch.layout = %d: must be an EP_LAYOUT_* value", l->layout);
+    if (l->layout == EP_LAYOUT_IN_COPY && s.k > 16)
+        return fail(EP_ERR_ARG, "launch.layout = EP_LAYOUT_IN_COPY needs num_experts_per_token "
+                    "<= 16 (it is %d)", s.k);
     if (l->cache_policy < 0 || l->cache_policy > EP_CACHE_KEEP)
         return fail(EP_ERR_ARG, "launch.cache_policy = %d: must be EP_CACHE_AUTO, "
                     "EP_CACHE_STREAM or EP_CACHE_KEEP", l->cache_policy);
@@ -436,6 +455,9 @@ int ep_dispatch(ep_plan_t* p, const ep_dispatch_args_t* a, void* stream_ptr)
     }
     tm.tile_start[s.W] = tiles;
     tm.total_tiles = tiles;
+    if (l.layout == EP_LAYOUT_IN_COPY && tiles > 0 && !layout_in_copy_fits(s, tiles))
+        return fail(EP_ERR_ARG, "launch.layout = EP_LAYOUT_IN_COPY: %d tiles x %d ranks exceed "
+                    "the %d counters of one block", tiles, s.W, ep::kLayoutInCopyCells);
 
     ep::RouteArgs ra;
     ra.idx = a->indices;
@@ -467,7 +489,10 @@ int ep_dispatch(ep_plan_t* p, const ep_dispatch_args_t* a, void* stream_ptr)
     ca.recv = a->recv_num_token;
     // a call without tiles launches no copy block: the scan kernel writes the
     // (zero) receive counts then
-    ca.scan_in_copy = (l.scan == EP_SCAN_IN_COPY && tiles > 0) ? 1 : 0;
+    ca.layout = tiles == 0                             ? ep::kLayoutFromScan
+                : l.layout == EP_LAYOUT_IN_COPY       ? ep::kLayoutInCopy
+                : l.layout == EP_LAYOUT_SCAN_IN_COPY  ? ep::kLayoutScanInCopy
+                                                       : ep::kLayoutFromScan;
     ca.src_pos = ws_src_pos(p);
     ca.fwd = ws_fwd(p);
     ca.row_vecs = (int32_t)(s.row_bytes / 16);
@@ -482,8 +507,10 @@ int ep_dispatch(ep_plan_t* p, const ep_dispatch_args_t* a, void* stream_ptr)
     ca.tile_stride = s.tile_stride;
     const int row_split = (int)((ca.row_vecs + ca.piece_vecs - 1) / ca.piece_vecs);
 
-    hipError_t e = timed(p, EP_KERNEL_ROUTE, stream, [&] { return ep::launch_route(ra, tm, stream); });
-    if (e == hipSuccess && !ca.scan_in_copy)
+    hipError_t e = hipSuccess;
+    if (ca.layout != ep::kLayoutInCopy)
+        e = timed(p, EP_KERNEL_ROUTE, stream, [&] { return ep::launch_route(ra, tm, stream); });
+    if (e == hipSuccess && ca.layout == ep::kLayoutFromScan)
         e = timed(p, EP_KERNEL_SCAN, stream, [&] { return ep::launch_scan(sa, s.W, stream); });
     if (e == hipSuccess)
         e = timed(p, EP_KERNEL_COPY, stream, [&] {

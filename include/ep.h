@@ -215,13 +215,27 @@ const char *ep_last_error(void);
  *                        outputs just written). Automatic: keep when the
  *                        call's rows (every token sent to min(W, k) ranks)
  *                        fit in 256 MB, stream above.
- *   scan                 EP_SCAN_KERNEL: a separate kernel turns the routing
- *                        counts into receive slots; EP_SCAN_IN_COPY: each
+ *   layout               where the receive slots are worked out:
+ *                        EP_LAYOUT_KERNELS: a routing kernel counts rows per
+ *                        tile and destination, a scan kernel turns the counts
+ *                        into first slots (large calls);
+ *                        EP_LAYOUT_SCAN_IN_COPY: routing kernel, then each
  *                        dispatch-copy block sums the counts before its tile
- *                        (one launch fewer; automatic for calls of at most
- *                        256 routing tiles).
- * Geometry, cache policy and scan placement never change results. */
-enum { EP_SCAN_AUTO = 0, EP_SCAN_KERNEL = 1, EP_SCAN_IN_COPY = 2 };
+ *                        (at most 256 tiles);
+ *                        EP_LAYOUT_IN_COPY: no extra kernel; each copy block
+ *                        counts every tile of the call itself (k <= 16 and
+ *                        tiles x world_size <= 4096; otherwise ep_dispatch
+ *                        fails with EP_ERR_ARG).
+ *                        Automatic: EP_LAYOUT_IN_COPY up to 256 tokens when
+ *                        it fits, else EP_LAYOUT_SCAN_IN_COPY up to 256 tiles,
+ *                        else EP_LAYOUT_KERNELS.
+ * Geometry, cache policy and layout placement never change results. */
+enum {
+    EP_LAYOUT_AUTO = 0,
+    EP_LAYOUT_KERNELS = 1,
+    EP_LAYOUT_SCAN_IN_COPY = 2,
+    EP_LAYOUT_IN_COPY = 3
+};
 enum { EP_CACHE_AUTO = 0, EP_CACHE_STREAM = 1, EP_CACHE_KEEP = 2 };
 typedef struct ep_launch {
     int32_t tile_tokens;
@@ -230,7 +244,7 @@ typedef struct ep_launch {
     int32_t combine_waves;
     int32_t combine_row_split;
     int32_t cache_policy;
-    int32_t scan;
+    int32_t layout;
 } ep_launch_t;
 
 /* Override (launch != NULL) or reset to automatic (launch == NULL) the plan's

@@ -227,7 +227,7 @@ def test_launch_override_limits_and_auto_geometry(lib):
     assert 1 <= auto["dispatch_row_split"] <= 7168 * 2 // 16
     for bad in (dict(tile_tokens=8), dict(dispatch_waves=17), dict(combine_waves=17),
                 dict(dispatch_row_split=7168 * 2 // 16 + 1), dict(combine_row_split=897),
-                dict(cache_policy=3), dict(cache_policy=-1), dict(scan=3), dict(scan=-2)):
+                dict(cache_policy=3), dict(cache_policy=-1), dict(layout=4), dict(layout=-2)):
         with pytest.raises(cra.EpError):
             cra.ep_plan_set_launch(plan, bad)
     cra.ep_plan_set_launch(plan, dict(tile_tokens=32, dispatch_waves=2))
@@ -241,11 +241,25 @@ def test_launch_override_limits_and_auto_geometry(lib):
     # one token's rows fit: cached moves
     assert auto["cache_policy"] == cra.EP_CACHE_STREAM
     assert small["cache_policy"] == cra.EP_CACHE_KEEP
-    # 512 routing tiles: a separate scan; one tile: the copy blocks scan
-    assert auto["scan"] == cra.EP_SCAN_KERNEL
-    assert small["scan"] == cra.EP_SCAN_IN_COPY
+    # 32768 tokens in 512 tiles: routing and scan kernels; one token: the copy
+    # blocks work out the layout alone
+    assert auto["layout"] == cra.EP_LAYOUT_KERNELS
+    assert small["layout"] == cra.EP_LAYOUT_IN_COPY
+    assert cra.ep_plan_get_launch(plan, [200, 56] + [0] * 6)["layout"] == cra.EP_LAYOUT_IN_COPY
+    assert cra.ep_plan_get_launch(plan, [200, 57] + [0] * 6)["layout"] == \
+        cra.EP_LAYOUT_SCAN_IN_COPY
+    assert cra.ep_plan_get_launch(plan, [4096, 1024] + [0] * 6)["layout"] == \
+        cra.EP_LAYOUT_KERNELS
     with pytest.raises(cra.EpError):
         cra.ep_plan_get_launch(plan, [4097] + [0] * 7)
+    lib.ep_plan_destroy(plan)
+    # k > 16: the copy blocks cannot route the whole call; few tiles: they scan
+    wl = workloads.WORKLOADS["ep4_ragged1024_h2048_fp16_k64"]
+    rc, plan = make_plan(lib, wl_config(wl))
+    got = cra.ep_plan_get_launch(plan, workloads.token_counts(wl))
+    assert got["layout"] == cra.EP_LAYOUT_SCAN_IN_COPY
+    with pytest.raises(cra.EpError):
+        cra.ep_plan_set_launch(plan, dict(layout=cra.EP_LAYOUT_IN_COPY))
     lib.ep_plan_destroy(plan)
 
 

@@ -175,9 +175,11 @@ def test_topk_and_world_sweep(W, k):
     dict(dispatch_row_split=64, combine_row_split=64, dispatch_waves=2),
     dict(cache_policy=cra.EP_CACHE_STREAM), dict(cache_policy=cra.EP_CACHE_KEEP),
     dict(tile_tokens=64, dispatch_row_split=1, cache_policy=cra.EP_CACHE_STREAM),
-    dict(scan=cra.EP_SCAN_KERNEL), dict(scan=cra.EP_SCAN_IN_COPY),
-    dict(scan=cra.EP_SCAN_IN_COPY, tile_tokens=64, dispatch_row_split=1),
-    dict(scan=cra.EP_SCAN_KERNEL, tile_tokens=16, dispatch_row_split=2),
+    dict(layout=cra.EP_LAYOUT_KERNELS), dict(layout=cra.EP_LAYOUT_SCAN_IN_COPY),
+    dict(layout=cra.EP_LAYOUT_IN_COPY),
+    dict(layout=cra.EP_LAYOUT_SCAN_IN_COPY, tile_tokens=64, dispatch_row_split=1),
+    dict(layout=cra.EP_LAYOUT_IN_COPY, tile_tokens=32, dispatch_row_split=3),
+    dict(layout=cra.EP_LAYOUT_KERNELS, tile_tokens=16, dispatch_row_split=2),
 ], ids=str)
 def test_geometry_does_not_change_results(launch):
     wl = workloads.custom("geom_ep4_t300_h4096", 4, 300, 4096, 8, 256, "bf16", ragged=True,
@@ -331,7 +333,7 @@ def test_kernel_timing_counts_launches():
     wl = workloads.WORKLOADS["ep2_t16_h256_bf16_k2"]
     inp = workloads.make_inputs(wl)
     op = cra.EpDispatchCombineOp(config_of(wl))
-    op.set_launch(dict(scan=cra.EP_SCAN_KERNEL))
+    op.set_launch(dict(layout=cra.EP_LAYOUT_KERNELS))
     cra.ep_plan_set_timing(op.plan, True)
     for _ in range(3):
         gpu_dispatch(op, inp)
@@ -340,22 +342,41 @@ def test_kernel_timing_counts_launches():
     for kern in range(4):
         c, ms = cra.ep_plan_kernel_time(op.plan, kern)
         assert c == 3 and ms > 0.0
-    # with the scan in the copy kernel, no scan launch is timed
-    op.set_launch(dict(scan=cra.EP_SCAN_IN_COPY))
+    # with the scan in the copy kernel, no scan launch is timed; with the
+    # whole layout there, no routing launch either
+    op.set_launch(dict(layout=cra.EP_LAYOUT_SCAN_IN_COPY))
+    gpu_dispatch(op, inp)
+    op.set_launch(dict(layout=cra.EP_LAYOUT_IN_COPY))
     gpu_dispatch(op, inp)
     torch.cuda.synchronize()
+    assert cra.ep_plan_kernel_time(op.plan, cra.EP_KERNEL_ROUTE)[0] == 4
     assert cra.ep_plan_kernel_time(op.plan, cra.EP_KERNEL_SCAN)[0] == 3
-    assert cra.ep_plan_kernel_time(op.plan, cra.EP_KERNEL_COPY)[0] == 4
+    assert cra.ep_plan_kernel_time(op.plan, cra.EP_KERNEL_COPY)[0] == 5
     cra.ep_plan_set_timing(op.plan, False)
     op.close()
 
 
-@pytest.mark.parametrize("scan", [1, 2], ids=["scan_kernel", "scan_in_copy"])
-def test_scan_placement_many_tiles(scan):
-    """Both scan placements over more tiles than the automatic limit."""
-    wl = workloads.custom("scan_ep8_t700_h256_k8", 8, 700, 256, 8, 64, "bf16", ragged=True,
+@pytest.mark.parametrize("layout", [1, 2, 3], ids=["kernels", "scan_in_copy", "in_copy"])
+def test_layout_placement_many_tiles(layout):
+    """Every layout placement, over more tiles than the automatic limits."""
+    wl = workloads.custom("layout_ep8_t700_h256_k8", 8, 700, 256, 8, 64, "bf16", ragged=True,
                           seed_index=408)
-    run_case(wl, launch=dict(tile_tokens=16, scan=scan))
+    run_case(wl, launch=dict(tile_tokens=16 if layout != 3 else 32, layout=layout))
+
+
+def test_layout_in_copy_rejects_what_does_not_fit():
+    wl = workloads.custom("layout_k32", 4, 64, 256, 32, 64, "bf16", seed_index=409)
+    op = cra.EpDispatchCombineOp(config_of(wl))
+    with pytest.raises(cra.EpError):
+        op.set_launch(dict(layout=cra.EP_LAYOUT_IN_COPY))  # k > 16
+    op.close()
+    wl = workloads.custom("layout_many_tiles", 64, 128, 256, 8, 128, "bf16", seed_index=410)
+    op = cra.EpDispatchCombineOp(config_of(wl))
+    op.set_launch(dict(layout=cra.EP_LAYOUT_IN_COPY, tile_tokens=16))  # 512 tiles x 64 ranks
+    inp = workloads.make_inputs(wl)
+    with pytest.raises(cra.EpError):
+        gpu_dispatch(op, inp)
+    op.close()
 
 
 def test_binding_rejects_small_or_host_tensors():
