@@ -299,6 +299,17 @@ def run(args):
         end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
+    # host time to issue K steps (no GPU wait), after a synchronised start:
+    # when it approaches ms_per_step the host, not the GPU, sets the pace
+    torch.cuda.synchronize()
+    host_t0 = time.perf_counter()
+    for _ in range(args.steps):
+        if args.graph:
+            graph.replay()
+        else:
+            step()
+    host_us = (time.perf_counter() - host_t0) / args.steps * 1e6
+    torch.cuda.synchronize()
     # -- the same K steps again with every kernel bracketed by HIP events on
     # its stream (the library records them), for per-kernel durations; the
     # records add small gaps between kernels, so this pass is not the value
@@ -340,6 +351,7 @@ def run(args):
                    "launches": "graph replay" if args.graph else "eager",
                    "launch": cra.ep_plan_get_launch(op.plan, ntok)},
         "us_per_call": round(ms_per_step * 1e3, 2),
+        "host_issue_us_per_call": round(host_us, 2),
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "payload_bytes_per_call": payload_bytes,
         "received_rows": int(recv.sum()),

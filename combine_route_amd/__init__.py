@@ -141,8 +141,14 @@ def _dev(t: Optional[torch.Tensor], name: str, nbytes: int):
     return t.data_ptr()
 
 
-def _stream(stream) -> Optional[int]:
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(stream, device_index: Optional[int] = None) -> Optional[int]:
+    """hipStream_t handle: the given stream, else torch's current stream."""
     if stream is None:
+        if _raw_stream is not None and device_index is not None:
+            return _raw_stream(device_index)
         return torch.cuda.current_stream().cuda_stream
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
@@ -171,15 +177,14 @@ def _sizes(cfg: EpConfig):
     return W, M, k, row, crow, srow
 
 
-def ep_dispatch(plan: int, cfg: EpConfig, num_tokens: Sequence[int], x, indices, weights,
-                scales, out_x, out_indices, out_weights, out_scales, recv_num_token,
-                stream=None) -> None:
-    """ep_dispatch(); tensors as in include/ep.h, sizes checked against cfg."""
+def _dispatch_args(cfg: EpConfig, num_tokens: Sequence[int], x, indices, weights, scales, out_x,
+                   out_indices, out_weights, out_scales, recv_num_token):
+    """Checked ep_dispatch_args_t, and the ctypes array it points into."""
     W, M, k, row, _, srow = _sizes(cfg)
     WM = W * M
-    nt = (ctypes.c_int32 * W)(*[int(v) for v in num_tokens])
     if len(num_tokens) != W:
         raise ValueError(f"num_tokens has {len(num_tokens)} entries; world_size is {W}")
+    nt = (ctypes.c_int32 * W)(*[int(v) for v in num_tokens])
     a = EpDispatchArgs(
         ctypes.cast(nt, ctypes.c_void_p),
         _dev(x, "x", W * M * row), _dev(indices, "indices", W * M * k * 4),
@@ -188,16 +193,44 @@ def ep_dispatch(plan: int, cfg: EpConfig, num_tokens: Sequence[int], x, indices,
         _dev(out_weights, "out_weights", W * WM * k * 4),
         _dev(out_scales, "out_scales", W * WM * srow),
         _dev(recv_num_token, "recv_num_token", W * 4))
+    return a, nt
+
+
+def _combine_args(cfg: EpConfig, y, y_weights, out, out_weights):
+    W, M, k, _, crow, _ = _sizes(cfg)
+    WM = W * M
+    return EpCombineArgs(_dev(y, "y", W * WM * crow), _dev(y_weights, "y_weights", W * WM * k * 4),
+                         _dev(out, "out", W * M * crow),
+                         _dev(out_weights, "out_weights", W * M * k * 4))
+
+
+def ep_dispatch(plan: int, cfg: EpConfig, num_tokens: Sequence[int], x, indices, weights,
+                scales, out_x, out_indices, out_weights, out_scales, recv_num_token,
+                stream=None) -> None:
+    """ep_dispatch(); tensors as in include/ep.h, sizes checked against cfg."""
+    a, nt = _dispatch_args(cfg, num_tokens, x, indices, weights, scales, out_x, out_indices,
+                           out_weights, out_scales, recv_num_token)
     _check("ep_dispatch", load().ep_dispatch(plan, ctypes.byref(a), _stream(stream)))
 
 
 def ep_combine(plan: int, cfg: EpConfig, y, y_weights, out, out_weights, stream=None) -> None:
     """ep_combine(); tensors as in include/ep.h, sizes checked against cfg."""
-    W, M, k, _, crow, _ = _sizes(cfg)
-    WM = W * M
-    a = EpCombineArgs(_dev(y, "y", W * WM * crow), _dev(y_weights, "y_weights", W * WM * k * 4),
-                      _dev(out, "out", W * M * crow), _dev(out_weights, "out_weights", W * M * k * 4))
+    a = _combine_args(cfg, y, y_weights, out, out_weights)
     _check("ep_combine", load().ep_combine(plan, ctypes.byref(a), _stream(stream)))
+
+
+def _same_tensors(held, given):
+    """The very same tensor objects as before, still over the same memory."""
+    if len(held) != len(given):
+        return False
+    for (h, ptr), g in zip(held, given):
+        if h is not g or (g is not None and g.data_ptr() != ptr):
+            return False
+    return True
+
+
+def _hold(tensors):
+    return tuple((t, None if t is None else t.data_ptr()) for t in tensors)
 
 
 def ep_get_src_token_pos(plan: int, rank: int) -> int:
@@ -264,17 +297,40 @@ class EpDispatchCombineOp:
         self.plan = ep_plan_create(cfg, self.workspace)
         self._src_pos_off = [ep_get_src_token_pos(self.plan, r) - self.workspace.data_ptr()
                              for r in range(W)]
+        # Checked argument structs of the last call, reused while the same
+        # tensor objects (over the same memory) and token counts come back:
+        # the per-tensor checks cost more host time than a small call's GPU
+        # work. Holding the tensors keeps their memory alive meanwhile.
+        self._dcache = None
+        self._ccache = None
+        self._lib = load()
+        self._dev_index = dev.index if dev.index is not None else torch.cuda.current_device()
 
     def dispatch(self, num_tokens, x, indices, weights=None, scales=None, stream=None):
-        ep_dispatch(self.plan, self.cfg, num_tokens, x, indices, weights, scales, self.out_x,
-                    self.out_indices, self.out_weights if weights is not None else None,
-                    self.out_scales if scales is not None else None, self.recv_num_token, stream)
+        given = (x, indices, weights, scales)
+        nt = tuple(num_tokens)
+        c = self._dcache
+        if c is None or c[1] != nt or not _same_tensors(c[0], given):
+            a, arr = _dispatch_args(self.cfg, nt, x, indices, weights, scales, self.out_x,
+                                    self.out_indices,
+                                    self.out_weights if weights is not None else None,
+                                    self.out_scales if scales is not None else None,
+                                    self.recv_num_token)
+            c = self._dcache = (_hold(given), nt, a, arr)
+        _check("ep_dispatch", self._lib.ep_dispatch(self.plan, ctypes.byref(c[2]),
+                                                    _stream(stream, self._dev_index)))
         return (self.out_x, self.out_weights, self.out_scales, self.out_indices,
                 self.recv_num_token)
 
     def combine(self, y, y_weights=None, stream=None):
-        ep_combine(self.plan, self.cfg, y, y_weights, self.combine_out,
-                   self.combine_weights if y_weights is not None else None, stream)
+        given = (y, y_weights)
+        c = self._ccache
+        if c is None or not _same_tensors(c[0], given):
+            a = _combine_args(self.cfg, y, y_weights, self.combine_out,
+                              self.combine_weights if y_weights is not None else None)
+            c = self._ccache = (_hold(given), a)
+        _check("ep_combine", self._lib.ep_combine(self.plan, ctypes.byref(c[1]),
+                                                  _stream(stream, self._dev_index)))
         return self.combine_out, (self.combine_weights if y_weights is not None else None)
 
     def src_token_pos(self, rank: int) -> torch.Tensor:
@@ -287,6 +343,7 @@ class EpDispatchCombineOp:
         ep_plan_set_launch(self.plan, launch)
 
     def close(self):
+        self._dcache = self._ccache = None
         if self.plan:
             ep_plan_destroy(self.plan)
             self.plan = None

@@ -6,23 +6,26 @@
 // routing metadata to it and records the way back; combine gathers each
 // token's rows back, sums them in FP32 and casts to BF16/FP16.
 //
-// Four kernels, all enqueued on the caller's stream, none waiting on another
-// block or on a flag:
-//   route    one wave per routing tile (16..64 tokens of one rank, one token a
-//            lane): each token's destination mask, then one 64-lane ballot per
-//            destination rank gives the tile's per-rank row counts.
-//   scan     one block per destination rank: exclusive prefix sum of the
-//            tile counts in (source rank, tile) order -> first receive slot of
-//            every tile on every rank, and the rank's received-row count.
-//            Together with the in-tile ballot prefix this is a counting sort:
-//            rows on a rank are ordered by (source rank, source token), with
-//            no atomic deciding any position.
-//   copy     one block per (tile, row piece): wave 0 routes the tile again
-//            (masks, ordered rank lists, ballot prefixes into LDS); then every
-//            wave takes tokens, loads its piece of the payload row into
-//            registers once (16 B a lane) and stores it to each destination
-//            row; blocks of piece 0 also write the id, weight and scale rows,
-//            src_pos and the forward map.
+// Kernels, all enqueued on the caller's stream, none waiting on another block
+// or on a flag:
+//   route    per routing tile (16..64 consecutive tokens of one rank) and
+//            destination rank, the number of the tile's tokens that go there:
+//            one 64-lane ballot per destination over the tokens' masks. For
+//            k <= 16 one lane holds one token; for k > 16 the waves of a block
+//            share the tile's tokens, one lane per top-k slot.
+//   scan     one block per destination rank: exclusive prefix sum of the tile
+//            counts in (source rank, tile) order -> first receive slot of every
+//            tile on every rank, and the rank's received-row count. With the
+//            in-tile ballot prefix this is a counting sort: rows on a rank are
+//            ordered by (source rank, source token), and no atomic decides any
+//            position. Calls of few tiles fold the scan into the copy kernel,
+//            and tiny calls the counting too (LayoutMode).
+//   copy     one block per (tile, row piece): routes its tile again (masks,
+//            ordered rank lists and ballot prefixes into LDS), then every wave
+//            loads a token's piece of the payload row into registers once (16 B
+//            a lane) and stores it to each destination row; piece-0 blocks
+//            also write the id, weight and scale rows, src_pos and the forward
+//            map.
 //   combine  one wave per (token, row piece): the token's forward-map entries
 //            (at most min(W, k), one a lane) become scalar row numbers; for
 //            each 16-byte column every contribution row is loaded before any
@@ -41,6 +44,15 @@
 
 #include "ep_kernels.h"
 
+namespace ep {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxTile = 64;
+
 // Cache policy of the row moves, as gfx950 buffer-instruction bits (1 = sc0,
 // 2 = nt, 16 = sc1). Streaming calls (footprint well past the 256 MB MALL)
 // touch every payload row once, so loads stream past the caches (nt); the
@@ -51,27 +63,20 @@
 // us. Calls that fit in the MALL use plain (cache-allocating) moves: rows an
 // expert has just written are still there, and 8 ranks x 128 fp8 tokens runs
 // ~10% faster that way.
-template <bool kStream> struct Policy {
+template <bool kStream>
+struct Policy {
     static constexpr int copy_load = kStream ? 2 : 0;
     static constexpr int copy_store = 0;
     static constexpr int combine_load = kStream ? 2 : 0;
     static constexpr int combine_store = kStream ? 2 : 0;
 };
+
 // The combine loads up to kCombineGroup contribution rows, kCombineColumns
 // 16-byte columns each, before folding (8 x 2 measured best: smaller groups
 // split a top-8 token's rows into two dependent rounds, larger column counts
 // cost occupancy).
 constexpr int kCombineGroup = 8;
 constexpr int kCombineColumns = 2;
-
-namespace ep {
-namespace {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-constexpr int kMaxTile = 64;
 
 // Number of lanes below this one whose bit is set in b.
 __device__ __forceinline__ int lanes_below(uint64_t b)
@@ -240,7 +245,8 @@ __global__ __launch_bounds__(1024) void ep_route_kernel(RouteArgs a, TileMap tm)
     __shared__ uint64_t s_mask[kMaxTile];
     __shared__ int32_t s_n[kMaxTile];
     const int lane = threadIdx.x & (kWave - 1);
-    const int g = KB >= 32 ? (int)blockIdx.x : (int)(blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave);
+    const int g = KB >= 32 ? (int)blockIdx.x
+                           : (int)(blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave);
     if (g >= tm.total_tiles)
         return;  // whole waves only (one tile a block when k > 16)
     const int r = rank_of_tile(tm, g);
@@ -471,41 +477,38 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
                 s_base[lane] = a.tile_base[(int64_t)lane * a.tile_stride + g];
             return;
         }
-        extern __shared__ int32_t s_cnt[];  // [total_tiles][W], kLayoutInCopy only
-        constexpr bool in_copy = kInCopy;
+        extern __shared__ int32_t s_cnt[];  // [total_tiles][W], kInCopy only
         if constexpr (kInCopy) {
-            {
-                // a wave takes 64 / TT whole tiles a pass, a lane per token;
-                // a tile's count on d is the popcount of its lanes' ballot bits
-                const int TT = tm.tile_tokens;
-                const int per_wave = kWave / TT;
-                const int seg = lane / TT;
-                const uint64_t seg_bits = TT == 64 ? ~0ull : ((1ull << TT) - 1);
-                for (int g0 = wave * per_wave; g0 < tm.total_tiles; g0 += nwaves * per_wave) {
-                    const int tile = g0 + seg;
-                    int n;
-                    uint64_t m = 0;
-                    if (tile < tm.total_tiles) {
-                        const int rr = rank_of_tile(tm, tile);
-                        const int t = (tile - tm.tile_start[rr]) * TT + lane % TT;
-                        m = route_token<false, KB>(a.idx + ((int64_t)rr * a.M + t) * k,
-                                                   t < tm.ntok[rr], k, a.Er, a.E, nullptr, n);
-                    }
-                    for (int d = 0; d < tm.W; ++d) {
-                        const uint64_t b = __ballot((m >> d) & 1);
-                        if (lane % TT == 0 && tile < tm.total_tiles)
-                            s_cnt[tile * tm.W + d] = __popcll((b >> (seg * TT)) & seg_bits);
-                    }
+            // a wave takes 64 / TT whole tiles a pass, a lane per token; a
+            // tile's count on d is the popcount of its lanes' ballot bits
+            const int TT = tm.tile_tokens;
+            const int per_wave = kWave / TT;
+            const int seg = lane / TT;
+            const uint64_t seg_bits = TT == 64 ? ~0ull : ((1ull << TT) - 1);
+            for (int g0 = wave * per_wave; g0 < tm.total_tiles; g0 += nwaves * per_wave) {
+                const int tile = g0 + seg;
+                int n;
+                uint64_t m = 0;
+                if (tile < tm.total_tiles) {
+                    const int rr = rank_of_tile(tm, tile);
+                    const int t = (tile - tm.tile_start[rr]) * TT + lane % TT;
+                    m = route_token<false, KB>(a.idx + ((int64_t)rr * a.M + t) * k,
+                                               t < tm.ntok[rr], k, a.Er, a.E, nullptr, n);
                 }
-                __syncthreads();
+                for (int d = 0; d < tm.W; ++d) {
+                    const uint64_t b = __ballot((m >> d) & 1);
+                    if (lane % TT == 0 && tile < tm.total_tiles)
+                        s_cnt[tile * tm.W + d] = __popcll((b >> (seg * TT)) & seg_bits);
+                }
             }
+            __syncthreads();
         }
         const bool first = g == 0 && piece == 0;
         for (int d = wave; d < tm.W; d += nwaves) {
             const int32_t* col = a.tile_counts + (int64_t)d * a.tile_stride;
             int32_t before = 0, all = 0;
             for (int gg = lane; gg < (first ? tm.total_tiles : g); gg += kWave) {
-                const int32_t c = in_copy ? s_cnt[gg * tm.W + d] : col[gg];
+                const int32_t c = kInCopy ? s_cnt[gg * tm.W + d] : col[gg];
                 before += gg < g ? c : 0;
                 all += c;
             }
@@ -662,7 +665,8 @@ __global__ __launch_bounds__(1024) void ep_combine_kernel(CombineArgs a, TokenMa
                     for (int u = 0; u < U; ++u) {
                         const int v = v0 + u * kWave + lane;
                         if (v < vend)
-                            rows[u][q] = bload16<Policy<kStream>::combine_load>(ry, (uint32_t)v * 16u);
+                            rows[u][q] = bload16<Policy<kStream>::combine_load>(
+                                ry, (uint32_t)v * 16u);
                     }
                 }
             }
@@ -695,7 +699,8 @@ __global__ __launch_bounds__(1024) void ep_combine_kernel(CombineArgs a, TokenMa
                     for (int e = 0; e < 8; ++e)
                         acc[u][e] = 0.0f;
                 }
-                bstore16<Policy<kStream>::combine_store>(narrow<DT>(acc[u]), rdst, (uint32_t)v * 16u);
+                bstore16<Policy<kStream>::combine_store>(narrow<DT>(acc[u]), rdst,
+                                                         (uint32_t)v * 16u);
             }
         }
     }

@@ -434,7 +434,8 @@ int ep_dispatch(ep_plan_t* p, const ep_dispatch_args_t* a, void* stream_ptr)
         return fail(EP_ERR_ALIGN, "args.weights / args.out_weights are not 16-byte aligned");
     if (s.scale_bytes > 0) {
         if (!a->scales || !a->out_scales)
-            return fail(EP_ERR_NULL, "args.scales and args.out_scales are required (scale_dim = %d)",
+            return fail(EP_ERR_NULL,
+                        "args.scales and args.out_scales are required (scale_dim = %d)",
                         p->cfg.scale_dim);
         if (!aligned(a->scales, kPtrAlign) || !aligned(a->out_scales, kPtrAlign))
             return fail(EP_ERR_ALIGN, "args.scales / args.out_scales are not 16-byte aligned");
@@ -541,7 +542,8 @@ int ep_combine(ep_plan_t* p, const ep_combine_args_t* a, void* stream_ptr)
     if (!aligned(a->y, kPtrAlign) || !aligned(a->out, kPtrAlign))
         return fail(EP_ERR_ALIGN, "args.y / args.out are not 16-byte aligned");
     if ((a->y_weights == nullptr) != (a->out_weights == nullptr))
-        return fail(EP_ERR_ARG, "args.y_weights and args.out_weights must both be set or both NULL");
+        return fail(EP_ERR_ARG,
+                    "args.y_weights and args.out_weights must both be set or both NULL");
     if (a->y_weights && (!aligned(a->y_weights, 4) || !aligned(a->out_weights, 4)))
         return fail(EP_ERR_ALIGN, "args.y_weights / args.out_weights are not 4-byte aligned");
     if (!p->dispatched)

@@ -379,6 +379,32 @@ def test_layout_in_copy_rejects_what_does_not_fit():
     op.close()
 
 
+def test_argument_cache_follows_new_tensors_and_counts():
+    """The op reuses checked arguments only for the same tensors and counts."""
+    wl = workloads.custom("cache_ep4_t64_h512", 4, 64, 512, 8, 64, "bf16", seed_index=411)
+    op = cra.EpDispatchCombineOp(config_of(wl))
+    _say("[case] argument cache")
+    for seed, ntok in ((None, [64, 64, 64, 64]), (7, [64, 64, 64, 64]), (7, [3, 0, 64, 17])):
+        inp = workloads.make_inputs(wl, seed)
+        inp["ntok"] = ntok
+        ref = oracle_dispatch(wl, inp)
+        gpu_dispatch(op, inp)  # new tensor objects every time
+        torch.cuda.synchronize()
+        compare_dispatch(wl, op, ref, f"seed {seed} ntok {ntok}")
+    # same tensor objects, new contents: the cached arguments still apply
+    x, idx, w = inp["x"].cuda(), inp["idx"].cuda(), inp["w"].cuda()
+    for seed in (8, 9):
+        nxt = workloads.make_inputs(wl, seed)
+        nxt["ntok"] = ntok
+        x.copy_(nxt["x"])
+        idx.copy_(nxt["idx"])
+        w.copy_(nxt["w"])
+        op.dispatch(ntok, x, idx, w)
+        torch.cuda.synchronize()
+        compare_dispatch(wl, op, oracle_dispatch(wl, nxt), f"in place seed {seed}")
+    op.close()
+
+
 def test_binding_rejects_small_or_host_tensors():
     wl = workloads.WORKLOADS["ep2_t16_h256_bf16_k2"]
     op = cra.EpDispatchCombineOp(config_of(wl))
