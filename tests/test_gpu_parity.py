@@ -414,3 +414,59 @@ def test_binding_rejects_small_or_host_tensors():
     with pytest.raises(ValueError):
         op.dispatch(inp["ntok"], inp["x"].cuda()[:, :8], inp["idx"].cuda(), inp["w"].cuda())
     op.close()
+
+
+def _random_case(seed):
+    """A seeded random configuration and launch override, small enough for the
+    oracle to finish in well under a second."""
+    rng = np.random.default_rng(10_000 + seed)
+    W = int(rng.choice([1, 2, 3, 5, 8, 13, 16, 32, 64]))
+    k = int(rng.integers(1, 65))
+    Er = int(rng.integers(max(1, -(-k // W)), max(1, -(-k // W)) + 6))
+    M = int(rng.integers(1, 97))
+    dd = str(rng.choice(["bf16", "fp16", "fp8"]))
+    cd = "fp16" if dd == "fp16" else str(rng.choice(["bf16", "fp16"]))
+    H = 16 * int(rng.integers(1, 49))
+    S, sts = 0, 4
+    if dd == "fp8" and rng.random() < 0.7:
+        sts = int(rng.choice([1, 2, 4, 8]))
+        S = int(rng.integers(1, 20)) * (4 // min(sts, 4))
+    wl = workloads.custom(f"rand{seed}", W, M, H, k, W * Er, dd, cd, ragged=bool(rng.random() < 0.6),
+                          seed_index=500 + seed)
+    launch = {}
+    if rng.random() < 0.7:
+        launch = dict(tile_tokens=int(rng.choice([16, 32, 64])),
+                      dispatch_waves=int(rng.integers(1, 17)),
+                      dispatch_row_split=int(rng.integers(1, max(2, H // 8))),
+                      combine_waves=int(rng.integers(1, 17)),
+                      combine_row_split=int(rng.integers(1, max(2, H // 8))),
+                      cache_policy=int(rng.integers(0, 3)),
+                      layout=int(rng.choice([0, 1, 2] + ([3] if k <= 16 else []))))
+        launch["dispatch_row_split"] = min(launch["dispatch_row_split"],
+                                           H * (1 if dd == "fp8" else 2) // 16)
+        launch["combine_row_split"] = min(launch["combine_row_split"], H * 2 // 16)
+    return wl, S, sts, launch
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_configurations(seed):
+    wl, S, sts, launch = _random_case(seed)
+    inp = workloads.make_inputs(wl)
+    if S:
+        g = torch.Generator().manual_seed(seed)
+        inp["scales"] = torch.randint(0, 256, (wl.world_size, wl.max_tokens, S * sts),
+                                      generator=g, dtype=torch.uint8)
+    cfg = cra.make_config(wl.world_size, wl.hidden, wl.max_tokens, wl.experts_per_rank, wl.topk,
+                          wl.dispatch_dtype, wl.combine_dtype, scale_dim=S, scale_type_size=sts)
+    op = cra.EpDispatchCombineOp(cfg)
+    if launch.get("layout") == 3:
+        tt = launch["tile_tokens"]
+        tiles = sum(-(-t // tt) for t in inp["ntok"])
+        if tiles * wl.world_size > 4096:
+            launch["layout"] = 2
+    g = torch.Generator().manual_seed(seed + 1)
+    y = torch.randn((wl.world_size, wl.world_size * wl.max_tokens, wl.hidden), generator=g)
+    y16 = y.to(workloads.TORCH_DTYPE[wl.combine_dtype]).view(torch.int16).numpy().view(np.uint16)
+    run_case(wl, inp=inp, launch=launch, y16=y16, op=op,
+             tag=f"random seed {seed} S={S}x{sts}")
+    op.close()
