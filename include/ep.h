@@ -50,6 +50,14 @@
  * ep_last_error() then names the argument at fault. Every precondition is
  * checked on the host before anything is enqueued: on error nothing is
  * enqueued and no output is touched.
+ *
+ * Devices, streams, threads: a plan's workspace, every buffer passed to it
+ * and the streams it is used on belong to one device. A plan holds one
+ * routing handle, so a plan must not be used by two threads at once, and its
+ * calls on different streams must be ordered by the caller (events); plans
+ * are independent of each other. Only sizes and pointers are checked on the
+ * host: whether a pointer is device memory of the right size is the
+ * caller's responsibility (the Python binding checks both).
  */
 #ifndef COMBINE_ROUTE_AMD_EP_H
 #define COMBINE_ROUTE_AMD_EP_H
