@@ -1,4 +1,5 @@
-"""CPU oracle for MoE expert-parallel dispatch and combine.
+"""CPU oracle for MoE expert-parallel dispatch and combine, and the
+expert-major layout of the received rows.
 
 TEST INFRASTRUCTURE ONLY. A plain, slow, single-threaded C definition of what
 dispatch and combine compute (``ep_oracle.c``), bound here with ctypes over
@@ -39,6 +40,10 @@ def _load():
     lib.oracle_combine.restype = I
     lib.oracle_combine_push.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P]
     lib.oracle_combine_push.restype = I
+    lib.oracle_expert_layout.argtypes = [I, I, I, I, I, Z, Z, P, P, P, P, P, P, P, P, P, P]
+    lib.oracle_expert_layout.restype = I
+    lib.oracle_expert_combine.argtypes = [I, I, I, I, I, I, I, P, P, P, P]
+    lib.oracle_expert_combine.restype = I
     for name in ("oracle_f32_to_bf16_n", "oracle_f32_to_f16_n",
                  "oracle_bf16_to_f32_n", "oracle_f16_to_f32_n"):
         getattr(lib, name).argtypes = [P, P, Z]
@@ -143,6 +148,54 @@ def combine_push(W, M, k, Er, H, dtype, ntok, idx, recv, src_pos, y, y_w=None):
     if rc != 0:
         raise RuntimeError(f"oracle_combine_push failed ({rc})")
     return out, out_w
+
+
+def expert_layout(W, M, k, Er, cap, recv, src_pos, x, idx, scales=None, fill=-1):
+    """Expert-major layout of dispatch outputs by definition. ``x`` is any
+    contiguous array shaped [W, W*M, ...] (one payload row per trailing block),
+    ``idx`` int32 [W, W*M, k], ``scales`` likewise or None. Returns a dict of
+    px (uint8 [W, Er, cap, row_bytes]), psc (uint8 rows or None), count
+    [W, Er], src_info [W, Er, cap] (slots past the kept rows hold ``fill``),
+    layout_range int64 [W, Er, W]. Unwritten payload bytes stay zero."""
+    lib = _load()
+    WM = W * M
+    recv = _c(np.asarray(recv, dtype=np.int32))
+    src_pos = _c(src_pos, np.int32)
+    x = _c(x)
+    idx = _c(idx, np.int32)
+    scales = _c(scales)
+    row_bytes = x.nbytes // (W * WM)
+    scale_bytes = 0 if scales is None else scales.nbytes // (W * WM)
+    out = dict(
+        px=np.zeros((W, Er, cap, row_bytes), np.uint8),
+        psc=None if scales is None else np.zeros((W, Er, cap, scale_bytes), np.uint8),
+        count=np.zeros((W, Er), np.int32),
+        src_info=np.full((W, Er, cap), fill, np.int32),
+        layout_range=np.zeros((W, Er, W), np.int64),
+    )
+    rc = lib.oracle_expert_layout(W, M, k, Er, cap, row_bytes, scale_bytes, _ptr(recv),
+                                  _ptr(src_pos), _ptr(x), _ptr(idx), _ptr(scales),
+                                  _ptr(out["px"]), _ptr(out["psc"]), _ptr(out["count"]),
+                                  _ptr(out["src_info"]), _ptr(out["layout_range"]))
+    if rc != 0:
+        raise RuntimeError(f"oracle_expert_layout failed ({rc})")
+    return out
+
+
+def expert_combine(W, M, k, Er, cap, H, dtype, recv, idx, py):
+    """Inverse of the expert-major layout by definition: ``py`` holds 16-bit
+    words [W, Er, cap, H]. Returns y uint16 [W, W*M, H]; rows past recv[d]
+    stay zero."""
+    lib = _load()
+    recv = _c(np.asarray(recv, dtype=np.int32))
+    idx = _c(idx, np.int32)
+    py = _c(py).view(np.uint16)
+    y = np.zeros((W, W * M, H), np.uint16)
+    rc = lib.oracle_expert_combine(W, M, k, Er, cap, H, dtype, _ptr(recv), _ptr(idx), _ptr(py),
+                                   _ptr(y))
+    if rc != 0:
+        raise RuntimeError(f"oracle_expert_combine failed ({rc})")
+    return y
 
 
 def _conv(name, a, in_dtype, out_dtype):

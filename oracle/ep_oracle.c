@@ -366,3 +366,129 @@ int oracle_combine_push(int W, int M, int k, int Er, int H, int dtype,
     free(slots);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Expert-major layout and its inverse.                                      */
+/* ------------------------------------------------------------------------ */
+
+/* Local experts of one received row on rank d, in the order they first
+ * appear in its id row: [GUIDE4] groups a rank's received rows by the local
+ * expert that processes them, and an expert processes a row once, so a
+ * repeated id adds nothing. Ids of other ranks' experts and ids outside
+ * [0, W*Er) are not local. Returns the count; js[] gets j = e - d * Er. */
+static int row_local_experts(const int32_t *idx_row, int k, int Er, int d, int32_t *js)
+{
+    int n = 0;
+    for (int i = 0; i < k; ++i) {
+        int32_t e = idx_row[i];
+        if (e < (int64_t)d * Er || e >= (int64_t)(d + 1) * Er)
+            continue;
+        int32_t j = e - d * Er;
+        int seen = 0;
+        for (int q = 0; q < n; ++q)
+            if (js[q] == j)
+                seen = 1;
+        if (!seen)
+            js[n++] = j;
+    }
+    return n;
+}
+
+int oracle_expert_layout(int W, int M, int k, int Er, int cap, size_t row_bytes,
+                         size_t scale_bytes, const int32_t *recv, const int32_t *src_pos,
+                         const uint8_t *x, const int32_t *idx, const uint8_t *sc,
+                         uint8_t *px, uint8_t *psc, int32_t *count, int32_t *src_info,
+                         int64_t *layout_range)
+{
+    const int64_t WM = (int64_t)W * M;
+    int32_t *js = malloc(sizeof(int32_t) * (size_t)(k > 0 ? k : 1));
+    /* srcs[d][j][p]: source rank of the p-th row of expert j's full list */
+    int32_t *srcs = malloc(sizeof(int32_t) * (size_t)(WM + 1));
+    if (!js || !srcs) { free(js); free(srcs); return -1; }
+
+    for (int d = 0; d < W; ++d) {
+        int32_t *cnt = count + (int64_t)d * Er;
+        for (int j = 0; j < Er; ++j)
+            cnt[j] = 0;
+        /* Step 1: walk the rank's received rows in receive order; each (row,
+         * local expert) pair takes the next position of that expert's list.
+         * Positions below cap are stored: the row's payload, scales and the
+         * source token index of its src_pos entry. */
+        for (int64_t q = 0; q < recv[d]; ++q) {
+            int64_t row = (int64_t)d * WM + q;
+            int n = row_local_experts(idx + row * k, k, Er, d, js);
+            for (int i = 0; i < n; ++i) {
+                int j = js[i];
+                int64_t p = cnt[j]++;
+                if (p >= cap)
+                    continue;
+                int64_t slot = ((int64_t)d * Er + j) * cap + p;
+                memcpy(px + (size_t)slot * row_bytes, x + (size_t)row * row_bytes, row_bytes);
+                if (scale_bytes)
+                    memcpy(psc + (size_t)slot * scale_bytes, sc + (size_t)row * scale_bytes,
+                           scale_bytes);
+                src_info[slot] = (int32_t)(src_pos[row] % WM);
+            }
+        }
+        /* Step 2: layout ranges. For expert j and source rank s, lo counts the
+         * list entries whose row came from a rank below s and hi those from a
+         * rank up to s; both are clipped to cap, since only kept rows are in
+         * packed_x. The lists are walked again entry by entry. */
+        for (int j = 0; j < Er; ++j) {
+            int64_t n = 0;
+            for (int64_t q = 0; q < recv[d]; ++q) {
+                int64_t row = (int64_t)d * WM + q;
+                int nl = row_local_experts(idx + row * k, k, Er, d, js);
+                for (int i = 0; i < nl; ++i)
+                    if (js[i] == j)
+                        srcs[n++] = (int32_t)(src_pos[row] / WM);
+            }
+            for (int s = 0; s < W; ++s) {
+                int64_t lo = 0, hi = 0;
+                for (int64_t p = 0; p < n; ++p) {
+                    lo += srcs[p] < s;
+                    hi += srcs[p] <= s;
+                }
+                if (lo > cap) lo = cap;
+                if (hi > cap) hi = cap;
+                layout_range[((int64_t)d * Er + j) * W + s] = (lo << 32) | (hi - lo);
+            }
+        }
+    }
+    free(js);
+    free(srcs);
+    return 0;
+}
+
+int oracle_expert_combine(int W, int M, int k, int Er, int cap, int H, int dtype,
+                          const int32_t *recv, const int32_t *idx, const uint16_t *py,
+                          uint16_t *y)
+{
+    const int64_t WM = (int64_t)W * M;
+    int32_t *js = malloc(sizeof(int32_t) * (size_t)(k > 0 ? k : 1));
+    int64_t *rows = malloc(sizeof(int64_t) * (size_t)(k > 0 ? k : 1));
+    int64_t *next = malloc(sizeof(int64_t) * (size_t)Er);
+    if (!js || !rows || !next) { free(js); free(rows); free(next); return -1; }
+    for (int d = 0; d < W; ++d) {
+        for (int j = 0; j < Er; ++j)
+            next[j] = 0;
+        /* Each received row finds its expert outputs at the positions step 1
+         * of the layout gave it, and sums the kept ones in the order its local
+         * experts first appear, like the combine sums a token's ranks. */
+        for (int64_t q = 0; q < recv[d]; ++q) {
+            int64_t row = (int64_t)d * WM + q;
+            int n = row_local_experts(idx + row * k, k, Er, d, js);
+            int kept = 0;
+            for (int i = 0; i < n; ++i) {
+                int64_t p = next[js[i]]++;
+                if (p < cap)
+                    rows[kept++] = ((int64_t)d * Er + js[i]) * cap + p;
+            }
+            fold_token(kept, rows, H, k, dtype, py, NULL, y + (size_t)row * H, NULL);
+        }
+    }
+    free(js);
+    free(rows);
+    free(next);
+    return 0;
+}

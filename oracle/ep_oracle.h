@@ -19,6 +19,11 @@
  *  [PR703]  "refactor(EPv2): replace per-module __device__ staging with shared
  *           buffer" (ROCm/mori PR 703), section "Motivation": the receive
  *           capacity of a rank is world size x max tokens per rank.
+ *  [GUIDE4] "MORI-EP User Guide", section 4 "Standard MoE Compatibility
+ *           (DeepEP)": convert_dispatch_output() turns a rank's received rows
+ *           into the expert-major layout (packed rows, counts, source info,
+ *           layout ranges) and convert_combine_input() turns expert-major
+ *           outputs back into one combine row per received row.
  *
  * Readings taken where the pages are silent (each also listed in the design
  * notes): expert e lives on rank e / experts_per_rank; received rows on a
@@ -26,6 +31,13 @@
  * first-occurrence top-k order of the token's distinct ranks, seeded with the
  * first contribution; the FP32 result is rounded to nearest even; an expert
  * id outside [0, E) selects no rank; a token with no rank combines to +0.
+ * Expert-major layout (section 4 names the calls and outputs only): a
+ * received row goes once to each distinct local expert among its ids; an
+ * expert's rows keep the receive order; rows past the capacity are dropped
+ * but counted; source info is the source token index; a layout range packs
+ * (start << 32) | count of one source rank's rows in an expert's list; the
+ * inverse sums a row's kept expert outputs in first-occurrence order like the
+ * combine and rounds once.
  *
  * Parity status: every function here is pinned by tests that do not call it
  * through itself (brute force, a second formulation, closed forms, library
@@ -90,6 +102,37 @@ int oracle_combine_push(int W, int M, int k, int Er, int H, int dtype,
                         const int32_t *recv, const int32_t *src_pos,
                         const uint16_t *y, const float *y_w,
                         uint16_t *out, float *out_w);
+
+/* Expert-major layout of the received rows, by definition ([GUIDE4],
+ * convert_dispatch_output).
+ *   Inputs are dispatch outputs: recv[W], src_pos[W][WM], x[W][WM][row_bytes],
+ *   idx[W][WM][k] (global expert ids), sc[W][WM][scale_bytes] (scale_bytes 0:
+ *   sc/psc unused). Er experts per rank; cap = rows kept per local expert.
+ * Outputs, for each rank d and local expert j (global id d * Er + j):
+ *   count[W][Er]            received rows that name expert j (all of them,
+ *                           also those past cap).
+ *   px[W][Er][cap][row_bytes], psc[W][Er][cap][scale_bytes],
+ *   src_info[W][Er][cap]    the p-th row of j's list (p < min(count, cap)):
+ *                           its payload, its scales, its source token index.
+ *                           Slots past that are untouched.
+ *   layout_range[W][Er][W]  for source rank s: (lo << 32) | (hi - lo), with lo
+ *                           and hi the list positions where s's rows start and
+ *                           end, each clipped to cap.
+ * Returns 0, or -1 if memory runs out. */
+int oracle_expert_layout(int W, int M, int k, int Er, int cap, size_t row_bytes,
+                         size_t scale_bytes, const int32_t *recv, const int32_t *src_pos,
+                         const uint8_t *x, const int32_t *idx, const uint8_t *sc,
+                         uint8_t *px, uint8_t *psc, int32_t *count, int32_t *src_info,
+                         int64_t *layout_range);
+
+/* The inverse ([GUIDE4], convert_combine_input): for every received row q <
+ * recv[d] of rank d, the sum of its kept expert outputs py[d][j][p] (bf16 or
+ * fp16, H wide), in the order its local experts first appear in its id row,
+ * folded in FP32 from the first and rounded once; a row with none is +0.
+ * Writes y[W][WM][H] rows q < recv[d]; others untouched. Returns 0. */
+int oracle_expert_combine(int W, int M, int k, int Er, int cap, int H, int dtype,
+                          const int32_t *recv, const int32_t *idx, const uint16_t *py,
+                          uint16_t *y);
 
 /* IEEE 754 conversions used by the combine cast, written from the formats'
  * definitions: binary32 -> bfloat16 / binary16 with round-to-nearest-even,
