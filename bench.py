@@ -34,7 +34,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
 METRIC = "dispatch+combine µs/call and payload HBM GB/s (% of peak), EP8 H=7168 k=8"
 KERNEL_SOURCES = [os.path.join(ROOT, "combine_route_amd", "csrc", f)
-                  for f in ("ep_kernels.hip", "ep_kernels.h", "ep_plan.cpp")]
+                  for f in ("ep_kernels.hip", "ep_kernels.h", "ep_device.h", "ep_plan.cpp")]
 KERNELS = {"copy": "ep_copy_kernel", "combine": "ep_combine_kernel"}
 
 

@@ -24,6 +24,8 @@ EP_BF16, EP_FP16, EP_FP8_E4M3 = 0, 1, 2
 EP_OK, EP_ERR_NULL, EP_ERR_ARG, EP_ERR_ALIGN, EP_ERR_SIZE, EP_ERR_STATE, EP_ERR_HIP = (
     0, -1, -2, -3, -4, -5, -6)
 EP_KERNEL_ROUTE, EP_KERNEL_SCAN, EP_KERNEL_COPY, EP_KERNEL_COMBINE = 0, 1, 2, 3
+(EP_KERNEL_EXPERT_COUNT, EP_KERNEL_EXPERT_SCAN, EP_KERNEL_EXPERT_COPY,
+ EP_KERNEL_EXPERT_COMBINE) = 4, 5, 6, 7
 EP_CACHE_AUTO, EP_CACHE_STREAM, EP_CACHE_KEEP = 0, 1, 2
 EP_LAYOUT_AUTO, EP_LAYOUT_KERNELS, EP_LAYOUT_SCAN_IN_COPY, EP_LAYOUT_IN_COPY = 0, 1, 2, 3
 
@@ -32,7 +34,9 @@ ELEM_BYTES = {EP_BF16: 2, EP_FP16: 2, EP_FP8_E4M3: 1}
 
 EXPORTED = ("ep_workspace_bytes", "ep_plan_create", "ep_plan_destroy", "ep_dispatch",
             "ep_combine", "ep_get_src_token_pos", "ep_last_error", "ep_plan_set_launch",
-            "ep_plan_get_launch", "ep_plan_set_timing", "ep_plan_kernel_time")
+            "ep_plan_get_launch", "ep_plan_set_timing", "ep_plan_kernel_time",
+            "ep_expert_workspace_bytes", "ep_expert_plan_create", "ep_expert_plan_destroy",
+            "ep_convert_dispatch_output", "ep_convert_combine_input")
 
 
 class EpConfig(ctypes.Structure):
@@ -55,7 +59,18 @@ class EpCombineArgs(ctypes.Structure):
 class EpLaunch(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "tile_tokens", "dispatch_waves", "dispatch_row_split", "combine_waves",
-        "combine_row_split", "cache_policy", "layout")]
+        "combine_row_split", "cache_policy", "layout", "expert_waves", "expert_row_split",
+        "expert_combine_waves", "expert_combine_row_split")]
+
+
+class EpConvertDispatchArgs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "x", "indices", "scales", "recv_num_token", "packed_x", "packed_scales",
+        "packed_count", "packed_src_info", "packed_layout_range")]
+
+
+class EpConvertCombineArgs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("packed_y", "y")]
 
 
 class EpError(RuntimeError):
@@ -90,8 +105,14 @@ def load():
     lib.ep_plan_get_launch.argtypes = [V, V, P(EpLaunch)]
     lib.ep_plan_set_timing.argtypes = [V, I]
     lib.ep_plan_kernel_time.argtypes = [V, I, P(ctypes.c_int32), P(ctypes.c_double)]
+    lib.ep_expert_workspace_bytes.argtypes = [V, ctypes.c_int32]
+    lib.ep_expert_workspace_bytes.restype = Z
+    lib.ep_expert_plan_create.argtypes = [V, ctypes.c_int32, V, Z, P(V)]
+    lib.ep_expert_plan_destroy.argtypes = [V]
+    lib.ep_convert_dispatch_output.argtypes = [V, P(EpConvertDispatchArgs), V]
+    lib.ep_convert_combine_input.argtypes = [V, P(EpConvertCombineArgs), V]
     for name in EXPORTED:
-        if name not in ("ep_workspace_bytes", "ep_last_error"):
+        if name not in ("ep_workspace_bytes", "ep_last_error", "ep_expert_workspace_bytes"):
             getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -267,6 +288,69 @@ def ep_plan_kernel_time(plan: int, kernel: int):
     return c.value, ms.value
 
 
+def ep_expert_workspace_bytes(plan: int, cap: int) -> int:
+    n = load().ep_expert_workspace_bytes(plan, int(cap))
+    if n == 0:
+        raise EpError("ep_expert_workspace_bytes", EP_ERR_ARG, ep_last_error())
+    return n
+
+
+def ep_expert_plan_create(plan: int, cap: int, workspace: torch.Tensor) -> int:
+    """Create an expert plan of capacity cap over a caller-owned workspace
+    tensor (keep it alive, and the plan too, until ep_expert_plan_destroy)."""
+    need = ep_expert_workspace_bytes(plan, cap)
+    ws = _dev(workspace, "workspace", need)
+    out = ctypes.c_void_p()
+    _check("ep_expert_plan_create", load().ep_expert_plan_create(
+        plan, int(cap), ws, workspace.numel() * workspace.element_size(), ctypes.byref(out)))
+    return out.value
+
+
+def ep_expert_plan_destroy(eplan: int) -> None:
+    _check("ep_expert_plan_destroy", load().ep_expert_plan_destroy(eplan))
+
+
+def _convert_dispatch_args(cfg: EpConfig, cap: int, x, indices, scales, recv_num_token,
+                           packed_x, packed_scales, packed_count, packed_src_info,
+                           packed_layout_range):
+    W, M, k, row, _, srow = _sizes(cfg)
+    WM = W * M
+    Er = cfg.num_experts_per_rank
+    return EpConvertDispatchArgs(
+        _dev(x, "x", W * WM * row), _dev(indices, "indices", W * WM * k * 4),
+        _dev(scales, "scales", W * WM * srow), _dev(recv_num_token, "recv_num_token", W * 4),
+        _dev(packed_x, "packed_x", W * Er * cap * row),
+        _dev(packed_scales, "packed_scales", W * Er * cap * srow),
+        _dev(packed_count, "packed_count", W * Er * 4),
+        _dev(packed_src_info, "packed_src_info", W * Er * cap * 4),
+        _dev(packed_layout_range, "packed_layout_range", W * Er * W * 8))
+
+
+def _convert_combine_args(cfg: EpConfig, cap: int, packed_y, y):
+    W, M, _, _, crow, _ = _sizes(cfg)
+    Er = cfg.num_experts_per_rank
+    return EpConvertCombineArgs(_dev(packed_y, "packed_y", W * Er * cap * crow),
+                                _dev(y, "y", W * W * M * crow))
+
+
+def ep_convert_dispatch_output(eplan: int, cfg: EpConfig, cap: int, x, indices, scales,
+                               recv_num_token, packed_x, packed_scales, packed_count,
+                               packed_src_info, packed_layout_range, stream=None) -> None:
+    """ep_convert_dispatch_output(); tensors as in include/ep.h."""
+    a = _convert_dispatch_args(cfg, cap, x, indices, scales, recv_num_token, packed_x,
+                               packed_scales, packed_count, packed_src_info, packed_layout_range)
+    _check("ep_convert_dispatch_output",
+           load().ep_convert_dispatch_output(eplan, ctypes.byref(a), _stream(stream)))
+
+
+def ep_convert_combine_input(eplan: int, cfg: EpConfig, cap: int, packed_y, y,
+                             stream=None) -> None:
+    """ep_convert_combine_input(); tensors as in include/ep.h."""
+    a = _convert_combine_args(cfg, cap, packed_y, y)
+    _check("ep_convert_combine_input",
+           load().ep_convert_combine_input(eplan, ctypes.byref(a), _stream(stream)))
+
+
 _TORCH = {EP_BF16: torch.bfloat16, EP_FP16: torch.float16, EP_FP8_E4M3: torch.float8_e4m3fn}
 
 
@@ -277,8 +361,13 @@ class EpDispatchCombineOp:
     and combine() return views of those buffers, valid until the next
     dispatch ("MORI (ROCm/mori) — L2 Distillation", section 9)."""
 
-    def __init__(self, cfg: EpConfig, device=None, with_weights=True):
+    def __init__(self, cfg: EpConfig, device=None, with_weights=True, expert_capacity=None):
         self.cfg = cfg
+        # rows kept per local expert by convert_dispatch_output (W * M: none
+        # dropped); its buffers are allocated on first use
+        self.expert_capacity = (cfg.world_size * cfg.max_num_inp_token_per_rank
+                                if expert_capacity is None else int(expert_capacity))
+        self._ex = None
         dev = torch.device("cuda") if device is None else torch.device(device)
         W, M, k, _, _, srow = _sizes(cfg)
         WM = W * M
@@ -342,8 +431,78 @@ class EpDispatchCombineOp:
     def set_launch(self, launch: Optional[dict] = None):
         ep_plan_set_launch(self.plan, launch)
 
+    def _expert_state(self):
+        if self._ex is None:
+            cfg, cap = self.cfg, self.expert_capacity
+            W, M, _, _, _, srow = _sizes(cfg)
+            Er, H = cfg.num_experts_per_rank, cfg.hidden_dim
+            dev = self.workspace.device
+            ws = torch.empty(ep_expert_workspace_bytes(self.plan, cap), dtype=torch.uint8,
+                             device=dev)
+            ex = dict(
+                workspace=ws,
+                packed_x=torch.empty((W, Er, cap, H), dtype=_TORCH[cfg.dispatch_dtype],
+                                     device=dev),
+                packed_scales=(torch.empty((W, Er, cap, srow), dtype=torch.uint8, device=dev)
+                               if cfg.scale_dim else None),
+                packed_count=torch.empty((W, Er), dtype=torch.int32, device=dev),
+                packed_src_info=torch.empty((W, Er, cap), dtype=torch.int32, device=dev),
+                packed_layout_range=torch.empty((W, Er, W), dtype=torch.int64, device=dev),
+                y=torch.empty((W, W * M, H), dtype=_TORCH[cfg.combine_dtype], device=dev),
+                cache=None)
+            ex["plan"] = ep_expert_plan_create(self.plan, cap, ws)
+            self._ex = ex
+        return self._ex
+
+    def convert_dispatch_output(self, dispatch_out_x, dispatch_out_topk_idx,
+                                dispatch_out_scales=None, stream=None):
+        """The last dispatch's received rows regrouped by local expert ("MORI-EP
+        User Guide", section 4, convert_dispatch_output). Returns
+        (packed_recv_x, packed_recv_count, packed_recv_src_info,
+        packed_recv_layout_range); packed_recv_x is (rows, scale rows) when
+        the config has scales. Views of buffers the next call overwrites."""
+        ex = self._expert_state()
+        given = (dispatch_out_x, dispatch_out_topk_idx, dispatch_out_scales)
+        c = ex["cache"]
+        if c is None or not _same_tensors(c[0], given):
+            a = _convert_dispatch_args(self.cfg, self.expert_capacity, dispatch_out_x,
+                                       dispatch_out_topk_idx, dispatch_out_scales,
+                                       self.recv_num_token, ex["packed_x"], ex["packed_scales"],
+                                       ex["packed_count"], ex["packed_src_info"],
+                                       ex["packed_layout_range"])
+            c = ex["cache"] = (_hold(given), a)
+        _check("ep_convert_dispatch_output", self._lib.ep_convert_dispatch_output(
+            ex["plan"], ctypes.byref(c[1]), _stream(stream, self._dev_index)))
+        px = ex["packed_x"] if ex["packed_scales"] is None else (ex["packed_x"],
+                                                                  ex["packed_scales"])
+        return px, ex["packed_count"], ex["packed_src_info"], ex["packed_layout_range"]
+
+    def convert_combine_input(self, packed_recv_y, packed_recv_src_info=None,
+                              packed_recv_layout_range=None, stream=None):
+        """One combine input row per received row from the experts' outputs
+        ("MORI-EP User Guide", section 4, convert_combine_input). The
+        positions come from this op's last convert_dispatch_output;
+        packed_recv_src_info / packed_recv_layout_range, if given, must be the
+        tensors it returned. Returns y [W, W*M, H] for combine()."""
+        ex = self._ex
+        if ex is None:
+            raise EpError("ep_convert_combine_input", EP_ERR_STATE,
+                          "convert_combine_input before any convert_dispatch_output")
+        for t, key, name in ((packed_recv_src_info, "packed_src_info", "packed_recv_src_info"),
+                             (packed_recv_layout_range, "packed_layout_range",
+                              "packed_recv_layout_range")):
+            if t is not None and t is not ex[key]:
+                raise ValueError(f"{name} must be the tensor convert_dispatch_output returned")
+        a = _convert_combine_args(self.cfg, self.expert_capacity, packed_recv_y, ex["y"])
+        _check("ep_convert_combine_input", self._lib.ep_convert_combine_input(
+            ex["plan"], ctypes.byref(a), _stream(stream, self._dev_index)))
+        return ex["y"]
+
     def close(self):
         self._dcache = self._ccache = None
+        if self._ex is not None:
+            ex, self._ex = self._ex, None
+            ep_expert_plan_destroy(ex["plan"])
         if self.plan:
             ep_plan_destroy(self.plan)
             self.plan = None

@@ -10,7 +10,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libcombine_route_amd.so")
-SOURCES = [os.path.join(PKG, "csrc", "ep_plan.cpp"), os.path.join(PKG, "csrc", "ep_kernels.hip")]
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("ep_plan.cpp", "ep_kernels.hip", "ep_expert.hip")]
 ARCH = "gfx950"
 
 FLAGS = [

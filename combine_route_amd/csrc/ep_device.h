@@ -1,0 +1,175 @@
+// Device helpers shared by the gfx950 kernels: row moves through per-row
+// buffer resources, wave-level bit counting, and the ordered FP32 fold with
+// its round-to-nearest-even cast.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ep_kernels.h"
+
+namespace ep {
+namespace dev {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Cache policy of the row moves, as gfx950 buffer-instruction bits (1 = sc0,
+// 2 = nt, 16 = sc1). Streaming calls (footprint well past the 256 MB MALL)
+// touch every payload row once, so loads stream past the caches (nt); the
+// combine's stores stream too; the copies' stores do not. Measured on MI355X
+// at 8 ranks x 4096 tokens x 7168 bf16: nt stores in the dispatch copy cost it
+// ~40 us a call, plain stores in the combine leave dirty lines that the next
+// dispatch pays ~40 us to write back, and cached combine loads cost ~70 us.
+// Calls that fit in the MALL use plain (cache-allocating) moves: rows an
+// expert has just written are still there, and 8 ranks x 128 fp8 tokens runs
+// ~10% faster that way.
+template <bool kStream>
+struct Policy {
+    static constexpr int copy_load = kStream ? 2 : 0;
+    static constexpr int copy_store = 0;
+    static constexpr int combine_load = kStream ? 2 : 0;
+    static constexpr int combine_store = kStream ? 2 : 0;
+};
+
+// A combine loads up to kCombineGroup contribution rows, kCombineColumns
+// 16-byte columns each, before folding (8 x 2 measured best: smaller groups
+// split a top-8 token's rows into two dependent rounds, larger column counts
+// cost occupancy).
+constexpr int kCombineGroup = 8;
+constexpr int kCombineColumns = 2;
+
+// Number of lanes below this one whose bit is set in b.
+__device__ __forceinline__ int lanes_below(uint64_t b)
+{
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+}
+
+// A value every lane of the wave holds identically, moved to a scalar register.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// A buffer resource covering one row: every access through it is range-checked
+// by the hardware against the row's bytes (an out-of-range load reads zero, an
+// out-of-range store is dropped), so a row move cannot spill into its
+// neighbour. Word 3 is the raw (untyped) buffer format.
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
+}
+
+template <int AUX>
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX);
+}
+
+template <int AUX>
+__device__ __forceinline__ void bstore16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, AUX);
+}
+
+template <int DT>
+__device__ __forceinline__ void widen(const u32x4& w, float (&f)[8])
+{
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if constexpr (DT == 0) {  // bf16: the upper half of a binary32
+            f[2 * q] = __builtin_bit_cast(float, w[q] << 16);
+            f[2 * q + 1] = __builtin_bit_cast(float, w[q] & 0xFFFF0000u);
+        } else {                  // fp16: exact hardware widening
+            f[2 * q] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[q] & 0xFFFFu));
+            f[2 * q + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[q] >> 16));
+        }
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ u32x4 narrow(const float (&f)[8])
+{
+    u32x4 w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if constexpr (DT == 0) {  // v_cvt_pk_bf16_f32: round to nearest even
+            const f32x2 p = {f[2 * q], f[2 * q + 1]};
+            w[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
+        } else {                  // v_cvt_f16_f32: round to nearest even
+            const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)f[2 * q]);
+            const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)f[2 * q + 1]);
+            w[q] = lo | (hi << 16);
+        }
+    }
+    return w;
+}
+
+// One wave folds the n contribution rows whose row numbers (in units of
+// row_bytes from src) are held by lanes 0..n-1 of gl, over the 16-byte
+// columns [vbeg, vend) of the output row rdst: for each column every
+// contribution is loaded before any is added (G rows x U columns a lane in
+// flight), then they are summed in lane order in FP32 starting from the
+// first, and the sum is rounded to nearest even once. n = 0 stores +0.
+template <int G, int U, int DT, bool kStream>
+__device__ __forceinline__ void fold_rows(const uint8_t* src, uint32_t row_bytes, int32_t gl,
+                                          int n, __amdgpu_buffer_rsrc_t rdst, int vbeg, int vend,
+                                          int lane)
+{
+    for (int v0 = vbeg; v0 < vend; v0 += kWave * U) {
+        float acc[U][8];
+        for (int i0 = 0; i0 < n; i0 += G) {
+            u32x4 rows[U][G];
+#pragma unroll
+            for (int q = 0; q < G; ++q) {
+                if (i0 + q < n) {
+                    const int64_t gq = __builtin_amdgcn_readlane(gl, i0 + q);
+                    const __amdgpu_buffer_rsrc_t ry = row_rsrc(src + gq * row_bytes, row_bytes);
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int v = v0 + u * kWave + lane;
+                        if (v < vend)
+                            rows[u][q] = bload16<Policy<kStream>::combine_load>(
+                                ry, (uint32_t)v * 16u);
+                    }
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < G; ++q) {
+                if (i0 + q < n) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        float f[8];
+                        widen<DT>(rows[u][q], f);
+                        if (i0 + q == 0) {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                acc[u][e] = f[e];
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                acc[u][e] = acc[u][e] + f[e];
+                        }
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = v0 + u * kWave + lane;
+            if (v < vend) {
+                if (n == 0) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        acc[u][e] = 0.0f;
+                }
+                bstore16<Policy<kStream>::combine_store>(narrow<DT>(acc[u]), rdst,
+                                                         (uint32_t)v * 16u);
+            }
+        }
+    }
+}
+
+}  // namespace dev
+}  // namespace ep

@@ -1,0 +1,417 @@
+// gfx950 (MI355X, CDNA4) kernels of the expert-major layout of received rows
+// and its inverse ("MORI-EP User Guide", section 4 "Standard MoE
+// Compatibility (DeepEP)": convert_dispatch_output, convert_combine_input).
+//
+// Each rank's received rows are counting-sorted by local expert with the same
+// deterministic scheme as the dispatch: one 64-lane ballot per local expert
+// over a tile of 64 rows, an exclusive scan over tiles per (rank, expert)
+// list, and the ballot prefix (mbcnt) inside a tile. No atomic decides a
+// position, and an expert's rows keep the receive order.
+//   count    a wave per tile: how many of its rows name each local expert;
+//            where each source rank's rows start, with the in-tile prefixes
+//            there, for the layout ranges.
+//   scan     a wave per list: exclusive scan of its tile counts -> tile bases,
+//            the expert's row count and its layout ranges.
+//   copy     a block per (tile, row piece): wave 0 works out the kept packed
+//            row of every (row, local expert) pair into LDS; then every wave
+//            loads a row piece once (16 B a lane) and stores it to each of the
+//            row's packed rows; piece-0 blocks also write the scale rows, the
+//            source info and the map the inverse gathers through.
+//   combine  a wave per (received row, row piece): the row's kept expert
+//            outputs, folded in FP32 in first-occurrence order and rounded to
+//            nearest even once (the combine's fold).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ep_device.h"
+#include "ep_kernels.h"
+
+namespace ep {
+namespace {
+
+using namespace dev;
+
+constexpr int kExWaves = 4;  // count and scan: waves a block, one tile or list each
+
+// Received rows of rank d that the call covers. The dispatch never fills more
+// than `rows` (every token goes at most once to a rank); the clamp keeps a
+// wrong count from reaching past the tiles.
+__device__ __forceinline__ int received(int recv, int rows) { return max(0, min(recv, rows)); }
+
+// All KB ids of a row, at addresses clamped into it, so every load issues
+// before any is waited on; ids past k are loaded but ignored.
+template <int KB>
+__device__ __forceinline__ void load_row_ids(const int32_t* row, int k, int32_t (&ids)[KB])
+{
+#pragma unroll
+    for (int i = 0; i < KB; ++i)
+        ids[i] = row[min(i, k - 1)];
+}
+
+// Word w of a row's set of local experts: bit b for local expert 64w + b.
+// An id is local when it lies in [lo, lo + Er).
+template <int KB>
+__device__ __forceinline__ uint64_t local_word(const int32_t (&ids)[KB], int k, bool valid,
+                                               int64_t lo, int Er, int w)
+{
+    uint64_t m = 0;
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+        const int64_t j = (int64_t)ids[i] - lo;
+        const int64_t b = j - 64 * w;
+        if (valid && i < k && j >= 0 && j < Er && b >= 0 && b < 64)
+            m |= 1ull << b;
+    }
+    return m;
+}
+
+__device__ __forceinline__ int source_rank(const ExpertArgs& a, int64_t row)
+{
+    return min(max(a.src_pos[row] / a.WM, 0), a.W - 1);
+}
+
+template <int KB>
+__global__ __launch_bounds__(kExWaves * kWave) void ex_count_kernel(ExpertArgs a)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int tile = blockIdx.x * kExWaves + threadIdx.x / kWave;
+    const int d = blockIdx.y;
+    if (tile >= a.T)
+        return;  // whole waves
+    const int R = received(a.recv[d], a.rows);
+    const int q = tile * kWave + lane;
+    const bool valid = q < R;
+    const int64_t row0 = (int64_t)d * a.WM;
+    const int64_t lo = (int64_t)d * a.Er;
+    int32_t* counts = a.tile_counts + lo * a.T + tile;  // list lo + j at [j * T]
+    int32_t* start = a.src_start + d * a.W;
+    if (tile * kWave >= R) {  // no received row here
+        for (int j = lane; j < a.Er; j += kWave)
+            counts[(int64_t)j * a.T] = 0;
+        if (R == 0 && tile == 0 && lane < a.W)
+            start[lane] = 0;
+        return;
+    }
+    int32_t ids[KB];
+    load_row_ids<KB>(a.idx + (row0 + (valid ? q : 0)) * a.k, a.k, ids);
+
+    // Rows are in source-rank order, so source s starts at the first row
+    // whose source is >= s. The row that starts sources (s_prev, s_cur]
+    // records itself and, below, its in-tile prefix on every expert; the last
+    // row gives every later source the end, R.
+    const int s_cur = valid ? source_rank(a, row0 + q) : a.W;
+    int s_prev = __shfl_up(s_cur, 1);
+    if (lane == 0)
+        s_prev = q > 0 ? source_rank(a, row0 + q - 1) : -1;
+    const bool starts = valid && s_prev < s_cur;
+    if (starts)
+        for (int s = s_prev + 1; s <= s_cur; ++s)
+            start[s] = q;
+    if (valid && q == R - 1)
+        for (int s = s_cur + 1; s < a.W; ++s)
+            start[s] = R;
+
+    for (int w = 0; 64 * w < a.Er; ++w) {
+        const uint64_t m = local_word<KB>(ids, a.k, valid, lo, a.Er, w);
+        const int nj = min(kWave, a.Er - 64 * w);
+        int c = 0;
+        for (int jj = 0; jj < nj; ++jj) {
+            const uint64_t b = __ballot((m >> jj) & 1);
+            if (lane == jj)
+                c = __popcll(b);
+            if (starts) {
+                const int pre = lanes_below(b);
+                int32_t* sp = a.src_prefix + (lo + 64 * w + jj) * a.W;
+                for (int s = s_prev + 1; s <= s_cur; ++s)
+                    sp[s] = pre;
+            }
+        }
+        if (lane < nj)
+            counts[(int64_t)(64 * w + lane) * a.T] = c;
+    }
+}
+
+__global__ __launch_bounds__(kExWaves * kWave) void ex_scan_kernel(ExpertArgs a)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t g = (int64_t)blockIdx.x * kExWaves + threadIdx.x / kWave;
+    if (g >= (int64_t)a.W * a.Er)
+        return;  // whole waves
+    const int d = (int)(g / a.Er);
+    const int R = received(a.recv[d], a.rows);
+    const int32_t* cnt = a.tile_counts + g * a.T;
+    int32_t* base = a.tile_base + g * a.T;
+    // lane s < W: the row where source s starts and the expert's rows before
+    // it in that row's tile
+    int start_row = R, pre = 0;
+    if (lane < a.W) {
+        start_row = min(a.src_start[d * a.W + lane], R);
+        if (start_row < R)
+            pre = a.src_prefix[g * a.W + lane];
+    }
+    const int start_tile = start_row / kWave;
+    int start = 0, carry = 0;
+    for (int c0 = 0; c0 < a.T; c0 += kWave) {
+        const int t = c0 + lane;
+        const int v = t < a.T ? cnt[t] : 0;
+        int inc = v;  // inclusive prefix over the wave
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int u = __shfl_up(inc, o);
+            if (lane >= o)
+                inc += u;
+        }
+        const int excl = carry + inc - v;
+        if (t < a.T)
+            base[t] = excl;
+        const int at = __shfl(excl, (start_tile - c0) & (kWave - 1));
+        if (start_row < R && start_tile >= c0 && start_tile < c0 + kWave)
+            start = at + pre;
+        carry += __shfl(inc, kWave - 1);
+    }
+    if (start_row >= R)
+        start = carry;
+    if (lane == 0)
+        a.count[g] = carry;
+    int next = __shfl_down(start, 1);
+    if (lane == a.W - 1)
+        next = carry;
+    if (lane < a.W) {
+        const int64_t lo = min(start, a.cap);
+        const int64_t hi = min(next, a.cap);
+        a.layout_range[g * a.W + lane] = (lo << 32) | (hi - lo);
+    }
+}
+
+template <int VPL, int KB, bool kStream>
+__global__ __launch_bounds__(1024) void ex_copy_kernel(ExpertArgs a)
+{
+    __shared__ int32_t s_j[kWave][KB];  // a row's local experts, first-occurrence order
+    __shared__ int32_t s_p[kWave][KB];  // their positions, then the kept packed rows
+    __shared__ int32_t s_n[kWave];      // kept packed rows of the row
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nwaves = blockDim.x / kWave;
+    const int tile = blockIdx.x;
+    const int piece = blockIdx.y;
+    const int d = blockIdx.z;
+    const int R = received(a.recv[d], a.rows);
+    const int q0 = tile * kWave;
+    const int cnt = min(kWave, R - q0);
+    if (cnt <= 0)
+        return;  // the whole block
+    const int64_t row0 = (int64_t)d * a.WM + q0;
+    const int64_t lo = (int64_t)d * a.Er;
+
+    if (wave == 0) {
+        const bool valid = lane < cnt;
+        int32_t ids[KB];
+        load_row_ids<KB>(a.idx + (row0 + (valid ? lane : 0)) * a.k, a.k, ids);
+        int n = 0;
+#pragma unroll
+        for (int i = 0; i < KB; ++i) {
+            const int64_t j = (int64_t)ids[i] - lo;
+            if (valid && i < a.k && j >= 0 && j < a.Er) {
+                bool seen = false;
+                for (int u = 0; u < n; ++u)
+                    seen = seen || s_j[lane][u] == (int)j;
+                if (!seen)
+                    s_j[lane][n++] = (int)j;
+            }
+        }
+        for (int w = 0; 64 * w < a.Er; ++w) {
+            const uint64_t m = local_word<KB>(ids, a.k, valid, lo, a.Er, w);
+            const int nj = min(kWave, a.Er - 64 * w);
+            const int bw = lane < nj ? a.tile_base[(lo + 64 * w + lane) * a.T + tile] : 0;
+            for (int jj = 0; jj < nj; ++jj) {
+                const bool has = (m >> jj) & 1;
+                const uint64_t b = __ballot(has);
+                if (has) {
+                    const int p = __builtin_amdgcn_readlane(bw, jj) + lanes_below(b);
+                    for (int u = 0; u < n; ++u)
+                        if (s_j[lane][u] == 64 * w + jj)
+                            s_p[lane][u] = p;
+                }
+            }
+        }
+        int kept = 0;  // positions past the capacity are dropped
+        for (int u = 0; u < n; ++u) {
+            const int p = s_p[lane][u];
+            if (p < a.cap)
+                s_p[lane][kept++] = (int32_t)((lo + s_j[lane][u]) * a.cap + p);
+        }
+        s_n[lane] = kept;
+    }
+    __syncthreads();
+
+    const int sd = a.scale_dwords;
+    if (piece == 0) {
+        for (int r = wave; r < cnt; r += nwaves) {
+            const int64_t row = row0 + r;
+            const int n = uniform(s_n[r]);
+            if (lane < a.Pe)
+                a.efwd[row * a.Pe + lane] = lane < n ? s_p[r][lane] : -1;
+            if (lane < n)
+                a.src_info[s_p[r][lane]] = a.src_pos[row] % a.WM;
+            for (int c0 = 0; n > 0 && c0 < sd; c0 += kWave) {
+                const int c = c0 + lane;
+                const uint32_t v = c < sd ? a.sc[row * sd + c] : 0u;
+                for (int i = 0; i < n; ++i) {
+                    const int64_t gi = uniform(s_p[r][i]);
+                    if (c < sd)
+                        a.psc[gi * sd + c] = v;
+                }
+            }
+        }
+    }
+
+    const uint32_t row_bytes = (uint32_t)a.row_vecs * 16u;
+    const int vbeg = piece * a.piece_vecs;
+    const int vend = min(a.row_vecs, vbeg + a.piece_vecs);
+    for (int r = wave; r < cnt; r += nwaves) {
+        const int n = uniform(s_n[r]);
+        if (n == 0)
+            continue;
+        const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.x + (row0 + r) * row_bytes, row_bytes);
+        for (int v0 = vbeg; v0 < vend; v0 += kWave * VPL) {
+            u32x4 v[VPL];
+#pragma unroll
+            for (int u = 0; u < VPL; ++u) {
+                const int vv = v0 + u * kWave + lane;
+                if (vv < vend)
+                    v[u] = bload16<Policy<kStream>::copy_load>(rs, (uint32_t)vv * 16u);
+            }
+            for (int i = 0; i < n; ++i) {
+                const int64_t gi = uniform(s_p[r][i]);
+                const __amdgpu_buffer_rsrc_t rd = row_rsrc(a.px + gi * row_bytes, row_bytes);
+#pragma unroll
+                for (int u = 0; u < VPL; ++u) {
+                    const int vv = v0 + u * kWave + lane;
+                    if (vv < vend)
+                        bstore16<Policy<kStream>::copy_store>(v[u], rd, (uint32_t)vv * 16u);
+                }
+            }
+        }
+    }
+}
+
+template <int G, int U, int DT, bool kStream>
+__global__ __launch_bounds__(1024) void ex_combine_kernel(ExpertCombineArgs a)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int q = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const int piece = blockIdx.y;
+    const int d = blockIdx.z;
+    if (q >= received(a.recv[d], a.rows))
+        return;  // whole waves
+    const int64_t row = (int64_t)d * a.WM + q;
+    const int32_t gl = lane < a.Pe ? a.efwd[row * a.Pe + lane] : -1;
+    const int n = __popcll(__ballot(gl >= 0));  // entries >= 0 form a prefix
+    const uint32_t row_bytes = (uint32_t)a.row_vecs * 16u;
+    const __amdgpu_buffer_rsrc_t rdst = row_rsrc(a.y + row * row_bytes, row_bytes);
+    const int vbeg = piece * a.piece_vecs;
+    const int vend = min(a.row_vecs, vbeg + a.piece_vecs);
+    fold_rows<G, U, DT, kStream>(a.py, row_bytes, gl, n, rdst, vbeg, vend, lane);
+}
+
+// Top-k bucket of the expert kernels: the smallest of 8, 16, 32, 64 >= k.
+int ex_bucket(int k) { return k <= 8 ? 8 : k <= 16 ? 16 : k <= 32 ? 32 : 64; }
+
+template <int VPL, int KB>
+hipError_t ex_copy_with(const ExpertArgs& a, dim3 grid, dim3 block, bool stream, hipStream_t s)
+{
+    if (stream)
+        hipLaunchKernelGGL((ex_copy_kernel<VPL, KB, true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((ex_copy_kernel<VPL, KB, false>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+template <int VPL>
+hipError_t ex_copy_with_vpl(const ExpertArgs& a, dim3 grid, dim3 block, bool stream,
+                            hipStream_t s)
+{
+    switch (ex_bucket(a.k)) {
+    case 8: return ex_copy_with<VPL, 8>(a, grid, block, stream, s);
+    case 16: return ex_copy_with<VPL, 16>(a, grid, block, stream, s);
+    case 32: return ex_copy_with<VPL, 32>(a, grid, block, stream, s);
+    default: return ex_copy_with<VPL, 64>(a, grid, block, stream, s);
+    }
+}
+
+template <int G, int U>
+hipError_t ex_combine_with(const ExpertCombineArgs& a, int dtype, dim3 grid, dim3 block,
+                           bool stream, hipStream_t s)
+{
+    if (dtype == 0) {
+        if (stream)
+            hipLaunchKernelGGL((ex_combine_kernel<G, U, 0, true>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((ex_combine_kernel<G, U, 0, false>), grid, block, 0, s, a);
+    } else {
+        if (stream)
+            hipLaunchKernelGGL((ex_combine_kernel<G, U, 1, true>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((ex_combine_kernel<G, U, 1, false>), grid, block, 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_expert_count(const ExpertArgs& a, hipStream_t s)
+{
+    const dim3 grid((a.T + kExWaves - 1) / kExWaves, a.W);
+    const dim3 block(kExWaves * kWave);
+    switch (ex_bucket(a.k)) {
+    case 8: hipLaunchKernelGGL((ex_count_kernel<8>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((ex_count_kernel<16>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((ex_count_kernel<32>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((ex_count_kernel<64>), grid, block, 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_expert_scan(const ExpertArgs& a, hipStream_t s)
+{
+    const int64_t lists = (int64_t)a.W * a.Er;
+    hipLaunchKernelGGL(ex_scan_kernel, dim3((unsigned)((lists + kExWaves - 1) / kExWaves)),
+                       dim3(kExWaves * kWave), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_expert_copy(const ExpertArgs& a, int waves, int row_split, bool stream,
+                              hipStream_t s)
+{
+    if (a.rows == 0)
+        return hipSuccess;
+    const dim3 grid(a.T, row_split, a.W);
+    const dim3 block(waves * kWave);
+    const int per_lane = (a.piece_vecs + kWave - 1) / kWave;
+    if (per_lane <= 1)
+        return ex_copy_with_vpl<1>(a, grid, block, stream, s);
+    if (per_lane <= 2)
+        return ex_copy_with_vpl<2>(a, grid, block, stream, s);
+    if (per_lane <= 4)
+        return ex_copy_with_vpl<4>(a, grid, block, stream, s);
+    return ex_copy_with_vpl<8>(a, grid, block, stream, s);
+}
+
+hipError_t launch_expert_combine(const ExpertCombineArgs& a, int W, int dtype, int waves,
+                                 int row_split, bool stream, hipStream_t s)
+{
+    if (a.rows == 0)
+        return hipSuccess;
+    const dim3 grid((a.rows + waves - 1) / waves, row_split, W);
+    const dim3 block(waves * kWave);
+    if (a.Pe <= 1)
+        return ex_combine_with<1, 4>(a, dtype, grid, block, stream, s);
+    if (a.Pe <= 2)
+        return ex_combine_with<2, 4>(a, dtype, grid, block, stream, s);
+    if (a.Pe <= 4)
+        return ex_combine_with<4, kCombineColumns>(a, dtype, grid, block, stream, s);
+    return ex_combine_with<kCombineGroup, kCombineColumns>(a, dtype, grid, block, stream, s);
+}
+
+}  // namespace ep

@@ -1,6 +1,7 @@
 // Internal interface between the host side of the library (ep_plan.cpp) and
-// its gfx950 kernels (ep_kernels.hip). Not installed; the public ABI is
-// include/ep.h.
+// its gfx950 kernels (ep_kernels.hip: dispatch and combine; ep_expert.hip:
+// the expert-major layout of received rows and its inverse). Not installed;
+// the public ABI is include/ep.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -88,6 +89,45 @@ struct CombineArgs {
     int32_t M, k, P;
 };
 
+// Expert-major layout of the received rows of every rank. A tile is 64
+// consecutive received rows of one rank (one lane each); T tiles a rank cover
+// the most rows any rank can hold in this call. A list is one (rank, local
+// expert) pair, g = d * Er + j.
+struct ExpertArgs {
+    const uint8_t* x;            // [W][WM][row_bytes] received rows
+    const int32_t* idx;          // [W][WM][k] their expert ids
+    const uint32_t* sc;          // [W][WM][scale_dwords] or null
+    const int32_t* recv;         // [W] received rows of each rank
+    const int32_t* src_pos;      // [W][WM] src_rank * WM + src_token
+    uint8_t* px;                 // [W][Er][cap][row_bytes]
+    uint32_t* psc;               // [W][Er][cap][scale_dwords] or null
+    int32_t* count;              // [W][Er] rows naming each local expert
+    int32_t* src_info;           // [W][Er][cap] source token index
+    int64_t* layout_range;       // [W][Er][W] (lo << 32) | n, clipped to cap
+    int32_t* tile_counts;        // [W * Er][T] rows of tile t naming the list's expert
+    int32_t* tile_base;          // [W * Er][T] position of tile t's first such row
+    int32_t* src_start;          // [W][W] first received row from each source rank
+    int32_t* src_prefix;         // [W * Er][W] rows naming the expert in that row's tile before it
+    int32_t* efwd;               // [W][WM][Pe] kept packed rows of each received row
+    int32_t row_vecs;            // 16-byte vectors per payload row
+    int32_t piece_vecs;          // vectors per row piece (one block)
+    int32_t scale_dwords;        // 4-byte words per scale row (0: none)
+    int32_t W, WM, k, Er, Pe, cap;
+    int32_t rows;                // most received rows any rank can hold in this call
+    int32_t T;                   // tiles a rank: max(1, ceil(rows / 64))
+};
+
+struct ExpertCombineArgs {
+    const uint8_t* py;           // [W][Er][cap][H] expert outputs, combine dtype
+    const int32_t* recv;         // [W]
+    const int32_t* efwd;         // [W][WM][Pe]
+    uint8_t* y;                  // [W][WM][H]
+    int32_t row_vecs;            // 16-byte vectors per row
+    int32_t piece_vecs;
+    int32_t WM, Pe;
+    int32_t rows;                // most received rows any rank can hold in this call
+};
+
 hipError_t launch_route(const RouteArgs& a, const TileMap& tm, hipStream_t s);
 hipError_t launch_scan(const ScanArgs& a, int W, hipStream_t s);
 // stream: true = streaming cache policy (rows bypass the caches), false =
@@ -96,5 +136,12 @@ hipError_t launch_copy(const CopyArgs& a, const TileMap& tm, int waves, int row_
                        bool stream, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, const TokenMap& tk, int dtype, int waves,
                           int row_split, bool stream, hipStream_t s);
+
+hipError_t launch_expert_count(const ExpertArgs& a, hipStream_t s);
+hipError_t launch_expert_scan(const ExpertArgs& a, hipStream_t s);
+hipError_t launch_expert_copy(const ExpertArgs& a, int waves, int row_split, bool stream,
+                              hipStream_t s);
+hipError_t launch_expert_combine(const ExpertCombineArgs& a, int W, int dtype, int waves,
+                                 int row_split, bool stream, hipStream_t s);
 
 }  // namespace ep

@@ -1,5 +1,6 @@
 // Host side of the C ABI in include/ep.h: configuration checks, workspace
-// layout, launch geometry, argument checks and kernel launches.
+// layouts, launch geometry, argument checks and kernel launches, for plans and
+// the expert plans made from them.
 //
 // Every precondition is checked before anything is enqueued, and a failed
 // check names the argument, as the gfx125x staging refactor does for an
@@ -55,6 +56,7 @@ constexpr int kScanInCopyTiles = 256;
 constexpr int64_t kLayoutInCopyTokens = 256;
 constexpr size_t kPtrAlign = 16;
 constexpr int kTimerPool = 1024;
+constexpr int kTimedKernels = 8;  // EP_KERNEL_ROUTE .. EP_KERNEL_EXPERT_COMBINE
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -176,10 +178,62 @@ struct ep_plan {
     bool launched = false;
     ep_launch_t launch = {};
     bool timing = false;
-    Timer timers[4];
+    Timer timers[kTimedKernels];
+    uint64_t dispatch_gen = 0;  // successful dispatches so far
+    int experts = 0;            // live expert plans made from this plan
+};
+
+// Workspace of an expert plan of capacity cap: per-tile expert counts and
+// bases ([W * Er][T]), the first received row of each source rank ([W][W]),
+// the in-tile prefixes there ([W * Er][W]) and the inverse's map
+// ([W][WM][Pe], Pe = min(k, Er)).
+struct ExShape {
+    int32_t cap;
+    int Pe;
+    int64_t T;  // tiles a rank can need: max(1, ceil(WM / 64))
+    size_t off_counts, off_base, off_start, off_prefix, off_efwd, total;
+};
+
+struct ep_expert_plan {
+    ep_plan* plan;
+    ExShape e;
+    uint8_t* ws;
+    bool converted = false;
+    uint64_t gen = 0;                  // the plan's dispatch that was converted
+    const int32_t* recv = nullptr;     // its received-row counts
+    int32_t rows = 0;                  // most rows a rank could hold in it
+    hipStream_t last_stream = nullptr;
+    bool launched = false;
 };
 
 namespace {
+
+int expert_shape(const Shape& s, int32_t cap, ExShape* e)
+{
+    if (cap < 1 || cap > s.WM)
+        return fail(EP_ERR_ARG, "cap = %d: must be in [1, W * M = %lld]", cap, (long long)s.WM);
+    if ((int64_t)s.W * s.Er * cap > INT32_MAX)
+        return fail(EP_ERR_SIZE, "W * num_experts_per_rank * cap exceeds 2^31 - 1 (packed rows "
+                    "are int32 in the inverse's map)");
+    e->cap = cap;
+    e->Pe = std::min(s.k, s.Er);
+    e->T = std::max<int64_t>(1, (s.WM + ep::kWave - 1) / ep::kWave);
+    const size_t lists = (size_t)s.W * (size_t)s.Er;
+    size_t off = 0;
+    e->off_counts = off;
+    off = align_up(off + sizeof(int32_t) * lists * (size_t)e->T, kWorkspaceAlign);
+    e->off_base = off;
+    off = align_up(off + sizeof(int32_t) * lists * (size_t)e->T, kWorkspaceAlign);
+    e->off_start = off;
+    off = align_up(off + sizeof(int32_t) * (size_t)s.W * (size_t)s.W, kWorkspaceAlign);
+    e->off_prefix = off;
+    off = align_up(off + sizeof(int32_t) * lists * (size_t)s.W, kWorkspaceAlign);
+    e->off_efwd = off;
+    off = align_up(off + sizeof(int32_t) * (size_t)s.W * (size_t)s.WM * (size_t)e->Pe,
+                   kWorkspaceAlign);
+    e->total = off;
+    return EP_OK;
+}
 
 int32_t* ws_counts(ep_plan* p) { return reinterpret_cast<int32_t*>(p->ws + p->s.off_counts); }
 int32_t* ws_base(ep_plan* p) { return reinterpret_cast<int32_t*>(p->ws + p->s.off_base); }
@@ -195,6 +249,20 @@ bool layout_in_copy_fits(const Shape& s, int ntiles)
 {
     return s.k <= 16 && (int64_t)ntiles * s.W <= ep::kLayoutInCopyCells;
 }
+
+// Most rows any rank can receive from a dispatch of these token counts: a
+// token goes at most once to a rank.
+int64_t expert_rows(const Shape& s, const int32_t* ntok)
+{
+    int64_t N = 0;
+    for (int r = 0; r < s.W; ++r)
+        N += ntok[r];
+    return std::min<int64_t>(s.WM, N);
+}
+
+// 64-row tiles per rank of the expert-major layout (at least one, so the
+// counts and ranges are written even when nothing was received).
+int expert_tiles(int64_t rows) { return (int)std::max<int64_t>(1, (rows + ep::kWave - 1) / ep::kWave); }
 
 int tiles_for(const int32_t* ntok, int W, int tt)
 {
@@ -250,6 +318,17 @@ ep_launch_t auto_launch(const ep_plan* p, const int32_t* ntok)
         l.layout = EP_LAYOUT_SCAN_IN_COPY;
     else
         l.layout = EP_LAYOUT_KERNELS;
+    // expert-major layout: 64 received rows a copy block, a row a wave in the
+    // inverse, pieces until the grid has about kTargetBlocks blocks
+    const int64_t rows = expert_rows(s, ntok);
+    const int64_t eblocks = (int64_t)s.W * expert_tiles(rows);
+    l.expert_waves = 8;
+    l.expert_row_split = (int)std::min<int64_t>(
+        std::min<int64_t>(max_split, 65535), std::max<int64_t>(1, (kTargetBlocks + eblocks - 1) / eblocks));
+    l.expert_combine_waves = 4;
+    const int64_t iblocks = std::max<int64_t>(1, s.W * ((rows + 3) / 4));
+    l.expert_combine_row_split = (int)std::min<int64_t>(
+        std::min<int64_t>(cmax_split, 65535), std::max<int64_t>(1, (kTargetBlocks + iblocks - 1) / iblocks));
     return l;
 }
 
@@ -270,6 +349,14 @@ ep_launch_t effective_launch(const ep_plan* p, const int32_t* ntok)
         l.cache_policy = p->launch.cache_policy;
     if (p->launch.layout > 0)
         l.layout = p->launch.layout;
+    if (p->launch.expert_waves > 0)
+        l.expert_waves = p->launch.expert_waves;
+    if (p->launch.expert_row_split > 0)
+        l.expert_row_split = p->launch.expert_row_split;
+    if (p->launch.expert_combine_waves > 0)
+        l.expert_combine_waves = p->launch.expert_combine_waves;
+    if (p->launch.expert_combine_row_split > 0)
+        l.expert_combine_row_split = p->launch.expert_combine_row_split;
     return l;
 }
 
@@ -343,6 +430,19 @@ int check_launch(const ep_plan* p, const ep_launch_t* l)
     if (l->combine_row_split > s.crow_bytes / 16)
         return fail(EP_ERR_ARG, "launch.combine_row_split = %d: must be <= %lld",
                     l->combine_row_split, (long long)(s.crow_bytes / 16));
+    if (l->expert_waves > 16)
+        return fail(EP_ERR_ARG, "launch.expert_waves = %d: must be <= 16", l->expert_waves);
+    if (l->expert_combine_waves > 16)
+        return fail(EP_ERR_ARG, "launch.expert_combine_waves = %d: must be <= 16",
+                    l->expert_combine_waves);
+    if (l->expert_row_split > 65535 || l->expert_combine_row_split > 65535)
+        return fail(EP_ERR_ARG, "launch expert row splits must be <= 65535 (grid y limit)");
+    if (l->expert_row_split > s.row_bytes / 16)
+        return fail(EP_ERR_ARG, "launch.expert_row_split = %d: must be <= %lld",
+                    l->expert_row_split, (long long)(s.row_bytes / 16));
+    if (l->expert_combine_row_split > s.crow_bytes / 16)
+        return fail(EP_ERR_ARG, "launch.expert_combine_row_split = %d: must be <= %lld",
+                    l->expert_combine_row_split, (long long)(s.crow_bytes / 16));
     return EP_OK;
 }
 
@@ -390,6 +490,9 @@ int ep_plan_destroy(ep_plan_t* p)
 {
     if (!p)
         return ok();
+    if (p->experts > 0)
+        return fail(EP_ERR_STATE, "%d expert plan(s) made from this plan still exist: destroy "
+                    "them first", p->experts);
     int rc = EP_OK;
     if (p->launched) {
         const hipError_t e = hipStreamSynchronize(p->last_stream);
@@ -525,6 +628,7 @@ int ep_dispatch(ep_plan_t* p, const ep_dispatch_args_t* a, void* stream_ptr)
         return fail(EP_ERR_HIP, "dispatch launch failed: %s", hipGetErrorString(e));
     }
     p->dispatched = true;
+    p->dispatch_gen += 1;
     std::memcpy(p->last_ntok, a->num_tokens, sizeof(int32_t) * s.W);
     return ok();
 }
@@ -659,11 +763,212 @@ int ep_plan_set_timing(ep_plan_t* p, int enable)
     return ok();
 }
 
+size_t ep_expert_workspace_bytes(const ep_plan_t* p, int32_t cap)
+{
+    if (!p) {
+        fail(EP_ERR_NULL, "plan is NULL");
+        return 0;
+    }
+    ExShape e;
+    if (expert_shape(p->s, cap, &e) != EP_OK)
+        return 0;
+    ok();
+    return e.total;
+}
+
+int ep_expert_plan_create(ep_plan_t* p, int32_t cap, void* workspace, size_t workspace_bytes,
+                          ep_expert_plan_t** out)
+{
+    if (!p)
+        return fail(EP_ERR_NULL, "plan is NULL");
+    ExShape e;
+    const int rc = expert_shape(p->s, cap, &e);
+    if (rc != EP_OK)
+        return rc;
+    if (!workspace)
+        return fail(EP_ERR_NULL, "workspace is NULL");
+    if (!out)
+        return fail(EP_ERR_NULL, "out is NULL");
+    if (!aligned(workspace, kWorkspaceAlign))
+        return fail(EP_ERR_ALIGN, "workspace %p is not %zu-byte aligned", workspace,
+                    kWorkspaceAlign);
+    if (workspace_bytes < e.total)
+        return fail(EP_ERR_SIZE,
+                    "workspace_bytes = %zu: ep_expert_workspace_bytes() requires %zu",
+                    workspace_bytes, e.total);
+    ep_expert_plan* x = new (std::nothrow) ep_expert_plan();
+    if (!x)
+        return fail(EP_ERR_SIZE, "out of host memory for the expert plan");
+    x->plan = p;
+    x->e = e;
+    x->ws = static_cast<uint8_t*>(workspace);
+    p->experts += 1;
+    *out = x;
+    return ok();
+}
+
+int ep_expert_plan_destroy(ep_expert_plan_t* x)
+{
+    if (!x)
+        return ok();
+    int rc = EP_OK;
+    if (x->launched) {
+        const hipError_t e = hipStreamSynchronize(x->last_stream);
+        if (e != hipSuccess)
+            rc = fail(EP_ERR_HIP, "hipStreamSynchronize before destroy: %s", hipGetErrorString(e));
+    }
+    x->plan->experts -= 1;
+    delete x;
+    return rc == EP_OK ? ok() : rc;
+}
+
+int ep_convert_dispatch_output(ep_expert_plan_t* x, const ep_convert_dispatch_args_t* a,
+                               void* stream_ptr)
+{
+    if (!x)
+        return fail(EP_ERR_NULL, "plan is NULL");
+    if (!a)
+        return fail(EP_ERR_NULL, "args is NULL");
+    ep_plan* p = x->plan;
+    const Shape& s = p->s;
+    struct {
+        const void* ptr;
+        const char* name;
+        size_t align;
+    } req[] = {{a->x, "args.x", kPtrAlign},
+               {a->indices, "args.indices", 4},
+               {a->recv_num_token, "args.recv_num_token", 4},
+               {a->packed_x, "args.packed_x", kPtrAlign},
+               {a->packed_count, "args.packed_count", 4},
+               {a->packed_src_info, "args.packed_src_info", 4},
+               {a->packed_layout_range, "args.packed_layout_range", 8}};
+    for (auto& q : req) {
+        if (!q.ptr)
+            return fail(EP_ERR_NULL, "%s is NULL", q.name);
+        if (!aligned(q.ptr, q.align))
+            return fail(EP_ERR_ALIGN, "%s = %p is not %zu-byte aligned", q.name, q.ptr, q.align);
+    }
+    if (s.scale_bytes > 0) {
+        if (!a->scales || !a->packed_scales)
+            return fail(EP_ERR_NULL,
+                        "args.scales and args.packed_scales are required (scale_dim = %d)",
+                        p->cfg.scale_dim);
+        if (!aligned(a->scales, 4) || !aligned(a->packed_scales, 4))
+            return fail(EP_ERR_ALIGN, "args.scales / args.packed_scales are not 4-byte aligned");
+    } else if (a->scales || a->packed_scales) {
+        return fail(EP_ERR_ARG,
+                    "args.scales and args.packed_scales must be NULL when scale_dim = 0");
+    }
+    if (!p->dispatched)
+        return fail(EP_ERR_STATE, "convert before any dispatch on the plan");
+    const ep_launch_t l = effective_launch(p, p->last_ntok);
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    const int64_t rows = expert_rows(s, p->last_ntok);
+
+    ep::ExpertArgs ea;
+    ea.x = static_cast<const uint8_t*>(a->x);
+    ea.idx = a->indices;
+    ea.sc = static_cast<const uint32_t*>(a->scales);
+    ea.recv = a->recv_num_token;
+    ea.src_pos = ws_src_pos(p);
+    ea.px = static_cast<uint8_t*>(a->packed_x);
+    ea.psc = static_cast<uint32_t*>(a->packed_scales);
+    ea.count = a->packed_count;
+    ea.src_info = a->packed_src_info;
+    ea.layout_range = a->packed_layout_range;
+    ea.tile_counts = reinterpret_cast<int32_t*>(x->ws + x->e.off_counts);
+    ea.tile_base = reinterpret_cast<int32_t*>(x->ws + x->e.off_base);
+    ea.src_start = reinterpret_cast<int32_t*>(x->ws + x->e.off_start);
+    ea.src_prefix = reinterpret_cast<int32_t*>(x->ws + x->e.off_prefix);
+    ea.efwd = reinterpret_cast<int32_t*>(x->ws + x->e.off_efwd);
+    ea.row_vecs = (int32_t)(s.row_bytes / 16);
+    ea.piece_vecs = (ea.row_vecs + l.expert_row_split - 1) / l.expert_row_split;
+    ea.scale_dwords = (int32_t)(s.scale_bytes / 4);
+    ea.W = s.W;
+    ea.WM = (int32_t)s.WM;
+    ea.k = s.k;
+    ea.Er = s.Er;
+    ea.Pe = x->e.Pe;
+    ea.cap = x->e.cap;
+    ea.rows = (int32_t)rows;
+    ea.T = expert_tiles(rows);
+    const int row_split = (ea.row_vecs + ea.piece_vecs - 1) / ea.piece_vecs;
+
+    hipError_t e =
+        timed(p, EP_KERNEL_EXPERT_COUNT, stream, [&] { return ep::launch_expert_count(ea, stream); });
+    if (e == hipSuccess)
+        e = timed(p, EP_KERNEL_EXPERT_SCAN, stream,
+                  [&] { return ep::launch_expert_scan(ea, stream); });
+    if (e == hipSuccess)
+        e = timed(p, EP_KERNEL_EXPERT_COPY, stream, [&] {
+            return ep::launch_expert_copy(ea, l.expert_waves, row_split,
+                                          l.cache_policy == EP_CACHE_STREAM, stream);
+        });
+    x->launched = true;
+    x->last_stream = stream;
+    if (e != hipSuccess) {
+        x->converted = false;
+        return fail(EP_ERR_HIP, "convert_dispatch_output launch failed: %s", hipGetErrorString(e));
+    }
+    x->converted = true;
+    x->gen = p->dispatch_gen;
+    x->recv = a->recv_num_token;
+    x->rows = (int32_t)rows;
+    return ok();
+}
+
+int ep_convert_combine_input(ep_expert_plan_t* x, const ep_convert_combine_args_t* a,
+                             void* stream_ptr)
+{
+    if (!x)
+        return fail(EP_ERR_NULL, "plan is NULL");
+    if (!a)
+        return fail(EP_ERR_NULL, "args is NULL");
+    if (!a->packed_y)
+        return fail(EP_ERR_NULL, "args.packed_y is NULL");
+    if (!a->y)
+        return fail(EP_ERR_NULL, "args.y is NULL");
+    if (!aligned(a->packed_y, kPtrAlign) || !aligned(a->y, kPtrAlign))
+        return fail(EP_ERR_ALIGN, "args.packed_y / args.y are not 16-byte aligned");
+    ep_plan* p = x->plan;
+    if (!x->converted)
+        return fail(EP_ERR_STATE, "convert_combine_input before any convert_dispatch_output");
+    if (!p->dispatched || x->gen != p->dispatch_gen)
+        return fail(EP_ERR_STATE, "the plan dispatched again since the last "
+                    "convert_dispatch_output on this expert plan");
+    const Shape& s = p->s;
+    const ep_launch_t l = effective_launch(p, p->last_ntok);
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+
+    ep::ExpertCombineArgs ca;
+    ca.py = static_cast<const uint8_t*>(a->packed_y);
+    ca.recv = x->recv;
+    ca.efwd = reinterpret_cast<const int32_t*>(x->ws + x->e.off_efwd);
+    ca.y = static_cast<uint8_t*>(a->y);
+    ca.row_vecs = (int32_t)(s.crow_bytes / 16);
+    ca.piece_vecs = (ca.row_vecs + l.expert_combine_row_split - 1) / l.expert_combine_row_split;
+    ca.WM = (int32_t)s.WM;
+    ca.Pe = x->e.Pe;
+    ca.rows = x->rows;
+    const int row_split = (ca.row_vecs + ca.piece_vecs - 1) / ca.piece_vecs;
+    const int dtype = p->cfg.combine_dtype == EP_BF16 ? 0 : 1;
+
+    const hipError_t e = timed(p, EP_KERNEL_EXPERT_COMBINE, stream, [&] {
+        return ep::launch_expert_combine(ca, s.W, dtype, l.expert_combine_waves, row_split,
+                                         l.cache_policy == EP_CACHE_STREAM, stream);
+    });
+    x->launched = true;
+    x->last_stream = stream;
+    if (e != hipSuccess)
+        return fail(EP_ERR_HIP, "convert_combine_input launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 int ep_plan_kernel_time(ep_plan_t* p, int kernel, int32_t* count, double* total_ms)
 {
     if (!p)
         return fail(EP_ERR_NULL, "plan is NULL");
-    if (kernel < 0 || kernel > 3)
+    if (kernel < 0 || kernel >= kTimedKernels)
         return fail(EP_ERR_ARG, "kernel = %d: must be an EP_KERNEL_* value", kernel);
     if (!count || !total_ms)
         return fail(EP_ERR_NULL, "count / total_ms is NULL");

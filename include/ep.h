@@ -21,6 +21,9 @@
  *  [PR726]  "gfx1250 EPv2: EP4 topk-9 geometry; selfFirst follows
  *           MORI_EP_TOKOFF_EXT" (ROCm/mori PR 726): a token has at most
  *           min(W, k) destination rows.
+ *  [GUIDE4] "MORI-EP User Guide", section 4 "Standard MoE Compatibility
+ *           (DeepEP)": convert_dispatch_output() and convert_combine_input(),
+ *           the expert-major (3-D) layout of received rows and its inverse.
  *
  * Notation: W = world_size, M = max_num_inp_token_per_rank, k =
  * num_experts_per_token, Er = num_experts_per_rank, E = W * Er, H =
@@ -129,8 +132,8 @@ int ep_plan_create(const ep_config_t *cfg, void *workspace, size_t workspace_byt
 
 /* Destroy a plan: waits for the last stream the plan launched on, then frees
  * the plan's host state. The caller frees the workspace afterwards. NULL is a
- * no-op returning EP_OK. EP_ERR_HIP if that wait fails (the plan is freed
- * anyway). */
+ * no-op returning EP_OK. EP_ERR_STATE (nothing freed) while expert plans made
+ * from it exist. EP_ERR_HIP if that wait fails (the plan is freed anyway). */
 int ep_plan_destroy(ep_plan_t *plan);
 
 /* Dispatch arguments. Device pointers are caller-owned, 16-byte aligned, and
@@ -253,6 +256,17 @@ typedef struct ep_launch {
     int32_t combine_row_split;
     int32_t cache_policy;
     int32_t layout;
+    /* Expert-major layout (ep_convert_dispatch_output and its inverse; the
+     * cache policy above applies to them too):
+     *   expert_waves              wavefronts per copy block (64 received
+     *                             rows a block): 1..16.
+     *   expert_row_split          blocks sharing a tile's rows: 1..row_bytes/16.
+     *   expert_combine_waves      wavefronts per inverse block: 1..16.
+     *   expert_combine_row_split  pieces an inverse row is split into: 1..H/8. */
+    int32_t expert_waves;
+    int32_t expert_row_split;
+    int32_t expert_combine_waves;
+    int32_t expert_combine_row_split;
 } ep_launch_t;
 
 /* Override (launch != NULL) or reset to automatic (launch == NULL) the plan's
@@ -269,11 +283,127 @@ int ep_plan_get_launch(const ep_plan_t *plan, const int32_t *num_tokens, ep_laun
  * one kernel, how many launches were timed and their total milliseconds since
  * enabling. Kernels: EP_KERNEL_ROUTE (per-tile rank counts), EP_KERNEL_SCAN
  * (receive layout), EP_KERNEL_COPY (dispatch row and metadata copy),
- * EP_KERNEL_COMBINE (gather-reduce). Enabling creates the events (no device
- * memory); disabling destroys them. Not for use under graph capture. */
-enum { EP_KERNEL_ROUTE = 0, EP_KERNEL_SCAN = 1, EP_KERNEL_COPY = 2, EP_KERNEL_COMBINE = 3 };
+ * EP_KERNEL_COMBINE (gather-reduce), and those of the plan's expert plans:
+ * EP_KERNEL_EXPERT_COUNT (per-tile expert counts), EP_KERNEL_EXPERT_SCAN
+ * (expert lists and layout ranges), EP_KERNEL_EXPERT_COPY (rows into the
+ * expert-major layout), EP_KERNEL_EXPERT_COMBINE (the inverse). Enabling
+ * creates the events (no device memory); disabling destroys them. Not for use
+ * under graph capture. */
+enum {
+    EP_KERNEL_ROUTE = 0,
+    EP_KERNEL_SCAN = 1,
+    EP_KERNEL_COPY = 2,
+    EP_KERNEL_COMBINE = 3,
+    EP_KERNEL_EXPERT_COUNT = 4,
+    EP_KERNEL_EXPERT_SCAN = 5,
+    EP_KERNEL_EXPERT_COPY = 6,
+    EP_KERNEL_EXPERT_COMBINE = 7
+};
 int ep_plan_set_timing(ep_plan_t *plan, int enable);
 int ep_plan_kernel_time(ep_plan_t *plan, int kernel, int32_t *count, double *total_ms);
+
+/* ------------------------------------------------------------------------
+ * Expert-major layout ([GUIDE4]). After a dispatch, each rank's received
+ * rows are regrouped by the local expert that processes them, the layout a
+ * grouped GEMM reads ([W][Er][cap][H]); the inverse turns the experts'
+ * outputs back into one combine input row per received row.
+ *
+ * Semantics (readings of [GUIDE4], which names the calls and outputs only):
+ *  - On rank d, a received row goes once to each distinct local expert j
+ *    (global id d * Er + j) among its ids (R). An expert's rows keep the
+ *    receive order, so they are grouped by source rank (R).
+ *  - cap (1 <= cap <= WM, chosen by the caller) rows are kept per expert;
+ *    rows at positions >= cap are dropped, and the count still includes them,
+ *    so count > cap shows an overflow (R). cap = WM never drops.
+ *  - src_info is the row's source token index within its source rank (R);
+ *    layout_range[d][j][s] = (lo << 32) | (hi - lo), lo and hi the list
+ *    positions where source rank s's rows start and end, each clipped to
+ *    cap (R).
+ *  - The inverse writes, for every received row, the FP32 sum of its kept
+ *    experts' outputs in the order its local experts first appear in its ids,
+ *    from the first, rounded to nearest even once, unweighted (R, like
+ *    combine); a row with none is +0.
+ * Deterministic bit for bit, like the rest of the library.
+ * ------------------------------------------------------------------------ */
+typedef struct ep_expert_plan ep_expert_plan_t;
+
+/* Bytes of device workspace an expert plan of capacity cap needs on top of
+ * its plan's: per-tile expert counts and bases, source starts, and the map
+ * [W][WM][min(k, Er)] int32 the inverse gathers through. Returns 0 if plan is
+ * NULL or cap is out of range (1 <= cap <= WM and W * Er * cap <= 2^31 - 1);
+ * ep_last_error() says why. */
+size_t ep_expert_workspace_bytes(const ep_plan_t *plan, int32_t cap);
+
+/* Create an expert plan on top of a plan, whose config it shares and whose
+ * last dispatch it converts. Host-only, no HIP call. workspace: caller-owned
+ * device memory of at least ep_expert_workspace_bytes(plan, cap) bytes,
+ * 256-byte aligned, kept alive until ep_expert_plan_destroy; no
+ * initialisation needed. The plan must outlive it.
+ * Errors: EP_ERR_NULL, EP_ERR_ARG (cap), EP_ERR_ALIGN, EP_ERR_SIZE. */
+int ep_expert_plan_create(ep_plan_t *plan, int32_t cap, void *workspace,
+                          size_t workspace_bytes, ep_expert_plan_t **out);
+
+/* Waits for the last stream the expert plan launched on, then frees it. NULL
+ * is a no-op. EP_ERR_HIP if the wait fails (freed anyway). */
+int ep_expert_plan_destroy(ep_expert_plan_t *plan);
+
+/* Arguments of ep_convert_dispatch_output. Inputs are the outputs of the
+ * plan's last ep_dispatch (the call reads that dispatch's src_pos from the
+ * plan's workspace):
+ *   x                    [W][WM][H] dispatch_dtype (the dispatch's out_x),
+ *                        16-byte aligned.
+ *   indices              [W][WM][k] int32 (out_indices).
+ *   scales               [W][WM][S] (out_scales); NULL iff S == 0.
+ *   recv_num_token       DEVICE int32 [W] (recv_num_token).
+ * Outputs (device, caller-owned, must not overlap the inputs or workspaces):
+ *   packed_x             [W][Er][cap][H] dispatch_dtype, 16-byte aligned:
+ *                        slots p < min(count, cap) are written.
+ *   packed_scales        [W][Er][cap][S]; NULL iff S == 0.
+ *   packed_count         [W][Er] int32.
+ *   packed_src_info      [W][Er][cap] int32: slots p < min(count, cap).
+ *   packed_layout_range  [W][Er][W] int64, 8-byte aligned.
+ * Slots past min(count, cap) are left untouched. ([GUIDE4]: the four
+ * outputs of convert_dispatch_output, and the scales beside packed_x.) */
+typedef struct ep_convert_dispatch_args {
+    const void *x;
+    const int32_t *indices;
+    const void *scales;
+    const int32_t *recv_num_token;
+    void *packed_x;
+    void *packed_scales;
+    int32_t *packed_count;
+    int32_t *packed_src_info;
+    int64_t *packed_layout_range;
+} ep_convert_dispatch_args_t;
+
+/* Regroup the received rows of every rank by local expert ([GUIDE4]
+ * convert_dispatch_output). Asynchronous on stream; no allocation;
+ * capturable. Overwrites the expert plan's map: the inverse then works on
+ * this conversion.
+ * Errors: EP_ERR_NULL, EP_ERR_ALIGN, EP_ERR_ARG (scales pairing),
+ * EP_ERR_STATE (no dispatch yet on the plan), EP_ERR_HIP. */
+int ep_convert_dispatch_output(ep_expert_plan_t *plan, const ep_convert_dispatch_args_t *args,
+                               void *stream);
+
+/* Arguments of ep_convert_combine_input (device, 16-byte aligned):
+ *   packed_y   [W][Er][cap][H] combine_dtype: the experts' outputs, slot for
+ *              slot with packed_x (slots past min(count, cap) are not read).
+ *   y          [W][WM][H] combine_dtype: rows q < recv_num_token[d] are
+ *              written (the combine input, ep_combine_args_t.y); others
+ *              untouched. Must not overlap packed_y. */
+typedef struct ep_convert_combine_args {
+    const void *packed_y;
+    void *y;
+} ep_convert_combine_args_t;
+
+/* The inverse ([GUIDE4] convert_combine_input), through the map of the last
+ * ep_convert_dispatch_output on this expert plan, which must have converted
+ * the plan's current dispatch. Asynchronous; no allocation; capturable; may be
+ * called any number of times per conversion.
+ * Errors: EP_ERR_NULL, EP_ERR_ALIGN, EP_ERR_STATE (no conversion yet, or
+ * the plan dispatched again since), EP_ERR_HIP. */
+int ep_convert_combine_input(ep_expert_plan_t *plan, const ep_convert_combine_args_t *args,
+                             void *stream);
 
 #ifdef __cplusplus
 }

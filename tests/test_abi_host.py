@@ -39,7 +39,7 @@ def header_functions():
 
 def test_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) == 11
+    assert len(names) == 16
     assert sorted(cra.EXPORTED) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -267,7 +267,166 @@ def test_kernel_time_argument_checks(lib):
     cfg = cra.make_config(2, 256, 16, 4, 2)
     rc, plan = make_plan(lib, cfg)
     c, ms = ctypes.c_int32(), ctypes.c_double()
-    assert lib.ep_plan_kernel_time(plan, 4, ctypes.byref(c), ctypes.byref(ms)) == cra.EP_ERR_ARG
+    assert lib.ep_plan_kernel_time(plan, 8, ctypes.byref(c), ctypes.byref(ms)) == cra.EP_ERR_ARG
+    assert lib.ep_plan_kernel_time(plan, -1, ctypes.byref(c), ctypes.byref(ms)) == cra.EP_ERR_ARG
     assert lib.ep_plan_kernel_time(plan, 0, ctypes.byref(c), ctypes.byref(ms)) == 0
+    assert lib.ep_plan_kernel_time(plan, cra.EP_KERNEL_EXPERT_COMBINE, ctypes.byref(c),
+                                   ctypes.byref(ms)) == 0
     assert c.value == 0 and ms.value == 0.0
+    lib.ep_plan_destroy(plan)
+
+
+# ---------------------------------------------------------------------------
+# expert plans ("MORI-EP User Guide", section 4: convert_dispatch_output and
+# convert_combine_input)
+# ---------------------------------------------------------------------------
+
+def expected_expert_workspace(W, M, k, Er):
+    """Layout: tile counts and bases (W*Er x max(1, ceil(W*M/64)) int32 each),
+    source starts (W x W int32), in-tile prefixes (W*Er x W int32), the
+    inverse's map (W x W*M x min(k, Er) int32), each rounded up to 256 bytes."""
+    up = lambda v: (v + 255) // 256 * 256
+    T = max(1, (W * M + 63) // 64)
+    return (2 * up(4 * W * Er * T) + up(4 * W * W) + up(4 * W * Er * W)
+            + up(4 * W * W * M * min(k, Er)))
+
+
+def make_expert(lib, plan, cap, ws=FAKE_WS + (1 << 30), nbytes=None):
+    out = ctypes.c_void_p(0)
+    n = lib.ep_expert_workspace_bytes(plan, cap) if nbytes is None else nbytes
+    rc = lib.ep_expert_plan_create(plan, cap, ws, n, ctypes.byref(out))
+    return rc, out.value
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_expert_workspace_bytes_golden(lib, name):
+    wl = workloads.WORKLOADS[name]
+    rc, plan = make_plan(lib, wl_config(wl))
+    for cap in (1, 7, wl.world_size * wl.max_tokens):
+        assert lib.ep_expert_workspace_bytes(plan, cap) == expected_expert_workspace(
+            wl.world_size, wl.max_tokens, wl.topk, wl.experts_per_rank)
+    lib.ep_plan_destroy(plan)
+
+
+def test_expert_plan_create_errors_and_lifetime(lib):
+    W, M, Er = 4, 64, 16
+    cfg = cra.make_config(W, 512, M, Er, 8)
+    rc, plan = make_plan(lib, cfg)
+    for cap, code, word in ((0, cra.EP_ERR_ARG, "cap"), (W * M + 1, cra.EP_ERR_ARG, "cap")):
+        assert lib.ep_expert_workspace_bytes(plan, cap) == 0
+        assert word in cra.ep_last_error()
+        assert make_expert(lib, plan, cap, nbytes=1 << 30)[0] == code
+    assert lib.ep_expert_workspace_bytes(None, 4) == 0
+    need = lib.ep_expert_workspace_bytes(plan, 8)
+    out = ctypes.c_void_p(0)
+    assert lib.ep_expert_plan_create(None, 8, FAKE_WS, need, ctypes.byref(out)) == cra.EP_ERR_NULL
+    assert lib.ep_expert_plan_create(plan, 8, None, need, ctypes.byref(out)) == cra.EP_ERR_NULL
+    assert lib.ep_expert_plan_create(plan, 8, FAKE_WS, need, None) == cra.EP_ERR_NULL
+    assert make_expert(lib, plan, 8, ws=FAKE_WS + 64)[0] == cra.EP_ERR_ALIGN
+    assert make_expert(lib, plan, 8, nbytes=need - 1)[0] == cra.EP_ERR_SIZE
+    assert str(need) in cra.ep_last_error()
+    rc, ex = make_expert(lib, plan, 8)
+    assert rc == cra.EP_OK and ex
+    # the plan outlives its expert plans
+    assert lib.ep_plan_destroy(plan) == cra.EP_ERR_STATE
+    assert "expert plan" in cra.ep_last_error()
+    assert lib.ep_expert_plan_destroy(ex) == cra.EP_OK
+    assert lib.ep_expert_plan_destroy(None) == cra.EP_OK
+    assert lib.ep_plan_destroy(plan) == cra.EP_OK
+
+
+def test_expert_capacity_limit_is_int32(lib):
+    # W * Er * cap must stay below 2^31: packed rows are int32 in the map
+    cfg = cra.make_config(8, 256, 65536, 4096, 8)
+    rc, plan = make_plan(lib, cfg)
+    assert rc == 0
+    assert lib.ep_expert_workspace_bytes(plan, 65536) == 0
+    assert "2^31" in cra.ep_last_error()
+    assert lib.ep_expert_workspace_bytes(plan, 65535) > 0
+    lib.ep_plan_destroy(plan)
+
+
+def convert_args(**over):
+    a = dict(x=FAKE, indices=FAKE + 0x1000, scales=None, recv_num_token=FAKE + 0x2000,
+             packed_x=FAKE + 0x3000, packed_scales=None, packed_count=FAKE + 0x4000,
+             packed_src_info=FAKE + 0x5000, packed_layout_range=FAKE + 0x6000)
+    a.update(over)
+    return cra.EpConvertDispatchArgs(**a)
+
+
+@pytest.mark.parametrize("over,code,word", [
+    (dict(x=None), cra.EP_ERR_NULL, "args.x"),
+    (dict(indices=None), cra.EP_ERR_NULL, "args.indices"),
+    (dict(recv_num_token=None), cra.EP_ERR_NULL, "recv_num_token"),
+    (dict(packed_x=None), cra.EP_ERR_NULL, "packed_x"),
+    (dict(packed_count=None), cra.EP_ERR_NULL, "packed_count"),
+    (dict(packed_src_info=None), cra.EP_ERR_NULL, "packed_src_info"),
+    (dict(packed_layout_range=None), cra.EP_ERR_NULL, "packed_layout_range"),
+    (dict(x=FAKE + 8), cra.EP_ERR_ALIGN, "args.x"),
+    (dict(packed_x=FAKE + 0x3004), cra.EP_ERR_ALIGN, "packed_x"),
+    (dict(packed_layout_range=FAKE + 0x6004), cra.EP_ERR_ALIGN, "packed_layout_range"),
+    (dict(indices=FAKE + 0x1002), cra.EP_ERR_ALIGN, "indices"),
+    (dict(scales=FAKE + 0x7000, packed_scales=FAKE + 0x8000), cra.EP_ERR_ARG, "scale_dim = 0"),
+    ({}, cra.EP_ERR_STATE, "before any dispatch"),
+])
+def test_convert_dispatch_output_rejects_before_launch(lib, over, code, word):
+    cfg = cra.make_config(2, 256, 16, 4, 2)
+    rc, plan = make_plan(lib, cfg)
+    rc, ex = make_expert(lib, plan, 8)
+    a = convert_args(**over)
+    assert lib.ep_convert_dispatch_output(ex, ctypes.byref(a), None) == code
+    assert word in cra.ep_last_error()
+    assert lib.ep_convert_dispatch_output(None, ctypes.byref(a), None) == cra.EP_ERR_NULL
+    assert lib.ep_convert_dispatch_output(ex, None, None) == cra.EP_ERR_NULL
+    lib.ep_expert_plan_destroy(ex)
+    lib.ep_plan_destroy(plan)
+
+
+def test_convert_requires_scales_when_configured(lib):
+    cfg = cra.make_config(8, 7168, 128, 32, 8, "fp8", "bf16", scale_dim=56)
+    rc, plan = make_plan(lib, cfg)
+    rc, ex = make_expert(lib, plan, 64)
+    a = convert_args(scales=FAKE + 0x7000)
+    assert lib.ep_convert_dispatch_output(ex, ctypes.byref(a), None) == cra.EP_ERR_NULL
+    assert "scales" in cra.ep_last_error()
+    a = convert_args(scales=FAKE + 0x7002, packed_scales=FAKE + 0x8000)
+    assert lib.ep_convert_dispatch_output(ex, ctypes.byref(a), None) == cra.EP_ERR_ALIGN
+    lib.ep_expert_plan_destroy(ex)
+    lib.ep_plan_destroy(plan)
+
+
+def test_convert_combine_input_errors_and_state(lib):
+    cfg = cra.make_config(2, 256, 16, 4, 2)
+    rc, plan = make_plan(lib, cfg)
+    rc, ex = make_expert(lib, plan, 8)
+    ok = dict(packed_y=FAKE, y=FAKE + 0x1000)
+    for over, code, word in [(dict(packed_y=None), cra.EP_ERR_NULL, "packed_y"),
+                             (dict(y=None), cra.EP_ERR_NULL, "args.y"),
+                             (dict(y=FAKE + 8), cra.EP_ERR_ALIGN, "aligned"),
+                             ({}, cra.EP_ERR_STATE, "before any convert_dispatch_output")]:
+        a = cra.EpConvertCombineArgs(**{**ok, **over})
+        assert lib.ep_convert_combine_input(ex, ctypes.byref(a), None) == code
+        assert word in cra.ep_last_error()
+    lib.ep_expert_plan_destroy(ex)
+    lib.ep_plan_destroy(plan)
+
+
+def test_expert_launch_overrides(lib):
+    wl = workloads.WORKLOADS[workloads.HEADLINE]
+    rc, plan = make_plan(lib, wl_config(wl))
+    auto = cra.ep_plan_get_launch(plan, [4096] * 8)
+    assert auto["expert_waves"] >= 1 and auto["expert_combine_waves"] >= 1
+    assert 1 <= auto["expert_row_split"] <= 7168 * 2 // 16
+    assert 1 <= auto["expert_combine_row_split"] <= 7168 * 2 // 16
+    for bad in (dict(expert_waves=17), dict(expert_combine_waves=17),
+                dict(expert_row_split=897), dict(expert_combine_row_split=897),
+                dict(expert_row_split=70000)):
+        with pytest.raises(cra.EpError):
+            cra.ep_plan_set_launch(plan, bad)
+    cra.ep_plan_set_launch(plan, dict(expert_waves=2, expert_combine_row_split=3))
+    got = cra.ep_plan_get_launch(plan, [4096] * 8)
+    assert got["expert_waves"] == 2 and got["expert_combine_row_split"] == 3
+    # a small call splits rows to fill the chip
+    small = cra.ep_plan_get_launch(plan, [16] + [0] * 7)
+    assert small["expert_combine_row_split"] > 1
     lib.ep_plan_destroy(plan)
