@@ -34,8 +34,10 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
 METRIC = "dispatch+combine µs/call and payload HBM GB/s (% of peak), EP8 H=7168 k=8"
 KERNEL_SOURCES = [os.path.join(ROOT, "combine_route_amd", "csrc", f)
-                  for f in ("ep_kernels.hip", "ep_kernels.h", "ep_device.h", "ep_plan.cpp")]
+                  for f in ("ep_kernels.hip", "ep_expert.hip", "ep_kernels.h", "ep_device.h",
+                            "ep_plan.cpp")]
 KERNELS = {"copy": "ep_copy_kernel", "combine": "ep_combine_kernel"}
+EXPERT_KERNELS = {"copy": "ex_copy_kernel", "combine": "ex_combine_kernel"}
 
 
 def kernel_source_hash() -> str:
@@ -87,6 +89,123 @@ def algorithmic_bytes(wl, ntok, recv_total):
     return payload, {"copy": copy, "combine": combine}
 
 
+def expert_capacity(wl, ntok):
+    """Rows kept per local expert in the expert-major measurement: twice the
+    mean rows an expert receives under uniform routing (N * k / E), rounded up
+    to 64, at most W * M. Rows past it would be dropped and are reported."""
+    N = int(sum(ntok))
+    mean = -(-N * wl.topk // wl.num_experts)
+    return max(1, min(wl.world_size * wl.max_tokens, -(-2 * mean // 64) * 64))
+
+
+def expert_bytes(wl, recv_total, pairs):
+    """Bytes the expert-major copy and its inverse must move, each read or
+    written once: R received rows, `pairs` kept (row, local expert) pairs."""
+    R = int(recv_total)
+    k, Pe = wl.topk, min(wl.topk, wl.experts_per_rank)
+    row = wl.hidden * (1 if wl.dispatch_dtype == "fp8" else 2)
+    crow = wl.hidden * 2
+    sb = wl.scale_dim * 4
+    # copy: each received row's payload, scale row, ids and source read once;
+    # each kept pair's payload and scale row and source info written; the
+    # inverse's map written for every row
+    copy = R * (row + sb + 4 * k + 4) + pairs * (row + sb + 4) + R * Pe * 4
+    # inverse: each kept pair's output read, each received row written, map read
+    combine = pairs * crow + R * crow + R * Pe * 4
+    return {"copy": copy, "combine": combine}
+
+
+def measure_expert_major(args, cra, torch, np, wl, op, inp, stream):
+    """The expert-major layout and its inverse (convert_dispatch_output,
+    convert_combine_input) on the last dispatch of op: K timed steps of both,
+    per-kernel HIP-event durations and their HBM rooflines."""
+    W, M, k, Er, H = wl.world_size, wl.max_tokens, wl.topk, wl.experts_per_rank, wl.hidden
+    ntok = inp["ntok"]
+    cap = expert_capacity(wl, ntok)
+    op.expert_capacity = cap
+    ex = op._expert_state()
+    if wl.dispatch_dtype == wl.combine_dtype:
+        py = ex["packed_x"]              # identity experts, in place
+        py_kind = "identity, in place"
+    else:
+        g = torch.Generator(device="cuda").manual_seed(7)
+        py = torch.randn((W, Er, cap, H), generator=g, device="cuda").to(
+            ex["y"].dtype)
+        py_kind = "random output"
+
+    def step():
+        op.convert_dispatch_output(op.out_x, op.out_indices, op.out_scales, stream=stream)
+        op.convert_combine_input(py, stream=stream)
+
+    step()
+    torch.cuda.synchronize()
+    cnt = ex["packed_count"].cpu().numpy()
+    recv = op.recv_num_token.cpu().numpy()
+    check = "skipped"
+    if not args.no_cpu_baseline:
+        # the index outputs against the oracle (payload bytes are covered by
+        # the parity tests): first 16 bytes of each row stand in for the row
+        import oracle
+
+        x16 = np.ascontiguousarray(inp["x"].view(torch.uint8).numpy()[:, :, :16])
+        ref = oracle.dispatch(W, M, k, Er, ntok, x16, inp["idx"].numpy())
+        o = oracle.expert_layout(W, M, k, Er, cap, ref["recv"], ref["src_pos"], ref["out_x"],
+                                 ref["out_idx"])
+        ok = (np.array_equal(cnt, o["count"]) and np.array_equal(
+            ex["packed_layout_range"].cpu().numpy(), o["layout_range"]))
+        si = ex["packed_src_info"].cpu().numpy()
+        for d in range(W):
+            for j in range(Er):
+                n = min(int(o["count"][d, j]), cap)
+                ok = ok and np.array_equal(si[d, j, :n], o["src_info"][d, j, :n])
+        if not ok:
+            print("bench.py: expert-major indices differ from the oracle", file=sys.stderr)
+            sys.exit(1)
+        check = "counts, layout ranges and source info bit-exact vs oracle"
+    for _ in range(args.warmup):
+        step()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    cra.ep_plan_set_timing(op.plan, True)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kern = {}
+    for name, kid in (("count", cra.EP_KERNEL_EXPERT_COUNT), ("scan", cra.EP_KERNEL_EXPERT_SCAN),
+                      ("copy", cra.EP_KERNEL_EXPERT_COPY),
+                      ("combine", cra.EP_KERNEL_EXPERT_COMBINE)):
+        c, t = cra.ep_plan_kernel_time(op.plan, kid)
+        kern[name] = t / max(c, 1)
+    cra.ep_plan_set_timing(op.plan, False)
+    pairs = int(np.minimum(cnt, cap).sum())
+    nb = expert_bytes(wl, recv.sum(), pairs)
+    roof = {}
+    for name, kname in EXPERT_KERNELS.items():
+        a = nb[name] / (kern[name] * 1e-3) / 1e9
+        roof[name] = {"bound": "hbm", "kernel": kname, "achieved": round(a, 2),
+                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(a / PEAK_HBM_GBS, 4),
+                      "traffic": read_traffic(wl.name, kname),
+                      "algorithmic_bytes_per_launch": nb[name]}
+    return {
+        "what": "convert_dispatch_output + convert_combine_input on the dispatch above",
+        "expert_capacity": cap, "kept_pairs": pairs,
+        "dropped_rows": int(np.maximum(cnt - cap, 0).sum()),
+        "expert_output": py_kind,
+        "us_per_call": round(ms * 1e3, 2),
+        "kernel_us": {k_: round(v * 1e3, 2) for k_, v in kern.items()},
+        "check": check,
+        "roofline": roof,
+    }
+
+
 def copy_ceiling(torch, mib, steps, warmup):
     """Plain copy of mib MiB between two device buffers: reads and writes
     mib MiB each per launch."""
@@ -135,7 +254,7 @@ def _counter_means(path):
 
 
 def summarize_counters(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, cal_mib, workload):
-    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the two large kernels,
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the four large kernels,
     each scaled by what the same counter reads for the calibration copy
     (cal_mib MiB read and cal_mib MiB written per launch)."""
     import workloads
@@ -148,7 +267,7 @@ def summarize_counters(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, cal_m
     w_cal = max(v for (k, c), v in cal_w.items() if c == "WRITE_SIZE") * 1024
     f_scale, w_scale = cal_bytes / f_cal, cal_bytes / w_cal
     wl = workloads.WORKLOADS[workload]
-    for short, kname in KERNELS.items():
+    for kname in list(KERNELS.values()) + list(EXPERT_KERNELS.values()):
         fk = [v for (k, c), v in fetch.items() if kname in k]
         wk = [v for (k, c), v in write.items() if kname in k]
         if not fk or not wk:
@@ -363,6 +482,8 @@ def run(args):
                      "algorithmic_bytes_per_launch": kernel_bytes[dom]},
         "cpu_baseline": cpu_baseline,
     }
+    if not args.no_expert:
+        line["expert_major"] = measure_expert_major(args, cra, torch, np, wl, op, inp, stream)
     op.close()
     print(json.dumps(line), flush=True)
 
@@ -375,6 +496,8 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle (CPU baseline and the bit-exact check); for profiling")
+    ap.add_argument("--no-expert", action="store_true",
+                    help="skip the expert-major layout measurement")
     ap.add_argument("--graph", action="store_true",
                     help="time K replays of one step captured in a HIP graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")

@@ -38,29 +38,38 @@ constexpr int kExWaves = 4;  // count and scan: waves a block, one tile or list 
 // wrong count from reaching past the tiles.
 __device__ __forceinline__ int received(int recv, int rows) { return max(0, min(recv, rows)); }
 
-// All KB ids of a row, at addresses clamped into it, so every load issues
-// before any is waited on; ids past k are loaded but ignored.
+// Ids of a row are read KC at a time (KC = min(KB, 16), so registers stay
+// bounded at any top-k): chunk c holds slots [c * KC, c * KC + KC), loaded at
+// addresses clamped into the row so every load issues before any is used;
+// slots past k are loaded but ignored.
 template <int KB>
-__device__ __forceinline__ void load_row_ids(const int32_t* row, int k, int32_t (&ids)[KB])
+constexpr int id_chunk() { return KB < 16 ? KB : 16; }
+
+template <int KC>
+__device__ __forceinline__ void load_ids(const int32_t* row, int k, int c, int32_t (&ids)[KC])
 {
 #pragma unroll
-    for (int i = 0; i < KB; ++i)
-        ids[i] = row[min(i, k - 1)];
+    for (int i = 0; i < KC; ++i)
+        ids[i] = row[min(c * KC + i, k - 1)];
 }
 
 // Word w of a row's set of local experts: bit b for local expert 64w + b.
 // An id is local when it lies in [lo, lo + Er).
-template <int KB>
-__device__ __forceinline__ uint64_t local_word(const int32_t (&ids)[KB], int k, bool valid,
-                                               int64_t lo, int Er, int w)
+template <int KC>
+__device__ __forceinline__ uint64_t local_word(const int32_t* row, int k, bool valid, int64_t lo,
+                                               int Er, int w)
 {
     uint64_t m = 0;
+    for (int c = 0; c * KC < k; ++c) {
+        int32_t ids[KC];
+        load_ids<KC>(row, k, c, ids);
 #pragma unroll
-    for (int i = 0; i < KB; ++i) {
-        const int64_t j = (int64_t)ids[i] - lo;
-        const int64_t b = j - 64 * w;
-        if (valid && i < k && j >= 0 && j < Er && b >= 0 && b < 64)
-            m |= 1ull << b;
+        for (int i = 0; i < KC; ++i) {
+            const int64_t j = (int64_t)ids[i] - lo;
+            const int64_t b = j - 64 * w;
+            if (valid && c * KC + i < k && j >= 0 && j < Er && b >= 0 && b < 64)
+                m |= 1ull << b;
+        }
     }
     return m;
 }
@@ -92,8 +101,8 @@ __global__ __launch_bounds__(kExWaves * kWave) void ex_count_kernel(ExpertArgs a
             start[lane] = 0;
         return;
     }
-    int32_t ids[KB];
-    load_row_ids<KB>(a.idx + (row0 + (valid ? q : 0)) * a.k, a.k, ids);
+    constexpr int KC = id_chunk<KB>();
+    const int32_t* ids = a.idx + (row0 + (valid ? q : 0)) * a.k;
 
     // Rows are in source-rank order, so source s starts at the first row
     // whose source is >= s. The row that starts sources (s_prev, s_cur]
@@ -112,7 +121,7 @@ __global__ __launch_bounds__(kExWaves * kWave) void ex_count_kernel(ExpertArgs a
             start[s] = R;
 
     for (int w = 0; 64 * w < a.Er; ++w) {
-        const uint64_t m = local_word<KB>(ids, a.k, valid, lo, a.Er, w);
+        const uint64_t m = local_word<KC>(ids, a.k, valid, lo, a.Er, w);
         const int nj = min(kWave, a.Er - 64 * w);
         int c = 0;
         for (int jj = 0; jj < nj; ++jj) {
@@ -204,35 +213,102 @@ __global__ __launch_bounds__(1024) void ex_copy_kernel(ExpertArgs a)
     const int64_t row0 = (int64_t)d * a.WM + q0;
     const int64_t lo = (int64_t)d * a.Er;
 
-    if (wave == 0) {
-        const bool valid = lane < cnt;
-        int32_t ids[KB];
-        load_row_ids<KB>(a.idx + (row0 + (valid ? lane : 0)) * a.k, a.k, ids);
-        int n = 0;
+    // This wave's items: rows wave, wave + nwaves, ... of the tile, each cut
+    // into nch chunks of its row piece [vbeg, vend).
+    const uint32_t row_bytes = (uint32_t)a.row_vecs * 16u;
+    const int vbeg = piece * a.piece_vecs;
+    const int vend = min(a.row_vecs, vbeg + a.piece_vecs);
+    const int nch = (vend - vbeg + kWave * VPL - 1) / (kWave * VPL);
+    const int items = (wave < cnt ? (cnt - wave + nwaves - 1) / nwaves : 0) * nch;
+    auto load_item = [&](int it, u32x4 (&v)[VPL]) {
+        const int r = wave + (it / nch) * nwaves;
+        const int v0 = vbeg + (it % nch) * kWave * VPL;
+        const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.x + (row0 + r) * row_bytes, row_bytes);
 #pragma unroll
-        for (int i = 0; i < KB; ++i) {
-            const int64_t j = (int64_t)ids[i] - lo;
-            if (valid && i < a.k && j >= 0 && j < a.Er) {
-                bool seen = false;
-                for (int u = 0; u < n; ++u)
-                    seen = seen || s_j[lane][u] == (int)j;
-                if (!seen)
-                    s_j[lane][n++] = (int)j;
+        for (int u = 0; u < VPL; ++u) {
+            const int vv = v0 + u * kWave + lane;
+            if (vv < vend)
+                v[u] = bload16<Policy<kStream>::copy_load>(rs, (uint32_t)vv * 16u);
+        }
+    };
+    auto store_item = [&](int it, const u32x4 (&v)[VPL]) {
+        const int r = wave + (it / nch) * nwaves;
+        const int v0 = vbeg + (it % nch) * kWave * VPL;
+        const int n = uniform(s_n[r]);
+        for (int i = 0; i < n; ++i) {
+            const int64_t gi = uniform(s_p[r][i]);
+            const __amdgpu_buffer_rsrc_t rd = row_rsrc(a.px + gi * row_bytes, row_bytes);
+#pragma unroll
+            for (int u = 0; u < VPL; ++u) {
+                const int vv = v0 + u * kWave + lane;
+                if (vv < vend)
+                    bstore16<Policy<kStream>::copy_store>(v[u], rd, (uint32_t)vv * 16u);
             }
         }
+    };
+    // Small pieces (small rows or small calls, where time is latency): each
+    // wave's first item loads while wave 0 routes the tile.
+    u32x4 A[VPL], B[VPL];
+    if (VPL < 8 && items > 0)
+        load_item(0, A);
+
+    if (wave == 0) {
+        const bool valid = lane < cnt;
+        constexpr int KC = id_chunk<KB>();
+        const int32_t* ids = a.idx + (row0 + (valid ? lane : 0)) * a.k;
+        // the row's distinct local experts in first-occurrence order; with one
+        // mask word (Er <= 64) repeats are found in a register, else in LDS
+        int n = 0;
+        uint64_t seen = 0;
+        for (int c = 0; c * KC < a.k; ++c) {
+            int32_t id[KC];
+            load_ids<KC>(ids, a.k, c, id);
+#pragma unroll
+            for (int i = 0; i < KC; ++i) {
+                const int64_t j = (int64_t)id[i] - lo;
+                if (!valid || c * KC + i >= a.k || j < 0 || j >= a.Er)
+                    continue;
+                if (a.Er <= kWave) {
+                    if ((seen >> j) & 1)
+                        continue;
+                    seen |= 1ull << j;
+                } else {
+                    bool dup = false;
+                    for (int u = 0; u < n; ++u)
+                        dup = dup || s_j[lane][u] == (int)j;
+                    if (dup)
+                        continue;
+                }
+                s_j[lane][n++] = (int)j;
+            }
+        }
+        int n_max = n;  // the wave's longest list
+#pragma unroll
+        for (int off = kWave / 2; off > 0; off >>= 1)
+            n_max = max(n_max, __shfl_xor(n_max, off));
+        // Positions, one mask word (64 experts) at a time: lane jj holds the
+        // ballot of expert 64w + jj over the tile and its tile base; each
+        // lane fetches both for its own entries with cross-lane reads.
         for (int w = 0; 64 * w < a.Er; ++w) {
-            const uint64_t m = local_word<KB>(ids, a.k, valid, lo, a.Er, w);
+            const uint64_t m = a.Er <= kWave ? seen : local_word<KC>(ids, a.k, valid, lo, a.Er, w);
             const int nj = min(kWave, a.Er - 64 * w);
             const int bw = lane < nj ? a.tile_base[(lo + 64 * w + lane) * a.T + tile] : 0;
+            uint64_t mine = 0;
             for (int jj = 0; jj < nj; ++jj) {
-                const bool has = (m >> jj) & 1;
-                const uint64_t b = __ballot(has);
-                if (has) {
-                    const int p = __builtin_amdgcn_readlane(bw, jj) + lanes_below(b);
-                    for (int u = 0; u < n; ++u)
-                        if (s_j[lane][u] == 64 * w + jj)
-                            s_p[lane][u] = p;
-                }
+                const uint64_t b = __ballot((m >> jj) & 1);
+                if (lane == jj)
+                    mine = b;
+            }
+            const int mlo = (int)(uint32_t)mine;
+            const int mhi = (int)(uint32_t)(mine >> 32);
+            for (int u = 0; u < n_max; ++u) {
+                const int j = u < n ? s_j[lane][u] - 64 * w : -1;
+                const int src = j & (kWave - 1);
+                const uint32_t blo = (uint32_t)__shfl(mlo, src);
+                const uint32_t bhi = (uint32_t)__shfl(mhi, src);
+                const int base = __shfl(bw, src);
+                if (j >= 0 && j < kWave)
+                    s_p[lane][u] = base + lanes_below(((uint64_t)bhi << 32) | blo);
             }
         }
         int kept = 0;  // positions past the capacity are dropped
@@ -266,32 +342,26 @@ __global__ __launch_bounds__(1024) void ex_copy_kernel(ExpertArgs a)
         }
     }
 
-    const uint32_t row_bytes = (uint32_t)a.row_vecs * 16u;
-    const int vbeg = piece * a.piece_vecs;
-    const int vend = min(a.row_vecs, vbeg + a.piece_vecs);
-    for (int r = wave; r < cnt; r += nwaves) {
-        const int n = uniform(s_n[r]);
-        if (n == 0)
-            continue;
-        const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.x + (row0 + r) * row_bytes, row_bytes);
-        for (int v0 = vbeg; v0 < vend; v0 += kWave * VPL) {
-            u32x4 v[VPL];
-#pragma unroll
-            for (int u = 0; u < VPL; ++u) {
-                const int vv = v0 + u * kWave + lane;
-                if (vv < vend)
-                    v[u] = bload16<Policy<kStream>::copy_load>(rs, (uint32_t)vv * 16u);
+    if constexpr (VPL < 8) {
+        // two items in flight: item i + 1 loads while item i stores
+        for (int it = 0; it < items; it += 2) {
+            if (it + 1 < items)
+                load_item(it + 1, B);
+            store_item(it, A);
+            if (it + 1 < items) {
+                if (it + 2 < items)
+                    load_item(it + 2, A);
+                store_item(it + 1, B);
             }
-            for (int i = 0; i < n; ++i) {
-                const int64_t gi = uniform(s_p[r][i]);
-                const __amdgpu_buffer_rsrc_t rd = row_rsrc(a.px + gi * row_bytes, row_bytes);
-#pragma unroll
-                for (int u = 0; u < VPL; ++u) {
-                    const int vv = v0 + u * kWave + lane;
-                    if (vv < vend)
-                        bstore16<Policy<kStream>::copy_store>(v[u], rd, (uint32_t)vv * 16u);
-                }
-            }
+        }
+    } else {
+        // large pieces (throughput): one chunk a wave in flight, which keeps
+        // the register count, and so the waves resident per SIMD, lowest
+        for (int it = 0; it < items; ++it) {
+            if (uniform(s_n[wave + (it / nch) * nwaves]) == 0)
+                continue;  // a row without a kept expert is not read
+            load_item(it, A);
+            store_item(it, A);
         }
     }
 }

@@ -256,17 +256,23 @@ typedef struct ep_launch {
     int32_t combine_row_split;
     int32_t cache_policy;
     int32_t layout;
-    /* Expert-major layout (ep_convert_dispatch_output and its inverse; the
-     * cache policy above applies to them too):
+    /* Expert-major layout (ep_convert_dispatch_output and its inverse):
      *   expert_waves              wavefronts per copy block (64 received
      *                             rows a block): 1..16.
      *   expert_row_split          blocks sharing a tile's rows: 1..row_bytes/16.
      *   expert_combine_waves      wavefronts per inverse block: 1..16.
-     *   expert_combine_row_split  pieces an inverse row is split into: 1..H/8. */
+     *   expert_combine_row_split  pieces an inverse row is split into: 1..H/8.
+     *   expert_cache_policy       as cache_policy, for these calls; automatic:
+     *                             keep when their rows (each token's
+     *                             min(W, k) received rows and k expert rows,
+     *                             out and back) stay within 512 MB (rows read
+     *                             were just written, so they partly hit the
+     *                             256 MB cache), stream above. */
     int32_t expert_waves;
     int32_t expert_row_split;
     int32_t expert_combine_waves;
     int32_t expert_combine_row_split;
+    int32_t expert_cache_policy;
 } ep_launch_t;
 
 /* Override (launch != NULL) or reset to automatic (launch == NULL) the plan's

@@ -420,7 +420,8 @@ def test_expert_launch_overrides(lib):
     assert 1 <= auto["expert_combine_row_split"] <= 7168 * 2 // 16
     for bad in (dict(expert_waves=17), dict(expert_combine_waves=17),
                 dict(expert_row_split=897), dict(expert_combine_row_split=897),
-                dict(expert_row_split=70000)):
+                dict(expert_row_split=70000), dict(expert_cache_policy=3),
+                dict(expert_cache_policy=-1)):
         with pytest.raises(cra.EpError):
             cra.ep_plan_set_launch(plan, bad)
     cra.ep_plan_set_launch(plan, dict(expert_waves=2, expert_combine_row_split=3))
@@ -429,4 +430,7 @@ def test_expert_launch_overrides(lib):
     # a small call splits rows to fill the chip
     small = cra.ep_plan_get_launch(plan, [16] + [0] * 7)
     assert small["expert_combine_row_split"] > 1
+    # the expert calls' own footprint decides their cache policy
+    assert auto["expert_cache_policy"] == cra.EP_CACHE_STREAM
+    assert small["expert_cache_policy"] == cra.EP_CACHE_KEEP
     lib.ep_plan_destroy(plan)

@@ -196,8 +196,8 @@ def test_world_expert_topk_sweep(W, E, k):
     dict(expert_waves=1, expert_combine_waves=1),
     dict(expert_waves=16, expert_row_split=7, expert_combine_waves=16,
          expert_combine_row_split=5),
-    dict(expert_row_split=1, expert_combine_row_split=1, cache_policy=cra.EP_CACHE_STREAM),
-    dict(expert_waves=3, expert_row_split=2, cache_policy=cra.EP_CACHE_KEEP),
+    dict(expert_row_split=1, expert_combine_row_split=1, expert_cache_policy=cra.EP_CACHE_STREAM),
+    dict(expert_waves=3, expert_row_split=2, expert_cache_policy=cra.EP_CACHE_KEEP),
 ])
 def test_geometry_does_not_change_results(launch):
     wl = workloads.custom("ex_geom_ep4_t200_h1024", 4, 200, 1024, 8, 64, "bf16", ragged=True,
@@ -366,7 +366,7 @@ def _random_case(seed):
                       expert_row_split=int(rng.integers(1, max(2, H // 8))),
                       expert_combine_waves=int(rng.integers(1, 17)),
                       expert_combine_row_split=int(rng.integers(1, max(2, H // 8))),
-                      cache_policy=int(rng.integers(0, 3)))
+                      expert_cache_policy=int(rng.integers(0, 3)))
         launch["expert_row_split"] = min(launch["expert_row_split"],
                                          H * (1 if dd == "fp8" else 2) // 16)
         launch["expert_combine_row_split"] = min(launch["expert_combine_row_split"], H * 2 // 16)
