@@ -42,7 +42,7 @@ def _load():
     lib.oracle_combine_push.restype = I
     lib.oracle_expert_layout.argtypes = [I, I, I, I, I, Z, Z, P, P, P, P, P, P, P, P, P, P]
     lib.oracle_expert_layout.restype = I
-    lib.oracle_expert_combine.argtypes = [I, I, I, I, I, I, I, P, P, P, P]
+    lib.oracle_expert_combine.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P]
     lib.oracle_expert_combine.restype = I
     for name in ("oracle_f32_to_bf16_n", "oracle_f32_to_f16_n",
                  "oracle_bf16_to_f32_n", "oracle_f16_to_f32_n"):
@@ -182,17 +182,19 @@ def expert_layout(W, M, k, Er, cap, recv, src_pos, x, idx, scales=None, fill=-1)
     return out
 
 
-def expert_combine(W, M, k, Er, cap, H, dtype, recv, idx, py):
+def expert_combine(W, M, k, Er, cap, H, dtype, recv, idx, py, w=None):
     """Inverse of the expert-major layout by definition: ``py`` holds 16-bit
-    words [W, Er, cap, H]. Returns y uint16 [W, W*M, H]; rows past recv[d]
-    stay zero."""
+    words [W, Er, cap, H]; ``w`` the dispatched weight rows float32
+    [W, W*M, k] for the weighted form (None: unweighted). Returns y uint16
+    [W, W*M, H]; rows past recv[d] stay zero."""
     lib = _load()
     recv = _c(np.asarray(recv, dtype=np.int32))
     idx = _c(idx, np.int32)
+    w = _c(w, np.float32)
     py = _c(py).view(np.uint16)
     y = np.zeros((W, W * M, H), np.uint16)
-    rc = lib.oracle_expert_combine(W, M, k, Er, cap, H, dtype, _ptr(recv), _ptr(idx), _ptr(py),
-                                   _ptr(y))
+    rc = lib.oracle_expert_combine(W, M, k, Er, cap, H, dtype, _ptr(recv), _ptr(idx), _ptr(w),
+                                   _ptr(py), _ptr(y))
     if rc != 0:
         raise RuntimeError(f"oracle_expert_combine failed ({rc})")
     return y

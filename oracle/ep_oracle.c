@@ -461,14 +461,15 @@ int oracle_expert_layout(int W, int M, int k, int Er, int cap, size_t row_bytes,
 }
 
 int oracle_expert_combine(int W, int M, int k, int Er, int cap, int H, int dtype,
-                          const int32_t *recv, const int32_t *idx, const uint16_t *py,
-                          uint16_t *y)
+                          const int32_t *recv, const int32_t *idx, const float *w,
+                          const uint16_t *py, uint16_t *y)
 {
     const int64_t WM = (int64_t)W * M;
     int32_t *js = malloc(sizeof(int32_t) * (size_t)(k > 0 ? k : 1));
     int64_t *rows = malloc(sizeof(int64_t) * (size_t)(k > 0 ? k : 1));
+    float *cw = malloc(sizeof(float) * (size_t)(k > 0 ? k : 1));
     int64_t *next = malloc(sizeof(int64_t) * (size_t)Er);
-    if (!js || !rows || !next) { free(js); free(rows); free(next); return -1; }
+    if (!js || !rows || !cw || !next) { free(js); free(rows); free(cw); free(next); return -1; }
     for (int d = 0; d < W; ++d) {
         for (int j = 0; j < Er; ++j)
             next[j] = 0;
@@ -481,14 +482,43 @@ int oracle_expert_combine(int W, int M, int k, int Er, int cap, int H, int dtype
             int kept = 0;
             for (int i = 0; i < n; ++i) {
                 int64_t p = next[js[i]]++;
-                if (p < cap)
-                    rows[kept++] = ((int64_t)d * Er + js[i]) * cap + p;
+                if (p >= cap)
+                    continue;
+                rows[kept] = ((int64_t)d * Er + js[i]) * cap + p;
+                if (w) {
+                    /* the expert's weight: the row's weights on every slot
+                     * that names it, summed in slot order from the first */
+                    int first = 1;
+                    float c = 0.0f;
+                    for (int s = 0; s < k; ++s)
+                        if (idx[row * k + s] == d * Er + js[i]) {
+                            c = first ? w[row * k + s] : c + w[row * k + s];
+                            first = 0;
+                        }
+                    cw[kept] = c;
+                }
+                ++kept;
             }
-            fold_token(kept, rows, H, k, dtype, py, NULL, y + (size_t)row * H, NULL);
+            uint16_t *out = y + (size_t)row * H;
+            if (!w) {
+                fold_token(kept, rows, H, k, dtype, py, NULL, out, NULL);
+                continue;
+            }
+            for (int h = 0; h < H; ++h) {
+                if (kept == 0) {
+                    out[h] = 0;
+                    continue;
+                }
+                float acc = cw[0] * widen(py[(size_t)rows[0] * H + h], dtype);
+                for (int i = 1; i < kept; ++i)
+                    acc = fmaf(cw[i], widen(py[(size_t)rows[i] * H + h], dtype), acc);
+                out[h] = narrow(acc, dtype);
+            }
         }
     }
     free(js);
     free(rows);
+    free(cw);
     free(next);
     return 0;
 }

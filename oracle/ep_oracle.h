@@ -37,7 +37,8 @@
  * but counted; source info is the source token index; a layout range packs
  * (start << 32) | count of one source rank's rows in an expert's list; the
  * inverse sums a row's kept expert outputs in first-occurrence order like the
- * combine and rounds once.
+ * combine and rounds once; weighted, each output is scaled by the sum of the
+ * row's weights on the slots naming its expert, with a fused multiply-add.
  *
  * Parity status: every function here is pinned by tests that do not call it
  * through itself (brute force, a second formulation, closed forms, library
@@ -129,10 +130,16 @@ int oracle_expert_layout(int W, int M, int k, int Er, int cap, size_t row_bytes,
  * recv[d] of rank d, the sum of its kept expert outputs py[d][j][p] (bf16 or
  * fp16, H wide), in the order its local experts first appear in its id row,
  * folded in FP32 from the first and rounded once; a row with none is +0.
+ * With routing weights w[W][WM][k] (the dispatched weight rows; NULL for the
+ * unweighted sum), each output is scaled by its expert's weight for the row,
+ * the FP32 sum of the row's weights on the slots naming that expert (slot
+ * order, from the first): acc = c * v for the first kept output, then
+ * acc = fma(c, v, acc) ("MORI-EP User Guide", section 3: combine weights are
+ * for a weighted combination).
  * Writes y[W][WM][H] rows q < recv[d]; others untouched. Returns 0. */
 int oracle_expert_combine(int W, int M, int k, int Er, int cap, int H, int dtype,
-                          const int32_t *recv, const int32_t *idx, const uint16_t *py,
-                          uint16_t *y);
+                          const int32_t *recv, const int32_t *idx, const float *w,
+                          const uint16_t *py, uint16_t *y);
 
 /* IEEE 754 conversions used by the combine cast, written from the formats'
  * definitions: binary32 -> bfloat16 / binary16 with round-to-nearest-even,

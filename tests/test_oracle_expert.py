@@ -20,7 +20,13 @@ Pins, none of which calls the oracle through itself:
   identity experts give RNE(n * x) with the cast done by torch, and rows whose
   outputs are (2^24, 1, -2^24) in first-occurrence order fold to +0;
 * the round trip dispatch -> layout -> identity experts -> inverse -> combine
-  gives K * x for integer payloads, K = the token's distinct valid experts.
+  gives K * x for integer payloads, K = the token's distinct valid experts;
+* the weighted inverse: a hand-worked case where one fused multiply-add per
+  term gives 2^-24 and a separate multiply and add gives +0; a repeated
+  expert's weights add up; dyadic weights over integer outputs are exact
+  (float64 reference); and the weighted round trip through dispatch and
+  combine equals the mixture-of-experts sum over the token's valid slots of
+  w_i * x.
 """
 import json
 import os
@@ -296,3 +302,92 @@ def test_round_trip_through_dispatch_and_combine(wl):
         for t in range(inp["ntok"][r]):
             K = len({int(e) for e in ids[r, t] if 0 <= e < E})
             assert torch.equal(got[r, t], x[r, t].double() * K), (r, t)
+
+
+# --------------------------------------------------------------------------
+# the weighted inverse ("MORI-EP User Guide", section 3: combine weights are
+# for a weighted combination)
+# --------------------------------------------------------------------------
+
+def _one_row_case(ids, weights, outputs, k, Er=2):
+    """One rank, one received row naming `ids`, the given weights, and the
+    expert outputs (bf16 words, H = 1) in slot p = 0 of each local expert."""
+    W, M, cap = 1, 2, 2
+    idx = np.full((W, W * M, k), -1, np.int32)
+    idx[0, 0] = ids
+    w = np.zeros((W, W * M, k), np.float32)
+    w[0, 0] = weights
+    py = np.zeros((W, Er, cap, 1), np.uint16)
+    for j, v in outputs.items():
+        py[0, j, 0, 0] = v
+    return oracle.expert_combine(W, M, k, Er, cap, 1, oracle.BF16, [1], idx, py, w=w)[0, 0, 0]
+
+
+def test_weighted_inverse_uses_one_fused_multiply_add_per_term():
+    # c0 = -(1 + 2^-17), c1 = 1 + 2^-17, both outputs 1 + 2^-7 (bf16 0x3F81).
+    # c0 * v rounds the exact -(1 + 2^-7 + 2^-17 + 2^-24) (a tie) to
+    # -(1 + 2^-7 + 2^-17); fma(c1, v, acc) then leaves exactly 2^-24 (bf16
+    # 0x3380). A separate multiply and add would give +0.
+    c = np.float32(1 + 2.0 ** -17)
+    got = _one_row_case([0, 1], [-c, c], {0: 0x3F81, 1: 0x3F81}, k=2)
+    assert got == 0x3380
+
+
+def test_weighted_inverse_sums_the_weights_of_a_repeated_expert():
+    # ids [1, 1]: expert 1 processes the row once, weight 0.5 + 0.25; output 2
+    got = _one_row_case([1, 1], [0.5, 0.25], {1: 0x4000}, k=2)
+    assert got == 0x3FC0                                    # 1.5
+
+
+def test_weighted_inverse_exact_closed_form():
+    wl = CASES[1]
+    W, M, k, Er, H = wl.world_size, wl.max_tokens, wl.topk, wl.experts_per_rank, wl.hidden
+    inp, x, disp = _dispatched(wl)
+    lists = _local_lists(W, k, Er, disp["recv"], disp["out_idx"])
+    groups = _sorted_triples(W, Er, lists)
+    pos = _positions(W, Er, groups)
+    cap = max(len(v) for v in groups.values())
+    g = torch.Generator().manual_seed(21)
+    wts = np.array([0.25, 0.5, 1.0, 2.0, -1.0, -0.5], np.float32)
+    w = wts[torch.randint(0, len(wts), (W, W * M, k), generator=g).numpy()]
+    vals = torch.randint(-8, 9, (W, Er, cap, H), generator=g)
+    py = vals.to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    y = oracle.expert_combine(W, M, k, Er, cap, H, oracle.FP16, disp["recv"], disp["out_idx"],
+                              py, w=w)
+    got = torch.from_numpy(y.view(np.int16)).view(torch.float16).double().numpy()
+    # every product and partial sum is a small dyadic number: exact in binary32
+    for (d, q), js in lists.items():
+        want = np.zeros(H)
+        ids = disp["out_idx"][d, q]
+        for j in js:
+            c = sum(float(w[d, q, s]) for s in range(k) if ids[s] == d * Er + j)
+            want += c * vals[d, j, pos[(d, int(j), q)]].numpy().astype(np.float64)
+        assert np.array_equal(got[d, q], want), (d, q)
+
+
+@pytest.mark.parametrize("wl", [CASES[0], CASES[3], CASES[4]], ids=lambda w: w.name)
+def test_weighted_round_trip_is_the_moe_sum(wl):
+    """dispatch -> layout -> identity experts -> weighted inverse -> combine
+    gives sum over the token's valid slots of w_i * x, the mixture-of-experts
+    output, for integer payloads and dyadic weights (all exact)."""
+    W, M, k, Er, H, E = (wl.world_size, wl.max_tokens, wl.topk, wl.experts_per_rank, wl.hidden,
+                         wl.num_experts)
+    inp, x, disp = _dispatched(wl, integer_payload=True)
+    g = torch.Generator().manual_seed(22)
+    wts = np.array([0.25, 0.5, 1.0, 2.0], np.float32)
+    w_tok = wts[torch.randint(0, 4, (W, M, k), generator=g).numpy()]
+    disp = oracle.dispatch(W, M, k, Er, inp["ntok"], x.view(torch.uint8).numpy(),
+                           inp["idx"].numpy(), w_tok)
+    cap = W * M
+    o = oracle.expert_layout(W, M, k, Er, cap, disp["recv"], disp["src_pos"], disp["out_x"],
+                             disp["out_idx"])
+    y = oracle.expert_combine(W, M, k, Er, cap, H, oracle.BF16, disp["recv"], disp["out_idx"],
+                              o["px"].view(np.uint16), w=disp["out_w"])
+    out, _ = oracle.combine(W, M, k, H, oracle.BF16, inp["ntok"], disp["fwd"], y)
+    got = torch.from_numpy(out.view(np.int16)).view(torch.bfloat16).double()
+    ids = inp["idx"].numpy()
+    for r in range(W):
+        for t in range(inp["ntok"][r]):
+            c = sum(float(w_tok[r, t, s]) for s in range(k) if 0 <= ids[r, t, s] < E)
+            want = (x[r, t].double() * c).to(torch.bfloat16).double()
+            assert torch.equal(got[r, t], want), (r, t)
