@@ -65,12 +65,13 @@ class EpLaunch(ctypes.Structure):
 
 class EpConvertDispatchArgs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
-        "x", "indices", "scales", "recv_num_token", "packed_x", "packed_scales",
+        "x", "indices", "weights", "scales", "recv_num_token", "packed_x", "packed_scales",
         "packed_count", "packed_src_info", "packed_layout_range")]
 
 
 class EpConvertCombineArgs(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("packed_y", "y")]
+    _fields_ = [("packed_y", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("apply_weights", ctypes.c_int32)]
 
 
 class EpError(RuntimeError):
@@ -310,14 +311,15 @@ def ep_expert_plan_destroy(eplan: int) -> None:
     _check("ep_expert_plan_destroy", load().ep_expert_plan_destroy(eplan))
 
 
-def _convert_dispatch_args(cfg: EpConfig, cap: int, x, indices, scales, recv_num_token,
-                           packed_x, packed_scales, packed_count, packed_src_info,
-                           packed_layout_range):
+def _convert_dispatch_args(cfg: EpConfig, cap: int, x, indices, weights, scales,
+                           recv_num_token, packed_x, packed_scales, packed_count,
+                           packed_src_info, packed_layout_range):
     W, M, k, row, _, srow = _sizes(cfg)
     WM = W * M
     Er = cfg.num_experts_per_rank
     return EpConvertDispatchArgs(
         _dev(x, "x", W * WM * row), _dev(indices, "indices", W * WM * k * 4),
+        _dev(weights, "weights", W * WM * k * 4),
         _dev(scales, "scales", W * WM * srow), _dev(recv_num_token, "recv_num_token", W * 4),
         _dev(packed_x, "packed_x", W * Er * cap * row),
         _dev(packed_scales, "packed_scales", W * Er * cap * srow),
@@ -326,27 +328,27 @@ def _convert_dispatch_args(cfg: EpConfig, cap: int, x, indices, scales, recv_num
         _dev(packed_layout_range, "packed_layout_range", W * Er * W * 8))
 
 
-def _convert_combine_args(cfg: EpConfig, cap: int, packed_y, y):
+def _convert_combine_args(cfg: EpConfig, cap: int, packed_y, y, apply_weights=False):
     W, M, _, _, crow, _ = _sizes(cfg)
     Er = cfg.num_experts_per_rank
     return EpConvertCombineArgs(_dev(packed_y, "packed_y", W * Er * cap * crow),
-                                _dev(y, "y", W * W * M * crow))
+                                _dev(y, "y", W * W * M * crow), 1 if apply_weights else 0)
 
 
-def ep_convert_dispatch_output(eplan: int, cfg: EpConfig, cap: int, x, indices, scales,
-                               recv_num_token, packed_x, packed_scales, packed_count,
+def ep_convert_dispatch_output(eplan: int, cfg: EpConfig, cap: int, x, indices, weights,
+                               scales, recv_num_token, packed_x, packed_scales, packed_count,
                                packed_src_info, packed_layout_range, stream=None) -> None:
     """ep_convert_dispatch_output(); tensors as in include/ep.h."""
-    a = _convert_dispatch_args(cfg, cap, x, indices, scales, recv_num_token, packed_x,
+    a = _convert_dispatch_args(cfg, cap, x, indices, weights, scales, recv_num_token, packed_x,
                                packed_scales, packed_count, packed_src_info, packed_layout_range)
     _check("ep_convert_dispatch_output",
            load().ep_convert_dispatch_output(eplan, ctypes.byref(a), _stream(stream)))
 
 
 def ep_convert_combine_input(eplan: int, cfg: EpConfig, cap: int, packed_y, y,
-                             stream=None) -> None:
+                             apply_weights=False, stream=None) -> None:
     """ep_convert_combine_input(); tensors as in include/ep.h."""
-    a = _convert_combine_args(cfg, cap, packed_y, y)
+    a = _convert_combine_args(cfg, cap, packed_y, y, apply_weights)
     _check("ep_convert_combine_input",
            load().ep_convert_combine_input(eplan, ctypes.byref(a), _stream(stream)))
 
@@ -455,18 +457,23 @@ class EpDispatchCombineOp:
         return self._ex
 
     def convert_dispatch_output(self, dispatch_out_x, dispatch_out_topk_idx,
-                                dispatch_out_scales=None, stream=None):
+                                dispatch_out_scales=None, dispatch_out_weights=None,
+                                stream=None):
         """The last dispatch's received rows regrouped by local expert ("MORI-EP
         User Guide", section 4, convert_dispatch_output). Returns
         (packed_recv_x, packed_recv_count, packed_recv_src_info,
         packed_recv_layout_range); packed_recv_x is (rows, scale rows) when
-        the config has scales. Views of buffers the next call overwrites."""
+        the config has scales. Views of buffers the next call overwrites.
+        With dispatch_out_weights, each kept pair records its expert's weight
+        for a weighted convert_combine_input."""
         ex = self._expert_state()
-        given = (dispatch_out_x, dispatch_out_topk_idx, dispatch_out_scales)
+        given = (dispatch_out_x, dispatch_out_topk_idx, dispatch_out_scales,
+                 dispatch_out_weights)
         c = ex["cache"]
         if c is None or not _same_tensors(c[0], given):
             a = _convert_dispatch_args(self.cfg, self.expert_capacity, dispatch_out_x,
-                                       dispatch_out_topk_idx, dispatch_out_scales,
+                                       dispatch_out_topk_idx, dispatch_out_weights,
+                                       dispatch_out_scales,
                                        self.recv_num_token, ex["packed_x"], ex["packed_scales"],
                                        ex["packed_count"], ex["packed_src_info"],
                                        ex["packed_layout_range"])
@@ -478,12 +485,14 @@ class EpDispatchCombineOp:
         return px, ex["packed_count"], ex["packed_src_info"], ex["packed_layout_range"]
 
     def convert_combine_input(self, packed_recv_y, packed_recv_src_info=None,
-                              packed_recv_layout_range=None, stream=None):
+                              packed_recv_layout_range=None, apply_weights=False, stream=None):
         """One combine input row per received row from the experts' outputs
         ("MORI-EP User Guide", section 4, convert_combine_input). The
         positions come from this op's last convert_dispatch_output;
         packed_recv_src_info / packed_recv_layout_range, if given, must be the
-        tensors it returned. Returns y [W, W*M, H] for combine()."""
+        tensors it returned. apply_weights scales each output by its expert's
+        routing weight (the conversion must have had weights). Returns y
+        [W, W*M, H] for combine()."""
         ex = self._ex
         if ex is None:
             raise EpError("ep_convert_combine_input", EP_ERR_STATE,
@@ -493,7 +502,8 @@ class EpDispatchCombineOp:
                               "packed_recv_layout_range")):
             if t is not None and t is not ex[key]:
                 raise ValueError(f"{name} must be the tensor convert_dispatch_output returned")
-        a = _convert_combine_args(self.cfg, self.expert_capacity, packed_recv_y, ex["y"])
+        a = _convert_combine_args(self.cfg, self.expert_capacity, packed_recv_y, ex["y"],
+                                  apply_weights)
         _check("ep_convert_combine_input", self._lib.ep_convert_combine_input(
             ex["plan"], ctypes.byref(a), _stream(stream, self._dev_index)))
         return ex["y"]

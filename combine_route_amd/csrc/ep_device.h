@@ -112,10 +112,12 @@ __device__ __forceinline__ u32x4 narrow(const float (&f)[8])
 // contribution is loaded before any is added (G rows x U columns a lane in
 // flight), then they are summed in lane order in FP32 starting from the
 // first, and the sum is rounded to nearest even once. n = 0 stores +0.
-template <int G, int U, int DT, bool kStream>
+// kWeighted: contribution i is scaled by lane i's gw, the first as a product
+// and the rest with one fused multiply-add each.
+template <int G, int U, int DT, bool kStream, bool kWeighted = false>
 __device__ __forceinline__ void fold_rows(const uint8_t* src, uint32_t row_bytes, int32_t gl,
                                           int n, __amdgpu_buffer_rsrc_t rdst, int vbeg, int vend,
-                                          int lane)
+                                          int lane, float gw = 0.0f)
 {
     for (int v0 = vbeg; v0 < vend; v0 += kWave * U) {
         float acc[U][8];
@@ -138,6 +140,10 @@ __device__ __forceinline__ void fold_rows(const uint8_t* src, uint32_t row_bytes
 #pragma unroll
             for (int q = 0; q < G; ++q) {
                 if (i0 + q < n) {
+                    float c = 1.0f;
+                    if constexpr (kWeighted)
+                        c = __builtin_bit_cast(
+                            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gw), i0 + q));
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         float f[8];
@@ -145,11 +151,12 @@ __device__ __forceinline__ void fold_rows(const uint8_t* src, uint32_t row_bytes
                         if (i0 + q == 0) {
 #pragma unroll
                             for (int e = 0; e < 8; ++e)
-                                acc[u][e] = f[e];
+                                acc[u][e] = kWeighted ? c * f[e] : f[e];
                         } else {
 #pragma unroll
                             for (int e = 0; e < 8; ++e)
-                                acc[u][e] = acc[u][e] + f[e];
+                                acc[u][e] = kWeighted ? __builtin_fmaf(c, f[e], acc[u][e])
+                                                      : acc[u][e] + f[e];
                         }
                     }
                 }

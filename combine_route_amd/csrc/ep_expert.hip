@@ -197,6 +197,7 @@ __global__ __launch_bounds__(1024) void ex_copy_kernel(ExpertArgs a)
 {
     __shared__ int32_t s_j[kWave][KB];  // a row's local experts, first-occurrence order
     __shared__ int32_t s_p[kWave][KB];  // their positions, then the kept packed rows
+    __shared__ float s_c[kWave][KB];    // their weights for the row (when a.w is set)
     __shared__ int32_t s_n[kWave];      // kept packed rows of the row
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -255,31 +256,47 @@ __global__ __launch_bounds__(1024) void ex_copy_kernel(ExpertArgs a)
     if (wave == 0) {
         const bool valid = lane < cnt;
         constexpr int KC = id_chunk<KB>();
-        const int32_t* ids = a.idx + (row0 + (valid ? lane : 0)) * a.k;
+        const int64_t rowq = row0 + (valid ? lane : 0);
+        const int32_t* ids = a.idx + rowq * a.k;
+        const bool weighted = a.w != nullptr;
         // the row's distinct local experts in first-occurrence order; with one
-        // mask word (Er <= 64) repeats are found in a register, else in LDS
+        // mask word (Er <= 64) repeats are found in a register, else in LDS.
+        // Weighted: an expert's weight is the sum, in slot order, of the
+        // row's weights on the slots naming it.
         int n = 0;
         uint64_t seen = 0;
         for (int c = 0; c * KC < a.k; ++c) {
             int32_t id[KC];
             load_ids<KC>(ids, a.k, c, id);
+            float wt[KC];
+            if (weighted) {
+#pragma unroll
+                for (int i = 0; i < KC; ++i)
+                    wt[i] = a.w[rowq * a.k + min(c * KC + i, a.k - 1)];
+            }
 #pragma unroll
             for (int i = 0; i < KC; ++i) {
                 const int64_t j = (int64_t)id[i] - lo;
                 if (!valid || c * KC + i >= a.k || j < 0 || j >= a.Er)
                     continue;
+                bool dup;
                 if (a.Er <= kWave) {
-                    if ((seen >> j) & 1)
-                        continue;
+                    dup = (seen >> j) & 1;
                     seen |= 1ull << j;
                 } else {
-                    bool dup = false;
+                    dup = false;
                     for (int u = 0; u < n; ++u)
                         dup = dup || s_j[lane][u] == (int)j;
-                    if (dup)
-                        continue;
                 }
-                s_j[lane][n++] = (int)j;
+                if (!dup) {
+                    if (weighted)
+                        s_c[lane][n] = wt[i];
+                    s_j[lane][n++] = (int)j;
+                } else if (weighted) {
+                    for (int u = 0; u < n; ++u)
+                        if (s_j[lane][u] == (int)j)
+                            s_c[lane][u] = s_c[lane][u] + wt[i];
+                }
             }
         }
         int n_max = n;  // the wave's longest list
@@ -314,8 +331,11 @@ __global__ __launch_bounds__(1024) void ex_copy_kernel(ExpertArgs a)
         int kept = 0;  // positions past the capacity are dropped
         for (int u = 0; u < n; ++u) {
             const int p = s_p[lane][u];
-            if (p < a.cap)
+            if (p < a.cap) {
+                if (weighted)
+                    s_c[lane][kept] = s_c[lane][u];
                 s_p[lane][kept++] = (int32_t)((lo + s_j[lane][u]) * a.cap + p);
+            }
         }
         s_n[lane] = kept;
     }
@@ -326,8 +346,11 @@ __global__ __launch_bounds__(1024) void ex_copy_kernel(ExpertArgs a)
         for (int r = wave; r < cnt; r += nwaves) {
             const int64_t row = row0 + r;
             const int n = uniform(s_n[r]);
-            if (lane < a.Pe)
+            if (lane < a.Pe) {
                 a.efwd[row * a.Pe + lane] = lane < n ? s_p[r][lane] : -1;
+                if (a.w)
+                    a.ew[row * a.Pe + lane] = lane < n ? s_c[r][lane] : 0.0f;
+            }
             if (lane < n)
                 a.src_info[s_p[r][lane]] = a.src_pos[row] % a.WM;
             for (int c0 = 0; n > 0 && c0 < sd; c0 += kWave) {
@@ -366,7 +389,7 @@ __global__ __launch_bounds__(1024) void ex_copy_kernel(ExpertArgs a)
     }
 }
 
-template <int G, int U, int DT, bool kStream>
+template <int G, int U, int DT, bool kStream, bool kWeighted>
 __global__ __launch_bounds__(1024) void ex_combine_kernel(ExpertCombineArgs a)
 {
     const int lane = threadIdx.x & (kWave - 1);
@@ -378,11 +401,14 @@ __global__ __launch_bounds__(1024) void ex_combine_kernel(ExpertCombineArgs a)
     const int64_t row = (int64_t)d * a.WM + q;
     const int32_t gl = lane < a.Pe ? a.efwd[row * a.Pe + lane] : -1;
     const int n = __popcll(__ballot(gl >= 0));  // entries >= 0 form a prefix
+    float gw = 0.0f;
+    if constexpr (kWeighted)
+        gw = lane < a.Pe ? a.ew[row * a.Pe + lane] : 0.0f;
     const uint32_t row_bytes = (uint32_t)a.row_vecs * 16u;
     const __amdgpu_buffer_rsrc_t rdst = row_rsrc(a.y + row * row_bytes, row_bytes);
     const int vbeg = piece * a.piece_vecs;
     const int vend = min(a.row_vecs, vbeg + a.piece_vecs);
-    fold_rows<G, U, DT, kStream>(a.py, row_bytes, gl, n, rdst, vbeg, vend, lane);
+    fold_rows<G, U, DT, kStream, kWeighted>(a.py, row_bytes, gl, n, rdst, vbeg, vend, lane, gw);
 }
 
 // Top-k bucket of the expert kernels: the smallest of 8, 16, 32, 64 >= k.
@@ -410,20 +436,29 @@ hipError_t ex_copy_with_vpl(const ExpertArgs& a, dim3 grid, dim3 block, bool str
     }
 }
 
+template <int G, int U, int DT, bool kStream>
+void ex_combine_launch(const ExpertCombineArgs& a, dim3 grid, dim3 block, hipStream_t s)
+{
+    if (a.ew)
+        hipLaunchKernelGGL((ex_combine_kernel<G, U, DT, kStream, true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((ex_combine_kernel<G, U, DT, kStream, false>), grid, block, 0, s, a);
+}
+
 template <int G, int U>
 hipError_t ex_combine_with(const ExpertCombineArgs& a, int dtype, dim3 grid, dim3 block,
                            bool stream, hipStream_t s)
 {
     if (dtype == 0) {
         if (stream)
-            hipLaunchKernelGGL((ex_combine_kernel<G, U, 0, true>), grid, block, 0, s, a);
+            ex_combine_launch<G, U, 0, true>(a, grid, block, s);
         else
-            hipLaunchKernelGGL((ex_combine_kernel<G, U, 0, false>), grid, block, 0, s, a);
+            ex_combine_launch<G, U, 0, false>(a, grid, block, s);
     } else {
         if (stream)
-            hipLaunchKernelGGL((ex_combine_kernel<G, U, 1, true>), grid, block, 0, s, a);
+            ex_combine_launch<G, U, 1, true>(a, grid, block, s);
         else
-            hipLaunchKernelGGL((ex_combine_kernel<G, U, 1, false>), grid, block, 0, s, a);
+            ex_combine_launch<G, U, 1, false>(a, grid, block, s);
     }
     return hipGetLastError();
 }

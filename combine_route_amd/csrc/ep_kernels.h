@@ -96,6 +96,7 @@ struct CombineArgs {
 struct ExpertArgs {
     const uint8_t* x;            // [W][WM][row_bytes] received rows
     const int32_t* idx;          // [W][WM][k] their expert ids
+    const float* w;              // [W][WM][k] their routing weights, or null
     const uint32_t* sc;          // [W][WM][scale_dwords] or null
     const int32_t* recv;         // [W] received rows of each rank
     const int32_t* src_pos;      // [W][WM] src_rank * WM + src_token
@@ -109,6 +110,7 @@ struct ExpertArgs {
     int32_t* src_start;          // [W][W] first received row from each source rank
     int32_t* src_prefix;         // [W * Er][W] rows naming the expert in that row's tile before it
     int32_t* efwd;               // [W][WM][Pe] kept packed rows of each received row
+    float* ew;                   // [W][WM][Pe] their experts' weights (when w is set)
     int32_t row_vecs;            // 16-byte vectors per payload row
     int32_t piece_vecs;          // vectors per row piece (one block)
     int32_t scale_dwords;        // 4-byte words per scale row (0: none)
@@ -121,6 +123,7 @@ struct ExpertCombineArgs {
     const uint8_t* py;           // [W][Er][cap][H] expert outputs, combine dtype
     const int32_t* recv;         // [W]
     const int32_t* efwd;         // [W][WM][Pe]
+    const float* ew;             // [W][WM][Pe] weights to apply, or null (plain sum)
     uint8_t* y;                  // [W][WM][H]
     int32_t row_vecs;            // 16-byte vectors per row
     int32_t piece_vecs;

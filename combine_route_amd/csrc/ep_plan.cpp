@@ -185,13 +185,13 @@ struct ep_plan {
 
 // Workspace of an expert plan of capacity cap: per-tile expert counts and
 // bases ([W * Er][T]), the first received row of each source rank ([W][W]),
-// the in-tile prefixes there ([W * Er][W]) and the inverse's map
-// ([W][WM][Pe], Pe = min(k, Er)).
+// the in-tile prefixes there ([W * Er][W]), the inverse's map and its weights
+// ([W][WM][Pe] each, Pe = min(k, Er)).
 struct ExShape {
     int32_t cap;
     int Pe;
     int64_t T;  // tiles a rank can need: max(1, ceil(WM / 64))
-    size_t off_counts, off_base, off_start, off_prefix, off_efwd, total;
+    size_t off_counts, off_base, off_start, off_prefix, off_efwd, off_ew, total;
 };
 
 struct ep_expert_plan {
@@ -199,6 +199,7 @@ struct ep_expert_plan {
     ExShape e;
     uint8_t* ws;
     bool converted = false;
+    bool weighted = false;             // the conversion recorded expert weights
     uint64_t gen = 0;                  // the plan's dispatch that was converted
     const int32_t* recv = nullptr;     // its received-row counts
     int32_t rows = 0;                  // most rows a rank could hold in it
@@ -230,6 +231,9 @@ int expert_shape(const Shape& s, int32_t cap, ExShape* e)
     off = align_up(off + sizeof(int32_t) * lists * (size_t)s.W, kWorkspaceAlign);
     e->off_efwd = off;
     off = align_up(off + sizeof(int32_t) * (size_t)s.W * (size_t)s.WM * (size_t)e->Pe,
+                   kWorkspaceAlign);
+    e->off_ew = off;
+    off = align_up(off + sizeof(float) * (size_t)s.W * (size_t)s.WM * (size_t)e->Pe,
                    kWorkspaceAlign);
     e->total = off;
     return EP_OK;
@@ -873,6 +877,8 @@ int ep_convert_dispatch_output(ep_expert_plan_t* x, const ep_convert_dispatch_ar
         return fail(EP_ERR_ARG,
                     "args.scales and args.packed_scales must be NULL when scale_dim = 0");
     }
+    if (a->weights && !aligned(a->weights, 4))
+        return fail(EP_ERR_ALIGN, "args.weights = %p is not 4-byte aligned", (const void*)a->weights);
     if (!p->dispatched)
         return fail(EP_ERR_STATE, "convert before any dispatch on the plan");
     const ep_launch_t l = effective_launch(p, p->last_ntok);
@@ -882,6 +888,7 @@ int ep_convert_dispatch_output(ep_expert_plan_t* x, const ep_convert_dispatch_ar
     ep::ExpertArgs ea;
     ea.x = static_cast<const uint8_t*>(a->x);
     ea.idx = a->indices;
+    ea.w = a->weights;
     ea.sc = static_cast<const uint32_t*>(a->scales);
     ea.recv = a->recv_num_token;
     ea.src_pos = ws_src_pos(p);
@@ -895,6 +902,7 @@ int ep_convert_dispatch_output(ep_expert_plan_t* x, const ep_convert_dispatch_ar
     ea.src_start = reinterpret_cast<int32_t*>(x->ws + x->e.off_start);
     ea.src_prefix = reinterpret_cast<int32_t*>(x->ws + x->e.off_prefix);
     ea.efwd = reinterpret_cast<int32_t*>(x->ws + x->e.off_efwd);
+    ea.ew = reinterpret_cast<float*>(x->ws + x->e.off_ew);
     ea.row_vecs = (int32_t)(s.row_bytes / 16);
     ea.piece_vecs = (ea.row_vecs + l.expert_row_split - 1) / l.expert_row_split;
     ea.scale_dwords = (int32_t)(s.scale_bytes / 4);
@@ -925,6 +933,7 @@ int ep_convert_dispatch_output(ep_expert_plan_t* x, const ep_convert_dispatch_ar
         return fail(EP_ERR_HIP, "convert_dispatch_output launch failed: %s", hipGetErrorString(e));
     }
     x->converted = true;
+    x->weighted = a->weights != nullptr;
     x->gen = p->dispatch_gen;
     x->recv = a->recv_num_token;
     x->rows = (int32_t)rows;
@@ -944,12 +953,17 @@ int ep_convert_combine_input(ep_expert_plan_t* x, const ep_convert_combine_args_
         return fail(EP_ERR_NULL, "args.y is NULL");
     if (!aligned(a->packed_y, kPtrAlign) || !aligned(a->y, kPtrAlign))
         return fail(EP_ERR_ALIGN, "args.packed_y / args.y are not 16-byte aligned");
+    if (a->apply_weights != 0 && a->apply_weights != 1)
+        return fail(EP_ERR_ARG, "args.apply_weights = %d: must be 0 or 1", a->apply_weights);
     ep_plan* p = x->plan;
     if (!x->converted)
         return fail(EP_ERR_STATE, "convert_combine_input before any convert_dispatch_output");
     if (!p->dispatched || x->gen != p->dispatch_gen)
         return fail(EP_ERR_STATE, "the plan dispatched again since the last "
                     "convert_dispatch_output on this expert plan");
+    if (a->apply_weights && !x->weighted)
+        return fail(EP_ERR_STATE, "args.apply_weights = 1, but the last "
+                    "convert_dispatch_output was given no weights");
     const Shape& s = p->s;
     const ep_launch_t l = effective_launch(p, p->last_ntok);
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
@@ -958,6 +972,7 @@ int ep_convert_combine_input(ep_expert_plan_t* x, const ep_convert_combine_args_
     ca.py = static_cast<const uint8_t*>(a->packed_y);
     ca.recv = x->recv;
     ca.efwd = reinterpret_cast<const int32_t*>(x->ws + x->e.off_efwd);
+    ca.ew = a->apply_weights ? reinterpret_cast<const float*>(x->ws + x->e.off_ew) : nullptr;
     ca.y = static_cast<uint8_t*>(a->y);
     ca.row_vecs = (int32_t)(s.crow_bytes / 16);
     ca.piece_vecs = (ca.row_vecs + l.expert_combine_row_split - 1) / l.expert_combine_row_split;

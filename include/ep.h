@@ -327,15 +327,17 @@ int ep_plan_kernel_time(ep_plan_t *plan, int kernel, int32_t *count, double *tot
  *    cap (R).
  *  - The inverse writes, for every received row, the FP32 sum of its kept
  *    experts' outputs in the order its local experts first appear in its ids,
- *    from the first, rounded to nearest even once, unweighted (R, like
- *    combine); a row with none is +0.
+ *    from the first, rounded to nearest even once (R, like combine); a row
+ *    with none is +0. On request each output is first scaled by its expert's
+ *    routing weight for the row, with a fused multiply-add (R).
  * Deterministic bit for bit, like the rest of the library.
  * ------------------------------------------------------------------------ */
 typedef struct ep_expert_plan ep_expert_plan_t;
 
 /* Bytes of device workspace an expert plan of capacity cap needs on top of
- * its plan's: per-tile expert counts and bases, source starts, and the map
- * [W][WM][min(k, Er)] int32 the inverse gathers through. Returns 0 if plan is
+ * its plan's: per-tile expert counts and bases, source starts, the map
+ * [W][WM][min(k, Er)] int32 the inverse gathers through and its weights
+ * [W][WM][min(k, Er)] float. Returns 0 if plan is
  * NULL or cap is out of range (1 <= cap <= WM and W * Er * cap <= 2^31 - 1);
  * ep_last_error() says why. */
 size_t ep_expert_workspace_bytes(const ep_plan_t *plan, int32_t cap);
@@ -359,6 +361,11 @@ int ep_expert_plan_destroy(ep_expert_plan_t *plan);
  *   x                    [W][WM][H] dispatch_dtype (the dispatch's out_x),
  *                        16-byte aligned.
  *   indices              [W][WM][k] int32 (out_indices).
+ *   weights              [W][WM][k] float (out_weights), or NULL. Given, each
+ *                        kept (row, expert) pair records its expert's weight
+ *                        for the row, the FP32 sum in slot order of the row's
+ *                        weights on the slots naming that expert (R), for a
+ *                        weighted inverse.
  *   scales               [W][WM][S] (out_scales); NULL iff S == 0.
  *   recv_num_token       DEVICE int32 [W] (recv_num_token).
  * Outputs (device, caller-owned, must not overlap the inputs or workspaces):
@@ -373,6 +380,7 @@ int ep_expert_plan_destroy(ep_expert_plan_t *plan);
 typedef struct ep_convert_dispatch_args {
     const void *x;
     const int32_t *indices;
+    const float *weights;
     const void *scales;
     const int32_t *recv_num_token;
     void *packed_x;
@@ -391,23 +399,33 @@ typedef struct ep_convert_dispatch_args {
 int ep_convert_dispatch_output(ep_expert_plan_t *plan, const ep_convert_dispatch_args_t *args,
                                void *stream);
 
-/* Arguments of ep_convert_combine_input (device, 16-byte aligned):
- *   packed_y   [W][Er][cap][H] combine_dtype: the experts' outputs, slot for
- *              slot with packed_x (slots past min(count, cap) are not read).
- *   y          [W][WM][H] combine_dtype: rows q < recv_num_token[d] are
- *              written (the combine input, ep_combine_args_t.y); others
- *              untouched. Must not overlap packed_y. */
+/* Arguments of ep_convert_combine_input (device pointers 16-byte aligned):
+ *   packed_y       [W][Er][cap][H] combine_dtype: the experts' outputs, slot
+ *                  for slot with packed_x (slots past min(count, cap) are not
+ *                  read).
+ *   y              [W][WM][H] combine_dtype: rows q < recv_num_token[d] are
+ *                  written (the combine input, ep_combine_args_t.y); others
+ *                  untouched. Must not overlap packed_y.
+ *   apply_weights  0: the plain sum. 1: each output is scaled by its
+ *                  expert's weight for the row (recorded by the conversion,
+ *                  which must have been given weights): acc = c * v for the
+ *                  first kept output, then acc = fma(c, v, acc) (R; [GUIDE]
+ *                  section 3: combine weights are for a weighted
+ *                  combination). The plain combine after it then gives the
+ *                  mixture sum over a token's slots of w_i * expert_i(x). */
 typedef struct ep_convert_combine_args {
     const void *packed_y;
     void *y;
+    int32_t apply_weights;
 } ep_convert_combine_args_t;
 
 /* The inverse ([GUIDE4] convert_combine_input), through the map of the last
  * ep_convert_dispatch_output on this expert plan, which must have converted
  * the plan's current dispatch. Asynchronous; no allocation; capturable; may be
  * called any number of times per conversion.
- * Errors: EP_ERR_NULL, EP_ERR_ALIGN, EP_ERR_STATE (no conversion yet, or
- * the plan dispatched again since), EP_ERR_HIP. */
+ * Errors: EP_ERR_NULL, EP_ERR_ALIGN, EP_ERR_ARG (apply_weights not 0 or 1),
+ * EP_ERR_STATE (no conversion yet, the plan dispatched again since, or
+ * weights asked for and the conversion had none), EP_ERR_HIP. */
 int ep_convert_combine_input(ep_expert_plan_t *plan, const ep_convert_combine_args_t *args,
                              void *stream);
 

@@ -284,11 +284,12 @@ def test_kernel_time_argument_checks(lib):
 def expected_expert_workspace(W, M, k, Er):
     """Layout: tile counts and bases (W*Er x max(1, ceil(W*M/64)) int32 each),
     source starts (W x W int32), in-tile prefixes (W*Er x W int32), the
-    inverse's map (W x W*M x min(k, Er) int32), each rounded up to 256 bytes."""
+    inverse's map and weights (W x W*M x min(k, Er) int32 / float), each
+    rounded up to 256 bytes."""
     up = lambda v: (v + 255) // 256 * 256
     T = max(1, (W * M + 63) // 64)
     return (2 * up(4 * W * Er * T) + up(4 * W * W) + up(4 * W * Er * W)
-            + up(4 * W * W * M * min(k, Er)))
+            + 2 * up(4 * W * W * M * min(k, Er)))
 
 
 def make_expert(lib, plan, cap, ws=FAKE_WS + (1 << 30), nbytes=None):
@@ -347,7 +348,8 @@ def test_expert_capacity_limit_is_int32(lib):
 
 
 def convert_args(**over):
-    a = dict(x=FAKE, indices=FAKE + 0x1000, scales=None, recv_num_token=FAKE + 0x2000,
+    a = dict(x=FAKE, indices=FAKE + 0x1000, weights=None, scales=None,
+             recv_num_token=FAKE + 0x2000,
              packed_x=FAKE + 0x3000, packed_scales=None, packed_count=FAKE + 0x4000,
              packed_src_info=FAKE + 0x5000, packed_layout_range=FAKE + 0x6000)
     a.update(over)
@@ -366,6 +368,7 @@ def convert_args(**over):
     (dict(packed_x=FAKE + 0x3004), cra.EP_ERR_ALIGN, "packed_x"),
     (dict(packed_layout_range=FAKE + 0x6004), cra.EP_ERR_ALIGN, "packed_layout_range"),
     (dict(indices=FAKE + 0x1002), cra.EP_ERR_ALIGN, "indices"),
+    (dict(weights=FAKE + 0x9002), cra.EP_ERR_ALIGN, "weights"),
     (dict(scales=FAKE + 0x7000, packed_scales=FAKE + 0x8000), cra.EP_ERR_ARG, "scale_dim = 0"),
     ({}, cra.EP_ERR_STATE, "before any dispatch"),
 ])
@@ -399,10 +402,12 @@ def test_convert_combine_input_errors_and_state(lib):
     cfg = cra.make_config(2, 256, 16, 4, 2)
     rc, plan = make_plan(lib, cfg)
     rc, ex = make_expert(lib, plan, 8)
-    ok = dict(packed_y=FAKE, y=FAKE + 0x1000)
+    ok = dict(packed_y=FAKE, y=FAKE + 0x1000, apply_weights=0)
     for over, code, word in [(dict(packed_y=None), cra.EP_ERR_NULL, "packed_y"),
                              (dict(y=None), cra.EP_ERR_NULL, "args.y"),
                              (dict(y=FAKE + 8), cra.EP_ERR_ALIGN, "aligned"),
+                             (dict(apply_weights=2), cra.EP_ERR_ARG, "apply_weights"),
+                             (dict(apply_weights=-1), cra.EP_ERR_ARG, "apply_weights"),
                              ({}, cra.EP_ERR_STATE, "before any convert_dispatch_output")]:
         a = cra.EpConvertCombineArgs(**{**ok, **over})
         assert lib.ep_convert_combine_input(ex, ctypes.byref(a), None) == code

@@ -99,10 +99,12 @@ def random_outputs(wl, cap, seed):
 
 
 def run_expert_case(wl, cap=None, cap_div=1, inp=None, launch=None, tag=None,
-                    check_untouched=True, py="random", round_trip=False):
+                    check_untouched=True, py="random", round_trip=False, weighted=False):
     """Dispatch on the GPU, convert, invert, and compare each stage with the
     oracle. cap: rows kept per expert (default: the largest count / cap_div).
-    py: "random" expert outputs or "identity" (the packed rows themselves)."""
+    py: "random" expert outputs or "identity" (the packed rows themselves).
+    weighted: the conversion gets the dispatched weights and the inverse
+    applies them."""
     W, M, k, Er, H = _dims(wl)
     inp = inp or workloads.make_inputs(wl)
     ref = oracle_dispatch(wl, inp)
@@ -111,17 +113,18 @@ def run_expert_case(wl, cap=None, cap_div=1, inp=None, launch=None, tag=None,
     tag = tag or f"{wl.name} cap={cap}"
     _say(f"[case] {tag}: W={W} M={M} H={H} k={k} Er={Er} {wl.dispatch_dtype}->"
          f"{wl.combine_dtype} launch={launch}")
-    op = cra.EpDispatchCombineOp(config_of(wl), with_weights=False, expert_capacity=cap)
+    op = cra.EpDispatchCombineOp(config_of(wl), with_weights=weighted, expert_capacity=cap)
     if launch is not None:
         op.set_launch(launch)
     ex = op._expert_state()
     if check_untouched:
         _fill_outputs(ex)
-    gpu_dispatch(op, dict(inp, w=None))
+    gpu_dispatch(op, inp if weighted else dict(inp, w=None))
     torch.cuda.synchronize()
-    compare_dispatch(wl, op, dict(ref, out_w=None), tag)
+    compare_dispatch(wl, op, ref if weighted else dict(ref, out_w=None), tag)
 
-    op.convert_dispatch_output(op.out_x, op.out_indices, op.out_scales)
+    op.convert_dispatch_output(op.out_x, op.out_indices, op.out_scales,
+                               op.out_weights if weighted else None)
     torch.cuda.synchronize()
     ref_ex = oracle.expert_layout(W, M, k, Er, cap, ref["recv"], ref["src_pos"], ref["out_x"],
                                   ref["out_idx"], ref["out_scales"], fill=SENTINEL_INT)
@@ -136,9 +139,11 @@ def run_expert_case(wl, cap=None, cap_div=1, inp=None, launch=None, tag=None,
         v = random_outputs(wl, cap, seed=sum(tag.encode()) % 10007)
         py_dev = v.cuda()
         py16 = v.view(torch.int16).numpy().view(np.uint16)
-    y = op.convert_combine_input(py_dev, ex["packed_src_info"], ex["packed_layout_range"])
+    y = op.convert_combine_input(py_dev, ex["packed_src_info"], ex["packed_layout_range"],
+                                 apply_weights=weighted)
     torch.cuda.synchronize()
-    ref_y = oracle.expert_combine(W, M, k, Er, cap, H, dt, ref["recv"], ref["out_idx"], py16)
+    ref_y = oracle.expert_combine(W, M, k, Er, cap, H, dt, ref["recv"], ref["out_idx"], py16,
+                                  w=ref["out_w"] if weighted else None)
     compare_inverse(wl, ref, y, ref_y, tag, check_untouched)
 
     if round_trip:
@@ -223,6 +228,53 @@ def test_invalid_and_duplicate_ids():
     idx[2, :5, :3] = 5                   # one expert named three times
     inp["idx"] = idx.contiguous()
     run_expert_case(wl, inp=inp, tag="ex invalid+duplicate ids", round_trip=True)
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_weighted_full_size(name):
+    """The weighted inverse at full size, through combine (the mixture sum)."""
+    wl = workloads.WORKLOADS[name]
+    identity = wl.dispatch_dtype == wl.combine_dtype
+    run_expert_case(wl, check_untouched=name != workloads.HEADLINE,
+                    py="identity" if identity else "random", round_trip=True, weighted=True)
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+@pytest.mark.parametrize("cap_div", [1, 3])
+def test_weighted_capacity_drops(wl, cap_div):
+    run_expert_case(wl, cap_div=cap_div, weighted=True, tag=f"weighted {wl.name} /{cap_div}")
+
+
+def test_weighted_repeated_ids_and_many_experts():
+    """Repeated ids (their weights add up), invalid ids, and more than 64
+    experts a rank (the LDS path for repeats)."""
+    for wl in (workloads.custom("exw_ids_ep4_t48_h256", 4, 48, 256, 6, 16, "bf16",
+                                seed_index=530),
+               workloads.custom("exw_ep2_t40_h128_E300_k9", 2, 40, 128, 9, 300, "bf16",
+                                seed_index=531)):
+        inp = workloads.make_inputs(wl)
+        g = torch.Generator().manual_seed(13)
+        E = wl.num_experts
+        idx = torch.randint(-2, E + 2, inp["idx"].shape, generator=g, dtype=torch.int32)
+        idx[:, :6, 1] = idx[:, :6, 0]          # repeated experts
+        inp["idx"] = idx.contiguous()
+        run_expert_case(wl, inp=inp, weighted=True, round_trip=True, tag=f"weighted ids {wl.name}")
+
+
+def test_weighted_needs_weights_at_conversion():
+    wl = workloads.custom("exw_state_ep2_t32_h128", 2, 32, 128, 4, 8, "bf16", seed_index=532)
+    inp = workloads.make_inputs(wl)
+    op = cra.EpDispatchCombineOp(config_of(wl), expert_capacity=64)
+    gpu_dispatch(op, inp)
+    px, _, _, _ = op.convert_dispatch_output(op.out_x, op.out_indices)
+    with pytest.raises(cra.EpError) as e:
+        op.convert_combine_input(px, apply_weights=True)
+    assert e.value.code == cra.EP_ERR_STATE and "no weights" in str(e.value)
+    op.convert_dispatch_output(op.out_x, op.out_indices, None, op.out_weights)
+    op.convert_combine_input(px, apply_weights=True)
+    op.convert_combine_input(px)               # the plain sum still works
+    torch.cuda.synchronize()
+    op.close()
 
 
 def test_state_errors_and_reconvert():
