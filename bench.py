@@ -106,12 +106,13 @@ def expert_bytes(wl, recv_total, pairs):
     row = wl.hidden * (1 if wl.dispatch_dtype == "fp8" else 2)
     crow = wl.hidden * 2
     sb = wl.scale_dim * 4
-    # copy: each received row's payload, scale row, ids and source read once;
-    # each kept pair's payload and scale row and source info written; the
-    # inverse's map written for every row
-    copy = R * (row + sb + 4 * k + 4) + pairs * (row + sb + 4) + R * Pe * 4
-    # inverse: each kept pair's output read, each received row written, map read
-    combine = pairs * crow + R * crow + R * Pe * 4
+    # copy: each received row's payload, scale row, ids, weights and source
+    # read once; each kept pair's payload and scale row and source info
+    # written; the inverse's map and weights written for every row
+    copy = R * (row + sb + 8 * k + 4) + pairs * (row + sb + 4) + R * Pe * 8
+    # inverse: each kept pair's output read, each received row written, map
+    # and weights read
+    combine = pairs * crow + R * crow + R * Pe * 8
     return {"copy": copy, "combine": combine}
 
 
@@ -133,9 +134,12 @@ def measure_expert_major(args, cra, torch, np, wl, op, inp, stream):
             ex["y"].dtype)
         py_kind = "random output"
 
+    # the mixture path: routing weights recorded by the conversion and applied
+    # by the inverse
     def step():
-        op.convert_dispatch_output(op.out_x, op.out_indices, op.out_scales, stream=stream)
-        op.convert_combine_input(py, stream=stream)
+        op.convert_dispatch_output(op.out_x, op.out_indices, op.out_scales, op.out_weights,
+                                   stream=stream)
+        op.convert_combine_input(py, apply_weights=True, stream=stream)
 
     step()
     torch.cuda.synchronize()
@@ -199,6 +203,7 @@ def measure_expert_major(args, cra, torch, np, wl, op, inp, stream):
         "expert_capacity": cap, "kept_pairs": pairs,
         "dropped_rows": int(np.maximum(cnt - cap, 0).sum()),
         "expert_output": py_kind,
+        "weighted": True,
         "us_per_call": round(ms * 1e3, 2),
         "kernel_us": {k_: round(v * 1e3, 2) for k_, v in kern.items()},
         "check": check,
