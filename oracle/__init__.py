@@ -44,6 +44,20 @@ def _load():
     lib.oracle_expert_layout.restype = I
     lib.oracle_expert_combine.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P]
     lib.oracle_expert_combine.restype = I
+    lib.oracle_f32_to_e4m3.argtypes = [ctypes.c_float]
+    lib.oracle_f32_to_e4m3.restype = ctypes.c_uint8
+    lib.oracle_e4m3_to_f32.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_to_f32.restype = ctypes.c_float
+    lib.oracle_f32_to_e2m1.argtypes = [ctypes.c_float]
+    lib.oracle_f32_to_e2m1.restype = ctypes.c_uint8
+    lib.oracle_e2m1_to_f32.argtypes = [ctypes.c_uint8]
+    lib.oracle_e2m1_to_f32.restype = ctypes.c_float
+    lib.oracle_cast_to_e4m3_n.argtypes = [P, I, P, Z]
+    lib.oracle_cast_to_e4m3_n.restype = None
+    lib.oracle_quantize_rows.argtypes = [ctypes.c_int64, I, I, I, P, P, P]
+    lib.oracle_quantize_rows.restype = I
+    lib.oracle_combine_wire.argtypes = [I, I, I, I, I, I, P, P, P, P, P]
+    lib.oracle_combine_wire.restype = I
     for name in ("oracle_f32_to_bf16_n", "oracle_f32_to_f16_n",
                  "oracle_bf16_to_f32_n", "oracle_f16_to_f32_n"):
         getattr(lib, name).argtypes = [P, P, Z]
@@ -198,6 +212,72 @@ def expert_combine(W, M, k, Er, cap, H, dtype, recv, idx, py, w=None):
     if rc != 0:
         raise RuntimeError(f"oracle_expert_combine failed ({rc})")
     return y
+
+
+WIRE_FP8_BLOCK128 = 1
+WIRE_MXFP4 = 2
+
+
+def f32_to_e4m3(v):
+    return _load().oracle_f32_to_e4m3(float(v))
+
+
+def e4m3_to_f32(c):
+    return _load().oracle_e4m3_to_f32(int(c))
+
+
+def f32_to_e2m1(v):
+    return _load().oracle_f32_to_e2m1(float(v))
+
+
+def e2m1_to_f32(c):
+    return _load().oracle_e2m1_to_f32(int(c))
+
+
+def cast_to_e4m3(words, dtype):
+    """bf16 (dtype BF16) / fp16 (FP16) words -> E4M3 codes, direct cast."""
+    lib = _load()
+    words = np.ascontiguousarray(words, dtype=np.uint16)
+    out = np.empty(words.shape, np.uint8)
+    lib.oracle_cast_to_e4m3_n(_ptr(words), dtype, _ptr(out), words.size)
+    return out
+
+
+def quantize_rows(words, dtype, wire):
+    """Rows [..., H] of bf16 / fp16 words into a wire format. Returns (codes,
+    scales): FP8 block-128: uint8 [..., H] and float32 [..., H/128]; MXFP4:
+    uint8 [..., H/2] packed and uint8 E8M0 [..., H/32]."""
+    lib = _load()
+    words = np.ascontiguousarray(words, dtype=np.uint16)
+    H = words.shape[-1]
+    lead = words.shape[:-1]
+    n = words.size // H
+    if wire == WIRE_FP8_BLOCK128:
+        out = np.zeros(lead + (H,), np.uint8)
+        scales = np.zeros(lead + (H // 128,), np.float32)
+    else:
+        out = np.zeros(lead + (H // 2,), np.uint8)
+        scales = np.zeros(lead + (H // 32,), np.uint8)
+    rc = lib.oracle_quantize_rows(n, H, dtype, wire, _ptr(words), _ptr(out), _ptr(scales))
+    if rc != 0:
+        raise RuntimeError(f"oracle_quantize_rows failed ({rc})")
+    return out, scales
+
+
+def combine_wire(W, M, k, H, dtype, wire, ntok, fwd, y, y_scales):
+    """Combine by definition from wire rows y [W, W*M, ...] and their scales.
+    Returns out uint16 [W, M, H]; rows of absent tokens stay zero."""
+    lib = _load()
+    ntok = _c(np.asarray(ntok, dtype=np.int32))
+    fwd = _c(fwd, np.int32)
+    y = _c(y)
+    y_scales = _c(y_scales)
+    out = np.zeros((W, M, H), np.uint16)
+    rc = lib.oracle_combine_wire(W, M, k, H, dtype, wire, _ptr(ntok), _ptr(fwd), _ptr(y),
+                                 _ptr(y_scales), _ptr(out))
+    if rc != 0:
+        raise RuntimeError(f"oracle_combine_wire failed ({rc})")
+    return out
 
 
 def _conv(name, a, in_dtype, out_dtype):

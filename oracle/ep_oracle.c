@@ -522,3 +522,176 @@ int oracle_expert_combine(int W, int M, int k, int Er, int cap, int H, int dtype
     free(next);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Quantized wires.                                                          */
+/* ------------------------------------------------------------------------ */
+
+/* E4M3: a code S.EEEE.MMM is (-1)^S * 2^(E-7) * (1 + M/8) for E >= 1 and
+ * (-1)^S * 2^-6 * M/8 for E = 0; S.1111.111 is NaN, so the largest finite
+ * magnitude is S.1111.110 = 448. */
+float oracle_e4m3_to_f32(uint8_t c)
+{
+    int sign = c >> 7, e = (c >> 3) & 0xF, m = c & 7;
+    if (e == 15 && m == 7)
+        return NAN;
+    float v = e == 0 ? ldexpf((float)m, -9) : ldexpf((float)(8 + m), e - 10);
+    return sign ? -v : v;
+}
+
+/* Nearest finite E4M3 value by search over all 127 magnitudes; a tie goes
+ * to the code whose mantissa is even; beyond 448 saturate. */
+uint8_t oracle_f32_to_e4m3(float v)
+{
+    if (isnan(v))
+        return 0x7F;
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    double a = fabs((double)v);
+    if (a >= 448.0)
+        return sign | 0x7E;
+    int best = 0;
+    double bd = a;                      /* distance to code 0 (zero) */
+    for (int c = 1; c <= 0x7E; ++c) {
+        double d = fabs((double)oracle_e4m3_to_f32((uint8_t)c) - a);
+        if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) {
+            bd = d;
+            best = c;
+        }
+    }
+    return sign | (uint8_t)best;
+}
+
+/* E2M1: S.EE.M is (-1)^S * 2^(E-1) * (1 + M/2) for E >= 1 and (-1)^S * M/2
+ * for E = 0: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+float oracle_e2m1_to_f32(uint8_t c)
+{
+    int sign = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+    float v = e == 0 ? 0.5f * (float)m : ldexpf(1.0f + 0.5f * (float)m, e - 1);
+    return sign ? -v : v;
+}
+
+uint8_t oracle_f32_to_e2m1(float v)
+{
+    uint8_t sign = signbit(v) ? 8 : 0;
+    double a = fabs((double)v);
+    if (a >= 6.0)
+        return sign | 7;
+    int best = 0;
+    double bd = a;
+    for (int c = 1; c <= 7; ++c) {
+        double d = fabs((double)oracle_e2m1_to_f32((uint8_t)c) - a);
+        if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) {
+            bd = d;
+            best = c;
+        }
+    }
+    return sign | (uint8_t)best;
+}
+
+void oracle_cast_to_e4m3_n(const uint16_t *in, int dtype, uint8_t *out, size_t n)
+{
+    for (size_t i = 0; i < n; ++i)
+        out[i] = oracle_f32_to_e4m3(widen(in[i], dtype));
+}
+
+int oracle_quantize_rows(int64_t n, int H, int dtype, int wire, const uint16_t *in,
+                         uint8_t *out, void *scales)
+{
+    if (wire == ORACLE_WIRE_FP8_BLOCK128) {
+        if (H % 128)
+            return -1;
+        float *sc = scales;
+        for (int64_t r = 0; r < n; ++r)
+            for (int b = 0; b < H / 128; ++b) {
+                const uint16_t *v = in + r * H + b * 128;
+                float amax = 0.0f;
+                for (int i = 0; i < 128; ++i)
+                    amax = fmaxf(amax, fabsf(widen(v[i], dtype)));
+                float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+                float rcp = amax > 0.0f ? 448.0f / amax : 1.0f;
+                sc[r * (H / 128) + b] = s;
+                for (int i = 0; i < 128; ++i)
+                    out[r * H + b * 128 + i] = oracle_f32_to_e4m3(widen(v[i], dtype) * rcp);
+            }
+        return 0;
+    }
+    if (wire == ORACLE_WIRE_MXFP4) {
+        if (H % 32)
+            return -1;
+        uint8_t *sc = scales;
+        for (int64_t r = 0; r < n; ++r)
+            for (int b = 0; b < H / 32; ++b) {
+                const uint16_t *v = in + r * H + b * 32;
+                float amax = 0.0f;
+                for (int i = 0; i < 32; ++i)
+                    amax = fmaxf(amax, fabsf(widen(v[i], dtype)));
+                /* the largest E2M1 exponent is 2 (6 = 1.5 * 2^2): the block's
+                 * largest magnitude lands in [4, 8) before saturation */
+                int E = -127;
+                if (amax > 0.0f) {
+                    int e2;
+                    frexpf(amax, &e2);          /* amax = f * 2^e2, f in [0.5, 1) */
+                    E = e2 - 1 - 2;
+                    if (E < -127)
+                        E = -127;
+                }
+                sc[r * (H / 32) + b] = (uint8_t)(E + 127);
+                for (int i = 0; i < 32; i += 2) {
+                    uint8_t lo = oracle_f32_to_e2m1(ldexpf(widen(v[i], dtype), -E));
+                    uint8_t hi = oracle_f32_to_e2m1(ldexpf(widen(v[i + 1], dtype), -E));
+                    out[r * (H / 2) + (b * 32 + i) / 2] = (uint8_t)(lo | (hi << 4));
+                }
+            }
+        return 0;
+    }
+    return -1;
+}
+
+float oracle_wire_value(int wire, const uint8_t *row, const void *scale_row, int h)
+{
+    if (wire == ORACLE_WIRE_FP8_BLOCK128)
+        return oracle_e4m3_to_f32(row[h]) * ((const float *)scale_row)[h / 128];
+    uint8_t byte = row[h / 2];
+    uint8_t code = (h & 1) ? (byte >> 4) : (byte & 0xF);
+    return ldexpf(oracle_e2m1_to_f32(code), (int)((const uint8_t *)scale_row)[h / 32] - 127);
+}
+
+int oracle_combine_wire(int W, int M, int k, int H, int dtype, int wire, const int32_t *ntok,
+                        const int32_t *fwd, const uint8_t *y, const void *y_scales,
+                        uint16_t *out)
+{
+    const int P = W < k ? W : k;
+    size_t row_bytes, scale_bytes;
+    if (wire == ORACLE_WIRE_FP8_BLOCK128) {
+        row_bytes = (size_t)H;
+        scale_bytes = sizeof(float) * (size_t)(H / 128);
+    } else if (wire == ORACLE_WIRE_MXFP4) {
+        row_bytes = (size_t)H / 2;
+        scale_bytes = (size_t)(H / 32);
+    } else {
+        return -1;
+    }
+    for (int r = 0; r < W; ++r)
+        for (int t = 0; t < ntok[r]; ++t) {
+            int64_t tok = (int64_t)r * M + t;
+            int64_t rows[64];
+            int n = 0;
+            for (int i = 0; i < P; ++i)
+                if (fwd[tok * P + i] >= 0)
+                    rows[n++] = fwd[tok * P + i];
+            /* [PR712] Combine: FP32 sum in the token's rank order from the
+             * first contribution, one rounding; each contribution comes off
+             * the wire through its scale first */
+            for (int h = 0; h < H; ++h) {
+                float acc = 0.0f;
+                for (int i = 0; i < n; ++i) {
+                    float v = oracle_wire_value(wire, y + (size_t)rows[i] * row_bytes,
+                                                (const uint8_t *)y_scales
+                                                    + (size_t)rows[i] * scale_bytes, h);
+                    acc = i == 0 ? v : acc + v;
+                }
+                out[(size_t)tok * H + h] = n ? narrow(acc, dtype) : 0;
+            }
+        }
+    return 0;
+}

@@ -141,6 +141,50 @@ int oracle_expert_combine(int W, int M, int k, int Er, int cap, int H, int dtype
                           const int32_t *recv, const int32_t *idx, const float *w,
                           const uint16_t *py, uint16_t *y);
 
+/* ------------------------------------------------------------------------
+ * Quantized wires ([PR726] and [GUIDE] section 10 name fp8_direct_cast,
+ * fp8_blockwise and fp4 with e8m0 scales without defining them; the
+ * definitions below follow the formats' published specifications, OCP
+ * "8-bit Floating Point Specification (OFP8)" for E4M3 and OCP
+ * "Microscaling Formats (MX) v1.0" for E2M1, E8M0 and the MX conversion).
+ * Readings: round to nearest even; finite values past the largest magnitude
+ * saturate to it; an E4M3 NaN input becomes 0x7F; blockwise FP8 uses blocks
+ * of 128 elements with an FP32 scale s = amax / 448 and elements multiplied
+ * by r = 448 / amax (s = 1, r = 1 for an all-zero block); MXFP4 uses blocks
+ * of 32 with scale 2^(floor(log2 amax) - 2) (E8M0 code 0 for an all-zero
+ * block), two E2M1 codes a byte, the even element in the low nibble. MX
+ * inputs are finite.
+ * ------------------------------------------------------------------------ */
+enum { ORACLE_WIRE_FP8_BLOCK128 = 1, ORACLE_WIRE_MXFP4 = 2 };
+
+/* OCP E4M3 (bias 7, no infinities, largest 448, NaN S.1111.111). */
+uint8_t oracle_f32_to_e4m3(float v);
+float oracle_e4m3_to_f32(uint8_t c);
+/* OCP E2M1 (bias 1, magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6): a 4-bit code. */
+uint8_t oracle_f32_to_e2m1(float v);
+float oracle_e2m1_to_f32(uint8_t c);
+
+/* Bulk direct cast: bf16 (dtype 0) or fp16 (1) words -> E4M3 codes. */
+void oracle_cast_to_e4m3_n(const uint16_t *in, int dtype, uint8_t *out, size_t n);
+
+/* Quantize rows[n][H] of bf16 (dtype 0) / fp16 (1) into a wire format:
+ *   ORACLE_WIRE_FP8_BLOCK128: out[n][H] E4M3 codes, scales[n][H/128] float.
+ *   ORACLE_WIRE_MXFP4:        out[n][H/2] packed E2M1, scales[n][H/32] E8M0.
+ * Returns 0, or -1 if H does not divide into blocks. */
+int oracle_quantize_rows(int64_t n, int H, int dtype, int wire, const uint16_t *in,
+                         uint8_t *out, void *scales);
+
+/* One element of a wire row, back in FP32: E4M3 value times the block's
+ * scale (one FP32 multiply), or E2M1 value times 2^(code - 127) (exact). */
+float oracle_wire_value(int wire, const uint8_t *row, const void *scale_row, int h);
+
+/* Combine from a wire (gather form): like oracle_combine, with each
+ * contribution element taken through oracle_wire_value before the FP32 fold.
+ *   y[W][WM][...] wire rows, y_scales[W][WM][...] their scales. */
+int oracle_combine_wire(int W, int M, int k, int H, int dtype, int wire, const int32_t *ntok,
+                        const int32_t *fwd, const uint8_t *y, const void *y_scales,
+                        uint16_t *out);
+
 /* IEEE 754 conversions used by the combine cast, written from the formats'
  * definitions: binary32 -> bfloat16 / binary16 with round-to-nearest-even,
  * overflow to infinity, NaN to a quiet NaN; and the exact widenings back. */
