@@ -29,21 +29,26 @@ EP_KERNEL_ROUTE, EP_KERNEL_SCAN, EP_KERNEL_COPY, EP_KERNEL_COMBINE = 0, 1, 2, 3
 EP_CACHE_AUTO, EP_CACHE_STREAM, EP_CACHE_KEEP = 0, 1, 2
 EP_LAYOUT_AUTO, EP_LAYOUT_KERNELS, EP_LAYOUT_SCAN_IN_COPY, EP_LAYOUT_IN_COPY = 0, 1, 2, 3
 
+EP_WIRE_NONE, EP_WIRE_FP8_BLOCK128, EP_WIRE_MXFP4 = 0, 1, 2
+
 DTYPES = {"bf16": EP_BF16, "fp16": EP_FP16, "fp8": EP_FP8_E4M3}
+WIRES = {None: EP_WIRE_NONE, "none": EP_WIRE_NONE, "fp8_block128": EP_WIRE_FP8_BLOCK128,
+         "mxfp4": EP_WIRE_MXFP4}
 ELEM_BYTES = {EP_BF16: 2, EP_FP16: 2, EP_FP8_E4M3: 1}
 
 EXPORTED = ("ep_workspace_bytes", "ep_plan_create", "ep_plan_destroy", "ep_dispatch",
             "ep_combine", "ep_get_src_token_pos", "ep_last_error", "ep_plan_set_launch",
             "ep_plan_get_launch", "ep_plan_set_timing", "ep_plan_kernel_time",
             "ep_expert_workspace_bytes", "ep_expert_plan_create", "ep_expert_plan_destroy",
-            "ep_convert_dispatch_output", "ep_convert_combine_input")
+            "ep_convert_dispatch_output", "ep_convert_combine_input", "ep_quantize_rows")
 
 
 class EpConfig(ctypes.Structure):
     """ep_config_t: after the pages' EpDispatchCombineConfig."""
     _fields_ = [(n, ctypes.c_int32) for n in (
         "world_size", "hidden_dim", "scale_dim", "scale_type_size", "max_num_inp_token_per_rank",
-        "num_experts_per_rank", "num_experts_per_token", "dispatch_dtype", "combine_dtype")]
+        "num_experts_per_rank", "num_experts_per_token", "dispatch_dtype", "combine_dtype",
+        "combine_wire")]
 
 
 class EpDispatchArgs(ctypes.Structure):
@@ -53,7 +58,8 @@ class EpDispatchArgs(ctypes.Structure):
 
 
 class EpCombineArgs(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("y", "y_weights", "out", "out_weights")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("y", "y_weights", "out", "out_weights",
+                                               "y_scales")]
 
 
 class EpLaunch(ctypes.Structure):
@@ -112,6 +118,8 @@ def load():
     lib.ep_expert_plan_destroy.argtypes = [V]
     lib.ep_convert_dispatch_output.argtypes = [V, P(EpConvertDispatchArgs), V]
     lib.ep_convert_combine_input.argtypes = [V, P(EpConvertCombineArgs), V]
+    lib.ep_quantize_rows.argtypes = [V, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_int32, V, V, V]
     for name in EXPORTED:
         if name not in ("ep_workspace_bytes", "ep_last_error", "ep_expert_workspace_bytes"):
             getattr(lib, name).restype = I
@@ -130,14 +138,16 @@ def _check(fn, rc):
 
 def make_config(world_size, hidden_dim, max_num_inp_token_per_rank, num_experts_per_rank,
                 num_experts_per_token, dispatch_dtype="bf16", combine_dtype=None,
-                scale_dim=0, scale_type_size=4) -> EpConfig:
+                scale_dim=0, scale_type_size=4, combine_wire=None) -> EpConfig:
     dd = DTYPES[dispatch_dtype] if isinstance(dispatch_dtype, str) else dispatch_dtype
     if combine_dtype is None:
         combine_dtype = EP_FP16 if dd == EP_FP16 else EP_BF16
     cd = DTYPES[combine_dtype] if isinstance(combine_dtype, str) else combine_dtype
+    cw = WIRES[combine_wire] if combine_wire is None or isinstance(combine_wire, str) \
+        else combine_wire
     return EpConfig(world_size, hidden_dim, scale_dim, scale_type_size if scale_dim else 0,
                     max_num_inp_token_per_rank, num_experts_per_rank, num_experts_per_token,
-                    dd, cd)
+                    dd, cd, cw)
 
 
 def ep_workspace_bytes(cfg: EpConfig) -> int:
@@ -218,12 +228,25 @@ def _dispatch_args(cfg: EpConfig, num_tokens: Sequence[int], x, indices, weights
     return a, nt
 
 
-def _combine_args(cfg: EpConfig, y, y_weights, out, out_weights):
+def wire_row_bytes(cfg: EpConfig):
+    """(bytes of one combine input row, bytes of its scale row) for the
+    config's combine wire."""
+    H = cfg.hidden_dim
+    if cfg.combine_wire == EP_WIRE_FP8_BLOCK128:
+        return H, H // 128 * 4
+    if cfg.combine_wire == EP_WIRE_MXFP4:
+        return H // 2, H // 32
+    return H * 2, 0
+
+
+def _combine_args(cfg: EpConfig, y, y_weights, out, out_weights, y_scales=None):
     W, M, k, _, crow, _ = _sizes(cfg)
     WM = W * M
-    return EpCombineArgs(_dev(y, "y", W * WM * crow), _dev(y_weights, "y_weights", W * WM * k * 4),
+    yrow, srow = wire_row_bytes(cfg)
+    return EpCombineArgs(_dev(y, "y", W * WM * yrow), _dev(y_weights, "y_weights", W * WM * k * 4),
                          _dev(out, "out", W * M * crow),
-                         _dev(out_weights, "out_weights", W * M * k * 4))
+                         _dev(out_weights, "out_weights", W * M * k * 4),
+                         _dev(y_scales, "y_scales", W * WM * srow))
 
 
 def ep_dispatch(plan: int, cfg: EpConfig, num_tokens: Sequence[int], x, indices, weights,
@@ -235,9 +258,10 @@ def ep_dispatch(plan: int, cfg: EpConfig, num_tokens: Sequence[int], x, indices,
     _check("ep_dispatch", load().ep_dispatch(plan, ctypes.byref(a), _stream(stream)))
 
 
-def ep_combine(plan: int, cfg: EpConfig, y, y_weights, out, out_weights, stream=None) -> None:
+def ep_combine(plan: int, cfg: EpConfig, y, y_weights, out, out_weights, stream=None,
+               y_scales=None) -> None:
     """ep_combine(); tensors as in include/ep.h, sizes checked against cfg."""
-    a = _combine_args(cfg, y, y_weights, out, out_weights)
+    a = _combine_args(cfg, y, y_weights, out, out_weights, y_scales)
     _check("ep_combine", load().ep_combine(plan, ctypes.byref(a), _stream(stream)))
 
 
@@ -253,6 +277,27 @@ def _same_tensors(held, given):
 
 def _hold(tensors):
     return tuple((t, None if t is None else t.data_ptr()) for t in tensors)
+
+
+def ep_quantize_rows(rows: torch.Tensor, wire, out: torch.Tensor, scales: torch.Tensor,
+                     stream=None) -> None:
+    """ep_quantize_rows(): rows [..., H] bf16 / fp16 into the wire format
+    (EP_WIRE_* or its name); out and scales sized as include/ep.h says."""
+    w = WIRES[wire] if wire is None or isinstance(wire, str) else wire
+    H = rows.shape[-1]
+    n = rows.numel() // H if H else 0
+    dt = {torch.bfloat16: EP_BF16, torch.float16: EP_FP16}.get(rows.dtype)
+    if dt is None:
+        raise ValueError(f"rows must be bf16 or fp16, not {rows.dtype}")
+    if w == EP_WIRE_FP8_BLOCK128:
+        need_out, need_sc = n * H, n * (H // 128) * 4
+    elif w == EP_WIRE_MXFP4:
+        need_out, need_sc = n * H // 2, n * (H // 32)
+    else:
+        raise ValueError(f"wire must be fp8_block128 or mxfp4, not {wire!r}")
+    _check("ep_quantize_rows", load().ep_quantize_rows(
+        _dev(rows, "rows", n * H * 2), n, H, dt, w, _dev(out, "out", need_out),
+        _dev(scales, "scales", need_sc), _stream(stream, rows.device.index)))
 
 
 def ep_get_src_token_pos(plan: int, rank: int) -> int:
@@ -413,12 +458,14 @@ class EpDispatchCombineOp:
         return (self.out_x, self.out_weights, self.out_scales, self.out_indices,
                 self.recv_num_token)
 
-    def combine(self, y, y_weights=None, stream=None):
-        given = (y, y_weights)
+    def combine(self, y, y_weights=None, stream=None, y_scales=None):
+        """With a combine wire in the config, y holds wire rows and y_scales
+        their scales (ep_quantize_rows writes both)."""
+        given = (y, y_weights, y_scales)
         c = self._ccache
         if c is None or not _same_tensors(c[0], given):
             a = _combine_args(self.cfg, y, y_weights, self.combine_out,
-                              self.combine_weights if y_weights is not None else None)
+                              self.combine_weights if y_weights is not None else None, y_scales)
             c = self._ccache = (_hold(given), a)
         _check("ep_combine", self._lib.ep_combine(self.plan, ctypes.byref(c[1]),
                                                   _stream(stream, self._dev_index)))

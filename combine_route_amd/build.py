@@ -10,7 +10,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libcombine_route_amd.so")
-SOURCES = [os.path.join(PKG, "csrc", f) for f in ("ep_plan.cpp", "ep_kernels.hip", "ep_expert.hip")]
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("ep_plan.cpp", "ep_kernels.hip", "ep_expert.hip", "ep_wire.hip")]
 ARCH = "gfx950"
 
 FLAGS = [
@@ -33,8 +33,25 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, extra=()) -> str:
+    """Compile every source to an object in parallel, then link the library."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+
+    def compile_one(src):
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        cmd = [hipcc(), *compile_flags, *extra, "-c", "-o", obj, src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as pool:
+        objs = list(pool.map(compile_one, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, *extra, "-o", tmp, *SOURCES]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -1,7 +1,7 @@
 // Internal interface between the host side of the library (ep_plan.cpp) and
 // its gfx950 kernels (ep_kernels.hip: dispatch and combine; ep_expert.hip:
-// the expert-major layout of received rows and its inverse). Not installed;
-// the public ABI is include/ep.h.
+// the expert-major layout of received rows and its inverse; ep_wire.hip: the
+// quantized combine wire). Not installed; the public ABI is include/ep.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -131,6 +131,31 @@ struct ExpertCombineArgs {
     int32_t rows;                // most received rows any rank can hold in this call
 };
 
+// Quantized combine wire (ep_wire.hip).
+constexpr int kWireFp8Block128 = 1;  // E4M3 codes, one FP32 scale per 128 elements
+constexpr int kWireMxfp4 = 2;        // packed E2M1 codes, one E8M0 scale per 32
+
+struct QuantizeArgs {
+    const uint8_t* in;           // [rows][H] bf16 / fp16
+    uint8_t* out;                // [rows][H] E4M3 or [rows][H / 2] packed E2M1
+    uint8_t* scales;             // [rows][H / 128] float or [rows][H / 32] E8M0
+    int64_t rows;
+    int32_t H;
+};
+
+struct WireCombineArgs {
+    const uint8_t* y;            // [W][WM] wire rows of row_bytes
+    const uint8_t* ys;           // [W][WM] scale rows of scale_bytes
+    const float* yw;             // [W][WM][k] or null
+    uint8_t* out;                // [W][M][H] combine dtype
+    float* out_w;                // [W][M][k] or null
+    const int32_t* fwd;          // [W][M][P]
+    int32_t cols;                // 8-element columns per row (H / 8)
+    int32_t piece_cols;          // columns per row piece
+    uint32_t row_bytes, scale_bytes;
+    int32_t M, k, P;
+};
+
 hipError_t launch_route(const RouteArgs& a, const TileMap& tm, hipStream_t s);
 hipError_t launch_scan(const ScanArgs& a, int W, hipStream_t s);
 // stream: true = streaming cache policy (rows bypass the caches), false =
@@ -146,5 +171,9 @@ hipError_t launch_expert_copy(const ExpertArgs& a, int waves, int row_split, boo
                               hipStream_t s);
 hipError_t launch_expert_combine(const ExpertCombineArgs& a, int W, int dtype, int waves,
                                  int row_split, bool stream, hipStream_t s);
+
+hipError_t launch_quantize(const QuantizeArgs& a, int wire, int dtype, hipStream_t s);
+hipError_t launch_combine_wire(const WireCombineArgs& a, const TokenMap& tk, int wire, int dtype,
+                               int waves, int row_split, bool stream, hipStream_t s);
 
 }  // namespace ep

@@ -101,6 +101,15 @@ int check_config(const ep_config_t* c, Shape* s)
                     c->combine_dtype);
     if (c->hidden_dim < 1)
         return fail(EP_ERR_ARG, "cfg.hidden_dim = %d: must be >= 1", c->hidden_dim);
+    if (c->combine_wire < EP_WIRE_NONE || c->combine_wire > EP_WIRE_MXFP4)
+        return fail(EP_ERR_ARG, "cfg.combine_wire = %d: must be an EP_WIRE_* value",
+                    c->combine_wire);
+    if (c->combine_wire == EP_WIRE_FP8_BLOCK128 && c->hidden_dim % 128 != 0)
+        return fail(EP_ERR_ARG, "cfg.hidden_dim = %d: EP_WIRE_FP8_BLOCK128 needs a multiple of 128",
+                    c->hidden_dim);
+    if (c->combine_wire == EP_WIRE_MXFP4 && c->hidden_dim % 32 != 0)
+        return fail(EP_ERR_ARG, "cfg.hidden_dim = %d: EP_WIRE_MXFP4 needs a multiple of 32",
+                    c->hidden_dim);
     const int64_t W = c->world_size, M = c->max_num_inp_token_per_rank;
     const int64_t row = (int64_t)c->hidden_dim * elem_bytes(c->dispatch_dtype);
     const int64_t crow = (int64_t)c->hidden_dim * 2;
@@ -668,6 +677,15 @@ int ep_combine(ep_plan_t* p, const ep_combine_args_t* a, void* stream_ptr)
                     "args.y_weights and args.out_weights must both be set or both NULL");
     if (a->y_weights && (!aligned(a->y_weights, 4) || !aligned(a->out_weights, 4)))
         return fail(EP_ERR_ALIGN, "args.y_weights / args.out_weights are not 4-byte aligned");
+    const int wire = p->cfg.combine_wire;
+    if (wire != EP_WIRE_NONE) {
+        if (!a->y_scales)
+            return fail(EP_ERR_NULL, "args.y_scales is NULL (cfg.combine_wire = %d)", wire);
+        if (!aligned(a->y_scales, 4))
+            return fail(EP_ERR_ALIGN, "args.y_scales is not 4-byte aligned");
+    } else if (a->y_scales) {
+        return fail(EP_ERR_ARG, "args.y_scales must be NULL when cfg.combine_wire = EP_WIRE_NONE");
+    }
     if (!p->dispatched)
         return fail(EP_ERR_STATE, "combine before any dispatch on this plan");
     const Shape& s = p->s;
@@ -683,29 +701,90 @@ int ep_combine(ep_plan_t* p, const ep_combine_args_t* a, void* stream_ptr)
     }
     tk.tok_start[s.W] = total;
     tk.total = total;
-
-    ep::CombineArgs ca;
-    ca.y = static_cast<const uint8_t*>(a->y);
-    ca.yw = a->y_weights;
-    ca.out = static_cast<uint8_t*>(a->out);
-    ca.out_w = a->out_weights;
-    ca.fwd = ws_fwd(p);
-    ca.row_vecs = (int32_t)(s.crow_bytes / 16);
-    ca.piece_vecs = (ca.row_vecs + l.combine_row_split - 1) / l.combine_row_split;
-    ca.M = s.M;
-    ca.k = s.k;
-    ca.P = s.P;
-    const int row_split = (ca.row_vecs + ca.piece_vecs - 1) / ca.piece_vecs;
     const int dtype = p->cfg.combine_dtype == EP_BF16 ? 0 : 1;
+    const bool streaming = l.cache_policy == EP_CACHE_STREAM;
 
-    const hipError_t e = timed(p, EP_KERNEL_COMBINE, stream, [&] {
-        return ep::launch_combine(ca, tk, dtype, l.combine_waves, row_split,
-                                  l.cache_policy == EP_CACHE_STREAM, stream);
-    });
+    hipError_t e;
+    if (wire == EP_WIRE_NONE) {
+        ep::CombineArgs ca;
+        ca.y = static_cast<const uint8_t*>(a->y);
+        ca.yw = a->y_weights;
+        ca.out = static_cast<uint8_t*>(a->out);
+        ca.out_w = a->out_weights;
+        ca.fwd = ws_fwd(p);
+        ca.row_vecs = (int32_t)(s.crow_bytes / 16);
+        ca.piece_vecs = (ca.row_vecs + l.combine_row_split - 1) / l.combine_row_split;
+        ca.M = s.M;
+        ca.k = s.k;
+        ca.P = s.P;
+        const int row_split = (ca.row_vecs + ca.piece_vecs - 1) / ca.piece_vecs;
+        e = timed(p, EP_KERNEL_COMBINE, stream, [&] {
+            return ep::launch_combine(ca, tk, dtype, l.combine_waves, row_split, streaming,
+                                      stream);
+        });
+    } else {
+        ep::WireCombineArgs wa;
+        wa.y = static_cast<const uint8_t*>(a->y);
+        wa.ys = static_cast<const uint8_t*>(a->y_scales);
+        wa.yw = a->y_weights;
+        wa.out = static_cast<uint8_t*>(a->out);
+        wa.out_w = a->out_weights;
+        wa.fwd = ws_fwd(p);
+        wa.cols = s.H / 8;
+        wa.piece_cols = (wa.cols + l.combine_row_split - 1) / l.combine_row_split;
+        if (wire == EP_WIRE_FP8_BLOCK128) {
+            wa.row_bytes = (uint32_t)s.H;
+            wa.scale_bytes = (uint32_t)(s.H / 128 * 4);
+        } else {
+            wa.row_bytes = (uint32_t)(s.H / 2);
+            wa.scale_bytes = (uint32_t)(s.H / 32);
+        }
+        wa.M = s.M;
+        wa.k = s.k;
+        wa.P = s.P;
+        const int row_split = (wa.cols + wa.piece_cols - 1) / wa.piece_cols;
+        const int kwire = wire == EP_WIRE_FP8_BLOCK128 ? ep::kWireFp8Block128 : ep::kWireMxfp4;
+        e = timed(p, EP_KERNEL_COMBINE, stream, [&] {
+            return ep::launch_combine_wire(wa, tk, kwire, dtype, l.combine_waves, row_split,
+                                           streaming, stream);
+        });
+    }
     p->launched = true;
     p->last_stream = stream;
     if (e != hipSuccess)
         return fail(EP_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int ep_quantize_rows(const void* in, int64_t rows, int32_t hidden, int32_t in_dtype,
+                     int32_t wire, void* out, void* scales, void* stream_ptr)
+{
+    if (!in || !out || !scales)
+        return fail(EP_ERR_NULL, "in, out and scales are required");
+    if (!aligned(in, kPtrAlign) || !aligned(out, kPtrAlign) || !aligned(scales, 4))
+        return fail(EP_ERR_ALIGN, "in / out must be 16-byte and scales 4-byte aligned");
+    if (in_dtype != EP_BF16 && in_dtype != EP_FP16)
+        return fail(EP_ERR_ARG, "in_dtype = %d: must be EP_BF16 or EP_FP16", in_dtype);
+    if (wire != EP_WIRE_FP8_BLOCK128 && wire != EP_WIRE_MXFP4)
+        return fail(EP_ERR_ARG, "wire = %d: must be EP_WIRE_FP8_BLOCK128 or EP_WIRE_MXFP4", wire);
+    if (rows < 0)
+        return fail(EP_ERR_ARG, "rows = %lld: must be >= 0", (long long)rows);
+    const int block = wire == EP_WIRE_FP8_BLOCK128 ? 128 : 32;
+    if (hidden < 1 || hidden % block != 0)
+        return fail(EP_ERR_ARG, "hidden = %d: must be a positive multiple of %d", hidden, block);
+    if (rows * (int64_t)hidden >= ((int64_t)1 << 40))
+        return fail(EP_ERR_SIZE, "rows * hidden is too large");
+    ep::QuantizeArgs qa;
+    qa.in = static_cast<const uint8_t*>(in);
+    qa.out = static_cast<uint8_t*>(out);
+    qa.scales = static_cast<uint8_t*>(scales);
+    qa.rows = rows;
+    qa.H = hidden;
+    const hipError_t e =
+        ep::launch_quantize(qa, wire == EP_WIRE_FP8_BLOCK128 ? ep::kWireFp8Block128 : ep::kWireMxfp4,
+                            in_dtype == EP_BF16 ? 0 : 1, static_cast<hipStream_t>(stream_ptr));
+    if (e != hipSuccess)
+        return fail(EP_ERR_HIP, "quantize launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 

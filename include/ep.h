@@ -76,6 +76,20 @@ extern "C" {
  * bytes; EP_FP8_E4M3 is one byte an element). Combine: EP_BF16 or EP_FP16. */
 enum { EP_BF16 = 0, EP_FP16 = 1, EP_FP8_E4M3 = 2 };
 
+/* Combine wire formats (the rows the combine reads; R: the pages name
+ * fp8_blockwise and fp4 with e8m0 scales, [PR726], [GUIDE] section 10, and
+ * the arithmetic follows the OCP OFP8 and MX v1.0 specifications):
+ *   EP_WIRE_NONE          rows in combine_dtype.
+ *   EP_WIRE_FP8_BLOCK128  OCP E4M3 codes, H bytes a row, with one FP32 scale
+ *                         per 128 elements (H / 128 floats a row): value =
+ *                         code value * scale.
+ *   EP_WIRE_MXFP4         OCP E2M1 codes, two a byte (even element in the low
+ *                         nibble), H / 2 bytes a row, with one E8M0 scale per
+ *                         32 elements (H / 32 bytes a row): value = code
+ *                         value * 2^(scale - 127).
+ * ep_quantize_rows writes either from bf16 / fp16 rows. */
+enum { EP_WIRE_NONE = 0, EP_WIRE_FP8_BLOCK128 = 1, EP_WIRE_MXFP4 = 2 };
+
 enum {
     EP_OK = 0,
     EP_ERR_NULL = -1,  /* a required pointer is NULL                          */
@@ -98,7 +112,9 @@ enum {
  *   scale_dim >= 0; if scale_dim > 0: scale_type_size in {1, 2, 4, 8} and
  *   scale_dim * scale_type_size % 4 == 0;
  *   dispatch_dtype in {EP_BF16, EP_FP16, EP_FP8_E4M3};
- *   combine_dtype in {EP_BF16, EP_FP16}. */
+ *   combine_dtype in {EP_BF16, EP_FP16};
+ *   combine_wire in EP_WIRE_*: with EP_WIRE_FP8_BLOCK128 hidden_dim % 128 ==
+ *   0, with EP_WIRE_MXFP4 hidden_dim % 32 == 0. */
 typedef struct ep_config {
     int32_t world_size;
     int32_t hidden_dim;
@@ -109,6 +125,7 @@ typedef struct ep_config {
     int32_t num_experts_per_token;
     int32_t dispatch_dtype;
     int32_t combine_dtype;
+    int32_t combine_wire;
 } ep_config_t;
 
 typedef struct ep_plan ep_plan_t;
@@ -177,7 +194,11 @@ int ep_dispatch(ep_plan_t *plan, const ep_dispatch_args_t *args, void *stream);
 /* Combine arguments (device pointers, 16-byte aligned):
  *   y            [W][WM][H] combine_dtype: expert output for each received
  *                row (rows s < recv_num_token[d] are read). May be the
- *                dispatch's out_x when the types match.
+ *                dispatch's out_x when the types match. With a combine_wire,
+ *                [W][WM] rows of that wire format instead.
+ *   y_scales     the wire rows' scales, [W][WM][H / 128] float or
+ *                [W][WM][H / 32] E8M0 bytes (4-byte aligned); NULL iff
+ *                combine_wire is EP_WIRE_NONE.
  *   y_weights    [W][WM][k] float, or NULL (then out_weights must be NULL).
  *   out          [W][M][H] combine_dtype: rows t < T_r of the last dispatch
  *                are written, others untouched. Must not overlap y.
@@ -188,6 +209,7 @@ typedef struct ep_combine_args {
     const float *y_weights;
     void *out;
     float *out_weights;
+    const void *y_scales;
 } ep_combine_args_t;
 
 /* Combine ([PR712] Combine) using the routing handle of the last ep_dispatch
@@ -198,6 +220,20 @@ typedef struct ep_combine_args {
  * Errors: EP_ERR_NULL, EP_ERR_ARG (NULL/non-NULL pairing), EP_ERR_ALIGN,
  * EP_ERR_STATE (no dispatch yet on this plan), EP_ERR_HIP. */
 int ep_combine(ep_plan_t *plan, const ep_combine_args_t *args, void *stream);
+
+/* Quantize rows[rows][hidden] of in_dtype (EP_BF16 or EP_FP16) into the wire
+ * format `wire` (EP_WIRE_FP8_BLOCK128 or EP_WIRE_MXFP4; see EP_WIRE_*), the
+ * send side of a quantized combine: out gets the codes, scales the block
+ * scales. FP8: s = amax / 448 and codes E4M3(v * (448 / amax)), round to
+ * nearest even, saturating (s = 1 for an all-zero block). MXFP4 (the OCP MX
+ * conversion): scale 2^(floor(log2 amax) - 2), codes E2M1(v / scale), round
+ * to nearest even, saturating at 6 (scale code 0 for an all-zero block);
+ * inputs finite. Device pointers: in and out 16-byte aligned, scales 4-byte
+ * aligned; no plan, no allocation, asynchronous on stream, capturable.
+ * Errors: EP_ERR_NULL, EP_ERR_ALIGN, EP_ERR_ARG (types, wire, rows < 0,
+ * hidden not a positive multiple of the block), EP_ERR_HIP. */
+int ep_quantize_rows(const void *in, int64_t rows, int32_t hidden, int32_t in_dtype,
+                     int32_t wire, void *out, void *scales, void *stream);
 
 /* Reverse map of rank `rank` ([GUIDE] section 3, get_dispatch_src_token_pos():
  * src_rank * (world_size * max_num_inp_token_per_rank) + src_token_id).

@@ -539,8 +539,10 @@ float oracle_e4m3_to_f32(uint8_t c)
     return sign ? -v : v;
 }
 
-/* Nearest finite E4M3 value by search over all 127 magnitudes; a tie goes
- * to the code whose mantissa is even; beyond 448 saturate. */
+/* Nearest finite E4M3 value: codes 0..0x7E of one sign are ordered like
+ * their magnitudes, so a binary search finds the two neighbours of |v|; the
+ * nearer wins and a tie goes to the code whose mantissa is even; beyond 448
+ * saturate. */
 uint8_t oracle_f32_to_e4m3(float v)
 {
     if (isnan(v))
@@ -549,15 +551,17 @@ uint8_t oracle_f32_to_e4m3(float v)
     double a = fabs((double)v);
     if (a >= 448.0)
         return sign | 0x7E;
-    int best = 0;
-    double bd = a;                      /* distance to code 0 (zero) */
-    for (int c = 1; c <= 0x7E; ++c) {
-        double d = fabs((double)oracle_e4m3_to_f32((uint8_t)c) - a);
-        if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) {
-            bd = d;
-            best = c;
-        }
+    int lo = 0, hi = 0x7E;             /* value(lo) <= a < value(hi) */
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if ((double)oracle_e4m3_to_f32((uint8_t)mid) <= a)
+            lo = mid;
+        else
+            hi = mid;
     }
+    double dlo = a - (double)oracle_e4m3_to_f32((uint8_t)lo);
+    double dhi = (double)oracle_e4m3_to_f32((uint8_t)hi) - a;
+    int best = dlo < dhi ? lo : dhi < dlo ? hi : ((lo & 1) == 0 ? lo : hi);
     return sign | (uint8_t)best;
 }
 

@@ -39,7 +39,7 @@ def header_functions():
 
 def test_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     assert sorted(cra.EXPORTED) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -84,6 +84,9 @@ BAD_CONFIGS = [
     (dict(scale_dim=-1), "scale_dim"), (dict(scale_dim=3, scale_type_size=3), "scale_type_size"),
     (dict(scale_dim=3, scale_type_size=2), "scale_dim * cfg.scale_type_size"),
     (dict(world_size=64, max_num_inp_token_per_rank=600000), "2^31"),
+    (dict(combine_wire=3), "combine_wire"), (dict(combine_wire=-1), "combine_wire"),
+    (dict(combine_wire=1, hidden_dim=7168 + 64), "EP_WIRE_FP8_BLOCK128"),
+    (dict(combine_wire=2, hidden_dim=7168 + 16), "EP_WIRE_MXFP4"),
 ]
 
 
@@ -205,10 +208,11 @@ def test_dispatch_requires_scales_when_configured(lib):
 def test_combine_errors_and_state(lib):
     cfg = cra.make_config(2, 256, 16, 4, 2)
     rc, plan = make_plan(lib, cfg)
-    ok = dict(y=FAKE, y_weights=None, out=FAKE + 0x1000, out_weights=None)
+    ok = dict(y=FAKE, y_weights=None, out=FAKE + 0x1000, out_weights=None, y_scales=None)
     cases = [(dict(y=None), cra.EP_ERR_NULL, "args.y"), (dict(out=None), cra.EP_ERR_NULL, "args.out"),
              (dict(y=FAKE + 2), cra.EP_ERR_ALIGN, "aligned"),
              (dict(y_weights=FAKE + 0x2000), cra.EP_ERR_ARG, "weights"),
+             (dict(y_scales=FAKE + 0x3000), cra.EP_ERR_ARG, "y_scales"),
              ({}, cra.EP_ERR_STATE, "before any dispatch")]
     for over, code, word in cases:
         a = cra.EpCombineArgs(**{**ok, **over})
@@ -439,3 +443,46 @@ def test_expert_launch_overrides(lib):
     assert auto["expert_cache_policy"] == cra.EP_CACHE_STREAM
     assert small["expert_cache_policy"] == cra.EP_CACHE_KEEP
     lib.ep_plan_destroy(plan)
+
+
+# ---------------------------------------------------------------------------
+# quantized combine wire
+# ---------------------------------------------------------------------------
+
+def test_wire_combine_requires_scales(lib):
+    for wire in (cra.EP_WIRE_FP8_BLOCK128, cra.EP_WIRE_MXFP4):
+        cfg = cra.make_config(2, 256, 16, 4, 2, combine_wire=wire)
+        rc, plan = make_plan(lib, cfg)
+        assert rc == 0
+        a = cra.EpCombineArgs(y=FAKE, y_weights=None, out=FAKE + 0x1000, out_weights=None,
+                              y_scales=None)
+        assert lib.ep_combine(plan, ctypes.byref(a), None) == cra.EP_ERR_NULL
+        assert "y_scales" in cra.ep_last_error()
+        a.y_scales = FAKE + 0x2002
+        assert lib.ep_combine(plan, ctypes.byref(a), None) == cra.EP_ERR_ALIGN
+        a.y_scales = FAKE + 0x2000
+        assert lib.ep_combine(plan, ctypes.byref(a), None) == cra.EP_ERR_STATE
+        lib.ep_plan_destroy(plan)
+
+
+@pytest.mark.parametrize("args,code,word", [
+    ((None, 4, 256, 0, 1, FAKE, FAKE + 0x1000), cra.EP_ERR_NULL, "required"),
+    ((FAKE, 4, 256, 0, 1, FAKE, None), cra.EP_ERR_NULL, "required"),
+    ((FAKE + 8, 4, 256, 0, 1, FAKE, FAKE + 0x1000), cra.EP_ERR_ALIGN, "aligned"),
+    ((FAKE, 4, 256, 0, 1, FAKE, FAKE + 0x1002), cra.EP_ERR_ALIGN, "aligned"),
+    ((FAKE, 4, 256, 2, 1, FAKE, FAKE + 0x1000), cra.EP_ERR_ARG, "in_dtype"),
+    ((FAKE, 4, 256, 0, 0, FAKE, FAKE + 0x1000), cra.EP_ERR_ARG, "wire"),
+    ((FAKE, 4, 256, 0, 3, FAKE, FAKE + 0x1000), cra.EP_ERR_ARG, "wire"),
+    ((FAKE, -1, 256, 0, 1, FAKE, FAKE + 0x1000), cra.EP_ERR_ARG, "rows"),
+    ((FAKE, 4, 192, 0, 1, FAKE, FAKE + 0x1000), cra.EP_ERR_ARG, "multiple of 128"),
+    ((FAKE, 4, 48, 1, 2, FAKE, FAKE + 0x1000), cra.EP_ERR_ARG, "multiple of 32"),
+    ((FAKE, 4, 0, 0, 2, FAKE, FAKE + 0x1000), cra.EP_ERR_ARG, "multiple of 32"),
+])
+def test_quantize_rows_rejects_before_launch(lib, args, code, word):
+    src, rows, H, dt, wire, out, sc = args
+    assert lib.ep_quantize_rows(src, rows, H, dt, wire, out, sc, None) == code
+    assert word in cra.ep_last_error()
+
+
+def test_quantize_zero_rows_is_a_no_op(lib):
+    assert lib.ep_quantize_rows(FAKE, 0, 256, 0, 1, FAKE, FAKE + 0x1000, None) == cra.EP_OK

@@ -1,0 +1,189 @@
+"""GPU parity of the quantized combine wire, through the C ABI.
+
+The wire formats (FP8 E4M3 with FP32 scales per 128 elements; MXFP4) follow
+the OCP OFP8 and MX v1.0 specifications, as the oracle does; the pages name
+fp8_blockwise and fp4 with e8m0 scales ("gfx1250 EPv2: ..." PR 726; "MORI-EP
+User Guide", section 10). Every comparison is bit for bit: codes and scales
+of ep_quantize_rows against the oracle's quantizer, every in-range bf16
+value through the element conversions, and the combine from wire rows (the
+oracle's own quantized rows, uploaded) against the oracle's combine.
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_route_amd as cra
+import oracle
+import workloads
+
+from test_gpu_parity import _say, compare_dispatch, gpu_dispatch, oracle_dispatch
+
+pytestmark = pytest.mark.gpu
+
+WIRES = {"fp8_block128": (cra.EP_WIRE_FP8_BLOCK128, oracle.WIRE_FP8_BLOCK128),
+         "mxfp4": (cra.EP_WIRE_MXFP4, oracle.WIRE_MXFP4)}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cra.load()
+
+
+def rows_of(seed, n, H, dtype, spread=4.0):
+    """Rows with magnitudes spread over many binades per 32-element group,
+    some all-zero groups and some tiny (subnormal-range) ones."""
+    g = torch.Generator().manual_seed(seed)
+    mag = torch.exp(torch.randn((n, H // 32, 1), generator=g) * spread)
+    v = torch.randn((n, H // 32, 32), generator=g) * mag
+    v[:, ::7] = 0.0
+    v[:, 3::11] *= 1e-38
+    return v.reshape(n, H).to(dtype)
+
+
+def gpu_quantize(v, wire):
+    n, H = v.shape
+    if wire == cra.EP_WIRE_FP8_BLOCK128:
+        out = torch.empty((n, H), dtype=torch.uint8, device="cuda")
+        sc = torch.empty((n, H // 128), dtype=torch.float32, device="cuda")
+    else:
+        out = torch.empty((n, H // 2), dtype=torch.uint8, device="cuda")
+        sc = torch.empty((n, H // 32), dtype=torch.uint8, device="cuda")
+    cra.ep_quantize_rows(v.cuda(), wire, out, sc)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), sc.cpu().numpy()
+
+
+def words(v):
+    return v.view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("name", list(WIRES))
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("n,H", [(1, 128), (5, 384), (33, 1024), (300, 7168)])
+def test_quantize_matches_oracle(name, dtype, n, H):
+    cw, ow = WIRES[name]
+    _say(f"[case] quantize {name} {dtype} n={n} H={H}")
+    v = rows_of(n * 7 + H, n, H, dtype, spread=2.0 if dtype == torch.float16 else 4.0)
+    got_c, got_s = gpu_quantize(v, cw)
+    ref_c, ref_s = oracle.quantize_rows(words(v), oracle.BF16 if dtype == torch.bfloat16
+                                        else oracle.FP16, ow)
+    assert np.array_equal(got_c, ref_c)
+    assert np.array_equal(got_s.view(np.uint8), ref_s.view(np.uint8))
+
+
+def test_e4m3_conversion_of_every_in_range_bf16_value():
+    """Blocks whose largest magnitude is 448 have scale 1: each code is then
+    the direct E4M3 conversion of the bf16 value itself."""
+    w = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16)
+    keep = torch.isfinite(v) & (v.float().abs() < 448)
+    vals = v[keep]
+    nb = -(-vals.numel() // 127)
+    blocks = torch.zeros((nb, 128), dtype=torch.bfloat16)
+    blocks[:, 0] = 448.0
+    flat = blocks[:, 1:].reshape(-1)
+    flat[:vals.numel()] = vals
+    blocks[:, 1:] = flat.reshape(nb, 127)
+    rows = blocks.reshape(-1, 1024) if nb % 8 == 0 else blocks.reshape(nb, 128)
+    got_c, got_s = gpu_quantize(rows, cra.EP_WIRE_FP8_BLOCK128)
+    assert (got_s == 1.0).all()
+    ref = oracle.cast_to_e4m3(words(rows), oracle.BF16)
+    assert np.array_equal(got_c, ref)
+
+
+def test_e2m1_conversion_of_every_bf16_value_below_8():
+    """Blocks whose largest magnitude is 4 have scale 2^0: each code is then
+    the E2M1 conversion of the value itself."""
+    w = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16)
+    keep = torch.isfinite(v) & (v.float().abs() <= 4)
+    vals = v[keep]
+    nb = -(-vals.numel() // 31)
+    blocks = torch.zeros((nb, 32), dtype=torch.bfloat16)
+    blocks[:, 0] = 4.0
+    flat = blocks[:, 1:].reshape(-1)
+    flat[:vals.numel()] = vals
+    blocks[:, 1:] = flat.reshape(nb, 31)
+    got_c, got_s = gpu_quantize(blocks, cra.EP_WIRE_MXFP4)
+    assert (got_s == 127).all()
+    ref_c, _ = oracle.quantize_rows(words(blocks), oracle.BF16, oracle.WIRE_MXFP4)
+    assert np.array_equal(got_c, ref_c)
+
+
+def run_wire_case(wl, name, launch=None, with_weights=True, tag=None):
+    cw, ow = WIRES[name]
+    W, M, k, H = wl.world_size, wl.max_tokens, wl.topk, wl.hidden
+    tag = tag or f"{wl.name} {name}"
+    _say(f"[case] wire combine {tag}: W={W} M={M} H={H} k={k} launch={launch}")
+    inp = workloads.make_inputs(wl)
+    if not with_weights:
+        inp["w"] = None
+    ref = oracle_dispatch(wl, inp)
+    cfg = cra.make_config(W, H, M, wl.experts_per_rank, k, wl.dispatch_dtype, wl.combine_dtype,
+                          scale_dim=wl.scale_dim, scale_type_size=4, combine_wire=cw)
+    op = cra.EpDispatchCombineOp(cfg, with_weights=with_weights)
+    if launch:
+        op.set_launch(launch)
+    gpu_dispatch(op, inp)
+    torch.cuda.synchronize()
+    compare_dispatch(wl, op, ref, tag)
+    # expert outputs: up to 4096 seeded bf16/fp16 rows quantized by the
+    # oracle, repeated over the [W][W*M] rows
+    cdt = workloads.TORCH_DTYPE[wl.combine_dtype]
+    base = min(4096, W * W * M)
+    yb = rows_of(W * M + H, base, H, cdt, spread=2.0 if cdt == torch.float16 else 4.0)
+    assert torch.isfinite(yb).all()                  # the wire takes finite rows
+    cb, sb = oracle.quantize_rows(words(yb), oracle.BF16 if wl.combine_dtype == "bf16"
+                                  else oracle.FP16, ow)
+    sel = np.arange(W * W * M) % base
+    codes, scales = cb[sel], sb[sel]
+    yq = torch.from_numpy(codes.reshape(W, W * M, -1)).cuda()
+    ys = torch.from_numpy(scales.reshape(W, W * M, -1)).cuda()
+    yw = None if ref["out_w"] is None else torch.from_numpy(ref["out_w"]).cuda()
+    out, out_w = op.combine(yq, yw, y_scales=ys)
+    torch.cuda.synchronize()
+    dt = oracle.BF16 if wl.combine_dtype == "bf16" else oracle.FP16
+    ro = oracle.combine_wire(W, M, k, H, dt, ow, inp["ntok"], ref["fwd"],
+                             codes.reshape(W, W * M, -1), scales.reshape(W, W * M, -1))
+    g = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    for r in range(W):
+        T = inp["ntok"][r]
+        assert np.array_equal(g[r, :T], ro[r, :T]), (tag, "wire combine", r)
+    if yw is not None:
+        # the weight sums do not depend on the payload: an 8-wide dummy
+        _, rw = oracle.combine(W, M, k, 8, dt, inp["ntok"], ref["fwd"],
+                               np.zeros((W, W * M, 8), np.uint16), ref["out_w"])
+        gw = out_w.cpu().numpy().view(np.uint32)
+        for r in range(W):
+            T = inp["ntok"][r]
+            assert np.array_equal(gw[r, :T], rw[r, :T].view(np.uint32)), (tag, "weights", r)
+    op.close()
+
+
+@pytest.mark.parametrize("name", list(WIRES))
+@pytest.mark.parametrize("wl_name", ["ep8_t4096_h7168_bf16_k8", "ep8_t128_h7168_fp8_k8_zipf",
+                                     "ep4_ragged1024_h2048_fp16_k64"])
+def test_wire_combine_full_size(name, wl_name):
+    run_wire_case(workloads.WORKLOADS[wl_name], name)
+
+
+@pytest.mark.parametrize("name", list(WIRES))
+@pytest.mark.parametrize("W,k,H", [(1, 1, 128), (2, 2, 256), (3, 9, 384), (16, 8, 1024),
+                                   (64, 64, 128)])
+def test_wire_combine_shapes(name, W, k, H):
+    M = 40 if W <= 16 else 6
+    wl = workloads.custom(f"wire_W{W}_k{k}_H{H}", W, M, H, k, max(k, W * 4), "bf16",
+                          ragged=True, seed_index=800 + W + k)
+    run_wire_case(wl, name, with_weights=W % 2 == 0)
+
+
+@pytest.mark.parametrize("launch", [dict(combine_waves=1, combine_row_split=3),
+                                    dict(combine_waves=16, cache_policy=cra.EP_CACHE_STREAM),
+                                    dict(combine_row_split=7, cache_policy=cra.EP_CACHE_KEEP)])
+def test_wire_geometry_does_not_change_results(launch):
+    wl = workloads.custom("wire_geom_ep4_t200_h1024", 4, 200, 1024, 8, 64, "bf16", ragged=True,
+                          seed_index=820)
+    for name in WIRES:
+        run_wire_case(wl, name, launch=launch, tag=f"geom {name} {launch}")
