@@ -30,6 +30,9 @@ EP_CACHE_AUTO, EP_CACHE_STREAM, EP_CACHE_KEEP = 0, 1, 2
 EP_LAYOUT_AUTO, EP_LAYOUT_KERNELS, EP_LAYOUT_SCAN_IN_COPY, EP_LAYOUT_IN_COPY = 0, 1, 2, 3
 
 EP_WIRE_NONE, EP_WIRE_FP8_BLOCK128, EP_WIRE_MXFP4 = 0, 1, 2
+EP_CAST_NONE, EP_CAST_FP8_FROM_BF16, EP_CAST_FP8_FROM_FP16 = 0, 1, 2
+CASTS = {None: EP_CAST_NONE, "none": EP_CAST_NONE, "bf16": EP_CAST_FP8_FROM_BF16,
+         "fp16": EP_CAST_FP8_FROM_FP16}
 
 DTYPES = {"bf16": EP_BF16, "fp16": EP_FP16, "fp8": EP_FP8_E4M3}
 WIRES = {None: EP_WIRE_NONE, "none": EP_WIRE_NONE, "fp8_block128": EP_WIRE_FP8_BLOCK128,
@@ -48,7 +51,7 @@ class EpConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "world_size", "hidden_dim", "scale_dim", "scale_type_size", "max_num_inp_token_per_rank",
         "num_experts_per_rank", "num_experts_per_token", "dispatch_dtype", "combine_dtype",
-        "combine_wire")]
+        "combine_wire", "dispatch_cast")]
 
 
 class EpDispatchArgs(ctypes.Structure):
@@ -138,16 +141,20 @@ def _check(fn, rc):
 
 def make_config(world_size, hidden_dim, max_num_inp_token_per_rank, num_experts_per_rank,
                 num_experts_per_token, dispatch_dtype="bf16", combine_dtype=None,
-                scale_dim=0, scale_type_size=4, combine_wire=None) -> EpConfig:
+                scale_dim=0, scale_type_size=4, combine_wire=None, dispatch_cast=None) -> EpConfig:
+    """dispatch_cast: None, or "bf16" / "fp16": x of that type received as
+    FP8 E4M3 (dispatch_dtype must then be "fp8")."""
     dd = DTYPES[dispatch_dtype] if isinstance(dispatch_dtype, str) else dispatch_dtype
     if combine_dtype is None:
         combine_dtype = EP_FP16 if dd == EP_FP16 else EP_BF16
     cd = DTYPES[combine_dtype] if isinstance(combine_dtype, str) else combine_dtype
     cw = WIRES[combine_wire] if combine_wire is None or isinstance(combine_wire, str) \
         else combine_wire
+    dc = CASTS[dispatch_cast] if dispatch_cast is None or isinstance(dispatch_cast, str) \
+        else dispatch_cast
     return EpConfig(world_size, hidden_dim, scale_dim, scale_type_size if scale_dim else 0,
                     max_num_inp_token_per_rank, num_experts_per_rank, num_experts_per_token,
-                    dd, cd, cw)
+                    dd, cd, cw, dc)
 
 
 def ep_workspace_bytes(cfg: EpConfig) -> int:
@@ -213,13 +220,14 @@ def _dispatch_args(cfg: EpConfig, num_tokens: Sequence[int], x, indices, weights
                    out_indices, out_weights, out_scales, recv_num_token):
     """Checked ep_dispatch_args_t, and the ctypes array it points into."""
     W, M, k, row, _, srow = _sizes(cfg)
+    xrow = cfg.hidden_dim * 2 if cfg.dispatch_cast else row
     WM = W * M
     if len(num_tokens) != W:
         raise ValueError(f"num_tokens has {len(num_tokens)} entries; world_size is {W}")
     nt = (ctypes.c_int32 * W)(*[int(v) for v in num_tokens])
     a = EpDispatchArgs(
         ctypes.cast(nt, ctypes.c_void_p),
-        _dev(x, "x", W * M * row), _dev(indices, "indices", W * M * k * 4),
+        _dev(x, "x", W * M * xrow), _dev(indices, "indices", W * M * k * 4),
         _dev(weights, "weights", W * M * k * 4), _dev(scales, "scales", W * M * srow),
         _dev(out_x, "out_x", W * WM * row), _dev(out_indices, "out_indices", W * WM * k * 4),
         _dev(out_weights, "out_weights", W * WM * k * 4),

@@ -14,6 +14,7 @@ namespace dev {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Cache policy of the row moves, as gfx950 buffer-instruction bits (1 = sc0,
 // 2 = nt, 16 = sc1). Streaming calls (footprint well past the 256 MB MALL)
@@ -104,6 +105,30 @@ __device__ __forceinline__ u32x4 narrow(const float (&f)[8])
         }
     }
     return w;
+}
+
+constexpr float kE4M3Max = 448.0f;
+
+// OCP E4M3 code (the OFP8 specification: bias 7, no infinities, largest
+// finite 448) of an FP32 value: round to nearest even, saturate past 448,
+// NaN -> 0x7F. Integer and power-of-two arithmetic plus rint, so exact.
+__device__ __forceinline__ uint32_t to_e4m3(float v)
+{
+    if (__builtin_isnan(v))
+        return 0x7Fu;
+    const uint32_t sign = (__builtin_bit_cast(uint32_t, v) >> 24) & 0x80u;
+    const float a = __builtin_fabsf(v);
+    uint32_t c;
+    if (a >= kE4M3Max) {
+        c = 0x7Eu;
+    } else if (a < 0x1p-6f) {  // subnormal codes: multiples of 2^-9
+        c = (uint32_t)__builtin_rintf(a * 0x1p9f);
+    } else {
+        const int e = __builtin_amdgcn_frexp_expf(a) - 1;  // floor(log2 a), -6..8
+        const uint32_t m = (uint32_t)__builtin_rintf(__builtin_ldexpf(a, 3 - e));  // 8..16
+        c = ((uint32_t)(e + 7) << 3) + m - 8;  // m = 16 carries into the next binade
+    }
+    return sign | c;
 }
 
 // One wave folds the n contribution rows whose row numbers (in units of

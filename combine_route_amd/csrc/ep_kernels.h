@@ -71,11 +71,12 @@ struct CopyArgs {
     int32_t layout;              // LayoutMode
     int32_t* src_pos;            // [W][WM]
     int32_t* fwd;                // [W][M][P]
-    int32_t row_vecs;            // 16-byte vectors per payload row
+    int32_t row_vecs;            // 16-byte vectors per payload row (of x)
     int32_t piece_vecs;          // 16-byte vectors per row piece (one block)
     int32_t scale_dwords;        // 4-byte words per scale row (0: none)
     int32_t M, k, Er, E, P, WM;
     int32_t tile_stride;
+    int32_t cast;                // 0: rows copied; 1 / 2: bf16 / fp16 x cast to E4M3
 };
 
 struct CombineArgs {

@@ -275,6 +275,21 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(ScanArgs a)
 // ---------------------------------------------------------------------------
 // copy: payload rows, metadata rows, src_pos and the forward map.
 // ---------------------------------------------------------------------------
+// 8 bf16 (cast 1) or fp16 (cast 2) elements -> 8 E4M3 codes.
+__device__ __forceinline__ u32x2 cast_e4m3(const u32x4& w, int cast)
+{
+    float f[8];
+    if (cast == 2)
+        widen<1>(w, f);
+    else
+        widen<0>(w, f);
+    u32x2 out = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        out[i / 4] |= to_e4m3(f[i]) << (8 * (i % 4));
+    return out;
+}
+
 // One work item of a wave: one chunk (up to 64 x VPL 16-byte vectors) of one
 // token's row piece, and, for the first chunk of a piece-0 block, the lane's
 // share of the token's id, weight and scale rows.
@@ -288,8 +303,10 @@ struct CopyItem {
 
 // kInCopy: the block counts every tile of the call itself (kLayoutInCopy, k <=
 // 16 only); a separate instantiation, so the other calls do not carry its
-// registers.
-template <int VPL, int KB, bool kStream, bool kInCopy>
+// registers. kCast: the payload arrives as bf16 / fp16 (a.cast) and each
+// element is stored as its OCP E4M3 code (round to nearest even, saturating
+// at 448); a 16-byte vector of 8 input elements becomes 8 output bytes.
+template <int VPL, int KB, bool kStream, bool kInCopy, bool kCast = false>
 __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
 {
     __shared__ uint8_t s_list[kMaxTile][kMaxRanks];  // [token][i]: i-th distinct rank
@@ -315,7 +332,8 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
     const int ntw = wave < cnt ? (cnt - wave + nwaves - 1) / nwaves : 0;
     const int items = ntw * nch;
     const bool meta = piece == 0;
-    const uint32_t row_bytes = (uint32_t)a.row_vecs * 16u;
+    const uint32_t row_bytes = (uint32_t)a.row_vecs * 16u;                  // input row
+    const uint32_t out_bytes = kCast ? (uint32_t)a.row_vecs * 8u : row_bytes;  // received row
     const int k = a.k;
     const int per = kWave / k;  // destination id/weight rows per store instruction
     const int j = lane % k;
@@ -371,12 +389,18 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
             const int d = uniform(s_list[tok][i]);
             const int s = uniform(s_base[d] + s_loc[tok][d]);
             const __amdgpu_buffer_rsrc_t rd =
-                row_rsrc(a.out_x + ((int64_t)d * a.WM + s) * row_bytes, row_bytes);
+                row_rsrc(a.out_x + ((int64_t)d * a.WM + s) * out_bytes, out_bytes);
 #pragma unroll
             for (int u = 0; u < VPL; ++u) {
                 const int vv = v0 + u * kWave + lane;
-                if (vv < vend)
-                    bstore16<Policy<kStream>::copy_store>(v[u], rd, (uint32_t)vv * 16u);
+                if (vv < vend) {
+                    if constexpr (kCast)
+                        __builtin_amdgcn_raw_buffer_store_b64(
+                            cast_e4m3(v[u], a.cast), rd, (int)((uint32_t)vv * 8u), 0,
+                            Policy<kStream>::copy_store);
+                    else
+                        bstore16<Policy<kStream>::copy_store>(v[u], rd, (uint32_t)vv * 16u);
+                }
             }
         }
     };
@@ -580,6 +604,17 @@ template <int VPL, int KB>
 hipError_t copy_with(const CopyArgs& a, const TileMap& tm, dim3 grid, dim3 block, bool stream,
                      hipStream_t s)
 {
+    if (a.cast) {
+        if (a.layout == kLayoutInCopy)
+            return hipErrorInvalidValue;  // the host never selects it with a cast
+        if (stream)
+            hipLaunchKernelGGL((ep_copy_kernel<VPL, KB, true, false, true>), grid, block, 0, s,
+                               a, tm);
+        else
+            hipLaunchKernelGGL((ep_copy_kernel<VPL, KB, false, false, true>), grid, block, 0, s,
+                               a, tm);
+        return hipGetLastError();
+    }
     if constexpr (KB <= 16) {
         if (a.layout == kLayoutInCopy) {
             const size_t lds = sizeof(int32_t) * tm.total_tiles * tm.W;

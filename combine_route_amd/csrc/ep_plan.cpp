@@ -68,7 +68,9 @@ int elem_bytes(int dtype) { return dtype == EP_FP8_E4M3 ? 1 : 2; }
 struct Shape {
     int W, M, k, Er, P, H;
     int64_t E, WM;
-    int64_t row_bytes;    // dispatch payload row
+    int64_t row_bytes;    // dispatch payload row as received
+    int64_t x_bytes;      // dispatch payload row as sent (2H with a cast)
+    int row_vecs;         // 16-byte vectors of an x row: the copy's work unit
     int64_t crow_bytes;   // combine row
     int64_t scale_bytes;  // scale row
     int tile_stride;      // tiles a rank-major tile array can need (tile 16)
@@ -110,6 +112,12 @@ int check_config(const ep_config_t* c, Shape* s)
     if (c->combine_wire == EP_WIRE_MXFP4 && c->hidden_dim % 32 != 0)
         return fail(EP_ERR_ARG, "cfg.hidden_dim = %d: EP_WIRE_MXFP4 needs a multiple of 32",
                     c->hidden_dim);
+    if (c->dispatch_cast < EP_CAST_NONE || c->dispatch_cast > EP_CAST_FP8_FROM_FP16)
+        return fail(EP_ERR_ARG, "cfg.dispatch_cast = %d: must be an EP_CAST_* value",
+                    c->dispatch_cast);
+    if (c->dispatch_cast != EP_CAST_NONE && c->dispatch_dtype != EP_FP8_E4M3)
+        return fail(EP_ERR_ARG, "cfg.dispatch_cast = %d needs dispatch_dtype = EP_FP8_E4M3",
+                    c->dispatch_cast);
     const int64_t W = c->world_size, M = c->max_num_inp_token_per_rank;
     const int64_t row = (int64_t)c->hidden_dim * elem_bytes(c->dispatch_dtype);
     const int64_t crow = (int64_t)c->hidden_dim * 2;
@@ -151,6 +159,8 @@ int check_config(const ep_config_t* c, Shape* s)
     s->E = W * c->num_experts_per_rank;
     s->WM = W * M;
     s->row_bytes = row;
+    s->x_bytes = c->dispatch_cast != EP_CAST_NONE ? crow : row;
+    s->row_vecs = (int)(s->x_bytes / 16);
     s->crow_bytes = crow;
     s->scale_bytes = sbytes;
     const int64_t tiles_per_rank = (M + ep::kMinTile - 1) / ep::kMinTile;
@@ -258,9 +268,11 @@ int32_t* ws_fwd(ep_plan* p) { return reinterpret_cast<int32_t*>(p->ws + p->s.off
 
 // Whether the copy blocks can count every tile of a call themselves: a lane
 // per token reads whole id rows (k <= 16), and the counters fit in LDS.
-bool layout_in_copy_fits(const Shape& s, int ntiles)
+bool layout_in_copy_fits(const ep_plan* p, int ntiles)
 {
-    return s.k <= 16 && (int64_t)ntiles * s.W <= ep::kLayoutInCopyCells;
+    const Shape& s = p->s;
+    return s.k <= 16 && (int64_t)ntiles * s.W <= ep::kLayoutInCopyCells &&
+           p->cfg.dispatch_cast == EP_CAST_NONE;
 }
 
 // Most rows any rank can receive from a dispatch of these token counts: a
@@ -306,7 +318,7 @@ ep_launch_t auto_launch(const ep_plan* p, const int32_t* ntok)
         }
     }
     const int tiles = std::max(1, tiles_for(ntok, s.W, l.tile_tokens));
-    const int64_t row_vecs = s.row_bytes / 16;
+    const int64_t row_vecs = s.row_vecs;
     const int64_t max_split = std::max<int64_t>(1, row_vecs / ep::kWave);
     l.dispatch_row_split = (int)std::min<int64_t>(
         std::min<int64_t>(max_split, 65535), std::max(1, (kTargetBlocks + tiles - 1) / tiles));
@@ -325,7 +337,7 @@ ep_launch_t auto_launch(const ep_plan* p, const int32_t* ntok)
     l.cache_policy = rows_bytes <= kKeepBytes ? EP_CACHE_KEEP : EP_CACHE_STREAM;
     // few tiles: the copy blocks work out the receive slots themselves
     const int ntiles = tiles_for(ntok, s.W, l.tile_tokens);
-    if (ntiles >= 1 && N <= kLayoutInCopyTokens && layout_in_copy_fits(s, ntiles))
+    if (ntiles >= 1 && N <= kLayoutInCopyTokens && layout_in_copy_fits(p, ntiles))
         l.layout = EP_LAYOUT_IN_COPY;
     else if (ntiles >= 1 && ntiles <= kScanInCopyTiles)
         l.layout = EP_LAYOUT_SCAN_IN_COPY;
@@ -336,8 +348,10 @@ ep_launch_t auto_launch(const ep_plan* p, const int32_t* ntok)
     const int64_t rows = expert_rows(s, ntok);
     const int64_t eblocks = (int64_t)s.W * expert_tiles(rows);
     l.expert_waves = 8;
+    const int64_t ex_max_split = std::max<int64_t>(1, s.row_bytes / 16 / ep::kWave);
     l.expert_row_split = (int)std::min<int64_t>(
-        std::min<int64_t>(max_split, 65535), std::max<int64_t>(1, (kTargetBlocks + eblocks - 1) / eblocks));
+        std::min<int64_t>(ex_max_split, 65535),
+        std::max<int64_t>(1, (kTargetBlocks + eblocks - 1) / eblocks));
     l.expert_combine_waves = 4;
     const int64_t iblocks = std::max<int64_t>(1, s.W * ((rows + 3) / 4));
     l.expert_combine_row_split = (int)std::min<int64_t>(
@@ -443,6 +457,9 @@ int check_launch(const ep_plan* p, const ep_launch_t* l)
     if (l->layout == EP_LAYOUT_IN_COPY && s.k > 16)
         return fail(EP_ERR_ARG, "launch.layout = EP_LAYOUT_IN_COPY needs num_experts_per_token "
                     "<= 16 (it is %d)", s.k);
+    if (l->layout == EP_LAYOUT_IN_COPY && p->cfg.dispatch_cast != EP_CAST_NONE)
+        return fail(EP_ERR_ARG, "launch.layout = EP_LAYOUT_IN_COPY is not available with a "
+                    "dispatch_cast");
     if (l->cache_policy < 0 || l->cache_policy > EP_CACHE_KEEP)
         return fail(EP_ERR_ARG, "launch.cache_policy = %d: must be EP_CACHE_AUTO, "
                     "EP_CACHE_STREAM or EP_CACHE_KEEP", l->cache_policy);
@@ -451,9 +468,9 @@ int check_launch(const ep_plan* p, const ep_launch_t* l)
                     "EP_CACHE_STREAM or EP_CACHE_KEEP", l->expert_cache_policy);
     if (l->dispatch_row_split > 65535 || l->combine_row_split > 65535)
         return fail(EP_ERR_ARG, "launch row splits must be <= 65535 (grid y limit)");
-    if (l->dispatch_row_split > s.row_bytes / 16)
-        return fail(EP_ERR_ARG, "launch.dispatch_row_split = %d: must be <= %lld",
-                    l->dispatch_row_split, (long long)(s.row_bytes / 16));
+    if (l->dispatch_row_split > s.row_vecs)
+        return fail(EP_ERR_ARG, "launch.dispatch_row_split = %d: must be <= %d",
+                    l->dispatch_row_split, s.row_vecs);
     if (l->combine_row_split > s.crow_bytes / 16)
         return fail(EP_ERR_ARG, "launch.combine_row_split = %d: must be <= %lld",
                     l->combine_row_split, (long long)(s.crow_bytes / 16));
@@ -586,7 +603,7 @@ int ep_dispatch(ep_plan_t* p, const ep_dispatch_args_t* a, void* stream_ptr)
     }
     tm.tile_start[s.W] = tiles;
     tm.total_tiles = tiles;
-    if (l.layout == EP_LAYOUT_IN_COPY && tiles > 0 && !layout_in_copy_fits(s, tiles))
+    if (l.layout == EP_LAYOUT_IN_COPY && tiles > 0 && !layout_in_copy_fits(p, tiles))
         return fail(EP_ERR_ARG, "launch.layout = EP_LAYOUT_IN_COPY: %d tiles x %d ranks exceed "
                     "the %d counters of one block", tiles, s.W, ep::kLayoutInCopyCells);
 
@@ -626,8 +643,9 @@ int ep_dispatch(ep_plan_t* p, const ep_dispatch_args_t* a, void* stream_ptr)
                                                        : ep::kLayoutFromScan;
     ca.src_pos = ws_src_pos(p);
     ca.fwd = ws_fwd(p);
-    ca.row_vecs = (int32_t)(s.row_bytes / 16);
+    ca.row_vecs = s.row_vecs;
     ca.piece_vecs = (ca.row_vecs + l.dispatch_row_split - 1) / l.dispatch_row_split;
+    ca.cast = p->cfg.dispatch_cast;
     ca.scale_dwords = (int32_t)(s.scale_bytes / 4);
     ca.M = s.M;
     ca.k = s.k;

@@ -24,31 +24,6 @@ namespace {
 
 using namespace dev;
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr float kE4M3Max = 448.0f;
-
-// OCP E4M3 code of a finite-or-not FP32 value: round to nearest even,
-// saturate past 448, NaN -> 0x7F.
-__device__ __forceinline__ uint32_t to_e4m3(float v)
-{
-    if (__builtin_isnan(v))
-        return 0x7Fu;
-    const uint32_t sign = (__builtin_bit_cast(uint32_t, v) >> 24) & 0x80u;
-    const float a = __builtin_fabsf(v);
-    uint32_t c;
-    if (a >= kE4M3Max) {
-        c = 0x7Eu;
-    } else if (a < 0x1p-6f) {  // subnormal codes: multiples of 2^-9
-        c = (uint32_t)__builtin_rintf(a * 0x1p9f);
-    } else {
-        const int e = __builtin_amdgcn_frexp_expf(a) - 1;  // floor(log2 a), -6..8
-        const uint32_t m = (uint32_t)__builtin_rintf(__builtin_ldexpf(a, 3 - e));  // 8..16
-        c = ((uint32_t)(e + 7) << 3) + m - 8;  // m = 16 carries into the next binade
-    }
-    return sign | c;
-}
-
 __device__ __forceinline__ float from_e4m3(uint32_t c)
 {
     const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;

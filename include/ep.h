@@ -90,6 +90,14 @@ enum { EP_BF16 = 0, EP_FP16 = 1, EP_FP8_E4M3 = 2 };
  * ep_quantize_rows writes either from bf16 / fp16 rows. */
 enum { EP_WIRE_NONE = 0, EP_WIRE_FP8_BLOCK128 = 1, EP_WIRE_MXFP4 = 2 };
 
+/* Dispatch cast (R: fp8_direct_cast, named by [GUIDE] section 10 and [PR726]):
+ *   EP_CAST_NONE           x has dispatch_dtype and its rows are copied.
+ *   EP_CAST_FP8_FROM_BF16  x is bf16; dispatch_dtype must be EP_FP8_E4M3;
+ *   EP_CAST_FP8_FROM_FP16  x is fp16; every element is received as its OCP
+ *                          E4M3 code (round to nearest even, saturating at
+ *                          +-448, NaN -> 0x7F), on the fly, with no scale. */
+enum { EP_CAST_NONE = 0, EP_CAST_FP8_FROM_BF16 = 1, EP_CAST_FP8_FROM_FP16 = 2 };
+
 enum {
     EP_OK = 0,
     EP_ERR_NULL = -1,  /* a required pointer is NULL                          */
@@ -114,7 +122,8 @@ enum {
  *   dispatch_dtype in {EP_BF16, EP_FP16, EP_FP8_E4M3};
  *   combine_dtype in {EP_BF16, EP_FP16};
  *   combine_wire in EP_WIRE_*: with EP_WIRE_FP8_BLOCK128 hidden_dim % 128 ==
- *   0, with EP_WIRE_MXFP4 hidden_dim % 32 == 0. */
+ *   0, with EP_WIRE_MXFP4 hidden_dim % 32 == 0;
+ *   dispatch_cast in EP_CAST_*: with a cast, dispatch_dtype == EP_FP8_E4M3. */
 typedef struct ep_config {
     int32_t world_size;
     int32_t hidden_dim;
@@ -126,6 +135,7 @@ typedef struct ep_config {
     int32_t dispatch_dtype;
     int32_t combine_dtype;
     int32_t combine_wire;
+    int32_t dispatch_cast;
 } ep_config_t;
 
 typedef struct ep_plan ep_plan_t;
@@ -156,7 +166,8 @@ int ep_plan_destroy(ep_plan_t *plan);
 /* Dispatch arguments. Device pointers are caller-owned, 16-byte aligned, and
  * laid out rank-major with the rank stride fixed by M (not by T_r):
  *   num_tokens     HOST int32 [W]: T_r, 0 <= T_r <= M.
- *   x              [W][M][H] dispatch_dtype: rows t < T_r are read.
+ *   x              [W][M][H] dispatch_dtype (bf16 / fp16 with a dispatch_cast):
+ *                  rows t < T_r are read.
  *   indices        [W][M][k] int32 expert ids.
  *   weights        [W][M][k] float, or NULL (then out_weights must be NULL).
  *   scales         [W][M][S] elements of scale_type_size bytes; NULL iff S == 0.
@@ -271,8 +282,8 @@ const char *ep_last_error(void);
  *                        (at most 256 tiles);
  *                        EP_LAYOUT_IN_COPY: no extra kernel; each copy block
  *                        counts every tile of the call itself (k <= 16 and
- *                        tiles x world_size <= 4096; otherwise ep_dispatch
- *                        fails with EP_ERR_ARG).
+ *                        tiles x world_size <= 4096, no dispatch_cast;
+ *                        otherwise ep_dispatch fails with EP_ERR_ARG).
  *                        Automatic: EP_LAYOUT_IN_COPY up to 256 tokens when
  *                        it fits, else EP_LAYOUT_SCAN_IN_COPY up to 256 tiles,
  *                        else EP_LAYOUT_KERNELS.

@@ -87,6 +87,8 @@ BAD_CONFIGS = [
     (dict(combine_wire=3), "combine_wire"), (dict(combine_wire=-1), "combine_wire"),
     (dict(combine_wire=1, hidden_dim=7168 + 64), "EP_WIRE_FP8_BLOCK128"),
     (dict(combine_wire=2, hidden_dim=7168 + 16), "EP_WIRE_MXFP4"),
+    (dict(dispatch_cast=3), "dispatch_cast"), (dict(dispatch_cast=-1), "dispatch_cast"),
+    (dict(dispatch_cast=1), "EP_FP8_E4M3"),
 ]
 
 
@@ -486,3 +488,19 @@ def test_quantize_rows_rejects_before_launch(lib, args, code, word):
 
 def test_quantize_zero_rows_is_a_no_op(lib):
     assert lib.ep_quantize_rows(FAKE, 0, 256, 0, 1, FAKE, FAKE + 0x1000, None) == cra.EP_OK
+
+
+def test_dispatch_cast_layout_and_sizes(lib):
+    cfg = cra.make_config(8, 7168, 128, 32, 8, "fp8", "bf16", dispatch_cast="bf16")
+    rc, plan = make_plan(lib, cfg)
+    assert rc == 0
+    # a cast never runs in the all-in-copy layout
+    small = cra.ep_plan_get_launch(plan, [1] + [0] * 7)
+    assert small["layout"] != cra.EP_LAYOUT_IN_COPY
+    with pytest.raises(cra.EpError):
+        cra.ep_plan_set_launch(plan, dict(layout=cra.EP_LAYOUT_IN_COPY))
+    # row pieces are counted in 16-byte vectors of the bf16 input row
+    cra.ep_plan_set_launch(plan, dict(dispatch_row_split=7168 * 2 // 16))
+    with pytest.raises(cra.EpError):
+        cra.ep_plan_set_launch(plan, dict(dispatch_row_split=7168 * 2 // 16 + 1))
+    lib.ep_plan_destroy(plan)
