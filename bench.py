@@ -211,6 +211,107 @@ def measure_expert_major(args, cra, torch, np, wl, op, inp, stream):
     }
 
 
+def _timed(torch, stream, fn, steps, warmup):
+    """Average ms of fn() over `steps` calls between two HIP events."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for _ in range(steps):
+        fn()
+    e.record(stream)
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
+def _kernel_ms(cra, torch, plan, kid, fn, steps):
+    cra.ep_plan_set_timing(plan, True)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    c, ms = cra.ep_plan_kernel_time(plan, kid)
+    cra.ep_plan_set_timing(plan, False)
+    return ms / max(c, 1)
+
+
+def _roof(nbytes, ms, kernel):
+    a = nbytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "kernel": kernel, "achieved": round(a, 2), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(a / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes_per_launch": int(nbytes)}
+
+
+def measure_quantized_wires(args, cra, torch, np, wl, inp, stream):
+    """The quantized wires on the same workload: the dispatch with the
+    on-the-fly FP8 cast (bf16 tokens received as E4M3), the send-side
+    quantizer, and the combine from FP8 block-128 and MXFP4 rows."""
+    W, M, k, Er, H = wl.world_size, wl.max_tokens, wl.topk, wl.experts_per_rank, wl.hidden
+    ntok = inp["ntok"]
+    N, P = int(sum(ntok)), min(W, k)
+    dev = torch.device("cuda:0")
+    x = inp["x"].to(dev)
+    idx = inp["idx"].to(dev)
+    w = inp["w"].to(dev)
+    out = {}
+    if wl.dispatch_dtype in ("bf16", "fp16"):
+        cfg = cra.make_config(W, H, M, Er, k, "fp8", wl.combine_dtype, dispatch_cast=wl.dispatch_dtype)
+        op = cra.EpDispatchCombineOp(cfg, device=dev)
+        step = lambda: op.dispatch(ntok, x, idx, w, stream=stream)
+        ms = _timed(torch, stream, step, args.steps, args.warmup)
+        kms = _kernel_ms(cra, torch, op.plan, cra.EP_KERNEL_COPY, step, args.steps)
+        R = int(op.recv_num_token.sum().item())
+        nb = N * (2 * H + 8 * k) + R * (H + 8 * k + 4) + N * P * 4
+        out["dispatch_fp8_direct_cast"] = {
+            "us_per_call": round(ms * 1e3, 2), "copy_kernel_us": round(kms * 1e3, 2),
+            "received_bytes_saved": R * H,
+            "roofline": _roof(nb, kms, "ep_copy_kernel (cast)")}
+        op.close()
+        del op
+        torch.cuda.empty_cache()
+    for name, wire, row, srow in (("fp8_block128", cra.EP_WIRE_FP8_BLOCK128, H, H // 128 * 4),
+                                  ("mxfp4", cra.EP_WIRE_MXFP4, H // 2, H // 32)):
+        cfg = cra.make_config(W, H, M, Er, k, wl.dispatch_dtype, wl.combine_dtype,
+                              scale_dim=wl.scale_dim, scale_type_size=4, combine_wire=wire)
+        op = cra.EpDispatchCombineOp(cfg, device=dev)
+        sc = None if inp["scales"] is None else inp["scales"].to(dev)
+        op.dispatch(ntok, x, idx, w, sc, stream=stream)
+        R = int(op.recv_num_token.sum().item())
+        # expert outputs: the received rows themselves (bf16), or seeded rows
+        cdt = workloads_dtype(torch, wl.combine_dtype)
+        if wl.dispatch_dtype == wl.combine_dtype:
+            y = op.out_x
+        else:
+            g = torch.Generator(device="cuda").manual_seed(11)
+            y = torch.randn((W, W * M, H), generator=g, device=dev).to(cdt)
+        yq = torch.empty((W, W * M, row), dtype=torch.uint8, device=dev)
+        ys = torch.empty((W, W * M, srow), dtype=torch.uint8, device=dev)
+        qstep = lambda: cra.ep_quantize_rows(y, wire, yq, ys, stream=stream)
+        qms = _timed(torch, stream, qstep, args.steps, args.warmup)
+        cstep = lambda: op.combine(yq, op.out_weights, stream=stream, y_scales=ys)
+        cms = _timed(torch, stream, cstep, args.steps, args.warmup)
+        kms = _kernel_ms(cra, torch, op.plan, cra.EP_KERNEL_COMBINE, cstep, args.steps)
+        rows = W * W * M
+        qb = rows * (2 * H + row + srow)
+        cb = R * (row + srow + 4 * k) + N * (2 * H + 4 * k) + N * P * 4
+        out["combine_" + name] = {
+            "wire_bytes_per_row": row + srow, "bf16_bytes_per_row": 2 * H,
+            "combine_us_per_call": round(cms * 1e3, 2), "combine_kernel_us": round(kms * 1e3, 2),
+            "quantize_us_per_call": round(qms * 1e3, 2),
+            "quantize_rows": rows,
+            "roofline_combine": _roof(cb, kms, "ep_combine_wire_kernel"),
+            "roofline_quantize": _roof(qb, qms, "ep_quantize_kernel")}
+        op.close()
+        del op, yq, ys
+        torch.cuda.empty_cache()
+    return out
+
+
+def workloads_dtype(torch, name):
+    return {"bf16": torch.bfloat16, "fp16": torch.float16}[name]
+
+
 def copy_ceiling(torch, mib, steps, warmup):
     """Plain copy of mib MiB between two device buffers: reads and writes
     mib MiB each per launch."""
@@ -489,6 +590,10 @@ def run(args):
     }
     if not args.no_expert:
         line["expert_major"] = measure_expert_major(args, cra, torch, np, wl, op, inp, stream)
+    if not args.no_wires:
+        op.close()
+        torch.cuda.empty_cache()
+        line["quantized_wires"] = measure_quantized_wires(args, cra, torch, np, wl, inp, stream)
     op.close()
     print(json.dumps(line), flush=True)
 
@@ -503,6 +608,8 @@ def main():
                     help="skip the oracle (CPU baseline and the bit-exact check); for profiling")
     ap.add_argument("--no-expert", action="store_true",
                     help="skip the expert-major layout measurement")
+    ap.add_argument("--no-wires", action="store_true",
+                    help="skip the quantized-wire measurements")
     ap.add_argument("--graph", action="store_true",
                     help="time K replays of one step captured in a HIP graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")

@@ -385,6 +385,12 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
     // one chunk of a token's row piece to every destination row of the token
     auto store_payload = [&](int tok, int v0, const u32x4 (&v)[VPL]) {
         const int n = uniform(s_n[tok]);
+        u32x2 c[kCast ? VPL : 1];  // the chunk's E4M3 codes, converted once
+        if constexpr (kCast) {
+#pragma unroll
+            for (int u = 0; u < VPL; ++u)
+                c[u] = cast_e4m3(v[u], a.cast);
+        }
         for (int i = 0; i < n; ++i) {
             const int d = uniform(s_list[tok][i]);
             const int s = uniform(s_base[d] + s_loc[tok][d]);
@@ -395,9 +401,8 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
                 const int vv = v0 + u * kWave + lane;
                 if (vv < vend) {
                     if constexpr (kCast)
-                        __builtin_amdgcn_raw_buffer_store_b64(
-                            cast_e4m3(v[u], a.cast), rd, (int)((uint32_t)vv * 8u), 0,
-                            Policy<kStream>::copy_store);
+                        __builtin_amdgcn_raw_buffer_store_b64(c[u], rd, (int)((uint32_t)vv * 8u),
+                                                              0, Policy<kStream>::copy_store);
                     else
                         bstore16<Policy<kStream>::copy_store>(v[u], rd, (uint32_t)vv * 16u);
                 }
@@ -604,17 +609,21 @@ template <int VPL, int KB>
 hipError_t copy_with(const CopyArgs& a, const TileMap& tm, dim3 grid, dim3 block, bool stream,
                      hipStream_t s)
 {
-    if (a.cast) {
-        if (a.layout == kLayoutInCopy)
-            return hipErrorInvalidValue;  // the host never selects it with a cast
-        if (stream)
-            hipLaunchKernelGGL((ep_copy_kernel<VPL, KB, true, false, true>), grid, block, 0, s,
-                               a, tm);
-        else
-            hipLaunchKernelGGL((ep_copy_kernel<VPL, KB, false, false, true>), grid, block, 0, s,
-                               a, tm);
-        return hipGetLastError();
+    if constexpr (VPL <= 4) {
+        if (a.cast) {
+            if (a.layout == kLayoutInCopy)
+                return hipErrorInvalidValue;  // the host never selects it with a cast
+            if (stream)
+                hipLaunchKernelGGL((ep_copy_kernel<VPL, KB, true, false, true>), grid, block, 0,
+                                   s, a, tm);
+            else
+                hipLaunchKernelGGL((ep_copy_kernel<VPL, KB, false, false, true>), grid, block, 0,
+                                   s, a, tm);
+            return hipGetLastError();
+        }
     }
+    if (a.cast)
+        return hipErrorInvalidValue;  // casts run with at most 4 vectors a lane
     if constexpr (KB <= 16) {
         if (a.layout == kLayoutInCopy) {
             const size_t lds = sizeof(int32_t) * tm.total_tiles * tm.W;
@@ -707,7 +716,9 @@ hipError_t launch_copy(const CopyArgs& a, const TileMap& tm, int waves, int row_
         return copy_with_vpl<1>(a, tm, grid, block, stream, s);
     if (per_lane <= 2)
         return copy_with_vpl<2>(a, tm, grid, block, stream, s);
-    if (per_lane <= 4)
+    // a cast keeps at most 4 vectors a lane in flight: its conversion needs
+    // the registers
+    if (per_lane <= 4 || a.cast)
         return copy_with_vpl<4>(a, tm, grid, block, stream, s);
     return copy_with_vpl<8>(a, tm, grid, block, stream, s);
 }

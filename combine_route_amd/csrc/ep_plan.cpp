@@ -748,8 +748,8 @@ int ep_combine(ep_plan_t* p, const ep_combine_args_t* a, void* stream_ptr)
         wa.out = static_cast<uint8_t*>(a->out);
         wa.out_w = a->out_weights;
         wa.fwd = ws_fwd(p);
-        wa.cols = s.H / 8;
-        wa.piece_cols = (wa.cols + l.combine_row_split - 1) / l.combine_row_split;
+        wa.units = wire == EP_WIRE_FP8_BLOCK128 ? s.H / 16 : s.H / 32;
+        wa.piece_units = (wa.units + l.combine_row_split - 1) / l.combine_row_split;
         if (wire == EP_WIRE_FP8_BLOCK128) {
             wa.row_bytes = (uint32_t)s.H;
             wa.scale_bytes = (uint32_t)(s.H / 128 * 4);
@@ -760,7 +760,7 @@ int ep_combine(ep_plan_t* p, const ep_combine_args_t* a, void* stream_ptr)
         wa.M = s.M;
         wa.k = s.k;
         wa.P = s.P;
-        const int row_split = (wa.cols + wa.piece_cols - 1) / wa.piece_cols;
+        const int row_split = (wa.units + wa.piece_units - 1) / wa.piece_units;
         const int kwire = wire == EP_WIRE_FP8_BLOCK128 ? ep::kWireFp8Block128 : ep::kWireMxfp4;
         e = timed(p, EP_KERNEL_COMBINE, stream, [&] {
             return ep::launch_combine_wire(wa, tk, kwire, dtype, l.combine_waves, row_split,

@@ -9,10 +9,12 @@
 //             (MXFP4) lanes with cross-lane xors, then every element is
 //             rounded to the format in registers.
 //   combine   the combine's gather-fold, with each contribution taken off the
-//             wire (code times scale, in FP32) before it is added.
-// All conversions are integer and power-of-two arithmetic plus rint (round
-// to nearest even), so they are exact functions of their inputs; the two
-// block-scale divisions are correctly rounded.
+//             wire (code times scale, in FP32) before it is added; a lane
+//             reads 16 bytes of codes a row and decodes them with the
+//             hardware conversions.
+// Encoding is integer and power-of-two arithmetic plus rint (round to
+// nearest even), and decoding is exact, so every result is an exact function
+// of its inputs; the two block-scale divisions are correctly rounded.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -23,15 +25,6 @@ namespace ep {
 namespace {
 
 using namespace dev;
-
-__device__ __forceinline__ float from_e4m3(uint32_t c)
-{
-    const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
-    float v = e == 0 ? (float)m * 0x1p-9f : __builtin_ldexpf((float)(8u + m), (int)e - 10);
-    if (e == 15 && m == 7)
-        v = __builtin_nanf("");
-    return (c & 0x80u) ? -v : v;
-}
 
 // OCP E2M1 code (4 bits) of a finite value: nearest of 0, 0.5, 1, 1.5, 2, 3,
 // 4, 6, ties to the even code, saturating at 6.
@@ -49,13 +42,6 @@ __device__ __forceinline__ uint32_t to_e2m1(float v)
     else
         c = (uint32_t)__builtin_rintf(a * 0.5f) + 4;     // 4, 6
     return sign | c;
-}
-
-__device__ __forceinline__ float from_e2m1(uint32_t c)
-{
-    const uint32_t e = (c >> 1) & 3u, m = c & 1u;
-    const float v = e == 0 ? 0.5f * (float)m : __builtin_ldexpf(1.0f + 0.5f * (float)m, (int)e - 1);
-    return (c & 8u) ? -v : v;
 }
 
 // Maximum over groups of G consecutive lanes (G a power of two <= 16).
@@ -120,25 +106,48 @@ __global__ __launch_bounds__(256) void ep_quantize_kernel(QuantizeArgs a)
     }
 }
 
-// The 8 elements of one 16-byte output column of a wire row, in FP32.
-template <int WIRE, bool kStream>
-__device__ __forceinline__ void wire_column(__amdgpu_buffer_rsrc_t ry, __amdgpu_buffer_rsrc_t rs,
-                                            int col, float (&f)[8])
+// A lane's unit of a wire row: 16 bytes of codes, 16 FP8 elements (inside one
+// 128-element scale block) or 32 MXFP4 elements (exactly one scale block).
+template <int WIRE>
+constexpr int unit_elems() { return WIRE == kWireFp8Block128 ? 16 : 32; }
+
+// Decode one unit into FP32 with the hardware conversions, which are exact:
+// an E4M3 code to FP32 (v_cvt_pk_f32_fp8), then one FP32 multiply by the
+// block scale; an E2M1 code times the power-of-two scale (v_cvt_scalef32_pk_
+// f32_fp4). Code order follows the row: byte i of dword d holds FP8 element
+// 4d + i; the low nibble of byte b holds MXFP4 element 2b.
+template <int WIRE>
+__device__ __forceinline__ void decode_unit(const u32x4& c, uint32_t sbits,
+                                            float (&f)[unit_elems<WIRE>()])
 {
-    constexpr int aux = Policy<kStream>::combine_load;
     if constexpr (WIRE == kWireFp8Block128) {
-        const u32x2 c = __builtin_amdgcn_raw_buffer_load_b64(ry, col * 8, 0, aux);
-        const float s = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(rs, (col / 16) * 4, 0, aux));
+        const float s = __builtin_bit_cast(float, sbits);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            f[i] = from_e4m3((c[i / 4] >> (8 * (i % 4))) & 0xFFu) * s;
+        for (int d = 0; d < 4; ++d) {
+            const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(c[d], false);
+            const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(c[d], true);
+            f[4 * d + 0] = lo.x * s;
+            f[4 * d + 1] = lo.y * s;
+            f[4 * d + 2] = hi.x * s;
+            f[4 * d + 3] = hi.y * s;
+        }
     } else {
-        const uint32_t c = __builtin_amdgcn_raw_buffer_load_b32(ry, col * 4, 0, aux);
-        const int E = (int)__builtin_amdgcn_raw_buffer_load_b8(rs, col / 4, 0, aux) - 127;
+        const float s = __builtin_ldexpf(1.0f, (int)(sbits & 0xFFu) - 127);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            f[i] = __builtin_ldexpf(from_e2m1((c >> (4 * i)) & 0xFu), E);
+        for (int d = 0; d < 4; ++d) {
+            const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[d], s, 0);
+            const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[d], s, 1);
+            const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[d], s, 2);
+            const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[d], s, 3);
+            f[8 * d + 0] = v0.x;
+            f[8 * d + 1] = v0.y;
+            f[8 * d + 2] = v1.x;
+            f[8 * d + 3] = v1.y;
+            f[8 * d + 4] = v2.x;
+            f[8 * d + 5] = v2.y;
+            f[8 * d + 6] = v3.x;
+            f[8 * d + 7] = v3.y;
+        }
     }
 }
 
@@ -155,13 +164,15 @@ __device__ __forceinline__ int rank_of_token(const TokenMap& tk, int flat)
     return lo;
 }
 
-// A wave per (token, row piece), as the combine: the token's contribution
-// rows come off the wire column by column (G rows loaded before any is
-// added), are summed in the token's rank order in FP32 from the first, and
-// rounded to nearest even once.
+// A wave per (token, row piece), as the combine: for each lane's unit the
+// token's contribution rows are all loaded (G at a time) before any is
+// decoded and added, summed in the token's rank order in FP32 from the
+// first, and rounded to nearest even once.
 template <int G, int WIRE, int DT, bool kStream>
 __global__ __launch_bounds__(1024) void ep_combine_wire_kernel(WireCombineArgs a, TokenMap tk)
 {
+    constexpr int UE = unit_elems<WIRE>();
+    constexpr int aux = Policy<kStream>::combine_load;
     const int lane = threadIdx.x & (kWave - 1);
     const int flat = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
     if (flat >= tk.total)
@@ -172,40 +183,56 @@ __global__ __launch_bounds__(1024) void ep_combine_wire_kernel(WireCombineArgs a
     const int32_t gl = lane < a.P ? a.fwd[tok * a.P + lane] : -1;
     const int n = __popcll(__ballot(gl >= 0));  // entries >= 0 form a prefix
 
-    const uint32_t out_bytes = (uint32_t)a.cols * 16u;
+    const uint32_t out_bytes = (uint32_t)a.units * (UE * 2);
     const __amdgpu_buffer_rsrc_t rdst = row_rsrc(a.out + tok * out_bytes, out_bytes);
-    const int cbeg = piece * a.piece_cols;
-    const int cend = min(a.cols, cbeg + a.piece_cols);
-    for (int col = cbeg + lane; col - lane < cend; col += kWave) {
-        const bool live = col < cend;
-        float acc[8];
+    const int ubeg = piece * a.piece_units;
+    const int uend = min(a.units, ubeg + a.piece_units);
+    for (int u = ubeg + lane; u - lane < uend; u += kWave) {
+        const bool live = u < uend;
+        float acc[UE];
         for (int i0 = 0; i0 < n; i0 += G) {
-            float v[G][8];
+            u32x4 raw[G];
+            uint32_t sc[G];
 #pragma unroll
             for (int q = 0; q < G; ++q) {
                 if (i0 + q < n && live) {
                     const int64_t gq = __builtin_amdgcn_readlane(gl, i0 + q);
-                    wire_column<WIRE, kStream>(
-                        row_rsrc(a.y + gq * a.row_bytes, a.row_bytes),
-                        row_rsrc(a.ys + gq * a.scale_bytes, a.scale_bytes), col, v[q]);
+                    const __amdgpu_buffer_rsrc_t ry = row_rsrc(a.y + gq * a.row_bytes, a.row_bytes);
+                    const __amdgpu_buffer_rsrc_t rs =
+                        row_rsrc(a.ys + gq * a.scale_bytes, a.scale_bytes);
+                    raw[q] = bload16<aux>(ry, (uint32_t)u * 16u);
+                    if constexpr (WIRE == kWireFp8Block128)
+                        sc[q] = __builtin_amdgcn_raw_buffer_load_b32(rs, (u / 8) * 4, 0, aux);
+                    else
+                        sc[q] = __builtin_amdgcn_raw_buffer_load_b8(rs, u, 0, aux);
                 }
             }
 #pragma unroll
             for (int q = 0; q < G; ++q) {
                 if (i0 + q < n) {
+                    float f[UE];
+                    decode_unit<WIRE>(raw[q], sc[q], f);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        acc[e] = (i0 + q == 0) ? v[q][e] : acc[e] + v[q][e];
+                    for (int e = 0; e < UE; ++e)
+                        acc[e] = (i0 + q == 0) ? f[e] : acc[e] + f[e];
                 }
             }
         }
         if (live) {
             if (n == 0) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
+                for (int e = 0; e < UE; ++e)
                     acc[e] = 0.0f;
             }
-            bstore16<Policy<kStream>::combine_store>(narrow<DT>(acc), rdst, (uint32_t)col * 16u);
+#pragma unroll
+            for (int o = 0; o < UE / 8; ++o) {
+                float f8[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    f8[e] = acc[8 * o + e];
+                bstore16<Policy<kStream>::combine_store>(narrow<DT>(f8), rdst,
+                                                         (uint32_t)(u * (UE / 8) + o) * 16u);
+            }
         }
     }
 

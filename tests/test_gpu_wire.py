@@ -187,3 +187,39 @@ def test_wire_geometry_does_not_change_results(launch):
                           seed_index=820)
     for name in WIRES:
         run_wire_case(wl, name, launch=launch, tag=f"geom {name} {launch}")
+
+
+@pytest.mark.parametrize("name", list(WIRES))
+def test_wire_decode_of_every_code(name):
+    """One token with one contribution whose codes are all 256 byte values
+    (FP8: scale 1 and another power of two; MXFP4: several scale codes):
+    the combine's output is each decoded value, exact in bf16; the FP8 NaN
+    codes must come out NaN."""
+    cw, ow = WIRES[name]
+    H = 512
+    wl = workloads.custom(f"wire_codes_{name}", 1, 1, H, 1, 4, "bf16", seed_index=830)
+    inp = workloads.make_inputs(wl)
+    inp["ntok"] = [1]
+    ref = oracle_dispatch(wl, inp)
+    cfg = cra.make_config(1, H, 1, 4, 1, "bf16", "bf16", combine_wire=cw)
+    op = cra.EpDispatchCombineOp(cfg, with_weights=False)
+    gpu_dispatch(op, dict(inp, w=None))
+    codes = np.tile(np.arange(256, dtype=np.uint8), 2)
+    if cw == cra.EP_WIRE_FP8_BLOCK128:
+        y = codes.reshape(1, 1, H)
+        ys = np.array([1.0, 1.0, 2.0 ** -3, 2.0 ** 5], np.float32).reshape(1, 1, 4)
+    else:
+        y = codes[:H // 2].reshape(1, 1, H // 2)
+        ys = np.array([127, 100, 150, 120, 127, 131, 90, 140, 127, 126, 128, 127, 127, 110, 145,
+                       127], np.uint8).reshape(1, 1, H // 32)
+    out, _ = op.combine(torch.from_numpy(y).cuda(), None, y_scales=torch.from_numpy(ys).cuda())
+    torch.cuda.synchronize()
+    ro = oracle.combine_wire(1, 1, 1, H, oracle.BF16, ow, [1], ref["fwd"], y, ys)
+    g = out.view(torch.int16).cpu().numpy().view(np.uint16)[0, 0]
+    r = ro[0, 0]
+    nan_g = (g & 0x7F80) == 0x7F80
+    nan_g &= (g & 0x7F) != 0
+    nan_r = ((r & 0x7F80) == 0x7F80) & ((r & 0x7F) != 0)
+    assert np.array_equal(nan_g, nan_r)
+    assert np.array_equal(g[~nan_g], r[~nan_r])
+    op.close()
