@@ -109,26 +109,25 @@ __device__ __forceinline__ u32x4 narrow(const float (&f)[8])
 
 constexpr float kE4M3Max = 448.0f;
 
-// OCP E4M3 code (the OFP8 specification: bias 7, no infinities, largest
-// finite 448) of an FP32 value: round to nearest even, saturate past 448,
-// NaN -> 0x7F. Integer and power-of-two arithmetic plus rint, so exact.
-__device__ __forceinline__ uint32_t to_e4m3(float v)
+// OCP E4M3 codes (the OFP8 specification: bias 7, no infinities, largest
+// finite 448) of 4 FP32 values, one a byte in order: round to nearest even,
+// saturating past 448, NaN -> 0x7F. v_cvt_pk_fp8_f32 rounds to nearest even
+// but turns overflow into NaN, so values are clamped to +-448 first (NaN kept
+// apart, since min/max would drop it); it writes NaN as 0xFF, which no finite
+// value can produce, and those bytes become 0x7F. Checked against the
+// definition on every bf16 and fp16 value.
+__device__ __forceinline__ uint32_t e4m3x4(float f0, float f1, float f2, float f3)
 {
-    if (__builtin_isnan(v))
-        return 0x7Fu;
-    const uint32_t sign = (__builtin_bit_cast(uint32_t, v) >> 24) & 0x80u;
-    const float a = __builtin_fabsf(v);
-    uint32_t c;
-    if (a >= kE4M3Max) {
-        c = 0x7Eu;
-    } else if (a < 0x1p-6f) {  // subnormal codes: multiples of 2^-9
-        c = (uint32_t)__builtin_rintf(a * 0x1p9f);
-    } else {
-        const int e = __builtin_amdgcn_frexp_expf(a) - 1;  // floor(log2 a), -6..8
-        const uint32_t m = (uint32_t)__builtin_rintf(__builtin_ldexpf(a, 3 - e));  // 8..16
-        c = ((uint32_t)(e + 7) << 3) + m - 8;  // m = 16 carries into the next binade
-    }
-    return sign | c;
+    auto clamp = [](float v) {
+        return v != v ? v : __builtin_fminf(__builtin_fmaxf(v, -kE4M3Max), kE4M3Max);
+    };
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp(f0), clamp(f1), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp(f2), clamp(f3), w, true);
+    const uint32_t x = (uint32_t)w;
+    // bytes equal to 0xFF: their complement is zero; clear bit 7 of each
+    const uint32_t t = ~x;
+    const uint32_t ff = ~(((t & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | t) & 0x80808080u;
+    return x ^ ff;
 }
 
 // One wave folds the n contribution rows whose row numbers (in units of

@@ -151,7 +151,7 @@ struct WireCombineArgs {
     uint8_t* out;                // [W][M][H] combine dtype
     float* out_w;                // [W][M][k] or null
     const int32_t* fwd;          // [W][M][P]
-    int32_t units;               // 16-byte code units per row (16 FP8 or 32 MXFP4 elements)
+    int32_t units;               // 16-element units per row (H / 16)
     int32_t piece_units;         // units per row piece
     uint32_t row_bytes, scale_bytes;
     int32_t M, k, P;

@@ -283,19 +283,16 @@ __device__ __forceinline__ u32x2 cast_e4m3(const u32x4& w, int cast)
         widen<1>(w, f);
     else
         widen<0>(w, f);
-    u32x2 out = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        out[i / 4] |= to_e4m3(f[i]) << (8 * (i % 4));
-    return out;
+    return {e4m3x4(f[0], f[1], f[2], f[3]), e4m3x4(f[4], f[5], f[6], f[7])};
 }
 
 // One work item of a wave: one chunk (up to 64 x VPL 16-byte vectors) of one
 // token's row piece, and, for the first chunk of a piece-0 block, the lane's
-// share of the token's id, weight and scale rows.
-template <int VPL>
+// share of the token's id, weight and scale rows. NV = the 16-byte vectors
+// as loaded: 2 * VPL for a cast (32 input bytes for each vector stored).
+template <int VPL, int NV = VPL>
 struct CopyItem {
-    u32x4 v[VPL];
+    u32x4 v[NV];
     int32_t e;
     float wv;
     uint32_t sc;
@@ -304,8 +301,10 @@ struct CopyItem {
 // kInCopy: the block counts every tile of the call itself (kLayoutInCopy, k <=
 // 16 only); a separate instantiation, so the other calls do not carry its
 // registers. kCast: the payload arrives as bf16 / fp16 (a.cast) and each
-// element is stored as its OCP E4M3 code (round to nearest even, saturating
-// at 448); a 16-byte vector of 8 input elements becomes 8 output bytes.
+// element is received as its OCP E4M3 code (round to nearest even,
+// saturating at 448): a vector is 8 elements, 16 bytes loaded (contiguous
+// across the wave, as in the plain copy), converted once, and 8 bytes stored
+// to each destination.
 template <int VPL, int KB, bool kStream, bool kInCopy, bool kCast = false>
 __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
 {
@@ -332,8 +331,9 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
     const int ntw = wave < cnt ? (cnt - wave + nwaves - 1) / nwaves : 0;
     const int items = ntw * nch;
     const bool meta = piece == 0;
-    const uint32_t row_bytes = (uint32_t)a.row_vecs * 16u;                  // input row
-    const uint32_t out_bytes = kCast ? (uint32_t)a.row_vecs * 8u : row_bytes;  // received row
+    const uint32_t in_bytes = (uint32_t)a.row_vecs * 16u;                  // input row
+    const uint32_t row_bytes = kCast ? (uint32_t)a.row_vecs * 8u : in_bytes;  // received row
+    constexpr int NV = VPL;
     const int k = a.k;
     const int per = kWave / k;  // destination id/weight rows per store instruction
     const int j = lane % k;
@@ -383,19 +383,19 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
             sc = a.sc[src * sd + lane];
     };
     // one chunk of a token's row piece to every destination row of the token
-    auto store_payload = [&](int tok, int v0, const u32x4 (&v)[VPL]) {
+    auto store_payload = [&](int tok, int v0, const u32x4 (&raw)[NV]) {
         const int n = uniform(s_n[tok]);
-        u32x2 c[kCast ? VPL : 1];  // the chunk's E4M3 codes, converted once
+        u32x2 c[kCast ? VPL : 1];  // a cast's codes, converted once per chunk
         if constexpr (kCast) {
 #pragma unroll
             for (int u = 0; u < VPL; ++u)
-                c[u] = cast_e4m3(v[u], a.cast);
+                c[u] = cast_e4m3(raw[u], a.cast);
         }
         for (int i = 0; i < n; ++i) {
             const int d = uniform(s_list[tok][i]);
             const int s = uniform(s_base[d] + s_loc[tok][d]);
             const __amdgpu_buffer_rsrc_t rd =
-                row_rsrc(a.out_x + ((int64_t)d * a.WM + s) * out_bytes, out_bytes);
+                row_rsrc(a.out_x + ((int64_t)d * a.WM + s) * row_bytes, row_bytes);
 #pragma unroll
             for (int u = 0; u < VPL; ++u) {
                 const int vv = v0 + u * kWave + lane;
@@ -404,13 +404,13 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
                         __builtin_amdgcn_raw_buffer_store_b64(c[u], rd, (int)((uint32_t)vv * 8u),
                                                               0, Policy<kStream>::copy_store);
                     else
-                        bstore16<Policy<kStream>::copy_store>(v[u], rd, (uint32_t)vv * 16u);
+                        bstore16<Policy<kStream>::copy_store>(raw[u], rd, (uint32_t)vv * 16u);
                 }
             }
         }
     };
-    auto load_payload = [&](int64_t src, int v0, u32x4 (&v)[VPL]) {
-        const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.x + src * row_bytes, row_bytes);
+    auto load_payload = [&](int64_t src, int v0, u32x4 (&v)[NV]) {
+        const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.x + src * in_bytes, in_bytes);
 #pragma unroll
         for (int u = 0; u < VPL; ++u) {
             const int vv = v0 + u * kWave + lane;
@@ -418,7 +418,7 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
                 v[u] = bload16<Policy<kStream>::copy_load>(rs, (uint32_t)vv * 16u);
         }
     };
-    auto load_item = [&](int it, CopyItem<VPL>& I) {
+    auto load_item = [&](int it, CopyItem<VPL, NV>& I) {
         const int q = it / nch;
         const int c = it - q * nch;
         const int64_t src = (int64_t)r * a.M + t0 + wave + q * nwaves;
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
         if (meta && c == 0)
             load_meta(src, I.e, I.wv, I.sc);
     };
-    auto store_item = [&](int it, const CopyItem<VPL>& I) {
+    auto store_item = [&](int it, const CopyItem<VPL, NV>& I) {
         const int q = it / nch;
         const int c = it - q * nch;
         const int tok = wave + q * nwaves;
@@ -524,7 +524,7 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
         // Small pieces (small calls, where time is latency): each wave's first
         // item loads while wave 0 routes the tile, then two items in flight,
         // item i+1 loading while item i stores.
-        CopyItem<VPL> A, B;
+        CopyItem<VPL, NV> A, B;
         if (items > 0)
             load_item(0, A);
         tile_bases();
@@ -559,7 +559,7 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
         for (int tok = wave; tok < cnt; tok += nwaves) {
             const int64_t src = (int64_t)r * a.M + t0 + tok;
             for (int v0 = vbeg; v0 < vend; v0 += kWave * VPL) {
-                u32x4 v[VPL];
+                u32x4 v[NV];
                 load_payload(src, v0, v);
                 store_payload(tok, v0, v);
             }
@@ -609,21 +609,17 @@ template <int VPL, int KB>
 hipError_t copy_with(const CopyArgs& a, const TileMap& tm, dim3 grid, dim3 block, bool stream,
                      hipStream_t s)
 {
-    if constexpr (VPL <= 4) {
-        if (a.cast) {
-            if (a.layout == kLayoutInCopy)
-                return hipErrorInvalidValue;  // the host never selects it with a cast
-            if (stream)
-                hipLaunchKernelGGL((ep_copy_kernel<VPL, KB, true, false, true>), grid, block, 0,
-                                   s, a, tm);
-            else
-                hipLaunchKernelGGL((ep_copy_kernel<VPL, KB, false, false, true>), grid, block, 0,
-                                   s, a, tm);
-            return hipGetLastError();
-        }
+    if (a.cast) {
+        if (a.layout == kLayoutInCopy)
+            return hipErrorInvalidValue;  // the host never selects it with a cast
+        if (stream)
+            hipLaunchKernelGGL((ep_copy_kernel<VPL, KB, true, false, true>), grid, block, 0, s,
+                               a, tm);
+        else
+            hipLaunchKernelGGL((ep_copy_kernel<VPL, KB, false, false, true>), grid, block, 0, s,
+                               a, tm);
+        return hipGetLastError();
     }
-    if (a.cast)
-        return hipErrorInvalidValue;  // casts run with at most 4 vectors a lane
     if constexpr (KB <= 16) {
         if (a.layout == kLayoutInCopy) {
             const size_t lds = sizeof(int32_t) * tm.total_tiles * tm.W;
@@ -716,9 +712,7 @@ hipError_t launch_copy(const CopyArgs& a, const TileMap& tm, int waves, int row_
         return copy_with_vpl<1>(a, tm, grid, block, stream, s);
     if (per_lane <= 2)
         return copy_with_vpl<2>(a, tm, grid, block, stream, s);
-    // a cast keeps at most 4 vectors a lane in flight: its conversion needs
-    // the registers
-    if (per_lane <= 4 || a.cast)
+    if (per_lane <= 4)
         return copy_with_vpl<4>(a, tm, grid, block, stream, s);
     return copy_with_vpl<8>(a, tm, grid, block, stream, s);
 }

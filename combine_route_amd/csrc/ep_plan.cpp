@@ -70,7 +70,7 @@ struct Shape {
     int64_t E, WM;
     int64_t row_bytes;    // dispatch payload row as received
     int64_t x_bytes;      // dispatch payload row as sent (2H with a cast)
-    int row_vecs;         // 16-byte vectors of an x row: the copy's work unit
+    int row_vecs;         // 16-byte vectors of an input row: the copy's work unit
     int64_t crow_bytes;   // combine row
     int64_t scale_bytes;  // scale row
     int tile_stride;      // tiles a rank-major tile array can need (tile 16)
@@ -160,7 +160,7 @@ int check_config(const ep_config_t* c, Shape* s)
     s->WM = W * M;
     s->row_bytes = row;
     s->x_bytes = c->dispatch_cast != EP_CAST_NONE ? crow : row;
-    s->row_vecs = (int)(s->x_bytes / 16);
+    s->row_vecs = (int)(s->x_bytes / 16);  // 16-byte vectors of an input row
     s->crow_bytes = crow;
     s->scale_bytes = sbytes;
     const int64_t tiles_per_rank = (M + ep::kMinTile - 1) / ep::kMinTile;
@@ -748,7 +748,7 @@ int ep_combine(ep_plan_t* p, const ep_combine_args_t* a, void* stream_ptr)
         wa.out = static_cast<uint8_t*>(a->out);
         wa.out_w = a->out_weights;
         wa.fwd = ws_fwd(p);
-        wa.units = wire == EP_WIRE_FP8_BLOCK128 ? s.H / 16 : s.H / 32;
+        wa.units = s.H / 16;
         wa.piece_units = (wa.units + l.combine_row_split - 1) / l.combine_row_split;
         if (wire == EP_WIRE_FP8_BLOCK128) {
             wa.row_bytes = (uint32_t)s.H;

@@ -80,10 +80,8 @@ __global__ __launch_bounds__(256) void ep_quantize_kernel(QuantizeArgs a)
         const float r = amax > 0.0f ? __fdiv_rn(kE4M3Max, amax) : 1.0f;
         if (!valid)
             return;
-        u32x2 out = {0u, 0u};
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            out[i / 4] |= to_e4m3(f[i] * r) << (8 * (i % 4));
+        const u32x2 out = {e4m3x4(f[0] * r, f[1] * r, f[2] * r, f[3] * r),
+                           e4m3x4(f[4] * r, f[5] * r, f[6] * r, f[7] * r)};
         *reinterpret_cast<u32x2*>(a.out + row * a.H + h0) = out;
         if ((lane & 15) == 0)
             reinterpret_cast<float*>(a.scales)[row * (a.H / 128) + h0 / 128] = s;
@@ -106,10 +104,9 @@ __global__ __launch_bounds__(256) void ep_quantize_kernel(QuantizeArgs a)
     }
 }
 
-// A lane's unit of a wire row: 16 bytes of codes, 16 FP8 elements (inside one
-// 128-element scale block) or 32 MXFP4 elements (exactly one scale block).
-template <int WIRE>
-constexpr int unit_elems() { return WIRE == kWireFp8Block128 ? 16 : 32; }
+// A lane's unit of a wire row: 16 elements, inside one scale block: 16 bytes
+// of FP8 codes, or 8 bytes of MXFP4 codes (half of a 32-element block).
+constexpr int kUnitElems = 16;
 
 // Decode one unit into FP32 with the hardware conversions, which are exact:
 // an E4M3 code to FP32 (v_cvt_pk_f32_fp8), then one FP32 multiply by the
@@ -117,8 +114,7 @@ constexpr int unit_elems() { return WIRE == kWireFp8Block128 ? 16 : 32; }
 // f32_fp4). Code order follows the row: byte i of dword d holds FP8 element
 // 4d + i; the low nibble of byte b holds MXFP4 element 2b.
 template <int WIRE>
-__device__ __forceinline__ void decode_unit(const u32x4& c, uint32_t sbits,
-                                            float (&f)[unit_elems<WIRE>()])
+__device__ __forceinline__ void decode_unit(const u32x4& c, uint32_t sbits, float (&f)[kUnitElems])
 {
     if constexpr (WIRE == kWireFp8Block128) {
         const float s = __builtin_bit_cast(float, sbits);
@@ -134,7 +130,7 @@ __device__ __forceinline__ void decode_unit(const u32x4& c, uint32_t sbits,
     } else {
         const float s = __builtin_ldexpf(1.0f, (int)(sbits & 0xFFu) - 127);
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
+        for (int d = 0; d < 2; ++d) {
             const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[d], s, 0);
             const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[d], s, 1);
             const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[d], s, 2);
@@ -171,7 +167,7 @@ __device__ __forceinline__ int rank_of_token(const TokenMap& tk, int flat)
 template <int G, int WIRE, int DT, bool kStream>
 __global__ __launch_bounds__(1024) void ep_combine_wire_kernel(WireCombineArgs a, TokenMap tk)
 {
-    constexpr int UE = unit_elems<WIRE>();
+    constexpr int UE = kUnitElems;
     constexpr int aux = Policy<kStream>::combine_load;
     const int lane = threadIdx.x & (kWave - 1);
     const int flat = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
@@ -200,11 +196,14 @@ __global__ __launch_bounds__(1024) void ep_combine_wire_kernel(WireCombineArgs a
                     const __amdgpu_buffer_rsrc_t ry = row_rsrc(a.y + gq * a.row_bytes, a.row_bytes);
                     const __amdgpu_buffer_rsrc_t rs =
                         row_rsrc(a.ys + gq * a.scale_bytes, a.scale_bytes);
-                    raw[q] = bload16<aux>(ry, (uint32_t)u * 16u);
-                    if constexpr (WIRE == kWireFp8Block128)
+                    if constexpr (WIRE == kWireFp8Block128) {
+                        raw[q] = bload16<aux>(ry, (uint32_t)u * 16u);
                         sc[q] = __builtin_amdgcn_raw_buffer_load_b32(rs, (u / 8) * 4, 0, aux);
-                    else
-                        sc[q] = __builtin_amdgcn_raw_buffer_load_b8(rs, u, 0, aux);
+                    } else {
+                        const u32x2 c = __builtin_amdgcn_raw_buffer_load_b64(ry, u * 8, 0, aux);
+                        raw[q] = {c.x, c.y, 0u, 0u};
+                        sc[q] = __builtin_amdgcn_raw_buffer_load_b8(rs, u / 2, 0, aux);
+                    }
                 }
             }
 #pragma unroll
