@@ -34,10 +34,24 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
 METRIC = "dispatch+combine µs/call and payload HBM GB/s (% of peak), EP8 H=7168 k=8"
 KERNEL_SOURCES = [os.path.join(ROOT, "combine_route_amd", "csrc", f)
-                  for f in ("ep_kernels.hip", "ep_expert.hip", "ep_kernels.h", "ep_device.h",
-                            "ep_plan.cpp")]
+                  for f in ("ep_kernels.hip", "ep_expert.hip", "ep_wire.hip", "ep_kernels.h",
+                            "ep_device.h", "ep_plan.cpp")]
 KERNELS = {"copy": "ep_copy_kernel", "combine": "ep_combine_kernel"}
 EXPERT_KERNELS = {"copy": "ex_copy_kernel", "combine": "ex_combine_kernel"}
+# counter summaries: label -> pattern over the demangled kernel name; the
+# copy kernel's last template argument says whether it casts to E4M3, and
+# the wire kernels name their wire (1 = FP8 block-128, 2 = MXFP4)
+COUNTER_KERNELS = {
+    "ep_copy_kernel": r"ep_copy_kernel<[^>]*, false>",
+    "ep_combine_kernel": r"ep_combine_kernel<",
+    "ex_copy_kernel": r"ex_copy_kernel<",
+    "ex_combine_kernel": r"ex_combine_kernel<",
+    "ep_copy_kernel_cast": r"ep_copy_kernel<[^>]*, true>",
+    "ep_quantize_kernel_fp8_block128": r"ep_quantize_kernel<1,",
+    "ep_quantize_kernel_mxfp4": r"ep_quantize_kernel<2,",
+    "ep_combine_wire_kernel_fp8_block128": r"ep_combine_wire_kernel<\d+, 1,",
+    "ep_combine_wire_kernel_mxfp4": r"ep_combine_wire_kernel<\d+, 2,",
+}
 
 
 def kernel_source_hash() -> str:
@@ -236,10 +250,11 @@ def _kernel_ms(cra, torch, plan, kid, fn, steps):
     return ms / max(c, 1)
 
 
-def _roof(nbytes, ms, kernel):
+def _roof(nbytes, ms, kernel, workload, label):
     a = nbytes / (ms * 1e-3) / 1e9
     return {"bound": "hbm", "kernel": kernel, "achieved": round(a, 2), "peak": PEAK_HBM_GBS,
             "unit": "GB/s", "frac": round(a / PEAK_HBM_GBS, 4),
+            "traffic": read_traffic(workload, label),
             "algorithmic_bytes_per_launch": int(nbytes)}
 
 
@@ -266,7 +281,7 @@ def measure_quantized_wires(args, cra, torch, np, wl, inp, stream):
         out["dispatch_fp8_direct_cast"] = {
             "us_per_call": round(ms * 1e3, 2), "copy_kernel_us": round(kms * 1e3, 2),
             "received_bytes_saved": R * H,
-            "roofline": _roof(nb, kms, "ep_copy_kernel (cast)")}
+            "roofline": _roof(nb, kms, "ep_copy_kernel (cast)", wl.name, "ep_copy_kernel_cast")}
         op.close()
         del op
         torch.cuda.empty_cache()
@@ -300,8 +315,10 @@ def measure_quantized_wires(args, cra, torch, np, wl, inp, stream):
             "combine_us_per_call": round(cms * 1e3, 2), "combine_kernel_us": round(kms * 1e3, 2),
             "quantize_us_per_call": round(qms * 1e3, 2),
             "quantize_rows": rows,
-            "roofline_combine": _roof(cb, kms, "ep_combine_wire_kernel"),
-            "roofline_quantize": _roof(qb, qms, "ep_quantize_kernel")}
+            "roofline_combine": _roof(cb, kms, "ep_combine_wire_kernel", wl.name,
+                                      "ep_combine_wire_kernel_" + name),
+            "roofline_quantize": _roof(qb, qms, "ep_quantize_kernel", wl.name,
+                                       "ep_quantize_kernel_" + name)}
         op.close()
         del op, yq, ys
         torch.cuda.empty_cache()
@@ -360,9 +377,11 @@ def _counter_means(path):
 
 
 def summarize_counters(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, cal_mib, workload):
-    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the four large kernels,
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the large kernels,
     each scaled by what the same counter reads for the calibration copy
     (cal_mib MiB read and cal_mib MiB written per launch)."""
+    import re
+
     import workloads
 
     fetch, write = _counter_means(fetch_csv), _counter_means(write_csv)
@@ -373,11 +392,13 @@ def summarize_counters(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, cal_m
     w_cal = max(v for (k, c), v in cal_w.items() if c == "WRITE_SIZE") * 1024
     f_scale, w_scale = cal_bytes / f_cal, cal_bytes / w_cal
     wl = workloads.WORKLOADS[workload]
-    for kname in list(KERNELS.values()) + list(EXPERT_KERNELS.values()):
-        fk = [v for (k, c), v in fetch.items() if kname in k]
-        wk = [v for (k, c), v in write.items() if kname in k]
+    for kname, pattern in COUNTER_KERNELS.items():
+        fk = [v for (k, c), v in fetch.items() if re.search(pattern, k)]
+        wk = [v for (k, c), v in write.items() if re.search(pattern, k)]
         if not fk or not wk:
             continue
+        if len(fk) > 1 or len(wk) > 1:
+            raise SystemExit(f"{kname}: several kernel instances match {pattern!r}")
         rd = fk[0] * 1024 * f_scale
         wr = wk[0] * 1024 * w_scale
         lines = [f"# HBM traffic per launch of {kname}, workload {workload}",
@@ -385,9 +406,9 @@ def summarize_counters(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, cal_m
                  f"# each scaled by the same counter on a plain {cal_mib} MiB device copy",
                  "# Commands (from the repository root):",
                  "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- "
-                 "python -u bench.py --no-cpu-baseline --steps 5 --warmup 2",
+                 "python -u bench.py --no-cpu-baseline --steps 3 --warmup 1",
                  "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- "
-                 "python -u bench.py --no-cpu-baseline --steps 5 --warmup 2",
+                 "python -u bench.py --no-cpu-baseline --steps 3 --warmup 1",
                  f"#   rocprofv3 --pmc FETCH_SIZE ... -- python -u bench.py --copy-calibration {cal_mib} --steps 3 --warmup 1",
                  f"#   rocprofv3 --pmc WRITE_SIZE ... -- python -u bench.py --copy-calibration {cal_mib} --steps 3 --warmup 1",
                  f"#   python bench.py --summarize-counters <the four counter_collection.csv> {cal_mib} {workload}",
