@@ -302,12 +302,14 @@ def measure_quantized_wires(args, cra, torch, np, wl, inp, stream):
             y = torch.randn((W, W * M, H), generator=g, device=dev).to(cdt)
         yq = torch.empty((W, W * M, row), dtype=torch.uint8, device=dev)
         ys = torch.empty((W, W * M, srow), dtype=torch.uint8, device=dev)
-        qstep = lambda: cra.ep_quantize_rows(y, wire, yq, ys, stream=stream)
+        # the send side converts the rows the combine reads: recv_num_token per rank
+        qstep = lambda: cra.ep_quantize_rows(y, wire, yq, ys, stream=stream,
+                                             counts=op.recv_num_token)
         qms = _timed(torch, stream, qstep, args.steps, args.warmup)
         cstep = lambda: op.combine(yq, op.out_weights, stream=stream, y_scales=ys)
         cms = _timed(torch, stream, cstep, args.steps, args.warmup)
         kms = _kernel_ms(cra, torch, op.plan, cra.EP_KERNEL_COMBINE, cstep, args.steps)
-        rows = W * W * M
+        rows = R
         qb = rows * (2 * H + row + srow)
         cb = R * (row + srow + 4 * k) + N * (2 * H + 4 * k) + N * P * 4
         out["combine_" + name] = {

@@ -122,7 +122,7 @@ def load():
     lib.ep_convert_dispatch_output.argtypes = [V, P(EpConvertDispatchArgs), V]
     lib.ep_convert_combine_input.argtypes = [V, P(EpConvertCombineArgs), V]
     lib.ep_quantize_rows.argtypes = [V, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
-                                     ctypes.c_int32, V, V, V]
+                                     ctypes.c_int32, V, V, V, ctypes.c_int64, V]
     for name in EXPORTED:
         if name not in ("ep_workspace_bytes", "ep_last_error", "ep_expert_workspace_bytes"):
             getattr(lib, name).restype = I
@@ -288,9 +288,12 @@ def _hold(tensors):
 
 
 def ep_quantize_rows(rows: torch.Tensor, wire, out: torch.Tensor, scales: torch.Tensor,
-                     stream=None) -> None:
+                     stream=None, counts: Optional[torch.Tensor] = None) -> None:
     """ep_quantize_rows(): rows [..., H] bf16 / fp16 into the wire format
-    (EP_WIRE_* or its name); out and scales sized as include/ep.h says."""
+    (EP_WIRE_* or its name); out and scales sized as include/ep.h says.
+    counts: an int32 device tensor of one count per leading index of rows
+    ([G, R, H] rows with counts [G]); only the first counts[g] rows of group
+    g are converted (recv_num_token for a combine's input)."""
     w = WIRES[wire] if wire is None or isinstance(wire, str) else wire
     H = rows.shape[-1]
     n = rows.numel() // H if H else 0
@@ -303,9 +306,17 @@ def ep_quantize_rows(rows: torch.Tensor, wire, out: torch.Tensor, scales: torch.
         need_out, need_sc = n * H // 2, n * (H // 32)
     else:
         raise ValueError(f"wire must be fp8_block128 or mxfp4, not {wire!r}")
+    cp, group = None, 0
+    if counts is not None:
+        if rows.dim() < 2 or rows.shape[0] == 0:
+            raise ValueError("counts needs rows of shape [G, ..., H] with G >= 1")
+        if counts.dtype != torch.int32:
+            raise ValueError(f"counts must be int32, not {counts.dtype}")
+        group = n // rows.shape[0]
+        cp = _dev(counts, "counts", rows.shape[0] * 4)
     _check("ep_quantize_rows", load().ep_quantize_rows(
         _dev(rows, "rows", n * H * 2), n, H, dt, w, _dev(out, "out", need_out),
-        _dev(scales, "scales", need_sc), _stream(stream, rows.device.index)))
+        _dev(scales, "scales", need_sc), cp, group, _stream(stream, rows.device.index)))
 
 
 def ep_get_src_token_pos(plan: int, rank: int) -> int:

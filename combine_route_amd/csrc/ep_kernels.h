@@ -136,12 +136,20 @@ struct ExpertCombineArgs {
 constexpr int kWireFp8Block128 = 1;  // E4M3 codes, one FP32 scale per 128 elements
 constexpr int kWireMxfp4 = 2;        // packed E2M1 codes, one E8M0 scale per 32
 
+// A quantize wave converts up to kQuantChunks chunks of kQuantChunk elements.
+constexpr int kQuantChunk = 512;
+constexpr int kQuantChunks = 8;
+
 struct QuantizeArgs {
     const uint8_t* in;           // [rows][H] bf16 / fp16
     uint8_t* out;                // [rows][H] E4M3 or [rows][H / 2] packed E2M1
     uint8_t* scales;             // [rows][H / 128] float or [rows][H / 32] E8M0
+    const int32_t* counts;       // [rows / group_rows] rows kept per group, or null
     int64_t rows;
+    int64_t group_rows;
     int32_t H;
+    int32_t pieces;              // row pieces (a wave each)
+    int32_t piece_chunks;        // chunks of a piece, <= kQuantChunks
 };
 
 struct WireCombineArgs {
@@ -152,10 +160,15 @@ struct WireCombineArgs {
     float* out_w;                // [W][M][k] or null
     const int32_t* fwd;          // [W][M][P]
     int32_t units;               // 16-element units per row (H / 16)
-    int32_t piece_units;         // units per row piece
+    int32_t piece_units;         // units per row piece: a multiple of 8, <= kWirePieceUnits
     uint32_t row_bytes, scale_bytes;
+    int32_t scale_pre;           // scale rows are whole dwords: preload them
     int32_t M, k, P;
 };
+
+// Most 16-element units in a wire combine's row piece: 64 lanes each hold
+// one scale dword (128 elements) of a contribution row.
+constexpr int kWirePieceUnits = 512;
 
 hipError_t launch_route(const RouteArgs& a, const TileMap& tm, hipStream_t s);
 hipError_t launch_scan(const ScanArgs& a, int W, hipStream_t s);
@@ -173,7 +186,7 @@ hipError_t launch_expert_copy(const ExpertArgs& a, int waves, int row_split, boo
 hipError_t launch_expert_combine(const ExpertCombineArgs& a, int W, int dtype, int waves,
                                  int row_split, bool stream, hipStream_t s);
 
-hipError_t launch_quantize(const QuantizeArgs& a, int wire, int dtype, hipStream_t s);
+hipError_t launch_quantize(const QuantizeArgs& a, int wire, int dtype, bool stream, hipStream_t s);
 hipError_t launch_combine_wire(const WireCombineArgs& a, const TokenMap& tk, int wire, int dtype,
                                int waves, int row_split, bool stream, hipStream_t s);
 

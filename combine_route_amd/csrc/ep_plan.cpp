@@ -749,7 +749,10 @@ int ep_combine(ep_plan_t* p, const ep_combine_args_t* a, void* stream_ptr)
         wa.out_w = a->out_weights;
         wa.fwd = ws_fwd(p);
         wa.units = s.H / 16;
+        // pieces start on a scale dword (8 units) and a lane holds one dword
+        // of each contribution's scale row
         wa.piece_units = (wa.units + l.combine_row_split - 1) / l.combine_row_split;
+        wa.piece_units = std::min((wa.piece_units + 7) / 8 * 8, ep::kWirePieceUnits);
         if (wire == EP_WIRE_FP8_BLOCK128) {
             wa.row_bytes = (uint32_t)s.H;
             wa.scale_bytes = (uint32_t)(s.H / 128 * 4);
@@ -757,6 +760,7 @@ int ep_combine(ep_plan_t* p, const ep_combine_args_t* a, void* stream_ptr)
             wa.row_bytes = (uint32_t)(s.H / 2);
             wa.scale_bytes = (uint32_t)(s.H / 32);
         }
+        wa.scale_pre = wa.scale_bytes % 4 == 0;
         wa.M = s.M;
         wa.k = s.k;
         wa.P = s.P;
@@ -775,7 +779,8 @@ int ep_combine(ep_plan_t* p, const ep_combine_args_t* a, void* stream_ptr)
 }
 
 int ep_quantize_rows(const void* in, int64_t rows, int32_t hidden, int32_t in_dtype,
-                     int32_t wire, void* out, void* scales, void* stream_ptr)
+                     int32_t wire, void* out, void* scales, const int32_t* row_counts,
+                     int64_t group_rows, void* stream_ptr)
 {
     if (!in || !out || !scales)
         return fail(EP_ERR_NULL, "in, out and scales are required");
@@ -792,15 +797,35 @@ int ep_quantize_rows(const void* in, int64_t rows, int32_t hidden, int32_t in_dt
         return fail(EP_ERR_ARG, "hidden = %d: must be a positive multiple of %d", hidden, block);
     if (rows * (int64_t)hidden >= ((int64_t)1 << 40))
         return fail(EP_ERR_SIZE, "rows * hidden is too large");
+    if (hidden > (1 << 30))
+        return fail(EP_ERR_SIZE, "hidden = %d is too large", hidden);
+    if (row_counts) {
+        if (!aligned(row_counts, 4))
+            return fail(EP_ERR_ALIGN, "row_counts must be 4-byte aligned");
+        if (group_rows < 1 || rows % group_rows != 0)
+            return fail(EP_ERR_ARG, "group_rows = %lld: must be >= 1 and divide rows = %lld",
+                        (long long)group_rows, (long long)rows);
+    }
     ep::QuantizeArgs qa;
     qa.in = static_cast<const uint8_t*>(in);
     qa.out = static_cast<uint8_t*>(out);
     qa.scales = static_cast<uint8_t*>(scales);
+    qa.counts = row_counts;
     qa.rows = rows;
+    qa.group_rows = row_counts ? group_rows : rows;
     qa.H = hidden;
+    // a wave per row piece of at most kQuantChunks chunks, pieces as even as
+    // the chunk count allows
+    const int chunks = (hidden + ep::kQuantChunk - 1) / ep::kQuantChunk;
+    qa.pieces = (chunks + ep::kQuantChunks - 1) / ep::kQuantChunks;
+    qa.piece_chunks = (chunks + qa.pieces - 1) / qa.pieces;
+    // the bytes a call may move against the MALL: past it, loads and stores stream
+    const int64_t out_row = wire == EP_WIRE_FP8_BLOCK128 ? hidden + hidden / 32 : hidden / 2 + hidden / 32;
+    const bool stream = rows * (2 * (int64_t)hidden + out_row) > kKeepBytes;
     const hipError_t e =
         ep::launch_quantize(qa, wire == EP_WIRE_FP8_BLOCK128 ? ep::kWireFp8Block128 : ep::kWireMxfp4,
-                            in_dtype == EP_BF16 ? 0 : 1, static_cast<hipStream_t>(stream_ptr));
+                            in_dtype == EP_BF16 ? 0 : 1, stream,
+                            static_cast<hipStream_t>(stream_ptr));
     if (e != hipSuccess)
         return fail(EP_ERR_HIP, "quantize launch failed: %s", hipGetErrorString(e));
     return ok();

@@ -54,53 +54,89 @@ __device__ __forceinline__ float group_max(float v)
     return v;
 }
 
-template <int WIRE, int DT>
+// A wave per (row, piece of up to kQuantChunks chunks of 512 elements): every
+// chunk of the piece is loaded (16 bytes a lane) before the first is
+// converted. Rows are addressed through per-row buffer resources: a chunk past
+// the row end loads zeros and its stores are dropped, and since blocks never
+// straddle the end (H is a multiple of the block) no lane needs a guard.
+template <int WIRE, int DT, bool kStream>
 __global__ __launch_bounds__(256) void ep_quantize_kernel(QuantizeArgs a)
 {
+    constexpr int ld = Policy<kStream>::combine_load;
+    constexpr int st = Policy<kStream>::combine_store;
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t item = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-    const int chunks = (a.H + 511) / 512;
-    const int64_t row = item / chunks;
+    const int64_t item = (int64_t)blockIdx.x * (blockDim.x / kWave) + uniform(threadIdx.x / kWave);
+    const int64_t row = item / a.pieces;
     if (row >= a.rows)
         return;  // whole waves
-    const int h0 = (int)(item - row * chunks) * 512 + lane * 8;  // this lane's 8 elements
-    const bool valid = h0 < a.H;  // blocks lie wholly inside or outside the row
-    float f[8] = {};
-    if (valid) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(a.in + (row * a.H + h0) * 2);
-        widen<DT>(w, f);
+    if (a.counts != nullptr) {
+        const int64_t g = row / a.group_rows;
+        if (row - g * a.group_rows >= (int64_t)a.counts[g])
+            return;  // a row past its group's count: whole waves
     }
-    float amax = 0.0f;
+    const int e0 = (int)(item - row * a.pieces) * a.piece_chunks * kQuantChunk + lane * 8;
+    const uint32_t in_bytes = (uint32_t)a.H * 2;
+    const __amdgpu_buffer_rsrc_t rin = row_rsrc(a.in + row * in_bytes, in_bytes);
+    // chunks past the piece load from past the row: zeros, with no memory access
+    u32x4 raw[kQuantChunks];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        amax = __builtin_fmaxf(amax, __builtin_fabsf(f[i]));
+    for (int c = 0; c < kQuantChunks; ++c)
+        raw[c] = bload16<ld>(rin, c < a.piece_chunks ? (uint32_t)(e0 + c * kQuantChunk) * 2u
+                                                     : in_bytes);
     if constexpr (WIRE == kWireFp8Block128) {
-        amax = group_max<16>(amax);
-        const float s = amax > 0.0f ? __fdiv_rn(amax, kE4M3Max) : 1.0f;
-        const float r = amax > 0.0f ? __fdiv_rn(kE4M3Max, amax) : 1.0f;
-        if (!valid)
-            return;
-        const u32x2 out = {e4m3x4(f[0] * r, f[1] * r, f[2] * r, f[3] * r),
-                           e4m3x4(f[4] * r, f[5] * r, f[6] * r, f[7] * r)};
-        *reinterpret_cast<u32x2*>(a.out + row * a.H + h0) = out;
-        if ((lane & 15) == 0)
-            reinterpret_cast<float*>(a.scales)[row * (a.H / 128) + h0 / 128] = s;
-    } else {
-        amax = group_max<4>(amax);
-        // the largest E2M1 exponent is 2: the block's largest magnitude lands
-        // in [4, 8) after scaling by 2^-E
-        int E = -127;
-        if (amax > 0.0f)
-            E = max(__builtin_amdgcn_frexp_expf(amax) - 3, -127);
-        if (!valid)
-            return;
-        uint32_t out = 0;
+        const __amdgpu_buffer_rsrc_t rout = row_rsrc(a.out + row * a.H, (uint32_t)a.H);
+        const uint32_t sbytes = (uint32_t)(a.H / 128) * 4u;
+        const __amdgpu_buffer_rsrc_t rsc = row_rsrc(a.scales + row * sbytes, sbytes);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            out |= to_e2m1(__builtin_ldexpf(f[i], -E)) << (4 * i);
-        *reinterpret_cast<uint32_t*>(a.out + row * (a.H / 2) + h0 / 2) = out;
-        if ((lane & 3) == 0)
-            a.scales[row * (a.H / 32) + h0 / 32] = (uint8_t)(E + 127);
+        for (int c = 0; c < kQuantChunks; ++c) {
+            if (c < a.piece_chunks) {
+                const int e = e0 + c * kQuantChunk;
+                float f[8];
+                widen<DT>(raw[c], f);
+                float amax = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    amax = __builtin_fmaxf(amax, __builtin_fabsf(f[i]));
+                amax = group_max<16>(amax);
+                const float s = amax > 0.0f ? __fdiv_rn(amax, kE4M3Max) : 1.0f;
+                const float r = amax > 0.0f ? __fdiv_rn(kE4M3Max, amax) : 1.0f;
+                const u32x2 q = {e4m3x4(f[0] * r, f[1] * r, f[2] * r, f[3] * r),
+                                 e4m3x4(f[4] * r, f[5] * r, f[6] * r, f[7] * r)};
+                __builtin_amdgcn_raw_buffer_store_b64(q, rout, (uint32_t)e, 0, st);
+                if ((lane & 15) == 0)
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, s), rsc,
+                                                          (uint32_t)(e / 128) * 4u, 0, st);
+            }
+        }
+    } else {
+        const __amdgpu_buffer_rsrc_t rout = row_rsrc(a.out + row * (a.H / 2), (uint32_t)a.H / 2u);
+        const __amdgpu_buffer_rsrc_t rsc = row_rsrc(a.scales + row * (a.H / 32), (uint32_t)a.H / 32u);
+#pragma unroll
+        for (int c = 0; c < kQuantChunks; ++c) {
+            if (c < a.piece_chunks) {
+                const int e = e0 + c * kQuantChunk;
+                float f[8];
+                widen<DT>(raw[c], f);
+                float amax = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    amax = __builtin_fmaxf(amax, __builtin_fabsf(f[i]));
+                amax = group_max<4>(amax);
+                // the largest E2M1 exponent is 2: the block's largest magnitude
+                // lands in [4, 8) after scaling by 2^-E
+                int E = -127;
+                if (amax > 0.0f)
+                    E = max(__builtin_amdgcn_frexp_expf(amax) - 3, -127);
+                uint32_t q = 0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    q |= to_e2m1(__builtin_ldexpf(f[i], -E)) << (4 * i);
+                __builtin_amdgcn_raw_buffer_store_b32(q, rout, (uint32_t)e / 2u, 0, st);
+                if ((lane & 3) == 0)
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(E + 127), rsc, (uint32_t)e / 32u,
+                                                         0, st);
+            }
+        }
     }
 }
 
@@ -183,6 +219,22 @@ __global__ __launch_bounds__(1024) void ep_combine_wire_kernel(WireCombineArgs a
     const __amdgpu_buffer_rsrc_t rdst = row_rsrc(a.out + tok * out_bytes, out_bytes);
     const int ubeg = piece * a.piece_units;
     const int uend = min(a.units, ubeg + a.piece_units);
+    // Scale rows are read once: lane l holds dword ubeg / 8 + l of each of the
+    // first G contribution rows (a dword covers 8 units), and a unit takes its
+    // row's scale from lane (u - ubeg) / 8. Re-reading the scales on every
+    // pass over the row fetched each scale line 7 times at H = 7168.
+    uint32_t spre[G];
+    if (a.scale_pre) {
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+            if (q < n) {
+                const int64_t gq = __builtin_amdgcn_readlane(gl, q);
+                const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.ys + gq * a.scale_bytes, a.scale_bytes);
+                spre[q] = __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)(ubeg / 8 + lane) * 4u,
+                                                               0, aux);
+            }
+        }
+    }
     for (int u = ubeg + lane; u - lane < uend; u += kWave) {
         const bool live = u < uend;
         float acc[UE];
@@ -194,15 +246,30 @@ __global__ __launch_bounds__(1024) void ep_combine_wire_kernel(WireCombineArgs a
                 if (i0 + q < n && live) {
                     const int64_t gq = __builtin_amdgcn_readlane(gl, i0 + q);
                     const __amdgpu_buffer_rsrc_t ry = row_rsrc(a.y + gq * a.row_bytes, a.row_bytes);
-                    const __amdgpu_buffer_rsrc_t rs =
-                        row_rsrc(a.ys + gq * a.scale_bytes, a.scale_bytes);
-                    if constexpr (WIRE == kWireFp8Block128) {
+                    if constexpr (WIRE == kWireFp8Block128)
                         raw[q] = bload16<aux>(ry, (uint32_t)u * 16u);
-                        sc[q] = __builtin_amdgcn_raw_buffer_load_b32(rs, (u / 8) * 4, 0, aux);
-                    } else {
+                    else {
                         const u32x2 c = __builtin_amdgcn_raw_buffer_load_b64(ry, u * 8, 0, aux);
                         raw[q] = {c.x, c.y, 0u, 0u};
-                        sc[q] = __builtin_amdgcn_raw_buffer_load_b8(rs, u / 2, 0, aux);
+                    }
+                    if (!a.scale_pre || i0 > 0) {
+                        const __amdgpu_buffer_rsrc_t rs =
+                            row_rsrc(a.ys + gq * a.scale_bytes, a.scale_bytes);
+                        if constexpr (WIRE == kWireFp8Block128)
+                            sc[q] = __builtin_amdgcn_raw_buffer_load_b32(rs, (u / 8) * 4, 0, aux);
+                        else
+                            sc[q] = __builtin_amdgcn_raw_buffer_load_b8(rs, u / 2, 0, aux);
+                    }
+                }
+            }
+            if (a.scale_pre && i0 == 0) {
+                // every lane takes part in the cross-lane reads
+#pragma unroll
+                for (int q = 0; q < G; ++q) {
+                    if (q < n) {
+                        const uint32_t d = (uint32_t)__shfl((int)spre[q], (u - ubeg) >> 3);
+                        // MXFP4: byte (u / 2) mod 4 of the dword
+                        sc[q] = WIRE == kWireFp8Block128 ? d : d >> (8 * ((u >> 1) & 3));
                     }
                 }
             }
@@ -279,25 +346,37 @@ hipError_t combine_wire_fmt(const WireCombineArgs& a, const TokenMap& tk, int dt
     return combine_wire_with<kCombineGroup, WIRE>(a, tk, dtype, grid, block, stream, s);
 }
 
+template <int WIRE, int DT>
+void quantize_with(const QuantizeArgs& a, dim3 grid, dim3 block, bool stream, hipStream_t s)
+{
+    if (stream)
+        hipLaunchKernelGGL((ep_quantize_kernel<WIRE, DT, true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((ep_quantize_kernel<WIRE, DT, false>), grid, block, 0, s, a);
+}
+
 }  // namespace
 
-hipError_t launch_quantize(const QuantizeArgs& a, int wire, int dtype, hipStream_t s)
+hipError_t launch_quantize(const QuantizeArgs& a, int wire, int dtype, bool stream, hipStream_t s)
 {
     if (a.rows == 0)
         return hipSuccess;
-    const int64_t items = a.rows * ((a.H + 511) / 512);
+    if (a.piece_chunks < 1 || a.piece_chunks > kQuantChunks ||
+        (int64_t)a.pieces * a.piece_chunks * kQuantChunk < a.H)
+        return hipErrorInvalidValue;
+    const int64_t items = a.rows * a.pieces;
     const dim3 grid((unsigned)((items + 3) / 4));
     const dim3 block(4 * kWave);
     if (wire == kWireFp8Block128) {
         if (dtype == 0)
-            hipLaunchKernelGGL((ep_quantize_kernel<kWireFp8Block128, 0>), grid, block, 0, s, a);
+            quantize_with<kWireFp8Block128, 0>(a, grid, block, stream, s);
         else
-            hipLaunchKernelGGL((ep_quantize_kernel<kWireFp8Block128, 1>), grid, block, 0, s, a);
+            quantize_with<kWireFp8Block128, 1>(a, grid, block, stream, s);
     } else {
         if (dtype == 0)
-            hipLaunchKernelGGL((ep_quantize_kernel<kWireMxfp4, 0>), grid, block, 0, s, a);
+            quantize_with<kWireMxfp4, 0>(a, grid, block, stream, s);
         else
-            hipLaunchKernelGGL((ep_quantize_kernel<kWireMxfp4, 1>), grid, block, 0, s, a);
+            quantize_with<kWireMxfp4, 1>(a, grid, block, stream, s);
     }
     return hipGetLastError();
 }

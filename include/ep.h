@@ -241,10 +241,19 @@ int ep_combine(ep_plan_t *plan, const ep_combine_args_t *args, void *stream);
  * to nearest even, saturating at 6 (scale code 0 for an all-zero block);
  * inputs finite. Device pointers: in and out 16-byte aligned, scales 4-byte
  * aligned; no plan, no allocation, asynchronous on stream, capturable.
+ * row_counts: NULL converts every row. Otherwise the rows form groups of
+ * group_rows consecutive rows (rows a multiple of group_rows), row_counts is a
+ * device int32 [rows / group_rows] array, and in group g only the first
+ * row_counts[g] rows are read and written (the rest of the group's in, out
+ * and scales rows are untouched; a count above group_rows means all of them).
+ * With recv_num_token and group_rows = world_size * max tokens this converts
+ * exactly the rows a combine reads.
  * Errors: EP_ERR_NULL, EP_ERR_ALIGN, EP_ERR_ARG (types, wire, rows < 0,
- * hidden not a positive multiple of the block), EP_ERR_HIP. */
+ * hidden not a positive multiple of the block, group_rows < 1 or not dividing
+ * rows when row_counts is given), EP_ERR_SIZE, EP_ERR_HIP. */
 int ep_quantize_rows(const void *in, int64_t rows, int32_t hidden, int32_t in_dtype,
-                     int32_t wire, void *out, void *scales, void *stream);
+                     int32_t wire, void *out, void *scales, const int32_t *row_counts,
+                     int64_t group_rows, void *stream);
 
 /* Reverse map of rank `rank` ([GUIDE] section 3, get_dispatch_src_token_pos():
  * src_rank * (world_size * max_num_inp_token_per_rank) + src_token_id).

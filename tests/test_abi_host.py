@@ -482,12 +482,28 @@ def test_wire_combine_requires_scales(lib):
 ])
 def test_quantize_rows_rejects_before_launch(lib, args, code, word):
     src, rows, H, dt, wire, out, sc = args
-    assert lib.ep_quantize_rows(src, rows, H, dt, wire, out, sc, None) == code
+    assert lib.ep_quantize_rows(src, rows, H, dt, wire, out, sc, None, 0, None) == code
+    assert word in cra.ep_last_error()
+
+
+@pytest.mark.parametrize("counts,group,code,word", [
+    (FAKE + 0x3002, 2, cra.EP_ERR_ALIGN, "row_counts"),
+    (FAKE + 0x3000, 0, cra.EP_ERR_ARG, "group_rows"),
+    (FAKE + 0x3000, -4, cra.EP_ERR_ARG, "group_rows"),
+    (FAKE + 0x3000, 3, cra.EP_ERR_ARG, "divide rows"),
+    (FAKE + 0x3000, 5, cra.EP_ERR_ARG, "divide rows"),
+])
+def test_quantize_row_counts_checked_before_launch(lib, counts, group, code, word):
+    assert lib.ep_quantize_rows(FAKE, 4, 256, 0, 1, FAKE, FAKE + 0x1000, counts, group,
+                                None) == code
     assert word in cra.ep_last_error()
 
 
 def test_quantize_zero_rows_is_a_no_op(lib):
-    assert lib.ep_quantize_rows(FAKE, 0, 256, 0, 1, FAKE, FAKE + 0x1000, None) == cra.EP_OK
+    assert lib.ep_quantize_rows(FAKE, 0, 256, 0, 1, FAKE, FAKE + 0x1000, None, 0,
+                                None) == cra.EP_OK
+    assert lib.ep_quantize_rows(FAKE, 0, 256, 0, 2, FAKE, FAKE + 0x1000, FAKE + 0x3000, 4,
+                                None) == cra.EP_OK
 
 
 def test_dispatch_cast_layout_and_sizes(lib):

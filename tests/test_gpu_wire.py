@@ -73,6 +73,37 @@ def test_quantize_matches_oracle(name, dtype, n, H):
     assert np.array_equal(got_s.view(np.uint8), ref_s.view(np.uint8))
 
 
+@pytest.mark.parametrize("name", list(WIRES))
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("G,R,H,counts", [
+    (3, 40, 7168, [0, 40, 17]),     # two pieces a row; an empty and a full group
+    (4, 9, 2048, [9, 1, 100, -3]),  # a count past the group and a negative one
+    (2, 130, 128, [129, 64]),
+])
+def test_quantize_with_row_counts(name, dtype, G, R, H, counts):
+    """Only the first counts[g] rows of each group are converted; every other
+    byte of the outputs keeps its previous value."""
+    cw, ow = WIRES[name]
+    _say(f"[case] quantize counts {name} {dtype} G={G} R={R} H={H} {counts}")
+    v = rows_of(G * R + H, G * R, H, dtype, spread=2.0 if dtype == torch.float16 else 4.0)
+    row, srow = (H, H // 128 * 4) if cw == cra.EP_WIRE_FP8_BLOCK128 else (H // 2, H // 32)
+    out = torch.full((G, R, row), 0xA5, dtype=torch.uint8, device="cuda")
+    sc = torch.full((G, R, srow), 0x5A, dtype=torch.uint8, device="cuda")
+    cnt = torch.tensor(counts, dtype=torch.int32, device="cuda")
+    cra.ep_quantize_rows(v.reshape(G, R, H).cuda(), cw, out, sc, counts=cnt)
+    torch.cuda.synchronize()
+    got_c, got_s = out.cpu().numpy(), sc.cpu().numpy()
+    ref_c, ref_s = oracle.quantize_rows(words(v), oracle.BF16 if dtype == torch.bfloat16
+                                        else oracle.FP16, ow)
+    ref_c = ref_c.reshape(G, R, row)
+    ref_s = ref_s.view(np.uint8).reshape(G, R, srow)
+    for g, c in enumerate(counts):
+        keep = min(max(c, 0), R)
+        assert np.array_equal(got_c[g, :keep], ref_c[g, :keep])
+        assert np.array_equal(got_s[g, :keep], ref_s[g, :keep])
+        assert (got_c[g, keep:] == 0xA5).all() and (got_s[g, keep:] == 0x5A).all()
+
+
 def test_e4m3_conversion_of_every_in_range_bf16_value():
     """Blocks whose largest magnitude is 448 have scale 1: each code is then
     the direct E4M3 conversion of the bf16 value itself."""
