@@ -83,7 +83,7 @@ template <int KB>
 __global__ __launch_bounds__(kExWaves * kWave) void ex_count_kernel(ExpertArgs a)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int tile = blockIdx.x * kExWaves + threadIdx.x / kWave;
+    const int tile = blockIdx.x * kExWaves + uniform(threadIdx.x / kWave);
     const int d = blockIdx.y;
     if (tile >= a.T)
         return;  // whole waves
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kExWaves * kWave) void ex_count_kernel(ExpertArgs a
 __global__ __launch_bounds__(kExWaves * kWave) void ex_scan_kernel(ExpertArgs a)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t g = (int64_t)blockIdx.x * kExWaves + threadIdx.x / kWave;
+    const int64_t g = (int64_t)blockIdx.x * kExWaves + uniform(threadIdx.x / kWave);
     if (g >= (int64_t)a.W * a.Er)
         return;  // whole waves
     const int d = (int)(g / a.Er);
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(1024) void ex_copy_kernel(ExpertArgs a)
     __shared__ int32_t s_n[kWave];      // kept packed rows of the row
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = uniform(threadIdx.x / kWave);
     const int nwaves = blockDim.x / kWave;
     const int tile = blockIdx.x;
     const int piece = blockIdx.y;
@@ -393,7 +393,7 @@ template <int G, int U, int DT, bool kStream, bool kWeighted>
 __global__ __launch_bounds__(1024) void ex_combine_kernel(ExpertCombineArgs a)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int q = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const int q = blockIdx.x * (blockDim.x / kWave) + uniform(threadIdx.x / kWave);
     const int piece = blockIdx.y;
     const int d = blockIdx.z;
     if (q >= received(a.recv[d], a.rows))

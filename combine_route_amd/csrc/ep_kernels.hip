@@ -147,7 +147,7 @@ __device__ __forceinline__ void route_tile_by_slot(const int32_t* rows, int cnt,
                                                    uint64_t* s_mask, int32_t* s_n)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = uniform(threadIdx.x / kWave);
     const int nwaves = blockDim.x / kWave;
     const int j = min(lane, k - 1);
     for (int tt = wave; tt < cnt; tt += nwaves) {
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(1024) void ep_route_kernel(RouteArgs a, TileMap tm)
     __shared__ int32_t s_n[kMaxTile];
     const int lane = threadIdx.x & (kWave - 1);
     const int g = KB >= 32 ? (int)blockIdx.x
-                           : (int)(blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave);
+                           : (int)(blockIdx.x * (blockDim.x / kWave) + uniform(threadIdx.x / kWave));
     if (g >= tm.total_tiles)
         return;  // whole waves only (one tile a block when k > 16)
     const int r = rank_of_tile(tm, g);
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(ScanArgs a)
     __shared__ int32_t s_wave[kScanThreads / kWave];
     const int d = blockIdx.x;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = uniform(threadIdx.x / kWave);
     const int32_t* col = a.tile_counts + (int64_t)d * a.tile_stride;
     int32_t* out = a.tile_base + (int64_t)d * a.tile_stride;
     const int n = a.total_tiles;
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
     __shared__ uint64_t s_mask[KB >= 32 ? kMaxTile : 1];  // destination masks (k > 16)
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = uniform(threadIdx.x / kWave);
     const int nwaves = blockDim.x / kWave;
     const int g = blockIdx.x;
     const int piece = blockIdx.y;
@@ -576,7 +576,7 @@ template <int G, int U, int DT, bool kStream>
 __global__ __launch_bounds__(1024) void ep_combine_kernel(CombineArgs a, TokenMap tk)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int flat = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const int flat = blockIdx.x * (blockDim.x / kWave) + uniform(threadIdx.x / kWave);
     if (flat >= tk.total)
         return;  // whole waves only
     const int piece = blockIdx.y;
