@@ -40,7 +40,8 @@ KERNELS = {"copy": "ep_copy_kernel", "combine": "ep_combine_kernel"}
 EXPERT_KERNELS = {"copy": "ex_copy_kernel", "combine": "ex_combine_kernel"}
 # counter summaries: label -> pattern over the demangled kernel name; the
 # copy kernel's last template argument says whether it casts to E4M3, and
-# the wire kernels name their wire (1 = FP8 block-128, 2 = MXFP4)
+# the wire kernels name their wire in the template argument after the
+# row group and units a lane (1 = FP8 block-128, 2 = MXFP4)
 COUNTER_KERNELS = {
     "ep_copy_kernel": r"ep_copy_kernel<[^>]*, false>",
     "ep_combine_kernel": r"ep_combine_kernel<",
@@ -49,8 +50,8 @@ COUNTER_KERNELS = {
     "ep_copy_kernel_cast": r"ep_copy_kernel<[^>]*, true>",
     "ep_quantize_kernel_fp8_block128": r"ep_quantize_kernel<1,",
     "ep_quantize_kernel_mxfp4": r"ep_quantize_kernel<2,",
-    "ep_combine_wire_kernel_fp8_block128": r"ep_combine_wire_kernel<\d+, 1,",
-    "ep_combine_wire_kernel_mxfp4": r"ep_combine_wire_kernel<\d+, 2,",
+    "ep_combine_wire_kernel_fp8_block128": r"ep_combine_wire_kernel<\d+, \d+, 1,",
+    "ep_combine_wire_kernel_mxfp4": r"ep_combine_wire_kernel<\d+, \d+, 2,",
 }
 
 
@@ -327,6 +328,55 @@ def measure_quantized_wires(args, cra, torch, np, wl, inp, stream):
     return out
 
 
+def measure_samples(args, torch, stream, dispatch, combine):
+    """The pages' sampling: rounds of per-call samples, each dispatch and
+    combine bracketed by its own HIP events on the launch stream, reported as
+    p50 and min; a point is flagged when the rounds' p50s spread by more than
+    1.2x. The cold variant writes a 512 MiB scratch buffer before every sample,
+    so the MALL holds none of the call's data when it starts."""
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def run(cold):
+        rounds = []
+        for _ in range(args.rounds):
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                  for _ in range(args.samples)]
+            for e in ev:
+                if cold:
+                    scratch.fill_(cold)
+                e[0].record(stream)
+                dispatch()
+                e[1].record(stream)
+                combine()
+                e[2].record(stream)
+            torch.cuda.synchronize()
+            rounds.append([(e[0].elapsed_time(e[1]) * 1e3, e[1].elapsed_time(e[2]) * 1e3,
+                            e[0].elapsed_time(e[2]) * 1e3) for e in ev])
+        flat = [t for r in rounds for t in r]
+
+        def stat(i):
+            v = sorted(t[i] for t in flat)
+            return {"p50": round(v[len(v) // 2], 2), "min": round(v[0], 2)}
+
+        p50s = [sorted(t[2] for t in r)[len(r) // 2] for r in rounds]
+        spread = max(p50s) / min(p50s)
+        return {"dispatch_us": stat(0), "combine_us": stat(1), "pair_us": stat(2),
+                "round_p50_spread": round(spread, 3), "rejected": spread > 1.2}
+
+    for _ in range(10):
+        dispatch()
+        combine()
+    torch.cuda.synchronize()
+    out = {"method": f"{args.rounds} rounds x {args.samples} eager calls after 10 warmups; "
+                     "each dispatch and combine between HIP events on the launch stream",
+           "warm": run(0)}
+    out["cold"] = run(1)
+    out["cold"]["method"] = "the same, with a 512 MiB device write before every sample"
+    del scratch
+    torch.cuda.empty_cache()
+    return out
+
+
 def workloads_dtype(torch, name):
     return {"bf16": torch.bfloat16, "fp16": torch.float16}[name]
 
@@ -572,6 +622,11 @@ def run(args):
         c, ms = cra.ep_plan_kernel_time(op.plan, kid)
         kern[name] = ms / max(c, 1)
     cra.ep_plan_set_timing(op.plan, False)
+    samples = None
+    if args.rounds > 0 and args.samples > 0:
+        samples = measure_samples(
+            args, torch, stream, lambda: op.dispatch(ntok, x, idx, w, sc, stream=stream),
+            lambda: op.combine(y, op.out_weights, stream=stream))
 
     dom = "copy" if kern["copy"] >= kern["combine"] else "combine"
     achieved = kernel_bytes[dom] / (kern[dom] * 1e-3) / 1e9
@@ -604,6 +659,7 @@ def run(args):
         "payload_bytes_per_call": payload_bytes,
         "received_rows": int(recv.sum()),
         "kernel_us": {k_: round(v * 1e3, 2) for k_, v in kern.items()},
+        "samples": samples,
         "check": check,
         "roofline": {"bound": "hbm", "kernel": KERNELS[dom], "achieved": round(achieved, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -633,6 +689,9 @@ def main():
                     help="skip the expert-major layout measurement")
     ap.add_argument("--no-wires", action="store_true",
                     help="skip the quantized-wire measurements")
+    ap.add_argument("--rounds", type=int, default=4,
+                    help="sampling rounds of per-call timings (0 skips the sampling)")
+    ap.add_argument("--samples", type=int, default=30, help="per-call samples a round")
     ap.add_argument("--graph", action="store_true",
                     help="time K replays of one step captured in a HIP graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
