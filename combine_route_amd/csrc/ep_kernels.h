@@ -162,7 +162,6 @@ struct WireCombineArgs {
     int32_t units;               // 16-element units per row (H / 16)
     int32_t piece_units;         // units per row piece: a multiple of 8, <= kWirePieceUnits
     uint32_t row_bytes, scale_bytes;
-    int32_t scale_pre;           // scale rows are whole dwords: preload them
     int32_t M, k, P;
 };
 

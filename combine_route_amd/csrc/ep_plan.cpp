@@ -760,7 +760,6 @@ int ep_combine(ep_plan_t* p, const ep_combine_args_t* a, void* stream_ptr)
             wa.row_bytes = (uint32_t)(s.H / 2);
             wa.scale_bytes = (uint32_t)(s.H / 32);
         }
-        wa.scale_pre = wa.scale_bytes % 4 == 0;
         wa.M = s.M;
         wa.k = s.k;
         wa.P = s.P;

@@ -4,14 +4,15 @@
 // fp4 with e8m0 scales: "gfx1250 EPv2: ..." PR 726, "MORI-EP User Guide"
 // section 10) but not their arithmetic; the conversions follow the OCP OFP8
 // and MX v1.0 specifications.
-//   quantize  a wave per (row, 512-element chunk): a lane holds 8 elements;
-//             a block's absolute maximum is reduced over its 16 (FP8) or 4
-//             (MXFP4) lanes with cross-lane xors, then every element is
-//             rounded to the format in registers.
+//   quantize  a wave per (row, piece of up to 8 chunks of 512 elements): a
+//             lane holds 8 elements of each chunk; a block's absolute maximum
+//             is reduced over its 16 (FP8) or 4 (MXFP4) lanes with
+//             cross-lane xors, then every element is rounded to the format in
+//             registers.
 //   combine   the combine's gather-fold, with each contribution taken off the
 //             wire (code times scale, in FP32) before it is added; a lane
-//             reads 16 bytes of codes a row and decodes them with the
-//             hardware conversions.
+//             decodes groups of 8 elements with the hardware conversions and
+//             writes each group's 16 output bytes with one store.
 // Encoding is power-of-two and integer arithmetic plus the hardware
 // conversions (round to nearest even), and decoding is exact, so every result
 // is an exact function of its inputs; the two block-scale divisions are
@@ -140,22 +141,24 @@ __global__ __launch_bounds__(256) void ep_quantize_kernel(QuantizeArgs a)
     }
 }
 
-// A lane's unit of a wire row: 16 elements, inside one scale block: 16 bytes
-// of FP8 codes, or 8 bytes of MXFP4 codes (half of a 32-element block).
-constexpr int kUnitElems = 16;
+// A lane decodes groups of 8 elements, inside one scale block: 8 bytes of
+// FP8 codes (two dwords) or 4 bytes of MXFP4 codes (one dword). Its 8 results
+// are one 16-byte store, so a wave's store covers 1 KiB contiguously.
+constexpr int kGroupElems = 8;
 
-// Decode one unit into FP32 with the hardware conversions, which are exact:
+// Decode one group into FP32 with the hardware conversions, which are exact:
 // an E4M3 code to FP32 (v_cvt_pk_f32_fp8), then one FP32 multiply by the
 // block scale; an E2M1 code times the power-of-two scale (v_cvt_scalef32_pk_
 // f32_fp4). Code order follows the row: byte i of dword d holds FP8 element
 // 4d + i; the low nibble of byte b holds MXFP4 element 2b.
 template <int WIRE>
-__device__ __forceinline__ void decode_unit(const u32x4& c, uint32_t sbits, float (&f)[kUnitElems])
+__device__ __forceinline__ void decode_group(const u32x2& c, uint32_t sbits,
+                                             float (&f)[kGroupElems])
 {
     if constexpr (WIRE == kWireFp8Block128) {
         const float s = __builtin_bit_cast(float, sbits);
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
+        for (int d = 0; d < 2; ++d) {
             const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(c[d], false);
             const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(c[d], true);
             f[4 * d + 0] = lo.x * s;
@@ -165,21 +168,18 @@ __device__ __forceinline__ void decode_unit(const u32x4& c, uint32_t sbits, floa
         }
     } else {
         const float s = __builtin_ldexpf(1.0f, (int)(sbits & 0xFFu) - 127);
-#pragma unroll
-        for (int d = 0; d < 2; ++d) {
-            const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[d], s, 0);
-            const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[d], s, 1);
-            const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[d], s, 2);
-            const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[d], s, 3);
-            f[8 * d + 0] = v0.x;
-            f[8 * d + 1] = v0.y;
-            f[8 * d + 2] = v1.x;
-            f[8 * d + 3] = v1.y;
-            f[8 * d + 4] = v2.x;
-            f[8 * d + 5] = v2.y;
-            f[8 * d + 6] = v3.x;
-            f[8 * d + 7] = v3.y;
-        }
+        const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[0], s, 0);
+        const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[0], s, 1);
+        const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[0], s, 2);
+        const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[0], s, 3);
+        f[0] = v0.x;
+        f[1] = v0.y;
+        f[2] = v1.x;
+        f[3] = v1.y;
+        f[4] = v2.x;
+        f[5] = v2.y;
+        f[6] = v3.x;
+        f[7] = v3.y;
     }
 }
 
@@ -196,23 +196,26 @@ __device__ __forceinline__ int rank_of_token(const TokenMap& tk, int flat)
     return lo;
 }
 
-// 16-element units a lane decodes at once per contribution row: C columns a
-// wave apart (unit u and u + 64), so every load and store instruction of the
-// wave covers one contiguous span. Measured on MI355X at 8 x 4096 tokens,
-// H = 7168, top-8: MXFP4 268 -> 240 us with two columns; FP8 364 -> 414 us
-// (two columns of FP8 codes spill registers). Adjacent units in one lane
-// instead were 2x slower: each store then covers a quarter of every 64 bytes.
-constexpr int kWireColumnsFp8 = 1;
+// 8-element groups a lane decodes at once per contribution row: C columns a
+// wave apart (group h and h + 64), so every load and store instruction of
+// the wave covers one contiguous span; a lane reads 8 * C bytes of FP8 codes
+// or 4 * C bytes of MXFP4 codes a row. Measured on MI355X at 8 x 4096
+// tokens, H = 7168, top-8 (FP8 / MXFP4): 330 / 214 us. Four columns: 219 us
+// for MXFP4; FP8 spills. A lane owning 16 contiguous elements instead wrote
+// its 32 output bytes with two stores that each cover half of every 32-byte
+// sector, and the streamed halves reached HBM separately (30% more bytes
+// written): 365 / 239 us.
+constexpr int kWireColumnsFp8 = 2;
 constexpr int kWireColumnsMxfp4 = 2;
 
-// A wave per (token, row piece), as the combine: for each lane's units the
+// A wave per (token, row piece), as the combine: for each lane's groups the
 // token's contribution rows are all loaded (G at a time) before any is
 // decoded and added, summed in the token's rank order in FP32 from the
 // first, and rounded to nearest even once.
 template <int G, int C, int WIRE, int DT, bool kStream>
 __global__ __launch_bounds__(1024) void ep_combine_wire_kernel(WireCombineArgs a, TokenMap tk)
 {
-    constexpr int UE = kUnitElems;
+    constexpr int GE = kGroupElems;
     constexpr int aux = Policy<kStream>::combine_load;
     const int lane = threadIdx.x & (kWave - 1);
     // wave-uniform, so the token's rank search and its output row stay scalar
@@ -225,82 +228,77 @@ __global__ __launch_bounds__(1024) void ep_combine_wire_kernel(WireCombineArgs a
     const int32_t gl = lane < a.P ? a.fwd[tok * a.P + lane] : -1;
     const int n = __popcll(__ballot(gl >= 0));  // entries >= 0 form a prefix
 
-    const uint32_t out_bytes = (uint32_t)a.units * (UE * 2);
+    const uint32_t out_bytes = (uint32_t)a.units * 32u;  // 16 elements of 2 bytes a unit
     const __amdgpu_buffer_rsrc_t rdst = row_rsrc(a.out + tok * out_bytes, out_bytes);
-    const int ubeg = piece * a.piece_units;
-    const int uend = min(a.units, ubeg + a.piece_units);
-    // Scale rows are read once: lane l holds dword ubeg / 8 + l of each of the
-    // first G contribution rows (a dword covers 8 units), and a unit takes its
-    // row's scale from lane (u - ubeg) / 8. Re-reading the scales on every
-    // pass over the row fetched each scale line 7 times at H = 7168.
+    // the piece's 8-element groups; a scale dword covers 16 of them (128
+    // elements), and pieces start on a dword
+    const int hbeg = piece * a.piece_units * 2;
+    const int hend = min(a.units, (piece + 1) * a.piece_units) * 2;
+    // Scale rows are read once: lane l holds dword hbeg / 16 + l of each
+    // contribution row of the current group of G, and a code group takes its
+    // row's scale from lane (h - hbeg) / 16. A token of at most G rows loads
+    // them once; larger ones reload them for every group of rows. Reading the
+    // scale on every pass over the row fetched each scale line 7 times at
+    // H = 7168.
     uint32_t spre[G];
-    if (a.scale_pre) {
+    auto load_scales = [&](int i0) {
 #pragma unroll
         for (int q = 0; q < G; ++q) {
-            if (q < n) {
-                const int64_t gq = __builtin_amdgcn_readlane(gl, q);
+            if (i0 + q < n) {
+                const int64_t gq = __builtin_amdgcn_readlane(gl, i0 + q);
                 const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.ys + gq * a.scale_bytes, a.scale_bytes);
-                spre[q] = __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)(ubeg / 8 + lane) * 4u,
-                                                               0, aux);
+                const uint32_t off = (uint32_t)(hbeg / 16 + lane) * 4u;
+                if (WIRE == kWireFp8Block128 || a.scale_bytes % 4 == 0) {
+                    spre[q] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, aux);
+                } else {  // MXFP4 scale rows that are not whole dwords: by bytes
+                    uint32_t d = 0;
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        d |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, off + b, 0, aux)
+                             << (8 * b);
+                    spre[q] = d;
+                }
             }
         }
-    }
-    for (int u0 = ubeg + lane; u0 - lane < uend; u0 += kWave * C) {
-        float acc[C][UE];
+    };
+    const bool regroup = n > G;  // uniform
+    if (!regroup)
+        load_scales(0);
+    for (int h0 = hbeg + lane; h0 - lane < hend; h0 += kWave * C) {
+        float acc[C][GE];
         for (int i0 = 0; i0 < n; i0 += G) {
-            u32x4 raw[G][C];
-            uint32_t sc[G][C];
+            if (regroup)
+                load_scales(i0);
+            u32x2 raw[G][C];
 #pragma unroll
             for (int q = 0; q < G; ++q) {
 #pragma unroll
                 for (int c = 0; c < C; ++c) {
-                    const int u = u0 + c * kWave;
-                    if (i0 + q < n && u < uend) {
+                    const int h = h0 + c * kWave;
+                    if (i0 + q < n && h < hend) {
                         const int64_t gq = __builtin_amdgcn_readlane(gl, i0 + q);
                         const __amdgpu_buffer_rsrc_t ry =
                             row_rsrc(a.y + gq * a.row_bytes, a.row_bytes);
-                        if constexpr (WIRE == kWireFp8Block128) {
-                            raw[q][c] = bload16<aux>(ry, (uint32_t)u * 16u);
-                        } else {
-                            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(ry, u * 8, 0, aux);
-                            raw[q][c] = {v.x, v.y, 0u, 0u};
-                        }
-                        if (!a.scale_pre || i0 > 0) {
-                            const __amdgpu_buffer_rsrc_t rs =
-                                row_rsrc(a.ys + gq * a.scale_bytes, a.scale_bytes);
-                            if constexpr (WIRE == kWireFp8Block128)
-                                sc[q][c] = __builtin_amdgcn_raw_buffer_load_b32(rs, (u / 8) * 4, 0,
-                                                                                aux);
-                            else
-                                sc[q][c] = __builtin_amdgcn_raw_buffer_load_b8(rs, u / 2, 0, aux);
-                        }
-                    }
-                }
-            }
-            if (a.scale_pre && i0 == 0) {
-                // every lane takes part in the cross-lane reads
-#pragma unroll
-                for (int q = 0; q < G; ++q) {
-                    if (q < n) {
-#pragma unroll
-                        for (int c = 0; c < C; ++c) {
-                            const int u = u0 + c * kWave;
-                            const uint32_t d = (uint32_t)__shfl((int)spre[q], (u - ubeg) >> 3);
-                            // MXFP4: byte (u / 2) mod 4 of the dword
-                            sc[q][c] = WIRE == kWireFp8Block128 ? d : d >> (8 * ((u >> 1) & 3));
-                        }
+                        if constexpr (WIRE == kWireFp8Block128)
+                            raw[q][c] = __builtin_amdgcn_raw_buffer_load_b64(ry, h * 8, 0, aux);
+                        else
+                            raw[q][c] = {__builtin_amdgcn_raw_buffer_load_b32(ry, h * 4, 0, aux), 0u};
                     }
                 }
             }
 #pragma unroll
             for (int q = 0; q < G; ++q) {
-                if (i0 + q < n) {
+                if (i0 + q < n) {  // uniform: every lane takes part in the cross-lane reads
 #pragma unroll
                     for (int c = 0; c < C; ++c) {
-                        float f[UE];
-                        decode_unit<WIRE>(raw[q][c], sc[q][c], f);
+                        const int h = h0 + c * kWave;
+                        const uint32_t d = (uint32_t)__shfl((int)spre[q], (h - hbeg) >> 4);
+                        // MXFP4: byte (h / 4) mod 4 of the dword
+                        const uint32_t sb = WIRE == kWireFp8Block128 ? d : d >> (8 * ((h >> 2) & 3));
+                        float f[GE];
+                        decode_group<WIRE>(raw[q][c], sb, f);
 #pragma unroll
-                        for (int e = 0; e < UE; ++e)
+                        for (int e = 0; e < GE; ++e)
                             acc[c][e] = (i0 + q == 0) ? f[e] : acc[c][e] + f[e];
                     }
                 }
@@ -308,22 +306,15 @@ __global__ __launch_bounds__(1024) void ep_combine_wire_kernel(WireCombineArgs a
         }
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            const int u = u0 + c * kWave;
-            if (u < uend) {
+            const int h = h0 + c * kWave;
+            if (h < hend) {
                 if (n == 0) {
 #pragma unroll
-                    for (int e = 0; e < UE; ++e)
+                    for (int e = 0; e < GE; ++e)
                         acc[c][e] = 0.0f;
                 }
-#pragma unroll
-                for (int o = 0; o < UE / 8; ++o) {
-                    float f8[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        f8[e] = acc[c][8 * o + e];
-                    bstore16<Policy<kStream>::combine_store>(
-                        narrow<DT>(f8), rdst, (uint32_t)(u * (UE / 8) + o) * 16u);
-                }
+                bstore16<Policy<kStream>::combine_store>(narrow<DT>(acc[c]), rdst,
+                                                         (uint32_t)h * 16u);
             }
         }
     }

@@ -210,6 +210,17 @@ def test_wire_combine_shapes(name, W, k, H):
     run_wire_case(wl, name, with_weights=W % 2 == 0)
 
 
+@pytest.mark.parametrize("W,k,H", [(2, 2, 32), (3, 9, 160), (4, 16, 1184), (16, 24, 96)])
+def test_mxfp4_combine_scale_rows_not_whole_dwords(W, k, H):
+    """MXFP4 takes any H that is a multiple of 32: with H / 32 scale bytes a
+    row not a multiple of 4, the scale rows are read byte by byte; k > 8
+    rows a token also reloads them per group of rows."""
+    M = 40 if W <= 4 else 6
+    wl = workloads.custom(f"wire_mx_W{W}_k{k}_H{H}", W, M, H, k, max(k, W * 4), "bf16",
+                          ragged=True, seed_index=840 + W + k)
+    run_wire_case(wl, "mxfp4", with_weights=True)
+
+
 @pytest.mark.parametrize("launch", [dict(combine_waves=1, combine_row_split=3),
                                     dict(combine_waves=16, cache_policy=cra.EP_CACHE_STREAM),
                                     dict(combine_row_split=7, cache_policy=cra.EP_CACHE_KEEP)])
