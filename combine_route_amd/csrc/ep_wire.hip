@@ -68,6 +68,12 @@ __global__ __launch_bounds__(256) void ep_quantize_kernel(QuantizeArgs a)
 {
     constexpr int ld = Policy<kStream>::combine_load;
     constexpr int st = Policy<kStream>::combine_store;
+    // A chunk's scales are 16 bytes of a row's scale line, written by several
+    // waves: they stay cache-allocating so the L2 merges them into whole
+    // lines (streamed, they cost 10-13% of the kernel's time at 8 x 4096
+    // tokens, H = 7168; streaming the codes too, or loading through the
+    // caches, was slower).
+    constexpr int kScaleStore = 0;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t item = (int64_t)blockIdx.x * (blockDim.x / kWave) + uniform(threadIdx.x / kWave);
     const int64_t row = item / a.pieces;
@@ -109,7 +115,7 @@ __global__ __launch_bounds__(256) void ep_quantize_kernel(QuantizeArgs a)
                 __builtin_amdgcn_raw_buffer_store_b64(q, rout, (uint32_t)e, 0, st);
                 if ((lane & 15) == 0)
                     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, s), rsc,
-                                                          (uint32_t)(e / 128) * 4u, 0, st);
+                                                          (uint32_t)(e / 128) * 4u, 0, kScaleStore);
             }
         }
     } else {
@@ -135,7 +141,7 @@ __global__ __launch_bounds__(256) void ep_quantize_kernel(QuantizeArgs a)
                 __builtin_amdgcn_raw_buffer_store_b32(q, rout, (uint32_t)e / 2u, 0, st);
                 if ((lane & 3) == 0)
                     __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(E + 127), rsc, (uint32_t)e / 32u,
-                                                         0, st);
+                                                         0, kScaleStore);
             }
         }
     }
