@@ -38,6 +38,7 @@ KERNEL_SOURCES = [os.path.join(ROOT, "combine_route_amd", "csrc", f)
                             "ep_device.h", "ep_plan.cpp")]
 KERNELS = {"copy": "ep_copy_kernel", "combine": "ep_combine_kernel"}
 EXPERT_KERNELS = {"copy": "ex_copy_kernel", "combine": "ex_combine_kernel"}
+STANDARD_KERNELS = {"copy": "sx_copy_kernel", "combine": "sx_combine_kernel"}
 # counter summaries: label -> pattern over the demangled kernel name; the
 # copy kernel's last template argument says whether it casts to E4M3, and
 # the wire kernels name their wire in the template argument after the
@@ -47,6 +48,8 @@ COUNTER_KERNELS = {
     "ep_combine_kernel": r"ep_combine_kernel<",
     "ex_copy_kernel": r"ex_copy_kernel<",
     "ex_combine_kernel": r"ex_combine_kernel<",
+    "sx_copy_kernel": r"sx_copy_kernel<",
+    "sx_combine_kernel": r"sx_combine_kernel<",
     "ep_copy_kernel_cast": r"ep_copy_kernel<[^>]*, true>",
     "ep_quantize_kernel_fp8_block128": r"ep_quantize_kernel<1,",
     "ep_quantize_kernel_mxfp4": r"ep_quantize_kernel<2,",
@@ -222,6 +225,93 @@ def measure_expert_major(args, cra, torch, np, wl, op, inp, stream):
         "us_per_call": round(ms * 1e3, 2),
         "kernel_us": {k_: round(v * 1e3, 2) for k_, v in kern.items()},
         "check": check,
+        "roofline": roof,
+    }
+
+
+def standard_bytes(wl, N, pairs):
+    """Bytes the fused dispatch copy and fused combine must move, each read or
+    written once: N source tokens, `pairs` kept (token, expert) pairs."""
+    k = wl.topk
+    row = wl.hidden * (1 if wl.dispatch_dtype == "fp8" else 2)
+    crow = wl.hidden * 2
+    sb = wl.scale_dim * 4
+    # dispatch: each token's payload, scale row and ids read once; each kept
+    # pair's payload, scale row and source info written; the slot map written
+    copy = N * (row + sb + 4 * k) + pairs * (row + sb + 4) + N * k * 4
+    # combine: each kept pair's output read once; each token's row written;
+    # its ids, slot map and weights read
+    combine = pairs * crow + N * crow + N * k * 12
+    return {"copy": copy, "combine": combine}
+
+
+def measure_standard_moe(args, cra, torch, np, wl, op, inp, stream, x, idx, w, sc):
+    """The fused expert-major path (dispatch_standard_moe, combine_standard_moe,
+    weighted) against the two steps it replaces (dispatch, convert, weighted
+    inverse, combine): both timed, and the fused results checked bit for bit
+    against the two-step results on the same inputs."""
+    W, M, k, Er, H = wl.world_size, wl.max_tokens, wl.topk, wl.experts_per_rank, wl.hidden
+    ntok = inp["ntok"]
+    cap = op.expert_capacity
+    ex = op._expert_state()
+    if wl.dispatch_dtype == wl.combine_dtype:
+        py = ex["packed_x"]              # identity experts, in place
+    else:
+        g = torch.Generator(device="cuda").manual_seed(7)
+        py = torch.randn((W, Er, cap, H), generator=g, device="cuda").to(ex["y"].dtype)
+
+    def two_step():
+        op.dispatch(ntok, x, idx, w, sc, stream=stream)
+        op.convert_dispatch_output(op.out_x, op.out_indices, op.out_scales, op.out_weights,
+                                   stream=stream)
+        y = op.convert_combine_input(py, apply_weights=True, stream=stream)
+        op.combine(y, stream=stream)
+
+    def fused():
+        op.dispatch_standard_moe(x, None, sc, idx, num_tokens=ntok, stream=stream)
+        op.combine_standard_moe(py, w, idx, stream=stream)
+
+    two_step()
+    torch.cuda.synchronize()
+    ref = (op.combine_out.view(torch.int16).clone(), ex["packed_count"].clone(),
+           ex["packed_layout_range"].clone())
+    fused()
+    torch.cuda.synchronize()
+    ok = torch.equal(ex["packed_count"], ref[1]) and torch.equal(ex["packed_layout_range"], ref[2])
+    got = op.combine_out.view(torch.int16)
+    for r in range(W):
+        ok = ok and torch.equal(got[r, :ntok[r]], ref[0][r, :ntok[r]])
+    if not ok:
+        print("bench.py: the fused path differs from the two-step path", file=sys.stderr)
+        sys.exit(1)
+    del ref
+    ms_two = _timed(torch, stream, two_step, args.steps, args.warmup)
+    ms = _timed(torch, stream, fused, args.steps, args.warmup)
+    cra.ep_plan_set_timing(op.plan, True)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        fused()
+    torch.cuda.synchronize()
+    kern = {}
+    for name, kid in (("count", cra.EP_KERNEL_STANDARD_COUNT),
+                      ("scan", cra.EP_KERNEL_STANDARD_SCAN),
+                      ("copy", cra.EP_KERNEL_STANDARD_COPY),
+                      ("combine", cra.EP_KERNEL_STANDARD_COMBINE)):
+        c, t = cra.ep_plan_kernel_time(op.plan, kid)
+        kern[name] = t / max(c, 1)
+    cra.ep_plan_set_timing(op.plan, False)
+    cnt = ex["packed_count"].cpu().numpy()
+    pairs = int(np.minimum(cnt, cap).sum())
+    nb = standard_bytes(wl, int(sum(ntok)), pairs)
+    roof = {name: _roof(nb[name], kern[name], kname, wl.name, kname)
+            for name, kname in STANDARD_KERNELS.items()}
+    return {
+        "what": "dispatch_standard_moe + weighted combine_standard_moe",
+        "expert_capacity": cap, "kept_pairs": pairs,
+        "us_per_call": round(ms * 1e3, 2),
+        "two_step_us_per_call": round(ms_two * 1e3, 2),
+        "kernel_us": {k_: round(v * 1e3, 2) for k_, v in kern.items()},
+        "check": "bit-exact vs the two-step path (dispatch, convert, weighted inverse, combine)",
         "roofline": roof,
     }
 
@@ -669,6 +759,8 @@ def run(args):
     }
     if not args.no_expert:
         line["expert_major"] = measure_expert_major(args, cra, torch, np, wl, op, inp, stream)
+        line["standard_moe"] = measure_standard_moe(args, cra, torch, np, wl, op, inp, stream,
+                                                    x, idx, w, sc)
     if not args.no_wires:
         op.close()
         torch.cuda.empty_cache()

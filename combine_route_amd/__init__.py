@@ -26,6 +26,8 @@ EP_OK, EP_ERR_NULL, EP_ERR_ARG, EP_ERR_ALIGN, EP_ERR_SIZE, EP_ERR_STATE, EP_ERR_
 EP_KERNEL_ROUTE, EP_KERNEL_SCAN, EP_KERNEL_COPY, EP_KERNEL_COMBINE = 0, 1, 2, 3
 (EP_KERNEL_EXPERT_COUNT, EP_KERNEL_EXPERT_SCAN, EP_KERNEL_EXPERT_COPY,
  EP_KERNEL_EXPERT_COMBINE) = 4, 5, 6, 7
+(EP_KERNEL_STANDARD_COUNT, EP_KERNEL_STANDARD_SCAN, EP_KERNEL_STANDARD_COPY,
+ EP_KERNEL_STANDARD_COMBINE) = 8, 9, 10, 11
 EP_CACHE_AUTO, EP_CACHE_STREAM, EP_CACHE_KEEP = 0, 1, 2
 EP_LAYOUT_AUTO, EP_LAYOUT_KERNELS, EP_LAYOUT_SCAN_IN_COPY, EP_LAYOUT_IN_COPY = 0, 1, 2, 3
 
@@ -43,7 +45,8 @@ EXPORTED = ("ep_workspace_bytes", "ep_plan_create", "ep_plan_destroy", "ep_dispa
             "ep_combine", "ep_get_src_token_pos", "ep_last_error", "ep_plan_set_launch",
             "ep_plan_get_launch", "ep_plan_set_timing", "ep_plan_kernel_time",
             "ep_expert_workspace_bytes", "ep_expert_plan_create", "ep_expert_plan_destroy",
-            "ep_convert_dispatch_output", "ep_convert_combine_input", "ep_quantize_rows")
+            "ep_convert_dispatch_output", "ep_convert_combine_input", "ep_quantize_rows",
+            "ep_dispatch_standard_moe", "ep_combine_standard_moe")
 
 
 class EpConfig(ctypes.Structure):
@@ -81,6 +84,16 @@ class EpConvertDispatchArgs(ctypes.Structure):
 class EpConvertCombineArgs(ctypes.Structure):
     _fields_ = [("packed_y", ctypes.c_void_p), ("y", ctypes.c_void_p),
                 ("apply_weights", ctypes.c_int32)]
+
+
+class EpDispatchStandardArgs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "num_tokens", "x", "indices", "scales", "packed_x", "packed_scales", "packed_count",
+        "packed_src_info", "packed_layout_range")]
+
+
+class EpCombineStandardArgs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("packed_y", "indices", "weights", "out")]
 
 
 class EpError(RuntimeError):
@@ -121,6 +134,8 @@ def load():
     lib.ep_expert_plan_destroy.argtypes = [V]
     lib.ep_convert_dispatch_output.argtypes = [V, P(EpConvertDispatchArgs), V]
     lib.ep_convert_combine_input.argtypes = [V, P(EpConvertCombineArgs), V]
+    lib.ep_dispatch_standard_moe.argtypes = [V, P(EpDispatchStandardArgs), V]
+    lib.ep_combine_standard_moe.argtypes = [V, P(EpCombineStandardArgs), V]
     lib.ep_quantize_rows.argtypes = [V, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_int32, V, V, V, ctypes.c_int64, V]
     for name in EXPORTED:
@@ -417,6 +432,51 @@ def ep_convert_combine_input(eplan: int, cfg: EpConfig, cap: int, packed_y, y,
            load().ep_convert_combine_input(eplan, ctypes.byref(a), _stream(stream)))
 
 
+def _dispatch_standard_args(cfg: EpConfig, cap: int, num_tokens: Sequence[int], x, indices,
+                            scales, packed_x, packed_scales, packed_count, packed_src_info,
+                            packed_layout_range):
+    W, M, k, row, _, srow = _sizes(cfg)
+    Er = cfg.num_experts_per_rank
+    if len(num_tokens) != W:
+        raise ValueError(f"num_tokens has {len(num_tokens)} entries; world_size is {W}")
+    arr = (ctypes.c_int32 * W)(*[int(t) for t in num_tokens])
+    a = EpDispatchStandardArgs(
+        ctypes.addressof(arr), _dev(x, "x", W * M * row), _dev(indices, "indices", W * M * k * 4),
+        _dev(scales, "scales", W * M * srow), _dev(packed_x, "packed_x", W * Er * cap * row),
+        _dev(packed_scales, "packed_scales", W * Er * cap * srow),
+        _dev(packed_count, "packed_count", W * Er * 4),
+        _dev(packed_src_info, "packed_src_info", W * Er * cap * 4),
+        _dev(packed_layout_range, "packed_layout_range", W * Er * W * 8))
+    return a, arr
+
+
+def _combine_standard_args(cfg: EpConfig, cap: int, packed_y, indices, weights, out):
+    W, M, k, _, crow, _ = _sizes(cfg)
+    Er = cfg.num_experts_per_rank
+    return EpCombineStandardArgs(
+        _dev(packed_y, "packed_y", W * Er * cap * crow), _dev(indices, "indices", W * M * k * 4),
+        _dev(weights, "weights", W * M * k * 4), _dev(out, "out", W * M * crow))
+
+
+def ep_dispatch_standard_moe(eplan: int, cfg: EpConfig, cap: int, num_tokens, x, indices, scales,
+                             packed_x, packed_scales, packed_count, packed_src_info,
+                             packed_layout_range, stream=None) -> None:
+    """ep_dispatch_standard_moe(); tensors as in include/ep.h."""
+    a, arr = _dispatch_standard_args(cfg, cap, num_tokens, x, indices, scales, packed_x,
+                                     packed_scales, packed_count, packed_src_info,
+                                     packed_layout_range)
+    _check("ep_dispatch_standard_moe",
+           load().ep_dispatch_standard_moe(eplan, ctypes.byref(a), _stream(stream)))
+
+
+def ep_combine_standard_moe(eplan: int, cfg: EpConfig, cap: int, packed_y, indices, weights, out,
+                            stream=None) -> None:
+    """ep_combine_standard_moe(); tensors as in include/ep.h."""
+    a = _combine_standard_args(cfg, cap, packed_y, indices, weights, out)
+    _check("ep_combine_standard_moe",
+           load().ep_combine_standard_moe(eplan, ctypes.byref(a), _stream(stream)))
+
+
 _TORCH = {EP_BF16: torch.bfloat16, EP_FP16: torch.float16, EP_FP8_E4M3: torch.float8_e4m3fn}
 
 
@@ -573,6 +633,59 @@ class EpDispatchCombineOp:
         _check("ep_convert_combine_input", self._lib.ep_convert_combine_input(
             ex["plan"], ctypes.byref(a), _stream(stream, self._dev_index)))
         return ex["y"]
+
+    def dispatch_standard_moe(self, input, weights, scales, indices, num_tokens=None,
+                              stream=None):
+        """Dispatch straight into the expert-major layout ("MORI-EP User
+        Guide", section 4, dispatch_standard_moe): the same four results as
+        dispatch() followed by convert_dispatch_output(), without the 2-D
+        receive buffer. input [W, M, H] and indices [W, M, k] hold every
+        rank's tokens; num_tokens (default: M each) the tokens T_r of each
+        rank. weights is taken for the pages' argument order and is not part
+        of the layout: give it to combine_standard_moe to apply it."""
+        if weights is not None and (weights.dtype != torch.float32 or
+                                    tuple(weights.shape[-1:]) != (self.cfg.num_experts_per_token,)):
+            raise ValueError("weights must be float32 [W, M, k] or None")
+        ex = self._expert_state()
+        W, M = self.cfg.world_size, self.cfg.max_num_inp_token_per_rank
+        nt = tuple([M] * W if num_tokens is None else num_tokens)
+        given = (input, indices, scales)
+        c = ex.get("scache")
+        if c is None or c[1] != nt or not _same_tensors(c[0], given):
+            a, arr = _dispatch_standard_args(self.cfg, self.expert_capacity, nt, input, indices,
+                                             scales, ex["packed_x"], ex["packed_scales"],
+                                             ex["packed_count"], ex["packed_src_info"],
+                                             ex["packed_layout_range"])
+            c = ex["scache"] = (_hold(given), nt, a, arr)
+        _check("ep_dispatch_standard_moe", self._lib.ep_dispatch_standard_moe(
+            ex["plan"], ctypes.byref(c[2]), _stream(stream, self._dev_index)))
+        ex["ccache"] = None
+        px = ex["packed_x"] if ex["packed_scales"] is None else (ex["packed_x"],
+                                                                  ex["packed_scales"])
+        return px, ex["packed_count"], ex["packed_src_info"], ex["packed_layout_range"]
+
+    def combine_standard_moe(self, input, weights, indices, call_reset=False, stream=None):
+        """Combine straight from the expert-major layout ("MORI-EP User Guide",
+        section 4, combine_standard_moe): input [W, Er, cap, H] holds the
+        experts' outputs for the last dispatch_standard_moe, indices its ids;
+        weights [W, M, k] (or None for the plain sum) are applied as
+        convert_combine_input(apply_weights=True) would. The result equals
+        convert_combine_input() followed by combine(). call_reset is taken
+        for the pages' signature: nothing needs resetting. Returns [W, M, H]
+        (rows t < T_r written), a view of the op's combine output buffer."""
+        ex = self._ex
+        if ex is None:
+            raise EpError("ep_combine_standard_moe", EP_ERR_STATE,
+                          "combine_standard_moe before any dispatch_standard_moe")
+        given = (input, weights, indices)
+        c = ex.get("ccache")
+        if c is None or not _same_tensors(c[0], given):
+            a = _combine_standard_args(self.cfg, self.expert_capacity, input, indices, weights,
+                                       self.combine_out)
+            c = ex["ccache"] = (_hold(given), a)
+        _check("ep_combine_standard_moe", self._lib.ep_combine_standard_moe(
+            ex["plan"], ctypes.byref(c[1]), _stream(stream, self._dev_index)))
+        return self.combine_out
 
     def close(self):
         self._dcache = self._ccache = None

@@ -10,7 +10,9 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libcombine_route_amd.so")
-SOURCES = [os.path.join(PKG, "csrc", f) for f in ("ep_plan.cpp", "ep_kernels.hip", "ep_expert.hip", "ep_wire.hip")]
+SOURCES = [os.path.join(PKG, "csrc", f)
+           for f in ("ep_plan.cpp", "ep_kernels.hip", "ep_expert.hip", "ep_wire.hip",
+                     "ep_standard.hip")]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -202,5 +202,56 @@ __device__ __forceinline__ void fold_rows(const uint8_t* src, uint32_t row_bytes
     }
 }
 
+// Source rank of flat token `flat` (tokens of all ranks in rank order): a
+// binary search over the ranks' first flat tokens.
+__device__ __forceinline__ int rank_of_token(const TokenMap& tk, int flat)
+{
+    int lo = 0, hi = tk.W - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tk.tok_start[mid] <= flat)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// Ids of a row are read KC at a time (KC = min(KB, 16), so registers stay
+// bounded at any top-k): chunk c holds slots [c * KC, c * KC + KC), loaded at
+// addresses clamped into the row so every load issues before any is used;
+// slots past k are loaded but ignored.
+template <int KB>
+constexpr int id_chunk() { return KB < 16 ? KB : 16; }
+
+template <int KC>
+__device__ __forceinline__ void load_ids(const int32_t* row, int k, int c, int32_t (&ids)[KC])
+{
+#pragma unroll
+    for (int i = 0; i < KC; ++i)
+        ids[i] = row[min(c * KC + i, k - 1)];
+}
+
+// Word w of a row's set of local experts: bit b for local expert 64w + b.
+// An id is local when it lies in [lo, lo + Er).
+template <int KC>
+__device__ __forceinline__ uint64_t local_word(const int32_t* row, int k, bool valid, int64_t lo,
+                                               int Er, int w)
+{
+    uint64_t m = 0;
+    for (int c = 0; c * KC < k; ++c) {
+        int32_t ids[KC];
+        load_ids<KC>(row, k, c, ids);
+#pragma unroll
+        for (int i = 0; i < KC; ++i) {
+            const int64_t j = (int64_t)ids[i] - lo;
+            const int64_t b = j - 64 * w;
+            if (valid && c * KC + i < k && j >= 0 && j < Er && b >= 0 && b < 64)
+                m |= 1ull << b;
+        }
+    }
+    return m;
+}
+
 }  // namespace dev
 }  // namespace ep

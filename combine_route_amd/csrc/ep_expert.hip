@@ -38,42 +38,6 @@ constexpr int kExWaves = 4;  // count and scan: waves a block, one tile or list 
 // wrong count from reaching past the tiles.
 __device__ __forceinline__ int received(int recv, int rows) { return max(0, min(recv, rows)); }
 
-// Ids of a row are read KC at a time (KC = min(KB, 16), so registers stay
-// bounded at any top-k): chunk c holds slots [c * KC, c * KC + KC), loaded at
-// addresses clamped into the row so every load issues before any is used;
-// slots past k are loaded but ignored.
-template <int KB>
-constexpr int id_chunk() { return KB < 16 ? KB : 16; }
-
-template <int KC>
-__device__ __forceinline__ void load_ids(const int32_t* row, int k, int c, int32_t (&ids)[KC])
-{
-#pragma unroll
-    for (int i = 0; i < KC; ++i)
-        ids[i] = row[min(c * KC + i, k - 1)];
-}
-
-// Word w of a row's set of local experts: bit b for local expert 64w + b.
-// An id is local when it lies in [lo, lo + Er).
-template <int KC>
-__device__ __forceinline__ uint64_t local_word(const int32_t* row, int k, bool valid, int64_t lo,
-                                               int Er, int w)
-{
-    uint64_t m = 0;
-    for (int c = 0; c * KC < k; ++c) {
-        int32_t ids[KC];
-        load_ids<KC>(row, k, c, ids);
-#pragma unroll
-        for (int i = 0; i < KC; ++i) {
-            const int64_t j = (int64_t)ids[i] - lo;
-            const int64_t b = j - 64 * w;
-            if (valid && c * KC + i < k && j >= 0 && j < Er && b >= 0 && b < 64)
-                m |= 1ull << b;
-        }
-    }
-    return m;
-}
-
 __device__ __forceinline__ int source_rank(const ExpertArgs& a, int64_t row)
 {
     return min(max(a.src_pos[row] / a.WM, 0), a.W - 1);

@@ -132,6 +132,40 @@ struct ExpertCombineArgs {
     int32_t rows;                // most received rows any rank can hold in this call
 };
 
+// Fused expert-major dispatch and combine (ep_standard.hip): the source
+// tokens go straight to the packed rows, and the combine folds the packed
+// expert outputs straight into the token's output row.
+struct StandardArgs {
+    const uint8_t* x;            // [W][M][row_bytes] source tokens
+    const int32_t* idx;          // [W][M][k] their expert ids
+    const uint32_t* sc;          // [W][M][scale_dwords] or null
+    uint8_t* px;                 // [W * Er][cap][row_bytes]
+    uint32_t* psc;               // [W * Er][cap][scale_dwords] or null
+    int32_t* count;              // [W * Er] tokens naming each expert
+    int32_t* src_info;           // [W * Er][cap] source token index within its rank
+    int64_t* layout_range;       // [W * Er][W] (lo << 32) | n, clipped to cap
+    int32_t* tile_counts;        // [W * Er][W * Tr] tokens of (rank, tile) naming the expert
+    int32_t* tile_base;          // [W * Er][W * Tr] position of that tile's first one
+    int32_t* fslot;              // [W][M][k] packed row of a kept first-occurrence slot, else -1
+    int32_t row_vecs;            // 16-byte vectors per payload row
+    int32_t piece_vecs;          // vectors per row piece (one block)
+    int32_t scale_dwords;
+    int32_t W, M, k, Er, E, cap;
+    int32_t Tr;                  // tiles a source rank: max(1, ceil(M / 64))
+    int32_t ntok[kMaxRanks];     // T_r
+};
+
+struct StandardCombineArgs {
+    const uint8_t* py;           // [W * Er][cap][H] expert outputs, combine dtype
+    const int32_t* idx;          // [W][M][k]
+    const float* w;              // [W][M][k] routing weights to apply, or null
+    const int32_t* fslot;        // [W][M][k]
+    uint8_t* out;                // [W][M][H]
+    int32_t row_vecs;            // 16-byte vectors per row
+    int32_t piece_vecs;
+    int32_t M, k, Er, E;
+};
+
 // Quantized combine wire (ep_wire.hip).
 constexpr int kWireFp8Block128 = 1;  // E4M3 codes, one FP32 scale per 128 elements
 constexpr int kWireMxfp4 = 2;        // packed E2M1 codes, one E8M0 scale per 32
@@ -185,6 +219,12 @@ hipError_t launch_expert_copy(const ExpertArgs& a, int waves, int row_split, boo
 hipError_t launch_expert_combine(const ExpertCombineArgs& a, int W, int dtype, int waves,
                                  int row_split, bool stream, hipStream_t s);
 
+hipError_t launch_standard_count(const StandardArgs& a, hipStream_t s);
+hipError_t launch_standard_scan(const StandardArgs& a, hipStream_t s);
+hipError_t launch_standard_copy(const StandardArgs& a, int waves, int row_split, bool stream,
+                                hipStream_t s);
+hipError_t launch_standard_combine(const StandardCombineArgs& a, const TokenMap& tk, int dtype,
+                                   int waves, int row_split, bool stream, hipStream_t s);
 hipError_t launch_quantize(const QuantizeArgs& a, int wire, int dtype, bool stream, hipStream_t s);
 hipError_t launch_combine_wire(const WireCombineArgs& a, const TokenMap& tk, int wire, int dtype,
                                int waves, int row_split, bool stream, hipStream_t s);

@@ -67,19 +67,6 @@ __device__ __forceinline__ int rank_of_tile(const TileMap& tm, int g)
     return lo;
 }
 
-__device__ __forceinline__ int rank_of_token(const TokenMap& tk, int flat)
-{
-    int lo = 0, hi = tk.W - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (tk.tok_start[mid] <= flat)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    return lo;
-}
-
 // Destination ranks of one token (one lane). Expert e is on rank e / Er; an id
 // outside [0, E) selects none. With kList, the distinct ranks are written to
 // list[] in the order their first expert appears in the top-k row. KB >= k is

@@ -56,7 +56,7 @@ constexpr int kScanInCopyTiles = 256;
 constexpr int64_t kLayoutInCopyTokens = 256;
 constexpr size_t kPtrAlign = 16;
 constexpr int kTimerPool = 1024;
-constexpr int kTimedKernels = 8;  // EP_KERNEL_ROUTE .. EP_KERNEL_EXPERT_COMBINE
+constexpr int kTimedKernels = 12;  // EP_KERNEL_ROUTE .. EP_KERNEL_STANDARD_COMBINE
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -205,11 +205,14 @@ struct ep_plan {
 // Workspace of an expert plan of capacity cap: per-tile expert counts and
 // bases ([W * Er][T]), the first received row of each source rank ([W][W]),
 // the in-tile prefixes there ([W * Er][W]), the inverse's map and its weights
-// ([W][WM][Pe] each, Pe = min(k, Er)).
+// ([W][WM][Pe] each, Pe = min(k, Er)). The fused path uses the counts and
+// bases as [W * Er][W * Tr] and the map's space as its per-slot map
+// [W][M][k]; each region is sized for the larger use.
 struct ExShape {
     int32_t cap;
     int Pe;
-    int64_t T;  // tiles a rank can need: max(1, ceil(WM / 64))
+    int64_t T;   // tiles a rank can need: max(1, ceil(WM / 64))
+    int64_t Tr;  // fused path: tiles a source rank can need, max(1, ceil(M / 64))
     size_t off_counts, off_base, off_start, off_prefix, off_efwd, off_ew, total;
 };
 
@@ -217,6 +220,8 @@ struct ep_expert_plan {
     ep_plan* plan;
     ExShape e;
     uint8_t* ws;
+    bool fused = false;                // the map holds the last fused dispatch's
+    int32_t fused_ntok[ep::kMaxRanks] = {};
     bool converted = false;
     bool weighted = false;             // the conversion recorded expert weights
     uint64_t gen = 0;                  // the plan's dispatch that was converted
@@ -238,18 +243,21 @@ int expert_shape(const Shape& s, int32_t cap, ExShape* e)
     e->cap = cap;
     e->Pe = std::min(s.k, s.Er);
     e->T = std::max<int64_t>(1, (s.WM + ep::kWave - 1) / ep::kWave);
+    e->Tr = std::max<int64_t>(1, (s.M + ep::kWave - 1) / ep::kWave);
     const size_t lists = (size_t)s.W * (size_t)s.Er;
+    const size_t tiles = std::max((size_t)e->T, (size_t)s.W * (size_t)e->Tr);
     size_t off = 0;
     e->off_counts = off;
-    off = align_up(off + sizeof(int32_t) * lists * (size_t)e->T, kWorkspaceAlign);
+    off = align_up(off + sizeof(int32_t) * lists * tiles, kWorkspaceAlign);
     e->off_base = off;
-    off = align_up(off + sizeof(int32_t) * lists * (size_t)e->T, kWorkspaceAlign);
+    off = align_up(off + sizeof(int32_t) * lists * tiles, kWorkspaceAlign);
     e->off_start = off;
     off = align_up(off + sizeof(int32_t) * (size_t)s.W * (size_t)s.W, kWorkspaceAlign);
     e->off_prefix = off;
     off = align_up(off + sizeof(int32_t) * lists * (size_t)s.W, kWorkspaceAlign);
     e->off_efwd = off;
-    off = align_up(off + sizeof(int32_t) * (size_t)s.W * (size_t)s.WM * (size_t)e->Pe,
+    off = align_up(off + sizeof(int32_t) * std::max((size_t)s.W * (size_t)s.WM * (size_t)e->Pe,
+                                                    (size_t)s.W * (size_t)s.M * (size_t)s.k),
                    kWorkspaceAlign);
     e->off_ew = off;
     off = align_up(off + sizeof(float) * (size_t)s.W * (size_t)s.WM * (size_t)e->Pe,
@@ -288,6 +296,20 @@ int64_t expert_rows(const Shape& s, const int32_t* ntok)
 // 64-row tiles per rank of the expert-major layout (at least one, so the
 // counts and ranges are written even when nothing was received).
 int expert_tiles(int64_t rows) { return (int)std::max<int64_t>(1, (rows + ep::kWave - 1) / ep::kWave); }
+
+// Where each rank's tokens start in the flat list of all tokens.
+void token_map(const Shape& s, const int32_t* ntok, ep::TokenMap* tk)
+{
+    *tk = {};
+    tk->W = s.W;
+    int total = 0;
+    for (int r = 0; r < s.W; ++r) {
+        tk->tok_start[r] = total;
+        total += ntok[r];
+    }
+    tk->tok_start[s.W] = total;
+    tk->total = total;
+}
 
 int tiles_for(const int32_t* ntok, int W, int tt)
 {
@@ -710,15 +732,8 @@ int ep_combine(ep_plan_t* p, const ep_combine_args_t* a, void* stream_ptr)
     const ep_launch_t l = effective_launch(p, p->last_ntok);
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
 
-    ep::TokenMap tk = {};
-    tk.W = s.W;
-    int total = 0;
-    for (int r = 0; r < s.W; ++r) {
-        tk.tok_start[r] = total;
-        total += p->last_ntok[r];
-    }
-    tk.tok_start[s.W] = total;
-    tk.total = total;
+    ep::TokenMap tk;
+    token_map(s, p->last_ntok, &tk);
     const int dtype = p->cfg.combine_dtype == EP_BF16 ? 0 : 1;
     const bool streaming = l.cache_policy == EP_CACHE_STREAM;
 
@@ -1051,9 +1066,11 @@ int ep_convert_dispatch_output(ep_expert_plan_t* x, const ep_convert_dispatch_ar
     x->last_stream = stream;
     if (e != hipSuccess) {
         x->converted = false;
+        x->fused = false;
         return fail(EP_ERR_HIP, "convert_dispatch_output launch failed: %s", hipGetErrorString(e));
     }
     x->converted = true;
+    x->fused = false;
     x->weighted = a->weights != nullptr;
     x->gen = p->dispatch_gen;
     x->recv = a->recv_num_token;
@@ -1111,6 +1128,175 @@ int ep_convert_combine_input(ep_expert_plan_t* x, const ep_convert_combine_args_
     x->last_stream = stream;
     if (e != hipSuccess)
         return fail(EP_ERR_HIP, "convert_combine_input launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int ep_dispatch_standard_moe(ep_expert_plan_t* x, const ep_dispatch_standard_args_t* a,
+                             void* stream_ptr)
+{
+    if (!x)
+        return fail(EP_ERR_NULL, "plan is NULL");
+    if (!a)
+        return fail(EP_ERR_NULL, "args is NULL");
+    ep_plan* p = x->plan;
+    const Shape& s = p->s;
+    if (p->cfg.dispatch_cast != EP_CAST_NONE)
+        return fail(EP_ERR_ARG, "the fused dispatch copies rows as they are: the config's "
+                    "dispatch_cast must be EP_CAST_NONE");
+    if (!a->num_tokens)
+        return fail(EP_ERR_NULL, "args.num_tokens is NULL");
+    struct {
+        const void* ptr;
+        const char* name;
+        size_t align;
+    } req[] = {{a->x, "args.x", kPtrAlign},
+               {a->indices, "args.indices", 4},
+               {a->packed_x, "args.packed_x", kPtrAlign},
+               {a->packed_count, "args.packed_count", 4},
+               {a->packed_src_info, "args.packed_src_info", 4},
+               {a->packed_layout_range, "args.packed_layout_range", 8}};
+    for (auto& q : req) {
+        if (!q.ptr)
+            return fail(EP_ERR_NULL, "%s is NULL", q.name);
+        if (!aligned(q.ptr, q.align))
+            return fail(EP_ERR_ALIGN, "%s = %p is not %zu-byte aligned", q.name, q.ptr, q.align);
+    }
+    if (s.scale_bytes > 0) {
+        if (!a->scales || !a->packed_scales)
+            return fail(EP_ERR_NULL,
+                        "args.scales and args.packed_scales are required (scale_dim = %d)",
+                        p->cfg.scale_dim);
+        if (!aligned(a->scales, 4) || !aligned(a->packed_scales, 4))
+            return fail(EP_ERR_ALIGN, "args.scales / args.packed_scales are not 4-byte aligned");
+    } else if (a->scales || a->packed_scales) {
+        return fail(EP_ERR_ARG,
+                    "args.scales and args.packed_scales must be NULL when scale_dim = 0");
+    }
+    for (int r = 0; r < s.W; ++r)
+        if (a->num_tokens[r] < 0 || a->num_tokens[r] > s.M)
+            return fail(EP_ERR_ARG, "args.num_tokens[%d] = %d: must be in [0, %d]", r,
+                        a->num_tokens[r], s.M);
+    const ep_launch_t l = effective_launch(p, a->num_tokens);
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+
+    ep::StandardArgs sa;
+    sa.x = static_cast<const uint8_t*>(a->x);
+    sa.idx = a->indices;
+    sa.sc = static_cast<const uint32_t*>(a->scales);
+    sa.px = static_cast<uint8_t*>(a->packed_x);
+    sa.psc = static_cast<uint32_t*>(a->packed_scales);
+    sa.count = a->packed_count;
+    sa.src_info = a->packed_src_info;
+    sa.layout_range = a->packed_layout_range;
+    sa.tile_counts = reinterpret_cast<int32_t*>(x->ws + x->e.off_counts);
+    sa.tile_base = reinterpret_cast<int32_t*>(x->ws + x->e.off_base);
+    sa.fslot = reinterpret_cast<int32_t*>(x->ws + x->e.off_efwd);
+    sa.row_vecs = (int32_t)(s.row_bytes / 16);
+    sa.scale_dwords = (int32_t)(s.scale_bytes / 4);
+    sa.W = s.W;
+    sa.M = s.M;
+    sa.k = s.k;
+    sa.Er = s.Er;
+    sa.E = (int32_t)s.E;
+    sa.cap = x->e.cap;
+    sa.Tr = (int32_t)x->e.Tr;
+    for (int r = 0; r < ep::kMaxRanks; ++r)
+        sa.ntok[r] = r < s.W ? a->num_tokens[r] : 0;
+    // row pieces until the copy grid has about 1024 blocks, unless overridden
+    int split = l.expert_row_split;
+    if (p->launch.expert_row_split <= 0) {
+        int tiles = 0;
+        for (int r = 0; r < s.W; ++r)
+            tiles += (a->num_tokens[r] + ep::kWave - 1) / ep::kWave;
+        const int max_split = std::max(1, sa.row_vecs / ep::kWave);
+        split = std::min(max_split, std::max(1, (1024 + tiles - 1) / std::max(1, tiles)));
+    }
+    sa.piece_vecs = (sa.row_vecs + split - 1) / split;
+    const int row_split = (sa.row_vecs + sa.piece_vecs - 1) / sa.piece_vecs;
+
+    hipError_t e = timed(p, EP_KERNEL_STANDARD_COUNT, stream,
+                         [&] { return ep::launch_standard_count(sa, stream); });
+    if (e == hipSuccess)
+        e = timed(p, EP_KERNEL_STANDARD_SCAN, stream,
+                  [&] { return ep::launch_standard_scan(sa, stream); });
+    if (e == hipSuccess)
+        e = timed(p, EP_KERNEL_STANDARD_COPY, stream, [&] {
+            return ep::launch_standard_copy(sa, l.expert_waves, row_split,
+                                            l.expert_cache_policy == EP_CACHE_STREAM, stream);
+        });
+    x->launched = true;
+    x->last_stream = stream;
+    // the map's space now holds the fused map: no conversion is current
+    x->converted = false;
+    if (e != hipSuccess) {
+        x->fused = false;
+        return fail(EP_ERR_HIP, "dispatch_standard_moe launch failed: %s", hipGetErrorString(e));
+    }
+    x->fused = true;
+    for (int r = 0; r < ep::kMaxRanks; ++r)
+        x->fused_ntok[r] = r < s.W ? a->num_tokens[r] : 0;
+    return ok();
+}
+
+int ep_combine_standard_moe(ep_expert_plan_t* x, const ep_combine_standard_args_t* a,
+                            void* stream_ptr)
+{
+    if (!x)
+        return fail(EP_ERR_NULL, "plan is NULL");
+    if (!a)
+        return fail(EP_ERR_NULL, "args is NULL");
+    ep_plan* p = x->plan;
+    const Shape& s = p->s;
+    if (p->cfg.combine_wire != EP_WIRE_NONE)
+        return fail(EP_ERR_ARG, "the fused combine reads combine_dtype rows: the config's "
+                    "combine_wire must be EP_WIRE_NONE");
+    if (!a->packed_y)
+        return fail(EP_ERR_NULL, "args.packed_y is NULL");
+    if (!a->indices)
+        return fail(EP_ERR_NULL, "args.indices is NULL");
+    if (!a->out)
+        return fail(EP_ERR_NULL, "args.out is NULL");
+    if (!aligned(a->packed_y, kPtrAlign) || !aligned(a->out, kPtrAlign))
+        return fail(EP_ERR_ALIGN, "args.packed_y / args.out are not 16-byte aligned");
+    if (!aligned(a->indices, 4) || (a->weights && !aligned(a->weights, 4)))
+        return fail(EP_ERR_ALIGN, "args.indices / args.weights are not 4-byte aligned");
+    if (!x->fused)
+        return fail(EP_ERR_STATE, "combine_standard_moe before any dispatch_standard_moe on "
+                    "this expert plan (or a convert_dispatch_output came since)");
+    const ep_launch_t l = effective_launch(p, x->fused_ntok);
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+
+    ep::StandardCombineArgs ca;
+    ca.py = static_cast<const uint8_t*>(a->packed_y);
+    ca.idx = a->indices;
+    ca.w = a->weights;
+    ca.fslot = reinterpret_cast<const int32_t*>(x->ws + x->e.off_efwd);
+    ca.out = static_cast<uint8_t*>(a->out);
+    ca.row_vecs = (int32_t)(s.crow_bytes / 16);
+    ca.M = s.M;
+    ca.k = s.k;
+    ca.Er = s.Er;
+    ca.E = (int32_t)s.E;
+    ep::TokenMap tk;
+    token_map(s, x->fused_ntok, &tk);
+    int split = l.expert_combine_row_split;
+    if (p->launch.expert_combine_row_split <= 0) {
+        const int64_t blocks = std::max<int64_t>(1, ((int64_t)tk.total + 3) / 4);
+        const int max_split = std::max(1, ca.row_vecs / ep::kWave);
+        split = (int)std::min<int64_t>(max_split, std::max<int64_t>(1, (1024 + blocks - 1) / blocks));
+    }
+    ca.piece_vecs = (ca.row_vecs + split - 1) / split;
+    const int row_split = (ca.row_vecs + ca.piece_vecs - 1) / ca.piece_vecs;
+    const int dtype = p->cfg.combine_dtype == EP_BF16 ? 0 : 1;
+
+    const hipError_t e = timed(p, EP_KERNEL_STANDARD_COMBINE, stream, [&] {
+        return ep::launch_standard_combine(ca, tk, dtype, l.expert_combine_waves, row_split,
+                                           l.expert_cache_policy == EP_CACHE_STREAM, stream);
+    });
+    x->launched = true;
+    x->last_stream = stream;
+    if (e != hipSuccess)
+        return fail(EP_ERR_HIP, "combine_standard_moe launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 

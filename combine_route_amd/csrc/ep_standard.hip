@@ -1,0 +1,584 @@
+// gfx950 (MI355X, CDNA4) kernels of the fused expert-major path ("MORI-EP
+// User Guide", section 4 "Standard MoE Compatibility (DeepEP)":
+// dispatch_standard_moe, dispatch and layout conversion in one call;
+// combine_standard_moe, the combine from the expert-major layout).
+//
+// The fused dispatch gives every (token, distinct expert) pair the packed row
+// that convert_dispatch_output gives it after a dispatch: an expert's list
+// keeps the receive order, which is source rank, then source token. Here the
+// lists are counting-sorted straight over the source tokens, with the same
+// deterministic scheme: a 64-lane ballot per expert over a tile of 64 tokens
+// of one source rank, an exclusive scan per expert over (source rank, tile),
+// and the ballot prefix inside a tile. A source rank starts a new tile, so a
+// layout range is read off the tile bases.
+//   count    a wave per (source rank, tile): how many of its tokens name each
+//            expert.
+//   scan     a wave per expert: tile bases, the expert's row count, and its
+//            layout range for every source rank.
+//   copy     a block per (source rank, tile, row piece): wave 0 works out the
+//            kept packed row of every (token, expert) pair into LDS and the
+//            per-slot map the combine reads; then every wave loads a token's
+//            row piece once (16 B a lane) and stores it to each kept packed
+//            row; piece-0 blocks also write the scale rows and source info.
+//   combine  a wave per (token, row piece): the result of
+//            convert_combine_input followed by the combine, without the
+//            intermediate rows. For each of the token's ranks in its rank
+//            order: the FP32 fold of the rank's kept expert outputs (in
+//            first-occurrence order, weighted or not), rounded to the combine
+//            type as the intermediate row would be; those are summed in FP32
+//            from the first and rounded once. A rank whose pairs were all
+//            dropped adds +0, as its intermediate row would.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ep_device.h"
+#include "ep_kernels.h"
+
+namespace ep {
+namespace {
+
+using namespace dev;
+
+constexpr int kSxWaves = 4;  // count and scan: waves a block, one tile or list each
+
+// Tokens of source rank r in this call.
+__device__ __forceinline__ int tokens_of(const StandardArgs& a, int r)
+{
+    return max(0, min(a.ntok[r], a.M));
+}
+
+template <int KB>
+__global__ __launch_bounds__(kSxWaves * kWave) void sx_count_kernel(StandardArgs a)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int tile = blockIdx.x * kSxWaves + uniform(threadIdx.x / kWave);
+    const int r = blockIdx.y;
+    if (tile >= a.Tr)
+        return;  // whole waves
+    const int T = tokens_of(a, r);
+    const int q = tile * kWave + lane;
+    const bool valid = q < T;
+    const int64_t TT = (int64_t)a.W * a.Tr;
+    int32_t* counts = a.tile_counts + (int64_t)r * a.Tr + tile;  // expert e at [e * TT]
+    if (tile * kWave >= T) {  // no token here
+        for (int e = lane; e < a.E; e += kWave)
+            counts[(int64_t)e * TT] = 0;
+        return;
+    }
+    constexpr int KC = id_chunk<KB>();
+    const int32_t* ids = a.idx + ((int64_t)r * a.M + (valid ? q : 0)) * a.k;
+    for (int w = 0; 64 * w < a.E; ++w) {
+        const uint64_t m = local_word<KC>(ids, a.k, valid, 0, a.E, w);
+        const int nj = min(kWave, a.E - 64 * w);
+        int c = 0;
+        for (int jj = 0; jj < nj; ++jj) {
+            const uint64_t b = __ballot((m >> jj) & 1);
+            if (lane == jj)
+                c = __popcll(b);
+        }
+        if (lane < nj)
+            counts[(int64_t)(64 * w + lane) * TT] = c;
+    }
+}
+
+__global__ __launch_bounds__(kSxWaves * kWave) void sx_scan_kernel(StandardArgs a)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t g = (int64_t)blockIdx.x * kSxWaves + uniform(threadIdx.x / kWave);
+    if (g >= a.E)
+        return;  // whole waves
+    const int TT = a.W * a.Tr;
+    const int32_t* cnt = a.tile_counts + g * TT;
+    int32_t* base = a.tile_base + g * TT;
+    // lane s < W: source rank s's first tile; its base is where s's rows start
+    const int start_tile = lane < a.W ? lane * a.Tr : TT;
+    int start = 0, carry = 0;
+    for (int c0 = 0; c0 < TT; c0 += kWave) {
+        const int t = c0 + lane;
+        const int v = t < TT ? cnt[t] : 0;
+        int inc = v;  // inclusive prefix over the wave
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int u = __shfl_up(inc, o);
+            if (lane >= o)
+                inc += u;
+        }
+        const int excl = carry + inc - v;
+        if (t < TT)
+            base[t] = excl;
+        const int at = __shfl(excl, (start_tile - c0) & (kWave - 1));
+        if (start_tile >= c0 && start_tile < c0 + kWave)
+            start = at;
+        carry += __shfl(inc, kWave - 1);
+    }
+    if (lane == 0)
+        a.count[g] = carry;
+    int next = __shfl_down(start, 1);
+    if (lane == a.W - 1)
+        next = carry;
+    if (lane < a.W) {
+        const int64_t lo = min(start, a.cap);
+        const int64_t hi = min(next, a.cap);
+        a.layout_range[g * a.W + lane] = (lo << 32) | (hi - lo);
+    }
+}
+
+template <int VPL, int KB, bool kStream>
+__global__ __launch_bounds__(1024) void sx_copy_kernel(StandardArgs a)
+{
+    __shared__ int32_t s_e[kWave][KB];  // a token's distinct experts, first-occurrence order
+    __shared__ int32_t s_p[kWave][KB];  // their positions, then the kept packed rows
+    __shared__ int8_t s_u[kWave][KB];   // each slot's index into s_e; -1: invalid or a repeat
+    __shared__ int32_t s_n[kWave];      // kept packed rows of the token
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = uniform(threadIdx.x / kWave);
+    const int nwaves = blockDim.x / kWave;
+    const int tile = blockIdx.x;
+    const int piece = blockIdx.y;
+    const int r = blockIdx.z;
+    const int q0 = tile * kWave;
+    const int cnt = min(kWave, tokens_of(a, r) - q0);
+    if (cnt <= 0)
+        return;  // the whole block
+    const int64_t row0 = (int64_t)r * a.M + q0;
+    const int64_t TT = (int64_t)a.W * a.Tr;
+
+    // This wave's items: tokens wave, wave + nwaves, ... of the tile, each cut
+    // into nch chunks of its row piece [vbeg, vend).
+    const uint32_t row_bytes = (uint32_t)a.row_vecs * 16u;
+    const int vbeg = piece * a.piece_vecs;
+    const int vend = min(a.row_vecs, vbeg + a.piece_vecs);
+    const int nch = (vend - vbeg + kWave * VPL - 1) / (kWave * VPL);
+    const int items = (wave < cnt ? (cnt - wave + nwaves - 1) / nwaves : 0) * nch;
+    auto load_item = [&](int it, u32x4 (&v)[VPL]) {
+        const int t = wave + (it / nch) * nwaves;
+        const int v0 = vbeg + (it % nch) * kWave * VPL;
+        const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.x + (row0 + t) * row_bytes, row_bytes);
+#pragma unroll
+        for (int u = 0; u < VPL; ++u) {
+            const int vv = v0 + u * kWave + lane;
+            if (vv < vend)
+                v[u] = bload16<Policy<kStream>::copy_load>(rs, (uint32_t)vv * 16u);
+        }
+    };
+    auto store_item = [&](int it, const u32x4 (&v)[VPL]) {
+        const int t = wave + (it / nch) * nwaves;
+        const int v0 = vbeg + (it % nch) * kWave * VPL;
+        const int n = uniform(s_n[t]);
+        for (int i = 0; i < n; ++i) {
+            const int64_t gi = uniform(s_p[t][i]);
+            const __amdgpu_buffer_rsrc_t rd = row_rsrc(a.px + gi * row_bytes, row_bytes);
+#pragma unroll
+            for (int u = 0; u < VPL; ++u) {
+                const int vv = v0 + u * kWave + lane;
+                if (vv < vend)
+                    bstore16<Policy<kStream>::copy_store>(v[u], rd, (uint32_t)vv * 16u);
+            }
+        }
+    };
+    // Small pieces (small rows or small calls, where time is latency): each
+    // wave's first item loads while wave 0 routes the tile.
+    u32x4 A[VPL], B[VPL];
+    if (VPL < 8 && items > 0)
+        load_item(0, A);
+
+    if (wave == 0) {
+        const bool valid = lane < cnt;
+        constexpr int KC = id_chunk<KB>();
+        const int64_t rowq = row0 + (valid ? lane : 0);
+        const int32_t* ids = a.idx + rowq * a.k;
+        // the token's distinct experts in first-occurrence order; with one
+        // mask word (E <= 64) repeats are found in a register, else in LDS
+        int n = 0;
+        uint64_t seen = 0;
+        for (int c = 0; c * KC < a.k; ++c) {
+            int32_t id[KC];
+            load_ids<KC>(ids, a.k, c, id);
+#pragma unroll
+            for (int i = 0; i < KC; ++i) {
+                const int slot = c * KC + i;
+                if (slot >= a.k)
+                    continue;
+                int u = -1;
+                const int e = id[i];
+                if (valid && e >= 0 && e < a.E) {
+                    bool dup;
+                    if (a.E <= kWave) {
+                        dup = (seen >> e) & 1;
+                        seen |= 1ull << e;
+                    } else {
+                        dup = false;
+                        for (int v = 0; v < n; ++v)
+                            dup = dup || s_e[lane][v] == e;
+                    }
+                    if (!dup) {
+                        u = n;
+                        s_e[lane][n++] = e;
+                    }
+                }
+                s_u[lane][slot] = (int8_t)u;
+            }
+        }
+        int n_max = n;  // the wave's longest list
+#pragma unroll
+        for (int off = kWave / 2; off > 0; off >>= 1)
+            n_max = max(n_max, __shfl_xor(n_max, off));
+        // Positions, one mask word (64 experts) at a time: lane jj holds the
+        // ballot of expert 64w + jj over the tile and its tile base; each
+        // lane fetches both for its own entries with cross-lane reads.
+        for (int w = 0; 64 * w < a.E; ++w) {
+            const uint64_t m = a.E <= kWave ? seen : local_word<KC>(ids, a.k, valid, 0, a.E, w);
+            const int nj = min(kWave, a.E - 64 * w);
+            const int bw =
+                lane < nj ? a.tile_base[(int64_t)(64 * w + lane) * TT + (int64_t)r * a.Tr + tile]
+                          : 0;
+            uint64_t mine = 0;
+            for (int jj = 0; jj < nj; ++jj) {
+                const uint64_t b = __ballot((m >> jj) & 1);
+                if (lane == jj)
+                    mine = b;
+            }
+            const int mlo = (int)(uint32_t)mine;
+            const int mhi = (int)(uint32_t)(mine >> 32);
+            for (int u = 0; u < n_max; ++u) {
+                const int j = u < n ? s_e[lane][u] - 64 * w : -1;
+                const int src = j & (kWave - 1);
+                const uint32_t blo = (uint32_t)__shfl(mlo, src);
+                const uint32_t bhi = (uint32_t)__shfl(mhi, src);
+                const int base = __shfl(bw, src);
+                if (j >= 0 && j < kWave)
+                    s_p[lane][u] = base + lanes_below(((uint64_t)bhi << 32) | blo);
+            }
+        }
+        // the combine's map: the packed row of each slot that is its expert's
+        // first occurrence and was kept, else -1
+        if (valid) {
+            for (int slot = 0; slot < a.k; ++slot) {
+                const int u = s_u[lane][slot];
+                const int p = u >= 0 ? s_p[lane][u] : a.cap;
+                a.fslot[rowq * a.k + slot] = p < a.cap ? s_e[lane][u] * a.cap + p : -1;
+            }
+        }
+        int kept = 0;  // positions past the capacity are dropped
+        for (int u = 0; u < n; ++u) {
+            const int p = s_p[lane][u];
+            if (p < a.cap)
+                s_p[lane][kept++] = s_e[lane][u] * a.cap + p;
+        }
+        s_n[lane] = kept;
+    }
+    __syncthreads();
+
+    const int sd = a.scale_dwords;
+    if (piece == 0) {
+        for (int t = wave; t < cnt; t += nwaves) {
+            const int n = uniform(s_n[t]);
+            if (lane < n)
+                a.src_info[s_p[t][lane]] = q0 + t;
+            for (int c0 = 0; n > 0 && c0 < sd; c0 += kWave) {
+                const int c = c0 + lane;
+                const uint32_t v = c < sd ? a.sc[(row0 + t) * sd + c] : 0u;
+                for (int i = 0; i < n; ++i) {
+                    const int64_t gi = uniform(s_p[t][i]);
+                    if (c < sd)
+                        a.psc[gi * sd + c] = v;
+                }
+            }
+        }
+    }
+
+    if constexpr (VPL < 8) {
+        // two items in flight: item i + 1 loads while item i stores
+        for (int it = 0; it < items; it += 2) {
+            if (it + 1 < items)
+                load_item(it + 1, B);
+            store_item(it, A);
+            if (it + 1 < items) {
+                if (it + 2 < items)
+                    load_item(it + 2, A);
+                store_item(it + 1, B);
+            }
+        }
+    } else {
+        // large pieces (throughput): one chunk a wave in flight
+        for (int it = 0; it < items; ++it) {
+            if (uniform(s_n[wave + (it / nch) * nwaves]) == 0)
+                continue;  // a token without a kept expert is not read
+            load_item(it, A);
+            store_item(it, A);
+        }
+    }
+}
+
+// Fold-position flags of a kept pair: the first or last kept pair of its
+// rank, and whether ranks without a kept pair come just before its rank.
+constexpr int kFoldFirst = 1;
+constexpr int kFoldLast = 2;
+constexpr int kFoldGap = 4;
+
+template <int G, int U, int DT, bool kStream, bool kWeighted>
+__global__ __launch_bounds__(1024) void sx_combine_kernel(StandardCombineArgs a, TokenMap tk)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int flat = blockIdx.x * (blockDim.x / kWave) + uniform(threadIdx.x / kWave);
+    if (flat >= tk.total)
+        return;  // whole waves only
+    const int piece = blockIdx.y;
+    const int r = rank_of_token(tk, flat);
+    const int64_t tok = (int64_t)r * a.M + (flat - tk.tok_start[r]);
+
+    // Lane j < k holds slot j of the token.
+    const bool has = lane < a.k;
+    const int32_t id = has ? a.idx[tok * a.k + lane] : -1;
+    const bool valid = has && id >= 0 && id < a.E;
+    const int32_t fs = has ? a.fslot[tok * a.k + lane] : -1;
+    const bool kept = fs >= 0;
+    const int rk = valid ? id / a.Er : -1;
+    float c = 0.0f;
+    if constexpr (kWeighted)
+        c = has ? a.w[tok * a.k + lane] : 0.0f;
+    // Each slot's rank: whether it is the rank's first slot (the token's rank
+    // order is the order of those), and which lane is. Weighted, a kept slot
+    // (its expert's first) sums the weights of every slot naming its expert,
+    // in slot order.
+    bool rfirst = valid;
+    int rsrc = lane;
+    const float cw_own = c;
+    for (int j = 0; j < a.k; ++j) {
+        const int rj = __builtin_amdgcn_readlane(rk, j);
+        if (rfirst && j < lane && rj == rk) {
+            rfirst = false;
+            rsrc = j;
+        }
+        if constexpr (kWeighted) {
+            const int ij = __builtin_amdgcn_readlane(id, j);
+            const float wj = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cw_own), j));
+            if (j > lane && ij == id)
+                c = c + wj;
+        }
+    }
+    const uint64_t dmask = __ballot(rfirst);
+    const int nD = __popcll(dmask);
+    const int dix = __shfl(lanes_below(dmask), rsrc);  // the slot's rank's place in the order
+    // Kept pairs in fold order (by rank place, then slot); lane s < nk then
+    // holds the s-th: its packed row, weight and rank place.
+    const uint64_t kmask = __ballot(kept);
+    const int nk = __popcll(kmask);
+    int pos = 0, src = 0;
+    for (int j = 0; j < a.k; ++j) {
+        const int dj = __builtin_amdgcn_readlane(dix, j);
+        if (((kmask >> j) & 1) && (dj < dix || (dj == dix && j < lane)))
+            ++pos;
+    }
+    for (int j = 0; j < a.k; ++j) {
+        const int pj = __builtin_amdgcn_readlane(pos, j);
+        if (((kmask >> j) & 1) && pj == lane)
+            src = j;
+    }
+    // every lane takes part in the cross-lane reads: one from an inactive
+    // lane returns 0, and a sequence position can read a slot lane >= nk
+    const int32_t gsrc = __shfl(fs, src);
+    const int32_t gl = lane < nk ? gsrc : -1;
+    const float gw = __shfl(c, src);
+    const int dx = __shfl(dix, src);
+    const int dprev = __shfl_up(dx, 1);
+    const int dnext = __shfl_down(dx, 1);
+    int flags = 0;
+    if (lane < nk) {
+        const int pv = lane == 0 ? -1 : dprev;
+        const bool last = lane == nk - 1 || dnext != dx;
+        flags = (pv != dx ? kFoldFirst : 0) | (last ? kFoldLast : 0) | (dx - pv > 1 ? kFoldGap : 0);
+    }
+    const int dlast = nk > 0 ? __builtin_amdgcn_readlane(dx, nk - 1) : -1;
+    const bool trailing = nD - 1 > dlast;  // ranks without a kept pair after the last
+
+    const uint32_t row_bytes = (uint32_t)a.row_vecs * 16u;
+    const __amdgpu_buffer_rsrc_t rdst = row_rsrc(a.out + tok * row_bytes, row_bytes);
+    const int vbeg = piece * a.piece_vecs;
+    const int vend = min(a.row_vecs, vbeg + a.piece_vecs);
+    for (int v0 = vbeg; v0 < vend; v0 += kWave * U) {
+        float tot[U][8], part[U][8];
+        bool have = false;  // uniform: tot holds a rank's contribution
+        for (int i0 = 0; i0 < nk; i0 += G) {
+            u32x4 rows[U][G];
+#pragma unroll
+            for (int q = 0; q < G; ++q) {
+                if (i0 + q < nk) {
+                    const int64_t gq = __builtin_amdgcn_readlane(gl, i0 + q);
+                    const __amdgpu_buffer_rsrc_t ry = row_rsrc(a.py + gq * row_bytes, row_bytes);
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int v = v0 + u * kWave + lane;
+                        if (v < vend)
+                            rows[u][q] = bload16<Policy<kStream>::combine_load>(
+                                ry, (uint32_t)v * 16u);
+                    }
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < G; ++q) {
+                if (i0 + q < nk) {
+                    const int fl = __builtin_amdgcn_readlane(flags, i0 + q);
+                    const float cq =
+                        kWeighted ? __builtin_bit_cast(
+                                        float, __builtin_amdgcn_readlane(
+                                                   __builtin_bit_cast(int, gw), i0 + q))
+                                  : 1.0f;
+                    const bool gap = fl & kFoldGap;
+                    const bool first = fl & kFoldFirst;
+                    const bool last = fl & kFoldLast;
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        float f[8];
+                        widen<DT>(rows[u][q], f);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            if (gap)  // ranks whose intermediate rows are +0
+                                tot[u][e] = have ? tot[u][e] + 0.0f : 0.0f;
+                            if (kWeighted)
+                                part[u][e] = first ? cq * f[e] : __builtin_fmaf(cq, f[e], part[u][e]);
+                            else
+                                part[u][e] = first ? f[e] : part[u][e] + f[e];
+                        }
+                        if (last) {
+                            // the rank's intermediate row: rounded to the combine type
+                            float p[8];
+                            widen<DT>(narrow<DT>(part[u]), p);
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                tot[u][e] = (have || gap) ? tot[u][e] + p[e] : p[e];
+                        }
+                    }
+                    have = have || gap || last;
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = v0 + u * kWave + lane;
+            if (v < vend) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    if (!have)
+                        tot[u][e] = 0.0f;  // no rank, or none with a kept pair
+                    else if (trailing)
+                        tot[u][e] = tot[u][e] + 0.0f;
+                }
+                bstore16<Policy<kStream>::combine_store>(narrow<DT>(tot[u]), rdst,
+                                                         (uint32_t)v * 16u);
+            }
+        }
+    }
+}
+
+// Top-k bucket: the smallest of 8, 16, 32, 64 >= k.
+int sx_bucket(int k) { return k <= 8 ? 8 : k <= 16 ? 16 : k <= 32 ? 32 : 64; }
+
+template <int VPL, int KB>
+hipError_t sx_copy_with(const StandardArgs& a, dim3 grid, dim3 block, bool stream, hipStream_t s)
+{
+    if (stream)
+        hipLaunchKernelGGL((sx_copy_kernel<VPL, KB, true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((sx_copy_kernel<VPL, KB, false>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+template <int VPL>
+hipError_t sx_copy_with_vpl(const StandardArgs& a, dim3 grid, dim3 block, bool stream,
+                            hipStream_t s)
+{
+    switch (sx_bucket(a.k)) {
+    case 8: return sx_copy_with<VPL, 8>(a, grid, block, stream, s);
+    case 16: return sx_copy_with<VPL, 16>(a, grid, block, stream, s);
+    case 32: return sx_copy_with<VPL, 32>(a, grid, block, stream, s);
+    default: return sx_copy_with<VPL, 64>(a, grid, block, stream, s);
+    }
+}
+
+template <int G, int U, int DT, bool kStream>
+void sx_combine_launch(const StandardCombineArgs& a, const TokenMap& tk, dim3 grid, dim3 block,
+                       hipStream_t s)
+{
+    if (a.w)
+        hipLaunchKernelGGL((sx_combine_kernel<G, U, DT, kStream, true>), grid, block, 0, s, a, tk);
+    else
+        hipLaunchKernelGGL((sx_combine_kernel<G, U, DT, kStream, false>), grid, block, 0, s, a,
+                           tk);
+}
+
+template <int G, int U>
+hipError_t sx_combine_with(const StandardCombineArgs& a, const TokenMap& tk, int dtype, dim3 grid,
+                           dim3 block, bool stream, hipStream_t s)
+{
+    if (dtype == 0) {
+        if (stream)
+            sx_combine_launch<G, U, 0, true>(a, tk, grid, block, s);
+        else
+            sx_combine_launch<G, U, 0, false>(a, tk, grid, block, s);
+    } else {
+        if (stream)
+            sx_combine_launch<G, U, 1, true>(a, tk, grid, block, s);
+        else
+            sx_combine_launch<G, U, 1, false>(a, tk, grid, block, s);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_standard_count(const StandardArgs& a, hipStream_t s)
+{
+    const dim3 grid((a.Tr + kSxWaves - 1) / kSxWaves, a.W);
+    const dim3 block(kSxWaves * kWave);
+    switch (sx_bucket(a.k)) {
+    case 8: hipLaunchKernelGGL((sx_count_kernel<8>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((sx_count_kernel<16>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((sx_count_kernel<32>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((sx_count_kernel<64>), grid, block, 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_standard_scan(const StandardArgs& a, hipStream_t s)
+{
+    hipLaunchKernelGGL(sx_scan_kernel, dim3((unsigned)((a.E + kSxWaves - 1) / kSxWaves)),
+                       dim3(kSxWaves * kWave), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_standard_copy(const StandardArgs& a, int waves, int row_split, bool stream,
+                                hipStream_t s)
+{
+    const dim3 grid(a.Tr, row_split, a.W);
+    const dim3 block(waves * kWave);
+    const int per_lane = (a.piece_vecs + kWave - 1) / kWave;
+    if (per_lane <= 1)
+        return sx_copy_with_vpl<1>(a, grid, block, stream, s);
+    if (per_lane <= 2)
+        return sx_copy_with_vpl<2>(a, grid, block, stream, s);
+    if (per_lane <= 4)
+        return sx_copy_with_vpl<4>(a, grid, block, stream, s);
+    return sx_copy_with_vpl<8>(a, grid, block, stream, s);
+}
+
+hipError_t launch_standard_combine(const StandardCombineArgs& a, const TokenMap& tk, int dtype,
+                                   int waves, int row_split, bool stream, hipStream_t s)
+{
+    if (tk.total == 0)
+        return hipSuccess;
+    const dim3 grid((tk.total + waves - 1) / waves, row_split);
+    const dim3 block(waves * kWave);
+    const int pe = a.k < a.E ? a.k : a.E;  // most kept pairs a token can have
+    if (pe <= 1)
+        return sx_combine_with<1, 4>(a, tk, dtype, grid, block, stream, s);
+    if (pe <= 2)
+        return sx_combine_with<2, 4>(a, tk, dtype, grid, block, stream, s);
+    if (pe <= 4)
+        return sx_combine_with<4, kCombineColumns>(a, tk, dtype, grid, block, stream, s);
+    return sx_combine_with<kCombineGroup, kCombineColumns>(a, tk, dtype, grid, block, stream, s);
+}
+
+}  // namespace ep

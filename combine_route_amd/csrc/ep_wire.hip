@@ -189,19 +189,6 @@ __device__ __forceinline__ void decode_group(const u32x2& c, uint32_t sbits,
     }
 }
 
-__device__ __forceinline__ int rank_of_token(const TokenMap& tk, int flat)
-{
-    int lo = 0, hi = tk.W - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (tk.tok_start[mid] <= flat)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    return lo;
-}
-
 // 8-element groups a lane decodes at once per contribution row: C columns a
 // wave apart (group h and h + 64), so every load and store instruction of
 // the wave covers one contiguous span; a lane reads 8 * C bytes of FP8 codes

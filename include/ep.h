@@ -348,9 +348,11 @@ int ep_plan_get_launch(const ep_plan_t *plan, const int32_t *num_tokens, ep_laun
  * EP_KERNEL_COMBINE (gather-reduce), and those of the plan's expert plans:
  * EP_KERNEL_EXPERT_COUNT (per-tile expert counts), EP_KERNEL_EXPERT_SCAN
  * (expert lists and layout ranges), EP_KERNEL_EXPERT_COPY (rows into the
- * expert-major layout), EP_KERNEL_EXPERT_COMBINE (the inverse). Enabling
- * creates the events (no device memory); disabling destroys them. Not for use
- * under graph capture. */
+ * expert-major layout), EP_KERNEL_EXPERT_COMBINE (the inverse), and the
+ * fused path's EP_KERNEL_STANDARD_COUNT, _SCAN, _COPY (ep_dispatch_standard_moe)
+ * and EP_KERNEL_STANDARD_COMBINE (ep_combine_standard_moe). Enabling creates
+ * the events (no device memory); disabling destroys them. Not for use under
+ * graph capture. */
 enum {
     EP_KERNEL_ROUTE = 0,
     EP_KERNEL_SCAN = 1,
@@ -359,7 +361,11 @@ enum {
     EP_KERNEL_EXPERT_COUNT = 4,
     EP_KERNEL_EXPERT_SCAN = 5,
     EP_KERNEL_EXPERT_COPY = 6,
-    EP_KERNEL_EXPERT_COMBINE = 7
+    EP_KERNEL_EXPERT_COMBINE = 7,
+    EP_KERNEL_STANDARD_COUNT = 8,
+    EP_KERNEL_STANDARD_SCAN = 9,
+    EP_KERNEL_STANDARD_COPY = 10,
+    EP_KERNEL_STANDARD_COMBINE = 11
 };
 int ep_plan_set_timing(ep_plan_t *plan, int enable);
 int ep_plan_kernel_time(ep_plan_t *plan, int kernel, int32_t *count, double *total_ms);
@@ -465,7 +471,7 @@ int ep_convert_dispatch_output(ep_expert_plan_t *plan, const ep_convert_dispatch
  *   apply_weights  0: the plain sum. 1: each output is scaled by its
  *                  expert's weight for the row (recorded by the conversion,
  *                  which must have been given weights): acc = c * v for the
- *                  first kept output, then acc = fma(c, v, acc) (R; [GUIDE]
+ *                  first kept output, then acc = fma(c, v, acc) ([GUIDE]
  *                  section 3: combine weights are for a weighted
  *                  combination). The plain combine after it then gives the
  *                  mixture sum over a token's slots of w_i * expert_i(x). */
@@ -484,6 +490,86 @@ typedef struct ep_convert_combine_args {
  * weights asked for and the conversion had none), EP_ERR_HIP. */
 int ep_convert_combine_input(ep_expert_plan_t *plan, const ep_convert_combine_args_t *args,
                              void *stream);
+
+/* Arguments of ep_dispatch_standard_moe (device pointers 16-byte aligned, id,
+ * count and info arrays 4-byte, layout ranges 8-byte; shapes as in
+ * ep_dispatch_args_t and ep_convert_dispatch_args_t):
+ *   num_tokens           host [W]: tokens T_r of each source rank, <= M.
+ *   x                    [W][M][H] dispatch_dtype; rows t < T_r are read.
+ *   indices              [W][M][k] int32 expert ids.
+ *   scales               [W][M][scale_dim] or NULL iff scale_dim == 0.
+ *   packed_x             [W][Er][cap][H] dispatch_dtype.
+ *   packed_scales        [W][Er][cap][scale_dim] or NULL iff scale_dim == 0.
+ *   packed_count         [W][Er] int32: tokens naming each expert (dropped
+ *                        ones included).
+ *   packed_src_info      [W][Er][cap] int32: the source token index within its
+ *                        source rank.
+ *   packed_layout_range  [W][Er][W] int64: (lo << 32) | (hi - lo), the list
+ *                        positions of each source rank's rows, clipped to cap.
+ * The routing weights are not part of the layout: ep_combine_standard_moe
+ * takes them. */
+typedef struct ep_dispatch_standard_args {
+    const int32_t *num_tokens;
+    const void *x;
+    const int32_t *indices;
+    const void *scales;
+    void *packed_x;
+    void *packed_scales;
+    int32_t *packed_count;
+    int32_t *packed_src_info;
+    int64_t *packed_layout_range;
+} ep_dispatch_standard_args_t;
+
+/* Dispatch straight into the expert-major layout ([GUIDE4]
+ * dispatch_standard_moe: dispatch and format conversion in one call). The
+ * outputs are exactly those of ep_dispatch followed by
+ * ep_convert_dispatch_output with the same capacity, without the
+ * intermediate receive buffer: expert e = d * Er + j keeps the tokens naming
+ * it in source-rank, then token order, a token once per distinct expert,
+ * positions >= cap dropped. Uses only the expert plan's configuration and
+ * workspace (not the plan's routing handle, which it leaves alone); it
+ * records the map ep_combine_standard_moe reads and ends any conversion on
+ * this expert plan (ep_convert_combine_input then fails until the next
+ * ep_convert_dispatch_output). The config must have no dispatch_cast.
+ * Asynchronous on stream; no allocation; capturable.
+ * Errors: EP_ERR_NULL, EP_ERR_ALIGN, EP_ERR_ARG (token counts, scales
+ * pairing, a dispatch_cast config), EP_ERR_HIP. */
+int ep_dispatch_standard_moe(ep_expert_plan_t *plan, const ep_dispatch_standard_args_t *args,
+                             void *stream);
+
+/* Arguments of ep_combine_standard_moe (device pointers; packed_y and out
+ * 16-byte aligned, indices and weights 4-byte):
+ *   packed_y  [W][Er][cap][H] combine_dtype: the experts' outputs, slot for
+ *             slot with packed_x (slots past min(count, cap) are not read).
+ *   indices   [W][M][k] int32: the ids given to the last
+ *             ep_dispatch_standard_moe on this expert plan.
+ *   weights   [W][M][k] float routing weights to apply, or NULL (the plain
+ *             sum).
+ *   out       [W][M][H] combine_dtype: rows t < T_r of the last fused
+ *             dispatch are written, others untouched. Must not overlap
+ *             packed_y. */
+typedef struct ep_combine_standard_args {
+    const void *packed_y;
+    const int32_t *indices;
+    const float *weights;
+    void *out;
+} ep_combine_standard_args_t;
+
+/* Combine straight from the expert-major layout ([GUIDE4]
+ * combine_standard_moe). The result is exactly that of
+ * ep_convert_combine_input (apply_weights = weights != NULL) followed by
+ * ep_combine, without the intermediate rows: for each of the token's ranks in
+ * its rank order, the FP32 fold of the rank's kept expert outputs in
+ * first-occurrence order (weighted: c * v, then fma), rounded to
+ * combine_dtype; those summed in FP32 from the first and rounded once to
+ * nearest even. A rank whose pairs were all dropped adds +0. Uses the map of
+ * the last ep_dispatch_standard_moe on this expert plan. Asynchronous; no
+ * allocation; capturable; may be called any number of times per dispatch.
+ * The config must have no combine_wire.
+ * Errors: EP_ERR_NULL, EP_ERR_ALIGN, EP_ERR_ARG (a combine_wire config),
+ * EP_ERR_STATE (no fused dispatch yet on this expert plan), EP_ERR_HIP. */
+int ep_combine_standard_moe(ep_expert_plan_t *plan, const ep_combine_standard_args_t *args,
+                            void *stream);
 
 #ifdef __cplusplus
 }

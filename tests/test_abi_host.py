@@ -39,7 +39,7 @@ def header_functions():
 
 def test_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) == 17
+    assert len(names) == 19
     assert sorted(cra.EXPORTED) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -273,10 +273,10 @@ def test_kernel_time_argument_checks(lib):
     cfg = cra.make_config(2, 256, 16, 4, 2)
     rc, plan = make_plan(lib, cfg)
     c, ms = ctypes.c_int32(), ctypes.c_double()
-    assert lib.ep_plan_kernel_time(plan, 8, ctypes.byref(c), ctypes.byref(ms)) == cra.EP_ERR_ARG
+    assert lib.ep_plan_kernel_time(plan, 12, ctypes.byref(c), ctypes.byref(ms)) == cra.EP_ERR_ARG
     assert lib.ep_plan_kernel_time(plan, -1, ctypes.byref(c), ctypes.byref(ms)) == cra.EP_ERR_ARG
     assert lib.ep_plan_kernel_time(plan, 0, ctypes.byref(c), ctypes.byref(ms)) == 0
-    assert lib.ep_plan_kernel_time(plan, cra.EP_KERNEL_EXPERT_COMBINE, ctypes.byref(c),
+    assert lib.ep_plan_kernel_time(plan, cra.EP_KERNEL_STANDARD_COMBINE, ctypes.byref(c),
                                    ctypes.byref(ms)) == 0
     assert c.value == 0 and ms.value == 0.0
     lib.ep_plan_destroy(plan)
@@ -288,14 +288,18 @@ def test_kernel_time_argument_checks(lib):
 # ---------------------------------------------------------------------------
 
 def expected_expert_workspace(W, M, k, Er):
-    """Layout: tile counts and bases (W*Er x max(1, ceil(W*M/64)) int32 each),
-    source starts (W x W int32), in-tile prefixes (W*Er x W int32), the
-    inverse's map and weights (W x W*M x min(k, Er) int32 / float), each
-    rounded up to 256 bytes."""
+    """Layout: tile counts and bases (W*Er x max(ceil(W*M/64), W*ceil(M/64)),
+    at least 1, int32 each: the convert path's tiles of received rows or the
+    fused path's tiles of source tokens), source starts (W x W int32),
+    in-tile prefixes (W*Er x W int32), the inverse's map (W x W*M x min(k, Er)
+    int32, or the fused path's per-slot map W x M x k, whichever is larger)
+    and its weights (W x W*M x min(k, Er) float), each rounded up to 256
+    bytes."""
     up = lambda v: (v + 255) // 256 * 256
     T = max(1, (W * M + 63) // 64)
-    return (2 * up(4 * W * Er * T) + up(4 * W * W) + up(4 * W * Er * W)
-            + 2 * up(4 * W * W * M * min(k, Er)))
+    tiles = max(T, W * max(1, (M + 63) // 64))
+    return (2 * up(4 * W * Er * tiles) + up(4 * W * W) + up(4 * W * Er * W)
+            + up(4 * max(W * W * M * min(k, Er), W * M * k)) + up(4 * W * W * M * min(k, Er)))
 
 
 def make_expert(lib, plan, cap, ws=FAKE_WS + (1 << 30), nbytes=None):
@@ -418,6 +422,86 @@ def test_convert_combine_input_errors_and_state(lib):
         a = cra.EpConvertCombineArgs(**{**ok, **over})
         assert lib.ep_convert_combine_input(ex, ctypes.byref(a), None) == code
         assert word in cra.ep_last_error()
+    lib.ep_expert_plan_destroy(ex)
+    lib.ep_plan_destroy(plan)
+
+
+def standard_args(**over):
+    a = dict(num_tokens=None, x=FAKE, indices=FAKE + 0x1000, scales=None,
+             packed_x=FAKE + 0x3000, packed_scales=None, packed_count=FAKE + 0x4000,
+             packed_src_info=FAKE + 0x5000, packed_layout_range=FAKE + 0x6000)
+    a.update(over)
+    return a
+
+
+@pytest.mark.parametrize("over,code,word", [
+    (dict(x=None), cra.EP_ERR_NULL, "args.x"),
+    (dict(indices=None), cra.EP_ERR_NULL, "args.indices"),
+    (dict(packed_x=None), cra.EP_ERR_NULL, "packed_x"),
+    (dict(packed_count=None), cra.EP_ERR_NULL, "packed_count"),
+    (dict(packed_src_info=None), cra.EP_ERR_NULL, "packed_src_info"),
+    (dict(packed_layout_range=None), cra.EP_ERR_NULL, "packed_layout_range"),
+    (dict(x=FAKE + 8), cra.EP_ERR_ALIGN, "args.x"),
+    (dict(packed_x=FAKE + 0x3004), cra.EP_ERR_ALIGN, "packed_x"),
+    (dict(packed_layout_range=FAKE + 0x6004), cra.EP_ERR_ALIGN, "packed_layout_range"),
+    (dict(indices=FAKE + 0x1002), cra.EP_ERR_ALIGN, "indices"),
+    (dict(scales=FAKE + 0x7000, packed_scales=FAKE + 0x8000), cra.EP_ERR_ARG, "scale_dim = 0"),
+    (dict(ntok=(17, 0)), cra.EP_ERR_ARG, "num_tokens[0]"),
+    (dict(ntok=(3, -1)), cra.EP_ERR_ARG, "num_tokens[1]"),
+])
+def test_dispatch_standard_rejects_before_launch(lib, over, code, word):
+    cfg = cra.make_config(2, 256, 16, 4, 2)
+    rc, plan = make_plan(lib, cfg)
+    rc, ex = make_expert(lib, plan, 8)
+    ntok = (ctypes.c_int32 * 2)(*over.pop("ntok", (16, 5)))
+    a = cra.EpDispatchStandardArgs(**standard_args(num_tokens=ctypes.addressof(ntok), **over))
+    assert lib.ep_dispatch_standard_moe(ex, ctypes.byref(a), None) == code
+    assert word in cra.ep_last_error()
+    assert lib.ep_dispatch_standard_moe(None, ctypes.byref(a), None) == cra.EP_ERR_NULL
+    assert lib.ep_dispatch_standard_moe(ex, None, None) == cra.EP_ERR_NULL
+    a.num_tokens = None
+    assert lib.ep_dispatch_standard_moe(ex, ctypes.byref(a), None) == cra.EP_ERR_NULL
+    lib.ep_expert_plan_destroy(ex)
+    lib.ep_plan_destroy(plan)
+
+
+def test_standard_paths_refuse_cast_and_wire_configs(lib):
+    ntok = (ctypes.c_int32 * 8)(*([4] * 8))
+    cfg = cra.make_config(8, 7168, 128, 32, 8, "fp8", "bf16", dispatch_cast="bf16")
+    rc, plan = make_plan(lib, cfg)
+    rc, ex = make_expert(lib, plan, 64)
+    a = cra.EpDispatchStandardArgs(**standard_args(num_tokens=ctypes.addressof(ntok)))
+    assert lib.ep_dispatch_standard_moe(ex, ctypes.byref(a), None) == cra.EP_ERR_ARG
+    assert "dispatch_cast" in cra.ep_last_error()
+    lib.ep_expert_plan_destroy(ex)
+    lib.ep_plan_destroy(plan)
+    cfg = cra.make_config(8, 7168, 128, 32, 8, combine_wire="mxfp4")
+    rc, plan = make_plan(lib, cfg)
+    rc, ex = make_expert(lib, plan, 64)
+    c = cra.EpCombineStandardArgs(packed_y=FAKE, indices=FAKE + 0x1000, weights=None,
+                                  out=FAKE + 0x2000)
+    assert lib.ep_combine_standard_moe(ex, ctypes.byref(c), None) == cra.EP_ERR_ARG
+    assert "combine_wire" in cra.ep_last_error()
+    lib.ep_expert_plan_destroy(ex)
+    lib.ep_plan_destroy(plan)
+
+
+def test_combine_standard_errors_and_state(lib):
+    cfg = cra.make_config(2, 256, 16, 4, 2)
+    rc, plan = make_plan(lib, cfg)
+    rc, ex = make_expert(lib, plan, 8)
+    ok = dict(packed_y=FAKE, indices=FAKE + 0x1000, weights=None, out=FAKE + 0x2000)
+    for over, code, word in [(dict(packed_y=None), cra.EP_ERR_NULL, "packed_y"),
+                             (dict(indices=None), cra.EP_ERR_NULL, "indices"),
+                             (dict(out=None), cra.EP_ERR_NULL, "args.out"),
+                             (dict(out=FAKE + 0x2008), cra.EP_ERR_ALIGN, "aligned"),
+                             (dict(weights=FAKE + 0x3002), cra.EP_ERR_ALIGN, "weights"),
+                             ({}, cra.EP_ERR_STATE, "before any dispatch_standard_moe")]:
+        a = cra.EpCombineStandardArgs(**{**ok, **over})
+        assert lib.ep_combine_standard_moe(ex, ctypes.byref(a), None) == code
+        assert word in cra.ep_last_error()
+    assert lib.ep_combine_standard_moe(None, ctypes.byref(a), None) == cra.EP_ERR_NULL
+    assert lib.ep_combine_standard_moe(ex, None, None) == cra.EP_ERR_NULL
     lib.ep_expert_plan_destroy(ex)
     lib.ep_plan_destroy(plan)
 

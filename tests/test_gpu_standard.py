@@ -1,0 +1,269 @@
+"""GPU parity of the fused expert-major dispatch and combine, through the C ABI.
+
+"MORI-EP User Guide", section 4 "Standard MoE Compatibility (DeepEP)":
+dispatch_standard_moe (dispatch and format conversion in one call) and
+combine_standard_moe. Their results are defined as those of the two-step
+path: dispatch, then convert_dispatch_output; convert_combine_input, then
+combine. So the oracle here is the oracle's two steps (oracle.dispatch ->
+oracle.expert_layout; oracle.expert_combine -> oracle.combine), each pinned
+on its own; every comparison is bit for bit, and the fused results are also
+compared with the GPU's own two-step path. Slots and rows the calls must not
+write are filled with a sentinel first and checked to still hold it.
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_route_amd as cra
+import oracle
+import workloads
+
+from test_gpu_expert import (SENTINEL_BYTE, SENTINEL_INT, SMALL, _dims, _fill_outputs,
+                             compare_layout, max_count, random_outputs)
+from test_gpu_parity import _say, config_of, gpu_dispatch, oracle_dispatch
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL_WORD = SENTINEL_BYTE << 8 | SENTINEL_BYTE
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cra.load()
+
+
+def _dev(t):
+    return None if t is None else t.cuda()
+
+
+def two_step_on_gpu(wl, inp, cap, py_dev, weighted, launch=None):
+    """The GPU's own dispatch -> convert -> inverse -> combine, on a fresh op."""
+    op = cra.EpDispatchCombineOp(config_of(wl), with_weights=weighted, expert_capacity=cap)
+    if launch is not None:
+        op.set_launch(launch)
+    gpu_dispatch(op, inp if weighted else dict(inp, w=None))
+    px, cnt, si, lr = op.convert_dispatch_output(op.out_x, op.out_indices, op.out_scales,
+                                                 op.out_weights if weighted else None)
+    y = op.convert_combine_input(py_dev, apply_weights=weighted)
+    out, _ = op.combine(y)
+    torch.cuda.synchronize()
+    res = dict(cnt=cnt.cpu(), lr=lr.cpu(), out=out.view(torch.int16).cpu(),
+               px=(px[0] if isinstance(px, tuple) else px).view(torch.uint8).cpu(),
+               si=si.cpu())
+    op.close()
+    return res
+
+
+def run_standard_case(wl, cap=None, cap_div=1, inp=None, launch=None, tag=None,
+                      check_untouched=True, py="random", weighted=False, two_step=True):
+    """Fused dispatch and combine on the GPU, each compared with the oracle's
+    two steps (and, with two_step, with the GPU's two-step path)."""
+    W, M, k, Er, H = _dims(wl)
+    inp = inp or workloads.make_inputs(wl)
+    ref = oracle_dispatch(wl, inp)
+    if cap is None:
+        cap = max(1, max_count(wl, ref) // cap_div)
+    tag = tag or f"std {wl.name} cap={cap}"
+    _say(f"[case] {tag}: W={W} M={M} H={H} k={k} Er={Er} {wl.dispatch_dtype}->"
+         f"{wl.combine_dtype} weighted={weighted} launch={launch}")
+    op = cra.EpDispatchCombineOp(config_of(wl), with_weights=False, expert_capacity=cap)
+    if launch is not None:
+        op.set_launch(launch)
+    ex = op._expert_state()
+    if check_untouched:
+        _fill_outputs(ex)
+        op.combine_out.view(torch.uint8).fill_(SENTINEL_BYTE)
+    x, idx, sc = _dev(inp["x"]), _dev(inp["idx"]), _dev(inp["scales"])
+    op.dispatch_standard_moe(x, None, sc, idx, num_tokens=inp["ntok"])
+    torch.cuda.synchronize()
+    ref_ex = oracle.expert_layout(W, M, k, Er, cap, ref["recv"], ref["src_pos"], ref["out_x"],
+                                  ref["out_idx"], ref["out_scales"], fill=SENTINEL_INT)
+    compare_layout(wl, cap, op, ref_ex, tag, check_untouched)
+
+    dt = oracle.BF16 if wl.combine_dtype == "bf16" else oracle.FP16
+    if py == "identity":
+        assert wl.dispatch_dtype == wl.combine_dtype
+        py_dev = ex["packed_x"].clone()
+        py16 = ref_ex["px"].view(np.uint16)
+    elif py == "neg_zero":
+        v = torch.full((W, Er, cap, H), -0.0, dtype=workloads.TORCH_DTYPE[wl.combine_dtype])
+        py_dev = v.cuda()
+        py16 = v.view(torch.int16).numpy().view(np.uint16)
+    else:
+        v = random_outputs(wl, cap, seed=sum(tag.encode()) % 10007)
+        py_dev = v.cuda()
+        py16 = v.view(torch.int16).numpy().view(np.uint16)
+    w = _dev(inp["w"]) if weighted else None
+    out = op.combine_standard_moe(py_dev, w, idx)
+    torch.cuda.synchronize()
+    ref_y = oracle.expert_combine(W, M, k, Er, cap, H, dt, ref["recv"], ref["out_idx"], py16,
+                                  w=ref["out_w"] if weighted else None)
+    ro, _ = oracle.combine(W, M, k, H, dt, inp["ntok"], ref["fwd"], ref_y)
+    g = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    for r in range(W):
+        T = inp["ntok"][r]
+        assert np.array_equal(g[r, :T], ro[r, :T]), (tag, "fused combine", r)
+        if check_untouched:
+            assert (g[r, T:] == SENTINEL_WORD).all(), (tag, "combine rows past T_r", r)
+
+    if two_step:
+        gs = two_step_on_gpu(wl, inp, cap, py_dev, weighted, launch)
+        assert torch.equal(gs["cnt"], ex["packed_count"].cpu()), (tag, "two-step count")
+        assert torch.equal(gs["lr"], ex["packed_layout_range"].cpu()), (tag, "two-step ranges")
+        gout = torch.from_numpy(g.view(np.int16))
+        for r in range(W):
+            T = inp["ntok"][r]
+            assert torch.equal(gs["out"][r, :T], gout[r, :T]), (tag, "two-step combine", r)
+    op.close()
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_workload_full_size(name):
+    """Every workload at full size in the automatic launch geometry, no pair
+    dropped; identity experts where the element types match."""
+    wl = workloads.WORKLOADS[name]
+    identity = wl.dispatch_dtype == wl.combine_dtype
+    run_standard_case(wl, check_untouched=name != workloads.HEADLINE,
+                      py="identity" if identity else "random",
+                      two_step=name != workloads.HEADLINE)
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_weighted_full_size(name):
+    wl = workloads.WORKLOADS[name]
+    run_standard_case(wl, check_untouched=False, weighted=True,
+                      two_step=name != workloads.HEADLINE)
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+@pytest.mark.parametrize("cap_div", [1, 2, 1000])
+@pytest.mark.parametrize("weighted", [False, True])
+def test_capacity_drops(wl, cap_div, weighted):
+    """Full capacity, half (pairs dropped, counts still full) and capacity 1,
+    where whole ranks of a token can lose every pair."""
+    run_standard_case(wl, cap_div=cap_div, weighted=weighted,
+                      tag=f"std {wl.name} /{cap_div} w={weighted}")
+
+
+@pytest.mark.parametrize("cap_div", [1, 3, 1000])
+def test_signed_zero_with_dropped_ranks(cap_div):
+    """Every expert output -0.0: a token's sum is -0.0 unless one of its ranks
+    lost all its pairs, whose +0 rows turn it to +0; the fused combine must
+    place those +0 terms exactly where the two-step path has them."""
+    wl = workloads.custom("std_zero_ep4_t64_h128_k6", 4, 64, 128, 6, 24, "bf16", ragged=True,
+                          seed_index=550)
+    run_standard_case(wl, cap_div=cap_div, py="neg_zero", tag=f"std -0 /{cap_div}")
+
+
+@pytest.mark.parametrize("W,E,k", [(2, 300, 8), (1, 130, 9), (4, 520, 17), (2, 40, 33),
+                                   (3, 66, 64), (64, 512, 8), (8, 64, 1), (16, 48, 24)])
+def test_world_expert_topk_sweep(W, E, k):
+    """More than 64 experts (several mask words), at most 64 (register
+    repeats), every top-k bucket, 64 source ranks, one rank, more ranks a
+    token than a fold group holds."""
+    M = 96 if W <= 8 else 12
+    wl = workloads.custom(f"std_sweep_W{W}_E{E}_k{k}", W, M, 128, k, E, "bf16", ragged=True,
+                          seed_index=560 + W + k)
+    run_standard_case(wl, cap_div=2 if W % 2 else 1, weighted=W % 2 == 0)
+
+
+@pytest.mark.parametrize("launch", [
+    dict(expert_waves=1, expert_combine_waves=1),
+    dict(expert_waves=16, expert_row_split=7, expert_combine_waves=16,
+         expert_combine_row_split=5),
+    dict(expert_row_split=1, expert_combine_row_split=1, expert_cache_policy=cra.EP_CACHE_STREAM),
+    dict(expert_waves=3, expert_row_split=2, expert_cache_policy=cra.EP_CACHE_KEEP),
+])
+def test_geometry_does_not_change_results(launch):
+    wl = workloads.custom("std_geom_ep4_t200_h1024", 4, 200, 1024, 8, 64, "bf16", ragged=True,
+                          seed_index=570)
+    run_standard_case(wl, launch=launch, cap_div=2, weighted=True)
+
+
+def test_empty_and_edge_counts():
+    wl = workloads.custom("std_edge_ep4_t70_h256", 4, 70, 256, 4, 32, "bf16", seed_index=571)
+    for ntok in ([0, 0, 0, 0], [70, 0, 0, 1], [1, 1, 1, 1], [64, 65, 0, 70]):
+        inp = workloads.make_inputs(wl)
+        inp["ntok"] = ntok
+        run_standard_case(wl, inp=inp, cap=8, tag=f"std edges ntok={ntok}")
+
+
+def test_invalid_and_duplicate_ids():
+    """Ids outside [0, E) select nothing; a repeated expert is one pair and,
+    weighted, its slots' weights add up."""
+    wl = workloads.custom("std_ids_ep4_t48_h256", 4, 48, 256, 6, 16, "bf16", seed_index=572)
+    inp = workloads.make_inputs(wl)
+    g = torch.Generator().manual_seed(19)
+    idx = torch.randint(-3, 19, inp["idx"].shape, generator=g, dtype=torch.int32)
+    idx[0, 0] = -1
+    idx[1, :8] = idx[1, :8, :1]
+    idx[2, :5, :3] = 5
+    inp["idx"] = idx.contiguous()
+    for weighted in (False, True):
+        run_standard_case(wl, inp=inp, weighted=weighted, cap=8,
+                          tag=f"std invalid+duplicate ids w={weighted}")
+
+
+def test_fp8_scales_and_fp16_combine():
+    for wl in (workloads.custom("std_fp8_ep3_t40_h256_k5_s2", 3, 40, 256, 5, 12, "fp8",
+                                scale_dim=2, seed_index=573),
+               workloads.custom("std_fp16_ep4_t48_h128_k6", 4, 48, 128, 6, 24, "fp16",
+                                ragged=True, seed_index=574)):
+        run_standard_case(wl, cap_div=2, weighted=True)
+
+
+def test_state_and_interleaving_with_the_two_step_path():
+    """The fused combine needs a fused dispatch on the expert plan; a
+    conversion on the same expert plan ends it (they share the map's space),
+    and a fused dispatch ends the conversion."""
+    wl = workloads.custom("std_state_ep2_t32_h128", 2, 32, 128, 4, 8, "bf16", seed_index=575)
+    inp = workloads.make_inputs(wl)
+    op = cra.EpDispatchCombineOp(config_of(wl), expert_capacity=64)
+    x, idx = inp["x"].cuda(), inp["idx"].cuda()
+    with pytest.raises(cra.EpError) as e:
+        op.combine_standard_moe(torch.zeros(1, device="cuda"), None, idx)
+    assert e.value.code == cra.EP_ERR_STATE
+    px, _, _, _ = op.dispatch_standard_moe(x, None, None, idx, num_tokens=inp["ntok"])
+    py = px.clone()
+    op.combine_standard_moe(py, None, idx)
+    gpu_dispatch(op, inp)                         # the plan's own routing: no effect
+    op.combine_standard_moe(py, None, idx)
+    op.convert_dispatch_output(op.out_x, op.out_indices)
+    with pytest.raises(cra.EpError) as e:
+        op.combine_standard_moe(py, None, idx)
+    assert e.value.code == cra.EP_ERR_STATE
+    op.convert_combine_input(py)
+    op.dispatch_standard_moe(x, None, None, idx, num_tokens=inp["ntok"])
+    with pytest.raises(cra.EpError) as e:
+        op.convert_combine_input(py)
+    assert e.value.code == cra.EP_ERR_STATE
+    op.combine_standard_moe(py, None, idx)
+    torch.cuda.synchronize()
+    op.close()
+
+
+def test_deterministic_across_runs():
+    wl = workloads.custom("std_det_ep8_t256_h512", 8, 256, 512, 8, 128, "bf16", seed_index=576)
+    inp = workloads.make_inputs(wl)
+    runs = []
+    for rep in range(2):
+        op = cra.EpDispatchCombineOp(config_of(wl), expert_capacity=300)
+        x, idx, w = inp["x"].cuda(), inp["idx"].cuda(), inp["w"].cuda()
+        px, cnt, si, lr = op.dispatch_standard_moe(x, w, None, idx, num_tokens=inp["ntok"])
+        out = op.combine_standard_moe(px, w, idx)
+        torch.cuda.synchronize()
+        cnt = cnt.cpu()
+        kept = [(d, j, min(int(cnt[d, j]), 300)) for d in range(8) for j in range(16)]
+        runs.append(dict(cnt=cnt, lr=lr.cpu(),
+                         px=[px[d, j, :n].view(torch.int16).cpu() for d, j, n in kept],
+                         si=[si[d, j, :n].cpu() for d, j, n in kept],
+                         out=out.view(torch.int16).cpu()))
+        op.close()
+    a, b = runs
+    assert torch.equal(a["cnt"], b["cnt"]) and torch.equal(a["lr"], b["lr"])
+    assert torch.equal(a["out"], b["out"])
+    for key in ("px", "si"):
+        for u, v in zip(a[key], b[key]):
+            assert torch.equal(u, v)
