@@ -265,3 +265,58 @@ def test_wire_decode_of_every_code(name):
     assert np.array_equal(nan_g, nan_r)
     assert np.array_equal(g[~nan_g], r[~nan_r])
     op.close()
+
+
+def test_graph_replay_of_dispatch_quantize_and_wire_combine():
+    """Dispatch, the send-side quantizer over the received rows (row counts on
+    the device) and the MXFP4 wire combine captured in one HIP graph;
+    replayed with new inputs, with eager work in between; every replay
+    equals the oracle."""
+    wl = workloads.custom("wire_graph_ep4_t96_h512", 4, 96, 512, 8, 64, "bf16", seed_index=850)
+    W, M, k, H = wl.world_size, wl.max_tokens, wl.topk, wl.hidden
+    cw, ow = WIRES["mxfp4"]
+    cfg = cra.make_config(W, H, M, wl.experts_per_rank, k, "bf16", "bf16", combine_wire=cw)
+    op = cra.EpDispatchCombineOp(cfg)
+    inp0 = workloads.make_inputs(wl)
+    x, idx, w = inp0["x"].cuda(), inp0["idx"].cuda(), inp0["w"].cuda()
+    ntok = inp0["ntok"]
+    yq = torch.zeros((W, W * M, H // 2), dtype=torch.uint8, device="cuda")
+    ys = torch.zeros((W, W * M, H // 32), dtype=torch.uint8, device="cuda")
+
+    def step():
+        op.dispatch(ntok, x, idx, w)
+        cra.ep_quantize_rows(op.out_x, cw, yq, ys, counts=op.recv_num_token)
+        op.combine(yq, op.out_weights, y_scales=ys)
+
+    _say("[case] wire graph capture")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        inp = workloads.make_inputs(wl, seed=3000 + rep)
+        inp["ntok"] = ntok
+        x.copy_(inp["x"])
+        idx.copy_(inp["idx"])
+        w.copy_(inp["w"])
+        junk = torch.randn(1 << 20, device="cuda").sum()  # unrelated eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = oracle_dispatch(wl, inp)
+        # the oracle's quantizer over the oracle's received rows (identity experts)
+        rows = ref["out_x"].view(np.uint16).reshape(W * W * M, H)
+        codes, scales = oracle.quantize_rows(rows, oracle.BF16, ow)
+        ro = oracle.combine_wire(W, M, k, H, oracle.BF16, ow, ntok, ref["fwd"],
+                                 codes.reshape(W, W * M, -1), scales.reshape(W, W * M, -1))
+        got = op.combine_out.view(torch.int16).cpu().numpy().view(np.uint16)
+        for r in range(W):
+            assert np.array_equal(got[r, :ntok[r]], ro[r, :ntok[r]]), ("wire graph", rep, r)
+        del junk
+    op.close()
