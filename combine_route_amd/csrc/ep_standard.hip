@@ -40,6 +40,8 @@ namespace {
 using namespace dev;
 
 constexpr int kSxWaves = 4;  // count and scan: waves a block, one tile or list each
+// Mask words of a token's expert set the copy keeps in registers (E <= 256).
+constexpr int kSeenWords = 4;
 
 // Tokens of source rank r in this call.
 __device__ __forceinline__ int tokens_of(const StandardArgs& a, int r)
@@ -47,38 +49,39 @@ __device__ __forceinline__ int tokens_of(const StandardArgs& a, int r)
     return max(0, min(a.ntok[r], a.M));
 }
 
+// A wave per (source rank, tile, mask word of 64 experts).
 template <int KB>
 __global__ __launch_bounds__(kSxWaves * kWave) void sx_count_kernel(StandardArgs a)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int tile = blockIdx.x * kSxWaves + uniform(threadIdx.x / kWave);
     const int r = blockIdx.y;
+    const int w = blockIdx.z;
     if (tile >= a.Tr)
         return;  // whole waves
     const int T = tokens_of(a, r);
     const int q = tile * kWave + lane;
     const bool valid = q < T;
     const int64_t TT = (int64_t)a.W * a.Tr;
-    int32_t* counts = a.tile_counts + (int64_t)r * a.Tr + tile;  // expert e at [e * TT]
+    const int nj = min(kWave, a.E - 64 * w);
+    // expert 64w + j at [j * TT]
+    int32_t* counts = a.tile_counts + (int64_t)(64 * w) * TT + (int64_t)r * a.Tr + tile;
     if (tile * kWave >= T) {  // no token here
-        for (int e = lane; e < a.E; e += kWave)
-            counts[(int64_t)e * TT] = 0;
+        if (lane < nj)
+            counts[(int64_t)lane * TT] = 0;
         return;
     }
     constexpr int KC = id_chunk<KB>();
     const int32_t* ids = a.idx + ((int64_t)r * a.M + (valid ? q : 0)) * a.k;
-    for (int w = 0; 64 * w < a.E; ++w) {
-        const uint64_t m = local_word<KC>(ids, a.k, valid, 0, a.E, w);
-        const int nj = min(kWave, a.E - 64 * w);
-        int c = 0;
-        for (int jj = 0; jj < nj; ++jj) {
-            const uint64_t b = __ballot((m >> jj) & 1);
-            if (lane == jj)
-                c = __popcll(b);
-        }
-        if (lane < nj)
-            counts[(int64_t)(64 * w + lane) * TT] = c;
+    const uint64_t m = local_word<KC>(ids, a.k, valid, 0, a.E, w);
+    int c = 0;
+    for (int jj = 0; jj < nj; ++jj) {
+        const uint64_t b = __ballot((m >> jj) & 1);
+        if (lane == jj)
+            c = __popcll(b);
     }
+    if (lane < nj)
+        counts[(int64_t)lane * TT] = c;
 }
 
 __global__ __launch_bounds__(kSxWaves * kWave) void sx_scan_kernel(StandardArgs a)
@@ -130,6 +133,8 @@ __global__ __launch_bounds__(1024) void sx_copy_kernel(StandardArgs a)
     __shared__ int32_t s_p[kWave][KB];  // their positions, then the kept packed rows
     __shared__ int8_t s_u[kWave][KB];   // each slot's index into s_e; -1: invalid or a repeat
     __shared__ int32_t s_n[kWave];      // kept packed rows of the token
+    __shared__ uint64_t s_bal[kSeenWords * kWave];  // expert e: its ballot over the tile
+    __shared__ int32_t s_base[kSeenWords * kWave];  // and its tile base
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
@@ -188,10 +193,13 @@ __global__ __launch_bounds__(1024) void sx_copy_kernel(StandardArgs a)
         constexpr int KC = id_chunk<KB>();
         const int64_t rowq = row0 + (valid ? lane : 0);
         const int32_t* ids = a.idx + rowq * a.k;
-        // the token's distinct experts in first-occurrence order; with one
-        // mask word (E <= 64) repeats are found in a register, else in LDS
+        // The token's distinct experts in first-occurrence order. With at
+        // most kSeenWords mask words (E <= 256) its expert set is kept in
+        // registers and repeats are found there; else in LDS.
+        const int nw = (a.E + kWave - 1) / kWave;
+        const bool regs = nw <= kSeenWords;  // uniform
         int n = 0;
-        uint64_t seen = 0;
+        uint64_t seen[kSeenWords] = {};
         for (int c = 0; c * KC < a.k; ++c) {
             int32_t id[KC];
             load_ids<KC>(ids, a.k, c, id);
@@ -203,12 +211,17 @@ __global__ __launch_bounds__(1024) void sx_copy_kernel(StandardArgs a)
                 int u = -1;
                 const int e = id[i];
                 if (valid && e >= 0 && e < a.E) {
-                    bool dup;
-                    if (a.E <= kWave) {
-                        dup = (seen >> e) & 1;
-                        seen |= 1ull << e;
+                    bool dup = false;
+                    if (regs) {
+                        const uint64_t bit = 1ull << (e & (kWave - 1));
+#pragma unroll
+                        for (int x = 0; x < kSeenWords; ++x) {
+                            if (x == (e >> 6)) {
+                                dup = (seen[x] & bit) != 0;
+                                seen[x] |= bit;
+                            }
+                        }
                     } else {
-                        dup = false;
                         for (int v = 0; v < n; ++v)
                             dup = dup || s_e[lane][v] == e;
                     }
@@ -220,35 +233,63 @@ __global__ __launch_bounds__(1024) void sx_copy_kernel(StandardArgs a)
                 s_u[lane][slot] = (int8_t)u;
             }
         }
-        int n_max = n;  // the wave's longest list
+        if (regs) {
+            // Every expert's ballot over the tile and its tile base go to LDS
+            // (lane jj of pass w writes expert 64w + jj); each lane then looks
+            // up its own experts there.
 #pragma unroll
-        for (int off = kWave / 2; off > 0; off >>= 1)
-            n_max = max(n_max, __shfl_xor(n_max, off));
-        // Positions, one mask word (64 experts) at a time: lane jj holds the
-        // ballot of expert 64w + jj over the tile and its tile base; each
-        // lane fetches both for its own entries with cross-lane reads.
-        for (int w = 0; 64 * w < a.E; ++w) {
-            const uint64_t m = a.E <= kWave ? seen : local_word<KC>(ids, a.k, valid, 0, a.E, w);
-            const int nj = min(kWave, a.E - 64 * w);
-            const int bw =
-                lane < nj ? a.tile_base[(int64_t)(64 * w + lane) * TT + (int64_t)r * a.Tr + tile]
-                          : 0;
-            uint64_t mine = 0;
-            for (int jj = 0; jj < nj; ++jj) {
-                const uint64_t b = __ballot((m >> jj) & 1);
-                if (lane == jj)
-                    mine = b;
+            for (int w = 0; w < kSeenWords; ++w) {
+                if (w < nw) {
+                    const int nj = min(kWave, a.E - 64 * w);
+                    uint64_t mine = 0;
+                    for (int jj = 0; jj < nj; ++jj) {
+                        const uint64_t b = __ballot((seen[w] >> jj) & 1);
+                        if (lane == jj)
+                            mine = b;
+                    }
+                    if (lane < nj) {
+                        s_bal[64 * w + lane] = mine;
+                        s_base[64 * w + lane] =
+                            a.tile_base[(int64_t)(64 * w + lane) * TT + (int64_t)r * a.Tr + tile];
+                    }
+                }
             }
-            const int mlo = (int)(uint32_t)mine;
-            const int mhi = (int)(uint32_t)(mine >> 32);
-            for (int u = 0; u < n_max; ++u) {
-                const int j = u < n ? s_e[lane][u] - 64 * w : -1;
-                const int src = j & (kWave - 1);
-                const uint32_t blo = (uint32_t)__shfl(mlo, src);
-                const uint32_t bhi = (uint32_t)__shfl(mhi, src);
-                const int base = __shfl(bw, src);
-                if (j >= 0 && j < kWave)
-                    s_p[lane][u] = base + lanes_below(((uint64_t)bhi << 32) | blo);
+            __builtin_amdgcn_wave_barrier();
+            for (int u = 0; u < n; ++u) {
+                const int e = s_e[lane][u];
+                s_p[lane][u] = s_base[e] + lanes_below(s_bal[e]);
+            }
+        } else {
+            int n_max = n;  // the wave's longest list
+#pragma unroll
+            for (int off = kWave / 2; off > 0; off >>= 1)
+                n_max = max(n_max, __shfl_xor(n_max, off));
+            // One mask word (64 experts) at a time: lane jj holds the ballot
+            // of expert 64w + jj over the tile and its tile base; each lane
+            // fetches both for its own entries with cross-lane reads.
+            for (int w = 0; w < nw; ++w) {
+                const uint64_t m = local_word<KC>(ids, a.k, valid, 0, a.E, w);
+                const int nj = min(kWave, a.E - 64 * w);
+                const int bw = lane < nj ? a.tile_base[(int64_t)(64 * w + lane) * TT +
+                                                       (int64_t)r * a.Tr + tile]
+                                         : 0;
+                uint64_t mine = 0;
+                for (int jj = 0; jj < nj; ++jj) {
+                    const uint64_t b = __ballot((m >> jj) & 1);
+                    if (lane == jj)
+                        mine = b;
+                }
+                const int mlo = (int)(uint32_t)mine;
+                const int mhi = (int)(uint32_t)(mine >> 32);
+                for (int u = 0; u < n_max; ++u) {
+                    const int j = u < n ? s_e[lane][u] - 64 * w : -1;
+                    const int src = j & (kWave - 1);
+                    const uint32_t blo = (uint32_t)__shfl(mlo, src);
+                    const uint32_t bhi = (uint32_t)__shfl(mhi, src);
+                    const int base = __shfl(bw, src);
+                    if (j >= 0 && j < kWave)
+                        s_p[lane][u] = base + lanes_below(((uint64_t)bhi << 32) | blo);
+                }
             }
         }
         // the combine's map: the packed row of each slot that is its expert's
@@ -531,7 +572,7 @@ hipError_t sx_combine_with(const StandardCombineArgs& a, const TokenMap& tk, int
 
 hipError_t launch_standard_count(const StandardArgs& a, hipStream_t s)
 {
-    const dim3 grid((a.Tr + kSxWaves - 1) / kSxWaves, a.W);
+    const dim3 grid((a.Tr + kSxWaves - 1) / kSxWaves, a.W, (a.E + kWave - 1) / kWave);
     const dim3 block(kSxWaves * kWave);
     switch (sx_bucket(a.k)) {
     case 8: hipLaunchKernelGGL((sx_count_kernel<8>), grid, block, 0, s, a); break;
