@@ -198,6 +198,14 @@ __global__ __launch_bounds__(1024) void sx_copy_kernel(StandardArgs a)
         // registers and repeats are found there; else in LDS.
         const int nw = (a.E + kWave - 1) / kWave;
         const bool regs = nw <= kSeenWords;  // uniform
+        // the tile bases of experts 64w + lane, loaded before the ids are
+        // read so their latency overlaps the routing
+        int bw[kSeenWords];
+#pragma unroll
+        for (int w = 0; w < kSeenWords; ++w)
+            bw[w] = regs && w < nw && 64 * w + lane < a.E
+                        ? a.tile_base[(int64_t)(64 * w + lane) * TT + (int64_t)r * a.Tr + tile]
+                        : 0;
         int n = 0;
         uint64_t seen[kSeenWords] = {};
         for (int c = 0; c * KC < a.k; ++c) {
@@ -249,8 +257,7 @@ __global__ __launch_bounds__(1024) void sx_copy_kernel(StandardArgs a)
                     }
                     if (lane < nj) {
                         s_bal[64 * w + lane] = mine;
-                        s_base[64 * w + lane] =
-                            a.tile_base[(int64_t)(64 * w + lane) * TT + (int64_t)r * a.Tr + tile];
+                        s_base[64 * w + lane] = bw[w];
                     }
                 }
             }
