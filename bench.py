@@ -471,6 +471,40 @@ def workloads_dtype(torch, name):
     return {"bf16": torch.bfloat16, "fp16": torch.float16}[name]
 
 
+def host_cpu():
+    """CPU model and logical CPU count of the host that runs the oracle."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu": model, "nproc": os.cpu_count()}
+
+
+def device_copy_rate(torch, mib=1024, steps=5):
+    """GB/s of a plain device-to-device copy of mib MiB (bytes read + written
+    per second), the box's own copy rate to set the path's rates against."""
+    n = mib << 20
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    rate = 2 * n * steps / (s.elapsed_time(e) * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return rate
+
+
 def copy_ceiling(torch, mib, steps, warmup):
     """Plain copy of mib MiB between two device buffers: reads and writes
     mib MiB each per launch."""
@@ -629,7 +663,8 @@ def run(args):
         cpu_baseline = {"value": round(payload_bytes / cpu_s / 1e9, 3), "unit": "GB/s",
                         "cores": 1, "kind": "oracle",
                         "sample": f"the whole {wl.name} workload: one dispatch+combine call of "
-                                  f"the single-threaded C oracle, {cpu_s:.2f} s"}
+                                  f"the single-threaded C oracle, {cpu_s:.2f} s",
+                        "host": host_cpu()}
         print(f"[bench] oracle call took {cpu_s:.2f}s", file=sys.stderr, flush=True)
         ok = np.array_equal(recv, ref["recv"])
         for d in range(W):
@@ -736,6 +771,7 @@ def run(args):
         "dtype": wl.dispatch_dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "world_size": W,
+                   "seed": f"{workloads.BASE_SEED} + 1000 * stream + {wl.seed_index}",
                    "tokens_per_rank": ntok[0] if len(set(ntok)) == 1 else ntok,
                    "hidden": H, "topk": k, "experts": wl.num_experts,
                    "dispatch_dtype": wl.dispatch_dtype, "combine_dtype": wl.combine_dtype,
@@ -766,6 +802,11 @@ def run(args):
         torch.cuda.empty_cache()
         line["quantized_wires"] = measure_quantized_wires(args, cra, torch, np, wl, inp, stream)
     op.close()
+    # the box's own device copy rate (1 GiB, torch), measured last so its
+    # buffers take no part in the placement of the timed ones
+    copy_rate = device_copy_rate(torch)
+    line["device_copy_GBps"] = round(copy_rate, 1)
+    line["pct_of_device_copy"] = round(100.0 * value / copy_rate, 2)
     print(json.dumps(line), flush=True)
 
 
