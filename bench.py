@@ -48,7 +48,8 @@ COUNTER_KERNELS = {
     "ep_combine_kernel": r"ep_combine_kernel<",
     "ex_copy_kernel": r"ex_copy_kernel<",
     "ex_combine_kernel": r"ex_combine_kernel<",
-    "sx_copy_kernel": r"sx_copy_kernel<",
+    "sx_copy_kernel": r"sx_copy_kernel<[^>]*, false>",
+    "sx_copy_kernel_cast": r"sx_copy_kernel<[^>]*, true>",
     "sx_combine_kernel": r"sx_combine_kernel<",
     "ep_copy_kernel_cast": r"ep_copy_kernel<[^>]*, true>",
     "ep_quantize_kernel_fp8_block128": r"ep_quantize_kernel<1,",
@@ -373,6 +374,22 @@ def measure_quantized_wires(args, cra, torch, np, wl, inp, stream):
             "us_per_call": round(ms * 1e3, 2), "copy_kernel_us": round(kms * 1e3, 2),
             "received_bytes_saved": R * H,
             "roofline": _roof(nb, kms, "ep_copy_kernel (cast)", wl.name, "ep_copy_kernel_cast")}
+        op.close()
+        del op
+        torch.cuda.empty_cache()
+        # the same cast straight into the expert-major layout
+        cap = expert_capacity(wl, ntok)
+        op = cra.EpDispatchCombineOp(cfg, device=dev, with_weights=False, expert_capacity=cap)
+        step = lambda: op.dispatch_standard_moe(x, None, None, idx, num_tokens=ntok,
+                                                stream=stream)
+        ms = _timed(torch, stream, step, args.steps, args.warmup)
+        kms = _kernel_ms(cra, torch, op.plan, cra.EP_KERNEL_STANDARD_COPY, step, args.steps)
+        pairs = int(op._expert_state()["packed_count"].clamp(max=cap).sum().item())
+        nb = N * (2 * H + 4 * k) + pairs * (H + 4) + N * k * 4
+        out["dispatch_standard_fp8_direct_cast"] = {
+            "us_per_call": round(ms * 1e3, 2), "copy_kernel_us": round(kms * 1e3, 2),
+            "expert_capacity": cap, "kept_pairs": pairs,
+            "roofline": _roof(nb, kms, "sx_copy_kernel (cast)", wl.name, "sx_copy_kernel_cast")}
         op.close()
         del op
         torch.cuda.empty_cache()

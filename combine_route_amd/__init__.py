@@ -436,12 +436,13 @@ def _dispatch_standard_args(cfg: EpConfig, cap: int, num_tokens: Sequence[int], 
                             scales, packed_x, packed_scales, packed_count, packed_src_info,
                             packed_layout_range):
     W, M, k, row, _, srow = _sizes(cfg)
+    xrow = cfg.hidden_dim * 2 if cfg.dispatch_cast else row
     Er = cfg.num_experts_per_rank
     if len(num_tokens) != W:
         raise ValueError(f"num_tokens has {len(num_tokens)} entries; world_size is {W}")
     arr = (ctypes.c_int32 * W)(*[int(t) for t in num_tokens])
     a = EpDispatchStandardArgs(
-        ctypes.addressof(arr), _dev(x, "x", W * M * row), _dev(indices, "indices", W * M * k * 4),
+        ctypes.addressof(arr), _dev(x, "x", W * M * xrow), _dev(indices, "indices", W * M * k * 4),
         _dev(scales, "scales", W * M * srow), _dev(packed_x, "packed_x", W * Er * cap * row),
         _dev(packed_scales, "packed_scales", W * Er * cap * srow),
         _dev(packed_count, "packed_count", W * Er * 4),

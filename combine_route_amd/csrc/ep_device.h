@@ -130,6 +130,17 @@ __device__ __forceinline__ uint32_t e4m3x4(float f0, float f1, float f2, float f
     return x ^ ff;
 }
 
+// 8 bf16 (cast 1) or fp16 (cast 2) elements -> 8 E4M3 codes.
+__device__ __forceinline__ u32x2 cast_e4m3(const u32x4& w, int cast)
+{
+    float f[8];
+    if (cast == 2)
+        widen<1>(w, f);
+    else
+        widen<0>(w, f);
+    return {e4m3x4(f[0], f[1], f[2], f[3]), e4m3x4(f[4], f[5], f[6], f[7])};
+}
+
 // One wave folds the n contribution rows whose row numbers (in units of
 // row_bytes from src) are held by lanes 0..n-1 of gl, over the 16-byte
 // columns [vbeg, vend) of the output row rdst: for each column every

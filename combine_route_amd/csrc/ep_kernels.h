@@ -147,8 +147,10 @@ struct StandardArgs {
     int32_t* tile_counts;        // [W * Er][W * Tr] tokens of (rank, tile) naming the expert
     int32_t* tile_base;          // [W * Er][W * Tr] position of that tile's first one
     int32_t* fslot;              // [W][M][k] packed row of a kept first-occurrence slot, else -1
-    int32_t row_vecs;            // 16-byte vectors per payload row
+    int32_t row_vecs;            // 16-byte vectors per source row
     int32_t piece_vecs;          // vectors per row piece (one block)
+    uint32_t out_row_bytes;      // bytes per packed row (half a source row with a cast)
+    int32_t cast;                // 0, or the source type (1 bf16, 2 fp16) cast to E4M3
     int32_t scale_dwords;
     int32_t W, M, k, Er, E, cap;
     int32_t Tr;                  // tiles a source rank: max(1, ceil(M / 64))

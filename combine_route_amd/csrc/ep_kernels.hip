@@ -262,24 +262,12 @@ __global__ __launch_bounds__(kScanThreads) void ep_scan_kernel(ScanArgs a)
 // ---------------------------------------------------------------------------
 // copy: payload rows, metadata rows, src_pos and the forward map.
 // ---------------------------------------------------------------------------
-// 8 bf16 (cast 1) or fp16 (cast 2) elements -> 8 E4M3 codes.
-__device__ __forceinline__ u32x2 cast_e4m3(const u32x4& w, int cast)
-{
-    float f[8];
-    if (cast == 2)
-        widen<1>(w, f);
-    else
-        widen<0>(w, f);
-    return {e4m3x4(f[0], f[1], f[2], f[3]), e4m3x4(f[4], f[5], f[6], f[7])};
-}
-
 // One work item of a wave: one chunk (up to 64 x VPL 16-byte vectors) of one
 // token's row piece, and, for the first chunk of a piece-0 block, the lane's
-// share of the token's id, weight and scale rows. NV = the 16-byte vectors
-// as loaded: 2 * VPL for a cast (32 input bytes for each vector stored).
-template <int VPL, int NV = VPL>
+// share of the token's id, weight and scale rows.
+template <int VPL>
 struct CopyItem {
-    u32x4 v[NV];
+    u32x4 v[VPL];
     int32_t e;
     float wv;
     uint32_t sc;
@@ -320,7 +308,6 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
     const bool meta = piece == 0;
     const uint32_t in_bytes = (uint32_t)a.row_vecs * 16u;                  // input row
     const uint32_t row_bytes = kCast ? (uint32_t)a.row_vecs * 8u : in_bytes;  // received row
-    constexpr int NV = VPL;
     const int k = a.k;
     const int per = kWave / k;  // destination id/weight rows per store instruction
     const int j = lane % k;
@@ -370,7 +357,7 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
             sc = a.sc[src * sd + lane];
     };
     // one chunk of a token's row piece to every destination row of the token
-    auto store_payload = [&](int tok, int v0, const u32x4 (&raw)[NV]) {
+    auto store_payload = [&](int tok, int v0, const u32x4 (&raw)[VPL]) {
         const int n = uniform(s_n[tok]);
         u32x2 c[kCast ? VPL : 1];  // a cast's codes, converted once per chunk
         if constexpr (kCast) {
@@ -396,7 +383,7 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
             }
         }
     };
-    auto load_payload = [&](int64_t src, int v0, u32x4 (&v)[NV]) {
+    auto load_payload = [&](int64_t src, int v0, u32x4 (&v)[VPL]) {
         const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.x + src * in_bytes, in_bytes);
 #pragma unroll
         for (int u = 0; u < VPL; ++u) {
@@ -405,7 +392,7 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
                 v[u] = bload16<Policy<kStream>::copy_load>(rs, (uint32_t)vv * 16u);
         }
     };
-    auto load_item = [&](int it, CopyItem<VPL, NV>& I) {
+    auto load_item = [&](int it, CopyItem<VPL>& I) {
         const int q = it / nch;
         const int c = it - q * nch;
         const int64_t src = (int64_t)r * a.M + t0 + wave + q * nwaves;
@@ -413,7 +400,7 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
         if (meta && c == 0)
             load_meta(src, I.e, I.wv, I.sc);
     };
-    auto store_item = [&](int it, const CopyItem<VPL, NV>& I) {
+    auto store_item = [&](int it, const CopyItem<VPL>& I) {
         const int q = it / nch;
         const int c = it - q * nch;
         const int tok = wave + q * nwaves;
@@ -511,7 +498,7 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
         // Small pieces (small calls, where time is latency): each wave's first
         // item loads while wave 0 routes the tile, then two items in flight,
         // item i+1 loading while item i stores.
-        CopyItem<VPL, NV> A, B;
+        CopyItem<VPL> A, B;
         if (items > 0)
             load_item(0, A);
         tile_bases();
@@ -546,7 +533,7 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
         for (int tok = wave; tok < cnt; tok += nwaves) {
             const int64_t src = (int64_t)r * a.M + t0 + tok;
             for (int v0 = vbeg; v0 < vend; v0 += kWave * VPL) {
-                u32x4 v[NV];
+                u32x4 v[VPL];
                 load_payload(src, v0, v);
                 store_payload(tok, v0, v);
             }

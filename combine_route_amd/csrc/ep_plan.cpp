@@ -1140,9 +1140,6 @@ int ep_dispatch_standard_moe(ep_expert_plan_t* x, const ep_dispatch_standard_arg
         return fail(EP_ERR_NULL, "args is NULL");
     ep_plan* p = x->plan;
     const Shape& s = p->s;
-    if (p->cfg.dispatch_cast != EP_CAST_NONE)
-        return fail(EP_ERR_ARG, "the fused dispatch copies rows as they are: the config's "
-                    "dispatch_cast must be EP_CAST_NONE");
     if (!a->num_tokens)
         return fail(EP_ERR_NULL, "args.num_tokens is NULL");
     struct {
@@ -1191,7 +1188,9 @@ int ep_dispatch_standard_moe(ep_expert_plan_t* x, const ep_dispatch_standard_arg
     sa.tile_counts = reinterpret_cast<int32_t*>(x->ws + x->e.off_counts);
     sa.tile_base = reinterpret_cast<int32_t*>(x->ws + x->e.off_base);
     sa.fslot = reinterpret_cast<int32_t*>(x->ws + x->e.off_efwd);
-    sa.row_vecs = (int32_t)(s.row_bytes / 16);
+    sa.row_vecs = s.row_vecs;  // of a source row (bf16 / fp16 with a cast)
+    sa.out_row_bytes = (uint32_t)s.row_bytes;
+    sa.cast = p->cfg.dispatch_cast;  // 1 bf16, 2 fp16 source rows
     sa.scale_dwords = (int32_t)(s.scale_bytes / 4);
     sa.W = s.W;
     sa.M = s.M;

@@ -126,7 +126,10 @@ __global__ __launch_bounds__(kSxWaves * kWave) void sx_scan_kernel(StandardArgs 
     }
 }
 
-template <int VPL, int KB, bool kStream>
+// kCast: the source rows are bf16 / fp16 (a.cast) and the packed rows E4M3
+// (round to nearest even, saturating at 448): each loaded 16-byte vector of 8
+// elements is converted once and 8 bytes are stored to each packed row.
+template <int VPL, int KB, bool kStream, bool kCast>
 __global__ __launch_bounds__(1024) void sx_copy_kernel(StandardArgs a)
 {
     __shared__ int32_t s_e[kWave][KB];  // a token's distinct experts, first-occurrence order
@@ -171,14 +174,26 @@ __global__ __launch_bounds__(1024) void sx_copy_kernel(StandardArgs a)
         const int t = wave + (it / nch) * nwaves;
         const int v0 = vbeg + (it % nch) * kWave * VPL;
         const int n = uniform(s_n[t]);
+        u32x2 c[kCast ? VPL : 1];
+        if constexpr (kCast) {
+#pragma unroll
+            for (int u = 0; u < VPL; ++u)
+                c[u] = cast_e4m3(v[u], a.cast);
+        }
         for (int i = 0; i < n; ++i) {
             const int64_t gi = uniform(s_p[t][i]);
-            const __amdgpu_buffer_rsrc_t rd = row_rsrc(a.px + gi * row_bytes, row_bytes);
+            const __amdgpu_buffer_rsrc_t rd =
+                row_rsrc(a.px + gi * a.out_row_bytes, a.out_row_bytes);
 #pragma unroll
             for (int u = 0; u < VPL; ++u) {
                 const int vv = v0 + u * kWave + lane;
-                if (vv < vend)
-                    bstore16<Policy<kStream>::copy_store>(v[u], rd, (uint32_t)vv * 16u);
+                if (vv < vend) {
+                    if constexpr (kCast)
+                        __builtin_amdgcn_raw_buffer_store_b64(c[u], rd, (int)((uint32_t)vv * 8u), 0,
+                                                              Policy<kStream>::copy_store);
+                    else
+                        bstore16<Policy<kStream>::copy_store>(v[u], rd, (uint32_t)vv * 16u);
+                }
             }
         }
     };
@@ -527,10 +542,17 @@ int sx_bucket(int k) { return k <= 8 ? 8 : k <= 16 ? 16 : k <= 32 ? 32 : 64; }
 template <int VPL, int KB>
 hipError_t sx_copy_with(const StandardArgs& a, dim3 grid, dim3 block, bool stream, hipStream_t s)
 {
-    if (stream)
-        hipLaunchKernelGGL((sx_copy_kernel<VPL, KB, true>), grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL((sx_copy_kernel<VPL, KB, false>), grid, block, 0, s, a);
+    if (a.cast) {
+        if (stream)
+            hipLaunchKernelGGL((sx_copy_kernel<VPL, KB, true, true>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((sx_copy_kernel<VPL, KB, false, true>), grid, block, 0, s, a);
+    } else {
+        if (stream)
+            hipLaunchKernelGGL((sx_copy_kernel<VPL, KB, true, false>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((sx_copy_kernel<VPL, KB, false, false>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 

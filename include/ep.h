@@ -495,7 +495,9 @@ int ep_convert_combine_input(ep_expert_plan_t *plan, const ep_convert_combine_ar
  * count and info arrays 4-byte, layout ranges 8-byte; shapes as in
  * ep_dispatch_args_t and ep_convert_dispatch_args_t):
  *   num_tokens           host [W]: tokens T_r of each source rank, <= M.
- *   x                    [W][M][H] dispatch_dtype; rows t < T_r are read.
+ *   x                    [W][M][H] dispatch_dtype (with a dispatch_cast, bf16 or
+ *                        fp16, each element written to packed_x as its E4M3
+ *                        code); rows t < T_r are read.
  *   indices              [W][M][k] int32 expert ids.
  *   scales               [W][M][scale_dim] or NULL iff scale_dim == 0.
  *   packed_x             [W][Er][cap][H] dispatch_dtype.
@@ -530,10 +532,11 @@ typedef struct ep_dispatch_standard_args {
  * workspace (not the plan's routing handle, which it leaves alone); it
  * records the map ep_combine_standard_moe reads and ends any conversion on
  * this expert plan (ep_convert_combine_input then fails until the next
- * ep_convert_dispatch_output). The config must have no dispatch_cast.
+ * ep_convert_dispatch_output). With a dispatch_cast the packed rows hold the
+ * E4M3 codes the cast dispatch would have received.
  * Asynchronous on stream; no allocation; capturable.
  * Errors: EP_ERR_NULL, EP_ERR_ALIGN, EP_ERR_ARG (token counts, scales
- * pairing, a dispatch_cast config), EP_ERR_HIP. */
+ * pairing), EP_ERR_HIP. */
 int ep_dispatch_standard_moe(ep_expert_plan_t *plan, const ep_dispatch_standard_args_t *args,
                              void *stream);
 

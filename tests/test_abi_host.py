@@ -465,16 +465,7 @@ def test_dispatch_standard_rejects_before_launch(lib, over, code, word):
     lib.ep_plan_destroy(plan)
 
 
-def test_standard_paths_refuse_cast_and_wire_configs(lib):
-    ntok = (ctypes.c_int32 * 8)(*([4] * 8))
-    cfg = cra.make_config(8, 7168, 128, 32, 8, "fp8", "bf16", dispatch_cast="bf16")
-    rc, plan = make_plan(lib, cfg)
-    rc, ex = make_expert(lib, plan, 64)
-    a = cra.EpDispatchStandardArgs(**standard_args(num_tokens=ctypes.addressof(ntok)))
-    assert lib.ep_dispatch_standard_moe(ex, ctypes.byref(a), None) == cra.EP_ERR_ARG
-    assert "dispatch_cast" in cra.ep_last_error()
-    lib.ep_expert_plan_destroy(ex)
-    lib.ep_plan_destroy(plan)
+def test_standard_combine_refuses_wire_configs(lib):
     cfg = cra.make_config(8, 7168, 128, 32, 8, combine_wire="mxfp4")
     rc, plan = make_plan(lib, cfg)
     rc, ex = make_expert(lib, plan, 64)

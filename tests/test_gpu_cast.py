@@ -83,3 +83,47 @@ def test_cast_dispatch_matches_oracle(src, W, M, H, k, E):
 def test_cast_geometry_and_scales(launch):
     run_cast_case(4, 200, 1024, 8, 64, "bf16", launch=launch, scale_dim=8, seed=31,
                   tag=f"cast geometry {launch}")
+
+
+@pytest.mark.parametrize("src", ["bf16", "fp16"])
+@pytest.mark.parametrize("W,M,H,k,E,cap_div,scale_dim", [
+    (8, 4096, 7168, 8, 256, 1, 0),     # the headline, nothing dropped
+    (4, 300, 2048, 64, 256, 2, 0),     # top-64, pairs dropped
+    (3, 50, 128, 5, 12, 3, 2),         # scale rows, few experts
+    (16, 20, 512, 8, 64, 1, 0),
+])
+def test_fused_cast_dispatch_matches_oracle(src, W, M, H, k, E, cap_div, scale_dim):
+    """dispatch_standard_moe with a cast config: the packed rows hold the E4M3
+    codes of the cast (the oracle's cast, dispatch and expert layout)."""
+    from test_gpu_expert import SENTINEL_INT, _fill_outputs, compare_layout
+    tdt = torch.bfloat16 if src == "bf16" else torch.float16
+    wl = workloads.custom(f"fcast_W{W}_M{M}_H{H}_k{k}_{src}", W, M, H, k, E, "bf16",
+                          ragged=True, seed_index=950 + W + k)
+    _say(f"[case] fused cast dispatch {wl.name} cap/{cap_div} scales={scale_dim}")
+    inp = workloads.make_inputs(wl)
+    g = torch.Generator().manual_seed(W * 31 + k)
+    x = (torch.randn((W, M, H), generator=g) * torch.exp(torch.randn((W, M, 1), generator=g)
+                                                          * 3)).to(tdt)
+    sc = None
+    if scale_dim:
+        sc = torch.randint(0, 256, (W, M, scale_dim * 4), generator=g, dtype=torch.uint8)
+    words = x.view(torch.int16).numpy().view(np.uint16)
+    codes = oracle.cast_to_e4m3(words, oracle.BF16 if src == "bf16" else oracle.FP16)
+    ref = oracle.dispatch(W, M, k, E // W, inp["ntok"], codes, inp["idx"].numpy(), None,
+                          None if sc is None else sc.numpy())
+    full = oracle.expert_layout(W, M, k, E // W, 1, ref["recv"], ref["src_pos"],
+                                ref["out_x"][:, :, :16], ref["out_idx"])
+    cap = max(1, int(full["count"].max()) // cap_div)
+    ref_ex = oracle.expert_layout(W, M, k, E // W, cap, ref["recv"], ref["src_pos"],
+                                  ref["out_x"], ref["out_idx"], ref["out_scales"],
+                                  fill=SENTINEL_INT)
+    cfg = cra.make_config(W, H, M, E // W, k, "fp8", "bf16", scale_dim=scale_dim,
+                          scale_type_size=4, dispatch_cast=src)
+    op = cra.EpDispatchCombineOp(cfg, with_weights=False, expert_capacity=cap)
+    ex = op._expert_state()
+    _fill_outputs(ex)
+    op.dispatch_standard_moe(x.cuda(), None, None if sc is None else sc.cuda(),
+                             inp["idx"].cuda(), num_tokens=inp["ntok"])
+    torch.cuda.synchronize()
+    compare_layout(wl, cap, op, ref_ex, wl.name)
+    op.close()
