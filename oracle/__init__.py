@@ -44,6 +44,8 @@ def _load():
     lib.oracle_expert_layout.restype = I
     lib.oracle_expert_combine.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P]
     lib.oracle_expert_combine.restype = I
+    lib.oracle_expert_combine_wire.argtypes = [I, I, I, I, I, I, I, I, P, P, P, P, P, P]
+    lib.oracle_expert_combine_wire.restype = I
     lib.oracle_f32_to_e4m3.argtypes = [ctypes.c_float]
     lib.oracle_f32_to_e4m3.restype = ctypes.c_uint8
     lib.oracle_e4m3_to_f32.argtypes = [ctypes.c_uint8]
@@ -211,6 +213,24 @@ def expert_combine(W, M, k, Er, cap, H, dtype, recv, idx, py, w=None):
                                    _ptr(py), _ptr(y))
     if rc != 0:
         raise RuntimeError(f"oracle_expert_combine failed ({rc})")
+    return y
+
+
+def expert_combine_wire(W, M, k, Er, cap, H, dtype, wire, recv, idx, py, py_scales, w=None):
+    """The inverse with the packed expert outputs on a wire: ``py`` uint8 wire
+    rows [W, Er, cap, ...], ``py_scales`` their scale rows (float32 or uint8
+    E8M0); otherwise as expert_combine."""
+    lib = _load()
+    recv = _c(np.asarray(recv, dtype=np.int32))
+    idx = _c(idx, np.int32)
+    w = _c(w, np.float32)
+    py = _c(py, np.uint8)
+    py_scales = _c(py_scales)
+    y = np.zeros((W, W * M, H), np.uint16)
+    rc = lib.oracle_expert_combine_wire(W, M, k, Er, cap, H, dtype, wire, _ptr(recv), _ptr(idx),
+                                        _ptr(w), _ptr(py), _ptr(py_scales), _ptr(y))
+    if rc != 0:
+        raise RuntimeError(f"oracle_expert_combine_wire failed ({rc})")
     return y
 
 

@@ -460,9 +460,25 @@ int oracle_expert_layout(int W, int M, int k, int Er, int cap, size_t row_bytes,
     return 0;
 }
 
-int oracle_expert_combine(int W, int M, int k, int Er, int cap, int H, int dtype,
+/* The value of element h of packed row `row`, as the inverse folds it. */
+typedef float (*packed_value_fn)(const void *src, int64_t row, int H, int h);
+
+struct packed_words {
+    const uint16_t *py;  /* [rows][H] bf16 / fp16 words */
+    int dtype;
+};
+
+static float packed_word_value(const void *src, int64_t row, int H, int h)
+{
+    const struct packed_words *s = src;
+    return widen(s->py[(size_t)row * H + h], s->dtype);
+}
+
+/* Inverse of the expert-major layout, reading packed values through `value`
+ * (the two public forms below differ only in where a value comes from). */
+static int expert_combine(int W, int M, int k, int Er, int cap, int H, int dtype,
                           const int32_t *recv, const int32_t *idx, const float *w,
-                          const uint16_t *py, uint16_t *y)
+                          packed_value_fn value, const void *src, uint16_t *y)
 {
     const int64_t WM = (int64_t)W * M;
     int32_t *js = malloc(sizeof(int32_t) * (size_t)(k > 0 ? k : 1));
@@ -500,18 +516,21 @@ int oracle_expert_combine(int W, int M, int k, int Er, int cap, int H, int dtype
                 ++kept;
             }
             uint16_t *out = y + (size_t)row * H;
-            if (!w) {
-                fold_token(kept, rows, H, k, dtype, py, NULL, out, NULL);
-                continue;
-            }
             for (int h = 0; h < H; ++h) {
                 if (kept == 0) {
                     out[h] = 0;
                     continue;
                 }
-                float acc = cw[0] * widen(py[(size_t)rows[0] * H + h], dtype);
-                for (int i = 1; i < kept; ++i)
-                    acc = fmaf(cw[i], widen(py[(size_t)rows[i] * H + h], dtype), acc);
+                /* unweighted: the first output, then plain FP32 adds (as the
+                 * combine folds); weighted: c * v, then one fused
+                 * multiply-add per later output */
+                float acc = value(src, rows[0], H, h);
+                if (w)
+                    acc = cw[0] * acc;
+                for (int i = 1; i < kept; ++i) {
+                    float v = value(src, rows[i], H, h);
+                    acc = w ? fmaf(cw[i], v, acc) : acc + v;
+                }
                 out[h] = narrow(acc, dtype);
             }
         }
@@ -521,6 +540,14 @@ int oracle_expert_combine(int W, int M, int k, int Er, int cap, int H, int dtype
     free(cw);
     free(next);
     return 0;
+}
+
+int oracle_expert_combine(int W, int M, int k, int Er, int cap, int H, int dtype,
+                          const int32_t *recv, const int32_t *idx, const float *w,
+                          const uint16_t *py, uint16_t *y)
+{
+    struct packed_words src = {py, dtype};
+    return expert_combine(W, M, k, Er, cap, H, dtype, recv, idx, w, packed_word_value, &src, y);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -698,4 +725,36 @@ int oracle_combine_wire(int W, int M, int k, int H, int dtype, int wire, const i
             }
         }
     return 0;
+}
+
+struct packed_wire {
+    const uint8_t *codes;   /* [rows][row_bytes] wire rows */
+    const uint8_t *scales;  /* [rows][scale_bytes] their scales */
+    size_t row_bytes, scale_bytes;
+    int wire;
+};
+
+static float packed_wire_value(const void *src, int64_t row, int H, int h)
+{
+    const struct packed_wire *s = src;
+    (void)H;
+    return oracle_wire_value(s->wire, s->codes + (size_t)row * s->row_bytes,
+                             s->scales + (size_t)row * s->scale_bytes, h);
+}
+
+int oracle_expert_combine_wire(int W, int M, int k, int Er, int cap, int H, int dtype, int wire,
+                               const int32_t *recv, const int32_t *idx, const float *w,
+                               const uint8_t *py, const void *py_scales, uint16_t *y)
+{
+    struct packed_wire src = {py, (const uint8_t *)py_scales, 0, 0, wire};
+    if (wire == ORACLE_WIRE_FP8_BLOCK128) {
+        src.row_bytes = (size_t)H;
+        src.scale_bytes = sizeof(float) * (size_t)(H / 128);
+    } else if (wire == ORACLE_WIRE_MXFP4) {
+        src.row_bytes = (size_t)H / 2;
+        src.scale_bytes = (size_t)(H / 32);
+    } else {
+        return -1;
+    }
+    return expert_combine(W, M, k, Er, cap, H, dtype, recv, idx, w, packed_wire_value, &src, y);
 }

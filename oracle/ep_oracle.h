@@ -185,6 +185,15 @@ int oracle_combine_wire(int W, int M, int k, int H, int dtype, int wire, const i
                         const int32_t *fwd, const uint8_t *y, const void *y_scales,
                         uint16_t *out);
 
+/* The expert-major inverse (oracle_expert_combine) with the packed expert
+ * outputs on a wire: each element is taken through oracle_wire_value (its
+ * exact FP32 value) instead of being widened from bf16 / fp16, then folded
+ * the same way.
+ *   py[W][Er][cap][...] wire rows, py_scales[W][Er][cap][...] their scales. */
+int oracle_expert_combine_wire(int W, int M, int k, int Er, int cap, int H, int dtype, int wire,
+                               const int32_t *recv, const int32_t *idx, const float *w,
+                               const uint8_t *py, const void *py_scales, uint16_t *y);
+
 /* IEEE 754 conversions used by the combine cast, written from the formats'
  * definitions: binary32 -> bfloat16 / binary16 with round-to-nearest-even,
  * overflow to infinity, NaN to a quiet NaN; and the exact widenings back. */

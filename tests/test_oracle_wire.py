@@ -170,3 +170,55 @@ def test_combine_from_wire_equals_combine_of_exact_dequantized_rows(wire):
     got = oracle.combine_wire(W, M, k, H, oracle.BF16, wire, inp["ntok"], disp["fwd"],
                               codes.reshape(W, W * M, -1), scales.reshape(W, W * M, -1))
     assert np.array_equal(got, ref)
+
+
+E2M1_VALUES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]  # the MX specification's E2M1 list
+
+
+def _decoded_wire_rows(rng, n, H, wire):
+    """Random wire rows whose values are exact in bf16 (power-of-two scales
+    near 1), and those values decoded independently of the oracle: FP8 by
+    torch's float8_e4m3fn, MXFP4 by the specification's table."""
+    if wire == oracle.WIRE_FP8_BLOCK128:
+        codes = rng.integers(0, 256, (n, H), dtype=np.uint8)
+        codes[(codes & 0x7F) == 0x7F] = 0x3C          # no NaN codes
+        scales = np.ldexp(1.0, rng.integers(-4, 5, (n, H // 128))).astype(np.float32)
+        vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+        vals = vals * np.repeat(scales, 128, axis=1)
+        return codes, scales, vals.astype(np.float32)
+    codes = rng.integers(0, 256, (n, H // 2), dtype=np.uint8)
+    scales = rng.integers(120, 135, (n, H // 32), dtype=np.uint8)
+    nib = np.empty((n, H), np.uint8)
+    nib[:, 0::2] = codes & 0xF
+    nib[:, 1::2] = codes >> 4
+    mag = np.array(E2M1_VALUES, np.float32)[nib & 7]
+    vals = np.where(nib & 8, -mag, mag) * np.ldexp(1.0, np.repeat(scales.astype(np.int64) - 127,
+                                                                  32, axis=1))
+    return codes, scales, vals.astype(np.float32)
+
+
+@pytest.mark.parametrize("wire", [oracle.WIRE_FP8_BLOCK128, oracle.WIRE_MXFP4])
+@pytest.mark.parametrize("weighted", [False, True])
+@pytest.mark.parametrize("cap", [3, 64])
+def test_expert_combine_wire_equals_the_inverse_of_its_decoded_values(wire, weighted, cap):
+    """The inverse from wire rows folds each element's exact value: with
+    values exact in bf16 it equals the (pinned) inverse of those bf16 rows,
+    plain and weighted, with and without capacity drops."""
+    W, M, k, Er, H = 3, 20, 5, 4, 256
+    rng = np.random.default_rng(17 + wire + 2 * weighted + cap)
+    ntok = [20, 7, 13]
+    idx = rng.integers(-1, W * Er + 1, (W, M, k)).astype(np.int32)
+    w = rng.random((W, M, k)).astype(np.float32)
+    x = rng.integers(0, 256, (W, M, 16), dtype=np.uint8)
+    ref = oracle.dispatch(W, M, k, Er, ntok, x, idx, w)
+    codes, scales, vals = _decoded_wire_rows(rng, W * Er * cap, H, wire)
+    words = oracle.f32_to_bf16(vals.reshape(-1)).reshape(W, Er, cap, H)
+    assert np.array_equal(oracle.bf16_to_f32(words.reshape(-1)), vals.reshape(-1))  # exact
+    wt = ref["out_w"] if weighted else None
+    got = oracle.expert_combine_wire(W, M, k, Er, cap, H, oracle.BF16, wire, ref["recv"],
+                                     ref["out_idx"], codes.reshape(W, Er, cap, -1),
+                                     scales.reshape(W, Er, cap, -1), w=wt)
+    want = oracle.expert_combine(W, M, k, Er, cap, H, oracle.BF16, ref["recv"], ref["out_idx"],
+                                 words, w=wt)
+    assert np.array_equal(got, want)
+    assert got.any()
