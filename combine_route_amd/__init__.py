@@ -93,7 +93,8 @@ class EpDispatchStandardArgs(ctypes.Structure):
 
 
 class EpCombineStandardArgs(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("packed_y", "indices", "weights", "out")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("packed_y", "indices", "weights", "out",
+                                               "packed_y_scales")]
 
 
 class EpError(RuntimeError):
@@ -451,12 +452,15 @@ def _dispatch_standard_args(cfg: EpConfig, cap: int, num_tokens: Sequence[int], 
     return a, arr
 
 
-def _combine_standard_args(cfg: EpConfig, cap: int, packed_y, indices, weights, out):
+def _combine_standard_args(cfg: EpConfig, cap: int, packed_y, indices, weights, out,
+                           packed_y_scales=None):
     W, M, k, _, crow, _ = _sizes(cfg)
     Er = cfg.num_experts_per_rank
+    yrow, srow = wire_row_bytes(cfg) if cfg.combine_wire else (crow, 0)
     return EpCombineStandardArgs(
-        _dev(packed_y, "packed_y", W * Er * cap * crow), _dev(indices, "indices", W * M * k * 4),
-        _dev(weights, "weights", W * M * k * 4), _dev(out, "out", W * M * crow))
+        _dev(packed_y, "packed_y", W * Er * cap * yrow), _dev(indices, "indices", W * M * k * 4),
+        _dev(weights, "weights", W * M * k * 4), _dev(out, "out", W * M * crow),
+        _dev(packed_y_scales, "packed_y_scales", W * Er * cap * srow))
 
 
 def ep_dispatch_standard_moe(eplan: int, cfg: EpConfig, cap: int, num_tokens, x, indices, scales,
@@ -471,9 +475,9 @@ def ep_dispatch_standard_moe(eplan: int, cfg: EpConfig, cap: int, num_tokens, x,
 
 
 def ep_combine_standard_moe(eplan: int, cfg: EpConfig, cap: int, packed_y, indices, weights, out,
-                            stream=None) -> None:
+                            stream=None, packed_y_scales=None) -> None:
     """ep_combine_standard_moe(); tensors as in include/ep.h."""
-    a = _combine_standard_args(cfg, cap, packed_y, indices, weights, out)
+    a = _combine_standard_args(cfg, cap, packed_y, indices, weights, out, packed_y_scales)
     _check("ep_combine_standard_moe",
            load().ep_combine_standard_moe(eplan, ctypes.byref(a), _stream(stream)))
 
@@ -665,24 +669,28 @@ class EpDispatchCombineOp:
                                                                   ex["packed_scales"])
         return px, ex["packed_count"], ex["packed_src_info"], ex["packed_layout_range"]
 
-    def combine_standard_moe(self, input, weights, indices, call_reset=False, stream=None):
+    def combine_standard_moe(self, input, weights, indices, call_reset=False, stream=None,
+                             input_scales=None):
         """Combine straight from the expert-major layout ("MORI-EP User Guide",
         section 4, combine_standard_moe): input [W, Er, cap, H] holds the
         experts' outputs for the last dispatch_standard_moe, indices its ids;
         weights [W, M, k] (or None for the plain sum) are applied as
         convert_combine_input(apply_weights=True) would. The result equals
         convert_combine_input() followed by combine(). call_reset is taken
-        for the pages' signature: nothing needs resetting. Returns [W, M, H]
-        (rows t < T_r written), a view of the op's combine output buffer."""
+        for the pages' signature: nothing needs resetting. With a combine
+        wire in the config, input holds wire rows and input_scales their
+        scales (ep_quantize_rows writes both, with counts=packed_count).
+        Returns [W, M, H] (rows t < T_r written), a view of the op's combine
+        output buffer."""
         ex = self._ex
         if ex is None:
             raise EpError("ep_combine_standard_moe", EP_ERR_STATE,
                           "combine_standard_moe before any dispatch_standard_moe")
-        given = (input, weights, indices)
+        given = (input, weights, indices, input_scales)
         c = ex.get("ccache")
         if c is None or not _same_tensors(c[0], given):
             a = _combine_standard_args(self.cfg, self.expert_capacity, input, indices, weights,
-                                       self.combine_out)
+                                       self.combine_out, input_scales)
             c = ex["ccache"] = (_hold(given), a)
         _check("ep_combine_standard_moe", self._lib.ep_combine_standard_moe(
             ex["plan"], ctypes.byref(c[1]), _stream(stream, self._dev_index)))

@@ -158,13 +158,17 @@ struct StandardArgs {
 };
 
 struct StandardCombineArgs {
-    const uint8_t* py;           // [W * Er][cap][H] expert outputs, combine dtype
+    const uint8_t* py;           // [W * Er][cap] expert outputs: combine dtype or wire rows
+    const uint8_t* pys;          // [W * Er][cap] wire scale rows, or null
     const int32_t* idx;          // [W][M][k]
     const float* w;              // [W][M][k] routing weights to apply, or null
     const int32_t* fslot;        // [W][M][k]
     uint8_t* out;                // [W][M][H]
-    int32_t row_vecs;            // 16-byte vectors per row
-    int32_t piece_vecs;
+    int32_t row_vecs;            // 16-byte vectors (8 elements) per output row
+    int32_t piece_vecs;          // with a wire: a multiple of 16, at most 1024
+    uint32_t py_row_bytes;       // bytes per wire row (unused without a wire)
+    uint32_t py_scale_bytes;     // bytes per wire scale row
+    int32_t wire;                // 0, kWireFp8Block128 or kWireMxfp4
     int32_t M, k, Er, E;
 };
 

@@ -1246,9 +1246,16 @@ int ep_combine_standard_moe(ep_expert_plan_t* x, const ep_combine_standard_args_
         return fail(EP_ERR_NULL, "args is NULL");
     ep_plan* p = x->plan;
     const Shape& s = p->s;
-    if (p->cfg.combine_wire != EP_WIRE_NONE)
-        return fail(EP_ERR_ARG, "the fused combine reads combine_dtype rows: the config's "
-                    "combine_wire must be EP_WIRE_NONE");
+    const int wire = p->cfg.combine_wire;
+    if (wire != EP_WIRE_NONE) {
+        if (!a->packed_y_scales)
+            return fail(EP_ERR_NULL, "args.packed_y_scales is required with a combine_wire");
+        if (!aligned(a->packed_y_scales, 4))
+            return fail(EP_ERR_ALIGN, "args.packed_y_scales must be 4-byte aligned");
+    } else if (a->packed_y_scales) {
+        return fail(EP_ERR_ARG,
+                    "args.packed_y_scales must be NULL when cfg.combine_wire = EP_WIRE_NONE");
+    }
     if (!a->packed_y)
         return fail(EP_ERR_NULL, "args.packed_y is NULL");
     if (!a->indices)
@@ -1267,6 +1274,13 @@ int ep_combine_standard_moe(ep_expert_plan_t* x, const ep_combine_standard_args_
 
     ep::StandardCombineArgs ca;
     ca.py = static_cast<const uint8_t*>(a->packed_y);
+    ca.pys = static_cast<const uint8_t*>(a->packed_y_scales);
+    ca.wire = wire == EP_WIRE_FP8_BLOCK128 ? ep::kWireFp8Block128
+              : wire == EP_WIRE_MXFP4      ? ep::kWireMxfp4
+                                           : 0;
+    ca.py_row_bytes = wire == EP_WIRE_FP8_BLOCK128 ? (uint32_t)s.H : (uint32_t)s.H / 2u;
+    ca.py_scale_bytes =
+        wire == EP_WIRE_FP8_BLOCK128 ? (uint32_t)(s.H / 128 * 4) : (uint32_t)(s.H / 32);
     ca.idx = a->indices;
     ca.w = a->weights;
     ca.fslot = reinterpret_cast<const int32_t*>(x->ws + x->e.off_efwd);
@@ -1285,6 +1299,11 @@ int ep_combine_standard_moe(ep_expert_plan_t* x, const ep_combine_standard_args_
         split = (int)std::min<int64_t>(max_split, std::max<int64_t>(1, (1024 + blocks - 1) / blocks));
     }
     ca.piece_vecs = (ca.row_vecs + split - 1) / split;
+    if (ca.wire) {
+        // pieces start on a scale dword (16 groups of 8 elements) and a lane
+        // holds one dword of each pair's scale row
+        ca.piece_vecs = std::min((ca.piece_vecs + 15) / 16 * 16, 16 * ep::kWave);
+    }
     const int row_split = (ca.row_vecs + ca.piece_vecs - 1) / ca.piece_vecs;
     const int dtype = p->cfg.combine_dtype == EP_BF16 ? 0 : 1;
 

@@ -380,7 +380,9 @@ constexpr int kFoldFirst = 1;
 constexpr int kFoldLast = 2;
 constexpr int kFoldGap = 4;
 
-template <int G, int U, int DT, bool kStream, bool kWeighted>
+// WIRE: 0 for bf16 / fp16 expert outputs, else the wire of the packed rows
+// (kWireFp8Block128, kWireMxfp4), each element decoded exactly before the fold.
+template <int G, int U, int DT, bool kStream, bool kWeighted, int WIRE>
 __global__ __launch_bounds__(1024) void sx_combine_kernel(StandardCombineArgs a, TokenMap tk)
 {
     const int lane = threadIdx.x & (kWave - 1);
@@ -457,32 +459,77 @@ __global__ __launch_bounds__(1024) void sx_combine_kernel(StandardCombineArgs a,
     const int dlast = nk > 0 ? __builtin_amdgcn_readlane(dx, nk - 1) : -1;
     const bool trailing = nD - 1 > dlast;  // ranks without a kept pair after the last
 
-    const uint32_t row_bytes = (uint32_t)a.row_vecs * 16u;
+    const uint32_t row_bytes = (uint32_t)a.row_vecs * 16u;  // an output row
     const __amdgpu_buffer_rsrc_t rdst = row_rsrc(a.out + tok * row_bytes, row_bytes);
     const int vbeg = piece * a.piece_vecs;
     const int vend = min(a.row_vecs, vbeg + a.piece_vecs);
+    // Wire rows: lane l holds dword vbeg / 16 + l of the scale row of each
+    // kept pair of the current group of G (a dword covers 16 groups of 8
+    // elements), loaded once when the token has at most G pairs.
+    uint32_t spre[WIRE ? G : 1];
+    auto load_scales = [&](int i0) {
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+            if (i0 + q < nk) {
+                const int64_t gq = __builtin_amdgcn_readlane(gl, i0 + q);
+                const __amdgpu_buffer_rsrc_t rs =
+                    row_rsrc(a.pys + gq * a.py_scale_bytes, a.py_scale_bytes);
+                const uint32_t off = (uint32_t)(vbeg / 16 + lane) * 4u;
+                if (WIRE == kWireFp8Block128 || a.py_scale_bytes % 4 == 0) {
+                    spre[q] = __builtin_amdgcn_raw_buffer_load_b32(
+                        rs, off, 0, Policy<kStream>::combine_load);
+                } else {  // MXFP4 scale rows that are not whole dwords: by bytes
+                    uint32_t d = 0;
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        d |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(
+                                 rs, off + b, 0, Policy<kStream>::combine_load)
+                             << (8 * b);
+                    spre[q] = d;
+                }
+            }
+        }
+    };
+    const bool regroup = nk > G;  // uniform
+    if constexpr (WIRE != 0) {
+        if (!regroup)
+            load_scales(0);
+    }
     for (int v0 = vbeg; v0 < vend; v0 += kWave * U) {
         float tot[U][8], part[U][8];
         bool have = false;  // uniform: tot holds a rank's contribution
         for (int i0 = 0; i0 < nk; i0 += G) {
-            u32x4 rows[U][G];
+            if constexpr (WIRE != 0) {
+                if (regroup)
+                    load_scales(i0);
+            }
+            u32x4 rows[WIRE ? 1 : U][WIRE ? 1 : G];   // bf16 / fp16 rows: 16 B a group
+            u32x2 codes[WIRE ? U : 1][WIRE ? G : 1];  // wire rows: 8 B (FP8) or 4 B (MXFP4)
 #pragma unroll
             for (int q = 0; q < G; ++q) {
                 if (i0 + q < nk) {
                     const int64_t gq = __builtin_amdgcn_readlane(gl, i0 + q);
-                    const __amdgpu_buffer_rsrc_t ry = row_rsrc(a.py + gq * row_bytes, row_bytes);
+                    const uint32_t pb = WIRE ? a.py_row_bytes : row_bytes;
+                    const __amdgpu_buffer_rsrc_t ry = row_rsrc(a.py + gq * pb, pb);
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         const int v = v0 + u * kWave + lane;
-                        if (v < vend)
-                            rows[u][q] = bload16<Policy<kStream>::combine_load>(
-                                ry, (uint32_t)v * 16u);
+                        if (v < vend) {
+                            constexpr int ld = Policy<kStream>::combine_load;
+                            if constexpr (WIRE == 0)
+                                rows[u][q] = bload16<ld>(ry, (uint32_t)v * 16u);
+                            else if constexpr (WIRE == kWireFp8Block128)
+                                codes[u][q] = __builtin_amdgcn_raw_buffer_load_b64(ry, v * 8, 0, ld);
+                            else
+                                codes[u][q] = {__builtin_amdgcn_raw_buffer_load_b32(ry, v * 4, 0, ld),
+                                               0u};
+                        }
                     }
                 }
             }
 #pragma unroll
             for (int q = 0; q < G; ++q) {
-                if (i0 + q < nk) {
+                if (i0 + q < nk) {  // uniform: every lane takes part in the cross-lane reads
                     const int fl = __builtin_amdgcn_readlane(flags, i0 + q);
                     const float cq =
                         kWeighted ? __builtin_bit_cast(
@@ -495,7 +542,16 @@ __global__ __launch_bounds__(1024) void sx_combine_kernel(StandardCombineArgs a,
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         float f[8];
-                        widen<DT>(rows[u][q], f);
+                        if constexpr (WIRE == 0) {
+                            widen<DT>(rows[u][q], f);
+                        } else {
+                            const int v = v0 + u * kWave + lane;
+                            const uint32_t d = (uint32_t)__shfl((int)spre[q], (v - vbeg) >> 4);
+                            // MXFP4: byte (v / 4) mod 4 of the dword
+                            const uint32_t sb =
+                                WIRE == kWireFp8Block128 ? d : d >> (8 * ((v >> 2) & 3));
+                            decode_group<WIRE>(codes[u][q], sb, f);
+                        }
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
                             if (gap)  // ranks whose intermediate rows are +0
@@ -568,15 +624,28 @@ hipError_t sx_copy_with_vpl(const StandardArgs& a, dim3 grid, dim3 block, bool s
     }
 }
 
-template <int G, int U, int DT, bool kStream>
+template <int G, int U, int DT, bool kStream, int WIRE>
 void sx_combine_launch(const StandardCombineArgs& a, const TokenMap& tk, dim3 grid, dim3 block,
                        hipStream_t s)
 {
     if (a.w)
-        hipLaunchKernelGGL((sx_combine_kernel<G, U, DT, kStream, true>), grid, block, 0, s, a, tk);
+        hipLaunchKernelGGL((sx_combine_kernel<G, U, DT, kStream, true, WIRE>), grid, block, 0, s,
+                           a, tk);
     else
-        hipLaunchKernelGGL((sx_combine_kernel<G, U, DT, kStream, false>), grid, block, 0, s, a,
-                           tk);
+        hipLaunchKernelGGL((sx_combine_kernel<G, U, DT, kStream, false, WIRE>), grid, block, 0, s,
+                           a, tk);
+}
+
+template <int G, int U, int DT, bool kStream>
+void sx_combine_wire(const StandardCombineArgs& a, const TokenMap& tk, dim3 grid, dim3 block,
+                     hipStream_t s)
+{
+    if (a.wire == kWireFp8Block128)
+        sx_combine_launch<G, U, DT, kStream, kWireFp8Block128>(a, tk, grid, block, s);
+    else if (a.wire == kWireMxfp4)
+        sx_combine_launch<G, U, DT, kStream, kWireMxfp4>(a, tk, grid, block, s);
+    else
+        sx_combine_launch<G, U, DT, kStream, 0>(a, tk, grid, block, s);
 }
 
 template <int G, int U>
@@ -585,14 +654,14 @@ hipError_t sx_combine_with(const StandardCombineArgs& a, const TokenMap& tk, int
 {
     if (dtype == 0) {
         if (stream)
-            sx_combine_launch<G, U, 0, true>(a, tk, grid, block, s);
+            sx_combine_wire<G, U, 0, true>(a, tk, grid, block, s);
         else
-            sx_combine_launch<G, U, 0, false>(a, tk, grid, block, s);
+            sx_combine_wire<G, U, 0, false>(a, tk, grid, block, s);
     } else {
         if (stream)
-            sx_combine_launch<G, U, 1, true>(a, tk, grid, block, s);
+            sx_combine_wire<G, U, 1, true>(a, tk, grid, block, s);
         else
-            sx_combine_launch<G, U, 1, false>(a, tk, grid, block, s);
+            sx_combine_wire<G, U, 1, false>(a, tk, grid, block, s);
     }
     return hipGetLastError();
 }

@@ -147,48 +147,6 @@ __global__ __launch_bounds__(256) void ep_quantize_kernel(QuantizeArgs a)
     }
 }
 
-// A lane decodes groups of 8 elements, inside one scale block: 8 bytes of
-// FP8 codes (two dwords) or 4 bytes of MXFP4 codes (one dword). Its 8 results
-// are one 16-byte store, so a wave's store covers 1 KiB contiguously.
-constexpr int kGroupElems = 8;
-
-// Decode one group into FP32 with the hardware conversions, which are exact:
-// an E4M3 code to FP32 (v_cvt_pk_f32_fp8), then one FP32 multiply by the
-// block scale; an E2M1 code times the power-of-two scale (v_cvt_scalef32_pk_
-// f32_fp4). Code order follows the row: byte i of dword d holds FP8 element
-// 4d + i; the low nibble of byte b holds MXFP4 element 2b.
-template <int WIRE>
-__device__ __forceinline__ void decode_group(const u32x2& c, uint32_t sbits,
-                                             float (&f)[kGroupElems])
-{
-    if constexpr (WIRE == kWireFp8Block128) {
-        const float s = __builtin_bit_cast(float, sbits);
-#pragma unroll
-        for (int d = 0; d < 2; ++d) {
-            const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(c[d], false);
-            const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(c[d], true);
-            f[4 * d + 0] = lo.x * s;
-            f[4 * d + 1] = lo.y * s;
-            f[4 * d + 2] = hi.x * s;
-            f[4 * d + 3] = hi.y * s;
-        }
-    } else {
-        const float s = __builtin_ldexpf(1.0f, (int)(sbits & 0xFFu) - 127);
-        const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[0], s, 0);
-        const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[0], s, 1);
-        const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[0], s, 2);
-        const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[0], s, 3);
-        f[0] = v0.x;
-        f[1] = v0.y;
-        f[2] = v1.x;
-        f[3] = v1.y;
-        f[4] = v2.x;
-        f[5] = v2.y;
-        f[6] = v3.x;
-        f[7] = v3.y;
-    }
-}
-
 // 8-element groups a lane decodes at once per contribution row: C columns a
 // wave apart (group h and h + 64), so every load and store instruction of
 // the wave covers one contiguous span; a lane reads 8 * C bytes of FP8 codes

@@ -550,12 +550,19 @@ int ep_dispatch_standard_moe(ep_expert_plan_t *plan, const ep_dispatch_standard_
  *             sum).
  *   out       [W][M][H] combine_dtype: rows t < T_r of the last fused
  *             dispatch are written, others untouched. Must not overlap
- *             packed_y. */
+ *             packed_y.
+ *   packed_y_scales  with a combine_wire config, packed_y holds the outputs
+ *             as wire rows ([W][Er][cap] rows of that format, as
+ *             ep_quantize_rows writes them) and this their scale rows
+ *             ([W][Er][cap][H / 128] float or [W][Er][cap][H / 32] E8M0,
+ *             4-byte aligned); each element is decoded to its exact value
+ *             before the fold. NULL iff combine_wire is EP_WIRE_NONE. */
 typedef struct ep_combine_standard_args {
     const void *packed_y;
     const int32_t *indices;
     const float *weights;
     void *out;
+    const void *packed_y_scales;
 } ep_combine_standard_args_t;
 
 /* Combine straight from the expert-major layout ([GUIDE4]
@@ -568,8 +575,7 @@ typedef struct ep_combine_standard_args {
  * nearest even. A rank whose pairs were all dropped adds +0. Uses the map of
  * the last ep_dispatch_standard_moe on this expert plan. Asynchronous; no
  * allocation; capturable; may be called any number of times per dispatch.
- * The config must have no combine_wire.
- * Errors: EP_ERR_NULL, EP_ERR_ALIGN, EP_ERR_ARG (a combine_wire config),
+ * Errors: EP_ERR_NULL, EP_ERR_ALIGN, EP_ERR_ARG (packed_y_scales pairing),
  * EP_ERR_STATE (no fused dispatch yet on this expert plan), EP_ERR_HIP. */
 int ep_combine_standard_moe(ep_expert_plan_t *plan, const ep_combine_standard_args_t *args,
                             void *stream);

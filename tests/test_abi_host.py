@@ -465,14 +465,26 @@ def test_dispatch_standard_rejects_before_launch(lib, over, code, word):
     lib.ep_plan_destroy(plan)
 
 
-def test_standard_combine_refuses_wire_configs(lib):
+def test_combine_standard_scales_pairing(lib):
+    """A combine wire needs the packed outputs' scale rows; no wire, none."""
     cfg = cra.make_config(8, 7168, 128, 32, 8, combine_wire="mxfp4")
     rc, plan = make_plan(lib, cfg)
     rc, ex = make_expert(lib, plan, 64)
     c = cra.EpCombineStandardArgs(packed_y=FAKE, indices=FAKE + 0x1000, weights=None,
-                                  out=FAKE + 0x2000)
+                                  out=FAKE + 0x2000, packed_y_scales=None)
+    assert lib.ep_combine_standard_moe(ex, ctypes.byref(c), None) == cra.EP_ERR_NULL
+    assert "packed_y_scales" in cra.ep_last_error()
+    c.packed_y_scales = FAKE + 0x3002
+    assert lib.ep_combine_standard_moe(ex, ctypes.byref(c), None) == cra.EP_ERR_ALIGN
+    c.packed_y_scales = FAKE + 0x3000
+    assert lib.ep_combine_standard_moe(ex, ctypes.byref(c), None) == cra.EP_ERR_STATE
+    lib.ep_expert_plan_destroy(ex)
+    lib.ep_plan_destroy(plan)
+    cfg = cra.make_config(8, 7168, 128, 32, 8)
+    rc, plan = make_plan(lib, cfg)
+    rc, ex = make_expert(lib, plan, 64)
     assert lib.ep_combine_standard_moe(ex, ctypes.byref(c), None) == cra.EP_ERR_ARG
-    assert "combine_wire" in cra.ep_last_error()
+    assert "packed_y_scales" in cra.ep_last_error()
     lib.ep_expert_plan_destroy(ex)
     lib.ep_plan_destroy(plan)
 

@@ -323,3 +323,108 @@ def test_graph_replay_matches_oracle():
             assert np.array_equal(got[r, :ntok[r]], ro[r, :ntok[r]]), ("graph", rep, r)
         del junk
     op.close()
+
+
+WIRES = {"fp8_block128": (cra.EP_WIRE_FP8_BLOCK128, oracle.WIRE_FP8_BLOCK128),
+         "mxfp4": (cra.EP_WIRE_MXFP4, oracle.WIRE_MXFP4)}
+
+
+def run_standard_wire_case(wl, name, cap_div=1, weighted=False, tag=None, cols=None):
+    """The fused combine from quantized expert outputs: the packed outputs are
+    quantized on the GPU with the per-expert counts (checked against the
+    oracle's quantizer on every kept row), then the oracle's own codes go to
+    the fused combine, compared with the oracle's wire inverse and combine."""
+    cw, ow = WIRES[name]
+    W, M, k, Er, H = _dims(wl)
+    inp = workloads.make_inputs(wl)
+    ref = oracle_dispatch(wl, inp)
+    cap = max(1, max_count(wl, ref) // cap_div)
+    tag = tag or f"std wire {name} {wl.name} cap={cap} w={weighted}"
+    _say(f"[case] {tag}: W={W} M={M} H={H} k={k} Er={Er}")
+    cfg = cra.make_config(W, H, M, Er, k, wl.dispatch_dtype, wl.combine_dtype,
+                          scale_dim=wl.scale_dim, scale_type_size=4, combine_wire=cw)
+    op = cra.EpDispatchCombineOp(cfg, with_weights=False, expert_capacity=cap)
+    x, idx, sc = _dev(inp["x"]), _dev(inp["idx"]), _dev(inp["scales"])
+    _, cnt, _, _ = op.dispatch_standard_moe(x, None, sc, idx, num_tokens=inp["ntok"])
+    dt = oracle.BF16 if wl.combine_dtype == "bf16" else oracle.FP16
+    cdt = workloads.TORCH_DTYPE[wl.combine_dtype]
+    # up to 512 distinct seeded rows, repeated over the packed rows, so the
+    # oracle quantizes few rows
+    g = torch.Generator().manual_seed(sum(tag.encode()) % 10007)
+    base = min(512, W * Er * cap)
+    vb = (torch.randn((base, H), generator=g)
+          * torch.exp(torch.randn((base, 1), generator=g))).to(cdt)
+    cb, sb = oracle.quantize_rows(vb.view(torch.int16).numpy().view(np.uint16), dt, ow)
+    sel = np.arange(W * Er * cap) % base
+    v = vb[torch.from_numpy(sel)]
+    codes, scales = cb[sel], sb[sel]
+    row, srow = (H, H // 128 * 4) if cw == cra.EP_WIRE_FP8_BLOCK128 else (H // 2, H // 32)
+    # the send side on the GPU: only the kept rows of each expert are converted
+    yq = torch.zeros((W * Er, cap, row), dtype=torch.uint8, device="cuda")
+    ys = torch.zeros((W * Er, cap, srow), dtype=torch.uint8, device="cuda")
+    cra.ep_quantize_rows(v.cuda().view(W * Er, cap, H), cw, yq, ys, counts=cnt.view(-1))
+    torch.cuda.synchronize()
+    gq, gs = yq.cpu().numpy(), ys.cpu().numpy()
+    cn = cnt.cpu().numpy().reshape(-1)
+    cq = codes.reshape(W * Er, cap, row)
+    cs = scales.view(np.uint8).reshape(W * Er, cap, srow)
+    for e in range(W * Er):
+        n = min(int(cn[e]), cap)
+        assert np.array_equal(gq[e, :n], cq[e, :n]), (tag, "quantized rows", e)
+        assert np.array_equal(gs[e, :n], cs[e, :n]), (tag, "quantized scales", e)
+    w = _dev(inp["w"]) if weighted else None
+    out = op.combine_standard_moe(torch.from_numpy(cq.copy()).cuda(), w, idx,
+                                  input_scales=torch.from_numpy(cs.copy()).cuda())
+    torch.cuda.synchronize()
+    # cols: the oracle sees only the first cols columns of every row (and
+    # their scale blocks); every column's sums depend on that column alone
+    Ho = cols or H
+    oc = codes[:, :Ho if cw == cra.EP_WIRE_FP8_BLOCK128 else Ho // 2]
+    osc = scales[:, :Ho // 128] if cw == cra.EP_WIRE_FP8_BLOCK128 else scales[:, :Ho // 32]
+    ref_y = oracle.expert_combine_wire(W, M, k, Er, cap, Ho, dt, ow, ref["recv"], ref["out_idx"],
+                                       np.ascontiguousarray(oc).reshape(W, Er, cap, -1),
+                                       np.ascontiguousarray(osc).reshape(W, Er, cap, -1),
+                                       w=ref["out_w"] if weighted else None)
+    ro, _ = oracle.combine(W, M, k, Ho, dt, inp["ntok"], ref["fwd"], ref_y)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    for r in range(W):
+        T = inp["ntok"][r]
+        assert np.array_equal(got[r, :T, :Ho], ro[r, :T]), (tag, "fused wire combine", r)
+    op.close()
+
+
+@pytest.mark.parametrize("name", list(WIRES))
+@pytest.mark.parametrize("wl_name", ["ep8_t128_h7168_fp8_k8_zipf",
+                                     "ep4_ragged1024_h2048_fp16_k64"])
+def test_wire_full_size(name, wl_name):
+    """Two workloads at full size (the oracle's wire inverse of the headline's
+    1.9 G packed elements would take minutes; its wire combines are covered
+    by the rank-level wire tests and the bench's checks)."""
+    run_standard_wire_case(workloads.WORKLOADS[wl_name], name, weighted=True)
+
+
+@pytest.mark.parametrize("name", list(WIRES))
+def test_wire_headline_first_block(name):
+    """The headline at full size in the bench's geometry; the oracle checks the
+    first 128 columns of every token (its wire inverse of all 7168 would take
+    minutes), the GPU computes whole rows."""
+    run_standard_wire_case(workloads.WORKLOADS[workloads.HEADLINE], name, weighted=True,
+                           cols=128)
+
+
+@pytest.mark.parametrize("name", list(WIRES))
+@pytest.mark.parametrize("W,E,k,H,cap_div,weighted", [
+    (2, 16, 8, 256, 2, False), (4, 64, 16, 1024, 1, True), (16, 48, 24, 128, 3, True),
+    (3, 12, 5, 384, 1000, False)])
+def test_wire_shapes_and_drops(name, W, E, k, H, cap_div, weighted):
+    wl = workloads.custom(f"stdw_W{W}_E{E}_k{k}_H{H}", W, 40 if W <= 4 else 12, H, k, E, "bf16",
+                          ragged=True, seed_index=580 + W + k)
+    run_standard_wire_case(wl, name, cap_div=cap_div, weighted=weighted)
+
+
+@pytest.mark.parametrize("H,k", [(160, 6), (96, 24)])
+def test_mxfp4_scale_rows_not_whole_dwords(H, k):
+    """MXFP4 at H not a multiple of 128: the scale rows are read by bytes."""
+    wl = workloads.custom(f"stdw_mx_H{H}_k{k}", 4, 24, H, k, 32, "bf16", ragged=True,
+                          seed_index=590 + k)
+    run_standard_wire_case(wl, "mxfp4", cap_div=2, weighted=True)
