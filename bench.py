@@ -50,7 +50,9 @@ COUNTER_KERNELS = {
     "ex_combine_kernel": r"ex_combine_kernel<",
     "sx_copy_kernel": r"sx_copy_kernel<[^>]*, false>",
     "sx_copy_kernel_cast": r"sx_copy_kernel<[^>]*, true>",
-    "sx_combine_kernel": r"sx_combine_kernel<",
+    "sx_combine_kernel": r"sx_combine_kernel<[^>]*, 0>",
+    "sx_combine_kernel_fp8_block128": r"sx_combine_kernel<[^>]*, 1>",
+    "sx_combine_kernel_mxfp4": r"sx_combine_kernel<[^>]*, 2>",
     "ep_copy_kernel_cast": r"ep_copy_kernel<[^>]*, true>",
     "ep_quantize_kernel_fp8_block128": r"ep_quantize_kernel<1,",
     "ep_quantize_kernel_mxfp4": r"ep_quantize_kernel<2,",
@@ -420,7 +422,34 @@ def measure_quantized_wires(args, cra, torch, np, wl, inp, stream):
         rows = R
         qb = rows * (2 * H + row + srow)
         cb = R * (row + srow + 4 * k) + N * (2 * H + 4 * k) + N * P * 4
+        # the fused path from quantized expert outputs: the packed outputs
+        # quantized with the per-expert counts, then the fused combine
+        cap = expert_capacity(wl, ntok)
+        fop = cra.EpDispatchCombineOp(cfg, device=dev, with_weights=False, expert_capacity=cap)
+        fex = fop._expert_state()
+        fop.dispatch_standard_moe(x, None, sc, idx, num_tokens=ntok, stream=stream)
+        pairs = int(fex["packed_count"].clamp(max=cap).sum().item())
+        g = torch.Generator(device="cuda").manual_seed(13)
+        py = torch.randn((W * Er, cap, H), generator=g, device=dev).to(cdt)
+        pq = torch.empty((W * Er, cap, row), dtype=torch.uint8, device=dev)
+        ps = torch.empty((W * Er, cap, srow), dtype=torch.uint8, device=dev)
+        pstep = lambda: cra.ep_quantize_rows(py, wire, pq, ps, stream=stream,
+                                             counts=fex["packed_count"].view(-1))
+        pms = _timed(torch, stream, pstep, args.steps, args.warmup)
+        fstep = lambda: fop.combine_standard_moe(pq, w, idx, stream=stream, input_scales=ps)
+        fms = _timed(torch, stream, fstep, args.steps, args.warmup)
+        fkms = _kernel_ms(cra, torch, fop.plan, cra.EP_KERNEL_STANDARD_COMBINE, fstep, args.steps)
+        fb = pairs * (row + srow) + N * (2 * H + 12 * k)
+        fused = {"quantize_us_per_call": round(pms * 1e3, 2), "kept_pairs": pairs,
+                 "combine_us_per_call": round(fms * 1e3, 2),
+                 "combine_kernel_us": round(fkms * 1e3, 2),
+                 "roofline_combine": _roof(fb, fkms, "sx_combine_kernel (wire)", wl.name,
+                                           "sx_combine_kernel_" + name)}
+        fop.close()
+        del fop, fex, py, pq, ps
+        torch.cuda.empty_cache()
         out["combine_" + name] = {
+            "standard_moe": fused,
             "wire_bytes_per_row": row + srow, "bf16_bytes_per_row": 2 * H,
             "combine_us_per_call": round(cms * 1e3, 2), "combine_kernel_us": round(kms * 1e3, 2),
             "quantize_us_per_call": round(qms * 1e3, 2),
