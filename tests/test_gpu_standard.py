@@ -428,3 +428,37 @@ def test_mxfp4_scale_rows_not_whole_dwords(H, k):
     wl = workloads.custom(f"stdw_mx_H{H}_k{k}", 4, 24, H, k, 32, "bf16", ragged=True,
                           seed_index=590 + k)
     run_standard_wire_case(wl, "mxfp4", cap_div=2, weighted=True)
+
+
+def _random_standard_case(seed):
+    """A seeded random configuration for the fused path, small enough for the
+    oracle to finish in well under a second."""
+    rng = np.random.default_rng(30_000 + seed)
+    W = int(rng.choice([1, 2, 3, 5, 8, 13, 16, 32, 64]))
+    k = int(rng.integers(1, 65))
+    Er = int(rng.integers(max(1, -(-k // W)), max(1, -(-k // W)) + 6))
+    M = int(rng.integers(1, 97)) if W <= 16 else int(rng.integers(1, 13))
+    dd = str(rng.choice(["bf16", "fp16", "fp8"]))
+    cd = "fp16" if dd == "fp16" else str(rng.choice(["bf16", "fp16"]))
+    H = 16 * int(rng.integers(1, 33))
+    S = int(rng.integers(1, 20)) if dd == "fp8" and rng.random() < 0.7 else 0
+    wl = workloads.custom(f"std_rand{seed}", W, M, H, k, W * Er, dd, cd, scale_dim=S,
+                          routing=str(rng.choice(["uniform", "zipf"])) if W * Er >= 2 * k
+                          else "uniform", ragged=bool(rng.random() < 0.6),
+                          seed_index=700 + seed)
+    launch = None
+    if rng.random() < 0.7:
+        row_vecs = H * (1 if dd == "fp8" else 2) // 16
+        launch = dict(expert_waves=int(rng.integers(1, 17)),
+                      expert_row_split=int(rng.integers(1, max(2, row_vecs + 1))),
+                      expert_combine_waves=int(rng.integers(1, 17)),
+                      expert_combine_row_split=int(rng.integers(1, max(2, H * 2 // 16 + 1))),
+                      expert_cache_policy=int(rng.integers(0, 3)))
+    return wl, launch, int(rng.choice([1, 2, 5, 1000])), bool(rng.random() < 0.5)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_configurations(seed):
+    wl, launch, cap_div, weighted = _random_standard_case(seed)
+    run_standard_case(wl, cap_div=cap_div, launch=launch, weighted=weighted,
+                      tag=f"std random {seed}")
