@@ -35,7 +35,7 @@ PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
 METRIC = "dispatch+combine µs/call and payload HBM GB/s (% of peak), EP8 H=7168 k=8"
 KERNEL_SOURCES = [os.path.join(ROOT, "combine_route_amd", "csrc", f)
                   for f in ("ep_kernels.hip", "ep_expert.hip", "ep_wire.hip", "ep_kernels.h",
-                            "ep_device.h", "ep_plan.cpp")]
+                            "ep_device.h", "ep_plan.cpp", "ep_standard.hip")]
 KERNELS = {"copy": "ep_copy_kernel", "combine": "ep_combine_kernel"}
 EXPERT_KERNELS = {"copy": "ex_copy_kernel", "combine": "ex_combine_kernel"}
 STANDARD_KERNELS = {"copy": "sx_copy_kernel", "combine": "sx_combine_kernel"}
@@ -54,8 +54,12 @@ COUNTER_KERNELS = {
     "sx_combine_kernel_fp8_block128": r"sx_combine_kernel<[^>]*, 1>",
     "sx_combine_kernel_mxfp4": r"sx_combine_kernel<[^>]*, 2>",
     "ep_copy_kernel_cast": r"ep_copy_kernel<[^>]*, true>",
-    "ep_quantize_kernel_fp8_block128": r"ep_quantize_kernel<1,",
-    "ep_quantize_kernel_mxfp4": r"ep_quantize_kernel<2,",
+    # the quantizer runs on the W*W*M receive rows and on the W*Er*cap packed
+    # rows, one instance for both: the smaller grid is the receive rows
+    "ep_quantize_kernel_fp8_block128": (r"ep_quantize_kernel<1,", "min"),
+    "ep_quantize_kernel_mxfp4": (r"ep_quantize_kernel<2,", "min"),
+    "ep_quantize_kernel_packed_fp8_block128": (r"ep_quantize_kernel<1,", "max"),
+    "ep_quantize_kernel_packed_mxfp4": (r"ep_quantize_kernel<2,", "max"),
     "ep_combine_wire_kernel_fp8_block128": r"ep_combine_wire_kernel<\d+, \d+, 1,",
     "ep_combine_wire_kernel_mxfp4": r"ep_combine_wire_kernel<\d+, \d+, 2,",
 }
@@ -590,9 +594,10 @@ def summarize_stats(csv_path, out_md, command):
 
 
 def _counter_means(path):
+    """Mean counter value per (kernel, grid size, counter)."""
     sums, counts = {}, {}
     for r in csv.DictReader(open(path)):
-        key = (r["Kernel_Name"], r["Counter_Name"])
+        key = (r["Kernel_Name"], int(r["Grid_Size"]), r["Counter_Name"])
         sums[key] = sums.get(key, 0.0) + float(r["Counter_Value"])
         counts[key] = counts.get(key, 0) + 1
     return {k: sums[k] / counts[k] for k in sums}
@@ -610,17 +615,25 @@ def summarize_counters(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, cal_m
     cal_f, cal_w = _counter_means(cal_fetch_csv), _counter_means(cal_write_csv)
     cal_bytes = cal_mib << 20
     # the calibration copy is the kernel that moved the most bytes in its run
-    f_cal = max(v for (k, c), v in cal_f.items() if c == "FETCH_SIZE") * 1024
-    w_cal = max(v for (k, c), v in cal_w.items() if c == "WRITE_SIZE") * 1024
+    f_cal = max(v for (k, g, c), v in cal_f.items() if c == "FETCH_SIZE") * 1024
+    w_cal = max(v for (k, g, c), v in cal_w.items() if c == "WRITE_SIZE") * 1024
     f_scale, w_scale = cal_bytes / f_cal, cal_bytes / w_cal
     wl = workloads.WORKLOADS[workload]
-    for kname, pattern in COUNTER_KERNELS.items():
-        fk = [v for (k, c), v in fetch.items() if re.search(pattern, k)]
-        wk = [v for (k, c), v in write.items() if re.search(pattern, k)]
+    def pick(means, pattern, grid):
+        hits = sorted((g, v) for (k, g, c), v in means.items() if re.search(pattern, k))
+        if grid == "min":
+            hits = hits[:1]
+        elif grid == "max":
+            hits = hits[-1:]
+        if len(hits) > 1:
+            raise SystemExit(f"several kernel instances or grids match {pattern!r}")
+        return [v for g, v in hits]
+
+    for kname, sel in COUNTER_KERNELS.items():
+        pattern, grid = sel if isinstance(sel, tuple) else (sel, None)
+        fk, wk = pick(fetch, pattern, grid), pick(write, pattern, grid)
         if not fk or not wk:
             continue
-        if len(fk) > 1 or len(wk) > 1:
-            raise SystemExit(f"{kname}: several kernel instances match {pattern!r}")
         rd = fk[0] * 1024 * f_scale
         wr = wk[0] * 1024 * w_scale
         lines = [f"# HBM traffic per launch of {kname}, workload {workload}",
