@@ -374,11 +374,10 @@ __global__ __launch_bounds__(1024) void sx_copy_kernel(StandardArgs a)
     }
 }
 
-// Fold-position flags of a kept pair: the first or last kept pair of its
-// rank, and whether ranks without a kept pair come just before its rank.
-constexpr int kFoldFirst = 1;
-constexpr int kFoldLast = 2;
-constexpr int kFoldGap = 4;
+// Fold-position flags of a kept pair: the last kept pair of its rank, and
+// whether ranks without a kept pair come just before its rank.
+constexpr int kFoldLast = 1;
+constexpr int kFoldGap = 2;
 
 // WIRE: 0 for bf16 / fp16 expert outputs, else the wire of the packed rows
 // (kWireFp8Block128, kWireMxfp4), each element decoded exactly before the fold.
@@ -454,7 +453,7 @@ __global__ __launch_bounds__(1024) void sx_combine_kernel(StandardCombineArgs a,
     if (lane < nk) {
         const int pv = lane == 0 ? -1 : dprev;
         const bool last = lane == nk - 1 || dnext != dx;
-        flags = (pv != dx ? kFoldFirst : 0) | (last ? kFoldLast : 0) | (dx - pv > 1 ? kFoldGap : 0);
+        flags = (last ? kFoldLast : 0) | (dx - pv > 1 ? kFoldGap : 0);
     }
     const int dlast = nk > 0 ? __builtin_amdgcn_readlane(dx, nk - 1) : -1;
     const bool trailing = nD - 1 > dlast;  // ranks without a kept pair after the last
@@ -496,7 +495,16 @@ __global__ __launch_bounds__(1024) void sx_combine_kernel(StandardCombineArgs a,
             load_scales(0);
     }
     for (int v0 = vbeg; v0 < vend; v0 += kWave * U) {
+        // Both sums start at -0, the identity of IEEE addition: -0 + x = x
+        // and fma(c, f, -0) = c * f exactly, for every x, signed zeros
+        // included, so the first pair of a rank and the first rank need no
+        // case of their own; a rank's sum goes back to -0 after its rounding.
         float tot[U][8], part[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                tot[u][e] = part[u][e] = -0.0f;
         bool have = false;  // uniform: tot holds a rank's contribution
         for (int i0 = 0; i0 < nk; i0 += G) {
             if constexpr (WIRE != 0) {
@@ -537,7 +545,6 @@ __global__ __launch_bounds__(1024) void sx_combine_kernel(StandardCombineArgs a,
                                                    __builtin_bit_cast(int, gw), i0 + q))
                                   : 1.0f;
                     const bool gap = fl & kFoldGap;
-                    const bool first = fl & kFoldFirst;
                     const bool last = fl & kFoldLast;
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
@@ -552,22 +559,27 @@ __global__ __launch_bounds__(1024) void sx_combine_kernel(StandardCombineArgs a,
                                 WIRE == kWireFp8Block128 ? d : d >> (8 * ((v >> 2) & 3));
                             decode_group<WIRE>(codes[u][q], sb, f);
                         }
+                        if (gap) {  // ranks whose intermediate rows are +0
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                tot[u][e] = tot[u][e] + 0.0f;
+                        }
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
-                            if (gap)  // ranks whose intermediate rows are +0
-                                tot[u][e] = have ? tot[u][e] + 0.0f : 0.0f;
                             if (kWeighted)
-                                part[u][e] = first ? cq * f[e] : __builtin_fmaf(cq, f[e], part[u][e]);
+                                part[u][e] = __builtin_fmaf(cq, f[e], part[u][e]);
                             else
-                                part[u][e] = first ? f[e] : part[u][e] + f[e];
+                                part[u][e] = part[u][e] + f[e];
                         }
                         if (last) {
                             // the rank's intermediate row: rounded to the combine type
                             float p[8];
                             widen<DT>(narrow<DT>(part[u]), p);
 #pragma unroll
-                            for (int e = 0; e < 8; ++e)
-                                tot[u][e] = (have || gap) ? tot[u][e] + p[e] : p[e];
+                            for (int e = 0; e < 8; ++e) {
+                                tot[u][e] = tot[u][e] + p[e];
+                                part[u][e] = -0.0f;
+                            }
                         }
                     }
                     have = have || gap || last;
@@ -578,11 +590,9 @@ __global__ __launch_bounds__(1024) void sx_combine_kernel(StandardCombineArgs a,
         for (int u = 0; u < U; ++u) {
             const int v = v0 + u * kWave + lane;
             if (v < vend) {
+                if (!have || trailing) {  // no rank with a kept pair, or +0 ranks after the last
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    if (!have)
-                        tot[u][e] = 0.0f;  // no rank, or none with a kept pair
-                    else if (trailing)
+                    for (int e = 0; e < 8; ++e)
                         tot[u][e] = tot[u][e] + 0.0f;
                 }
                 bstore16<Policy<kStream>::combine_store>(narrow<DT>(tot[u]), rdst,
