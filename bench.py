@@ -852,14 +852,21 @@ def run(args):
                      "algorithmic_bytes_per_launch": kernel_bytes[dom]},
         "cpu_baseline": cpu_baseline,
     }
+    def progress(what):
+        print(f"[bench] {what} done at {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    progress(f"headline timing ({line['us_per_call']} us a call)")
     if not args.no_expert:
         line["expert_major"] = measure_expert_major(args, cra, torch, np, wl, op, inp, stream)
+        progress("expert-major layout")
         line["standard_moe"] = measure_standard_moe(args, cra, torch, np, wl, op, inp, stream,
                                                     x, idx, w, sc)
+        progress("fused expert-major path")
     if not args.no_wires:
         op.close()
         torch.cuda.empty_cache()
         line["quantized_wires"] = measure_quantized_wires(args, cra, torch, np, wl, inp, stream)
+        progress("quantized wires")
     op.close()
     # the box's own device copy rate (1 GiB, torch), measured last so its
     # buffers take no part in the placement of the timed ones
