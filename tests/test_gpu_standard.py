@@ -147,14 +147,20 @@ def test_capacity_drops(wl, cap_div, weighted):
                       tag=f"std {wl.name} /{cap_div} w={weighted}")
 
 
+def _zero_workload():
+    return workloads.custom("std_zero_ep4_t64_h128_k6", 4, 64, 128, 6, 24, "bf16", ragged=True,
+                            seed_index=550)
+
+
 @pytest.mark.parametrize("cap_div", [1, 3, 1000])
-def test_signed_zero_with_dropped_ranks(cap_div):
+@pytest.mark.parametrize("weighted", [False, True])
+def test_signed_zero_with_dropped_ranks(cap_div, weighted):
     """Every expert output -0.0: a token's sum is -0.0 unless one of its ranks
     lost all its pairs, whose +0 rows turn it to +0; the fused combine must
-    place those +0 terms exactly where the two-step path has them."""
-    wl = workloads.custom("std_zero_ep4_t64_h128_k6", 4, 64, 128, 6, 24, "bf16", ragged=True,
-                          seed_index=550)
-    run_standard_case(wl, cap_div=cap_div, py="neg_zero", tag=f"std -0 /{cap_div}")
+    place those +0 terms exactly where the two-step path has them (weighted,
+    each term is weight * -0.0 = -0.0)."""
+    run_standard_case(_zero_workload(), cap_div=cap_div, py="neg_zero", weighted=weighted,
+                      tag=f"std -0 /{cap_div} w={weighted}")
 
 
 @pytest.mark.parametrize("W,E,k", [(2, 300, 8), (1, 130, 9), (4, 520, 17), (2, 40, 33),
@@ -329,7 +335,8 @@ WIRES = {"fp8_block128": (cra.EP_WIRE_FP8_BLOCK128, oracle.WIRE_FP8_BLOCK128),
          "mxfp4": (cra.EP_WIRE_MXFP4, oracle.WIRE_MXFP4)}
 
 
-def run_standard_wire_case(wl, name, cap_div=1, weighted=False, tag=None, cols=None):
+def run_standard_wire_case(wl, name, cap_div=1, weighted=False, tag=None, cols=None,
+                           neg_zero=False):
     """The fused combine from quantized expert outputs: the packed outputs are
     quantized on the GPU with the per-expert counts (checked against the
     oracle's quantizer on every kept row), then the oracle's own codes go to
@@ -352,8 +359,11 @@ def run_standard_wire_case(wl, name, cap_div=1, weighted=False, tag=None, cols=N
     # oracle quantizes few rows
     g = torch.Generator().manual_seed(sum(tag.encode()) % 10007)
     base = min(512, W * Er * cap)
-    vb = (torch.randn((base, H), generator=g)
-          * torch.exp(torch.randn((base, 1), generator=g))).to(cdt)
+    if neg_zero:  # every expert output -0.0 (all-zero blocks, sign kept in the codes)
+        vb = torch.full((base, H), -0.0, dtype=cdt)
+    else:
+        vb = (torch.randn((base, H), generator=g)
+              * torch.exp(torch.randn((base, 1), generator=g))).to(cdt)
     cb, sb = oracle.quantize_rows(vb.view(torch.int16).numpy().view(np.uint16), dt, ow)
     sel = np.arange(W * Er * cap) % base
     v = vb[torch.from_numpy(sel)]
@@ -410,6 +420,17 @@ def test_wire_headline_first_block(name):
     minutes), the GPU computes whole rows."""
     run_standard_wire_case(workloads.WORKLOADS[workloads.HEADLINE], name, weighted=True,
                            cols=128)
+
+
+@pytest.mark.parametrize("name", list(WIRES))
+@pytest.mark.parametrize("cap_div", [1, 1000])
+@pytest.mark.parametrize("weighted", [False, True])
+def test_wire_signed_zero_with_dropped_ranks(name, cap_div, weighted):
+    """The signed-zero case from quantized rows: -0.0 survives the quantizer
+    and the decode, and +0 rows of ranks that lost every pair land where the
+    two steps put them."""
+    run_standard_wire_case(_zero_workload(), name, cap_div=cap_div, weighted=weighted,
+                           neg_zero=True, tag=f"std wire {name} -0 /{cap_div} w={weighted}")
 
 
 @pytest.mark.parametrize("name", list(WIRES))
