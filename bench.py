@@ -619,6 +619,10 @@ def summarize_counters(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, cal_m
     w_cal = max(v for (k, g, c), v in cal_w.items() if c == "WRITE_SIZE") * 1024
     f_scale, w_scale = cal_bytes / f_cal, cal_bytes / w_cal
     wl = workloads.WORKLOADS[workload]
+
+    def run_dir(csv_path):  # the -d directory of the rocprofv3 run that wrote csv_path
+        return os.path.dirname(csv_path) or "."
+
     def pick(means, pattern, grid):
         hits = sorted((g, v) for (k, g, c), v in means.items() if re.search(pattern, k))
         if grid == "min":
@@ -640,13 +644,16 @@ def summarize_counters(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, cal_m
                  "# rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE, one run each;",
                  f"# each scaled by the same counter on a plain {cal_mib} MiB device copy",
                  "# Commands (from the repository root):",
-                 "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- "
+                 f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d {run_dir(fetch_csv)} -o run -- "
                  "python -u bench.py --no-cpu-baseline --steps 3 --warmup 1",
-                 "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- "
+                 f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d {run_dir(write_csv)} -o run -- "
                  "python -u bench.py --no-cpu-baseline --steps 3 --warmup 1",
-                 f"#   rocprofv3 --pmc FETCH_SIZE ... -- python -u bench.py --copy-calibration {cal_mib} --steps 3 --warmup 1",
-                 f"#   rocprofv3 --pmc WRITE_SIZE ... -- python -u bench.py --copy-calibration {cal_mib} --steps 3 --warmup 1",
-                 f"#   python bench.py --summarize-counters <the four counter_collection.csv> {cal_mib} {workload}",
+                 f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d {run_dir(cal_fetch_csv)} -o run -- "
+                 f"python -u bench.py --copy-calibration {cal_mib} --steps 3 --warmup 1",
+                 f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d {run_dir(cal_write_csv)} -o run -- "
+                 f"python -u bench.py --copy-calibration {cal_mib} --steps 3 --warmup 1",
+                 f"#   python bench.py --summarize-counters {fetch_csv} {write_csv} {cal_fetch_csv} "
+                 f"{cal_write_csv} {cal_mib} {workload}",
                  f"kernel_source_sha256_16: {kernel_source_hash()}",
                  f"fetch_size_kib_raw: {fk[0]:.1f}",
                  f"write_size_kib_raw: {wk[0]:.1f}",
@@ -907,8 +914,8 @@ def main():
         summarize_counters(a[0], a[1], a[2], a[3], int(a[4]), a[5])
         return
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs all virtual "
-              "expert-parallel ranks on one GPU; only --gpus 1 is measured.", file=sys.stderr)
+        print(f"bench.py: --gpus {args.gpus} is not supported: all virtual expert-parallel "
+              "ranks run on one GPU, and only --gpus 1 is measured.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         import torch
