@@ -154,6 +154,7 @@ struct StandardArgs {
     int32_t scale_dwords;
     int32_t W, M, k, Er, E, cap;
     int32_t Tr;                  // tiles a source rank: max(1, ceil(M / 64))
+    int32_t token_split;         // copy blocks sharing a tile, each with its share of tokens
     int32_t ntok[kMaxRanks];     // T_r
 };
 

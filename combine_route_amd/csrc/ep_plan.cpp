@@ -319,6 +319,42 @@ int tiles_for(const int32_t* ntok, int W, int tt)
     return n;
 }
 
+// The fused dispatch's copy grid: 64-token tiles of the source ranks, each
+// row cut into pieces and each tile's tokens shared by blocks until the grid
+// has about a target number of blocks: 1024 up to top-16, 512 above (every
+// block routes its whole tile, which costs more the more ids a token has).
+// Calls whose row pieces alone reach the target share no tile; smaller ones
+// share tiles first (at most one token a wave), then cut rows. A value
+// given in the launch overrides (row_split, token_split > 0) is kept.
+struct FusedGrid {
+    int row_split, token_split;
+};
+
+FusedGrid fused_grid(const Shape& s, const int32_t* ntok, int waves, int row_split,
+                     int token_split)
+{
+    int tiles = 0;
+    for (int r = 0; r < s.W; ++r)
+        tiles += (ntok[r] + ep::kWave - 1) / ep::kWave;
+    tiles = std::max(1, tiles);
+    const int target = s.k <= 16 ? 1024 : 512;
+    const int max_split = std::max(1, s.row_vecs / ep::kWave);
+    const int max_share = std::max(1, ep::kWave / std::max(1, waves));
+    auto ceil_div = [](int64_t a, int64_t b) { return (int)((a + b - 1) / b); };
+    FusedGrid g{row_split, token_split};
+    if (g.row_split <= 0 && g.token_split <= 0 && (int64_t)tiles * max_split >= target) {
+        g.row_split = std::min(max_split, ceil_div(target, tiles));
+        g.token_split = 1;
+    }
+    if (g.token_split <= 0)
+        g.token_split = std::min(max_share, std::max(1, ceil_div(target, (int64_t)tiles *
+                                                                     std::max(1, g.row_split))));
+    if (g.row_split <= 0)
+        g.row_split = std::min(max_split,
+                               std::max(1, ceil_div(target, (int64_t)tiles * g.token_split)));
+    return g;
+}
+
 // Automatic geometry. Small calls get smaller routing tiles and rows split
 // into pieces so that the grid still covers the 256 compute units several
 // times over, as the gfx1201 kernels do below 256 tokens ("feat(ep): add
@@ -387,6 +423,7 @@ ep_launch_t auto_launch(const ep_plan* p, const int32_t* ntok)
     // cached vs 317 us streaming).
     const int64_t ex_bytes = N * (s.row_bytes + s.crow_bytes) * (s.P + s.k);
     l.expert_cache_policy = ex_bytes <= 2 * kKeepBytes ? EP_CACHE_KEEP : EP_CACHE_STREAM;
+    l.expert_token_split = fused_grid(s, ntok, l.expert_waves, 0, 0).token_split;
     return l;
 }
 
@@ -417,6 +454,8 @@ ep_launch_t effective_launch(const ep_plan* p, const int32_t* ntok)
         l.expert_combine_row_split = p->launch.expert_combine_row_split;
     if (p->launch.expert_cache_policy > 0)
         l.expert_cache_policy = p->launch.expert_cache_policy;
+    if (p->launch.expert_token_split > 0)
+        l.expert_token_split = p->launch.expert_token_split;
     return l;
 }
 
@@ -509,6 +548,9 @@ int check_launch(const ep_plan* p, const ep_launch_t* l)
     if (l->expert_combine_row_split > s.crow_bytes / 16)
         return fail(EP_ERR_ARG, "launch.expert_combine_row_split = %d: must be <= %lld",
                     l->expert_combine_row_split, (long long)(s.crow_bytes / 16));
+    if (l->expert_token_split > ep::kWave)
+        return fail(EP_ERR_ARG, "launch.expert_token_split = %d: must be <= %d",
+                    l->expert_token_split, ep::kWave);
     return EP_OK;
 }
 
@@ -1201,17 +1243,13 @@ int ep_dispatch_standard_moe(ep_expert_plan_t* x, const ep_dispatch_standard_arg
     sa.Tr = (int32_t)x->e.Tr;
     for (int r = 0; r < ep::kMaxRanks; ++r)
         sa.ntok[r] = r < s.W ? a->num_tokens[r] : 0;
-    // row pieces until the copy grid has about 1024 blocks, unless overridden
-    int split = l.expert_row_split;
-    if (p->launch.expert_row_split <= 0) {
-        int tiles = 0;
-        for (int r = 0; r < s.W; ++r)
-            tiles += (a->num_tokens[r] + ep::kWave - 1) / ep::kWave;
-        const int max_split = std::max(1, sa.row_vecs / ep::kWave);
-        split = std::min(max_split, std::max(1, (1024 + tiles - 1) / std::max(1, tiles)));
-    }
-    sa.piece_vecs = (sa.row_vecs + split - 1) / split;
+    // row pieces and blocks sharing a tile (fused_grid), unless overridden
+    const FusedGrid fg = fused_grid(s, a->num_tokens, l.expert_waves,
+                                    std::max(0, p->launch.expert_row_split),
+                                    std::max(0, p->launch.expert_token_split));
+    sa.piece_vecs = (sa.row_vecs + fg.row_split - 1) / fg.row_split;
     const int row_split = (sa.row_vecs + sa.piece_vecs - 1) / sa.piece_vecs;
+    sa.token_split = fg.token_split;
 
     hipError_t e = timed(p, EP_KERNEL_STANDARD_COUNT, stream,
                          [&] { return ep::launch_standard_count(sa, stream); });

@@ -15,11 +15,14 @@
 //            expert.
 //   scan     a wave per expert: tile bases, the expert's row count, and its
 //            layout range for every source rank.
-//   copy     a block per (source rank, tile, row piece): wave 0 works out the
-//            kept packed row of every (token, expert) pair into LDS and the
-//            per-slot map the combine reads; then every wave loads a token's
-//            row piece once (16 B a lane) and stores it to each kept packed
-//            row; piece-0 blocks also write the scale rows and source info.
+//   copy     a block per (source rank, tile, row piece, share of the tile's
+//            tokens): wave 0 works out the kept packed row of every (token,
+//            expert) pair of the tile into LDS; then every wave loads a token
+//            of the block's share once per row piece (16 B a lane) and stores
+//            it to each kept packed row; piece-0 blocks also write the per-slot
+//            map the combine reads, the scale rows and the source info of
+//            their share. Small calls share a tile between blocks so the grid
+//            still covers the compute units.
 //   combine  a wave per (token, row piece): the result of
 //            convert_combine_input followed by the combine, without the
 //            intermediate rows. For each of the token's ranks in its rank
@@ -40,8 +43,10 @@ namespace {
 using namespace dev;
 
 constexpr int kSxWaves = 4;  // count and scan: waves a block, one tile or list each
-// Mask words of a token's expert set the copy keeps in registers (E <= 256).
+// Mask words of a token's expert set the copy keeps in registers (E <= 256),
+// and the experts whose tile masks it holds in LDS at a time.
 constexpr int kSeenWords = 4;
+constexpr int kWinExperts = kSeenWords * kWave;
 
 // Tokens of source rank r in this call.
 __device__ __forceinline__ int tokens_of(const StandardArgs& a, int r)
@@ -136,31 +141,38 @@ __global__ __launch_bounds__(1024) void sx_copy_kernel(StandardArgs a)
     __shared__ int32_t s_p[kWave][KB];  // their positions, then the kept packed rows
     __shared__ int8_t s_u[kWave][KB];   // each slot's index into s_e; -1: invalid or a repeat
     __shared__ int32_t s_n[kWave];      // kept packed rows of the token
-    __shared__ uint64_t s_bal[kSeenWords * kWave];  // expert e: its ballot over the tile
-    __shared__ int32_t s_base[kSeenWords * kWave];  // and its tile base
+    __shared__ uint64_t s_bal[kWinExperts];  // expert e0 + j: the tile's lanes naming it
+    __shared__ int32_t s_base[kWinExperts];  // and its tile base
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
     const int nwaves = blockDim.x / kWave;
-    const int tile = blockIdx.x;
+    const int tile = blockIdx.x / a.token_split;
+    const int sub = blockIdx.x - tile * a.token_split;
     const int piece = blockIdx.y;
     const int r = blockIdx.z;
     const int q0 = tile * kWave;
     const int cnt = min(kWave, tokens_of(a, r) - q0);
-    if (cnt <= 0)
-        return;  // the whole block
+    // Blocks sharing the tile copy tokens [t_lo, t_hi) of it each; every one
+    // works out the whole tile's positions (the in-tile prefix needs them all).
+    const int span = (kWave + a.token_split - 1) / a.token_split;
+    const int t_lo = sub * span;
+    const int t_hi = min(cnt, t_lo + span);
+    if (t_lo >= t_hi)
+        return;  // the whole block: no token of its own
     const int64_t row0 = (int64_t)r * a.M + q0;
     const int64_t TT = (int64_t)a.W * a.Tr;
 
-    // This wave's items: tokens wave, wave + nwaves, ... of the tile, each cut
-    // into nch chunks of its row piece [vbeg, vend).
+    // This wave's items: tokens t_lo + wave, t_lo + wave + nwaves, ... below
+    // t_hi, each cut into nch chunks of its row piece [vbeg, vend).
     const uint32_t row_bytes = (uint32_t)a.row_vecs * 16u;
     const int vbeg = piece * a.piece_vecs;
     const int vend = min(a.row_vecs, vbeg + a.piece_vecs);
     const int nch = (vend - vbeg + kWave * VPL - 1) / (kWave * VPL);
-    const int items = (wave < cnt ? (cnt - wave + nwaves - 1) / nwaves : 0) * nch;
+    const int nt = t_hi - t_lo;
+    const int items = (wave < nt ? (nt - wave + nwaves - 1) / nwaves : 0) * nch;
     auto load_item = [&](int it, u32x4 (&v)[VPL]) {
-        const int t = wave + (it / nch) * nwaves;
+        const int t = t_lo + wave + (it / nch) * nwaves;
         const int v0 = vbeg + (it % nch) * kWave * VPL;
         const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.x + (row0 + t) * row_bytes, row_bytes);
 #pragma unroll
@@ -171,7 +183,7 @@ __global__ __launch_bounds__(1024) void sx_copy_kernel(StandardArgs a)
         }
     };
     auto store_item = [&](int it, const u32x4 (&v)[VPL]) {
-        const int t = wave + (it / nch) * nwaves;
+        const int t = t_lo + wave + (it / nch) * nwaves;
         const int v0 = vbeg + (it % nch) * kWave * VPL;
         const int n = uniform(s_n[t]);
         u32x2 c[kCast ? VPL : 1];
@@ -213,12 +225,12 @@ __global__ __launch_bounds__(1024) void sx_copy_kernel(StandardArgs a)
         // registers and repeats are found there; else in LDS.
         const int nw = (a.E + kWave - 1) / kWave;
         const bool regs = nw <= kSeenWords;  // uniform
-        // the tile bases of experts 64w + lane, loaded before the ids are
-        // read so their latency overlaps the routing
+        // the tile bases of experts 64w + lane (the first window), loaded
+        // before the ids are read so their latency overlaps the routing
         int bw[kSeenWords];
 #pragma unroll
         for (int w = 0; w < kSeenWords; ++w)
-            bw[w] = regs && w < nw && 64 * w + lane < a.E
+            bw[w] = 64 * w + lane < a.E
                         ? a.tile_base[(int64_t)(64 * w + lane) * TT + (int64_t)r * a.Tr + tile]
                         : 0;
         int n = 0;
@@ -256,67 +268,41 @@ __global__ __launch_bounds__(1024) void sx_copy_kernel(StandardArgs a)
                 s_u[lane][slot] = (int8_t)u;
             }
         }
-        if (regs) {
-            // Every expert's ballot over the tile and its tile base go to LDS
-            // (lane jj of pass w writes expert 64w + jj); each lane then looks
-            // up its own experts there.
+        // Positions inside the tile: for a window of kWinExperts experts at a
+        // time, each lane ORs its bit into the 64-bit LDS mask of each of its
+        // experts (order-independent, so deterministic); a pair's position is
+        // its expert's tile base plus the mask's bits below the lane. The
+        // first window's tile bases were loaded before the ids.
+        const int nwin = (a.E + kWinExperts - 1) / kWinExperts;
+        for (int w0 = 0; w0 < nwin; ++w0) {
+            const int e0 = w0 * kWinExperts;
 #pragma unroll
             for (int w = 0; w < kSeenWords; ++w) {
-                if (w < nw) {
-                    const int nj = min(kWave, a.E - 64 * w);
-                    uint64_t mine = 0;
-                    for (int jj = 0; jj < nj; ++jj) {
-                        const uint64_t b = __ballot((seen[w] >> jj) & 1);
-                        if (lane == jj)
-                            mine = b;
-                    }
-                    if (lane < nj) {
-                        s_bal[64 * w + lane] = mine;
-                        s_base[64 * w + lane] = bw[w];
-                    }
-                }
+                const int e = e0 + 64 * w + lane;
+                int b = bw[w];
+                if (w0 > 0)
+                    b = e < a.E ? a.tile_base[(int64_t)e * TT + (int64_t)r * a.Tr + tile] : 0;
+                s_bal[64 * w + lane] = 0;
+                s_base[64 * w + lane] = b;
             }
             __builtin_amdgcn_wave_barrier();
             for (int u = 0; u < n; ++u) {
-                const int e = s_e[lane][u];
-                s_p[lane][u] = s_base[e] + lanes_below(s_bal[e]);
+                const int j = s_e[lane][u] - e0;
+                if (j >= 0 && j < kWinExperts)
+                    __hip_atomic_fetch_or(&s_bal[j], 1ull << lane, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_WORKGROUP);
             }
-        } else {
-            int n_max = n;  // the wave's longest list
-#pragma unroll
-            for (int off = kWave / 2; off > 0; off >>= 1)
-                n_max = max(n_max, __shfl_xor(n_max, off));
-            // One mask word (64 experts) at a time: lane jj holds the ballot
-            // of expert 64w + jj over the tile and its tile base; each lane
-            // fetches both for its own entries with cross-lane reads.
-            for (int w = 0; w < nw; ++w) {
-                const uint64_t m = local_word<KC>(ids, a.k, valid, 0, a.E, w);
-                const int nj = min(kWave, a.E - 64 * w);
-                const int bw = lane < nj ? a.tile_base[(int64_t)(64 * w + lane) * TT +
-                                                       (int64_t)r * a.Tr + tile]
-                                         : 0;
-                uint64_t mine = 0;
-                for (int jj = 0; jj < nj; ++jj) {
-                    const uint64_t b = __ballot((m >> jj) & 1);
-                    if (lane == jj)
-                        mine = b;
-                }
-                const int mlo = (int)(uint32_t)mine;
-                const int mhi = (int)(uint32_t)(mine >> 32);
-                for (int u = 0; u < n_max; ++u) {
-                    const int j = u < n ? s_e[lane][u] - 64 * w : -1;
-                    const int src = j & (kWave - 1);
-                    const uint32_t blo = (uint32_t)__shfl(mlo, src);
-                    const uint32_t bhi = (uint32_t)__shfl(mhi, src);
-                    const int base = __shfl(bw, src);
-                    if (j >= 0 && j < kWave)
-                        s_p[lane][u] = base + lanes_below(((uint64_t)bhi << 32) | blo);
-                }
+            __builtin_amdgcn_wave_barrier();
+            for (int u = 0; u < n; ++u) {
+                const int j = s_e[lane][u] - e0;
+                if (j >= 0 && j < kWinExperts)
+                    s_p[lane][u] = s_base[j] + lanes_below(s_bal[j]);
             }
+            __builtin_amdgcn_wave_barrier();
         }
         // the combine's map: the packed row of each slot that is its expert's
-        // first occurrence and was kept, else -1
-        if (valid) {
+        // first occurrence and was kept, else -1 (each block its own tokens)
+        if (piece == 0 && valid && lane >= t_lo && lane < t_hi) {
             for (int slot = 0; slot < a.k; ++slot) {
                 const int u = s_u[lane][slot];
                 const int p = u >= 0 ? s_p[lane][u] : a.cap;
@@ -335,7 +321,7 @@ __global__ __launch_bounds__(1024) void sx_copy_kernel(StandardArgs a)
 
     const int sd = a.scale_dwords;
     if (piece == 0) {
-        for (int t = wave; t < cnt; t += nwaves) {
+        for (int t = t_lo + wave; t < t_hi; t += nwaves) {
             const int n = uniform(s_n[t]);
             if (lane < n)
                 a.src_info[s_p[t][lane]] = q0 + t;
@@ -366,7 +352,7 @@ __global__ __launch_bounds__(1024) void sx_copy_kernel(StandardArgs a)
     } else {
         // large pieces (throughput): one chunk a wave in flight
         for (int it = 0; it < items; ++it) {
-            if (uniform(s_n[wave + (it / nch) * nwaves]) == 0)
+            if (uniform(s_n[t_lo + wave + (it / nch) * nwaves]) == 0)
                 continue;  // a token without a kept expert is not read
             load_item(it, A);
             store_item(it, A);
@@ -701,7 +687,7 @@ hipError_t launch_standard_scan(const StandardArgs& a, hipStream_t s)
 hipError_t launch_standard_copy(const StandardArgs& a, int waves, int row_split, bool stream,
                                 hipStream_t s)
 {
-    const dim3 grid(a.Tr, row_split, a.W);
+    const dim3 grid(a.Tr * a.token_split, row_split, a.W);
     const dim3 block(waves * kWave);
     const int per_lane = (a.piece_vecs + kWave - 1) / kWave;
     if (per_lane <= 1)

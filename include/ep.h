@@ -323,12 +323,18 @@ typedef struct ep_launch {
      *                             min(W, k) received rows and k expert rows,
      *                             out and back) stay within 512 MB (rows read
      *                             were just written, so they partly hit the
-     *                             256 MB cache), stream above. */
+     *                             256 MB cache), stream above.
+     *   expert_token_split        blocks sharing a 64-token tile of
+     *                             ep_dispatch_standard_moe's copy, each
+     *                             copying its share of the tile's tokens:
+     *                             1..64; automatic: until the grid has about
+     *                             1024 blocks, at most 64 / expert_waves. */
     int32_t expert_waves;
     int32_t expert_row_split;
     int32_t expert_combine_waves;
     int32_t expert_combine_row_split;
     int32_t expert_cache_policy;
+    int32_t expert_token_split;
 } ep_launch_t;
 
 /* Override (launch != NULL) or reset to automatic (launch == NULL) the plan's

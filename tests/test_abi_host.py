@@ -258,6 +258,19 @@ def test_launch_override_limits_and_auto_geometry(lib):
         cra.EP_LAYOUT_KERNELS
     with pytest.raises(cra.EpError):
         cra.ep_plan_get_launch(plan, [4097] + [0] * 7)
+    # the fused dispatch's copy: 512 tiles x 14 row pieces reach 1024 blocks
+    # without sharing a tile; 16 tiles x 14 pieces do not, so small calls
+    # share each tile first, at most one token a wave
+    assert auto["expert_token_split"] == 1
+    for few in ([128] * 8, [16] * 8, [1] + [0] * 7):
+        dec = cra.ep_plan_get_launch(plan, few)
+        assert dec["expert_token_split"] == 64 // dec["expert_waves"]
+    for bad in (dict(expert_token_split=65),):
+        with pytest.raises(cra.EpError):
+            cra.ep_plan_set_launch(plan, bad)
+    cra.ep_plan_set_launch(plan, dict(expert_token_split=64))
+    assert cra.ep_plan_get_launch(plan, [4096] * 8)["expert_token_split"] == 64
+    cra.ep_plan_set_launch(plan, None)
     lib.ep_plan_destroy(plan)
     # k > 16: the copy blocks cannot route the whole call; few tiles: they scan
     wl = workloads.WORKLOADS["ep4_ragged1024_h2048_fp16_k64"]
