@@ -12,11 +12,13 @@
 //            there, for the layout ranges.
 //   scan     a wave per list: exclusive scan of its tile counts -> tile bases,
 //            the expert's row count and its layout ranges.
-//   copy     a block per (tile, row piece): wave 0 works out the kept packed
-//            row of every (row, local expert) pair into LDS; then every wave
-//            loads a row piece once (16 B a lane) and stores it to each of the
-//            row's packed rows; piece-0 blocks also write the scale rows, the
-//            source info and the map the inverse gathers through.
+//   copy     a block per (tile, row piece, share of the tile's rows): wave 0
+//            works out the kept packed row of every (row, local expert) pair
+//            of the tile into LDS; then every wave loads a row of the block's
+//            share once per row piece (16 B a lane) and stores it to each of
+//            the row's packed rows; piece-0 blocks also write the scale rows,
+//            the source info and the map the inverse gathers through, for
+//            their share. Small calls share a tile between blocks.
 //   combine  a wave per (received row, row piece): the row's kept expert
 //            outputs, folded in FP32 in first-occurrence order and rounded to
 //            nearest even once (the combine's fold).
@@ -32,6 +34,8 @@ namespace {
 using namespace dev;
 
 constexpr int kExWaves = 4;  // count and scan: waves a block, one tile or list each
+// Local experts whose tile masks the copy holds in LDS at a time.
+constexpr int kExWindow = 256;
 
 // Received rows of rank d that the call covers. The dispatch never fills more
 // than `rows` (every token goes at most once to a rank); the clamp keeps a
@@ -163,30 +167,39 @@ __global__ __launch_bounds__(1024) void ex_copy_kernel(ExpertArgs a)
     __shared__ int32_t s_p[kWave][KB];  // their positions, then the kept packed rows
     __shared__ float s_c[kWave][KB];    // their weights for the row (when a.w is set)
     __shared__ int32_t s_n[kWave];      // kept packed rows of the row
+    __shared__ uint64_t s_bal[kExWindow];  // local expert j0 + j: the tile's lanes naming it
+    __shared__ int32_t s_base[kExWindow];  // and its tile base
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
     const int nwaves = blockDim.x / kWave;
-    const int tile = blockIdx.x;
+    const int tile = blockIdx.x / a.token_split;
+    const int sub = blockIdx.x - tile * a.token_split;
     const int piece = blockIdx.y;
     const int d = blockIdx.z;
     const int R = received(a.recv[d], a.rows);
     const int q0 = tile * kWave;
     const int cnt = min(kWave, R - q0);
-    if (cnt <= 0)
-        return;  // the whole block
+    // Blocks sharing the tile copy rows [r_lo, r_hi) of it each; every one
+    // works out the whole tile's positions (the in-tile prefix needs them all).
+    const int span = (kWave + a.token_split - 1) / a.token_split;
+    const int r_lo = sub * span;
+    const int r_hi = min(cnt, r_lo + span);
+    if (r_lo >= r_hi)
+        return;  // the whole block: no row of its own
     const int64_t row0 = (int64_t)d * a.WM + q0;
     const int64_t lo = (int64_t)d * a.Er;
 
-    // This wave's items: rows wave, wave + nwaves, ... of the tile, each cut
-    // into nch chunks of its row piece [vbeg, vend).
+    // This wave's items: rows r_lo + wave, r_lo + wave + nwaves, ... below
+    // r_hi, each cut into nch chunks of its row piece [vbeg, vend).
     const uint32_t row_bytes = (uint32_t)a.row_vecs * 16u;
     const int vbeg = piece * a.piece_vecs;
     const int vend = min(a.row_vecs, vbeg + a.piece_vecs);
     const int nch = (vend - vbeg + kWave * VPL - 1) / (kWave * VPL);
-    const int items = (wave < cnt ? (cnt - wave + nwaves - 1) / nwaves : 0) * nch;
+    const int nr = r_hi - r_lo;
+    const int items = (wave < nr ? (nr - wave + nwaves - 1) / nwaves : 0) * nch;
     auto load_item = [&](int it, u32x4 (&v)[VPL]) {
-        const int r = wave + (it / nch) * nwaves;
+        const int r = r_lo + wave + (it / nch) * nwaves;
         const int v0 = vbeg + (it % nch) * kWave * VPL;
         const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.x + (row0 + r) * row_bytes, row_bytes);
 #pragma unroll
@@ -197,7 +210,7 @@ __global__ __launch_bounds__(1024) void ex_copy_kernel(ExpertArgs a)
         }
     };
     auto store_item = [&](int it, const u32x4 (&v)[VPL]) {
-        const int r = wave + (it / nch) * nwaves;
+        const int r = r_lo + wave + (it / nch) * nwaves;
         const int v0 = vbeg + (it % nch) * kWave * VPL;
         const int n = uniform(s_n[r]);
         for (int i = 0; i < n; ++i) {
@@ -223,6 +236,12 @@ __global__ __launch_bounds__(1024) void ex_copy_kernel(ExpertArgs a)
         const int64_t rowq = row0 + (valid ? lane : 0);
         const int32_t* ids = a.idx + rowq * a.k;
         const bool weighted = a.w != nullptr;
+        // the first window's tile bases, loaded before the ids are read so
+        // their latency overlaps the routing
+        int bw[kExWindow / kWave];
+#pragma unroll
+        for (int w = 0; w < kExWindow / kWave; ++w)
+            bw[w] = 64 * w + lane < a.Er ? a.tile_base[(lo + 64 * w + lane) * a.T + tile] : 0;
         // the row's distinct local experts in first-occurrence order; with one
         // mask word (Er <= 64) repeats are found in a register, else in LDS.
         // Weighted: an expert's weight is the sum, in slot order, of the
@@ -263,34 +282,33 @@ __global__ __launch_bounds__(1024) void ex_copy_kernel(ExpertArgs a)
                 }
             }
         }
-        int n_max = n;  // the wave's longest list
+        // Positions inside the tile: for a window of kExWindow local experts
+        // at a time, each lane ORs its bit into the 64-bit LDS mask of each
+        // of its experts (order-independent, so deterministic); a pair's
+        // position is its expert's tile base plus the mask's bits below the
+        // lane.
+        for (int j0 = 0; j0 < a.Er; j0 += kExWindow) {
 #pragma unroll
-        for (int off = kWave / 2; off > 0; off >>= 1)
-            n_max = max(n_max, __shfl_xor(n_max, off));
-        // Positions, one mask word (64 experts) at a time: lane jj holds the
-        // ballot of expert 64w + jj over the tile and its tile base; each
-        // lane fetches both for its own entries with cross-lane reads.
-        for (int w = 0; 64 * w < a.Er; ++w) {
-            const uint64_t m = a.Er <= kWave ? seen : local_word<KC>(ids, a.k, valid, lo, a.Er, w);
-            const int nj = min(kWave, a.Er - 64 * w);
-            const int bw = lane < nj ? a.tile_base[(lo + 64 * w + lane) * a.T + tile] : 0;
-            uint64_t mine = 0;
-            for (int jj = 0; jj < nj; ++jj) {
-                const uint64_t b = __ballot((m >> jj) & 1);
-                if (lane == jj)
-                    mine = b;
+            for (int w = 0; w < kExWindow / kWave; ++w) {
+                const int jj = 64 * w + lane;
+                s_bal[jj] = 0;
+                s_base[jj] = j0 == 0 ? bw[w]
+                             : j0 + jj < a.Er ? a.tile_base[(lo + j0 + jj) * a.T + tile] : 0;
             }
-            const int mlo = (int)(uint32_t)mine;
-            const int mhi = (int)(uint32_t)(mine >> 32);
-            for (int u = 0; u < n_max; ++u) {
-                const int j = u < n ? s_j[lane][u] - 64 * w : -1;
-                const int src = j & (kWave - 1);
-                const uint32_t blo = (uint32_t)__shfl(mlo, src);
-                const uint32_t bhi = (uint32_t)__shfl(mhi, src);
-                const int base = __shfl(bw, src);
-                if (j >= 0 && j < kWave)
-                    s_p[lane][u] = base + lanes_below(((uint64_t)bhi << 32) | blo);
+            __builtin_amdgcn_wave_barrier();
+            for (int u = 0; u < n; ++u) {
+                const int j = s_j[lane][u] - j0;
+                if (j >= 0 && j < kExWindow)
+                    __hip_atomic_fetch_or(&s_bal[j], 1ull << lane, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_WORKGROUP);
             }
+            __builtin_amdgcn_wave_barrier();
+            for (int u = 0; u < n; ++u) {
+                const int j = s_j[lane][u] - j0;
+                if (j >= 0 && j < kExWindow)
+                    s_p[lane][u] = s_base[j] + lanes_below(s_bal[j]);
+            }
+            __builtin_amdgcn_wave_barrier();
         }
         int kept = 0;  // positions past the capacity are dropped
         for (int u = 0; u < n; ++u) {
@@ -307,7 +325,7 @@ __global__ __launch_bounds__(1024) void ex_copy_kernel(ExpertArgs a)
 
     const int sd = a.scale_dwords;
     if (piece == 0) {
-        for (int r = wave; r < cnt; r += nwaves) {
+        for (int r = r_lo + wave; r < r_hi; r += nwaves) {
             const int64_t row = row0 + r;
             const int n = uniform(s_n[r]);
             if (lane < a.Pe) {
@@ -345,7 +363,7 @@ __global__ __launch_bounds__(1024) void ex_copy_kernel(ExpertArgs a)
         // large pieces (throughput): one chunk a wave in flight, which keeps
         // the register count, and so the waves resident per SIMD, lowest
         for (int it = 0; it < items; ++it) {
-            if (uniform(s_n[wave + (it / nch) * nwaves]) == 0)
+            if (uniform(s_n[r_lo + wave + (it / nch) * nwaves]) == 0)
                 continue;  // a row without a kept expert is not read
             load_item(it, A);
             store_item(it, A);
@@ -455,7 +473,7 @@ hipError_t launch_expert_copy(const ExpertArgs& a, int waves, int row_split, boo
 {
     if (a.rows == 0)
         return hipSuccess;
-    const dim3 grid(a.T, row_split, a.W);
+    const dim3 grid(a.T * a.token_split, row_split, a.W);
     const dim3 block(waves * kWave);
     const int per_lane = (a.piece_vecs + kWave - 1) / kWave;
     if (per_lane <= 1)

@@ -118,6 +118,7 @@ struct ExpertArgs {
     int32_t W, WM, k, Er, Pe, cap;
     int32_t rows;                // most received rows any rank can hold in this call
     int32_t T;                   // tiles a rank: max(1, ceil(rows / 64))
+    int32_t token_split;         // copy blocks sharing a tile, each with its share of rows
 };
 
 struct ExpertCombineArgs {

@@ -319,40 +319,45 @@ int tiles_for(const int32_t* ntok, int W, int tt)
     return n;
 }
 
-// The fused dispatch's copy grid: 64-token tiles of the source ranks, each
-// row cut into pieces and each tile's tokens shared by blocks until the grid
-// has about a target number of blocks: 1024 up to top-16, 512 above (every
-// block routes its whole tile, which costs more the more ids a token has).
-// Calls whose row pieces alone reach the target share no tile; smaller ones
-// share tiles first (at most one token a wave), then cut rows. A value
-// given in the launch overrides (row_split, token_split > 0) is kept.
-struct FusedGrid {
+// The grid of an expert-major copy (ep_convert_dispatch_output's over tiles
+// of 64 received rows, ep_dispatch_standard_moe's over tiles of 64 source
+// tokens): each row cut into pieces and each tile's rows shared by blocks
+// until the grid has about a target number of blocks, 1024 up to top-16 and
+// 512 above (every block routes its whole tile, which costs more the more
+// ids a row has). Calls whose row pieces alone reach the target share no
+// tile; smaller ones share tiles first (at most one row a wave), then cut
+// rows. A value the launch overrides give (row_split, token_split > 0) is kept.
+struct ShareGrid {
     int row_split, token_split;
 };
 
-FusedGrid fused_grid(const Shape& s, const int32_t* ntok, int waves, int row_split,
+ShareGrid share_grid(int64_t tiles, int64_t row_vecs, int k, int waves, int row_split,
                      int token_split)
 {
-    int tiles = 0;
-    for (int r = 0; r < s.W; ++r)
-        tiles += (ntok[r] + ep::kWave - 1) / ep::kWave;
-    tiles = std::max(1, tiles);
-    const int target = s.k <= 16 ? 1024 : 512;
-    const int max_split = std::max(1, s.row_vecs / ep::kWave);
+    tiles = std::max<int64_t>(1, tiles);
+    const int64_t target = k <= 16 ? 1024 : 512;
+    const int max_split = (int)std::min<int64_t>(65535, std::max<int64_t>(1, row_vecs / ep::kWave));
     const int max_share = std::max(1, ep::kWave / std::max(1, waves));
-    auto ceil_div = [](int64_t a, int64_t b) { return (int)((a + b - 1) / b); };
-    FusedGrid g{row_split, token_split};
-    if (g.row_split <= 0 && g.token_split <= 0 && (int64_t)tiles * max_split >= target) {
-        g.row_split = std::min(max_split, ceil_div(target, tiles));
+    auto want = [&](int64_t blocks) { return std::max<int64_t>(1, (target + blocks - 1) / blocks); };
+    ShareGrid g{row_split, token_split};
+    if (g.row_split <= 0 && g.token_split <= 0 && tiles * max_split >= target) {
+        g.row_split = (int)std::min<int64_t>(max_split, want(tiles));
         g.token_split = 1;
     }
     if (g.token_split <= 0)
-        g.token_split = std::min(max_share, std::max(1, ceil_div(target, (int64_t)tiles *
-                                                                     std::max(1, g.row_split))));
+        g.token_split = (int)std::min<int64_t>(max_share, want(tiles * std::max(1, g.row_split)));
     if (g.row_split <= 0)
-        g.row_split = std::min(max_split,
-                               std::max(1, ceil_div(target, (int64_t)tiles * g.token_split)));
+        g.row_split = (int)std::min<int64_t>(max_split, want(tiles * g.token_split));
     return g;
+}
+
+// Tiles of 64 source tokens of a fused dispatch.
+int64_t fused_tiles(const Shape& s, const int32_t* ntok)
+{
+    int64_t tiles = 0;
+    for (int r = 0; r < s.W; ++r)
+        tiles += (ntok[r] + ep::kWave - 1) / ep::kWave;
+    return tiles;
 }
 
 // Automatic geometry. Small calls get smaller routing tiles and rows split
@@ -401,15 +406,15 @@ ep_launch_t auto_launch(const ep_plan* p, const int32_t* ntok)
         l.layout = EP_LAYOUT_SCAN_IN_COPY;
     else
         l.layout = EP_LAYOUT_KERNELS;
-    // expert-major layout: 64 received rows a copy block, a row a wave in the
-    // inverse, pieces until the grid has about kTargetBlocks blocks
+    // expert-major layout: 64 received rows a copy tile (share_grid), a row
+    // a wave in the inverse, pieces until the grid has about kTargetBlocks
+    // blocks
     const int64_t rows = expert_rows(s, ntok);
-    const int64_t eblocks = (int64_t)s.W * expert_tiles(rows);
     l.expert_waves = 8;
-    const int64_t ex_max_split = std::max<int64_t>(1, s.row_bytes / 16 / ep::kWave);
-    l.expert_row_split = (int)std::min<int64_t>(
-        std::min<int64_t>(ex_max_split, 65535),
-        std::max<int64_t>(1, (kTargetBlocks + eblocks - 1) / eblocks));
+    const ShareGrid eg = share_grid((int64_t)s.W * expert_tiles(rows), s.row_bytes / 16, s.k,
+                                    l.expert_waves, 0, 0);
+    l.expert_row_split = eg.row_split;
+    l.expert_token_split = eg.token_split;
     l.expert_combine_waves = 4;
     const int64_t iblocks = std::max<int64_t>(1, s.W * ((rows + 3) / 4));
     l.expert_combine_row_split = (int)std::min<int64_t>(
@@ -423,7 +428,6 @@ ep_launch_t auto_launch(const ep_plan* p, const int32_t* ntok)
     // cached vs 317 us streaming).
     const int64_t ex_bytes = N * (s.row_bytes + s.crow_bytes) * (s.P + s.k);
     l.expert_cache_policy = ex_bytes <= 2 * kKeepBytes ? EP_CACHE_KEEP : EP_CACHE_STREAM;
-    l.expert_token_split = fused_grid(s, ntok, l.expert_waves, 0, 0).token_split;
     return l;
 }
 
@@ -1082,7 +1086,11 @@ int ep_convert_dispatch_output(ep_expert_plan_t* x, const ep_convert_dispatch_ar
     ea.efwd = reinterpret_cast<int32_t*>(x->ws + x->e.off_efwd);
     ea.ew = reinterpret_cast<float*>(x->ws + x->e.off_ew);
     ea.row_vecs = (int32_t)(s.row_bytes / 16);
-    ea.piece_vecs = (ea.row_vecs + l.expert_row_split - 1) / l.expert_row_split;
+    const ShareGrid eg = share_grid((int64_t)s.W * expert_tiles(rows), ea.row_vecs, s.k,
+                                    l.expert_waves, std::max(0, p->launch.expert_row_split),
+                                    std::max(0, p->launch.expert_token_split));
+    ea.piece_vecs = (ea.row_vecs + eg.row_split - 1) / eg.row_split;
+    ea.token_split = eg.token_split;
     ea.scale_dwords = (int32_t)(s.scale_bytes / 4);
     ea.W = s.W;
     ea.WM = (int32_t)s.WM;
@@ -1243,9 +1251,9 @@ int ep_dispatch_standard_moe(ep_expert_plan_t* x, const ep_dispatch_standard_arg
     sa.Tr = (int32_t)x->e.Tr;
     for (int r = 0; r < ep::kMaxRanks; ++r)
         sa.ntok[r] = r < s.W ? a->num_tokens[r] : 0;
-    // row pieces and blocks sharing a tile (fused_grid), unless overridden
-    const FusedGrid fg = fused_grid(s, a->num_tokens, l.expert_waves,
-                                    std::max(0, p->launch.expert_row_split),
+    // row pieces and blocks sharing a tile (share_grid), unless overridden
+    const ShareGrid fg = share_grid(fused_tiles(s, a->num_tokens), sa.row_vecs, s.k,
+                                    l.expert_waves, std::max(0, p->launch.expert_row_split),
                                     std::max(0, p->launch.expert_token_split));
     sa.piece_vecs = (sa.row_vecs + fg.row_split - 1) / fg.row_split;
     const int row_split = (sa.row_vecs + sa.piece_vecs - 1) / sa.piece_vecs;

@@ -315,7 +315,8 @@ typedef struct ep_launch {
     /* Expert-major layout (ep_convert_dispatch_output and its inverse):
      *   expert_waves              wavefronts per copy block (64 received
      *                             rows a block): 1..16.
-     *   expert_row_split          blocks sharing a tile's rows: 1..row_bytes/16.
+     *   expert_row_split          pieces a copied row is cut into, a block
+     *                             each: 1..row_bytes/16.
      *   expert_combine_waves      wavefronts per inverse block: 1..16.
      *   expert_combine_row_split  pieces an inverse row is split into: 1..H/8.
      *   expert_cache_policy       as cache_policy, for these calls; automatic:
@@ -324,11 +325,15 @@ typedef struct ep_launch {
      *                             out and back) stay within 512 MB (rows read
      *                             were just written, so they partly hit the
      *                             256 MB cache), stream above.
-     *   expert_token_split        blocks sharing a 64-token tile of
-     *                             ep_dispatch_standard_moe's copy, each
-     *                             copying its share of the tile's tokens:
-     *                             1..64; automatic: until the grid has about
-     *                             1024 blocks, at most 64 / expert_waves. */
+     *   expert_token_split        blocks sharing a tile of 64 rows (received
+     *                             rows in ep_convert_dispatch_output, source
+     *                             tokens in ep_dispatch_standard_moe), each
+     *                             copying its share of them: 1..64.
+     *   Automatic expert_row_split and expert_token_split: a call whose row
+     *   pieces alone give about 1024 copy blocks (512 above top-16) shares no
+     *   tile; a smaller call shares tiles first (at most 64 / expert_waves
+     *   blocks a tile), then cuts rows. ep_plan_get_launch reports the values
+     *   of ep_convert_dispatch_output. */
     int32_t expert_waves;
     int32_t expert_row_split;
     int32_t expert_combine_waves;

@@ -258,11 +258,14 @@ def test_launch_override_limits_and_auto_geometry(lib):
         cra.EP_LAYOUT_KERNELS
     with pytest.raises(cra.EpError):
         cra.ep_plan_get_launch(plan, [4097] + [0] * 7)
-    # the fused dispatch's copy: 512 tiles x 14 row pieces reach 1024 blocks
-    # without sharing a tile; 16 tiles x 14 pieces do not, so small calls
-    # share each tile first, at most one token a wave
-    assert auto["expert_token_split"] == 1
-    for few in ([128] * 8, [16] * 8, [1] + [0] * 7):
+    # the expert-major copy (tiles of 64 of the most rows a rank can hold):
+    # 8 x 512 tiles, and 8 x 16 tiles x 14 row pieces, reach 1024 blocks
+    # without sharing a tile; 8 x 2 tiles x 14 pieces do not, so small calls
+    # share each tile first, at most one row a wave
+    assert auto["expert_token_split"] == 1 and auto["expert_row_split"] == 1
+    mid = cra.ep_plan_get_launch(plan, [128] * 8)
+    assert mid["expert_token_split"] == 1 and mid["expert_row_split"] == 8
+    for few in ([16] * 8, [1] + [0] * 7):
         dec = cra.ep_plan_get_launch(plan, few)
         assert dec["expert_token_split"] == 64 // dec["expert_waves"]
     for bad in (dict(expert_token_split=65),):

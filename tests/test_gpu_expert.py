@@ -203,6 +203,10 @@ def test_world_expert_topk_sweep(W, E, k):
          expert_combine_row_split=5),
     dict(expert_row_split=1, expert_combine_row_split=1, expert_cache_policy=cra.EP_CACHE_STREAM),
     dict(expert_waves=3, expert_row_split=2, expert_cache_policy=cra.EP_CACHE_KEEP),
+    # tiles shared between blocks: shares of 22, 13 (ragged tails), 1 row
+    dict(expert_token_split=3),
+    dict(expert_token_split=5, expert_waves=2, expert_row_split=1),
+    dict(expert_token_split=64, expert_waves=1),
 ])
 def test_geometry_does_not_change_results(launch):
     wl = workloads.custom("ex_geom_ep4_t200_h1024", 4, 200, 1024, 8, 64, "bf16", ragged=True,
@@ -423,6 +427,8 @@ def _random_case(seed):
                                          H * (1 if dd == "fp8" else 2) // 16)
         launch["expert_combine_row_split"] = min(launch["expert_combine_row_split"], H * 2 // 16)
     cap_div = int(rng.choice([1, 1, 2, 5]))
+    if launch is not None:  # drawn last, so the draws above stay as they were
+        launch["expert_token_split"] = int(rng.integers(0, 65))
     return wl, launch, cap_div
 
 

@@ -479,7 +479,10 @@ def _random_standard_case(seed):
                       expert_combine_waves=int(rng.integers(1, 17)),
                       expert_combine_row_split=int(rng.integers(1, max(2, H * 2 // 16 + 1))),
                       expert_cache_policy=int(rng.integers(0, 3)))
-    return wl, launch, int(rng.choice([1, 2, 5, 1000])), bool(rng.random() < 0.5)
+    cap_div, weighted = int(rng.choice([1, 2, 5, 1000])), bool(rng.random() < 0.5)
+    if launch is not None:  # drawn last, so the draws above stay as they were
+        launch["expert_token_split"] = int(rng.integers(0, 65))
+    return wl, launch, cap_div, weighted
 
 
 @pytest.mark.parametrize("seed", range(16))
