@@ -228,6 +228,13 @@ hipError_t launch_expert_combine(const ExpertCombineArgs& a, int W, int dtype, i
                                  int row_split, bool stream, hipStream_t s);
 
 hipError_t launch_standard_count(const StandardArgs& a, hipStream_t s);
+// Calls of at most kCountScanTiles (source rank, tile) pairs and top-k at
+// most kCountScanTopK: count and scan in one launch, a tile a wave (the count
+// launch is not made). Every block of it reads all the call's ids, which
+// measured slower than two launches at 64 tiles of top-64 tokens.
+constexpr int kCountScanTiles = 16;
+constexpr int kCountScanTopK = 16;
+hipError_t launch_standard_count_scan(const StandardArgs& a, hipStream_t s);
 hipError_t launch_standard_scan(const StandardArgs& a, hipStream_t s);
 hipError_t launch_standard_copy(const StandardArgs& a, int waves, int row_split, bool stream,
                                 hipStream_t s);

@@ -1259,11 +1259,20 @@ int ep_dispatch_standard_moe(ep_expert_plan_t* x, const ep_dispatch_standard_arg
     const int row_split = (sa.row_vecs + sa.piece_vecs - 1) / sa.piece_vecs;
     sa.token_split = fg.token_split;
 
-    hipError_t e = timed(p, EP_KERNEL_STANDARD_COUNT, stream,
-                         [&] { return ep::launch_standard_count(sa, stream); });
-    if (e == hipSuccess)
+    // small calls count and scan in one launch (timed as the scan)
+    const bool one = (int64_t)s.W * sa.Tr <= ep::kCountScanTiles &&
+                     s.k <= ep::kCountScanTopK && p->launch.layout != EP_LAYOUT_KERNELS;
+    hipError_t e = hipSuccess;
+    if (one) {
         e = timed(p, EP_KERNEL_STANDARD_SCAN, stream,
-                  [&] { return ep::launch_standard_scan(sa, stream); });
+                  [&] { return ep::launch_standard_count_scan(sa, stream); });
+    } else {
+        e = timed(p, EP_KERNEL_STANDARD_COUNT, stream,
+                  [&] { return ep::launch_standard_count(sa, stream); });
+        if (e == hipSuccess)
+            e = timed(p, EP_KERNEL_STANDARD_SCAN, stream,
+                      [&] { return ep::launch_standard_scan(sa, stream); });
+    }
     if (e == hipSuccess)
         e = timed(p, EP_KERNEL_STANDARD_COPY, stream, [&] {
             return ep::launch_standard_copy(sa, l.expert_waves, row_split,

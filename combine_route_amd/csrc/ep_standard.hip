@@ -47,6 +47,8 @@ constexpr int kSxWaves = 4;  // count and scan: waves a block, one tile or list 
 // and the experts whose tile masks it holds in LDS at a time.
 constexpr int kSeenWords = 4;
 constexpr int kWinExperts = kSeenWords * kWave;
+// The one-launch count and scan: a wave per tile.
+constexpr int kCountScanWaves = kCountScanTiles;
 
 // Tokens of source rank r in this call.
 __device__ __forceinline__ int tokens_of(const StandardArgs& a, int r)
@@ -89,21 +91,22 @@ __global__ __launch_bounds__(kSxWaves * kWave) void sx_count_kernel(StandardArgs
         counts[(int64_t)lane * TT] = c;
 }
 
-__global__ __launch_bounds__(kSxWaves * kWave) void sx_scan_kernel(StandardArgs a)
+// Expert g's exclusive scan over its (source rank, tile) counts, one wave:
+// tile bases, the expert's row count, and its layout range for every source
+// rank (a source rank's first tile's base is where its rows start). cnt(t)
+// gives tile t's count.
+template <typename Count>
+__device__ __forceinline__ void scan_expert(const StandardArgs& a, int64_t g, Count cnt)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t g = (int64_t)blockIdx.x * kSxWaves + uniform(threadIdx.x / kWave);
-    if (g >= a.E)
-        return;  // whole waves
     const int TT = a.W * a.Tr;
-    const int32_t* cnt = a.tile_counts + g * TT;
     int32_t* base = a.tile_base + g * TT;
     // lane s < W: source rank s's first tile; its base is where s's rows start
     const int start_tile = lane < a.W ? lane * a.Tr : TT;
     int start = 0, carry = 0;
     for (int c0 = 0; c0 < TT; c0 += kWave) {
         const int t = c0 + lane;
-        const int v = t < TT ? cnt[t] : 0;
+        const int v = t < TT ? cnt(t) : 0;
         int inc = v;  // inclusive prefix over the wave
 #pragma unroll
         for (int o = 1; o < kWave; o <<= 1) {
@@ -129,6 +132,58 @@ __global__ __launch_bounds__(kSxWaves * kWave) void sx_scan_kernel(StandardArgs 
         const int64_t hi = min(next, a.cap);
         a.layout_range[g * a.W + lane] = (lo << 32) | (hi - lo);
     }
+}
+
+__global__ __launch_bounds__(kSxWaves * kWave) void sx_scan_kernel(StandardArgs a)
+{
+    const int64_t g = (int64_t)blockIdx.x * kSxWaves + uniform(threadIdx.x / kWave);
+    if (g >= a.E)
+        return;  // whole waves
+    const int32_t* cnt = a.tile_counts + g * ((int64_t)a.W * a.Tr);
+    scan_expert(a, g, [&](int t) { return cnt[t]; });
+}
+
+// Calls of at most kCountScanTiles tiles: the count and the scan in one
+// launch, a block per expert. Its waves count the expert's tokens in the
+// tiles (a tile a wave, a lane per token, one ballot) into LDS; then wave 0
+// scans them as sx_scan_kernel does. Every block reads all the call's ids,
+// which is cheap only for small calls.
+template <int KB>
+__global__ __launch_bounds__(kCountScanWaves * kWave) void sx_count_scan_kernel(StandardArgs a)
+{
+    __shared__ int32_t s_cnt[kCountScanTiles];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = uniform(threadIdx.x / kWave);
+    const int g = blockIdx.x;
+    const int TT = a.W * a.Tr;
+    if (TT > kCountScanTiles)
+        return;  // not launched for such calls
+    constexpr int KC = id_chunk<KB>();
+    for (int t = wave; t < TT; t += kCountScanWaves) {
+        const int r = t / a.Tr;
+        const int tile = t - r * a.Tr;
+        const int T = tokens_of(a, r);
+        const int q = tile * kWave + lane;
+        const bool valid = q < T;
+        int c = 0;
+        if (tile * kWave < T) {  // uniform
+            const int32_t* ids = a.idx + ((int64_t)r * a.M + (valid ? q : 0)) * a.k;
+            bool names = false;
+            for (int c0 = 0; c0 * KC < a.k; ++c0) {
+                int32_t id[KC];
+                load_ids<KC>(ids, a.k, c0, id);
+#pragma unroll
+                for (int i = 0; i < KC; ++i)
+                    names = names || (c0 * KC + i < a.k && id[i] == g);
+            }
+            c = __popcll(__ballot(valid && names));
+        }
+        if (lane == 0)
+            s_cnt[t] = c;
+    }
+    __syncthreads();
+    if (wave == 0)
+        scan_expert(a, g, [&](int t) { return s_cnt[t]; });
 }
 
 // kCast: the source rows are bf16 / fp16 (a.cast) and the packed rows E4M3
@@ -673,6 +728,19 @@ hipError_t launch_standard_count(const StandardArgs& a, hipStream_t s)
     case 16: hipLaunchKernelGGL((sx_count_kernel<16>), grid, block, 0, s, a); break;
     case 32: hipLaunchKernelGGL((sx_count_kernel<32>), grid, block, 0, s, a); break;
     default: hipLaunchKernelGGL((sx_count_kernel<64>), grid, block, 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_standard_count_scan(const StandardArgs& a, hipStream_t s)
+{
+    const dim3 grid((unsigned)a.E);
+    const dim3 block(kCountScanWaves * kWave);
+    switch (sx_bucket(a.k)) {
+    case 8: hipLaunchKernelGGL((sx_count_scan_kernel<8>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((sx_count_scan_kernel<16>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((sx_count_scan_kernel<32>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((sx_count_scan_kernel<64>), grid, block, 0, s, a); break;
     }
     return hipGetLastError();
 }

@@ -185,6 +185,8 @@ def test_world_expert_topk_sweep(W, E, k):
     dict(expert_token_split=3),
     dict(expert_token_split=5, expert_waves=2, expert_row_split=1),
     dict(expert_token_split=64, expert_waves=1),
+    # count and scan as two kernels (this call's 16 tiles otherwise take one)
+    dict(layout=cra.EP_LAYOUT_KERNELS),
 ])
 def test_geometry_does_not_change_results(launch):
     wl = workloads.custom("std_geom_ep4_t200_h1024", 4, 200, 1024, 8, 64, "bf16", ragged=True,
