@@ -7,14 +7,16 @@
 // that convert_dispatch_output gives it after a dispatch: an expert's list
 // keeps the receive order, which is source rank, then source token. Here the
 // lists are counting-sorted straight over the source tokens, with the same
-// deterministic scheme: a 64-lane ballot per expert over a tile of 64 tokens
-// of one source rank, an exclusive scan per expert over (source rank, tile),
-// and the ballot prefix inside a tile. A source rank starts a new tile, so a
-// layout range is read off the tile bases.
-//   count    a wave per (source rank, tile): how many of its tokens name each
-//            expert.
+// deterministic scheme: per expert, the count of a tile of 64 tokens of one
+// source rank, an exclusive scan over (source rank, tile), and the prefix
+// inside a tile (the tile's tokens naming the expert below the token). A
+// source rank starts a new tile, so a layout range is read off the tile bases.
+//   count    a wave per (source rank, tile, 64 experts): one ballot per
+//            expert gives how many of the tile's tokens name it.
 //   scan     a wave per expert: tile bases, the expert's row count, and its
-//            layout range for every source rank.
+//            layout range for every source rank. Calls of at most 16 tiles
+//            (top-16 or fewer) count and scan in one launch, a block per
+//            expert.
 //   copy     a block per (source rank, tile, row piece, share of the tile's
 //            tokens): wave 0 works out the kept packed row of every (token,
 //            expert) pair of the tile into LDS; then every wave loads a token
