@@ -187,10 +187,11 @@ def test_capacity_drops(wl, cap_div):
 
 
 @pytest.mark.parametrize("W,E,k", [(2, 300, 8), (1, 130, 9), (4, 520, 17), (2, 40, 33),
-                                   (3, 66, 64), (64, 512, 8), (8, 64, 1)])
+                                   (3, 66, 64), (64, 512, 8), (8, 64, 1), (1, 600, 12)])
 def test_world_expert_topk_sweep(W, E, k):
-    """More than 64 experts a rank (several mask words), every top-k bucket,
-    64 source ranks, one rank."""
+    """More than 64 experts a rank (several mask words), more than 256 (the
+    copy's positions over several LDS windows), every top-k bucket, 64
+    source ranks, one rank."""
     M = 96 if W <= 8 else 12
     wl = workloads.custom(f"ex_sweep_W{W}_E{E}_k{k}", W, M, 128, k, E, "bf16", ragged=True,
                           seed_index=510 + W + k)

@@ -164,11 +164,13 @@ def test_signed_zero_with_dropped_ranks(cap_div, weighted):
 
 
 @pytest.mark.parametrize("W,E,k", [(2, 300, 8), (1, 130, 9), (4, 520, 17), (2, 40, 33),
-                                   (3, 66, 64), (64, 512, 8), (8, 64, 1), (16, 48, 24)])
+                                   (3, 66, 64), (64, 512, 8), (8, 64, 1), (16, 48, 24),
+                                   (2, 1100, 12)])
 def test_world_expert_topk_sweep(W, E, k):
-    """More than 64 experts (several mask words), at most 64 (register
-    repeats), every top-k bucket, 64 source ranks, one rank, more ranks a
-    token than a fold group holds."""
+    """More than 64 experts (several mask words), more than 256 (repeats in
+    LDS, positions over several LDS windows), at most 64 (register repeats),
+    every top-k bucket, 64 source ranks, one rank, more ranks a token than a
+    fold group holds."""
     M = 96 if W <= 8 else 12
     wl = workloads.custom(f"std_sweep_W{W}_E{E}_k{k}", W, M, 128, k, E, "bf16", ragged=True,
                           seed_index=560 + W + k)
