@@ -277,6 +277,46 @@ __device__ __forceinline__ int rank_of_token(const TokenMap& tk, int flat)
 template <int KB>
 constexpr int id_chunk() { return KB < 16 ? KB : 16; }
 
+// In-tile positions of a tile's (row, expert) pairs, one wave, lane = row.
+// The lane's n distinct experts are list[0..n) (indices in [0, count)); its
+// positions go to pos[0..n). For a window of 64 * kWords experts at a time,
+// each lane ORs its bit into the 64-bit LDS mask of each of its experts (OR
+// does not depend on the order the lanes arrive in, so the positions are
+// deterministic) and a pair's position is its expert's tile base plus the
+// mask's bits below the lane. first[w] holds the tile base of expert
+// 64w + lane of the first window (loaded early by the caller), base_at(e)
+// loads expert e's; s_bal and s_base hold 64 * kWords entries.
+template <int kWords, typename BaseAt>
+__device__ __forceinline__ void tile_positions(const int32_t* list, int32_t* pos, int n, int count,
+                                               const int (&first)[kWords], BaseAt base_at,
+                                               uint64_t* s_bal, int32_t* s_base)
+{
+    constexpr int kWin = kWords * kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int e0 = 0; e0 < count; e0 += kWin) {
+#pragma unroll
+        for (int w = 0; w < kWords; ++w) {
+            const int j = 64 * w + lane;
+            s_bal[j] = 0;
+            s_base[j] = e0 == 0 ? first[w] : e0 + j < count ? base_at(e0 + j) : 0;
+        }
+        __builtin_amdgcn_wave_barrier();
+        for (int u = 0; u < n; ++u) {
+            const int j = list[u] - e0;
+            if (j >= 0 && j < kWin)
+                __hip_atomic_fetch_or(&s_bal[j], 1ull << lane, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        __builtin_amdgcn_wave_barrier();
+        for (int u = 0; u < n; ++u) {
+            const int j = list[u] - e0;
+            if (j >= 0 && j < kWin)
+                pos[u] = s_base[j] + lanes_below(s_bal[j]);
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
 template <int KC>
 __device__ __forceinline__ void load_ids(const int32_t* row, int k, int c, int32_t (&ids)[KC])
 {

@@ -282,34 +282,10 @@ __global__ __launch_bounds__(1024) void ex_copy_kernel(ExpertArgs a)
                 }
             }
         }
-        // Positions inside the tile: for a window of kExWindow local experts
-        // at a time, each lane ORs its bit into the 64-bit LDS mask of each
-        // of its experts (order-independent, so deterministic); a pair's
-        // position is its expert's tile base plus the mask's bits below the
-        // lane.
-        for (int j0 = 0; j0 < a.Er; j0 += kExWindow) {
-#pragma unroll
-            for (int w = 0; w < kExWindow / kWave; ++w) {
-                const int jj = 64 * w + lane;
-                s_bal[jj] = 0;
-                s_base[jj] = j0 == 0 ? bw[w]
-                             : j0 + jj < a.Er ? a.tile_base[(lo + j0 + jj) * a.T + tile] : 0;
-            }
-            __builtin_amdgcn_wave_barrier();
-            for (int u = 0; u < n; ++u) {
-                const int j = s_j[lane][u] - j0;
-                if (j >= 0 && j < kExWindow)
-                    __hip_atomic_fetch_or(&s_bal[j], 1ull << lane, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_WORKGROUP);
-            }
-            __builtin_amdgcn_wave_barrier();
-            for (int u = 0; u < n; ++u) {
-                const int j = s_j[lane][u] - j0;
-                if (j >= 0 && j < kExWindow)
-                    s_p[lane][u] = s_base[j] + lanes_below(s_bal[j]);
-            }
-            __builtin_amdgcn_wave_barrier();
-        }
+        // positions inside the tile, from LDS expert masks
+        tile_positions<kExWindow / kWave>(
+            s_j[lane], s_p[lane], n, a.Er, bw,
+            [&](int j) { return a.tile_base[(lo + j) * a.T + tile]; }, s_bal, s_base);
         int kept = 0;  // positions past the capacity are dropped
         for (int u = 0; u < n; ++u) {
             const int p = s_p[lane][u];

@@ -325,38 +325,11 @@ __global__ __launch_bounds__(1024) void sx_copy_kernel(StandardArgs a)
                 s_u[lane][slot] = (int8_t)u;
             }
         }
-        // Positions inside the tile: for a window of kWinExperts experts at a
-        // time, each lane ORs its bit into the 64-bit LDS mask of each of its
-        // experts (order-independent, so deterministic); a pair's position is
-        // its expert's tile base plus the mask's bits below the lane. The
-        // first window's tile bases were loaded before the ids.
-        const int nwin = (a.E + kWinExperts - 1) / kWinExperts;
-        for (int w0 = 0; w0 < nwin; ++w0) {
-            const int e0 = w0 * kWinExperts;
-#pragma unroll
-            for (int w = 0; w < kSeenWords; ++w) {
-                const int e = e0 + 64 * w + lane;
-                int b = bw[w];
-                if (w0 > 0)
-                    b = e < a.E ? a.tile_base[(int64_t)e * TT + (int64_t)r * a.Tr + tile] : 0;
-                s_bal[64 * w + lane] = 0;
-                s_base[64 * w + lane] = b;
-            }
-            __builtin_amdgcn_wave_barrier();
-            for (int u = 0; u < n; ++u) {
-                const int j = s_e[lane][u] - e0;
-                if (j >= 0 && j < kWinExperts)
-                    __hip_atomic_fetch_or(&s_bal[j], 1ull << lane, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_WORKGROUP);
-            }
-            __builtin_amdgcn_wave_barrier();
-            for (int u = 0; u < n; ++u) {
-                const int j = s_e[lane][u] - e0;
-                if (j >= 0 && j < kWinExperts)
-                    s_p[lane][u] = s_base[j] + lanes_below(s_bal[j]);
-            }
-            __builtin_amdgcn_wave_barrier();
-        }
+        // positions inside the tile, from LDS expert masks
+        tile_positions<kSeenWords>(
+            s_e[lane], s_p[lane], n, a.E, bw,
+            [&](int e) { return a.tile_base[(int64_t)e * TT + (int64_t)r * a.Tr + tile]; }, s_bal,
+            s_base);
         // the combine's map: the packed row of each slot that is its expert's
         // first occurrence and was kept, else -1 (each block its own tokens)
         if (piece == 0 && valid && lane >= t_lo && lane < t_hi) {
