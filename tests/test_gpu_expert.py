@@ -433,7 +433,7 @@ def _random_case(seed):
     return wl, launch, cap_div
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(48))
 def test_random_configurations(seed):
     wl, launch, cap_div = _random_case(seed)
     run_expert_case(wl, launch=launch, cap_div=cap_div, tag=f"ex random seed {seed}")

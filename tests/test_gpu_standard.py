@@ -489,7 +489,7 @@ def _random_standard_case(seed):
     return wl, launch, cap_div, weighted
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(48))
 def test_random_configurations(seed):
     wl, launch, cap_div, weighted = _random_standard_case(seed)
     run_standard_case(wl, cap_div=cap_div, launch=launch, weighted=weighted,
