@@ -494,3 +494,51 @@ def test_random_configurations(seed):
     wl, launch, cap_div, weighted = _random_standard_case(seed)
     run_standard_case(wl, cap_div=cap_div, launch=launch, weighted=weighted,
                       tag=f"std random {seed}")
+
+
+def test_soak_500_rounds():
+    """500 fused dispatch + weighted combine rounds on one plan, alternating two
+    inputs, with capacity drops: every round's counts, layout ranges and
+    combine output equal the first round's for the same input, bit for bit;
+    the first rounds are checked against the oracle."""
+    wl = workloads.custom("std_soak_ep4_t96_h512", 4, 96, 512, 8, 64, "bf16", ragged=True,
+                          seed_index=590)
+    W, M, k, Er, H = _dims(wl)
+    inps = [workloads.make_inputs(wl, seed=5000 + i) for i in range(2)]
+    refs = [oracle_dispatch(wl, i) for i in inps]
+    cap = max(1, min(max_count(wl, r) for r in refs) // 2)
+    op = cra.EpDispatchCombineOp(config_of(wl), with_weights=False, expert_capacity=cap)
+    dev = [(i["x"].cuda(), i["idx"].cuda(), i["w"].cuda()) for i in inps]
+    v = random_outputs(wl, cap, seed=590)
+    py = v.cuda()
+    _say("[case] fused soak 500 rounds")
+    first = [None, None]
+    for rnd in range(500):
+        j = rnd % 2
+        x, idx, w = dev[j]
+        ntok = inps[j]["ntok"]
+        _, cnt, _, lr = op.dispatch_standard_moe(x, None, None, idx, num_tokens=ntok)
+        out = op.combine_standard_moe(py, w, idx)
+        # rows t < T_r only: the others keep whatever the other input left
+        got = (cnt.clone(), lr.clone(),
+               *[out[r, :ntok[r]].view(torch.int16).clone() for r in range(W)])
+        if first[j] is None:
+            first[j] = got
+        elif rnd % 7 == 0 or rnd >= 490:
+            assert all(torch.equal(a, b) for a, b in zip(got, first[j])), ("fused soak", rnd)
+    torch.cuda.synchronize()
+    py16 = v.view(torch.int16).numpy().view(np.uint16)
+    for j in range(2):
+        ref = refs[j]
+        ref_ex = oracle.expert_layout(W, M, k, Er, cap, ref["recv"], ref["src_pos"], ref["out_x"],
+                                      ref["out_idx"], ref["out_scales"], fill=SENTINEL_INT)
+        assert np.array_equal(first[j][0].cpu().numpy(), ref_ex["count"]), ("soak count", j)
+        assert np.array_equal(first[j][1].cpu().numpy(), ref_ex["layout_range"]), ("soak lr", j)
+        ref_y = oracle.expert_combine(W, M, k, Er, cap, H, oracle.BF16, ref["recv"],
+                                      ref["out_idx"], py16, w=ref["out_w"])
+        ro, _ = oracle.combine(W, M, k, H, oracle.BF16, inps[j]["ntok"], ref["fwd"], ref_y)
+        for r in range(W):
+            T = inps[j]["ntok"][r]
+            g = first[j][2 + r].cpu().numpy().view(np.uint16)
+            assert np.array_equal(g, ro[r, :T]), ("soak combine", j, r)
+    op.close()
