@@ -267,6 +267,39 @@ def test_two_plans_interleaved():
     opb.close()
 
 
+def test_two_plans_on_two_streams():
+    """Two plans enqueued on two streams (default priority) for ten rounds
+    without a synchronisation in between, so their kernels can run at the
+    same time: plans share no device state, so each matches the oracle."""
+    wa = workloads.custom("conc_a", 8, 256, 2048, 8, 256, "bf16", seed_index=407)
+    wb = workloads.custom("conc_b", 4, 512, 4096, 8, 64, "bf16", ragged=True, seed_index=408)
+    ia, ib = workloads.make_inputs(wa), workloads.make_inputs(wb)
+    ra, rb = oracle_dispatch(wa, ia), oracle_dispatch(wb, ib)
+    opa = cra.EpDispatchCombineOp(config_of(wa))
+    opb = cra.EpDispatchCombineOp(config_of(wb))
+    da = tuple(t.cuda() for t in (ia["x"], ia["idx"], ia["w"]))
+    db = tuple(t.cuda() for t in (ib["x"], ib["idx"], ib["w"]))
+    ya = upload_rows(experts.identity(wa, ra), ra["recv"], torch.bfloat16)
+    yb = upload_rows(experts.identity(wb, rb), rb["recv"], torch.bfloat16)
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    _say("[case] two plans on two streams")
+    for _ in range(10):
+        opa.dispatch(ia["ntok"], *da, stream=sa)
+        opb.dispatch(ib["ntok"], *db, stream=sb)
+        oa, _ = opa.combine(ya, stream=sa)
+        ob, _ = opb.combine(yb, stream=sb)
+    torch.cuda.synchronize()
+    compare_dispatch(wa, opa, ra, "a")
+    compare_dispatch(wb, opb, rb, "b")
+    for wl, inp, ref, out in ((wa, ia, ra, oa), (wb, ib, rb, ob)):
+        ro, _ = oracle.combine(wl.world_size, wl.max_tokens, wl.topk, wl.hidden, oracle.BF16,
+                               inp["ntok"], ref["fwd"], experts.identity(wl, ref))
+        compare_combine(wl, inp["ntok"], out, None, ro, None, wl.name)
+    opa.close()
+    opb.close()
+
+
 def test_deterministic_across_runs():
     wl = workloads.WORKLOADS["ep4_ragged1024_h2048_fp16_k64"]
     inp = workloads.make_inputs(wl)
