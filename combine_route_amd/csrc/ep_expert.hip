@@ -108,29 +108,26 @@ __global__ __launch_bounds__(kExWaves * kWave) void ex_count_kernel(ExpertArgs a
     }
 }
 
-__global__ __launch_bounds__(kExWaves * kWave) void ex_scan_kernel(ExpertArgs a)
+// List g's exclusive scan over its tile counts, one wave: tile bases, the
+// expert's row count, and its layout range for every source rank. cnt(t)
+// gives tile t's count; source(s) the row where source s starts (>= R: none)
+// and the list's rows before it in that row's tile.
+template <typename Count, typename Source>
+__device__ __forceinline__ void scan_list(const ExpertArgs& a, int64_t g, int R, Count cnt,
+                                          Source source)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t g = (int64_t)blockIdx.x * kExWaves + uniform(threadIdx.x / kWave);
-    if (g >= (int64_t)a.W * a.Er)
-        return;  // whole waves
-    const int d = (int)(g / a.Er);
-    const int R = received(a.recv[d], a.rows);
-    const int32_t* cnt = a.tile_counts + g * a.T;
     int32_t* base = a.tile_base + g * a.T;
     // lane s < W: the row where source s starts and the expert's rows before
     // it in that row's tile
     int start_row = R, pre = 0;
-    if (lane < a.W) {
-        start_row = min(a.src_start[d * a.W + lane], R);
-        if (start_row < R)
-            pre = a.src_prefix[g * a.W + lane];
-    }
+    if (lane < a.W)
+        source(lane, start_row, pre);
     const int start_tile = start_row / kWave;
     int start = 0, carry = 0;
     for (int c0 = 0; c0 < a.T; c0 += kWave) {
         const int t = c0 + lane;
-        const int v = t < a.T ? cnt[t] : 0;
+        const int v = t < a.T ? cnt(t) : 0;
         int inc = v;  // inclusive prefix over the wave
 #pragma unroll
         for (int o = 1; o < kWave; o <<= 1) {
@@ -158,6 +155,89 @@ __global__ __launch_bounds__(kExWaves * kWave) void ex_scan_kernel(ExpertArgs a)
         const int64_t hi = min(next, a.cap);
         a.layout_range[g * a.W + lane] = (lo << 32) | (hi - lo);
     }
+}
+
+__global__ __launch_bounds__(kExWaves * kWave) void ex_scan_kernel(ExpertArgs a)
+{
+    const int64_t g = (int64_t)blockIdx.x * kExWaves + uniform(threadIdx.x / kWave);
+    if (g >= (int64_t)a.W * a.Er)
+        return;  // whole waves
+    const int d = (int)(g / a.Er);
+    const int R = received(a.recv[d], a.rows);
+    const int32_t* cnt = a.tile_counts + g * a.T;
+    scan_list(a, g, R, [&](int t) { return cnt[t]; }, [&](int s, int& row, int& pre) {
+        row = min(a.src_start[d * a.W + s], R);
+        if (row < R)
+            pre = a.src_prefix[g * a.W + s];
+    });
+}
+
+// Calls of at most kCountScanTiles tiles a rank and top-k at most
+// kCountScanTopK: the count and the scan in one launch, a block per (rank,
+// local expert) list. Its waves count the list's rows in one tile each (a
+// lane per row, one ballot) into LDS, and the row that starts each source
+// rank records itself and the list's rows before it in its tile; then wave
+// 0 scans as ex_scan_kernel does. Every block reads its rank's ids.
+template <int KB>
+__global__ __launch_bounds__(kCountScanTiles * kWave) void ex_count_scan_kernel(ExpertArgs a)
+{
+    __shared__ int32_t s_cnt[kCountScanTiles];
+    __shared__ int32_t s_start[kMaxRanks];  // row where source s starts; R: none
+    __shared__ int32_t s_pre[kMaxRanks];    // the list's rows before it in its tile
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = uniform(threadIdx.x / kWave);
+    const int64_t g = blockIdx.x;
+    const int d = (int)(g / a.Er);
+    const int64_t e = g;  // the global id of the list's expert: d * Er + j
+    const int R = received(a.recv[d], a.rows);
+    if (a.T > kCountScanTiles)
+        return;  // not launched for such calls
+    if (wave == 0 && lane < a.W) {
+        s_start[lane] = R;
+        s_pre[lane] = 0;
+    }
+    __syncthreads();
+    const int64_t row0 = (int64_t)d * a.WM;
+    constexpr int KC = id_chunk<KB>();
+    for (int t = wave; t < a.T; t += kCountScanTiles) {
+        const int q = t * kWave + lane;
+        const bool valid = q < R;
+        int c = 0;
+        if (t * kWave < R) {  // uniform
+            const int32_t* ids = a.idx + (row0 + (valid ? q : 0)) * a.k;
+            bool names = false;
+            for (int c0 = 0; c0 * KC < a.k; ++c0) {
+                int32_t id[KC];
+                load_ids<KC>(ids, a.k, c0, id);
+#pragma unroll
+                for (int i = 0; i < KC; ++i)
+                    names = names || (c0 * KC + i < a.k && id[i] == e);
+            }
+            const uint64_t b = __ballot(valid && names);
+            c = __popcll(b);
+            // rows are in source-rank order: the row that starts sources
+            // (s_prev, s_cur] records itself and its in-tile prefix
+            const int s_cur = valid ? source_rank(a, row0 + q) : a.W;
+            int s_prev = __shfl_up(s_cur, 1);
+            if (lane == 0)
+                s_prev = q > 0 ? source_rank(a, row0 + q - 1) : -1;
+            if (valid && s_prev < s_cur) {
+                const int pre = lanes_below(b);
+                for (int s = s_prev + 1; s <= s_cur; ++s) {
+                    s_start[s] = q;
+                    s_pre[s] = pre;
+                }
+            }
+        }
+        if (lane == 0)
+            s_cnt[t] = c;
+    }
+    __syncthreads();
+    if (wave == 0)
+        scan_list(a, g, R, [&](int t) { return s_cnt[t]; }, [&](int s, int& row, int& pre) {
+            row = s_start[s];
+            pre = s_pre[s];
+        });
 }
 
 template <int VPL, int KB, bool kStream>
@@ -432,6 +512,17 @@ hipError_t launch_expert_count(const ExpertArgs& a, hipStream_t s)
     case 16: hipLaunchKernelGGL((ex_count_kernel<16>), grid, block, 0, s, a); break;
     case 32: hipLaunchKernelGGL((ex_count_kernel<32>), grid, block, 0, s, a); break;
     default: hipLaunchKernelGGL((ex_count_kernel<64>), grid, block, 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_expert_count_scan(const ExpertArgs& a, hipStream_t s)
+{
+    const dim3 grid((unsigned)((int64_t)a.W * a.Er));
+    const dim3 block(kCountScanTiles * kWave);
+    switch (ex_bucket(a.k)) {
+    case 8: hipLaunchKernelGGL((ex_count_scan_kernel<8>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((ex_count_scan_kernel<16>), grid, block, 0, s, a); break;
     }
     return hipGetLastError();
 }

@@ -221,6 +221,14 @@ hipError_t launch_combine(const CombineArgs& a, const TokenMap& tk, int dtype, i
                           int row_split, bool stream, hipStream_t s);
 
 hipError_t launch_expert_count(const ExpertArgs& a, hipStream_t s);
+// Small calls count and scan in one launch, a tile a wave, and the count
+// launch is not made: at most kCountScanTiles tiles (a rank's for the
+// expert-major layout, (source rank, tile) pairs for the fused dispatch) and
+// top-k at most kCountScanTopK. Every block of it reads the call's ids, which
+// measured slower than two launches at 64 tiles of top-64 tokens.
+constexpr int kCountScanTiles = 16;
+constexpr int kCountScanTopK = 16;
+hipError_t launch_expert_count_scan(const ExpertArgs& a, hipStream_t s);
 hipError_t launch_expert_scan(const ExpertArgs& a, hipStream_t s);
 hipError_t launch_expert_copy(const ExpertArgs& a, int waves, int row_split, bool stream,
                               hipStream_t s);
@@ -228,12 +236,6 @@ hipError_t launch_expert_combine(const ExpertCombineArgs& a, int W, int dtype, i
                                  int row_split, bool stream, hipStream_t s);
 
 hipError_t launch_standard_count(const StandardArgs& a, hipStream_t s);
-// Calls of at most kCountScanTiles (source rank, tile) pairs and top-k at
-// most kCountScanTopK: count and scan in one launch, a tile a wave (the count
-// launch is not made). Every block of it reads all the call's ids, which
-// measured slower than two launches at 64 tiles of top-64 tokens.
-constexpr int kCountScanTiles = 16;
-constexpr int kCountScanTopK = 16;
 hipError_t launch_standard_count_scan(const StandardArgs& a, hipStream_t s);
 hipError_t launch_standard_scan(const StandardArgs& a, hipStream_t s);
 hipError_t launch_standard_copy(const StandardArgs& a, int waves, int row_split, bool stream,

@@ -1102,11 +1102,20 @@ int ep_convert_dispatch_output(ep_expert_plan_t* x, const ep_convert_dispatch_ar
     ea.T = expert_tiles(rows);
     const int row_split = (ea.row_vecs + ea.piece_vecs - 1) / ea.piece_vecs;
 
-    hipError_t e =
-        timed(p, EP_KERNEL_EXPERT_COUNT, stream, [&] { return ep::launch_expert_count(ea, stream); });
-    if (e == hipSuccess)
+    // small calls count and scan in one launch (timed as the scan)
+    const bool one = ea.T <= ep::kCountScanTiles && s.k <= ep::kCountScanTopK &&
+                     p->launch.layout != EP_LAYOUT_KERNELS;
+    hipError_t e = hipSuccess;
+    if (one) {
         e = timed(p, EP_KERNEL_EXPERT_SCAN, stream,
-                  [&] { return ep::launch_expert_scan(ea, stream); });
+                  [&] { return ep::launch_expert_count_scan(ea, stream); });
+    } else {
+        e = timed(p, EP_KERNEL_EXPERT_COUNT, stream,
+                  [&] { return ep::launch_expert_count(ea, stream); });
+        if (e == hipSuccess)
+            e = timed(p, EP_KERNEL_EXPERT_SCAN, stream,
+                      [&] { return ep::launch_expert_scan(ea, stream); });
+    }
     if (e == hipSuccess)
         e = timed(p, EP_KERNEL_EXPERT_COPY, stream, [&] {
             return ep::launch_expert_copy(ea, l.expert_waves, row_split,

@@ -296,11 +296,13 @@ const char *ep_last_error(void);
  *                        Automatic: EP_LAYOUT_IN_COPY up to 256 tokens when
  *                        it fits, else EP_LAYOUT_SCAN_IN_COPY up to 256 tiles,
  *                        else EP_LAYOUT_KERNELS.
+ *                        ep_convert_dispatch_output and
  *                        ep_dispatch_standard_moe: EP_LAYOUT_KERNELS makes
- *                        its count and scan two kernels; otherwise a call of
- *                        at most 16 (source rank, 64-token tile) pairs with
- *                        top-k <= 16 counts and scans in one kernel, any
- *                        other in two.
+ *                        their count and scan two kernels; otherwise a call
+ *                        of at most 16 tiles of 64 rows (a rank's received
+ *                        rows, resp. (source rank, tile) pairs) with top-k
+ *                        <= 16 counts and scans in one kernel, any other in
+ *                        two.
  * Geometry, cache policy and layout placement never change results. */
 enum {
     EP_LAYOUT_AUTO = 0,

@@ -208,6 +208,8 @@ def test_world_expert_topk_sweep(W, E, k):
     dict(expert_token_split=3),
     dict(expert_token_split=5, expert_waves=2, expert_row_split=1),
     dict(expert_token_split=64, expert_waves=1),
+    # count and scan as two kernels (this call's tiles otherwise take one)
+    dict(layout=cra.EP_LAYOUT_KERNELS),
 ])
 def test_geometry_does_not_change_results(launch):
     wl = workloads.custom("ex_geom_ep4_t200_h1024", 4, 200, 1024, 8, 64, "bf16", ragged=True,
@@ -388,10 +390,16 @@ def test_graph_replay_matches_oracle():
     op.close()
 
 
-def test_kernel_timing_counts_expert_launches():
+@pytest.mark.parametrize("two_kernels", [False, True])
+def test_kernel_timing_counts_expert_launches(two_kernels):
+    """Each conversion and inverse is timed per kernel; this small call counts
+    and scans in one launch (timed as the scan) unless EP_LAYOUT_KERNELS asks
+    for two."""
     wl = workloads.custom("ex_time_ep2_t64_h256", 2, 64, 256, 4, 8, "bf16", seed_index=526)
     inp = workloads.make_inputs(wl)
     op = cra.EpDispatchCombineOp(config_of(wl), expert_capacity=64)
+    if two_kernels:
+        op.set_launch(dict(layout=cra.EP_LAYOUT_KERNELS))
     cra.ep_plan_set_timing(op.plan, True)
     for _ in range(3):
         gpu_dispatch(op, inp)
@@ -401,7 +409,8 @@ def test_kernel_timing_counts_expert_launches():
     for kern in (cra.EP_KERNEL_EXPERT_COUNT, cra.EP_KERNEL_EXPERT_SCAN, cra.EP_KERNEL_EXPERT_COPY,
                  cra.EP_KERNEL_EXPERT_COMBINE):
         n, ms = cra.ep_plan_kernel_time(op.plan, kern)
-        assert n == 3 and ms > 0, (kern, n, ms)
+        want = 0 if kern == cra.EP_KERNEL_EXPERT_COUNT and not two_kernels else 3
+        assert n == want and (ms > 0) == (want > 0), (kern, n, ms)
     cra.ep_plan_set_timing(op.plan, False)
     op.close()
 
