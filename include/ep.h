@@ -368,9 +368,11 @@ int ep_plan_get_launch(const ep_plan_t *plan, const int32_t *num_tokens, ep_laun
  * (expert lists and layout ranges), EP_KERNEL_EXPERT_COPY (rows into the
  * expert-major layout), EP_KERNEL_EXPERT_COMBINE (the inverse), and the
  * fused path's EP_KERNEL_STANDARD_COUNT, _SCAN, _COPY (ep_dispatch_standard_moe)
- * and EP_KERNEL_STANDARD_COMBINE (ep_combine_standard_moe). Enabling creates
- * the events (no device memory); disabling destroys them. Not for use under
- * graph capture. */
+ * and EP_KERNEL_STANDARD_COMBINE (ep_combine_standard_moe). A kernel a call
+ * does not launch counts nothing: the route and scan kernels of small calls
+ * (launch.layout), and the expert and fused count kernels of calls that count
+ * and scan in one launch (timed as the scan). Enabling creates the events (no
+ * device memory); disabling destroys them. Not for use under graph capture. */
 enum {
     EP_KERNEL_ROUTE = 0,
     EP_KERNEL_SCAN = 1,
