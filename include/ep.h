@@ -238,8 +238,10 @@ int ep_combine(ep_plan_t *plan, const ep_combine_args_t *args, void *stream);
  * scales. FP8: s = amax / 448 and codes E4M3(v * (448 / amax)), round to
  * nearest even, saturating (s = 1 for an all-zero block). MXFP4 (the OCP MX
  * conversion): scale 2^(floor(log2 amax) - 2), codes E2M1(v / scale), round
- * to nearest even, saturating at 6 (scale code 0 for an all-zero block);
- * inputs finite. Device pointers: in and out 16-byte aligned, scales 4-byte
+ * to nearest even, saturating at 6 (scale code 0 for an all-zero block).
+ * Both wires need finite inputs: a block holding a NaN or an infinity gets
+ * unspecified codes and scale (nothing outside the block is affected).
+ * Device pointers: in and out 16-byte aligned, scales 4-byte
  * aligned; no plan, no allocation, asynchronous on stream, capturable.
  * row_counts: NULL converts every row. Otherwise the rows form groups of
  * group_rows consecutive rows (rows a multiple of group_rows), row_counts is a
