@@ -13,6 +13,7 @@ the first call raises.
 """
 import ctypes
 import os
+import weakref
 from typing import Optional, Sequence
 
 import torch
@@ -294,14 +295,22 @@ def _same_tensors(held, given):
     """The very same tensor objects as before, still over the same memory."""
     if len(held) != len(given):
         return False
-    for (h, ptr), g in zip(held, given):
-        if h is not g or (g is not None and g.data_ptr() != ptr):
+    for h, g in zip(held, given):
+        if h is None or g is None:
+            if h is not g:
+                return False
+            continue
+        ref, ptr = h
+        if ref() is not g or g.data_ptr() != ptr:
             return False
     return True
 
 
 def _hold(tensors):
-    return tuple((t, None if t is None else t.data_ptr()) for t in tensors)
+    """Weak references to the tensors a cached argument struct was built from,
+    with their addresses: the cache keeps none of the caller's tensors alive,
+    and a tensor that is gone can only miss."""
+    return tuple(None if t is None else (weakref.ref(t), t.data_ptr()) for t in tensors)
 
 
 def ep_quantize_rows(rows: torch.Tensor, wire, out: torch.Tensor, scales: torch.Tensor,

@@ -623,3 +623,23 @@ def test_dispatch_cast_layout_and_sizes(lib):
     with pytest.raises(cra.EpError):
         cra.ep_plan_set_launch(plan, dict(dispatch_row_split=7168 * 2 // 16 + 1))
     lib.ep_plan_destroy(plan)
+
+
+def test_argument_cache_keeps_no_tensor_alive():
+    """The binding's argument cache holds weak references: a cached tensor
+    the caller drops is freed, and a later call with a new tensor misses."""
+    import gc
+    import weakref
+
+    import torch
+
+    a, b = torch.zeros(8), torch.zeros(8)
+    held = cra._hold((a, None, b))
+    assert cra._same_tensors(held, (a, None, b))
+    assert not cra._same_tensors(held, (b, None, a))
+    assert not cra._same_tensors(held, (a, b, None))
+    alive = weakref.ref(a)
+    del a
+    gc.collect()
+    assert alive() is None
+    assert not cra._same_tensors(held, (torch.zeros(8), None, b))
