@@ -583,11 +583,22 @@ def summarize_stats(csv_path, out_md, command):
            "Command (from the repository root):", "", "    " + command, "",
            "| kernel | calls | average us | min us | max us | share |",
            "|---|---|---|---|---|---|"]
+    # the library's kernels one a line; the bench's own torch and runtime
+    # kernels (input fills, random numbers, copies) summed in one line
+    other_calls, other_ns, other_pct = 0, 0.0, 0.0
     for r in rows:
         name = r["Name"].replace("(anonymous namespace)::", "")
+        if "ep::" not in name:
+            other_calls += int(r["Calls"])
+            other_ns += float(r["TotalDurationNs"])
+            other_pct += float(r["Percentage"])
+            continue
         out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                    f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                    f"{float(r['Percentage']):.2f}% |")
+    if other_calls:
+        out.append(f"| other kernels (torch and runtime: fills, random inputs, copies) | "
+                   f"{other_calls} | {other_ns / other_calls / 1e3:.1f} | | | {other_pct:.2f}% |")
     with open(out_md, "w") as f:
         f.write("\n".join(out) + "\n")
     print("\n".join(out))
