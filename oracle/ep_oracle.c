@@ -322,6 +322,32 @@ int oracle_combine(int W, int M, int k, int H, int dtype, const int32_t *ntok,
     return 0;
 }
 
+/* Place of rank d in a token's distinct-rank order, found without building
+ * the list: the id row's first expert on d sits at some slot; every rank whose
+ * first expert comes before that slot takes an earlier place. -1 if none of
+ * the token's ids is on d. */
+static int rank_place(const int32_t *idx_row, int k, int Er, int W, int d)
+{
+    const int64_t E = (int64_t)W * Er;
+    int first = -1;
+    for (int j = 0; j < k && first < 0; ++j)
+        if (idx_row[j] >= 0 && idx_row[j] < E && idx_row[j] / Er == d)
+            first = j;
+    if (first < 0)
+        return -1;
+    int place = 0;
+    for (int j = 0; j < first; ++j) {
+        if (idx_row[j] < 0 || idx_row[j] >= E)
+            continue;
+        int dj = idx_row[j] / Er, seen_before = 0;
+        for (int q = 0; q < j; ++q)
+            if (idx_row[q] >= 0 && idx_row[q] < E && idx_row[q] / Er == dj)
+                seen_before = 1;
+        place += !seen_before;     /* slot j holds the first expert of rank dj */
+    }
+    return place;
+}
+
 int oracle_combine_push(int W, int M, int k, int Er, int H, int dtype,
                         const int32_t *ntok, const int32_t *idx,
                         const int32_t *recv, const int32_t *src_pos,
@@ -330,41 +356,75 @@ int oracle_combine_push(int W, int M, int k, int Er, int H, int dtype,
 {
     const int64_t WM = (int64_t)W * M;
     const int P = W < k ? W : k;
-    int64_t *slots = malloc(sizeof(int64_t) * (size_t)(WM * P));
-    int32_t ranks[64];
-    if (!slots)
-        return -1;
-    for (int64_t q = 0; q < WM * P; ++q)
-        slots[q] = -1;
-    /* Every received row goes back to its source token, at the place its
-     * rank holds in that token's distinct-rank order. */
-    for (int d = 0; d < W; ++d)
-        for (int32_t s = 0; s < recv[d]; ++s) {
-            int64_t row = (int64_t)d * WM + s;
-            int32_t p = src_pos[row];
-            int r = (int)(p / WM), t = (int)(p % WM);
-            int nd = token_ranks(idx + ((int64_t)r * M + t) * k, k, Er, W, ranks);
-            for (int i = 0; i < nd; ++i)
-                if (ranks[i] == d)
-                    slots[((int64_t)r * M + t) * P + i] = row;
-        }
-    int64_t rows[64];
+    float *acc = malloc(sizeof(float) * (size_t)(WM * H + 1));
+    float *accw = malloc(sizeof(float) * (size_t)(WM * k + 1));
+    int32_t *added = calloc((size_t)(WM + 1), sizeof(int32_t));
+    int rc = 0;
+    if (!acc || !accw || !added) {
+        rc = -1;
+        goto done;
+    }
+    /* Scatter-add: each received row is pushed back into its source token's
+     * FP32 accumulator. The rows of place 0 (the token's first rank) go first
+     * and start the accumulator with their value; the rows of place 1 are
+     * added next, and so on, so every token adds its contributions in its
+     * distinct-rank order ([PR712] Combine: sum in FP32, then convert). */
+    for (int place = 0; place < P; ++place)
+        for (int d = 0; d < W; ++d)
+            for (int32_t s = 0; s < recv[d]; ++s) {
+                int64_t row = (int64_t)d * WM + s;
+                int64_t p = src_pos[row];
+                int64_t tok = (p / WM) * M + p % WM;
+                if (rank_place(idx + tok * k, k, Er, W, d) != place)
+                    continue;
+                if (added[tok] != place) {  /* a place skipped or sent twice */
+                    rc = -2;
+                    goto done;
+                }
+                float *a = acc + tok * H;
+                const uint16_t *v = y + row * H;
+                for (int h = 0; h < H; ++h) {
+                    float f = dtype == 0 ? oracle_bf16_to_f32(v[h]) : oracle_f16_to_f32(v[h]);
+                    a[h] = place == 0 ? f : a[h] + f;
+                }
+                if (y_w) {
+                    float *aw = accw + tok * k;
+                    for (int j = 0; j < k; ++j)
+                        aw[j] = place == 0 ? y_w[row * k + j] : aw[j] + y_w[row * k + j];
+                }
+                added[tok] += 1;
+            }
+    /* Every token must have received one row from each of its ranks; a token
+     * with none sums to +0. The FP32 sum is rounded once to the output type. */
     for (int r = 0; r < W; ++r)
         for (int t = 0; t < ntok[r]; ++t) {
             int64_t tok = (int64_t)r * M + t;
-            int nd = token_ranks(idx + tok * k, k, Er, W, ranks);
-            for (int i = 0; i < nd; ++i) {
-                rows[i] = slots[tok * P + i];
-                if (rows[i] < 0) {      /* a (token, rank) pair never received */
-                    free(slots);
-                    return -2;
-                }
+            uint64_t ranks = 0;
+            for (int j = 0; j < k; ++j) {
+                int32_t e = idx[tok * k + j];
+                if (e >= 0 && e < (int64_t)W * Er)
+                    ranks |= 1ull << (e / Er);
             }
-            fold_token(nd, rows, H, k, dtype, y, y_w, out + (size_t)tok * H,
-                       out_w ? out_w + (size_t)tok * k : NULL);
+            int nd = 0;
+            for (int d = 0; d < W; ++d)
+                nd += (int)((ranks >> d) & 1u);
+            if (added[tok] != nd) {
+                rc = -2;
+                goto done;
+            }
+            for (int h = 0; h < H; ++h)
+                out[tok * H + h] = nd == 0 ? 0
+                    : (dtype == 0 ? oracle_f32_to_bf16(acc[tok * H + h])
+                                  : oracle_f32_to_f16(acc[tok * H + h]));
+            if (y_w && out_w)
+                for (int j = 0; j < k; ++j)
+                    out_w[tok * k + j] = nd == 0 ? 0.0f : accw[tok * k + j];
         }
-    free(slots);
-    return 0;
+done:
+    free(acc);
+    free(accw);
+    free(added);
+    return rc;
 }
 
 /* ------------------------------------------------------------------------ */

@@ -94,10 +94,15 @@ int oracle_combine(int W, int M, int k, int H, int dtype, const int32_t *ntok,
                    const int32_t *fwd, const uint16_t *y, const float *y_w,
                    uint16_t *out, float *out_w);
 
-/* Combine, second formulation (push form): walk the received rows, route each
- * back to its source through src_pos, place it at the position its rank takes
- * in the token's distinct-rank order, then fold every token in that order.
- * Needs idx to know each token's rank order. Same outputs as oracle_combine. */
+/* Combine, second formulation (scatter-add, the push-back of [PR712]
+ * Combine): every received row is added into its source token's FP32
+ * accumulator, found through src_pos. Rows are pushed in passes by the place
+ * their rank takes in the token's distinct-rank order (that place computed
+ * from the id row on its own, not from a rank list), the first place seeding
+ * the accumulator. Shares no accumulation code with oracle_combine, so the
+ * two are independent formulations of one result. Needs idx for the places.
+ * Returns 0, -1 if memory runs out, -2 if a token's rows are not exactly one
+ * per distinct rank. W <= 64. */
 int oracle_combine_push(int W, int M, int k, int Er, int H, int dtype,
                         const int32_t *ntok, const int32_t *idx,
                         const int32_t *recv, const int32_t *src_pos,

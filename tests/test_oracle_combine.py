@@ -9,8 +9,13 @@ Pins, none of which calls the oracle through itself:
 * closed form of the identity round trip: with identity experts a token comes
   back as RNE(n * v), n = its number of distinct ranks (n * v is exact in
   FP32 for n <= 64), the cast done by torch / numpy, not by the oracle;
-* the push formulation (walk received rows through src_pos) equals the gather
-  formulation bit for bit, on random expert outputs;
+* the push formulation (a scatter-add: every received row is added into its
+  source token's accumulator through src_pos, with its own accumulation loop
+  and its own way of finding a rank's place) equals the gather formulation
+  bit for bit, on random expert outputs;
+* hand-derived order and seed cases for the payload and for the weights:
+  (2^24, 1, -2^24) in the token's rank order sums to 0 and in any other order
+  to 1; all -0.0 stays -0.0 only when the sum starts from the first term;
 * the relaxed-order bound: |out - exact sum| <= 1 ulp of the output type,
   exact sum in float64;
 * weights: n * w exactly for weights with few significant bits;
@@ -188,3 +193,85 @@ def test_sum_is_seeded_with_first_contribution():
     y = np.full((W, W * M, H), 0x8000, np.uint16)
     out, _ = oracle.combine(W, M, k, H, oracle.BF16, [1, 1], disp["fwd"], y)
     assert np.all(out == 0x8000)
+
+
+def _order_case():
+    """A token of rank 0 whose experts sit on ranks [2, 0, 1] in top-k order
+    (Er = 1, so expert e is on rank e); the other ranks send nothing."""
+    W, M, k, Er, H = 3, 1, 3, 1, 8
+    idx = np.array([[[2, 0, 1]], [[0, 0, 0]], [[0, 0, 0]]], np.int32)
+    ntok = [1, 0, 0]
+    disp = oracle.dispatch(W, M, k, Er, ntok, np.zeros((W, M, 2 * H), np.uint8), idx)
+    return W, M, k, Er, H, idx, ntok, disp
+
+
+@pytest.mark.parametrize("form", ["gather", "push"])
+def test_weight_sum_order_is_token_rank_order(form):
+    """Hand-derived weight fold: the rows received on ranks 2, 0, 1 carry
+    weight rows 2^24, 1, -2^24. In the token's rank order (2, 0, 1) the FP32
+    sum is (2^24 + 1) - 2^24 = 0, because 2^24 + 1 ties to the even 2^24.
+    Ascending ranks (0, 1, 2) give (1 - 2^24) + 2^24 = 1 (1 - 2^24 is exact),
+    and the reversed order (1, 0, 2) gives the same 1. A weight that is not
+    summed at all, or summed twice, leaves 2^24 or -2^24 in some slot."""
+    W, M, k, Er, H, idx, ntok, disp = _order_case()
+    y = np.zeros((W, W * M, H), np.uint16)
+    yw = np.zeros((W, W * M, k), np.float32)
+    yw[2, 0] = [2.0 ** 24, 3.0, -0.5]
+    yw[0, 0] = [1.0, 5.0, 0.25]
+    yw[1, 0] = [-(2.0 ** 24), 7.0, 0.125]
+    if form == "gather":
+        _, out_w = oracle.combine(W, M, k, H, oracle.BF16, ntok, disp["fwd"], y, yw)
+    else:
+        _, out_w = oracle.combine_push(W, M, k, Er, H, oracle.BF16, ntok, idx, disp["recv"],
+                                       disp["src_pos"], y, yw)
+    # slot 1: 3 + 5 + 7 = 15; slot 2: -0.5 + 0.25 + 0.125 = -0.125 (exact)
+    assert out_w[0, 0].tolist() == [0.0, 15.0, -0.125]
+
+
+@pytest.mark.parametrize("form", ["gather", "push"])
+def test_weight_sum_is_seeded_with_first_term(form):
+    """All weights -0.0: a sum that starts from the first term stays -0.0
+    (-0 + -0 = -0); one started at +0.0 gives +0.0."""
+    W, M, k, Er, H, idx, ntok, disp = _order_case()
+    y = np.zeros((W, W * M, H), np.uint16)
+    yw = np.full((W, W * M, k), -0.0, np.float32)
+    if form == "gather":
+        _, out_w = oracle.combine(W, M, k, H, oracle.BF16, ntok, disp["fwd"], y, yw)
+    else:
+        _, out_w = oracle.combine_push(W, M, k, Er, H, oracle.BF16, ntok, idx, disp["recv"],
+                                       disp["src_pos"], y, yw)
+    assert np.all(out_w[0, 0].view(np.uint32) == 0x80000000)
+
+
+@pytest.mark.parametrize("dtype,big,small,want", [
+    ("bf16", 0x4B80, 0x3F80, 0x0000),
+    ("fp16", 0x6400, 0x0400, 0x0000),
+])
+def test_push_summation_order_and_seed(dtype, big, small, want):
+    """The push form on the hand-derived payload cases of the gather form:
+    +big, +small, -big on ranks 2, 0, 1 in rank order gives +0; all -0.0
+    stays -0.0."""
+    W, M, k, Er, H, idx, ntok, disp = _order_case()
+    dt = oracle.BF16 if dtype == "bf16" else oracle.FP16
+    y = np.zeros((W, W * M, H), np.uint16)
+    y[2, 0], y[0, 0], y[1, 0] = big, small, big | 0x8000
+    out, _ = oracle.combine_push(W, M, k, Er, H, dt, ntok, idx, disp["recv"], disp["src_pos"], y)
+    assert np.all(out[0, 0] == want)
+    y[:] = 0x8000
+    out, _ = oracle.combine_push(W, M, k, Er, H, dt, ntok, idx, disp["recv"], disp["src_pos"], y)
+    assert np.all(out[0, 0] == 0x8000)
+
+
+def test_push_rejects_a_missing_row():
+    """The scatter-add checks that every token got one row per distinct rank:
+    a reverse map that sends a token's row twice (and so drops another)
+    fails instead of summing the wrong rows."""
+    wl = workloads.custom("ep3_t8_h64_bf16_k3", 3, 8, 64, 3, 9, "bf16")
+    inp, disp = _dispatch(wl)
+    y, yw = _random_y(wl, 2)
+    sp = disp["src_pos"].copy()
+    d = int(np.argmax(disp["recv"] >= 2))
+    sp[d, 1] = sp[d, 0]
+    with pytest.raises(RuntimeError):
+        oracle.combine_push(3, 8, 3, 3, 64, oracle.BF16, inp["ntok"], inp["idx"].numpy(),
+                            disp["recv"], sp, y, yw)

@@ -15,7 +15,10 @@ Pins, none of which calls the oracle through itself:
   saturation / NaN handling by hand beyond;
 * E2M1 values equal the specification's list, and hand-derived ties;
 * FP8 block-128: scale within one ulp of amax / 448, the largest element at
-  the largest code, every element within half a step of the code grid;
+  the largest code, every element within half a step of the code grid; and
+  bit for bit, computed in torch from the reading's arithmetic: scale =
+  fl32(amax / 448), code = E4M3(fl32(v * fl32(448 / amax))) by torch's
+  float8_e4m3fn conversion (round to nearest even);
 * MXFP4: the block's largest magnitude lands in [4, 8) after scaling, every
   element within half a step of the E2M1 grid or saturated;
 * combine from wire rows equals the plain combine of the dequantized rows
@@ -95,6 +98,48 @@ def test_fp8_block128_scale_codes_and_error_bound():
     scaled = vd * (448 / amax)[..., None]
     err = np.abs(dec - scaled)
     assert np.all(err <= _e4m3_step(np.abs(scaled)) / 2 * (1 + 1e-6) + np.abs(scaled) * 2e-7)
+
+
+def _fp8_block128_torch(v):
+    """The FP8 block-128 wire computed in torch, independently of the oracle:
+    per block of 128, amax = max |v| in FP32, scale = fl32(amax / 448) and
+    r = fl32(448 / amax) (both 1 for an all-zero block), code = E4M3 of the
+    FP32 product v * r. Returns (codes uint8 [n, H], scales float32 [n, H/128])."""
+    n, H = v.shape
+    b = v.float().reshape(n, H // 128, 128)
+    amax = b.abs().amax(-1, keepdim=True)
+    zero = amax == 0
+    f448 = torch.tensor(448.0, dtype=torch.float32)
+    s = torch.where(zero, torch.ones_like(amax), amax / f448)
+    r = torch.where(zero, torch.ones_like(amax), f448 / amax.clamp(min=torch.finfo(torch.float32).tiny))
+    q = (b * r).to(E4M3).view(torch.uint8).reshape(n, H)
+    return q.numpy(), s.reshape(n, H // 128).numpy()
+
+
+@pytest.mark.parametrize("dtype,seed,spread", [(torch.bfloat16, 21, 3.0),
+                                               (torch.bfloat16, 22, 8.0),
+                                               (torch.float16, 23, 1.5)])
+def test_fp8_block128_bit_exact_against_torch(dtype, seed, spread):
+    """Codes and scales bit for bit. The blocks mix binades (a factor up to
+    e^(3 spread) between 32-element groups), so scaled values fall on E4M3
+    normals, subnormals and zero; some blocks are all zero, some hold -0.0,
+    and one holds a single nonzero element. A quantizer that divides by the
+    scale instead of multiplying by fl32(448 / amax), or that rounds the scale
+    differently, changes codes here."""
+    v, _ = _rows(seed, 64, 1024, dtype=dtype, spread=spread)
+    v = v.clone()
+    v[0, :128] = 0.0
+    v[1, 128:256] = -0.0
+    v[2, 256:384] = 0.0
+    v[2, 300] = 3.0
+    v[3, 384:512] *= 2.0 ** -20 if dtype == torch.bfloat16 else 1.0
+    words = v.view(torch.int16).numpy().view(np.uint16)
+    dt = oracle.BF16 if dtype == torch.bfloat16 else oracle.FP16
+    codes, scales = oracle.quantize_rows(words, dt, oracle.WIRE_FP8_BLOCK128)
+    want_codes, want_scales = _fp8_block128_torch(v)
+    assert np.array_equal(scales.view(np.uint32), want_scales.view(np.uint32))
+    assert np.array_equal(codes, want_codes)
+    assert np.all(codes[1, 128:256] == 0x80)          # -0.0 keeps its sign
 
 
 def test_fp8_block128_all_zero_block():
