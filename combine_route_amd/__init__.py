@@ -182,12 +182,36 @@ def ep_workspace_bytes(cfg: EpConfig) -> int:
     return n
 
 
-def _dev(t: Optional[torch.Tensor], name: str, nbytes: int):
-    """Address of a contiguous device tensor of at least nbytes, or None."""
+_I32 = (torch.int32,)
+_F32 = (torch.float32,)
+
+
+def _payload(dtype_code):
+    """Element types accepted for rows of an EP_* type: the type itself, or
+    raw bytes (uint8) holding its encodings."""
+    return (_TORCH[dtype_code], torch.uint8)
+
+
+def _scale_types(elem_bytes):
+    """Scale rows are copied as bytes: uint8, or any type of the config's
+    scale element size."""
+    return (torch.uint8,) + tuple(t for t in (torch.float32, torch.int32, torch.float16,
+                                              torch.bfloat16, torch.int16, torch.float64,
+                                              torch.int64, torch.int8)
+                                  if torch.empty((), dtype=t).element_size() == elem_bytes)
+
+
+def _dev(t: Optional[torch.Tensor], name: str, nbytes: int, dtypes=None):
+    """Address of a contiguous device tensor of at least nbytes whose element
+    type is one of dtypes (any when None), or None. The type is checked first:
+    an int64 id tensor has enough bytes for the int32 ids it is mistaken for,
+    and would be misread without an error."""
     if t is None:
         return None
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} must be {' or '.join(str(d) for d in dtypes)}, not {t.dtype}")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on the GPU, not {t.device}")
     if not t.is_contiguous():
@@ -243,14 +267,17 @@ def _dispatch_args(cfg: EpConfig, num_tokens: Sequence[int], x, indices, weights
     if len(num_tokens) != W:
         raise ValueError(f"num_tokens has {len(num_tokens)} entries; world_size is {W}")
     nt = (ctypes.c_int32 * W)(*[int(v) for v in num_tokens])
+    xt = _payload(cfg.dispatch_cast - 1) if cfg.dispatch_cast else _payload(cfg.dispatch_dtype)
+    st = _scale_types(cfg.scale_type_size)
     a = EpDispatchArgs(
         ctypes.cast(nt, ctypes.c_void_p),
-        _dev(x, "x", W * M * xrow), _dev(indices, "indices", W * M * k * 4),
-        _dev(weights, "weights", W * M * k * 4), _dev(scales, "scales", W * M * srow),
-        _dev(out_x, "out_x", W * WM * row), _dev(out_indices, "out_indices", W * WM * k * 4),
-        _dev(out_weights, "out_weights", W * WM * k * 4),
-        _dev(out_scales, "out_scales", W * WM * srow),
-        _dev(recv_num_token, "recv_num_token", W * 4))
+        _dev(x, "x", W * M * xrow, xt), _dev(indices, "indices", W * M * k * 4, _I32),
+        _dev(weights, "weights", W * M * k * 4, _F32), _dev(scales, "scales", W * M * srow, st),
+        _dev(out_x, "out_x", W * WM * row, _payload(cfg.dispatch_dtype)),
+        _dev(out_indices, "out_indices", W * WM * k * 4, _I32),
+        _dev(out_weights, "out_weights", W * WM * k * 4, _F32),
+        _dev(out_scales, "out_scales", W * WM * srow, st),
+        _dev(recv_num_token, "recv_num_token", W * 4, _I32))
     return a, nt
 
 
@@ -265,14 +292,25 @@ def wire_row_bytes(cfg: EpConfig):
     return H * 2, 0
 
 
+def wire_types(cfg: EpConfig):
+    """(element types accepted for combine input rows, for their scales)."""
+    if cfg.combine_wire == EP_WIRE_FP8_BLOCK128:
+        return (torch.uint8, torch.float8_e4m3fn), (torch.float32, torch.uint8)
+    if cfg.combine_wire == EP_WIRE_MXFP4:
+        return (torch.uint8,), (torch.uint8,)
+    return _payload(cfg.combine_dtype), None
+
+
 def _combine_args(cfg: EpConfig, y, y_weights, out, out_weights, y_scales=None):
     W, M, k, _, crow, _ = _sizes(cfg)
     WM = W * M
     yrow, srow = wire_row_bytes(cfg)
-    return EpCombineArgs(_dev(y, "y", W * WM * yrow), _dev(y_weights, "y_weights", W * WM * k * 4),
-                         _dev(out, "out", W * M * crow),
-                         _dev(out_weights, "out_weights", W * M * k * 4),
-                         _dev(y_scales, "y_scales", W * WM * srow))
+    yt, yst = wire_types(cfg)
+    return EpCombineArgs(_dev(y, "y", W * WM * yrow, yt),
+                         _dev(y_weights, "y_weights", W * WM * k * 4, _F32),
+                         _dev(out, "out", W * M * crow, _payload(cfg.combine_dtype)),
+                         _dev(out_weights, "out_weights", W * M * k * 4, _F32),
+                         _dev(y_scales, "y_scales", W * WM * srow, yst))
 
 
 def ep_dispatch(plan: int, cfg: EpConfig, num_tokens: Sequence[int], x, indices, weights,
@@ -292,7 +330,9 @@ def ep_combine(plan: int, cfg: EpConfig, y, y_weights, out, out_weights, stream=
 
 
 def _same_tensors(held, given):
-    """The very same tensor objects as before, still over the same memory."""
+    """The very same tensor objects as before, still over the same memory,
+    with the same size, element type and contiguity: a tensor changed in place
+    (resize_, set_, a transpose_) misses and is checked again."""
     if len(held) != len(given):
         return False
     for h, g in zip(held, given):
@@ -300,17 +340,19 @@ def _same_tensors(held, given):
             if h is not g:
                 return False
             continue
-        ref, ptr = h
-        if ref() is not g or g.data_ptr() != ptr:
+        ref, ptr, nbytes, dtype = h
+        if (ref() is not g or g.data_ptr() != ptr or g.nbytes != nbytes or g.dtype != dtype
+                or not g.is_contiguous()):
             return False
     return True
 
 
 def _hold(tensors):
     """Weak references to the tensors a cached argument struct was built from,
-    with their addresses: the cache keeps none of the caller's tensors alive,
-    and a tensor that is gone can only miss."""
-    return tuple(None if t is None else (weakref.ref(t), t.data_ptr()) for t in tensors)
+    with their addresses, sizes and element types: the cache keeps none of the
+    caller's tensors alive, and a tensor that is gone can only miss."""
+    return tuple(None if t is None else (weakref.ref(t), t.data_ptr(), t.nbytes, t.dtype)
+                 for t in tensors)
 
 
 def ep_quantize_rows(rows: torch.Tensor, wire, out: torch.Tensor, scales: torch.Tensor,
@@ -340,9 +382,11 @@ def ep_quantize_rows(rows: torch.Tensor, wire, out: torch.Tensor, scales: torch.
             raise ValueError(f"counts must be int32, not {counts.dtype}")
         group = n // rows.shape[0]
         cp = _dev(counts, "counts", rows.shape[0] * 4)
+    ot = (torch.uint8, torch.float8_e4m3fn) if w == EP_WIRE_FP8_BLOCK128 else (torch.uint8,)
+    stt = (torch.float32, torch.uint8) if w == EP_WIRE_FP8_BLOCK128 else (torch.uint8,)
     _check("ep_quantize_rows", load().ep_quantize_rows(
-        _dev(rows, "rows", n * H * 2), n, H, dt, w, _dev(out, "out", need_out),
-        _dev(scales, "scales", need_sc), cp, group, _stream(stream, rows.device.index)))
+        _dev(rows, "rows", n * H * 2), n, H, dt, w, _dev(out, "out", need_out, ot),
+        _dev(scales, "scales", need_sc, stt), cp, group, _stream(stream, rows.device.index)))
 
 
 def ep_get_src_token_pos(plan: int, rank: int) -> int:
@@ -407,22 +451,25 @@ def _convert_dispatch_args(cfg: EpConfig, cap: int, x, indices, weights, scales,
     W, M, k, row, _, srow = _sizes(cfg)
     WM = W * M
     Er = cfg.num_experts_per_rank
+    xt, st = _payload(cfg.dispatch_dtype), _scale_types(cfg.scale_type_size)
     return EpConvertDispatchArgs(
-        _dev(x, "x", W * WM * row), _dev(indices, "indices", W * WM * k * 4),
-        _dev(weights, "weights", W * WM * k * 4),
-        _dev(scales, "scales", W * WM * srow), _dev(recv_num_token, "recv_num_token", W * 4),
-        _dev(packed_x, "packed_x", W * Er * cap * row),
-        _dev(packed_scales, "packed_scales", W * Er * cap * srow),
-        _dev(packed_count, "packed_count", W * Er * 4),
-        _dev(packed_src_info, "packed_src_info", W * Er * cap * 4),
-        _dev(packed_layout_range, "packed_layout_range", W * Er * W * 8))
+        _dev(x, "x", W * WM * row, xt), _dev(indices, "indices", W * WM * k * 4, _I32),
+        _dev(weights, "weights", W * WM * k * 4, _F32),
+        _dev(scales, "scales", W * WM * srow, st),
+        _dev(recv_num_token, "recv_num_token", W * 4, _I32),
+        _dev(packed_x, "packed_x", W * Er * cap * row, xt),
+        _dev(packed_scales, "packed_scales", W * Er * cap * srow, st),
+        _dev(packed_count, "packed_count", W * Er * 4, _I32),
+        _dev(packed_src_info, "packed_src_info", W * Er * cap * 4, _I32),
+        _dev(packed_layout_range, "packed_layout_range", W * Er * W * 8, (torch.int64,)))
 
 
 def _convert_combine_args(cfg: EpConfig, cap: int, packed_y, y, apply_weights=False):
     W, M, _, _, crow, _ = _sizes(cfg)
     Er = cfg.num_experts_per_rank
-    return EpConvertCombineArgs(_dev(packed_y, "packed_y", W * Er * cap * crow),
-                                _dev(y, "y", W * W * M * crow), 1 if apply_weights else 0)
+    ct = _payload(cfg.combine_dtype)
+    return EpConvertCombineArgs(_dev(packed_y, "packed_y", W * Er * cap * crow, ct),
+                                _dev(y, "y", W * W * M * crow, ct), 1 if apply_weights else 0)
 
 
 def ep_convert_dispatch_output(eplan: int, cfg: EpConfig, cap: int, x, indices, weights,
@@ -452,13 +499,16 @@ def _dispatch_standard_args(cfg: EpConfig, cap: int, num_tokens: Sequence[int], 
     if len(num_tokens) != W:
         raise ValueError(f"num_tokens has {len(num_tokens)} entries; world_size is {W}")
     arr = (ctypes.c_int32 * W)(*[int(t) for t in num_tokens])
+    xt = _payload(cfg.dispatch_cast - 1) if cfg.dispatch_cast else _payload(cfg.dispatch_dtype)
+    st = _scale_types(cfg.scale_type_size)
     a = EpDispatchStandardArgs(
-        ctypes.addressof(arr), _dev(x, "x", W * M * xrow), _dev(indices, "indices", W * M * k * 4),
-        _dev(scales, "scales", W * M * srow), _dev(packed_x, "packed_x", W * Er * cap * row),
-        _dev(packed_scales, "packed_scales", W * Er * cap * srow),
-        _dev(packed_count, "packed_count", W * Er * 4),
-        _dev(packed_src_info, "packed_src_info", W * Er * cap * 4),
-        _dev(packed_layout_range, "packed_layout_range", W * Er * W * 8))
+        ctypes.addressof(arr), _dev(x, "x", W * M * xrow, xt),
+        _dev(indices, "indices", W * M * k * 4, _I32), _dev(scales, "scales", W * M * srow, st),
+        _dev(packed_x, "packed_x", W * Er * cap * row, _payload(cfg.dispatch_dtype)),
+        _dev(packed_scales, "packed_scales", W * Er * cap * srow, st),
+        _dev(packed_count, "packed_count", W * Er * 4, _I32),
+        _dev(packed_src_info, "packed_src_info", W * Er * cap * 4, _I32),
+        _dev(packed_layout_range, "packed_layout_range", W * Er * W * 8, (torch.int64,)))
     return a, arr
 
 
@@ -467,10 +517,13 @@ def _combine_standard_args(cfg: EpConfig, cap: int, packed_y, indices, weights, 
     W, M, k, _, crow, _ = _sizes(cfg)
     Er = cfg.num_experts_per_rank
     yrow, srow = wire_row_bytes(cfg) if cfg.combine_wire else (crow, 0)
+    yt, yst = wire_types(cfg)
     return EpCombineStandardArgs(
-        _dev(packed_y, "packed_y", W * Er * cap * yrow), _dev(indices, "indices", W * M * k * 4),
-        _dev(weights, "weights", W * M * k * 4), _dev(out, "out", W * M * crow),
-        _dev(packed_y_scales, "packed_y_scales", W * Er * cap * srow))
+        _dev(packed_y, "packed_y", W * Er * cap * yrow, yt),
+        _dev(indices, "indices", W * M * k * 4, _I32),
+        _dev(weights, "weights", W * M * k * 4, _F32),
+        _dev(out, "out", W * M * crow, _payload(cfg.combine_dtype)),
+        _dev(packed_y_scales, "packed_y_scales", W * Er * cap * srow, yst))
 
 
 def ep_dispatch_standard_moe(eplan: int, cfg: EpConfig, cap: int, num_tokens, x, indices, scales,
@@ -528,9 +581,11 @@ class EpDispatchCombineOp:
         self._src_pos_off = [ep_get_src_token_pos(self.plan, r) - self.workspace.data_ptr()
                              for r in range(W)]
         # Checked argument structs of the last call, reused while the same
-        # tensor objects (over the same memory) and token counts come back:
-        # the per-tensor checks cost more host time than a small call's GPU
-        # work. Holding the tensors keeps their memory alive meanwhile.
+        # tensor objects (over the same memory, same size and type) and token
+        # counts come back: the per-tensor checks cost more host time than a
+        # small call's GPU work. The cache holds weak references only, so it
+        # keeps none of the caller's tensors alive; a tensor that is gone, or
+        # changed in place, misses and is checked again.
         self._dcache = None
         self._ccache = None
         self._lib = load()

@@ -17,9 +17,12 @@ ARCH = "gfx950"
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-    # packed FP32 instructions stay off: the compiler would otherwise pair
-    # the combine's FP32 adds into v_pk_add_f32
-    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # packed FP32 instructions stay off in the gfx950 code: the compiler would
+    # otherwise pair the combine's FP32 adds into v_pk_add_f32. The feature
+    # exists only for the device target, so each word of the option goes to
+    # the device pass alone (-Xarch_device) and the host pass never sees it.
+    *[w for a in ("-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops")
+      for w in ("-Xarch_device", a)],
     "-fno-fast-math", "-ffp-contract=off",
     "-Wall", "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"),

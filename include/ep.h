@@ -451,7 +451,11 @@ int ep_expert_plan_destroy(ep_expert_plan_t *plan);
  *                        weights on the slots naming that expert (R), for a
  *                        weighted inverse.
  *   scales               [W][WM][S] (out_scales); NULL iff S == 0.
- *   recv_num_token       DEVICE int32 [W] (recv_num_token).
+ *   recv_num_token       DEVICE int32 [W] (recv_num_token). The expert plan
+ *                        keeps this pointer: ep_convert_combine_input reads
+ *                        the counts through it again, so the buffer must stay
+ *                        allocated and hold the same counts until the last
+ *                        inverse of this conversion has run on its stream.
  * Outputs (device, caller-owned, must not overlap the inputs or workspaces):
  *   packed_x             [W][Er][cap][H] dispatch_dtype, 16-byte aligned:
  *                        slots p < min(count, cap) are written.
@@ -506,7 +510,10 @@ typedef struct ep_convert_combine_args {
 /* The inverse ([GUIDE4] convert_combine_input), through the map of the last
  * ep_convert_dispatch_output on this expert plan, which must have converted
  * the plan's current dispatch. Asynchronous; no allocation; capturable; may be
- * called any number of times per conversion.
+ * called any number of times per conversion. It reads the row counts from the
+ * recv_num_token buffer that conversion was given (the caller keeps that
+ * buffer alive and unchanged meanwhile; a freed or rewritten buffer gives
+ * wrong rows, bounded by the capacity W * M).
  * Errors: EP_ERR_NULL, EP_ERR_ALIGN, EP_ERR_ARG (apply_weights not 0 or 1),
  * EP_ERR_STATE (no conversion yet, the plan dispatched again since, or
  * weights asked for and the conversion had none), EP_ERR_HIP. */

@@ -643,3 +643,84 @@ def test_argument_cache_keeps_no_tensor_alive():
     gc.collect()
     assert alive() is None
     assert not cra._same_tensors(held, (torch.zeros(8), None, b))
+
+
+def test_argument_cache_misses_on_a_tensor_changed_in_place():
+    """A cached tensor resized, retyped or transposed in place keeps its object
+    (and maybe its address) but must be checked again."""
+    import torch
+
+    a = torch.zeros(64)
+    held = cra._hold((a,))
+    assert cra._same_tensors(held, (a,))
+    a.resize_(32)                       # same storage, same address, fewer bytes
+    assert not cra._same_tensors(held, (a,))
+    b = torch.zeros(8, 8)
+    held = cra._hold((b,))
+    b.t_()                              # same bytes, no longer contiguous
+    assert not cra._same_tensors(held, (b,))
+    c = torch.zeros(16, dtype=torch.int32)
+    held = cra._hold((c,))
+    c.data = c.data.view(torch.float32)  # same bytes, another element type
+    assert not cra._same_tensors(held, (c,))
+
+
+def _headline_cfg(**kw):
+    return cra.make_config(8, 7168, 64, 32, 8, kw.pop("dtype", "bf16"), **kw)
+
+
+@pytest.mark.parametrize("arg,bad,word", [
+    ("indices", "int64", "indices must be torch.int32"),
+    ("weights", "float64", "weights must be torch.float32"),
+    ("weights", "float16", "weights must be torch.float32"),
+    ("x", "float32", "x must be torch.bfloat16 or torch.uint8"),
+    ("recv_num_token", "int64", "recv_num_token must be torch.int32"),
+])
+def test_dispatch_rejects_wrong_element_types(arg, bad, word):
+    """The element type is checked before anything else: int64 ids (what
+    torch.topk returns) hold twice the bytes the int32 ids need, so a size
+    check alone would pass them and the kernel would read every id as a pair
+    of int32 words."""
+    import torch
+
+    cfg = _headline_cfg()
+    args = dict(x=None, indices=None, weights=None, scales=None, out_x=None, out_indices=None,
+                out_weights=None, out_scales=None, recv_num_token=None)
+    args[arg] = torch.zeros(4, dtype=getattr(torch, bad))
+    with pytest.raises(ValueError, match=word):
+        cra._dispatch_args(cfg, [64] * 8, **args)
+
+
+def test_dispatch_cast_takes_its_source_type():
+    import torch
+
+    cfg = _headline_cfg(dtype="fp8", dispatch_cast="fp16")
+    with pytest.raises(ValueError, match="x must be torch.float16 or torch.uint8"):
+        cra._dispatch_args(cfg, [64] * 8, torch.zeros(4, dtype=torch.bfloat16), *[None] * 8)
+
+
+@pytest.mark.parametrize("wire,arg,bad", [
+    (None, "y", "float32"), (None, "y_weights", "float64"), (None, "out", "float16"),
+    ("fp8_block128", "y", "bfloat16"), ("fp8_block128", "y_scales", "float64"),
+    ("mxfp4", "y_scales", "float32"),
+])
+def test_combine_rejects_wrong_element_types(wire, arg, bad):
+    import torch
+
+    cfg = _headline_cfg(combine_wire=wire)
+    args = dict(y=None, y_weights=None, out=None, out_weights=None, y_scales=None)
+    args[arg] = torch.zeros(4, dtype=getattr(torch, bad))
+    with pytest.raises(ValueError, match=f"{arg} must be"):
+        cra._combine_args(cfg, **args)
+
+
+def test_expert_calls_reject_wrong_element_types():
+    import torch
+
+    cfg = _headline_cfg()
+    with pytest.raises(ValueError, match="packed_layout_range must be torch.int64"):
+        cra._convert_dispatch_args(cfg, 64, *[None] * 9, torch.zeros(4, dtype=torch.int32))
+    with pytest.raises(ValueError, match="indices must be torch.int32"):
+        cra._combine_standard_args(cfg, 64, None, torch.zeros(4, dtype=torch.int64), None, None)
+    with pytest.raises(ValueError, match="packed_y must be torch.bfloat16"):
+        cra._convert_combine_args(cfg, 64, torch.zeros(4, dtype=torch.float16), None)
