@@ -25,6 +25,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -678,6 +679,256 @@ def summarize_counters(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, cal_m
         print("\n".join(lines))
 
 
+def measure_pattern_ceilings(cra, torch, wl, op, x, stream, kern_ms, launch, recv_total):
+    """What this memory delivers on the path's own access patterns, in this
+    process, on the same buffers (include/ep_probe.h): streaming reads, plain
+    writes and a 1:1 copy of 14 KB rows, the dispatch copy's fan-out of each
+    token row to its destination rows at the dispatch's own receive slots (the
+    plan's forward map), and the combine's gather-sum of those rows back. The
+    fan-out and gather move exactly the payload bytes of the copy and combine
+    kernels, so a kernel's time over its pattern's time is the share of the
+    pattern ceiling it reaches. Overwrites the op's outputs: the caller
+    dispatches again before using them."""
+    W, M, H = wl.world_size, wl.max_tokens, wl.hidden
+    WM = W * M
+    row = H * (1 if wl.dispatch_dtype == "fp8" else 2)
+    N, R = W * M, int(recv_total)
+    fmap, stride = cra.ep_probe_forward_map(op.plan)
+    dpieces, dwaves = launch["dispatch_row_split"], launch["dispatch_waves"]
+    sink = torch.empty(W * WM * dpieces * 4, dtype=torch.uint8, device="cuda")
+    cpieces, cwaves = launch["combine_row_split"], launch["combine_waves"]
+    probes = {
+        # name: (kind, rows, src, dst, map, map_rows, pieces, waves, bytes)
+        "read": (cra.EP_PROBE_READ, W * WM, op.out_x, sink, None, 0, dpieces, dwaves,
+                 W * WM * row),
+        "write": (cra.EP_PROBE_WRITE, W * WM, None, op.out_x, None, 0, dpieces, dwaves,
+                  W * WM * row),
+        "copy_1to1": (cra.EP_PROBE_COPY, N, x, op.out_x, None, 0, dpieces, dwaves, 2 * N * row),
+        "fanout_dispatch": (cra.EP_PROBE_FANOUT, N, x, op.out_x, fmap, W * WM, dpieces, dwaves,
+                            (N + R) * row),
+        "gather_combine": (cra.EP_PROBE_GATHER, N, op.out_x, op.combine_out, fmap, W * WM,
+                           cpieces, cwaves, (N + R) * row),
+    }
+    out = {"method": "include/ep_probe.h kernels on the op's own buffers, 2 warmups + 10 "
+                     "launches between HIP events on the launch stream; 14 KB rows; fan-out "
+                     "and gather through the dispatch's forward map (the same rows and bytes "
+                     "as the payload of the copy and combine kernels)"}
+    for name, (kind, rows, src, dst, mp, mrows, pieces, waves, nbytes) in probes.items():
+        fn = (lambda kind=kind, rows=rows, src=src, dst=dst, mp=mp, mrows=mrows, pieces=pieces,
+              waves=waves: cra.ep_probe_pattern(kind, row, rows, src, dst, mp, mrows, stride,
+                                                pieces, waves, stream=stream))
+        ms = _timed(torch, stream, fn, 10, 2)
+        out[name] = {"us": round(ms * 1e3, 2), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "pct_of_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 1),
+                     "bytes": int(nbytes)}
+    # the kernels against their patterns: same payload bytes, so the ratio of
+    # times; the kernels also move their metadata (ids, weights, maps)
+    out["copy_kernel_pct_of_fanout"] = round(100 * out["fanout_dispatch"]["us"] /
+                                             (kern_ms["copy"] * 1e3), 1)
+    out["combine_kernel_pct_of_gather"] = round(100 * out["gather_combine"]["us"] /
+                                                (kern_ms["combine"] * 1e3), 1)
+    del sink
+    return out
+
+
+def run_oracle_call(oracle, np, wl, inp, y_host, in_place):
+    """One dispatch + combine of the CPU oracle on the workload's inputs;
+    returns (dispatch results, combine out, combine weights)."""
+    W, M, k, H = wl.world_size, wl.max_tokens, wl.topk, wl.hidden
+    import torch
+
+    xb = inp["x"].view(torch.uint8).numpy()
+    scn = None if inp["scales"] is None else inp["scales"].numpy()
+    ref = oracle.dispatch(W, M, k, wl.experts_per_rank, inp["ntok"], xb, inp["idx"].numpy(),
+                          inp["w"].numpy(), scn)
+    y16 = (ref["out_x"].view(np.uint16).reshape(W, W * M, H) if in_place
+           else y_host.view(torch.int16).numpy().view(np.uint16))
+    ro, rw = oracle.combine(W, M, k, H, oracle.BF16 if wl.combine_dtype == "bf16" else oracle.FP16,
+                            inp["ntok"], ref["fwd"], y16, ref["out_w"])
+    return ref, ro, rw
+
+
+def cpu_baseline_all_cores(oracle, np, wl, payload_of, tokens=512):
+    """The oracle, unchanged and single-threaded per call, run as one call per
+    host core at once (ctypes releases the interpreter lock during each C
+    call): aggregate payload GB/s over a bounded sample, the workload's shape
+    with `tokens` tokens a rank (its first tokens, same ids and rows)."""
+    import threading
+
+    import torch
+
+    import workloads
+
+    W = wl.world_size
+    sub = workloads.Workload(wl.name + f"_first{tokens}", W, tokens, wl.hidden,
+                             wl.dispatch_dtype, wl.combine_dtype, wl.num_experts, wl.topk,
+                             wl.scale_dim, wl.routing, wl.ragged, wl.expert, wl.seed_index)
+    full = workloads.make_inputs(wl)
+    inp = {"ntok": [min(t, tokens) for t in full["ntok"]],
+           "x": full["x"][:, :tokens].contiguous(), "idx": full["idx"][:, :tokens].contiguous(),
+           "w": full["w"][:, :tokens].contiguous(),
+           "scales": None if full["scales"] is None else full["scales"][:, :tokens].contiguous()}
+    del full
+    cores = min(16, os.cpu_count() or 1)
+    recv = []
+
+    def one():
+        ref, _, _ = run_oracle_call(oracle, np, sub, inp, None, True)
+        recv.append(int(ref["recv"].sum()))
+
+    one()                       # warmup, and the sample's received rows
+    threads = [threading.Thread(target=one) for _ in range(cores)]
+    t = time.perf_counter()
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    wall = time.perf_counter() - t
+    nbytes = payload_of(sub, inp["ntok"], recv[0])
+    return {"value": round(cores * nbytes / wall / 1e9, 3), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{cores} concurrent single-threaded oracle calls (dispatch + combine), "
+                      f"each on the first {tokens} tokens of every rank of {wl.name}; "
+                      f"{wall:.2f} s wall for all of them"}
+
+
+def measure_small_workloads(args, cra, torch, np):
+    """Every workload other than the headline, at its full size: µs per
+    dispatch + combine call (eager launches and graph replay), per-kernel
+    durations, payload GB/s against the 8 TB/s peak, the time the 70% mark
+    asks for, and a bit-exact check against the oracle (whose time is that
+    workload's CPU baseline)."""
+    import workloads
+
+    out = {}
+    steps = max(args.small_steps, 1)
+    for name, wl in workloads.WORKLOADS.items():
+        if name == workloads.HEADLINE:
+            continue
+        W, M, k, H = wl.world_size, wl.max_tokens, wl.topk, wl.hidden
+        inp = workloads.make_inputs(wl)
+        cfg = cra.make_config(W, H, M, wl.experts_per_rank, k, wl.dispatch_dtype,
+                              wl.combine_dtype, scale_dim=wl.scale_dim, scale_type_size=4)
+        op = cra.EpDispatchCombineOp(cfg)
+        dev = torch.device("cuda")
+        x, idx, w = inp["x"].to(dev), inp["idx"].to(dev), inp["w"].to(dev)
+        sc = None if inp["scales"] is None else inp["scales"].to(dev)
+        ntok = inp["ntok"]
+        in_place = wl.expert == "identity" and wl.dispatch_dtype == wl.combine_dtype
+        if in_place:
+            y_host, y = None, op.out_x
+        else:   # a seeded expert output of the combine type
+            g = torch.Generator().manual_seed(workloads.BASE_SEED + 77)
+            y_host = torch.randn((W, W * M, H), generator=g).to(
+                workloads.TORCH_DTYPE[wl.combine_dtype])
+            y = y_host.to(dev)
+        stream = torch.cuda.current_stream()
+
+        def step():
+            op.dispatch(ntok, x, idx, w, sc, stream=stream)
+            op.combine(y, op.out_weights, stream=stream)
+
+        step()
+        torch.cuda.synchronize()
+        recv = op.recv_num_token.cpu().numpy()
+        payload, kb = algorithmic_bytes(wl, ntok, recv.sum())
+        rec = {"workload": name}
+        if not args.no_cpu_baseline:
+            import oracle
+
+            t = time.perf_counter()
+            ref, ro, rw = run_oracle_call(oracle, np, wl, inp, y_host, in_place)
+            cpu_s = time.perf_counter() - t
+            ok = np.array_equal(recv, ref["recv"])
+            gout = op.combine_out.view(torch.int16).cpu().numpy().view(np.uint16)
+            gw = op.combine_weights.cpu().numpy().view(np.uint32)
+            for d in range(W):
+                Rd = int(recv[d])
+                ok = ok and np.array_equal(op.out_x[d, :Rd].view(torch.uint8).cpu().numpy(),
+                                           ref["out_x"][d, :Rd])
+            for r in range(W):
+                ok = ok and np.array_equal(gout[r, :ntok[r]], ro[r, :ntok[r]])
+                ok = ok and np.array_equal(gw[r, :ntok[r]], rw[r, :ntok[r]].view(np.uint32))
+            if not ok:
+                print(f"bench.py: {name}: GPU results differ from the oracle", file=sys.stderr)
+                sys.exit(1)
+            rec["check"] = "bit-exact vs oracle (receive rows, combine rows and weights)"
+            rec["cpu_baseline"] = {"value": round(payload / cpu_s / 1e9, 3), "unit": "GB/s",
+                                   "cores": 1, "kind": "oracle",
+                                   "sample": f"one call, {cpu_s * 1e3:.1f} ms"}
+        ms = _timed(torch, stream, step, steps, 20)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(steps):
+            step()
+        host_us = (time.perf_counter() - t) / steps * 1e6
+        torch.cuda.synchronize()
+        # one step captured in a HIP graph and replayed (the pages' method)
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                op.dispatch(ntok, x, idx, w, sc, stream=side)
+                op.combine(y, op.out_weights, stream=side)
+        torch.cuda.synchronize()
+        ms_graph = _timed(torch, stream, graph.replay, steps, 20)
+        del graph
+        cra.ep_plan_set_timing(op.plan, True)
+        torch.cuda.synchronize()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        kern = {}
+        for kn, kid in (("route", cra.EP_KERNEL_ROUTE), ("scan", cra.EP_KERNEL_SCAN),
+                        ("copy", cra.EP_KERNEL_COPY), ("combine", cra.EP_KERNEL_COMBINE)):
+            c, t_ms = cra.ep_plan_kernel_time(op.plan, kid)
+            if c:
+                kern[kn] = round(t_ms / c * 1e3, 2)
+        cra.ep_plan_set_timing(op.plan, False)
+        rate = payload / (ms * 1e-3) / 1e9
+        rec.update({
+            "us_per_call": round(ms * 1e3, 2),
+            "us_per_call_graph_replay": round(ms_graph * 1e3, 2),
+            "host_issue_us_per_call": round(host_us, 2),
+            "kernel_us": kern,
+            "payload_bytes_per_call": int(payload),
+            "received_rows": int(recv.sum()),
+            "payload_GBps": round(rate, 1),
+            "frac_of_peak": round(rate / PEAK_HBM_GBS, 4),
+            "us_at_70pct_of_peak": round(payload / (0.7 * PEAK_HBM_GBS * 1e9) * 1e6, 2),
+            "launch": cra.ep_plan_get_launch(op.plan, ntok),
+            "steps": steps,
+        })
+        op.close()
+        del op, x, idx, w, sc, y
+        torch.cuda.empty_cache()
+        out[name] = rec
+    return out
+
+
+def rocprof_frac(workload, kernel_pattern, nbytes):
+    """The dominant kernel's average duration in the committed rocprofv3
+    summary of this workload, taken on the current kernel sources, and the
+    roofline fraction it gives for nbytes per launch; None if there is none."""
+    import re
+
+    path = os.path.join(ROOT, "profiles", f"kernel_stats_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"Kernel sources sha256\[:16\]: (\w+)", text)
+    if not m or m.group(1) != kernel_source_hash():
+        return None
+    for line in text.splitlines():
+        if re.search(kernel_pattern, line):
+            avg_us = float(line.split("|")[3])
+            a = nbytes / (avg_us * 1e-6) / 1e9
+            return {"average_us": avg_us, "achieved": round(a, 2),
+                    "frac": round(a / PEAK_HBM_GBS, 4), "source": os.path.relpath(path, ROOT)}
+    return None
+
+
 def run(args):
     import numpy as np
     import torch
@@ -727,22 +978,29 @@ def run(args):
     if not args.no_cpu_baseline:
         import oracle
 
-        xb = inp["x"].view(torch.uint8).numpy()
-        scn = None if inp["scales"] is None else inp["scales"].numpy()
-        t = time.perf_counter()
-        ref = oracle.dispatch(W, M, k, wl.experts_per_rank, ntok, xb, inp["idx"].numpy(),
-                              inp["w"].numpy(), scn)
-        y16 = (ref["out_x"].view(np.uint16).reshape(W, W * M, H) if in_place
-               else y_host.view(torch.int16).numpy().view(np.uint16))
-        ro, rw = oracle.combine(W, M, k, H, oracle.BF16 if wl.combine_dtype == "bf16"
-                                else oracle.FP16, ntok, ref["fwd"], y16, ref["out_w"])
-        cpu_s = time.perf_counter() - t
+        # 1 warmup call, then the median of cpu_runs timed calls (each the whole
+        # workload, single-threaded); the last call's results are checked
+        times = []
+        for i in range(1 + args.cpu_runs):
+            t = time.perf_counter()
+            ref, ro, rw = run_oracle_call(oracle, np, wl, inp, y_host, in_place)
+            if i:
+                times.append(time.perf_counter() - t)
+            if i < args.cpu_runs:
+                del ref, ro, rw
+            print(f"[bench] oracle call {i} took {time.perf_counter() - t:.2f}s", file=sys.stderr,
+                  flush=True)
+        cpu_s = sorted(times)[len(times) // 2]
         cpu_baseline = {"value": round(payload_bytes / cpu_s / 1e9, 3), "unit": "GB/s",
                         "cores": 1, "kind": "oracle",
                         "sample": f"the whole {wl.name} workload: one dispatch+combine call of "
-                                  f"the single-threaded C oracle, {cpu_s:.2f} s",
+                                  f"the single-threaded C oracle; 1 warmup call, then the median "
+                                  f"of {args.cpu_runs} timed calls: {cpu_s:.2f} s",
+                        "samples_s": [round(v, 3) for v in times],
                         "host": host_cpu()}
-        print(f"[bench] oracle call took {cpu_s:.2f}s", file=sys.stderr, flush=True)
+        if args.cpu_all_cores:
+            cpu_baseline["all_cores"] = cpu_baseline_all_cores(
+                oracle, np, wl, lambda w_, nt, r: algorithmic_bytes(w_, nt, r)[0])
         ok = np.array_equal(recv, ref["recv"])
         for d in range(W):
             Rd = int(recv[d])
@@ -762,7 +1020,7 @@ def run(args):
             T = ntok[r]
             ok = ok and np.array_equal(gout[r, :T], ro[r, :T])
             ok = ok and np.array_equal(gw[r, :T], rw[r, :T].view(np.uint32))
-        del ref, y16, ro, rw
+        del ref, ro, rw
         if not ok:
             print("bench.py: GPU results differ from the oracle; not timing", file=sys.stderr)
             sys.exit(1)
@@ -830,6 +1088,16 @@ def run(args):
             args, torch, stream, lambda: op.dispatch(ntok, x, idx, w, sc, stream=stream),
             lambda: op.combine(y, op.out_weights, stream=stream))
 
+    ceilings = None
+    uniform_tokens = all(t == M for t in ntok)
+    if args.ceilings and uniform_tokens and wl.dispatch_dtype != "fp8":
+        ceilings = measure_pattern_ceilings(cra, torch, wl, op, x, stream, kern,
+                                            cra.ep_plan_get_launch(op.plan, ntok), recv.sum())
+        step()                      # the op's outputs again, for what follows
+        torch.cuda.synchronize()
+        print(f"[bench] pattern ceilings done at {time.time() - t0:.1f}s", file=sys.stderr,
+              flush=True)
+
     dom = "copy" if kern["copy"] >= kern["combine"] else "combine"
     achieved = kernel_bytes[dom] / (kern[dom] * 1e-3) / 1e9
     traffic = read_traffic(wl.name, KERNELS[dom])
@@ -867,7 +1135,13 @@ def run(args):
         "roofline": {"bound": "hbm", "kernel": KERNELS[dom], "achieved": round(achieved, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": kernel_bytes[dom]},
+                     "algorithmic_bytes_per_launch": kernel_bytes[dom],
+                     "frac_method": "algorithmic bytes per launch (payload and metadata) over "
+                                    "the kernel's mean duration between HIP events recorded "
+                                    "by the library on its stream, in this run",
+                     "rocprof": rocprof_frac(wl.name, COUNTER_KERNELS[KERNELS[dom]],
+                                             kernel_bytes[dom])},
+        "pattern_ceilings": ceilings,
         "cpu_baseline": cpu_baseline,
     }
     def progress(what):
@@ -886,6 +1160,11 @@ def run(args):
         line["quantized_wires"] = measure_quantized_wires(args, cra, torch, np, wl, inp, stream)
         progress("quantized wires")
     op.close()
+    del op, x, idx, w, sc, y
+    torch.cuda.empty_cache()
+    if args.small and args.workload is None:
+        line["workloads"] = measure_small_workloads(args, cra, torch, np)
+        progress("the other workloads")
     # the box's own device copy rate (1 GiB, torch), measured last so its
     # buffers take no part in the placement of the timed ones
     copy_rate = device_copy_rate(torch)
@@ -911,6 +1190,16 @@ def main():
     ap.add_argument("--samples", type=int, default=30, help="per-call samples a round")
     ap.add_argument("--graph", action="store_true",
                     help="time K replays of one step captured in a HIP graph")
+    ap.add_argument("--cpu-runs", type=int, default=3,
+                    help="timed oracle calls after one warmup; the CPU baseline is their median")
+    ap.add_argument("--no-cpu-all-cores", dest="cpu_all_cores", action="store_false",
+                    help="skip the all-core oracle figure")
+    ap.add_argument("--no-ceilings", dest="ceilings", action="store_false",
+                    help="skip the access-pattern ceilings")
+    ap.add_argument("--no-small", dest="small", action="store_false",
+                    help="skip the other workloads (run with the headline by default)")
+    ap.add_argument("--small-steps", type=int, default=200,
+                    help="timed calls of each other workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--summarize-stats", nargs="+", metavar="ARG")
     ap.add_argument("--summarize-counters", nargs=6, metavar="ARG")

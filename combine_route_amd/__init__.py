@@ -47,7 +47,9 @@ EXPORTED = ("ep_workspace_bytes", "ep_plan_create", "ep_plan_destroy", "ep_dispa
             "ep_plan_get_launch", "ep_plan_set_timing", "ep_plan_kernel_time",
             "ep_expert_workspace_bytes", "ep_expert_plan_create", "ep_expert_plan_destroy",
             "ep_convert_dispatch_output", "ep_convert_combine_input", "ep_quantize_rows",
-            "ep_dispatch_standard_moe", "ep_combine_standard_moe")
+            "ep_dispatch_standard_moe", "ep_combine_standard_moe", "ep_probe_pattern",
+            "ep_probe_forward_map")
+EP_PROBE_READ, EP_PROBE_WRITE, EP_PROBE_COPY, EP_PROBE_FANOUT, EP_PROBE_GATHER = range(5)
 
 
 class EpConfig(ctypes.Structure):
@@ -99,6 +101,14 @@ class EpCombineStandardArgs(ctypes.Structure):
                                                "packed_y_scales")]
 
 
+class EpProbeArgs(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("row_bytes", ctypes.c_int32),
+                ("rows", ctypes.c_int64), ("src", ctypes.c_void_p), ("dst", ctypes.c_void_p),
+                ("map", ctypes.c_void_p), ("map_rows", ctypes.c_int64),
+                ("stride", ctypes.c_int32), ("pieces", ctypes.c_int32),
+                ("waves", ctypes.c_int32)]
+
+
 class EpError(RuntimeError):
     def __init__(self, fn, code, msg):
         super().__init__(f"{fn} failed ({code}): {msg}")
@@ -141,6 +151,8 @@ def load():
     lib.ep_combine_standard_moe.argtypes = [V, P(EpCombineStandardArgs), V]
     lib.ep_quantize_rows.argtypes = [V, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_int32, V, V, V, ctypes.c_int64, V]
+    lib.ep_probe_pattern.argtypes = [P(EpProbeArgs), V]
+    lib.ep_probe_forward_map.argtypes = [V, P(V), P(ctypes.c_int32)]
     for name in EXPORTED:
         if name not in ("ep_workspace_bytes", "ep_last_error", "ep_expert_workspace_bytes"):
             getattr(lib, name).restype = I
@@ -387,6 +399,33 @@ def ep_quantize_rows(rows: torch.Tensor, wire, out: torch.Tensor, scales: torch.
     _check("ep_quantize_rows", load().ep_quantize_rows(
         _dev(rows, "rows", n * H * 2), n, H, dt, w, _dev(out, "out", need_out, ot),
         _dev(scales, "scales", need_sc, stt), cp, group, _stream(stream, rows.device.index)))
+
+
+def ep_probe_pattern(kind: int, row_bytes: int, rows: int, src=None, dst=None, map=None,
+                     map_rows: int = 0, stride: int = 1, pieces: int = 1, waves: int = 8,
+                     stream=None) -> None:
+    """ep_probe_pattern() (include/ep_probe.h): one access-pattern probe
+    launch, for measurement. src / dst are device tensors (or None), map a
+    device int32 tensor or a device address (int), sizes checked here."""
+    rb, n = int(row_bytes), int(rows)
+    src_need = {EP_PROBE_READ: n * rb, EP_PROBE_COPY: n * rb, EP_PROBE_FANOUT: n * rb,
+                EP_PROBE_GATHER: int(map_rows) * rb}.get(kind, 0)
+    dst_need = {EP_PROBE_READ: n * pieces * 4, EP_PROBE_WRITE: n * rb, EP_PROBE_COPY: n * rb,
+                EP_PROBE_FANOUT: int(map_rows) * rb, EP_PROBE_GATHER: n * rb}.get(kind, 0)
+    mp = map if isinstance(map, int) or map is None else _dev(map, "map", n * stride * 4, _I32)
+    a = EpProbeArgs(kind, rb, n, _dev(src, "src", src_need), _dev(dst, "dst", dst_need), mp,
+                    int(map_rows), int(stride), int(pieces), int(waves))
+    dev_index = (dst if dst is not None else src).device.index
+    _check("ep_probe_pattern", load().ep_probe_pattern(ctypes.byref(a), _stream(stream, dev_index)))
+
+
+def ep_probe_forward_map(plan: int):
+    """(device address of the plan's forward map [W][M][stride] int32, stride)."""
+    p = ctypes.c_void_p()
+    st = ctypes.c_int32()
+    _check("ep_probe_forward_map", load().ep_probe_forward_map(plan, ctypes.byref(p),
+                                                                ctypes.byref(st)))
+    return p.value, st.value
 
 
 def ep_get_src_token_pos(plan: int, rank: int) -> int:

@@ -12,17 +12,17 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libcombine_route_amd.so")
 SOURCES = [os.path.join(PKG, "csrc", f)
            for f in ("ep_plan.cpp", "ep_kernels.hip", "ep_expert.hip", "ep_wire.hip",
-                     "ep_standard.hip")]
+                     "ep_standard.hip", "ep_probe.hip")]
 ARCH = "gfx950"
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-    # packed FP32 instructions stay off in the gfx950 code: the compiler would
-    # otherwise pair the combine's FP32 adds into v_pk_add_f32. The feature
-    # exists only for the device target, so each word of the option goes to
-    # the device pass alone (-Xarch_device) and the host pass never sees it.
-    *[w for a in ("-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops")
-      for w in ("-Xarch_device", a)],
+    # Packed FP32 instructions stay off in the gfx950 code: the compiler would
+    # otherwise pair the combine's FP32 adds into v_pk_add_f32. The feature is
+    # a device feature; -Xarch_device cannot forward -Xclang options, so the
+    # flag reaches the host pass too, which warns that x86 has no such
+    # feature and ignores it. build() checks the device code it links.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fno-fast-math", "-ffp-contract=off",
     "-Wall", "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"),
@@ -35,6 +35,45 @@ def hipcc() -> str:
         if c and os.path.exists(c):
             return c
     return "hipcc"
+
+
+PACKED_FP32 = ("v_pk_add_f32", "v_pk_mul_f32", "v_pk_fma_f32")
+
+
+def device_code(lib: str = LIB) -> str:
+    """Disassembly of the library's gfx950 code: its .hip_fatbin section holds
+    one offload bundle per source file, each unbundled and disassembled with
+    the ROCm LLVM tools."""
+    import re
+    import tempfile
+
+    llvm = "/opt/rocm/llvm/bin"
+    asm = []
+    with tempfile.TemporaryDirectory() as tmp:
+        fat = os.path.join(tmp, "fatbin")
+        subprocess.run([os.path.join(llvm, "llvm-objcopy"), f"--dump-section=.hip_fatbin={fat}",
+                        lib, os.path.join(tmp, "stripped")], check=True)
+        with open(fat, "rb") as f:
+            data = f.read()
+        starts = [m.start() for m in re.finditer(re.escape(b"__CLANG_OFFLOAD_BUNDLE__"), data)]
+        for i, beg in enumerate(starts):
+            part, co = os.path.join(tmp, f"bundle{i}"), os.path.join(tmp, f"device{i}.co")
+            with open(part, "wb") as f:
+                f.write(data[beg: starts[i + 1] if i + 1 < len(starts) else len(data)])
+            subprocess.run([os.path.join(llvm, "clang-offload-bundler"), "--unbundle",
+                            "--type=o", f"--targets=hipv4-amdgcn-amd-amdhsa--{ARCH}",
+                            f"--input={part}", f"--output={co}"], check=True)
+            asm.append(subprocess.run([os.path.join(llvm, "llvm-objdump"), "-d", co], check=True,
+                                      capture_output=True, text=True).stdout)
+    return "\n".join(asm)
+
+
+def device_packed_fp32(lib: str = LIB) -> dict:
+    """Packed FP32 instructions in the library's gfx950 code: {mnemonic: count}."""
+    import re
+
+    asm = device_code(lib)
+    return {m: len(re.findall(rf"\b{m}\b", asm)) for m in PACKED_FP32}
 
 
 def build(verbose: bool = False, extra=()) -> str:
@@ -60,6 +99,9 @@ def build(verbose: bool = False, extra=()) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+    found = {m: c for m, c in device_packed_fp32(tmp).items() if c}
+    if found:
+        raise RuntimeError(f"packed FP32 instructions in the gfx950 code: {found}")
     os.replace(tmp, LIB)
     return LIB
 

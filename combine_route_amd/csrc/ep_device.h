@@ -107,6 +107,21 @@ __device__ __forceinline__ u32x4 narrow(const float (&f)[8])
     return w;
 }
 
+// x rounded to the combine type (nearest even) and read back as FP32, in one
+// conversion an element for bf16: v_cvt_pk_bf16_f32 of the pair (0, x) puts
+// bf16(x) in the high half over a zero low half, which is bf16(x)'s value as
+// a binary32 exactly. fp16 converts there and back.
+template <int DT>
+__device__ __forceinline__ float round_to(float x)
+{
+    if constexpr (DT == 0) {
+        const f32x2 p = {0.0f, x};
+        return __builtin_bit_cast(float, __builtin_convertvector(p, bf16x2));
+    } else {
+        return (float)(_Float16)x;
+    }
+}
+
 constexpr float kE4M3Max = 448.0f;
 
 // OCP E4M3 codes (the OFP8 specification: bias 7, no infinities, largest

@@ -246,4 +246,18 @@ hipError_t launch_quantize(const QuantizeArgs& a, int wire, int dtype, bool stre
 hipError_t launch_combine_wire(const WireCombineArgs& a, const TokenMap& tk, int wire, int dtype,
                                int waves, int row_split, bool stream, hipStream_t s);
 
+// Access-pattern probes (include/ep_probe.h); kind is an EP_PROBE_* value.
+struct ProbeArgs {
+    int32_t kind;
+    uint32_t row_bytes;
+    int64_t rows;
+    const uint8_t* src;
+    uint8_t* dst;
+    const int32_t* map;
+    int64_t map_rows;
+    int32_t stride;
+    int32_t pieces;
+};
+hipError_t launch_probe(const ProbeArgs& a, int waves, hipStream_t s);
+
 }  // namespace ep

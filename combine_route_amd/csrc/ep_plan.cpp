@@ -8,6 +8,7 @@
 // staging with shared buffer", Caller contract). Plans never allocate device
 // memory: the caller's workspace holds all device state.
 #include "ep.h"
+#include "ep_probe.h"
 
 #include <hip/hip_runtime.h>
 
@@ -904,6 +905,68 @@ int ep_get_src_token_pos(const ep_plan_t* p, int32_t rank, const int32_t** dev_p
 }
 
 const char* ep_last_error(void) { return g_error.c_str(); }
+
+int ep_probe_forward_map(const ep_plan_t* p, const int32_t** map, int32_t* stride)
+{
+    if (!p)
+        return fail(EP_ERR_NULL, "plan is NULL");
+    if (!map || !stride)
+        return fail(EP_ERR_NULL, "map / stride is NULL");
+    *map = reinterpret_cast<const int32_t*>(p->ws + p->s.off_fwd);
+    *stride = p->s.P;
+    return ok();
+}
+
+int ep_probe_pattern(const ep_probe_args_t* a, void* stream_ptr)
+{
+    if (!a)
+        return fail(EP_ERR_NULL, "args is NULL");
+    if (a->kind < EP_PROBE_READ || a->kind > EP_PROBE_GATHER)
+        return fail(EP_ERR_ARG, "args.kind = %d: not an EP_PROBE_* value", a->kind);
+    if (a->row_bytes <= 0 || a->row_bytes % 16)
+        return fail(EP_ERR_ARG, "args.row_bytes = %d: must be a positive multiple of 16",
+                    a->row_bytes);
+    if (a->rows < 0)
+        return fail(EP_ERR_ARG, "args.rows = %lld: must be >= 0", (long long)a->rows);
+    if (a->pieces < 1 || a->pieces > 64)
+        return fail(EP_ERR_ARG, "args.pieces = %d: must be in [1, 64]", a->pieces);
+    if (a->waves < 1 || a->waves > 16)
+        return fail(EP_ERR_ARG, "args.waves = %d: must be in [1, 16]", a->waves);
+    if (a->rows * a->pieces > INT32_MAX)
+        return fail(EP_ERR_ARG, "args.rows * args.pieces is too large for one launch");
+    const bool mapped = a->kind == EP_PROBE_FANOUT || a->kind == EP_PROBE_GATHER;
+    if (a->kind != EP_PROBE_WRITE && !a->src)
+        return fail(EP_ERR_NULL, "args.src is NULL");
+    if (!a->dst)
+        return fail(EP_ERR_NULL, "args.dst is NULL");
+    if (mapped) {
+        if (!a->map)
+            return fail(EP_ERR_NULL, "args.map is NULL");
+        if (a->stride < 1 || a->stride > 64)
+            return fail(EP_ERR_ARG, "args.stride = %d: must be in [1, 64]", a->stride);
+        if (a->map_rows < 0)
+            return fail(EP_ERR_ARG, "args.map_rows = %lld: must be >= 0",
+                        (long long)a->map_rows);
+        if (!aligned(a->map, 4))
+            return fail(EP_ERR_ALIGN, "args.map is not 4-byte aligned");
+    }
+    if ((a->src && !aligned(a->src, kPtrAlign)) || !aligned(a->dst, kPtrAlign))
+        return fail(EP_ERR_ALIGN, "args.src / args.dst are not 16-byte aligned");
+    ep::ProbeArgs pa;
+    pa.kind = a->kind;
+    pa.row_bytes = (uint32_t)a->row_bytes;
+    pa.rows = a->rows;
+    pa.src = static_cast<const uint8_t*>(a->src);
+    pa.dst = static_cast<uint8_t*>(a->dst);
+    pa.map = a->map;
+    pa.map_rows = mapped ? a->map_rows : 0;
+    pa.stride = mapped ? a->stride : 0;
+    pa.pieces = a->pieces;
+    const hipError_t e = ep::launch_probe(pa, a->waves, static_cast<hipStream_t>(stream_ptr));
+    if (e != hipSuccess)
+        return fail(EP_ERR_HIP, "probe launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
 
 int ep_plan_set_launch(ep_plan_t* p, const ep_launch_t* l)
 {

@@ -589,11 +589,9 @@ __global__ __launch_bounds__(1024) void sx_combine_kernel(StandardCombineArgs a,
                         }
                         if (last) {
                             // the rank's intermediate row: rounded to the combine type
-                            float p[8];
-                            widen<DT>(narrow<DT>(part[u]), p);
 #pragma unroll
                             for (int e = 0; e < 8; ++e) {
-                                tot[u][e] = tot[u][e] + p[e];
+                                tot[u][e] = tot[u][e] + round_to<DT>(part[u][e]);
                                 part[u][e] = -0.0f;
                             }
                         }

@@ -31,15 +31,19 @@ def lib():
 
 
 def header_functions():
-    with open(os.path.join(ROOT, "include", "ep.h")) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ep_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            with open(os.path.join(ROOT, "include", h)) as f:
+                text = f.read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(ep_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) == 19
+    assert len(names) == 21
     assert sorted(cra.EXPORTED) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -724,3 +728,37 @@ def test_expert_calls_reject_wrong_element_types():
         cra._combine_standard_args(cfg, 64, None, torch.zeros(4, dtype=torch.int64), None, None)
     with pytest.raises(ValueError, match="packed_y must be torch.bfloat16"):
         cra._convert_combine_args(cfg, 64, torch.zeros(4, dtype=torch.float16), None)
+
+
+def test_device_code_has_no_packed_fp32(lib):
+    """The gfx950 code of the built library holds no packed FP32 arithmetic
+    (v_pk_add_f32, v_pk_mul_f32, v_pk_fma_f32): the build turns the feature
+    off for the device pass, and this reads the code object back."""
+    import combine_route_amd.build as b
+
+    if not os.path.exists("/opt/rocm/llvm/bin/clang-offload-bundler"):
+        pytest.skip("ROCm LLVM tools not installed")
+    counts = b.device_packed_fp32(cra.LIB_PATH)
+    assert counts == {m: 0 for m in b.PACKED_FP32}, counts
+
+
+def test_probe_rejects_before_launch(lib):
+    """ep_probe_pattern checks every field on the host; nothing is launched."""
+    def args(**kw):
+        a = dict(kind=cra.EP_PROBE_FANOUT, row_bytes=1024, rows=4, src=FAKE, dst=FAKE + 0x10000,
+                 map=FAKE + 0x20000, map_rows=8, stride=4, pieces=1, waves=8)
+        a.update(kw)
+        return cra.EpProbeArgs(**a)
+    for kw, code in [(dict(kind=7), cra.EP_ERR_ARG), (dict(row_bytes=24), cra.EP_ERR_ARG),
+                     (dict(rows=-1), cra.EP_ERR_ARG), (dict(pieces=0), cra.EP_ERR_ARG),
+                     (dict(waves=17), cra.EP_ERR_ARG), (dict(src=None), cra.EP_ERR_NULL),
+                     (dict(dst=None), cra.EP_ERR_NULL), (dict(map=None), cra.EP_ERR_NULL),
+                     (dict(stride=65), cra.EP_ERR_ARG), (dict(map=FAKE + 2), cra.EP_ERR_ALIGN),
+                     (dict(src=FAKE + 8), cra.EP_ERR_ALIGN),
+                     (dict(rows=1 << 31), cra.EP_ERR_ARG)]:
+        assert lib.ep_probe_pattern(ctypes.byref(args(**kw)), None) == code, kw
+        assert cra.ep_last_error()
+    assert lib.ep_probe_pattern(None, None) == cra.EP_ERR_NULL
+    p = ctypes.c_void_p()
+    s = ctypes.c_int32()
+    assert lib.ep_probe_forward_map(None, ctypes.byref(p), ctypes.byref(s)) == cra.EP_ERR_NULL
