@@ -34,9 +34,12 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
 METRIC = "dispatch+combine µs/call and payload HBM GB/s (% of peak), EP8 H=7168 k=8"
+# the path's device code and the argument structs it is compiled against; a
+# profile summary taken on other sources is not used (launch geometry, set by
+# the host code, is in each line's "launch" field)
 KERNEL_SOURCES = [os.path.join(ROOT, "combine_route_amd", "csrc", f)
                   for f in ("ep_kernels.hip", "ep_expert.hip", "ep_wire.hip", "ep_kernels.h",
-                            "ep_device.h", "ep_plan.cpp", "ep_standard.hip")]
+                            "ep_device.h", "ep_standard.hip")]
 KERNELS = {"copy": "ep_copy_kernel", "combine": "ep_combine_kernel"}
 EXPERT_KERNELS = {"copy": "ex_copy_kernel", "combine": "ex_combine_kernel"}
 STANDARD_KERNELS = {"copy": "sx_copy_kernel", "combine": "sx_combine_kernel"}
@@ -64,6 +67,10 @@ COUNTER_KERNELS = {
     "ep_combine_wire_kernel_fp8_block128": r"ep_combine_wire_kernel<\d+, \d+, 1,",
     "ep_combine_wire_kernel_mxfp4": r"ep_combine_wire_kernel<\d+, \d+, 2,",
 }
+
+
+# the bench arguments of the counter runs that profiles/*_counters.txt record
+COUNTER_RUN_ARGS = "--no-cpu-baseline --steps 3 --warmup 1 --no-small --rounds 0"
 
 
 def kernel_source_hash() -> str:
@@ -577,6 +584,116 @@ def copy_ceiling(torch, mib, steps, warmup):
                       "GB/s": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
+MEMORY_KERNELS = [  # label, pattern over the demangled name
+    ("dispatch copy", r"ep_copy_kernel<8, 8, true, false, false>"),
+    ("combine", r"ep_combine_kernel<8, 2, 0, true>"),
+    ("probe: read", r"ep_probe_kernel<0>"),
+    ("probe: write", r"ep_probe_kernel<1>"),
+    ("probe: 1:1 copy", r"ep_probe_kernel<2>"),
+    ("probe: dispatch fan-out", r"ep_probe_kernel<3>"),
+    ("probe: combine gather", r"ep_probe_kernel<4>"),
+]
+
+
+def summarize_memory(out_md, csv_paths, command):
+    """Memory-side counters of the headline kernels and the access-pattern
+    probes, per launch: TCC (L2) cycles stalled for want of DRAM read or
+    write credits, TCC busy share, mean read and write latency at the L2's
+    memory interface, and L1 address-translation misses."""
+    import re
+
+    vals = {}
+    for path in csv_paths:
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"]
+            for label, pat in MEMORY_KERNELS:
+                if re.search(pat, name):
+                    vals.setdefault(label, {}).setdefault(r["Counter_Name"], []).append(
+                        float(r["Counter_Value"]))
+    mean = {lab: {c: sum(v) / len(v) for c, v in cs.items()} for lab, cs in vals.items()}
+
+    def ratio(m, a, b):
+        return m[a] / m[b] if a in m and b in m and m[b] else float("nan")
+
+    out = ["# Memory-side counters of the headline kernels and the access-pattern probes", "",
+           f"Kernel sources sha256[:16]: {kernel_source_hash()}", "",
+           "Commands (from the repository root), one counter group a run:", ""]
+    out += ["    " + c for c in command.split(" ;; ")]
+    out += ["", "Per launch, means over the run's launches. TCC = the L2 (all channels summed); a "
+            "credit stall is a TCC cycle in which a request could not go to DRAM for want of "
+            "credits; latency is in-flight requests summed per cycle over requests "
+            "(TCC_EA0_*_LEVEL / TCC_EA0_*REQ), in cycles.", "",
+            "| kernel | write credit stall / TCC cycles | read credit stall / TCC cycles | "
+            "TCC busy / TCC cycles | read latency (cycles) | write latency (cycles) | "
+            "UTCL1 translation misses / requests |",
+            "|---|---|---|---|---|---|---|"]
+    for label, _ in MEMORY_KERNELS:
+        m = mean.get(label)
+        if not m:
+            continue
+        out.append(
+            f"| {label} | {ratio(m, 'TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum', 'TCC_CYCLE_sum'):.3f} "
+            f"| {ratio(m, 'TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum', 'TCC_CYCLE_sum'):.3f} "
+            f"| {ratio(m, 'TCC_BUSY_sum', 'TCC_CYCLE_sum'):.3f} "
+            f"| {ratio(m, 'TCC_EA0_RDREQ_LEVEL_sum', 'TCC_EA0_RDREQ_sum'):.0f} "
+            f"| {ratio(m, 'TCC_EA0_WRREQ_LEVEL_sum', 'TCC_EA0_WRREQ_sum'):.0f} "
+            f"| {ratio(m, 'TCP_UTCL1_TRANSLATION_MISS_sum', 'TCP_UTCL1_REQUEST_sum'):.5f} |")
+    out += ["", "Raw means per launch:", "", "| kernel | counter | value |", "|---|---|---|"]
+    for label, _ in MEMORY_KERNELS:
+        for c, v in sorted(mean.get(label, {}).items()):
+            out.append(f"| {label} | {c} | {v:.0f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
+def summarize_trace(out_md, eager_csv, graph_csv, skip_eager, skip_graph, steps, command):
+    """Kernel durations and the gaps between kernels of the timed calls of one
+    workload, eager launches against graph replay: for each mode, the calls
+    [skip, skip + steps) of the trace (route, copy, combine triples in start
+    order), medians of each kernel's duration, of the gaps route -> copy and
+    copy -> combine, of the gap from one call's combine to the next call's
+    route, and of the call period."""
+    import statistics
+
+    def calls(path):
+        rows = [r for r in csv.DictReader(open(path)) if "ep::" in r["Kernel_Name"]]
+        rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+        out, i = [], 0
+        while i + 2 < len(rows):
+            n = [rows[i + j]["Kernel_Name"] for j in range(3)]
+            if "ep_route_kernel" in n[0] and "ep_copy_kernel" in n[1] and "ep_combine_kernel" in n[2]:
+                out.append([(int(r["Start_Timestamp"]) / 1e3, int(r["End_Timestamp"]) / 1e3)
+                            for r in rows[i:i + 3]])
+                i += 3
+            else:
+                i += 1
+        return out
+
+    lines = ["# Kernel trace: eager launches against graph replay", "",
+             f"Kernel sources sha256[:16]: {kernel_source_hash()}", "",
+             "Commands (from the repository root):", ""]
+    lines += ["    " + c for c in command.split(" ;; ")]
+    lines += ["", "Medians over the timed calls, in microseconds (timestamps of the kernel trace):",
+              "", "| mode | calls | route | copy | combine | gap route -> copy | "
+              "gap copy -> combine | gap to the next call | call period |",
+              "|---|---|---|---|---|---|---|---|---|"]
+    for mode, path, skip in (("eager", eager_csv, skip_eager), ("graph replay", graph_csv,
+                                                                   skip_graph)):
+        c = calls(path)[skip: skip + steps]
+        med = lambda v: statistics.median(v) if v else float("nan")
+        dur = [med([x[j][1] - x[j][0] for x in c]) for j in range(3)]
+        g1 = med([x[1][0] - x[0][1] for x in c])
+        g2 = med([x[2][0] - x[1][1] for x in c])
+        g3 = med([c[i + 1][0][0] - c[i][2][1] for i in range(len(c) - 1)])
+        per = med([c[i + 1][0][0] - c[i][0][0] for i in range(len(c) - 1)])
+        lines.append(f"| {mode} | {len(c)} | {dur[0]:.2f} | {dur[1]:.2f} | {dur[2]:.2f} | "
+                     f"{g1:.2f} | {g2:.2f} | {g3:.2f} | {per:.2f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_stats(csv_path, out_md, command):
     rows = list(csv.DictReader(open(csv_path)))
     out = ["# rocprofv3 kernel statistics", "",
@@ -657,9 +774,9 @@ def summarize_counters(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, cal_m
                  f"# each scaled by the same counter on a plain {cal_mib} MiB device copy",
                  "# Commands (from the repository root):",
                  f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d {run_dir(fetch_csv)} -o run -- "
-                 "python -u bench.py --no-cpu-baseline --steps 3 --warmup 1",
+                 f"python -u bench.py {COUNTER_RUN_ARGS}",
                  f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d {run_dir(write_csv)} -o run -- "
-                 "python -u bench.py --no-cpu-baseline --steps 3 --warmup 1",
+                 f"python -u bench.py {COUNTER_RUN_ARGS}",
                  f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d {run_dir(cal_fetch_csv)} -o run -- "
                  f"python -u bench.py --copy-calibration {cal_mib} --steps 3 --warmup 1",
                  f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d {run_dir(cal_write_csv)} -o run -- "
@@ -1203,11 +1320,23 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--summarize-stats", nargs="+", metavar="ARG")
     ap.add_argument("--summarize-counters", nargs=6, metavar="ARG")
+    ap.add_argument("--summarize-memory", nargs="+", metavar="ARG",
+                    help="OUT.md COMMANDS CSV...: memory-side counter summary")
+    ap.add_argument("--summarize-trace", nargs=7, metavar="ARG",
+                    help="OUT.md EAGER_CSV GRAPH_CSV SKIP_EAGER SKIP_GRAPH STEPS COMMANDS")
     args = ap.parse_args()
 
     if args.summarize_stats:
         summarize_stats(args.summarize_stats[0], args.summarize_stats[1],
                         " ".join(args.summarize_stats[2:]))
+        return
+    if args.summarize_memory:
+        a = args.summarize_memory
+        summarize_memory(a[0], a[2:], a[1])
+        return
+    if args.summarize_trace:
+        a = args.summarize_trace
+        summarize_trace(a[0], a[1], a[2], int(a[3]), int(a[4]), int(a[5]), a[6])
         return
     if args.summarize_counters:
         a = args.summarize_counters

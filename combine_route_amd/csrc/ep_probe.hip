@@ -24,6 +24,8 @@ constexpr int kLoad = 2;        // nt: loads stream past the caches
 constexpr int kGatherStore = 2; // the combine's stores stream
 constexpr int kCopyStore = 0;   // the copies' stores do not
 
+// One instance per kind (EP_PROBE_*), so profiles name the pattern.
+template <int KIND>
 __global__ __launch_bounds__(1024) void ep_probe_kernel(ProbeArgs a)
 {
     const int lane = threadIdx.x & (kWave - 1);
@@ -42,14 +44,14 @@ __global__ __launch_bounds__(1024) void ep_probe_kernel(ProbeArgs a)
     // first entry < 0
     int32_t ent = -1;
     int n = 0;
-    if (a.kind == EP_PROBE_FANOUT || a.kind == EP_PROBE_GATHER) {
+    if constexpr (KIND == EP_PROBE_FANOUT || KIND == EP_PROBE_GATHER) {
         ent = lane < a.stride ? a.map[row * a.stride + lane] : -1;
         const uint64_t neg = __ballot(ent < 0);
         n = neg ? (int)__builtin_ctzll(neg) : kWave;
         n = min(n, a.stride);
     }
 
-    if (a.kind == EP_PROBE_READ) {
+    if constexpr (KIND == EP_PROBE_READ) {
         const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.src + row * a.row_bytes, a.row_bytes);
         uint32_t acc = 0;
         for (int v0 = vbeg; v0 < vend; v0 += kWave * kVpl) {
@@ -70,7 +72,7 @@ __global__ __launch_bounds__(1024) void ep_probe_kernel(ProbeArgs a)
             reinterpret_cast<uint32_t*>(a.dst)[flat] = acc;
         return;
     }
-    if (a.kind == EP_PROBE_WRITE) {
+    if constexpr (KIND == EP_PROBE_WRITE) {
         const __amdgpu_buffer_rsrc_t rd = row_rsrc(a.dst + row * a.row_bytes, a.row_bytes);
         for (int vv = vbeg + lane; vv < vend; vv += kWave) {
             const u32x4 w = {(uint32_t)row, (uint32_t)vv, 0u, 0u};
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(1024) void ep_probe_kernel(ProbeArgs a)
         }
         return;
     }
-    if (a.kind == EP_PROBE_COPY || a.kind == EP_PROBE_FANOUT) {
+    if constexpr (KIND == EP_PROBE_COPY || KIND == EP_PROBE_FANOUT) {
         const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.src + row * a.row_bytes, a.row_bytes);
         for (int v0 = vbeg; v0 < vend; v0 += kWave * kVpl) {
             u32x4 v[kVpl];
@@ -88,10 +90,10 @@ __global__ __launch_bounds__(1024) void ep_probe_kernel(ProbeArgs a)
                 if (vv < vend)
                     v[u] = bload16<kLoad>(rs, (uint32_t)vv * 16u);
             }
-            const int nd = a.kind == EP_PROBE_COPY ? 1 : n;
+            const int nd = KIND == EP_PROBE_COPY ? 1 : n;
             for (int i = 0; i < nd; ++i) {
                 int64_t d = row;
-                if (a.kind == EP_PROBE_FANOUT) {
+                if constexpr (KIND == EP_PROBE_FANOUT) {
                     d = __builtin_amdgcn_readlane(ent, i);
                     if (d >= a.map_rows)
                         continue;
@@ -107,6 +109,8 @@ __global__ __launch_bounds__(1024) void ep_probe_kernel(ProbeArgs a)
         }
         return;
     }
+    if constexpr (KIND != EP_PROBE_GATHER)
+        return;
     // EP_PROBE_GATHER: bf16 rows, FP32 sum in list order from the first row,
     // round to nearest even once
     const __amdgpu_buffer_rsrc_t rd = row_rsrc(a.dst + row * a.row_bytes, a.row_bytes);
@@ -167,7 +171,13 @@ hipError_t launch_probe(const ProbeArgs& a, int waves, hipStream_t s)
         return hipSuccess;
     const dim3 block((unsigned)(waves * kWave));
     const dim3 grid((unsigned)((waves_total + waves - 1) / waves));
-    hipLaunchKernelGGL(ep_probe_kernel, grid, block, 0, s, a);
+    switch (a.kind) {
+    case EP_PROBE_READ: hipLaunchKernelGGL(ep_probe_kernel<EP_PROBE_READ>, grid, block, 0, s, a); break;
+    case EP_PROBE_WRITE: hipLaunchKernelGGL(ep_probe_kernel<EP_PROBE_WRITE>, grid, block, 0, s, a); break;
+    case EP_PROBE_COPY: hipLaunchKernelGGL(ep_probe_kernel<EP_PROBE_COPY>, grid, block, 0, s, a); break;
+    case EP_PROBE_FANOUT: hipLaunchKernelGGL(ep_probe_kernel<EP_PROBE_FANOUT>, grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL(ep_probe_kernel<EP_PROBE_GATHER>, grid, block, 0, s, a); break;
+    }
     return hipGetLastError();
 }
 
