@@ -48,7 +48,8 @@ EXPORTED = ("ep_workspace_bytes", "ep_plan_create", "ep_plan_destroy", "ep_dispa
             "ep_expert_workspace_bytes", "ep_expert_plan_create", "ep_expert_plan_destroy",
             "ep_convert_dispatch_output", "ep_convert_combine_input", "ep_quantize_rows",
             "ep_dispatch_standard_moe", "ep_combine_standard_moe", "ep_probe_pattern",
-            "ep_probe_forward_map")
+            "ep_probe_forward_map", "ep_plan_static")
+EP_STATIC_SCRATCH_BYTES = 4 << 20
 EP_PROBE_READ, EP_PROBE_WRITE, EP_PROBE_COPY, EP_PROBE_FANOUT, EP_PROBE_GATHER = range(5)
 
 
@@ -132,6 +133,7 @@ def load():
     lib.ep_workspace_bytes.restype = Z
     lib.ep_plan_create.argtypes = [P(EpConfig), V, Z, P(V)]
     lib.ep_plan_destroy.argtypes = [V]
+    lib.ep_plan_static.argtypes = [P(EpConfig), P(V)]
     lib.ep_dispatch.argtypes = [V, P(EpDispatchArgs), V]
     lib.ep_combine.argtypes = [V, P(EpCombineArgs), V]
     lib.ep_get_src_token_pos.argtypes = [V, ctypes.c_int32, P(V)]
@@ -255,6 +257,15 @@ def ep_plan_create(cfg: EpConfig, workspace: torch.Tensor) -> int:
     out = ctypes.c_void_p()
     _check("ep_plan_create", load().ep_plan_create(
         ctypes.byref(cfg), ws, workspace.numel() * workspace.element_size(), ctypes.byref(out)))
+    return out.value
+
+
+def ep_plan_static(cfg: EpConfig) -> int:
+    """ep_plan_static(): the current device's plan over the library's static
+    scratch (no allocation). Every call returns the same plan, reset to cfg;
+    calls that overlap on one device race (include/ep.h)."""
+    out = ctypes.c_void_p()
+    _check("ep_plan_static", load().ep_plan_static(ctypes.byref(cfg), ctypes.byref(out)))
     return out.value
 
 

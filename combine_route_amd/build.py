@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libcombine_route_amd.so")
 SOURCES = [os.path.join(PKG, "csrc", f)
            for f in ("ep_plan.cpp", "ep_kernels.hip", "ep_expert.hip", "ep_wire.hip",
-                     "ep_standard.hip", "ep_probe.hip")]
+                     "ep_standard.hip", "ep_probe.hip", "ep_static.hip")]
 ARCH = "gfx950"
 
 FLAGS = [

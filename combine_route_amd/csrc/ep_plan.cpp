@@ -21,6 +21,7 @@
 #include <vector>
 
 #include "ep_kernels.h"
+#include "ep_static.h"
 
 namespace {
 
@@ -201,6 +202,7 @@ struct ep_plan {
     Timer timers[kTimedKernels];
     uint64_t dispatch_gen = 0;  // successful dispatches so far
     int experts = 0;            // live expert plans made from this plan
+    bool is_static = false;     // one of the per-device plans of ep_plan_static
 };
 
 // Workspace of an expert plan of capacity cap: per-tile expert counts and
@@ -613,9 +615,16 @@ int ep_plan_destroy(ep_plan_t* p)
             rc = fail(EP_ERR_HIP, "hipStreamSynchronize before destroy: %s", hipGetErrorString(e));
     }
     timers_destroy(p);
-    delete p;
+    if (p->is_static) {          // the library's own object: emptied, not freed
+        p->dispatched = p->launched = false;
+        p->last_stream = nullptr;
+    } else {
+        delete p;
+    }
     return rc == EP_OK ? ok() : rc;
 }
+
+
 
 int ep_dispatch(ep_plan_t* p, const ep_dispatch_args_t* a, void* stream_ptr)
 {
@@ -1461,3 +1470,56 @@ int ep_plan_kernel_time(ep_plan_t* p, int kernel, int32_t* count, double* total_
 }
 
 }  // extern "C"
+
+namespace ep {
+
+int set_error(int code, const char* msg) { return fail(code, "%s", msg); }
+
+// The per-device plans of ep_plan_static, over the library's static scratch.
+ep_plan g_static_plans[kMaxDevices];
+
+int static_plan_check(const ep_config_t* cfg, size_t scratch_bytes)
+{
+    Shape s;
+    const int rc = check_config(cfg, &s);
+    if (rc != EP_OK)
+        return rc;
+    if (s.total > scratch_bytes)
+        return fail(EP_ERR_SIZE, "this configuration needs a %zu-byte workspace; the static "
+                    "scratch of ep_plan_static holds %zu bytes (use ep_plan_create with a "
+                    "workspace of ep_workspace_bytes())", s.total, scratch_bytes);
+    return EP_OK;
+}
+
+int static_plan_reset(const ep_config_t* cfg, void* scratch, size_t scratch_bytes, int device,
+                      ep_plan_t** out)
+{
+    const int rc = static_plan_check(cfg, scratch_bytes);
+    if (rc != EP_OK)
+        return rc;
+    if (device < 0 || device >= kMaxDevices)
+        return fail(EP_ERR_ARG, "device %d: ep_plan_static serves devices 0..%d", device,
+                    kMaxDevices - 1);
+    ep_plan* p = &g_static_plans[device];
+    if (p->experts > 0)
+        return fail(EP_ERR_STATE, "%d expert plan(s) made from this device's static plan still "
+                    "exist: destroy them first", p->experts);
+    Shape s;
+    check_config(cfg, &s);
+    timers_destroy(p);
+    p->cfg = *cfg;
+    p->s = s;
+    p->ws = static_cast<uint8_t*>(scratch);
+    p->dispatched = false;
+    std::memset(p->last_ntok, 0, sizeof p->last_ntok);
+    p->last_stream = nullptr;
+    p->launched = false;
+    p->launch = ep_launch_t{};
+    p->timing = false;
+    p->dispatch_gen = 0;
+    p->is_static = true;
+    *out = p;
+    return ok();
+}
+
+}  // namespace ep

@@ -160,8 +160,31 @@ int ep_plan_create(const ep_config_t *cfg, void *workspace, size_t workspace_byt
 /* Destroy a plan: waits for the last stream the plan launched on, then frees
  * the plan's host state. The caller frees the workspace afterwards. NULL is a
  * no-op returning EP_OK. EP_ERR_STATE (nothing freed) while expert plans made
- * from it exist. EP_ERR_HIP if that wait fails (the plan is freed anyway). */
+ * from it exist. EP_ERR_HIP if that wait fails (the plan is freed anyway).
+ * A plan of ep_plan_static is waited for and emptied, not freed. */
 int ep_plan_destroy(ep_plan_t *plan);
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Like
+ * ep_plan_create, but the plan's workspace is the library's own static
+ * device array of EP_STATIC_SCRATCH_BYTES (4 MiB; each GPU the library runs
+ * on holds one until the process ends), and the plan object is the library's
+ * too: one per device, the current device's, reset to cfg by each call. No
+ * device or host memory is allocated. The plan serves the current device
+ * only; use it with ep_dispatch, ep_combine and the other calls as any plan.
+ * Every call on a device returns that device's one plan and shares its one
+ * scratch array, whose contents the last call left (nothing in it needs to
+ * start at zero): calls of two threads, or work of two streams, that overlap
+ * on one device race, so the caller orders them (one stream, or its own
+ * events), and a new ep_plan_static call ends the previous plan's state.
+ * Errors: EP_ERR_NULL (cfg or out NULL), EP_ERR_ARG (cfg invalid, or a device
+ * number past 63), EP_ERR_SIZE (cfg needs a workspace larger than the static
+ * array: ep_workspace_bytes(cfg) > EP_STATIC_SCRATCH_BYTES), EP_ERR_STATE
+ * (expert plans made from this device's static plan still exist), EP_ERR_HIP
+ * (the device or the array's address could not be had). Checks of cfg come
+ * first and make no HIP call. */
+#define EP_STATIC_SCRATCH_BYTES ((size_t)4 << 20)
+int ep_plan_static(const ep_config_t *cfg, ep_plan_t **out);
 
 /* Dispatch arguments. Device pointers are caller-owned, 16-byte aligned, and
  * laid out rank-major with the rank stride fixed by M (not by T_r):

@@ -43,7 +43,7 @@ def header_functions():
 
 def test_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     assert sorted(cra.EXPORTED) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -762,3 +762,21 @@ def test_probe_rejects_before_launch(lib):
     p = ctypes.c_void_p()
     s = ctypes.c_int32()
     assert lib.ep_probe_forward_map(None, ctypes.byref(p), ctypes.byref(s)) == cra.EP_ERR_NULL
+
+
+def test_static_plan_rejects_what_does_not_fit(lib):
+    """ep_plan_static checks the configuration and the static scratch's size
+    before any HIP call: a workspace past EP_STATIC_SCRATCH_BYTES is refused
+    with EP_ERR_SIZE, an invalid configuration with EP_ERR_ARG."""
+    big = cra.make_config(8, 7168, 16384, 32, 8, "bf16")
+    assert cra.ep_workspace_bytes(big) > cra.EP_STATIC_SCRATCH_BYTES
+    out = ctypes.c_void_p()
+    assert lib.ep_plan_static(ctypes.byref(big), ctypes.byref(out)) == cra.EP_ERR_SIZE
+    assert "static scratch" in cra.ep_last_error()
+    assert out.value is None
+    bad = cra.make_config(0, 7168, 64, 32, 8, "bf16")
+    assert lib.ep_plan_static(ctypes.byref(bad), ctypes.byref(out)) == cra.EP_ERR_ARG
+    assert lib.ep_plan_static(None, ctypes.byref(out)) == cra.EP_ERR_NULL
+    ok = cra.make_config(8, 7168, 4096, 32, 8, "bf16")
+    assert cra.ep_workspace_bytes(ok) <= cra.EP_STATIC_SCRATCH_BYTES
+    assert lib.ep_plan_static(ctypes.byref(ok), None) == cra.EP_ERR_NULL
