@@ -293,8 +293,11 @@ __global__ __launch_bounds__(1024) void ex_copy_kernel(ExpertArgs a)
         const int r = r_lo + wave + (it / nch) * nwaves;
         const int v0 = vbeg + (it % nch) * kWave * VPL;
         const int n = uniform(s_n[r]);
+        // lane i < n: the packed row of the row's i-th kept expert, read
+        // from LDS for all of them at once
+        const int32_t prow = lane < n ? s_p[r][lane] : 0;
         for (int i = 0; i < n; ++i) {
-            const int64_t gi = uniform(s_p[r][i]);
+            const int64_t gi = __builtin_amdgcn_readlane(prow, i);
             const __amdgpu_buffer_rsrc_t rd = row_rsrc(a.px + gi * row_bytes, row_bytes);
 #pragma unroll
             for (int u = 0; u < VPL; ++u) {

@@ -243,6 +243,9 @@ __global__ __launch_bounds__(1024) void sx_copy_kernel(StandardArgs a)
         const int t = t_lo + wave + (it / nch) * nwaves;
         const int v0 = vbeg + (it % nch) * kWave * VPL;
         const int n = uniform(s_n[t]);
+        // lane i < n: the packed row of the token's i-th kept expert, read
+        // from LDS for all of them at once
+        const int32_t prow = lane < n ? s_p[t][lane] : 0;
         u32x2 c[kCast ? VPL : 1];
         if constexpr (kCast) {
 #pragma unroll
@@ -250,7 +253,7 @@ __global__ __launch_bounds__(1024) void sx_copy_kernel(StandardArgs a)
                 c[u] = cast_e4m3(v[u], a.cast);
         }
         for (int i = 0; i < n; ++i) {
-            const int64_t gi = uniform(s_p[t][i]);
+            const int64_t gi = __builtin_amdgcn_readlane(prow, i);
             const __amdgpu_buffer_rsrc_t rd =
                 row_rsrc(a.px + gi * a.out_row_bytes, a.out_row_bytes);
 #pragma unroll

@@ -267,6 +267,47 @@ def test_wire_decode_of_every_code(name):
     op.close()
 
 
+@pytest.mark.parametrize("name", list(WIRES))
+def test_wire_decode_of_every_scale(name):
+    """Every scale a quantizer of finite inputs can write, each on its own
+    block, through the combine's decoder: MXFP4 E8M0 codes 0 to 254 (code 0
+    is 2^-127, a subnormal FP32 scale) over all 256 byte values of element
+    codes; FP8 block-128 scales 2^-149 (the smallest subnormal) to 2^127 and
+    subnormal, normal and odd-significand values. Bit for bit against the
+    oracle's decode (NaN codes: any NaN)."""
+    cw, ow = WIRES[name]
+    if cw == cra.EP_WIRE_MXFP4:
+        H = 32 * 255
+        ys = np.arange(255, dtype=np.uint8).reshape(1, 1, H // 32)
+        y = np.tile(np.arange(256, dtype=np.uint8), H // 2 // 256 + 1)[:H // 2].reshape(1, 1, H // 2)
+    else:
+        e = np.arange(-149, 128, 4)
+        sc = np.concatenate([np.ldexp(1.0, e), np.ldexp(1.5, e[::3]), [3.0e-39, 1.17e-38, 0.7,
+                                                                      1.2345678]])
+        H = 128 * len(sc)
+        ys = sc.astype(np.float32).reshape(1, 1, len(sc))
+        y = np.tile(np.arange(256, dtype=np.uint8), H // 256 + 1)[:H].reshape(1, 1, H)
+    _say(f"[case] every scale {name} H={H}")
+    wl = workloads.custom(f"wire_scales_{name}", 1, 1, H, 1, 4, "bf16", seed_index=833)
+    inp = workloads.make_inputs(wl)
+    inp["ntok"] = [1]
+    ref = oracle_dispatch(wl, inp)
+    cfg = cra.make_config(1, H, 1, 4, 1, "bf16", "bf16", combine_wire=cw)
+    op = cra.EpDispatchCombineOp(cfg, with_weights=False)
+    gpu_dispatch(op, dict(inp, w=None))
+    out, _ = op.combine(torch.from_numpy(np.ascontiguousarray(y)).cuda(), None,
+                        y_scales=torch.from_numpy(np.ascontiguousarray(ys)).cuda())
+    torch.cuda.synchronize()
+    ro = oracle.combine_wire(1, 1, 1, H, oracle.BF16, ow, [1], ref["fwd"], y, ys)
+    g = out.view(torch.int16).cpu().numpy().view(np.uint16)[0, 0]
+    r = ro[0, 0]
+    nan_g = ((g & 0x7F80) == 0x7F80) & ((g & 0x7F) != 0)
+    nan_r = ((r & 0x7F80) == 0x7F80) & ((r & 0x7F) != 0)
+    assert np.array_equal(nan_g, nan_r)
+    assert np.array_equal(g[~nan_g], r[~nan_r])
+    op.close()
+
+
 def test_graph_replay_of_dispatch_quantize_and_wire_combine():
     """Dispatch, the send-side quantizer over the received rows (row counts on
     the device) and the MXFP4 wire combine captured in one HIP graph;
