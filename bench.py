@@ -1024,6 +1024,108 @@ def measure_small_workloads(args, cra, torch, np):
     return out
 
 
+def placement_states(args):
+    """The headline's dispatch copy and combine, per call, in four
+    placements of the same buffers in one process: allocated fresh (A);
+    again after a cast op of the same shape was allocated, used and released
+    (B); again with nothing in between (C); after another such cast op (D).
+    Prints one line a call; under rocprofv3 --pmc the calls' counters are
+    told apart by their order."""
+    import torch
+
+    import combine_route_amd as cra
+    import workloads
+
+    wl = workloads.WORKLOADS[workloads.HEADLINE]
+    W, M, k, H, Er = wl.world_size, wl.max_tokens, wl.topk, wl.hidden, wl.experts_per_rank
+    inp = workloads.make_inputs(wl)
+    ntok = inp["ntok"]
+    x, idx, w = inp["x"].cuda(), inp["idx"].cuda(), inp["w"].cuda()
+    stream = torch.cuda.current_stream()
+
+    def phase(tag):
+        op = cra.EpDispatchCombineOp(cra.make_config(W, H, M, Er, k, "bf16", "bf16"))
+        cra.ep_plan_set_timing(op.plan, True)
+        prev = (0.0, 0.0)
+        for i in range(args.steps):
+            op.dispatch(ntok, x, idx, w, stream=stream)
+            op.combine(op.out_x, op.out_weights, stream=stream)
+            torch.cuda.synchronize()
+            # the plan's timers add up: this call's durations are the increments
+            c1 = cra.ep_plan_kernel_time(op.plan, cra.EP_KERNEL_COPY)[1]
+            c2 = cra.ep_plan_kernel_time(op.plan, cra.EP_KERNEL_COMBINE)[1]
+            print(json.dumps({"phase": tag, "call": i, "copy_us": round((c1 - prev[0]) * 1e3, 1),
+                              "combine_us": round((c2 - prev[1]) * 1e3, 1)}), flush=True)
+            prev = (c1, c2)
+        op.close()
+        del op
+        torch.cuda.empty_cache()
+
+    def perturb():
+        op = cra.EpDispatchCombineOp(cra.make_config(W, H, M, Er, k, "fp8", "bf16",
+                                                     dispatch_cast="bf16"))
+        for _ in range(3):
+            op.dispatch(ntok, x, idx, w, stream=stream)
+        torch.cuda.synchronize()
+        op.close()
+        del op
+        torch.cuda.empty_cache()
+
+    phase("A")
+    perturb()
+    phase("B")
+    phase("C")
+    perturb()
+    phase("D")
+
+
+def summarize_placement(out_md, timing_log, csv_paths, command, calls):
+    """Per call of placement_states: kernel times and memory-side counters."""
+    import re
+
+    times = [json.loads(l) for l in open(timing_log) if l.startswith("{")]
+    per = {}
+    for path in csv_paths:
+        for r in csv.DictReader(open(path)):
+            n = r["Kernel_Name"]
+            kind = ("copy" if re.search(r"ep_copy_kernel<8, 8, true, false, false>", n) else
+                    "combine" if re.search(r"ep_combine_kernel<8, 2, 0, true>", n) else None)
+            if kind:
+                key = (path, int(r["Dispatch_Id"]), kind)
+                per.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    lines = ["# The headline kernels in four placements of the same buffers", "",
+             f"Kernel sources sha256[:16]: {kernel_source_hash()}", "",
+             "Commands (from the repository root):", ""]
+    lines += ["    " + c for c in command.split(" ;; ")]
+    lines += ["", "Phases: A allocated fresh; B after a cast op of the same shape was "
+              "allocated, used and released; C allocated again; D after another cast op. "
+              "Kernel times from the library's HIP events (no profiler); counters from the "
+              "profiled runs, the same calls in the same order.", "",
+              "| phase | call | copy µs | combine µs | copy: read latency (cycles) | "
+              "copy: write credit stall / TCC cycles | copy: TCC cycles (M) |",
+              "|---|---|---|---|---|---|---|"]
+    for kind in ("copy",):
+        byfile = {}
+        for (path, d, kd), v in sorted(per.items()):
+            if kd == kind:
+                byfile.setdefault(path, []).append(v)
+    merged = [dict() for _ in range(len(times))]
+    for path, vs in byfile.items():
+        for i, v in enumerate(vs[:len(times)]):
+            merged[i].update(v)
+    for t, m in zip(times, merged):
+        lat = (m["TCC_EA0_RDREQ_LEVEL_sum"] / m["TCC_EA0_RDREQ_sum"]
+               if m.get("TCC_EA0_RDREQ_sum") else float("nan"))
+        st = (m["TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum"] / m["TCC_CYCLE_sum"]
+              if m.get("TCC_CYCLE_sum") else float("nan"))
+        cyc = m.get("TCC_CYCLE_sum", float("nan")) / 1e6
+        lines.append(f"| {t['phase']} | {t['call']} | {t['copy_us']} | {t['combine_us']} | "
+                     f"{lat:.0f} | {st:.3f} | {cyc:.1f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def rocprof_frac(workload, kernel_pattern, nbytes):
     """The dominant kernel's average duration in the committed rocprofv3
     summary of this workload, taken on the current kernel sources, and the
@@ -1320,6 +1422,10 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--summarize-stats", nargs="+", metavar="ARG")
     ap.add_argument("--summarize-counters", nargs=6, metavar="ARG")
+    ap.add_argument("--placement-states", action="store_true",
+                    help="the headline kernels, per call, in four placements of their buffers")
+    ap.add_argument("--summarize-placement", nargs="+", metavar="ARG",
+                    help="OUT.md TIMING_LOG COMMANDS CSV...")
     ap.add_argument("--summarize-memory", nargs="+", metavar="ARG",
                     help="OUT.md COMMANDS CSV...: memory-side counter summary")
     ap.add_argument("--summarize-trace", nargs=7, metavar="ARG",
@@ -1329,6 +1435,10 @@ def main():
     if args.summarize_stats:
         summarize_stats(args.summarize_stats[0], args.summarize_stats[1],
                         " ".join(args.summarize_stats[2:]))
+        return
+    if args.summarize_placement:
+        a = args.summarize_placement
+        summarize_placement(a[0], a[1], a[3:], a[2], None)
         return
     if args.summarize_memory:
         a = args.summarize_memory
@@ -1346,6 +1456,9 @@ def main():
         print(f"bench.py: --gpus {args.gpus} is not supported: all virtual expert-parallel "
               "ranks run on one GPU, and only --gpus 1 is measured.", file=sys.stderr)
         sys.exit(2)
+    if args.placement_states:
+        placement_states(args)
+        return
     if args.copy_calibration:
         import torch
 

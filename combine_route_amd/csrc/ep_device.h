@@ -254,7 +254,9 @@ __device__ __forceinline__ void decode_group(const u32x2& c, uint32_t sbits,
             f[4 * d + 3] = hi.y * s;
         }
     } else {
-        const float s = __builtin_ldexpf(1.0f, (int)(sbits & 0xFFu) - 127);
+        // 2^(code - 127) as 2^-127 (a subnormal) scaled by 2^code: one
+        // exact ldexp, no bias subtraction
+        const float s = __builtin_ldexpf(0x1p-127f, (int)(sbits & 0xFFu));
         const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[0], s, 0);
         const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[0], s, 1);
         const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[0], s, 2);
