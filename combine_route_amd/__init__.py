@@ -77,7 +77,7 @@ class EpLaunch(ctypes.Structure):
         "tile_tokens", "dispatch_waves", "dispatch_row_split", "combine_waves",
         "combine_row_split", "cache_policy", "layout", "expert_waves", "expert_row_split",
         "expert_combine_waves", "expert_combine_row_split", "expert_cache_policy",
-        "expert_token_split")]
+        "expert_token_split", "dispatch_token_split")]
 
 
 class EpConvertDispatchArgs(ctypes.Structure):

@@ -77,6 +77,11 @@ struct CopyArgs {
     int32_t M, k, Er, E, P, WM;
     int32_t tile_stride;
     int32_t cast;                // 0: rows copied; 1 / 2: bf16 / fp16 x cast to E4M3
+    // Blocks: one per (tile, token share, row piece), numbered in that order
+    // with the piece fastest, so blocks started together touch neighbouring
+    // rows. A share is ceil(tile_tokens / token_split) consecutive tokens.
+    int32_t pieces;              // row pieces: ceil(row_vecs / piece_vecs)
+    int32_t token_split;         // token shares a tile
 };
 
 struct CombineArgs {
@@ -215,8 +220,8 @@ hipError_t launch_route(const RouteArgs& a, const TileMap& tm, hipStream_t s);
 hipError_t launch_scan(const ScanArgs& a, int W, hipStream_t s);
 // stream: true = streaming cache policy (rows bypass the caches), false =
 // cache-allocating moves.
-hipError_t launch_copy(const CopyArgs& a, const TileMap& tm, int waves, int row_split,
-                       bool stream, hipStream_t s);
+hipError_t launch_copy(const CopyArgs& a, const TileMap& tm, int waves, bool stream,
+                       hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, const TokenMap& tk, int dtype, int waves,
                           int row_split, bool stream, hipStream_t s);
 

@@ -292,18 +292,23 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
     const int nwaves = blockDim.x / kWave;
-    const int g = blockIdx.x;
-    const int piece = blockIdx.y;
+    const int piece = blockIdx.x % a.pieces;
+    const int share = (blockIdx.x / a.pieces) % a.token_split;
+    const int g = blockIdx.x / a.pieces / a.token_split;
     const int r = rank_of_tile(tm, g);
     const int t0 = (g - tm.tile_start[r]) * tm.tile_tokens;
     const int cnt = min(tm.tile_tokens, tm.ntok[r] - t0);
+    // this block's tokens of the tile: [tb, te)
+    const int per_share = (tm.tile_tokens + a.token_split - 1) / a.token_split;
+    const int tb = min(cnt, share * per_share);
+    const int te = min(cnt, tb + per_share);
 
-    // This wave's items: tokens wave, wave + nwaves, ... of the tile, each cut
-    // into nch chunks of its row piece [vbeg, vend).
+    // This wave's items: tokens tb + wave, tb + wave + nwaves, ... of the
+    // tile, each cut into nch chunks of its row piece [vbeg, vend).
     const int vbeg = piece * a.piece_vecs;
     const int vend = min(a.row_vecs, vbeg + a.piece_vecs);
     const int nch = (vend - vbeg + kWave * VPL - 1) / (kWave * VPL);
-    const int ntw = wave < cnt ? (cnt - wave + nwaves - 1) / nwaves : 0;
+    const int ntw = wave < te - tb ? (te - tb - wave + nwaves - 1) / nwaves : 0;
     const int items = ntw * nch;
     const bool meta = piece == 0;
     const uint32_t in_bytes = (uint32_t)a.row_vecs * 16u;                  // input row
@@ -395,7 +400,7 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
     auto load_item = [&](int it, CopyItem<VPL>& I) {
         const int q = it / nch;
         const int c = it - q * nch;
-        const int64_t src = (int64_t)r * a.M + t0 + wave + q * nwaves;
+        const int64_t src = (int64_t)r * a.M + t0 + tb + wave + q * nwaves;
         load_payload(src, vbeg + c * kWave * VPL, I.v);
         if (meta && c == 0)
             load_meta(src, I.e, I.wv, I.sc);
@@ -403,7 +408,7 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
     auto store_item = [&](int it, const CopyItem<VPL>& I) {
         const int q = it / nch;
         const int c = it - q * nch;
-        const int tok = wave + q * nwaves;
+        const int tok = tb + wave + q * nwaves;
         store_payload(tok, vbeg + c * kWave * VPL, I.v);
         if (meta && c == 0)
             store_meta(tok, I.e, I.wv, I.sc);
@@ -447,7 +452,7 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
             }
             __syncthreads();
         }
-        const bool first = g == 0 && piece == 0;
+        const bool first = blockIdx.x == 0;
         for (int d = wave; d < tm.W; d += nwaves) {
             const int32_t* col = a.tile_counts + (int64_t)d * a.tile_stride;
             int32_t before = 0, all = 0;
@@ -522,7 +527,7 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
         route_tile();
         __syncthreads();
         if (meta) {
-            for (int tok = wave; tok < cnt; tok += nwaves) {
+            for (int tok = tb + wave; tok < te; tok += nwaves) {
                 int32_t e = 0;
                 float wv = 0.0f;
                 uint32_t sc = 0;
@@ -530,7 +535,7 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
                 store_meta(tok, e, wv, sc);
             }
         }
-        for (int tok = wave; tok < cnt; tok += nwaves) {
+        for (int tok = tb + wave; tok < te; tok += nwaves) {
             const int64_t src = (int64_t)r * a.M + t0 + tok;
             for (int v0 = vbeg; v0 < vend; v0 += kWave * VPL) {
                 u32x4 v[VPL];
@@ -674,12 +679,12 @@ hipError_t launch_scan(const ScanArgs& a, int W, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_copy(const CopyArgs& a, const TileMap& tm, int waves, int row_split,
-                       bool stream, hipStream_t s)
+hipError_t launch_copy(const CopyArgs& a, const TileMap& tm, int waves, bool stream,
+                       hipStream_t s)
 {
     if (tm.total_tiles == 0)
         return hipSuccess;
-    const dim3 grid(tm.total_tiles, row_split);
+    const dim3 grid((unsigned)((int64_t)tm.total_tiles * a.token_split * a.pieces));
     const dim3 block(waves * kWave);
     const int per_lane = (a.piece_vecs + kWave - 1) / kWave;
     if (per_lane <= 1)

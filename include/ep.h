@@ -362,8 +362,10 @@ typedef struct ep_launch {
      *                             tokens in ep_dispatch_standard_moe), each
      *                             copying its share of them: 1..64.
      *   Automatic expert_row_split and expert_token_split: a call whose row
-     *   pieces alone give about 1024 copy blocks (512 above top-16) shares no
-     *   tile; a smaller call shares tiles first (at most 64 / expert_waves
+     *   pieces alone give about 1024 copy blocks (512 above top-16) cuts rows
+     *   to reach that and, up to top-16, shares each tile among 64 /
+     *   expert_waves blocks of one row a wave (above top-16 it shares no
+     *   tile); a smaller call shares tiles first (at most 64 / expert_waves
      *   blocks a tile), then cuts rows. ep_plan_get_launch reports the values
      *   of ep_convert_dispatch_output. */
     int32_t expert_waves;
@@ -372,6 +374,22 @@ typedef struct ep_launch {
     int32_t expert_combine_row_split;
     int32_t expert_cache_policy;
     int32_t expert_token_split;
+    /* dispatch_token_split: blocks sharing one routing tile of ep_dispatch,
+     * each copying ceil(tile_tokens / dispatch_token_split) consecutive
+     * tokens of it: 1..64 (values above tile_tokens act as tile_tokens).
+     * Blocks are numbered tile, then share, then row piece, so the blocks
+     * the GPU starts together read and write neighbouring rows. Every block
+     * of a tile routes the whole tile again (its ids only). A launch whose
+     * blocks x dispatch_waves x 64 exceed 2^32 - 1 fails with EP_ERR_ARG.
+     * Automatic dispatch geometry: calls with 16-token tiles (fewer than
+     * 512 tiles of 32 tokens) use 16 waves, no shared tile and rows cut
+     * until the grid has about 1024 blocks; larger calls
+     * cut rows into pieces of at least 7 KB and, up to top-16, share each
+     * tile among blocks of one token a wave (4 waves, 16 with a
+     * dispatch_cast; dispatch_token_split = tile_tokens / dispatch_waves,
+     * recomputed when tile_tokens or dispatch_waves is overridden);
+     * above top-16 they share no tile. */
+    int32_t dispatch_token_split;
 } ep_launch_t;
 
 /* Override (launch != NULL) or reset to automatic (launch == NULL) the plan's

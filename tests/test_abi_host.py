@@ -200,6 +200,20 @@ def test_dispatch_rejects_token_counts(lib):
     lib.ep_plan_destroy(plan)
 
 
+def test_dispatch_rejects_a_copy_grid_past_32_bits(lib):
+    # 8 x 4096 tokens in 16-token tiles: 2048 tiles x 16 shares x 896 row
+    # pieces x 1024 work-items a block is past 2^32; checked before any launch
+    cfg = cra.make_config(8, 7168, 4096, 32, 8)
+    rc, plan = make_plan(lib, cfg)
+    cra.ep_plan_set_launch(plan, dict(tile_tokens=16, dispatch_waves=16, dispatch_row_split=896,
+                                      dispatch_token_split=16))
+    nt = (ctypes.c_int32 * 8)(*([4096] * 8))
+    a, _ = dispatch_args(8, num_tokens=ctypes.cast(nt, ctypes.c_void_p).value)
+    assert lib.ep_dispatch(plan, ctypes.byref(a), None) == cra.EP_ERR_ARG
+    assert "2^32" in cra.ep_last_error()
+    lib.ep_plan_destroy(plan)
+
+
 def test_dispatch_requires_scales_when_configured(lib):
     cfg = cra.make_config(8, 7168, 128, 32, 8, "fp8", "bf16", scale_dim=56)
     rc, plan = make_plan(lib, cfg)
@@ -235,6 +249,10 @@ def test_launch_override_limits_and_auto_geometry(lib):
     auto = cra.ep_plan_get_launch(plan, [4096] * 8)
     assert auto["tile_tokens"] in (16, 32, 64)
     assert 1 <= auto["dispatch_row_split"] <= 7168 * 2 // 16
+    # 512 tiles of 64 tokens: 14 KB rows in two 7 KB pieces, each tile shared
+    # by blocks of 4 waves, one token a wave
+    assert (auto["tile_tokens"], auto["dispatch_waves"], auto["dispatch_token_split"],
+            auto["dispatch_row_split"]) == (64, 4, 16, 2)
     for bad in (dict(tile_tokens=8), dict(dispatch_waves=17), dict(combine_waves=17),
                 dict(dispatch_row_split=7168 * 2 // 16 + 1), dict(combine_row_split=897),
                 dict(cache_policy=3), dict(cache_policy=-1), dict(layout=4), dict(layout=-2)):
@@ -243,6 +261,7 @@ def test_launch_override_limits_and_auto_geometry(lib):
     cra.ep_plan_set_launch(plan, dict(tile_tokens=32, dispatch_waves=2))
     got = cra.ep_plan_get_launch(plan, [4096] * 8)
     assert got["tile_tokens"] == 32 and got["dispatch_waves"] == 2
+    assert got["dispatch_token_split"] == 16  # still one token a wave
     cra.ep_plan_set_launch(plan, None)
     assert cra.ep_plan_get_launch(plan, [4096] * 8) == auto
     small = cra.ep_plan_get_launch(plan, [1] + [0] * 7)
@@ -264,11 +283,14 @@ def test_launch_override_limits_and_auto_geometry(lib):
         cra.ep_plan_get_launch(plan, [4097] + [0] * 7)
     # the expert-major copy (tiles of 64 of the most rows a rank can hold):
     # 8 x 512 tiles, and 8 x 16 tiles x 14 row pieces, reach 1024 blocks
-    # without sharing a tile; 8 x 2 tiles x 14 pieces do not, so small calls
-    # share each tile first, at most one row a wave
-    assert auto["expert_token_split"] == 1 and auto["expert_row_split"] == 1
+    # without sharing a tile, and share each tile among blocks of one row a
+    # wave; 8 x 2 tiles x 14 pieces do not, so small calls share each tile
+    # first, at most one row a wave
+    assert auto["expert_token_split"] == 64 // auto["expert_waves"]
+    assert auto["expert_row_split"] == 1
     mid = cra.ep_plan_get_launch(plan, [128] * 8)
-    assert mid["expert_token_split"] == 1 and mid["expert_row_split"] == 8
+    assert mid["expert_token_split"] == 64 // mid["expert_waves"]
+    assert mid["expert_row_split"] == 8
     for few in ([16] * 8, [1] + [0] * 7):
         dec = cra.ep_plan_get_launch(plan, few)
         assert dec["expert_token_split"] == 64 // dec["expert_waves"]
@@ -278,6 +300,13 @@ def test_launch_override_limits_and_auto_geometry(lib):
     cra.ep_plan_set_launch(plan, dict(expert_token_split=64))
     assert cra.ep_plan_get_launch(plan, [4096] * 8)["expert_token_split"] == 64
     cra.ep_plan_set_launch(plan, None)
+    # small calls share no tile
+    assert cra.ep_plan_get_launch(plan, [16] * 8)["dispatch_token_split"] == 1
+    with pytest.raises(cra.EpError):
+        cra.ep_plan_set_launch(plan, dict(dispatch_token_split=65))
+    cra.ep_plan_set_launch(plan, dict(dispatch_token_split=8))
+    assert cra.ep_plan_get_launch(plan, [4096] * 8)["dispatch_token_split"] == 8
+    cra.ep_plan_set_launch(plan, None)
     lib.ep_plan_destroy(plan)
     # k > 16: the copy blocks cannot route the whole call; few tiles: they scan
     wl = workloads.WORKLOADS["ep4_ragged1024_h2048_fp16_k64"]
@@ -286,6 +315,19 @@ def test_launch_override_limits_and_auto_geometry(lib):
     assert got["layout"] == cra.EP_LAYOUT_SCAN_IN_COPY
     with pytest.raises(cra.EpError):
         cra.ep_plan_set_launch(plan, dict(layout=cra.EP_LAYOUT_IN_COPY))
+    lib.ep_plan_destroy(plan)
+    # a large top-64 call: one block a tile, rows in one 4 KB piece
+    rc, plan = make_plan(lib, cra.make_config(4, 2048, 4096, 64, 64, "fp16", "fp16"))
+    big = cra.ep_plan_get_launch(plan, [4096] * 4)
+    assert (big["tile_tokens"], big["dispatch_token_split"], big["dispatch_row_split"]) == \
+        (32, 1, 1)
+    lib.ep_plan_destroy(plan)
+    # a cast dispatch: 16 waves a block, one token a wave
+    rc, plan = make_plan(lib, cra.make_config(8, 7168, 4096, 32, 8, "fp8", "bf16",
+                                              dispatch_cast="bf16"))
+    cast = cra.ep_plan_get_launch(plan, [4096] * 8)
+    assert (cast["dispatch_waves"], cast["dispatch_token_split"], cast["dispatch_row_split"]) == \
+        (16, 4, 2)
     lib.ep_plan_destroy(plan)
 
 

@@ -79,7 +79,11 @@ def test_cast_dispatch_matches_oracle(src, W, M, H, k, E):
 @pytest.mark.parametrize("launch", [dict(dispatch_row_split=5, dispatch_waves=3),
                                     dict(tile_tokens=64, layout=cra.EP_LAYOUT_SCAN_IN_COPY),
                                     dict(layout=cra.EP_LAYOUT_KERNELS,
-                                         cache_policy=cra.EP_CACHE_STREAM)])
+                                         cache_policy=cra.EP_CACHE_STREAM),
+                                    dict(tile_tokens=64, dispatch_token_split=8,
+                                         dispatch_row_split=2),
+                                    dict(tile_tokens=16, dispatch_token_split=3,
+                                         dispatch_waves=5)])
 def test_cast_geometry_and_scales(launch):
     run_cast_case(4, 200, 1024, 8, 64, "bf16", launch=launch, scale_dim=8, seed=31,
                   tag=f"cast geometry {launch}")

@@ -180,6 +180,12 @@ def test_topk_and_world_sweep(W, k):
     dict(layout=cra.EP_LAYOUT_SCAN_IN_COPY, tile_tokens=64, dispatch_row_split=1),
     dict(layout=cra.EP_LAYOUT_IN_COPY, tile_tokens=32, dispatch_row_split=3),
     dict(layout=cra.EP_LAYOUT_KERNELS, tile_tokens=16, dispatch_row_split=2),
+    dict(tile_tokens=64, dispatch_token_split=8),
+    dict(tile_tokens=32, dispatch_token_split=5, dispatch_row_split=3, dispatch_waves=3),
+    dict(tile_tokens=16, dispatch_token_split=64, dispatch_waves=1),
+    dict(layout=cra.EP_LAYOUT_SCAN_IN_COPY, tile_tokens=64, dispatch_token_split=4,
+         dispatch_row_split=2),
+    dict(layout=cra.EP_LAYOUT_IN_COPY, tile_tokens=32, dispatch_token_split=3),
 ], ids=str)
 def test_geometry_does_not_change_results(launch):
     wl = workloads.custom("geom_ep4_t300_h4096", 4, 300, 4096, 8, 256, "bf16", ragged=True,
@@ -478,6 +484,7 @@ def _random_case(seed):
         launch["dispatch_row_split"] = min(launch["dispatch_row_split"],
                                            H * (1 if dd == "fp8" else 2) // 16)
         launch["combine_row_split"] = min(launch["combine_row_split"], H * 2 // 16)
+        launch["dispatch_token_split"] = int(rng.integers(0, 65))
     return wl, S, sts, launch
 
 
