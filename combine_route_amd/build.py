@@ -17,17 +17,18 @@ ARCH = "gfx950"
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-    # Packed FP32 instructions stay off in the gfx950 code: the compiler would
-    # otherwise pair the combine's FP32 adds into v_pk_add_f32. The feature is
-    # a device feature; -Xarch_device cannot forward -Xclang options, so the
-    # flag reaches the host pass too, which warns that x86 has no such
-    # feature and ignores it. build() checks the device code it links.
-    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fno-fast-math", "-ffp-contract=off",
     "-Wall", "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"),
     "-I", os.path.join(PKG, "csrc"),
 ]
+# Packed FP32 instructions stay off in the gfx950 code: the compiler would
+# otherwise pair the combine's FP32 adds into v_pk_add_f32. The feature is a
+# device feature and is given to the device pass alone: a .hip source is
+# compiled twice, once for gfx950 only (to an offload bundle, with this flag)
+# and once for the host, which embeds that bundle. build() checks the device
+# code it links.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
 def hipcc() -> str:
@@ -84,12 +85,22 @@ def build(verbose: bool = False, extra=()) -> str:
     os.makedirs(objdir, exist_ok=True)
     compile_flags = [f for f in FLAGS if f != "-shared"]
 
-    def compile_one(src):
-        obj = os.path.join(objdir, os.path.basename(src) + ".o")
-        cmd = [hipcc(), *compile_flags, *extra, "-c", "-o", obj, src]
+    def run(cmd):
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
+
+    def compile_one(src):
+        name = os.path.basename(src)
+        obj = os.path.join(objdir, name + ".o")
+        if not src.endswith(".hip"):
+            run([hipcc(), *compile_flags, *extra, "-c", "-o", obj, src])
+            return obj
+        fatbin = os.path.join(objdir, name + ".hipfb")
+        run([hipcc(), *compile_flags, *DEVICE_FLAGS, *extra, "--offload-device-only", "-c",
+             "-o", fatbin, src])
+        run([hipcc(), *compile_flags, *extra, "--offload-host-only",
+             "-Xclang", "-fcuda-include-gpubinary", "-Xclang", fatbin, "-c", "-o", obj, src])
         return obj
 
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as pool:

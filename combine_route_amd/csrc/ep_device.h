@@ -228,6 +228,83 @@ __device__ __forceinline__ void fold_rows(const uint8_t* src, uint32_t row_bytes
     }
 }
 
+// The same fold, row by row: the wave's piece [vbeg, vend) holds at most
+// kWave * R columns, all R of a lane's columns of a row are loaded together,
+// and D rows are in flight (the loads of rows i+1 .. i+D-1 are issued before
+// row i is added). Same additions in the same order, so the same bits as
+// fold_rows. Fewer registers than fold_rows (more waves a SIMD), and a
+// token's pieces, run by neighbouring waves, read each contribution row
+// whole at about the same time.
+constexpr int kStreamDepth = 3;
+
+template <int R, int DT, bool kStream, bool kWeighted = false>
+__device__ __forceinline__ void fold_rows_streamed(const uint8_t* src, uint32_t row_bytes,
+                                                   int32_t gl, int n,
+                                                   __amdgpu_buffer_rsrc_t rdst, int vbeg,
+                                                   int vend, int lane, float gw = 0.0f)
+{
+    constexpr int D = kStreamDepth;
+    float acc[R][8];
+    u32x4 buf[D][R];
+    auto load = [&](int i, u32x4 (&b)[R]) {
+        const int64_t gi = __builtin_amdgcn_readlane(gl, i);
+        const __amdgpu_buffer_rsrc_t ry = row_rsrc(src + gi * row_bytes, row_bytes);
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            const int v = vbeg + u * kWave + lane;
+            if (v < vend)
+                b[u] = bload16<Policy<kStream>::combine_load>(ry, (uint32_t)v * 16u);
+        }
+    };
+    // row i lives in buf[i % D]; the loop runs D rows a pass so that every
+    // buffer index is a constant
+#pragma unroll
+    for (int j = 0; j < D - 1; ++j)
+        if (j < n)
+            load(j, buf[j]);
+    for (int i0 = 0; i0 < n; i0 += D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            const int i = i0 + j;
+            if (i < n) {
+                if (i + D - 1 < n)
+                    load(i + D - 1, buf[(j + D - 1) % D]);
+                float c = 1.0f;
+                if constexpr (kWeighted)
+                    c = __builtin_bit_cast(
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gw), i));
+#pragma unroll
+                for (int u = 0; u < R; ++u) {
+                    float f[8];
+                    widen<DT>(buf[j][u], f);
+                    if (i == 0) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            acc[u][e] = kWeighted ? c * f[e] : f[e];
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            acc[u][e] = kWeighted ? __builtin_fmaf(c, f[e], acc[u][e])
+                                                  : acc[u][e] + f[e];
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        const int v = vbeg + u * kWave + lane;
+        if (v < vend) {
+            if (n == 0) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    acc[u][e] = 0.0f;
+            }
+            bstore16<Policy<kStream>::combine_store>(narrow<DT>(acc[u]), rdst, (uint32_t)v * 16u);
+        }
+    }
+}
+
 // A lane decodes groups of 8 elements, inside one scale block: 8 bytes of
 // FP8 codes (two dwords) or 4 bytes of MXFP4 codes (one dword). Its 8 results
 // are one 16-byte store, so a wave's store covers 1 KiB contiguously.

@@ -434,11 +434,15 @@ template <int G, int U, int DT, bool kStream, bool kWeighted>
 __global__ __launch_bounds__(1024) void ex_combine_kernel(ExpertCombineArgs a)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int q = blockIdx.x * (blockDim.x / kWave) + uniform(threadIdx.x / kWave);
-    const int piece = blockIdx.y;
+    // wave items: (row, piece); piece_inner: piece fastest, so a row's
+    // pieces run in neighbouring waves
+    const uint32_t item = blockIdx.x * (blockDim.x / kWave) + uniform(threadIdx.x / kWave);
+    const uint32_t qu = a.piece_inner ? item / (uint32_t)a.pieces : item;
     const int d = blockIdx.z;
-    if (q >= received(a.recv[d], a.rows))
+    if (qu >= (uint32_t)received(a.recv[d], a.rows))
         return;  // whole waves
+    const int q = (int)qu;
+    const int piece = a.piece_inner ? (int)(item - qu * (uint32_t)a.pieces) : (int)blockIdx.y;
     const int64_t row = (int64_t)d * a.WM + q;
     const int32_t gl = lane < a.Pe ? a.efwd[row * a.Pe + lane] : -1;
     const int n = __popcll(__ballot(gl >= 0));  // entries >= 0 form a prefix
@@ -449,7 +453,12 @@ __global__ __launch_bounds__(1024) void ex_combine_kernel(ExpertCombineArgs a)
     const __amdgpu_buffer_rsrc_t rdst = row_rsrc(a.y + row * row_bytes, row_bytes);
     const int vbeg = piece * a.piece_vecs;
     const int vend = min(a.row_vecs, vbeg + a.piece_vecs);
-    fold_rows<G, U, DT, kStream, kWeighted>(a.py, row_bytes, gl, n, rdst, vbeg, vend, lane, gw);
+    if constexpr (G == 0)
+        fold_rows_streamed<U, DT, kStream, kWeighted>(a.py, row_bytes, gl, n, rdst, vbeg, vend,
+                                                      lane, gw);
+    else
+        fold_rows<G, U, DT, kStream, kWeighted>(a.py, row_bytes, gl, n, rdst, vbeg, vend, lane,
+                                                gw);
 }
 
 // Top-k bucket of the expert kernels: the smallest of 8, 16, 32, 64 >= k.
@@ -556,12 +565,19 @@ hipError_t launch_expert_copy(const ExpertArgs& a, int waves, int row_split, boo
 }
 
 hipError_t launch_expert_combine(const ExpertCombineArgs& a, int W, int dtype, int waves,
-                                 int row_split, bool stream, hipStream_t s)
+                                 bool stream, hipStream_t s)
 {
     if (a.rows == 0)
         return hipSuccess;
-    const dim3 grid((a.rows + waves - 1) / waves, row_split, W);
+    const dim3 grid = a.piece_inner
+                          ? dim3((unsigned)(((int64_t)a.rows * a.pieces + waves - 1) / waves), 1, W)
+                          : dim3((unsigned)((a.rows + waves - 1) / waves), (unsigned)a.pieces, W);
     const dim3 block(waves * kWave);
+    // pieces of up to 2 KB: folded row by row (fold_rows_streamed)
+    if (a.piece_vecs <= kWave)
+        return ex_combine_with<0, 1>(a, dtype, grid, block, stream, s);
+    if (a.piece_vecs <= 2 * kWave)
+        return ex_combine_with<0, 2>(a, dtype, grid, block, stream, s);
     if (a.Pe <= 1)
         return ex_combine_with<1, 4>(a, dtype, grid, block, stream, s);
     if (a.Pe <= 2)

@@ -77,11 +77,14 @@ struct CopyArgs {
     int32_t M, k, Er, E, P, WM;
     int32_t tile_stride;
     int32_t cast;                // 0: rows copied; 1 / 2: bf16 / fp16 x cast to E4M3
-    // Blocks: one per (tile, token share, row piece), numbered in that order
-    // with the piece fastest, so blocks started together touch neighbouring
-    // rows. A share is ceil(tile_tokens / token_split) consecutive tokens.
+    // Blocks: one per (tile, token share, row piece). piece_inner: a 1-D
+    // grid numbered tile, share, piece, the piece fastest, so blocks started
+    // together touch neighbouring rows (calls larger than the GPU holds at
+    // once); otherwise a 2-D grid, x = (tile, share), y = piece. A share is
+    // ceil(tile_tokens / token_split) consecutive tokens.
     int32_t pieces;              // row pieces: ceil(row_vecs / piece_vecs)
     int32_t token_split;         // token shares a tile
+    int32_t piece_inner;
 };
 
 struct CombineArgs {
@@ -92,6 +95,9 @@ struct CombineArgs {
     const int32_t* fwd;          // [W][M][P]
     int32_t row_vecs;            // 8-element (16-byte) vectors per row
     int32_t piece_vecs;          // vectors per row piece
+    int32_t pieces;              // ceil(row_vecs / piece_vecs): a wave each
+    int32_t piece_inner;         // 1: waves numbered (token, piece), piece fastest,
+                                 // in a 1-D grid; 0: grid y = piece
     int32_t M, k, P;
 };
 
@@ -134,6 +140,8 @@ struct ExpertCombineArgs {
     uint8_t* y;                  // [W][WM][H]
     int32_t row_vecs;            // 16-byte vectors per row
     int32_t piece_vecs;
+    int32_t pieces;              // ceil(row_vecs / piece_vecs): a wave each
+    int32_t piece_inner;         // as CombineArgs::piece_inner, rows for tokens
     int32_t WM, Pe;
     int32_t rows;                // most received rows any rank can hold in this call
 };
@@ -176,6 +184,8 @@ struct StandardCombineArgs {
     uint32_t py_row_bytes;       // bytes per wire row (unused without a wire)
     uint32_t py_scale_bytes;     // bytes per wire scale row
     int32_t wire;                // 0, kWireFp8Block128 or kWireMxfp4
+    int32_t pieces;              // ceil(row_vecs / piece_vecs): a wave each
+    int32_t piece_inner;         // as CombineArgs::piece_inner
     int32_t M, k, Er, E;
 };
 
@@ -208,6 +218,8 @@ struct WireCombineArgs {
     const int32_t* fwd;          // [W][M][P]
     int32_t units;               // 16-element units per row (H / 16)
     int32_t piece_units;         // units per row piece: a multiple of 8, <= kWirePieceUnits
+    int32_t pieces;              // ceil(units / piece_units): a wave each
+    int32_t piece_inner;         // as CombineArgs::piece_inner
     uint32_t row_bytes, scale_bytes;
     int32_t M, k, P;
 };
@@ -223,7 +235,7 @@ hipError_t launch_scan(const ScanArgs& a, int W, hipStream_t s);
 hipError_t launch_copy(const CopyArgs& a, const TileMap& tm, int waves, bool stream,
                        hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, const TokenMap& tk, int dtype, int waves,
-                          int row_split, bool stream, hipStream_t s);
+                          bool stream, hipStream_t s);
 
 hipError_t launch_expert_count(const ExpertArgs& a, hipStream_t s);
 // Small calls count and scan in one launch, a tile a wave, and the count
@@ -238,7 +250,7 @@ hipError_t launch_expert_scan(const ExpertArgs& a, hipStream_t s);
 hipError_t launch_expert_copy(const ExpertArgs& a, int waves, int row_split, bool stream,
                               hipStream_t s);
 hipError_t launch_expert_combine(const ExpertCombineArgs& a, int W, int dtype, int waves,
-                                 int row_split, bool stream, hipStream_t s);
+                                 bool stream, hipStream_t s);
 
 hipError_t launch_standard_count(const StandardArgs& a, hipStream_t s);
 hipError_t launch_standard_count_scan(const StandardArgs& a, hipStream_t s);
@@ -246,10 +258,10 @@ hipError_t launch_standard_scan(const StandardArgs& a, hipStream_t s);
 hipError_t launch_standard_copy(const StandardArgs& a, int waves, int row_split, bool stream,
                                 hipStream_t s);
 hipError_t launch_standard_combine(const StandardCombineArgs& a, const TokenMap& tk, int dtype,
-                                   int waves, int row_split, bool stream, hipStream_t s);
+                                   int waves, bool stream, hipStream_t s);
 hipError_t launch_quantize(const QuantizeArgs& a, int wire, int dtype, bool stream, hipStream_t s);
 hipError_t launch_combine_wire(const WireCombineArgs& a, const TokenMap& tk, int wire, int dtype,
-                               int waves, int row_split, bool stream, hipStream_t s);
+                               int waves, bool stream, hipStream_t s);
 
 // Access-pattern probes (include/ep_probe.h); kind is an EP_PROBE_* value.
 struct ProbeArgs {

@@ -292,9 +292,10 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
     const int nwaves = blockDim.x / kWave;
-    const int piece = blockIdx.x % a.pieces;
-    const int share = (blockIdx.x / a.pieces) % a.token_split;
-    const int g = blockIdx.x / a.pieces / a.token_split;
+    const int piece = a.piece_inner ? (int)(blockIdx.x % a.pieces) : (int)blockIdx.y;
+    const int tshare = a.piece_inner ? (int)(blockIdx.x / a.pieces) : (int)blockIdx.x;
+    const int share = tshare % a.token_split;
+    const int g = tshare / a.token_split;
     const int r = rank_of_tile(tm, g);
     const int t0 = (g - tm.tile_start[r]) * tm.tile_tokens;
     const int cnt = min(tm.tile_tokens, tm.ntok[r] - t0);
@@ -452,7 +453,7 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
             }
             __syncthreads();
         }
-        const bool first = blockIdx.x == 0;
+        const bool first = g == 0 && share == 0 && piece == 0;
         for (int d = wave; d < tm.W; d += nwaves) {
             const int32_t* col = a.tile_counts + (int64_t)d * a.tile_stride;
             int32_t before = 0, all = 0;
@@ -555,10 +556,14 @@ template <int G, int U, int DT, bool kStream>
 __global__ __launch_bounds__(1024) void ep_combine_kernel(CombineArgs a, TokenMap tk)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int flat = blockIdx.x * (blockDim.x / kWave) + uniform(threadIdx.x / kWave);
-    if (flat >= tk.total)
+    // wave items: (token, piece); piece_inner: piece fastest, so a token's
+    // pieces run in neighbouring waves
+    const uint32_t item = blockIdx.x * (blockDim.x / kWave) + uniform(threadIdx.x / kWave);
+    const uint32_t flat_u = a.piece_inner ? item / (uint32_t)a.pieces : item;
+    if (flat_u >= (uint32_t)tk.total)
         return;  // whole waves only
-    const int piece = blockIdx.y;
+    const int flat = (int)flat_u;
+    const int piece = a.piece_inner ? (int)(item - flat_u * (uint32_t)a.pieces) : (int)blockIdx.y;
     const int r = rank_of_token(tk, flat);
     const int64_t tok = (int64_t)r * a.M + (flat - tk.tok_start[r]);
     const int32_t gl = lane < a.P ? a.fwd[tok * a.P + lane] : -1;
@@ -568,7 +573,10 @@ __global__ __launch_bounds__(1024) void ep_combine_kernel(CombineArgs a, TokenMa
     const __amdgpu_buffer_rsrc_t rdst = row_rsrc(a.out + tok * row_bytes, row_bytes);
     const int vbeg = piece * a.piece_vecs;
     const int vend = min(a.row_vecs, vbeg + a.piece_vecs);
-    fold_rows<G, U, DT, kStream>(a.y, row_bytes, gl, n, rdst, vbeg, vend, lane);
+    if constexpr (G == 0)
+        fold_rows_streamed<U, DT, kStream>(a.y, row_bytes, gl, n, rdst, vbeg, vend, lane);
+    else
+        fold_rows<G, U, DT, kStream>(a.y, row_bytes, gl, n, rdst, vbeg, vend, lane);
 
     if (piece == 0 && a.yw != nullptr && lane < a.k) {
         float acc = 0.0f;
@@ -684,7 +692,9 @@ hipError_t launch_copy(const CopyArgs& a, const TileMap& tm, int waves, bool str
 {
     if (tm.total_tiles == 0)
         return hipSuccess;
-    const dim3 grid((unsigned)((int64_t)tm.total_tiles * a.token_split * a.pieces));
+    const int64_t tshares = (int64_t)tm.total_tiles * a.token_split;
+    const dim3 grid = a.piece_inner ? dim3((unsigned)(tshares * a.pieces))
+                                    : dim3((unsigned)tshares, (unsigned)a.pieces);
     const dim3 block(waves * kWave);
     const int per_lane = (a.piece_vecs + kWave - 1) / kWave;
     if (per_lane <= 1)
@@ -697,12 +707,19 @@ hipError_t launch_copy(const CopyArgs& a, const TileMap& tm, int waves, bool str
 }
 
 hipError_t launch_combine(const CombineArgs& a, const TokenMap& tk, int dtype, int waves,
-                          int row_split, bool stream, hipStream_t s)
+                          bool stream, hipStream_t s)
 {
     if (tk.total == 0)
         return hipSuccess;
-    const dim3 grid((tk.total + waves - 1) / waves, row_split);
+    const dim3 grid = a.piece_inner
+                          ? dim3((unsigned)(((int64_t)tk.total * a.pieces + waves - 1) / waves))
+                          : dim3((unsigned)((tk.total + waves - 1) / waves), (unsigned)a.pieces);
     const dim3 block(waves * kWave);
+    // pieces of up to 2 KB: folded row by row (fold_rows_streamed)
+    if (a.piece_vecs <= kWave)
+        return combine_with<0, 1>(a, tk, dtype, grid, block, stream, s);
+    if (a.piece_vecs <= 2 * kWave)
+        return combine_with<0, 2>(a, tk, dtype, grid, block, stream, s);
     if (a.P <= 1)
         return combine_with<1, 4>(a, tk, dtype, grid, block, stream, s);
     if (a.P <= 2)

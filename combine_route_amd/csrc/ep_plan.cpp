@@ -323,6 +323,15 @@ int tiles_for(const int32_t* ntok, int W, int tt)
     return n;
 }
 
+// Calls of at least 512 tiles of 32 tokens (the automatic geometry's large
+// calls) have more blocks than the GPU holds at once: their copy and combine
+// grids number the row pieces fastest, so the blocks that run together move
+// neighbouring rows. In smaller calls every block is resident from the start
+// and that order measured slower (MI355X, 8 x 128 fp8 tokens: combine 18.3 ->
+// 20.6 us; 4 x ~1024 top-64 tokens: copy 18.8 -> 20.0 us), so they keep the
+// piece in grid y.
+bool large_call(const Shape& s, const int32_t* ntok) { return tiles_for(ntok, s.W, 32) >= 512; }
+
 // The grid of an expert-major copy (ep_convert_dispatch_output's over tiles
 // of 64 received rows, ep_dispatch_standard_moe's over tiles of 64 source
 // tokens): each row cut into pieces and each tile's rows shared by blocks
@@ -375,6 +384,19 @@ int64_t fused_tiles(const Shape& s, const int32_t* ntok)
 // of 512 or 1024 elements).
 // Smallest row piece the automatic dispatch geometry cuts for large calls.
 constexpr int64_t kMinPieceBytes = 7168;
+// Wire codes a combine wave folds in large calls: ep_combine's wire combine,
+// and ep_combine_standard_moe's from wire rows.
+constexpr int64_t kWirePieceBytes = 1792;
+constexpr int64_t kStandardWirePieceBytes = 3584;
+
+// Bytes of one wire row's codes (not its scales); 0 without a wire.
+int64_t wire_row_bytes(const ep_plan* p)
+{
+    const int64_t H = p->s.H;
+    return p->cfg.combine_wire == EP_WIRE_FP8_BLOCK128 ? H
+           : p->cfg.combine_wire == EP_WIRE_MXFP4      ? H / 2
+                                                        : 0;
+}
 
 ep_launch_t auto_launch(const ep_plan* p, const int32_t* ntok)
 {
@@ -426,6 +448,23 @@ ep_launch_t auto_launch(const ep_plan* p, const int32_t* ntok)
     l.combine_row_split = (int)std::min<int64_t>(
         std::min<int64_t>(cmax_split, 65535),
         std::max<int64_t>(1, (kTargetBlocks + cblocks - 1) / cblocks));
+    if (l.tile_tokens > 16 && p->cfg.combine_wire == EP_WIRE_NONE) {
+        // large calls: 1 KB pieces (a wave's columns, folded row by row) and
+        // 16 waves a block; a token's pieces run in neighbouring waves, so
+        // each contribution row is read whole at about the same time.
+        // Measured on MI355X, combine kernel us, old rule (4 waves, whole
+        // rows) -> this one: 8 x 4096 tokens, top-8, 14 KB rows 558 -> 471,
+        // 8 KB rows 308 -> 273; 8 x 2048 tokens, 14 KB rows 280 -> 235;
+        // 4 x 4096 tokens, top-64, 4 KB rows 58 -> 56.
+        l.combine_waves = 16;
+        l.combine_row_split = (int)cmax_split;
+    } else if (l.tile_tokens > 16) {
+        // large calls from wire rows: pieces of about 1.75 KB of codes, 4
+        // waves a block (8 x 4096 tokens, top-8, H = 7168: FP8 block-128
+        // 327 -> 288 us, MXFP4 214 -> 203 us)
+        l.combine_waves = 4;
+        l.combine_row_split = (int)std::max<int64_t>(1, wire_row_bytes(p) / kWirePieceBytes);
+    }
     // rows one call moves at most (every token sent to min(W, k) ranks)
     const int64_t rows_bytes = N * (s.row_bytes + s.crow_bytes) * (1 + s.P);
     l.cache_policy = rows_bytes <= kKeepBytes ? EP_CACHE_KEEP : EP_CACHE_STREAM;
@@ -450,6 +489,11 @@ ep_launch_t auto_launch(const ep_plan* p, const int32_t* ntok)
     const int64_t iblocks = std::max<int64_t>(1, s.W * ((rows + 3) / 4));
     l.expert_combine_row_split = (int)std::min<int64_t>(
         std::min<int64_t>(cmax_split, 65535), std::max<int64_t>(1, (kTargetBlocks + iblocks - 1) / iblocks));
+    if (l.tile_tokens > 16) {
+        // large calls: as the combine, 1 KB pieces and 16 waves a block
+        l.expert_combine_waves = 16;
+        l.expert_combine_row_split = (int)cmax_split;
+    }
     // rows these calls move at most: N * min(W, k) received rows read and
     // N * k (row, expert) pairs written, and the same counts of expert
     // output rows on the way back. The rows they read were just written (by
@@ -770,6 +814,7 @@ int ep_dispatch(ep_plan_t* p, const ep_dispatch_args_t* a, void* stream_ptr)
     ca.tile_stride = s.tile_stride;
     ca.pieces = (int32_t)((ca.row_vecs + ca.piece_vecs - 1) / ca.piece_vecs);
     ca.token_split = std::min(l.dispatch_token_split, l.tile_tokens);
+    ca.piece_inner = large_call(s, a->num_tokens) ? 1 : 0;
     // a launch's work-items must fit in 32 bits
     const int64_t copy_items = (int64_t)tm.total_tiles * ca.token_split * ca.pieces *
                                l.dispatch_waves * ep::kWave;
@@ -847,13 +892,19 @@ int ep_combine(ep_plan_t* p, const ep_combine_args_t* a, void* stream_ptr)
         ca.fwd = ws_fwd(p);
         ca.row_vecs = (int32_t)(s.crow_bytes / 16);
         ca.piece_vecs = (ca.row_vecs + l.combine_row_split - 1) / l.combine_row_split;
+        ca.pieces = (ca.row_vecs + ca.piece_vecs - 1) / ca.piece_vecs;
+        ca.piece_inner = large_call(s, p->last_ntok) ? 1 : 0;
         ca.M = s.M;
         ca.k = s.k;
         ca.P = s.P;
-        const int row_split = (ca.row_vecs + ca.piece_vecs - 1) / ca.piece_vecs;
+        // a wave per (token, piece); the launch's work-items must fit in 32 bits
+        const int64_t items = (int64_t)tk.total * ca.pieces;
+        if ((items + l.combine_waves - 1) / l.combine_waves * l.combine_waves * ep::kWave >
+            (int64_t)UINT32_MAX)
+            return fail(EP_ERR_ARG, "combine grid of %lld waves (tokens x row pieces) exceeds "
+                        "2^32 - 1 work-items; lower combine_row_split", (long long)items);
         e = timed(p, EP_KERNEL_COMBINE, stream, [&] {
-            return ep::launch_combine(ca, tk, dtype, l.combine_waves, row_split, streaming,
-                                      stream);
+            return ep::launch_combine(ca, tk, dtype, l.combine_waves, streaming, stream);
         });
     } else {
         ep::WireCombineArgs wa;
@@ -878,11 +929,17 @@ int ep_combine(ep_plan_t* p, const ep_combine_args_t* a, void* stream_ptr)
         wa.M = s.M;
         wa.k = s.k;
         wa.P = s.P;
-        const int row_split = (wa.units + wa.piece_units - 1) / wa.piece_units;
+        wa.pieces = (wa.units + wa.piece_units - 1) / wa.piece_units;
+        wa.piece_inner = large_call(s, p->last_ntok) ? 1 : 0;
+        const int64_t witems = (int64_t)tk.total * wa.pieces;
+        if ((witems + l.combine_waves - 1) / l.combine_waves * l.combine_waves * ep::kWave >
+            (int64_t)UINT32_MAX)
+            return fail(EP_ERR_ARG, "combine grid of %lld waves (tokens x row pieces) exceeds "
+                        "2^32 - 1 work-items; lower combine_row_split", (long long)witems);
         const int kwire = wire == EP_WIRE_FP8_BLOCK128 ? ep::kWireFp8Block128 : ep::kWireMxfp4;
         e = timed(p, EP_KERNEL_COMBINE, stream, [&] {
-            return ep::launch_combine_wire(wa, tk, kwire, dtype, l.combine_waves, row_split,
-                                           streaming, stream);
+            return ep::launch_combine_wire(wa, tk, kwire, dtype, l.combine_waves, streaming,
+                                           stream);
         });
     }
     p->launched = true;
@@ -1292,11 +1349,19 @@ int ep_convert_combine_input(ep_expert_plan_t* x, const ep_convert_combine_args_
     ca.WM = (int32_t)s.WM;
     ca.Pe = x->e.Pe;
     ca.rows = x->rows;
-    const int row_split = (ca.row_vecs + ca.piece_vecs - 1) / ca.piece_vecs;
+    ca.pieces = (ca.row_vecs + ca.piece_vecs - 1) / ca.piece_vecs;
+    ca.piece_inner = large_call(s, p->last_ntok) ? 1 : 0;
     const int dtype = p->cfg.combine_dtype == EP_BF16 ? 0 : 1;
+    // a wave per (row, piece) of each rank; a launch's x work-items must fit
+    // in 32 bits
+    const int64_t items = (int64_t)ca.rows * ca.pieces;
+    if ((items + l.expert_combine_waves - 1) / l.expert_combine_waves * l.expert_combine_waves *
+            ep::kWave > (int64_t)UINT32_MAX)
+        return fail(EP_ERR_ARG, "inverse grid of %lld waves a rank (rows x row pieces) exceeds "
+                    "2^32 - 1 work-items; lower expert_combine_row_split", (long long)items);
 
     const hipError_t e = timed(p, EP_KERNEL_EXPERT_COMBINE, stream, [&] {
-        return ep::launch_expert_combine(ca, s.W, dtype, l.expert_combine_waves, row_split,
+        return ep::launch_expert_combine(ca, s.W, dtype, l.expert_combine_waves,
                                          l.expert_cache_policy == EP_CACHE_STREAM, stream);
     });
     x->launched = true;
@@ -1472,11 +1537,28 @@ int ep_combine_standard_moe(ep_expert_plan_t* x, const ep_combine_standard_args_
     ca.E = (int32_t)s.E;
     ep::TokenMap tk;
     token_map(s, x->fused_ntok, &tk);
+    // Automatic geometry of this fold (expert_combine_waves and
+    // expert_combine_row_split <= 0): small calls cut rows until about 1024
+    // blocks of 4 waves; large calls (numbered piece-fastest) fold pieces of
+    // 2 KB with 8 waves a block, or from wire rows pieces of about 3.5 KB of
+    // codes with 4 waves (8 x 4096 tokens, top-8, H = 7168, us: bf16 817 ->
+    // 737, FP8 block-128 470 -> 455, MXFP4 318 -> 318).
+    const bool large = large_call(s, x->fused_ntok);
+    int waves = p->launch.expert_combine_waves > 0 ? p->launch.expert_combine_waves
+                : large ? (wire != EP_WIRE_NONE ? 4 : 8)
+                        : 4;
     int split = l.expert_combine_row_split;
     if (p->launch.expert_combine_row_split <= 0) {
-        const int64_t blocks = std::max<int64_t>(1, ((int64_t)tk.total + 3) / 4);
         const int max_split = std::max(1, ca.row_vecs / ep::kWave);
-        split = (int)std::min<int64_t>(max_split, std::max<int64_t>(1, (1024 + blocks - 1) / blocks));
+        if (large) {
+            const int64_t piece = wire != EP_WIRE_NONE ? kStandardWirePieceBytes : 2048;
+            const int64_t bytes = wire != EP_WIRE_NONE ? wire_row_bytes(p) : s.crow_bytes;
+            split = (int)std::min<int64_t>(max_split, std::max<int64_t>(1, bytes / piece));
+        } else {
+            const int64_t blocks = std::max<int64_t>(1, ((int64_t)tk.total + 3) / 4);
+            split = (int)std::min<int64_t>(max_split,
+                                           std::max<int64_t>(1, (1024 + blocks - 1) / blocks));
+        }
     }
     ca.piece_vecs = (ca.row_vecs + split - 1) / split;
     if (ca.wire) {
@@ -1484,11 +1566,17 @@ int ep_combine_standard_moe(ep_expert_plan_t* x, const ep_combine_standard_args_
         // holds one dword of each pair's scale row
         ca.piece_vecs = std::min((ca.piece_vecs + 15) / 16 * 16, 16 * ep::kWave);
     }
-    const int row_split = (ca.row_vecs + ca.piece_vecs - 1) / ca.piece_vecs;
+    ca.pieces = (ca.row_vecs + ca.piece_vecs - 1) / ca.piece_vecs;
+    ca.piece_inner = large ? 1 : 0;
+    const int64_t items = (int64_t)tk.total * ca.pieces;
+    if ((items + waves - 1) / waves * waves * ep::kWave > (int64_t)UINT32_MAX)
+        return fail(EP_ERR_ARG, "combine_standard_moe grid of %lld waves (tokens x row pieces) "
+                    "exceeds 2^32 - 1 work-items; lower expert_combine_row_split",
+                    (long long)items);
     const int dtype = p->cfg.combine_dtype == EP_BF16 ? 0 : 1;
 
     const hipError_t e = timed(p, EP_KERNEL_STANDARD_COMBINE, stream, [&] {
-        return ep::launch_standard_combine(ca, tk, dtype, l.expert_combine_waves, row_split,
+        return ep::launch_standard_combine(ca, tk, dtype, waves,
                                            l.expert_cache_policy == EP_CACHE_STREAM, stream);
     });
     x->launched = true;

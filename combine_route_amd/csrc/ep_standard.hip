@@ -404,10 +404,13 @@ template <int G, int U, int DT, bool kStream, bool kWeighted, int WIRE>
 __global__ __launch_bounds__(1024) void sx_combine_kernel(StandardCombineArgs a, TokenMap tk)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int flat = blockIdx.x * (blockDim.x / kWave) + uniform(threadIdx.x / kWave);
-    if (flat >= tk.total)
+    // wave items: (token, piece); piece_inner: piece fastest
+    const uint32_t item = blockIdx.x * (blockDim.x / kWave) + uniform(threadIdx.x / kWave);
+    const uint32_t flat_u = a.piece_inner ? item / (uint32_t)a.pieces : item;
+    if (flat_u >= (uint32_t)tk.total)
         return;  // whole waves only
-    const int piece = blockIdx.y;
+    const int flat = (int)flat_u;
+    const int piece = a.piece_inner ? (int)(item - flat_u * (uint32_t)a.pieces) : (int)blockIdx.y;
     const int r = rank_of_token(tk, flat);
     const int64_t tok = (int64_t)r * a.M + (flat - tk.tok_start[r]);
 
@@ -744,11 +747,13 @@ hipError_t launch_standard_copy(const StandardArgs& a, int waves, int row_split,
 }
 
 hipError_t launch_standard_combine(const StandardCombineArgs& a, const TokenMap& tk, int dtype,
-                                   int waves, int row_split, bool stream, hipStream_t s)
+                                   int waves, bool stream, hipStream_t s)
 {
     if (tk.total == 0)
         return hipSuccess;
-    const dim3 grid((tk.total + waves - 1) / waves, row_split);
+    const dim3 grid = a.piece_inner
+                          ? dim3((unsigned)(((int64_t)tk.total * a.pieces + waves - 1) / waves))
+                          : dim3((unsigned)((tk.total + waves - 1) / waves), (unsigned)a.pieces);
     const dim3 block(waves * kWave);
     const int pe = a.k < a.E ? a.k : a.E;  // most kept pairs a token can have
     if (pe <= 1)

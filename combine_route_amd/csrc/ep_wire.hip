@@ -170,10 +170,13 @@ __global__ __launch_bounds__(1024) void ep_combine_wire_kernel(WireCombineArgs a
     constexpr int aux = Policy<kStream>::combine_load;
     const int lane = threadIdx.x & (kWave - 1);
     // wave-uniform, so the token's rank search and its output row stay scalar
-    const int flat = blockIdx.x * (blockDim.x / kWave) + uniform(threadIdx.x / kWave);
-    if (flat >= tk.total)
+    // wave items: (token, piece); piece_inner: piece fastest
+    const uint32_t item = blockIdx.x * (blockDim.x / kWave) + uniform(threadIdx.x / kWave);
+    const uint32_t flat_u = a.piece_inner ? item / (uint32_t)a.pieces : item;
+    if (flat_u >= (uint32_t)tk.total)
         return;  // whole waves only
-    const int piece = blockIdx.y;
+    const int flat = (int)flat_u;
+    const int piece = a.piece_inner ? (int)(item - flat_u * (uint32_t)a.pieces) : (int)blockIdx.y;
     const int r = rank_of_token(tk, flat);
     const int64_t tok = (int64_t)r * a.M + (flat - tk.tok_start[r]);
     const int32_t gl = lane < a.P ? a.fwd[tok * a.P + lane] : -1;
@@ -353,11 +356,13 @@ hipError_t launch_quantize(const QuantizeArgs& a, int wire, int dtype, bool stre
 }
 
 hipError_t launch_combine_wire(const WireCombineArgs& a, const TokenMap& tk, int wire, int dtype,
-                               int waves, int row_split, bool stream, hipStream_t s)
+                               int waves, bool stream, hipStream_t s)
 {
     if (tk.total == 0)
         return hipSuccess;
-    const dim3 grid((tk.total + waves - 1) / waves, row_split);
+    const dim3 grid = a.piece_inner
+                          ? dim3((unsigned)(((int64_t)tk.total * a.pieces + waves - 1) / waves))
+                          : dim3((unsigned)((tk.total + waves - 1) / waves), (unsigned)a.pieces);
     const dim3 block(waves * kWave);
     if (wire == kWireFp8Block128)
         return combine_wire_fmt<kWireFp8Block128>(a, tk, dtype, grid, block, stream, s);

@@ -299,8 +299,23 @@ const char *ep_last_error(void);
  *   dispatch_waves       wavefronts per dispatch-copy block: 1..16.
  *   dispatch_row_split   blocks sharing one tile's rows, each a contiguous
  *                        piece of the row: 1..row_bytes/16.
- *   combine_waves        wavefronts per combine block (a token each): 1..16.
- *   combine_row_split    pieces a combined row is split into: 1..H/8.
+ *   combine_waves        wavefronts per combine block (a token piece
+ *                        each): 1..16.
+ *   combine_row_split    pieces a combined row is split into, a wave each:
+ *                        1..H/8. A piece of at most 2 KB is folded row by row
+ *                        (every contribution row's piece loaded one row at a
+ *                        time, three rows in flight); a larger one a column
+ *                        chunk at a time. Automatic: calls with 16-token tiles
+ *                        cut rows until about 1024 blocks of 4 waves; larger
+ *                        calls fold 1 KB pieces with 16 waves, or from wire
+ *                        rows pieces of about 1.75 KB of codes with 4 waves.
+ *                        In calls of at least 512 tiles of 32 tokens, waves
+ *                        are numbered token by token with the pieces fastest
+ *                        (neighbouring rows in flight together), as are the
+ *                        dispatch copy's blocks (tile, share, piece) and the
+ *                        expert-major and fused combines' waves; smaller
+ *                        calls, whose blocks are all resident at once, put
+ *                        the piece in the grid's y dimension.
  *   cache_policy         EP_CACHE_STREAM: payload rows bypass the caches;
  *                        EP_CACHE_KEEP: rows are cached (best when the call's
  *                        rows fit in the 256 MB last-level cache, e.g. expert
@@ -350,7 +365,15 @@ typedef struct ep_launch {
      *   expert_row_split          pieces a copied row is cut into, a block
      *                             each: 1..row_bytes/16.
      *   expert_combine_waves      wavefronts per inverse block: 1..16.
-     *   expert_combine_row_split  pieces an inverse row is split into: 1..H/8.
+     *   expert_combine_row_split  pieces an inverse row is split into: 1..H/8
+     *                             (folded as combine_row_split says).
+     *                             Automatic: as combine_waves and
+     *                             combine_row_split for rows in the combine
+     *                             dtype. ep_combine_standard_moe takes both
+     *                             fields too; its automatic geometry: small
+     *                             calls as the combine; large calls fold 2 KB
+     *                             pieces with 8 waves, or from wire rows
+     *                             pieces of about 3.5 KB of codes with 4.
      *   expert_cache_policy       as cache_policy, for these calls; automatic:
      *                             keep when their rows (each token's
      *                             min(W, k) received rows and k expert rows,
@@ -377,8 +400,7 @@ typedef struct ep_launch {
     /* dispatch_token_split: blocks sharing one routing tile of ep_dispatch,
      * each copying ceil(tile_tokens / dispatch_token_split) consecutive
      * tokens of it: 1..64 (values above tile_tokens act as tile_tokens).
-     * Blocks are numbered tile, then share, then row piece, so the blocks
-     * the GPU starts together read and write neighbouring rows. Every block
+     * Blocks are numbered as combine_row_split describes. Every block
      * of a tile routes the whole tile again (its ids only). A launch whose
      * blocks x dispatch_waves x 64 exceed 2^32 - 1 fails with EP_ERR_ARG.
      * Automatic dispatch geometry: calls with 16-token tiles (fewer than

@@ -253,6 +253,9 @@ def test_launch_override_limits_and_auto_geometry(lib):
     # by blocks of 4 waves, one token a wave
     assert (auto["tile_tokens"], auto["dispatch_waves"], auto["dispatch_token_split"],
             auto["dispatch_row_split"]) == (64, 4, 16, 2)
+    # and the combines fold 1 KB pieces, 16 waves a block
+    assert (auto["combine_waves"], auto["combine_row_split"]) == (16, 14)
+    assert (auto["expert_combine_waves"], auto["expert_combine_row_split"]) == (16, 14)
     for bad in (dict(tile_tokens=8), dict(dispatch_waves=17), dict(combine_waves=17),
                 dict(dispatch_row_split=7168 * 2 // 16 + 1), dict(combine_row_split=897),
                 dict(cache_policy=3), dict(cache_policy=-1), dict(layout=4), dict(layout=-2)):

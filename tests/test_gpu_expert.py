@@ -217,6 +217,22 @@ def test_geometry_does_not_change_results(launch):
     run_expert_case(wl, launch=launch, cap_div=2)
 
 
+@pytest.mark.parametrize("launch", [
+    # inverse pieces of 512 and 256 columns: loaded a column chunk at a time
+    # for all rows of a token before folding (pieces of at most 128 columns
+    # fold row by row)
+    dict(expert_combine_row_split=1, expert_combine_waves=4),
+    dict(expert_combine_row_split=2, expert_combine_waves=3),
+    # 64 columns, the largest one-column-a-lane piece; 16 waves
+    dict(expert_combine_row_split=8, expert_combine_waves=16),
+])
+@pytest.mark.parametrize("weighted", [False, True])
+def test_inverse_fold_kinds(launch, weighted):
+    wl = workloads.custom("ex_fold_ep4_t150_h4096", 4, 150, 4096, 8, 64, "bf16", ragged=True,
+                          seed_index=523)
+    run_expert_case(wl, launch=launch, weighted=weighted, round_trip=True)
+
+
 def test_empty_and_edge_counts():
     wl = workloads.custom("ex_edge_ep4_t70_h256", 4, 70, 256, 4, 32, "bf16", seed_index=521)
     for ntok in ([0, 0, 0, 0], [70, 0, 0, 1], [1, 1, 1, 1], [64, 65, 0, 70]):
