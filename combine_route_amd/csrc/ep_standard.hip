@@ -262,7 +262,7 @@ __global__ __launch_bounds__(1024) void sx_copy_kernel(StandardArgs a)
                 if (vv < vend) {
                     if constexpr (kCast)
                         __builtin_amdgcn_raw_buffer_store_b64(c[u], rd, (int)((uint32_t)vv * 8u), 0,
-                                                              Policy<kStream>::copy_store);
+                                                              Policy<kStream>::cast_store);
                     else
                         bstore16<Policy<kStream>::copy_store>(v[u], rd, (uint32_t)vv * 16u);
                 }
