@@ -586,7 +586,7 @@ def copy_ceiling(torch, mib, steps, warmup):
 
 MEMORY_KERNELS = [  # label, pattern over the demangled name
     ("dispatch copy", r"ep_copy_kernel<8, 8, true, false, false>"),
-    ("combine", r"ep_combine_kernel<8, 2, 0, true>"),
+    ("combine", r"ep_combine_kernel<\d+, \d+, 0, true>"),
     ("probe: read", r"ep_probe_kernel<0>"),
     ("probe: write", r"ep_probe_kernel<1>"),
     ("probe: 1:1 copy", r"ep_probe_kernel<2>"),
@@ -1089,7 +1089,7 @@ def summarize_placement(out_md, timing_log, csv_paths, command, calls):
         for r in csv.DictReader(open(path)):
             n = r["Kernel_Name"]
             kind = ("copy" if re.search(r"ep_copy_kernel<8, 8, true, false, false>", n) else
-                    "combine" if re.search(r"ep_combine_kernel<8, 2, 0, true>", n) else None)
+                    "combine" if re.search(r"ep_combine_kernel<\d+, \d+, 0, true>", n) else None)
             if kind:
                 key = (path, int(r["Dispatch_Id"]), kind)
                 per.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
