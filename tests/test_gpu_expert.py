@@ -233,6 +233,18 @@ def test_inverse_fold_kinds(launch, weighted):
     run_expert_case(wl, launch=launch, weighted=weighted, round_trip=True)
 
 
+@pytest.mark.parametrize("weighted", [False, True])
+def test_large_ragged_call(weighted):
+    """The inverse of a large call (16 waves a block, rows numbered with the
+    piece fastest, 1 KB pieces folded row by row), ragged ranks, a row of
+    257 16-byte vectors."""
+    wl = workloads.custom("ex_large_ragged_ep8_h2056", 8, 4096, 2056, 8, 256, "bf16",
+                          seed_index=532)
+    inp = dict(workloads.make_inputs(wl),
+               ntok=[4096, 3001, 4095, 2048, 4096, 3333, 4000, 1])
+    run_expert_case(wl, inp=inp, weighted=weighted, round_trip=True)
+
+
 def test_empty_and_edge_counts():
     wl = workloads.custom("ex_edge_ep4_t70_h256", 4, 70, 256, 4, 32, "bf16", seed_index=521)
     for ntok in ([0, 0, 0, 0], [70, 0, 0, 1], [1, 1, 1, 1], [64, 65, 0, 70]):

@@ -193,6 +193,27 @@ def test_geometry_does_not_change_results(launch):
     run_case(wl, launch=launch)
 
 
+# Token counts of a call above the large-call threshold (at least 512 tiles of
+# 32 tokens: here 773), ragged, with a rank of one token.
+LARGE_RAGGED_NTOK = [4096, 3001, 4095, 2048, 4096, 3333, 4000, 1]
+
+
+@pytest.mark.parametrize("H", [2056, 1000, 7168])
+def test_large_ragged_call(H):
+    """Large calls number the dispatch copy's blocks and the combine's waves
+    with the row piece fastest and fold pieces of at most 2 KB row by row.
+    Ragged ranks and rows that the pieces do not divide (H = 2056: 257
+    16-byte vectors in 4 pieces of 65; H = 1000: one piece of 125)."""
+    wl = workloads.custom(f"large_ragged_ep8_h{H}", 8, 4096, H, 8, 256, "bf16",
+                          seed_index=531)
+    inp = dict(workloads.make_inputs(wl), ntok=list(LARGE_RAGGED_NTOK))
+    op = cra.EpDispatchCombineOp(config_of(wl))
+    auto = cra.ep_plan_get_launch(op.plan, inp["ntok"])
+    assert auto["combine_waves"] == 16, auto  # the large-call combine
+    run_case(wl, inp=inp, op=op, combine_twice=True)
+    op.close()
+
+
 def test_edge_token_counts():
     wl = workloads.custom("edges_ep4_t64_h512", 4, 64, 512, 8, 64, "bf16", seed_index=400)
     for ntok in ([0, 0, 0, 0], [64, 0, 64, 0], [0, 0, 0, 1], [64, 64, 64, 64], [1, 63, 17, 0]):

@@ -196,6 +196,18 @@ def test_geometry_does_not_change_results(launch):
     run_standard_case(wl, launch=launch, cap_div=2, weighted=True)
 
 
+@pytest.mark.parametrize("cap_div,weighted", [(1, True), (2, False)])
+def test_large_ragged_call(cap_div, weighted):
+    """The fused path on a large call (waves numbered token by token with the
+    piece fastest, 2 KB pieces, 8 waves a block), ragged ranks, a row of 257
+    16-byte vectors, with and without capacity drops."""
+    wl = workloads.custom("sx_large_ragged_ep8_h2056", 8, 4096, 2056, 8, 256, "bf16",
+                          seed_index=533)
+    inp = dict(workloads.make_inputs(wl),
+               ntok=[4096, 3001, 4095, 2048, 4096, 3333, 4000, 1])
+    run_standard_case(wl, cap_div=cap_div, inp=inp, weighted=weighted)
+
+
 def test_empty_and_edge_counts():
     wl = workloads.custom("std_edge_ep4_t70_h256", 4, 70, 256, 4, 32, "bf16", seed_index=571)
     for ntok in ([0, 0, 0, 0], [70, 0, 0, 1], [1, 1, 1, 1], [64, 65, 0, 70]):

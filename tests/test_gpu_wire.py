@@ -143,12 +143,14 @@ def test_e2m1_conversion_of_every_bf16_value_below_8():
     assert np.array_equal(got_c, ref_c)
 
 
-def run_wire_case(wl, name, launch=None, with_weights=True, tag=None):
+def run_wire_case(wl, name, launch=None, with_weights=True, tag=None, ntok=None):
     cw, ow = WIRES[name]
     W, M, k, H = wl.world_size, wl.max_tokens, wl.topk, wl.hidden
     tag = tag or f"{wl.name} {name}"
-    _say(f"[case] wire combine {tag}: W={W} M={M} H={H} k={k} launch={launch}")
+    _say(f"[case] wire combine {tag}: W={W} M={M} H={H} k={k} launch={launch} ntok={ntok}")
     inp = workloads.make_inputs(wl)
+    if ntok is not None:
+        inp["ntok"] = list(ntok)
     if not with_weights:
         inp["w"] = None
     ref = oracle_dispatch(wl, inp)
@@ -198,6 +200,16 @@ def run_wire_case(wl, name, launch=None, with_weights=True, tag=None):
                                      "ep4_ragged1024_h2048_fp16_k64"])
 def test_wire_combine_full_size(name, wl_name):
     run_wire_case(workloads.WORKLOADS[wl_name], name)
+
+
+@pytest.mark.parametrize("name", list(WIRES))
+def test_wire_combine_large_ragged_call(name):
+    """A large call (waves numbered token by token with the piece fastest,
+    pieces of about 1.75 KB of codes, 4 waves a block), ragged ranks, and a
+    row of 41 FP8 scale blocks (2 pieces of 168 and 160 16-element units)."""
+    wl = workloads.custom("wire_large_ragged_ep8_h5248", 8, 4096, 5248, 8, 256, "bf16",
+                          seed_index=534)
+    run_wire_case(wl, name, ntok=[4096, 3001, 4095, 2048, 4096, 3333, 4000, 1])
 
 
 @pytest.mark.parametrize("name", list(WIRES))
