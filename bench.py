@@ -991,6 +991,17 @@ def measure_small_workloads(args, cra, torch, np):
         torch.cuda.synchronize()
         ms_graph = _timed(torch, stream, graph.replay, steps, 20)
         del graph
+        # ten steps captured in one graph: the per-replay launch cost spread
+        # over ten calls
+        graph10 = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph10, stream=side):
+                for _ in range(10):
+                    op.dispatch(ntok, x, idx, w, sc, stream=side)
+                    op.combine(y, op.out_weights, stream=side)
+        torch.cuda.synchronize()
+        ms_graph10 = _timed(torch, stream, graph10.replay, max(1, steps // 10), 2) / 10
+        del graph10
         cra.ep_plan_set_timing(op.plan, True)
         torch.cuda.synchronize()
         for _ in range(steps):
@@ -1007,6 +1018,7 @@ def measure_small_workloads(args, cra, torch, np):
         rec.update({
             "us_per_call": round(ms * 1e3, 2),
             "us_per_call_graph_replay": round(ms_graph * 1e3, 2),
+            "us_per_call_graph_replay_10_calls_a_graph": round(ms_graph10 * 1e3, 2),
             "host_issue_us_per_call": round(host_us, 2),
             "kernel_us": kern,
             "payload_bytes_per_call": int(payload),
