@@ -198,15 +198,21 @@ def test_geometry_does_not_change_results(launch):
 LARGE_RAGGED_NTOK = [4096, 3001, 4095, 2048, 4096, 3333, 4000, 1]
 
 
-@pytest.mark.parametrize("H", [2056, 1000, 7168])
-def test_large_ragged_call(H):
+@pytest.mark.parametrize("W,k,H,dtype,ntok", [
+    (8, 8, 2056, "bf16", LARGE_RAGGED_NTOK),
+    (8, 8, 1000, "bf16", LARGE_RAGGED_NTOK),
+    (8, 8, 7168, "bf16", LARGE_RAGGED_NTOK),
+    (8, 2, 2056, "bf16", LARGE_RAGGED_NTOK),     # at most 2 rows a token
+    (4, 64, 2048, "fp16", [4096, 4096, 4095, 4096]),  # every token on every rank
+], ids=["h2056", "h1000", "h7168", "k2", "k64_fp16"])
+def test_large_ragged_call(W, k, H, dtype, ntok):
     """Large calls number the dispatch copy's blocks and the combine's waves
     with the row piece fastest and fold pieces of at most 2 KB row by row.
     Ragged ranks and rows that the pieces do not divide (H = 2056: 257
     16-byte vectors in 4 pieces of 65; H = 1000: one piece of 125)."""
-    wl = workloads.custom(f"large_ragged_ep8_h{H}", 8, 4096, H, 8, 256, "bf16",
+    wl = workloads.custom(f"large_ep{W}_k{k}_h{H}_{dtype}", W, 4096, H, k, 256, dtype,
                           seed_index=531)
-    inp = dict(workloads.make_inputs(wl), ntok=list(LARGE_RAGGED_NTOK))
+    inp = dict(workloads.make_inputs(wl), ntok=list(ntok))
     op = cra.EpDispatchCombineOp(config_of(wl))
     auto = cra.ep_plan_get_launch(op.plan, inp["ntok"])
     assert auto["combine_waves"] == 16, auto  # the large-call combine
