@@ -476,12 +476,15 @@ def measure_quantized_wires(args, cra, torch, np, wl, inp, stream):
     return out
 
 
-def measure_samples(args, torch, stream, dispatch, combine):
+def measure_samples(args, torch, stream, dispatch, combine, dispatch_on=None, combine_on=None):
     """The pages' sampling: rounds of per-call samples, each dispatch and
     combine bracketed by its own HIP events on the launch stream, reported as
     p50 and min; a point is flagged when the rounds' p50s spread by more than
     1.2x. The cold variant writes a 512 MiB scratch buffer before every sample,
-    so the MALL holds none of the call's data when it starts."""
+    so the MALL holds none of the call's data when it starts. With
+    dispatch_on / combine_on (the same calls on a given stream), the graph
+    variant replays captured graphs instead: the dispatch alone, the combine
+    alone, and the pair captured back to back in one graph."""
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
 
     def run(cold):
@@ -520,9 +523,59 @@ def measure_samples(args, torch, stream, dispatch, combine):
            "warm": run(0)}
     out["cold"] = run(1)
     out["cold"]["method"] = "the same, with a 512 MiB device write before every sample"
+    if dispatch_on is not None:
+        out["graph"] = graph_samples(args, torch, stream, dispatch_on, combine_on)
     del scratch
     torch.cuda.empty_cache()
     return out
+
+
+def graph_samples(args, torch, stream, dispatch_on, combine_on):
+    """Graph-replay samples: three graphs captured on a side stream (the
+    dispatch, the combine, and the pair back to back), 10 replays of each as
+    warmup, then rounds of samples, each replaying the dispatch graph, the
+    combine graph and the pair graph between HIP events."""
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    graphs = []
+    for fns in ((dispatch_on,), (combine_on,), (dispatch_on, combine_on)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for f in fns:
+                    f(side)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        for g in graphs:
+            g.replay()
+    torch.cuda.synchronize()
+    rounds = []
+    for _ in range(args.rounds):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+              for _ in range(args.samples)]
+        for e in ev:
+            for i, g in enumerate(graphs):
+                e[i].record(stream)
+                g.replay()
+            e[3].record(stream)
+        torch.cuda.synchronize()
+        rounds.append([tuple(e[i].elapsed_time(e[i + 1]) * 1e3 for i in range(3)) for e in ev])
+    del graphs
+    flat = [t for r in rounds for t in r]
+
+    def stat(i):
+        v = sorted(t[i] for t in flat)
+        return {"p50": round(v[len(v) // 2], 2), "min": round(v[0], 2)}
+
+    p50s = [sorted(t[2] for t in r)[len(r) // 2] for r in rounds]
+    spread = max(p50s) / min(p50s)
+    return {"method": f"{args.rounds} rounds x {args.samples} samples after 10 replays of each "
+                      "graph; a sample replays the dispatch graph, the combine graph and the "
+                      "pair (dispatch and combine captured back to back in one graph), each "
+                      "between HIP events on the launch stream",
+            "dispatch_us": stat(0), "combine_us": stat(1), "pair_us": stat(2),
+            "round_p50_spread": round(spread, 3), "rejected": spread > 1.2}
 
 
 def workloads_dtype(torch, name):
@@ -650,10 +703,11 @@ def summarize_memory(out_md, csv_paths, command):
 def summarize_trace(out_md, eager_csv, graph_csv, skip_eager, skip_graph, steps, command):
     """Kernel durations and the gaps between kernels of the timed calls of one
     workload, eager launches against graph replay: for each mode, the calls
-    [skip, skip + steps) of the trace (route, copy, combine triples in start
-    order), medians of each kernel's duration, of the gaps route -> copy and
-    copy -> combine, of the gap from one call's combine to the next call's
-    route, and of the call period."""
+    [skip, skip + steps) of the trace (the call's kernels in start order:
+    route, copy and combine, with a scan kernel between route and copy in
+    large calls), medians of each kernel's duration, of the gaps between
+    consecutive kernels of a call, of the gap from one call's combine to the
+    next call's route, and of the call period."""
     import statistics
 
     def calls(path):
@@ -661,11 +715,14 @@ def summarize_trace(out_md, eager_csv, graph_csv, skip_eager, skip_graph, steps,
         rows.sort(key=lambda r: int(r["Start_Timestamp"]))
         out, i = [], 0
         while i + 2 < len(rows):
-            n = [rows[i + j]["Kernel_Name"] for j in range(3)]
-            if "ep_route_kernel" in n[0] and "ep_copy_kernel" in n[1] and "ep_combine_kernel" in n[2]:
+            n = [rows[i + j]["Kernel_Name"] for j in range(min(4, len(rows) - i))]
+            span = (4 if len(n) == 4 and "ep_scan_kernel" in n[1] and "ep_copy_kernel" in n[2]
+                    and "ep_combine_kernel" in n[3] else
+                    3 if "ep_copy_kernel" in n[1] and "ep_combine_kernel" in n[2] else 0)
+            if span and "ep_route_kernel" in n[0]:
                 out.append([(int(r["Start_Timestamp"]) / 1e3, int(r["End_Timestamp"]) / 1e3)
-                            for r in rows[i:i + 3]])
-                i += 3
+                            for r in rows[i:i + span]])
+                i += span
             else:
                 i += 1
         return out
@@ -674,21 +731,27 @@ def summarize_trace(out_md, eager_csv, graph_csv, skip_eager, skip_graph, steps,
              f"Kernel sources sha256[:16]: {kernel_source_hash()}", "",
              "Commands (from the repository root):", ""]
     lines += ["    " + c for c in command.split(" ;; ")]
-    lines += ["", "Medians over the timed calls, in microseconds (timestamps of the kernel trace):",
-              "", "| mode | calls | route | copy | combine | gap route -> copy | "
-              "gap copy -> combine | gap to the next call | call period |",
-              "|---|---|---|---|---|---|---|---|---|"]
+    results = []
     for mode, path, skip in (("eager", eager_csv, skip_eager), ("graph replay", graph_csv,
                                                                    skip_graph)):
         c = calls(path)[skip: skip + steps]
-        med = lambda v: statistics.median(v) if v else float("nan")
-        dur = [med([x[j][1] - x[j][0] for x in c]) for j in range(3)]
-        g1 = med([x[1][0] - x[0][1] for x in c])
-        g2 = med([x[2][0] - x[1][1] for x in c])
-        g3 = med([c[i + 1][0][0] - c[i][2][1] for i in range(len(c) - 1)])
+        results.append((mode, c))
+    k = len(results[0][1][0]) if results[0][1] else 3
+    names = ["route", "scan", "copy", "combine"] if k == 4 else ["route", "copy", "combine"]
+    lines += ["", "Medians over the timed calls, in microseconds (timestamps of the kernel trace):",
+              "", "| mode | calls | " + " | ".join(names) + " | " +
+              " | ".join(f"gap {names[j]} -> {names[j + 1]}" for j in range(k - 1)) +
+              " | gap to the next call | call period |",
+              "|---|---|" + "---|" * (2 * k - 1) + "---|---|"]
+    med = lambda v: statistics.median(v) if v else float("nan")
+    for mode, c in results:
+        c = [x for x in c if len(x) == k]
+        dur = [med([x[j][1] - x[j][0] for x in c]) for j in range(k)]
+        gaps = [med([x[j + 1][0] - x[j][1] for x in c]) for j in range(k - 1)]
+        g3 = med([c[i + 1][0][0] - c[i][-1][1] for i in range(len(c) - 1)])
         per = med([c[i + 1][0][0] - c[i][0][0] for i in range(len(c) - 1)])
-        lines.append(f"| {mode} | {len(c)} | {dur[0]:.2f} | {dur[1]:.2f} | {dur[2]:.2f} | "
-                     f"{g1:.2f} | {g2:.2f} | {g3:.2f} | {per:.2f} |")
+        lines.append(f"| {mode} | {len(c)} | " + " | ".join(f"{d:.2f}" for d in dur) + " | " +
+                     " | ".join(f"{g:.2f}" for g in gaps) + f" | {g3:.2f} | {per:.2f} |")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -1317,7 +1380,9 @@ def run(args):
     if args.rounds > 0 and args.samples > 0:
         samples = measure_samples(
             args, torch, stream, lambda: op.dispatch(ntok, x, idx, w, sc, stream=stream),
-            lambda: op.combine(y, op.out_weights, stream=stream))
+            lambda: op.combine(y, op.out_weights, stream=stream),
+            lambda s: op.dispatch(ntok, x, idx, w, sc, stream=s),
+            lambda s: op.combine(y, op.out_weights, stream=s))
 
     ceilings = None
     uniform_tokens = all(t == M for t in ntok)
