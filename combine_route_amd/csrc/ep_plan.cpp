@@ -448,6 +448,12 @@ ep_launch_t auto_launch(const ep_plan* p, const int32_t* ntok)
     l.combine_row_split = (int)std::min<int64_t>(
         std::min<int64_t>(cmax_split, 65535),
         std::max<int64_t>(1, (kTargetBlocks + cblocks - 1) / cblocks));
+    if (l.tile_tokens == 16 && p->cfg.combine_wire == EP_WIRE_NONE) {
+        // small calls: pieces of at most 2 KB, folded row by row (8 x 128
+        // fp8 tokens, bf16 combine: 33.2 -> 32.6 us a call)
+        l.combine_row_split = (int)std::min<int64_t>(
+            cmax_split, std::max<int64_t>(l.combine_row_split, (s.crow_bytes + 2047) / 2048));
+    }
     if (l.tile_tokens > 16 && p->cfg.combine_wire == EP_WIRE_NONE) {
         // large calls: 1 KB pieces (a wave's columns, folded row by row) and
         // 16 waves a block; a token's pieces run in neighbouring waves, so

@@ -306,9 +306,11 @@ const char *ep_last_error(void);
  *                        (every contribution row's piece loaded one row at a
  *                        time, three rows in flight); a larger one a column
  *                        chunk at a time. Automatic: calls with 16-token tiles
- *                        cut rows until about 1024 blocks of 4 waves; larger
- *                        calls fold 1 KB pieces with 16 waves, or from wire
- *                        rows pieces of about 1.75 KB of codes with 4 waves.
+ *                        cut rows until about 1024 blocks of 4 waves, and
+ *                        into pieces of at most 2 KB (rows in the combine
+ *                        dtype); larger calls fold 1 KB pieces with 16
+ *                        waves, or from wire rows pieces of about 1.75 KB of
+ *                        codes with 4 waves.
  *                        In calls of at least 512 tiles of 32 tokens, waves
  *                        are numbered token by token with the pieces fastest
  *                        (neighbouring rows in flight together), as are the
