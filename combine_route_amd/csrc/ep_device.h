@@ -238,8 +238,11 @@ __device__ __forceinline__ void fold_rows(const uint8_t* src, uint32_t row_bytes
 // row i is added). Same additions in the same order, so the same bits as
 // fold_rows. Fewer registers than fold_rows (more waves a SIMD), and a
 // token's pieces, run by neighbouring waves, read each contribution row
-// whole at about the same time.
-constexpr int kStreamDepth = 3;
+// whole at about the same time. Two rows in flight: at 8 x 4096 tokens,
+// H = 7168, top-8, the combine takes the same time with 2 or 3 (4: +1%) and
+// the expert-major inverse, 8 rows a token, 1126 us with 2, 1180 with 3,
+// 1260 with 4 and 1503 with 6.
+constexpr int kStreamDepth = 2;
 
 template <int R, int DT, bool kStream, bool kWeighted = false>
 __device__ __forceinline__ void fold_rows_streamed(const uint8_t* src, uint32_t row_bytes,
@@ -250,29 +253,33 @@ __device__ __forceinline__ void fold_rows_streamed(const uint8_t* src, uint32_t 
     constexpr int D = kStreamDepth;
     float acc[R][8];
     u32x4 buf[D][R];
+    // Every load is issued, so that the compiler can wait for one row at a
+    // time (with a load skipped on some paths it waits for all of them, and
+    // only one row is in flight): a row past the last (i >= n) has an empty
+    // resource and a column past the piece an offset at the row's end, and
+    // both read zeros without touching memory.
     auto load = [&](int i, u32x4 (&b)[R]) {
-        const int64_t gi = __builtin_amdgcn_readlane(gl, i);
-        const __amdgpu_buffer_rsrc_t ry = row_rsrc(src + gi * row_bytes, row_bytes);
+        const bool in = i < n;  // uniform
+        const int64_t gi = in ? __builtin_amdgcn_readlane(gl, i & (kWave - 1)) : 0;
+        const __amdgpu_buffer_rsrc_t ry = row_rsrc(src + gi * row_bytes, in ? row_bytes : 0u);
 #pragma unroll
         for (int u = 0; u < R; ++u) {
             const int v = vbeg + u * kWave + lane;
-            if (v < vend)
-                b[u] = bload16<Policy<kStream>::combine_load>(ry, (uint32_t)v * 16u);
+            const uint32_t off = v < vend ? (uint32_t)v * 16u : row_bytes;
+            b[u] = bload16<Policy<kStream>::combine_load>(ry, off);
         }
     };
     // row i lives in buf[i % D]; the loop runs D rows a pass so that every
     // buffer index is a constant
 #pragma unroll
     for (int j = 0; j < D - 1; ++j)
-        if (j < n)
-            load(j, buf[j]);
+        load(j, buf[j]);
     for (int i0 = 0; i0 < n; i0 += D) {
 #pragma unroll
         for (int j = 0; j < D; ++j) {
             const int i = i0 + j;
+            load(i + D - 1, buf[(j + D - 1) % D]);
             if (i < n) {
-                if (i + D - 1 < n)
-                    load(i + D - 1, buf[(j + D - 1) % D]);
                 float c = 1.0f;
                 if constexpr (kWeighted)
                     c = __builtin_bit_cast(

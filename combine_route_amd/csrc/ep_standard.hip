@@ -393,10 +393,50 @@ __global__ __launch_bounds__(1024) void sx_copy_kernel(StandardArgs a)
     }
 }
 
-// Fold-position flags of a kept pair: the last kept pair of its rank, and
-// whether ranks without a kept pair come just before its rank.
+// Fold-position flags of a kept pair: the last and the first kept pair of
+// its rank, and whether ranks without a kept pair come just before its rank.
 constexpr int kFoldLast = 1;
 constexpr int kFoldGap = 2;
+constexpr int kFoldFirstBit = 2;
+constexpr int kFoldFirst = 1 << kFoldFirstBit;
+
+// One kept pair into its rank's sum, 8 elements in place: p = c * f for the
+// rank's first pair (the product, which is fma(c, f, -0) exactly, signed
+// zeros included), else p = fma(c, f, p). The choice is a uniform branch
+// inside one asm statement, so both forms write the same registers: written
+// as two C++ branches, the compiler joined them with a register copy per
+// element, and resetting the sum to -0 after each rank costs an instruction
+// per element and rank.
+__device__ __forceinline__ void fold_pair8(float (&p)[8], const float (&f)[8], float c, int flags)
+{
+    asm("s_bitcmp1_b32 %[fl], %[bit]\n\t"
+        "s_cbranch_scc1 1f\n\t"
+        "v_fmac_f32 %[p0], %[c], %[f0]\n\t"
+        "v_fmac_f32 %[p1], %[c], %[f1]\n\t"
+        "v_fmac_f32 %[p2], %[c], %[f2]\n\t"
+        "v_fmac_f32 %[p3], %[c], %[f3]\n\t"
+        "v_fmac_f32 %[p4], %[c], %[f4]\n\t"
+        "v_fmac_f32 %[p5], %[c], %[f5]\n\t"
+        "v_fmac_f32 %[p6], %[c], %[f6]\n\t"
+        "v_fmac_f32 %[p7], %[c], %[f7]\n\t"
+        "s_branch 2f\n"
+        "1:\n\t"
+        "v_mul_f32 %[p0], %[c], %[f0]\n\t"
+        "v_mul_f32 %[p1], %[c], %[f1]\n\t"
+        "v_mul_f32 %[p2], %[c], %[f2]\n\t"
+        "v_mul_f32 %[p3], %[c], %[f3]\n\t"
+        "v_mul_f32 %[p4], %[c], %[f4]\n\t"
+        "v_mul_f32 %[p5], %[c], %[f5]\n\t"
+        "v_mul_f32 %[p6], %[c], %[f6]\n\t"
+        "v_mul_f32 %[p7], %[c], %[f7]\n"
+        "2:"
+        : [p0] "+v"(p[0]), [p1] "+v"(p[1]), [p2] "+v"(p[2]), [p3] "+v"(p[3]),
+          [p4] "+v"(p[4]), [p5] "+v"(p[5]), [p6] "+v"(p[6]), [p7] "+v"(p[7])
+        : [c] "s"(c), [f0] "v"(f[0]), [f1] "v"(f[1]), [f2] "v"(f[2]), [f3] "v"(f[3]),
+          [f4] "v"(f[4]), [f5] "v"(f[5]), [f6] "v"(f[6]), [f7] "v"(f[7]), [fl] "s"(flags),
+          [bit] "n"(kFoldFirstBit)
+        : "scc");
+}
 
 // WIRE: 0 for bf16 / fp16 expert outputs, else the wire of the packed rows
 // (kWireFp8Block128, kWireMxfp4), each element decoded exactly before the fold.
@@ -475,7 +515,8 @@ __global__ __launch_bounds__(1024) void sx_combine_kernel(StandardCombineArgs a,
     if (lane < nk) {
         const int pv = lane == 0 ? -1 : dprev;
         const bool last = lane == nk - 1 || dnext != dx;
-        flags = (last ? kFoldLast : 0) | (dx - pv > 1 ? kFoldGap : 0);
+        flags = (last ? kFoldLast : 0) | (dx - pv > 1 ? kFoldGap : 0) |
+                (dx != pv ? kFoldFirst : 0);
     }
     const int dlast = nk > 0 ? __builtin_amdgcn_readlane(dx, nk - 1) : -1;
     const bool trailing = nD - 1 > dlast;  // ranks without a kept pair after the last
@@ -516,17 +557,23 @@ __global__ __launch_bounds__(1024) void sx_combine_kernel(StandardCombineArgs a,
         if (!regroup)
             load_scales(0);
     }
+    // A rank's sum starts at its first kept pair (fold_pair8), so it needs
+    // no reset between ranks; the total starts at -0, the identity of IEEE
+    // addition (-0 + x = x for every x, signed zeros included), so the first
+    // rank needs no case of its own.
+    float part[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            part[u][e] = -0.0f;
     for (int v0 = vbeg; v0 < vend; v0 += kWave * U) {
-        // Both sums start at -0, the identity of IEEE addition: -0 + x = x
-        // and fma(c, f, -0) = c * f exactly, for every x, signed zeros
-        // included, so the first pair of a rank and the first rank need no
-        // case of their own; a rank's sum goes back to -0 after its rounding.
-        float tot[U][8], part[U][8];
+        float tot[U][8];
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                tot[u][e] = part[u][e] = -0.0f;
+                tot[u][e] = -0.0f;
         bool have = false;  // uniform: tot holds a rank's contribution
         for (int i0 = 0; i0 < nk; i0 += G) {
             if constexpr (WIRE != 0) {
@@ -535,26 +582,28 @@ __global__ __launch_bounds__(1024) void sx_combine_kernel(StandardCombineArgs a,
             }
             u32x4 rows[WIRE ? 1 : U][WIRE ? 1 : G];   // bf16 / fp16 rows: 16 B a group
             u32x2 codes[WIRE ? U : 1][WIRE ? G : 1];  // wire rows: 8 B (FP8) or 4 B (MXFP4)
+            // Every load is issued, in the order the fold takes them, so a
+            // pair's fold waits for its own rows only. A pair past the token's
+            // last has an empty resource and a column past the piece an offset
+            // at the row's end: both read zeros without touching memory.
+            const uint32_t pb = WIRE ? a.py_row_bytes : row_bytes;
+            constexpr uint32_t vb = WIRE == 0 ? 16u : WIRE == kWireFp8Block128 ? 8u : 4u;
 #pragma unroll
             for (int q = 0; q < G; ++q) {
-                if (i0 + q < nk) {
-                    const int64_t gq = __builtin_amdgcn_readlane(gl, i0 + q);
-                    const uint32_t pb = WIRE ? a.py_row_bytes : row_bytes;
-                    const __amdgpu_buffer_rsrc_t ry = row_rsrc(a.py + gq * pb, pb);
+                const bool in = i0 + q < nk;  // uniform
+                const int64_t gq = in ? __builtin_amdgcn_readlane(gl, i0 + q) : 0;
+                const __amdgpu_buffer_rsrc_t ry = row_rsrc(a.py + gq * pb, in ? pb : 0u);
 #pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        const int v = v0 + u * kWave + lane;
-                        if (v < vend) {
-                            constexpr int ld = Policy<kStream>::combine_load;
-                            if constexpr (WIRE == 0)
-                                rows[u][q] = bload16<ld>(ry, (uint32_t)v * 16u);
-                            else if constexpr (WIRE == kWireFp8Block128)
-                                codes[u][q] = __builtin_amdgcn_raw_buffer_load_b64(ry, v * 8, 0, ld);
-                            else
-                                codes[u][q] = {__builtin_amdgcn_raw_buffer_load_b32(ry, v * 4, 0, ld),
-                                               0u};
-                        }
-                    }
+                for (int u = 0; u < U; ++u) {
+                    const int v = v0 + u * kWave + lane;
+                    const uint32_t off = v < vend ? (uint32_t)v * vb : pb;
+                    constexpr int ld = Policy<kStream>::combine_load;
+                    if constexpr (WIRE == 0)
+                        rows[u][q] = bload16<ld>(ry, off);
+                    else if constexpr (WIRE == kWireFp8Block128)
+                        codes[u][q] = __builtin_amdgcn_raw_buffer_load_b64(ry, off, 0, ld);
+                    else
+                        codes[u][q] = {__builtin_amdgcn_raw_buffer_load_b32(ry, off, 0, ld), 0u};
                 }
             }
 #pragma unroll
@@ -586,20 +635,13 @@ __global__ __launch_bounds__(1024) void sx_combine_kernel(StandardCombineArgs a,
                             for (int e = 0; e < 8; ++e)
                                 tot[u][e] = tot[u][e] + 0.0f;
                         }
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            if (kWeighted)
-                                part[u][e] = __builtin_fmaf(cq, f[e], part[u][e]);
-                            else
-                                part[u][e] = part[u][e] + f[e];
-                        }
+                        // unweighted, c = 1: fma(1, f, p) = p + f and 1 * f = f exactly
+                        fold_pair8(part[u], f, cq, fl);
                         if (last) {
                             // the rank's intermediate row: rounded to the combine type
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) {
+                            for (int e = 0; e < 8; ++e)
                                 tot[u][e] = tot[u][e] + round_to<DT>(part[u][e]);
-                                part[u][e] = -0.0f;
-                            }
                         }
                     }
                     have = have || gap || last;

@@ -223,20 +223,41 @@ __global__ __launch_bounds__(1024) void ep_combine_wire_kernel(WireCombineArgs a
         for (int i0 = 0; i0 < n; i0 += G) {
             if (regroup)
                 load_scales(i0);
+            // MXFP4: every load is issued, in the order the fold takes them,
+            // so a row's fold waits for that row only (a row past the token's
+            // last has an empty resource and a group past the piece an offset
+            // at the row's end: both read zeros without touching memory).
+            // FP8 issues only the token's loads and waits for all of them: its
+            // 8-byte loads of empty rows cost more than the waits save (at 8 x
+            // 4096 tokens, H = 7168, top-8: MXFP4 204 -> 200 us, FP8 288 ->
+            // 304 us with every load issued).
             u32x2 raw[G][C];
+            if constexpr (WIRE == kWireMxfp4) {
 #pragma unroll
-            for (int q = 0; q < G; ++q) {
+                for (int q = 0; q < G; ++q) {
+                    const bool in = i0 + q < n;  // uniform
+                    const int64_t gq = in ? __builtin_amdgcn_readlane(gl, i0 + q) : 0;
+                    const __amdgpu_buffer_rsrc_t ry =
+                        row_rsrc(a.y + gq * a.row_bytes, in ? a.row_bytes : 0u);
 #pragma unroll
-                for (int c = 0; c < C; ++c) {
-                    const int h = h0 + c * kWave;
-                    if (i0 + q < n && h < hend) {
-                        const int64_t gq = __builtin_amdgcn_readlane(gl, i0 + q);
-                        const __amdgpu_buffer_rsrc_t ry =
-                            row_rsrc(a.y + gq * a.row_bytes, a.row_bytes);
-                        if constexpr (WIRE == kWireFp8Block128)
+                    for (int c = 0; c < C; ++c) {
+                        const int h = h0 + c * kWave;
+                        const uint32_t off = h < hend ? (uint32_t)h * 4u : a.row_bytes;
+                        raw[q][c] = {__builtin_amdgcn_raw_buffer_load_b32(ry, off, 0, aux), 0u};
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < G; ++q) {
+#pragma unroll
+                    for (int c = 0; c < C; ++c) {
+                        const int h = h0 + c * kWave;
+                        if (i0 + q < n && h < hend) {
+                            const int64_t gq = __builtin_amdgcn_readlane(gl, i0 + q);
+                            const __amdgpu_buffer_rsrc_t ry =
+                                row_rsrc(a.y + gq * a.row_bytes, a.row_bytes);
                             raw[q][c] = __builtin_amdgcn_raw_buffer_load_b64(ry, h * 8, 0, aux);
-                        else
-                            raw[q][c] = {__builtin_amdgcn_raw_buffer_load_b32(ry, h * 4, 0, aux), 0u};
+                        }
                     }
                 }
             }
