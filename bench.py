@@ -598,7 +598,7 @@ def host_cpu():
 
 def device_copy_rate(torch, mib=1024, steps=5):
     """GB/s of a plain device-to-device copy of mib MiB (bytes read + written
-    per second), the box's own copy rate to set the path's rates against."""
+    per second), the machine's own copy rate to set the path's rates against."""
     n = mib << 20
     a = torch.ones(n, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
@@ -1461,7 +1461,7 @@ def run(args):
     if args.small and args.workload is None:
         line["workloads"] = measure_small_workloads(args, cra, torch, np)
         progress("the other workloads")
-    # the box's own device copy rate (1 GiB, torch), measured last so its
+    # the machine's own device copy rate (1 GiB, torch), measured last so its
     # buffers take no part in the placement of the timed ones
     copy_rate = device_copy_rate(torch)
     line["device_copy_GBps"] = round(copy_rate, 1)
