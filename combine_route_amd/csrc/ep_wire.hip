@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void ep_quantize_kernel(QuantizeArgs a)
         const __amdgpu_buffer_rsrc_t rsc = row_rsrc(a.scales + row * sbytes, sbytes);
 #pragma unroll
         for (int c = 0; c < kQuantChunks; ++c) {
-            if (c < a.piece_chunks) {
+            if (c == 0 || c < a.piece_chunks) {  // the host ensures piece_chunks >= 1
                 const int e = e0 + c * kQuantChunk;
                 float f[8];
                 widen<DT>(raw[c], f);
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) void ep_quantize_kernel(QuantizeArgs a)
         const __amdgpu_buffer_rsrc_t rsc = row_rsrc(a.scales + row * (a.H / 32), (uint32_t)a.H / 32u);
 #pragma unroll
         for (int c = 0; c < kQuantChunks; ++c) {
-            if (c < a.piece_chunks) {
+            if (c == 0 || c < a.piece_chunks) {  // the host ensures piece_chunks >= 1
                 const int e = e0 + c * kQuantChunk;
                 float f[8];
                 widen<DT>(raw[c], f);
