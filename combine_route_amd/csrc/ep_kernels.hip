@@ -371,7 +371,7 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
             for (int u = 0; u < VPL; ++u)
                 c[u] = cast_e4m3(raw[u], a.cast);
         }
-        for (int i = 0; i < n; ++i) {
+        auto store_to = [&](int i) {
             const int d = uniform(s_list[tok][i]);
             const int s = uniform(s_base[d] + s_loc[tok][d]);
             const __amdgpu_buffer_rsrc_t rd =
@@ -387,14 +387,31 @@ __global__ __launch_bounds__(1024) void ep_copy_kernel(CopyArgs a, TileMap tm)
                         bstore16<Policy<kStream>::copy_store>(raw[u], rd, (uint32_t)vv * 16u);
                 }
             }
+        };
+        // large pieces: the first destination outside the loop, so that each
+        // of its stores waits for its own vector only
+        int i0 = 0;
+        if constexpr (VPL >= 8) {
+            if (n > 0)
+                store_to(0);
+            i0 = 1;
         }
+        for (int i = i0; i < n; ++i)
+            store_to(i);
     };
     auto load_payload = [&](int64_t src, int v0, u32x4 (&v)[VPL]) {
         const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.x + src * in_bytes, in_bytes);
+        // Large pieces: every load issued (a vector past the piece reads zeros
+        // from the row's end without touching memory), so that the stores can
+        // wait for one vector at a time. Small pieces keep their guarded loads
+        // (issuing all of them cost small calls about 2 us a copy).
 #pragma unroll
         for (int u = 0; u < VPL; ++u) {
             const int vv = v0 + u * kWave + lane;
-            if (vv < vend)
+            if constexpr (VPL >= 8)
+                v[u] = bload16<Policy<kStream>::copy_load>(rs, vv < vend ? (uint32_t)vv * 16u
+                                                                         : in_bytes);
+            else if (vv < vend)
                 v[u] = bload16<Policy<kStream>::copy_load>(rs, (uint32_t)vv * 16u);
         }
     };

@@ -232,10 +232,17 @@ __global__ __launch_bounds__(1024) void sx_copy_kernel(StandardArgs a)
         const int t = t_lo + wave + (it / nch) * nwaves;
         const int v0 = vbeg + (it % nch) * kWave * VPL;
         const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.x + (row0 + t) * row_bytes, row_bytes);
+        // Large pieces: every load issued (a vector past the piece reads zeros
+        // from the row's end without touching memory), so that the conversions
+        // and stores can wait for one vector at a time; small pieces keep their
+        // guarded loads, as the dispatch copy does.
 #pragma unroll
         for (int u = 0; u < VPL; ++u) {
             const int vv = v0 + u * kWave + lane;
-            if (vv < vend)
+            if constexpr (VPL >= 8)
+                v[u] = bload16<Policy<kStream>::copy_load>(rs, vv < vend ? (uint32_t)vv * 16u
+                                                                         : row_bytes);
+            else if (vv < vend)
                 v[u] = bload16<Policy<kStream>::copy_load>(rs, (uint32_t)vv * 16u);
         }
     };
@@ -252,7 +259,7 @@ __global__ __launch_bounds__(1024) void sx_copy_kernel(StandardArgs a)
             for (int u = 0; u < VPL; ++u)
                 c[u] = cast_e4m3(v[u], a.cast);
         }
-        for (int i = 0; i < n; ++i) {
+        auto store_to = [&](int i) {
             const int64_t gi = __builtin_amdgcn_readlane(prow, i);
             const __amdgpu_buffer_rsrc_t rd =
                 row_rsrc(a.px + gi * a.out_row_bytes, a.out_row_bytes);
@@ -267,7 +274,17 @@ __global__ __launch_bounds__(1024) void sx_copy_kernel(StandardArgs a)
                         bstore16<Policy<kStream>::copy_store>(v[u], rd, (uint32_t)vv * 16u);
                 }
             }
+        };
+        // large pieces: the first packed row outside the loop, so that each of
+        // its stores waits for its own vector only
+        int i0 = 0;
+        if constexpr (VPL >= 8) {
+            if (n > 0)
+                store_to(0);
+            i0 = 1;
         }
+        for (int i = i0; i < n; ++i)
+            store_to(i);
     };
     // Small pieces (small rows or small calls, where time is latency): each
     // wave's first item loads while wave 0 routes the tile.
