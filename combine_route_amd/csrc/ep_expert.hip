@@ -282,10 +282,16 @@ __global__ __launch_bounds__(1024) void ex_copy_kernel(ExpertArgs a)
         const int r = r_lo + wave + (it / nch) * nwaves;
         const int v0 = vbeg + (it % nch) * kWave * VPL;
         const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.x + (row0 + r) * row_bytes, row_bytes);
+        // Large pieces: every load issued (a vector past the piece reads zeros
+        // from the row's end without touching memory), so that the stores can
+        // wait for one vector at a time; small pieces keep their guarded loads.
 #pragma unroll
         for (int u = 0; u < VPL; ++u) {
             const int vv = v0 + u * kWave + lane;
-            if (vv < vend)
+            if constexpr (VPL >= 8)
+                v[u] = bload16<Policy<kStream>::copy_load>(rs, vv < vend ? (uint32_t)vv * 16u
+                                                                         : row_bytes);
+            else if (vv < vend)
                 v[u] = bload16<Policy<kStream>::copy_load>(rs, (uint32_t)vv * 16u);
         }
     };
@@ -296,7 +302,7 @@ __global__ __launch_bounds__(1024) void ex_copy_kernel(ExpertArgs a)
         // lane i < n: the packed row of the row's i-th kept expert, read
         // from LDS for all of them at once
         const int32_t prow = lane < n ? s_p[r][lane] : 0;
-        for (int i = 0; i < n; ++i) {
+        auto store_to = [&](int i) {
             const int64_t gi = __builtin_amdgcn_readlane(prow, i);
             const __amdgpu_buffer_rsrc_t rd = row_rsrc(a.px + gi * row_bytes, row_bytes);
 #pragma unroll
@@ -305,7 +311,17 @@ __global__ __launch_bounds__(1024) void ex_copy_kernel(ExpertArgs a)
                 if (vv < vend)
                     bstore16<Policy<kStream>::copy_store>(v[u], rd, (uint32_t)vv * 16u);
             }
+        };
+        // large pieces: the first packed row outside the loop, so that each of
+        // its stores waits for its own vector only
+        int i0 = 0;
+        if constexpr (VPL >= 8) {
+            if (n > 0)
+                store_to(0);
+            i0 = 1;
         }
+        for (int i = i0; i < n; ++i)
+            store_to(i);
     };
     // Small pieces (small rows or small calls, where time is latency): each
     // wave's first item loads while wave 0 routes the tile.
