@@ -433,10 +433,12 @@ ep_launch_t auto_launch(const ep_plan* p, const int32_t* ntok)
         // more ids a token). Measured on MI355X, 8 x 4096 tokens, top-8, copy
         // kernel us, old rule -> this one: 14 KB bf16 rows 619 -> 592, 7 KB
         // fp8 rows 346 -> 308, 8 KB rows 384 -> 353, bf16 -> E4M3 cast 376 ->
-        // 337 (16 waves); 4 x 4096 tokens, top-64, 4 KB rows: 84 -> 66.
+        // 337 (16 waves); 4 x 4096 tokens, top-64, 4 KB rows: 84 -> 66. The
+        // cast takes 4 waves as well now that its large pieces keep their
+        // loads in flight together (it had waited for each load before
+        // issuing the next): 330-334 us with 4 or 16 waves.
         const bool share = s.k <= 16;
-        l.dispatch_waves = !share ? (l.tile_tokens >= 64 ? 8 : 16)
-                           : p->cfg.dispatch_cast != EP_CAST_NONE ? 16 : 4;
+        l.dispatch_waves = !share ? (l.tile_tokens >= 64 ? 8 : 16) : 4;
         l.dispatch_token_split = share ? l.tile_tokens / l.dispatch_waves : 1;
         l.dispatch_row_split = (int)std::min<int64_t>(
             max_split, std::max<int64_t>(1, row_vecs * 16 / kMinPieceBytes));

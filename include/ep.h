@@ -409,8 +409,8 @@ typedef struct ep_launch {
      * 512 tiles of 32 tokens) use 16 waves, no shared tile and rows cut
      * until the grid has about 1024 blocks; larger calls
      * cut rows into pieces of at least 7 KB and, up to top-16, share each
-     * tile among blocks of one token a wave (4 waves, 16 with a
-     * dispatch_cast; dispatch_token_split = tile_tokens / dispatch_waves,
+     * tile among blocks of one token a wave (4 waves;
+     * dispatch_token_split = tile_tokens / dispatch_waves,
      * recomputed when tile_tokens or dispatch_waves is overridden);
      * above top-16 they share no tile. */
     int32_t dispatch_token_split;

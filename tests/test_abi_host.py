@@ -325,12 +325,12 @@ def test_launch_override_limits_and_auto_geometry(lib):
     assert (big["tile_tokens"], big["dispatch_token_split"], big["dispatch_row_split"]) == \
         (32, 1, 1)
     lib.ep_plan_destroy(plan)
-    # a cast dispatch: 16 waves a block, one token a wave
+    # a cast dispatch: as the plain one, 4 waves a block, one token a wave
     rc, plan = make_plan(lib, cra.make_config(8, 7168, 4096, 32, 8, "fp8", "bf16",
                                               dispatch_cast="bf16"))
     cast = cra.ep_plan_get_launch(plan, [4096] * 8)
     assert (cast["dispatch_waves"], cast["dispatch_token_split"], cast["dispatch_row_split"]) == \
-        (16, 4, 2)
+        (4, 16, 2)
     lib.ep_plan_destroy(plan)
 
 
