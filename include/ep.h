@@ -304,7 +304,7 @@ const char *ep_last_error(void);
  *   combine_row_split    pieces a combined row is split into, a wave each:
  *                        1..H/8. A piece of at most 2 KB is folded row by row
  *                        (every contribution row's piece loaded one row at a
- *                        time, three rows in flight); a larger one a column
+ *                        time, two rows in flight); a larger one a column
  *                        chunk at a time. Automatic: calls with 16-token tiles
  *                        cut rows until about 1024 blocks of 4 waves, and
  *                        into pieces of at most 2 KB (rows in the combine
